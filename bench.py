@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MoE fine-tuning hot path on one MI355X.
+
+Default workload: one Qwen3-30B-A3B-shaped MoE layer (T=4096 tokens, H=2048,
+E=128 experts, top-8, SwiGLU I=768), bf16 activations and expert weights,
+fp32 router and Adam state, a fixed seeded 0.5% active mask.  One step =
+forward (router, routing, grouping, gate_up + SwiGLU, down + combine), MSE
+loss gradient, masked backward (dA, router gradient, dX, masked dW at the
+active entries) and SparseAdam (experts) + dense Adam (router).
+
+Also measured (reported beside the step): the RigL scan on 8192 tokens of the
+same layer after an int4 -> bf16 resident dequant (forward, dense backward,
+global top-0.5%, RigL drop/grow at 30%), and the CPU oracle on a bounded
+sample of the step (a baseline, not a target).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse MoE-layer train-step tokens/s (Qwen3-30B-A3B-shaped); RigL scan ms"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VEC_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, TFLOP/s
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_work(shape, k):
+    """Per-launch algorithmic flops and HBM bytes of each kernel class of one
+    step: every operand the method must move, counted once."""
+    T, H, E, K, I = shape
+    S = T * K
+    b = 2  # bf16 bytes
+    W_gu, W_d = E * 2 * I * H * b, E * H * I * b
+    X = T * H * b
+    gu, a = S * 2 * I * b, S * I * b
+    return {
+        "gate_up": (2.0 * S * H * 2 * I, W_gu + X + gu + a),
+        "down": (2.0 * S * I * H, W_d + a + X),
+        "da": (2.0 * S * H * I, W_d + X + gu + a + gu),
+        "dx": (2.0 * S * 2 * I * H, W_gu + gu + X),
+        "masked_dw": (2.0 * k * S / E, 2 * X + gu + a + 8 * k),
+        "adam": (0.0, 28 * k),
+        "router_gemm": (2.0 * T * H * E, X + E * H * 4 + T * E * 4),
+    }
+
+
+def roofline_entry(name, flops, nbytes, ms):
+    ai = flops / nbytes if nbytes else 0.0
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flops and ai >= ridge:
+        ach = flops / (ms * 1e-3) / 1e12
+        return dict(kernel=name, bound="mfma", achieved=ach, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=ach / BF16_PEAK_TFLOPS)
+    ach = nbytes / (ms * 1e-3) / 1e9
+    return dict(kernel=name, bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=ach / HBM_PEAK_GBS)
+
+
+def make_layer(lay_cls, dims, d, idx, act):
+    lay = lay_cls(*dims, act=act, device="cuda")
+    lay.load(d["X"], d["Wr"], d["W_gu"], d["W_d"], d["tgt"])
+    lay.set_active(idx)
+    return lay
+
+
+def time_kernel_classes(capi, lay, classes, lr):
+    """Average launch time (ms) of each kernel class over one step, events
+    recorded on the launch stream by the library's timing hook."""
+    import torch
+    out = {}
+    for c in classes:
+        capi.timer_arm(c, 8)
+        lay.train_step(lr=lr, check_skip=False)
+        torch.cuda.synchronize()
+        ms = capi.timer_read(8)
+        out[capi.KERNEL_CLASS_NAMES[c]] = sum(ms) / len(ms) if ms else 0.0
+    capi.timer_arm(-1)
+    return out
+
+
+def rigl_scan(capi, synth, layer_mod, d, idx, dims, scan_tokens, repeats=2):
+    """int4 resident dequant, then forward + dense backward + RigL on
+    `scan_tokens` tokens; returns timings and turnover."""
+    import numpy as np
+    import torch
+    T, H, E, K, I = dims
+    log("rigl: quantising expert weights to int4 (input preparation)")
+    rows_gu, rows_d = E * 2 * I, E * H
+    q_gu, s_gu = [], []
+    Wgu2 = d["W_gu"].reshape(rows_gu, H)
+    for r0 in range(0, rows_gu, 16384):
+        q, s = synth.quantize_int4_g64(Wgu2[r0:r0 + 16384])
+        q_gu.append(q); s_gu.append(s)
+    Wd2 = d["W_d"].reshape(rows_d, I)
+    q_d, s_d = [], []
+    for r0 in range(0, rows_d, 65536):
+        q, s = synth.quantize_int4_g64(Wd2[r0:r0 + 65536])
+        q_d.append(q); s_d.append(s)
+    dev = "cuda"
+    qg = torch.from_numpy(np.concatenate(q_gu)).to(dev)
+    sg = torch.from_numpy(np.concatenate(s_gu).view(np.int16)).to(dev)
+    qd = torch.from_numpy(np.concatenate(q_d)).to(dev)
+    sd = torch.from_numpy(np.concatenate(s_d).view(np.int16)).to(dev)
+    del q_gu, s_gu, q_d, s_d
+    Ts = scan_tokens
+    X = synth.to_bf16_values(synth.normal((Ts, H), 1.0, 10))
+    tgt = synth.to_bf16_values(synth.normal((Ts, H), 1.0, 14))
+    lay = layer_mod.SparseMoELayer(Ts, H, E, K, I, act=capi.BF16, device=dev)
+    lay.X = torch.from_numpy(X).to(dev).to(torch.bfloat16)
+    lay.tgt = torch.from_numpy(tgt).to(dev).to(torch.bfloat16)
+    lay.Wr = torch.from_numpy(d["Wr"]).to(dev)
+    N = lay.shape.N
+    lay.W = torch.empty(N, dtype=torch.bfloat16, device=dev)
+    ngu = lay.shape.n_gate_up
+    # dequant once into the resident bf16 working copy (timed)
+    for rep in range(2):
+        torch.cuda.synchronize()
+        capi.timer_arm(capi.K_DEQUANT, 4)
+        capi.dequant_resident(qg, sg, rows_gu, H, 64, lay.W[:ngu])
+        capi.dequant_resident(qd, sd, rows_d, I, 64, lay.W[ngu:])
+        torch.cuda.synchronize()
+        dq_ms = capi.timer_read(4)
+        capi.timer_arm(-1)
+    dq_bytes = qg.numel() + sg.numel() * 2 + qd.numel() + sd.numel() * 2 + N * 2
+    k = idx.size
+    r = (3 * k) // 10
+    grad = torch.empty(N, dtype=torch.float32, device=dev)
+    ws = torch.empty(capi.workspace_size(capi.WS_RIGL, None, N, k), dtype=torch.uint8, device=dev)
+    times, stats = [], None
+    for rep in range(repeats + 1):
+        lay.set_active(idx)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        lay.dense_scan(out=grad)
+        st = layer_mod.rigl(lay, grad, r, ws=ws)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) * 1e3
+        if rep > 0:
+            times.append(dt)
+        stats = st.cpu().numpy()
+        log(f"rigl: scan {rep} {dt:.2f} ms")
+    return dict(rigl_scan_ms=float(np.median(times)), scan_tokens=Ts,
+                dequant_ms=float(sum(dq_ms)), dequant_GBps=dq_bytes / (sum(dq_ms) * 1e-3) / 1e9,
+                turnover_applied=float(stats[1]) / k, turnover_topk_vs_old=float(stats[2]) / k,
+                rigl_k=int(k), rigl_r=int(r))
+
+
+def cpu_baseline(d, idx, dims, sample_tokens):
+    """The CPU oracle, as it stands, on one train step over a sample of the
+    layer's tokens (same weights and mask); tokens/s."""
+    import numpy as np
+    from oracle import usaf_oracle as O
+    T, H, E, K, I = dims
+    R = O.Rounding(O.BF16, O.CONTRACT)
+    X = d["X"][:sample_tokens]
+    tgt = d["tgt"][:sample_tokens]
+    z = np.zeros(idx.size)
+    t0 = time.perf_counter()
+    O.train_step(X, tgt, d["Wr"], d["W_gu"], d["W_d"], K, idx, z, z, np.zeros_like(d["Wr"]),
+                 np.zeros_like(d["Wr"]), 0, 1e-3, 0.9, 0.999, 1e-8, R)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(p.get("num_threads", 1)) for p in threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    return dict(value=sample_tokens / dt, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"one oracle train step (forward, loss, masked backward, SparseAdam, "
+                       f"router Adam) on {sample_tokens} of the {T} tokens of the same layer; "
+                       f"{dt:.1f} s", seconds=dt)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--scan-tokens", type=int, default=8192)
+    ap.add_argument("--no-scan", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=512)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not "
+              f"sharded across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import usaf_synth as synth
+    from sparse_fine_tuning_amd import capi
+    from sparse_fine_tuning_amd import layer as layer_mod
+
+    dims = (4096, 2048, 128, 8, 768)
+    T, H, E, K, I = dims
+    N = 3 * E * H * I
+    k = (N * 5) // 1000
+    lr = 1e-3
+    log("generating the seeded Qwen3-shaped layer")
+    d = synth.moe_layer(*dims, bf16=True, seeds=(0, 1, 2, 3, 4))
+    idx = synth.random_mask(N, k, 5)
+    lay = make_layer(layer_mod.SparseMoELayer, dims, d, idx, capi.BF16)
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        lay.train_step(lr=lr, check_skip=False)
+    torch.cuda.synchronize()
+    classes = [capi.K_ROUTER_GEMM, capi.K_ROUTE, capi.K_GATE_UP, capi.K_DOWN, capi.K_COMBINE_Y,
+               capi.K_MSE, capi.K_DA, capi.K_ROUTER_BWD, capi.K_DX, capi.K_COMBINE_DX,
+               capi.K_MASKED_DW, capi.K_ADAM]
+    per_class = time_kernel_classes(capi, lay, classes, lr)
+    work = algorithmic_work(dims, k)
+    dominant = max((c for c in per_class if c in work), key=lambda c: per_class[c])
+    dom_class = capi.KERNEL_CLASS_NAMES.index(dominant)
+    launches_per_step = 2 if dominant == "adam" else 1
+    log(f"per-class ms {json.dumps({c: round(v, 4) for c, v in per_class.items()})}; dominant {dominant}")
+
+    capi.timer_arm(dom_class, args.steps * launches_per_step)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        lay.train_step(lr=lr, check_skip=False)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kms = capi.timer_read(args.steps * launches_per_step)
+    capi.timer_arm(-1)
+    nonfinite = int(lay.nonfinite.item())
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    value = T / (ms_step * 1e-3)
+    kern_ms = sum(kms) / len(kms)
+    fl, by = work[dominant]
+    roof = roofline_entry(dominant, fl, by, kern_ms)
+    roof.update(kernel_ms=kern_ms, launches=len(kms), algorithmic_flops=fl,
+                algorithmic_bytes=by, traffic=None)
+    log(f"step {ms_step:.3f} ms -> {value:.0f} tokens/s; {dominant} {kern_ms:.3f} ms")
+    step_kernels = {c: dict(ms=per_class[c], **roofline_entry(c, *work[c], per_class[c]))
+                    for c in per_class if c in work and per_class[c] > 0}
+    del lay
+    torch.cuda.empty_cache()
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Qwen3-30B-A3B-shaped single MoE layer sparse train step",
+                   "tokens": T, "hidden": H, "experts": E, "top_k": K, "intermediate": I,
+                   "active_entries": k, "density": 0.005, "lr": lr},
+        "roofline": roof,
+        "nonfinite_steps": nonfinite,
+        "step_kernels": step_kernels,
+    }
+    if not args.no_scan:
+        log("rigl scan")
+        out["rigl"] = rigl_scan(capi, synth, layer_mod, d, idx, dims, args.scan_tokens)
+        out["rigl_scan_ms"] = out["rigl"]["rigl_scan_ms"]
+        torch.cuda.empty_cache()
+    if not args.no_cpu:
+        log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
+        out["cpu_baseline"] = cpu_baseline(d, idx, dims, args.cpu_tokens)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,70 @@
+// Device helpers shared by the USAF HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "usaf.h"
+
+namespace usaf {
+
+using bf16_t = uint16_t;  // bf16 storage (upper half of an fp32 word)
+
+constexpr int kWave = 64;
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// bf16 -> fp32 is exact: the bf16 bits are the fp32 word's upper half.
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16_t(u >> 16);
+}
+
+// Activation element access, fp32 or bf16 storage.
+template <class T> struct Act;
+template <> struct Act<float> {
+  static constexpr int32_t code = USAF_F32;
+  __device__ __forceinline__ static float ld(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void st(float* p, int64_t i, float v) { p[i] = v; }
+  // value as stored (rounded to the storage type)
+  __device__ __forceinline__ static float round(float v) { return v; }
+};
+template <> struct Act<bf16_t> {
+  static constexpr int32_t code = USAF_BF16;
+  __device__ __forceinline__ static float ld(const bf16_t* p, int64_t i) { return bf2f(p[i]); }
+  __device__ __forceinline__ static void st(bf16_t* p, int64_t i, float v) { p[i] = f2bf(v); }
+  __device__ __forceinline__ static float round(float v) { return bf2f(f2bf(v)); }
+};
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+__device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + expf(-g)); }
+
+__device__ __forceinline__ bool finite_f(float v) { return (__float_as_uint(v) & 0x7f800000u) != 0x7f800000u; }
+
+// Wave-wide helpers (64 lanes).
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Router weight as the forward GEMM multiplies it: bf16-rounded for bf16 layers.
+template <class T> __device__ __forceinline__ float router_w(const float* Wr, int64_t i) {
+  float w = Wr[i];
+  return Act<T>::code == USAF_BF16 ? bf2f(f2bf(w)) : w;
+}
+
+}  // namespace usaf
+
+// Host-side launch checking: every launcher returns a usaf_status.
+#define USAF_LAUNCH_CHECK()                                         \
+  do {                                                              \
+    if (hipGetLastError() != hipSuccess) return USAF_ERR_HIP;       \
+  } while (0)
+
+#define USAF_TRY(expr)                                              \
+  do {                                                              \
+    usaf_status _s = (expr);                                        \
+    if (_s != USAF_OK) return _s;                                   \
+  } while (0)

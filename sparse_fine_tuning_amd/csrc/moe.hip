@@ -1,0 +1,772 @@
+// MoE layer forward / masked backward for the USAF sparse fine-tuning step.
+//
+// Method: the usaf README ("tsuyu122/usaf"): tokens are routed to a few
+// experts, the router (gating network) is trained densely, and expert weights
+// get gradients only at the selected ~0.5% ("how it works" bullets, A100
+// per-operation table).  The expert MLP is SwiGLU over the fused gate_up /
+// down tensors of the README's quantisation recipe.
+#include <algorithm>
+
+#include "common.hpp"
+#include "gemm_fma.hpp"
+#include "moe_internal.hpp"
+#include "timing.hpp"
+
+namespace usaf {
+
+// ---------------------------------------------------------------------------
+// Routing
+// ---------------------------------------------------------------------------
+
+// Order-preserving map of an fp32 logit to uint32 (larger = better).  NaN
+// ranks below -inf; -0 and +0 are equal.
+__device__ __forceinline__ uint32_t logit_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave per token: K rounds of a wave-wide max over (key, -expert id),
+// then softmax over the K chosen logits.  E <= 1024, K <= 64.
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
+                                                         int E, int K, int32_t* __restrict__ ids,
+                                                         float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (t >= T) return;  // uniform per wave
+  const float* lt = logits + int64_t(t) * E;
+  uint64_t comp[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + 64 * i;
+    comp[i] = (e < E) ? ((uint64_t(logit_key(lt[e])) << 32) | uint64_t(0xffffffffu - uint32_t(e)))
+                      : 0ull;
+  }
+  int my_id = 0;
+  float my_l = 0.f;
+  for (int j = 0; j < K; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) best = comp[i] > best ? comp[i] : best;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      uint64_t o = __shfl_xor(best, off, 64);
+      best = o > best ? o : best;
+    }
+    const int e = int(0xffffffffu - uint32_t(best & 0xffffffffull));
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (lane + 64 * i == e) comp[i] = 0;
+    if (lane == j) {
+      my_id = e;
+      my_l = lt[e];
+    }
+  }
+  const float l0 = __shfl(my_l, 0, 64);
+  float z = lane < K ? expf(my_l - l0) : 0.f;
+  float sum = z;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  if (lane < K) {
+    ids[int64_t(t) * K + lane] = my_id;
+    w[int64_t(t) * K + lane] = z / sum;
+  }
+}
+
+// Stable grouping of slots by expert.  Block e counts the slots routed to
+// experts < e (its offset) and == e, then writes its slots in ascending slot
+// order with a block-wide ballot scan.
+__global__ __launch_bounds__(256) void expert_sort_kernel(const int32_t* __restrict__ ids, int S,
+                                                          int E, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ perm,
+                                                          int32_t* __restrict__ slot_pos) {
+  __shared__ int red[2][4];
+  __shared__ int wtot[4];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int lt = 0, eq = 0;
+  for (int s = tid; s < S; s += 256) {
+    const int id = ids[s];
+    lt += id < e;
+    eq += id == e;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    lt += __shfl_xor(lt, off, 64);
+    eq += __shfl_xor(eq, off, 64);
+  }
+  if (lane == 0) {
+    red[0][wid] = lt;
+    red[1][wid] = eq;
+  }
+  __syncthreads();
+  const int off_e = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  if (tid == 0) {
+    offsets[e] = off_e;
+    if (e == E - 1) offsets[E] = S;
+  }
+  int run = off_e;
+  for (int base = 0; base < S; base += 256) {
+    const int s = base + tid;
+    const bool f = s < S && ids[s] == e;
+    const uint64_t b = __ballot(f);
+    const int pre = __popcll(b & ((1ull << lane) - 1ull));
+    if (lane == 0) wtot[wid] = __popcll(b);
+    __syncthreads();
+    int wbase = 0;
+    for (int w = 0; w < wid; ++w) wbase += wtot[w];
+    const int tot = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    if (f) {
+      const int p = run + wbase + pre;
+      perm[p] = s;
+      slot_pos[s] = p;
+    }
+    run += tot;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32-FMA GEMM problems (see gemm_fma.hpp for the contract)
+// ---------------------------------------------------------------------------
+
+// logits[T, E] = X[T, H] * Wr'[E, H]^T
+template <class T>
+struct RouterGemm {
+  const T* X;
+  const float* Wr;
+  float* logits;
+  int Tn, H, E;
+  struct Tile { int m0, mc, n0, nc; };
+  __device__ bool get_tile(int bx, int by, int, Tile& t) const {
+    t.m0 = bx * 64; t.n0 = by * 64;
+    t.mc = min(64, Tn - t.m0); t.nc = min(64, E - t.n0);
+    return t.mc > 0 && t.nc > 0;
+  }
+  __device__ int kbeg(const Tile&) const { return 0; }
+  __device__ int kend(const Tile&) const { return H; }
+  __device__ void load_a(const Tile& t, int k0, float (*S)[kFmaLd], int tid) const {
+    load_kcontig(S, tid, t.mc, k0, H, [&](int r, int k) { return Act<T>::ld(X, int64_t(t.m0 + r) * H + k); });
+  }
+  __device__ void load_b(const Tile& t, int k0, float (*S)[kFmaLd], int tid) const {
+    load_kcontig(S, tid, t.nc, k0, H, [&](int r, int k) { return router_w<T>(Wr, int64_t(t.n0 + r) * H + k); });
+  }
+  __device__ void epilogue(const Tile& t, float (&acc)[4][4], int tm, int tn) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = tm + 16 * i, n = tn + 16 * j;
+        if (m < t.mc && n < t.nc) logits[int64_t(t.m0 + m) * E + t.n0 + n] = acc[i][j];
+      }
+  }
+};
+
+// gate_up forward for expert e: [g | u] = X[tokens of e] * W_gu[e]^T with the
+// SwiGLU epilogue.  A tile covers 32 gate features and the same 32 up
+// features, so each thread holds matching (g, u) pairs.
+template <class T>
+struct GateUpFwd {
+  const T* X; const T* Wgu; const int32_t* offsets; const int32_t* perm;
+  T* gu; T* a;
+  int H, E, K, I;
+  struct Tile { int e, m0, mc, f0, off; };
+  __device__ bool get_tile(int bx, int by, int, Tile& t) const {
+    if (!find_mtile(offsets, E, bx, 64, t.e, t.m0, t.mc)) return false;
+    t.off = offsets[t.e];
+    t.f0 = by * 32;
+    return true;
+  }
+  __device__ int kbeg(const Tile&) const { return 0; }
+  __device__ int kend(const Tile&) const { return H; }
+  __device__ void load_a(const Tile& t, int k0, float (*S)[kFmaLd], int tid) const {
+    load_kcontig(S, tid, t.mc, k0, H, [&](int r, int k) {
+      const int tok = perm[t.off + t.m0 + r] / K;
+      return Act<T>::ld(X, int64_t(tok) * H + k);
+    });
+  }
+  __device__ void load_b(const Tile& t, int k0, float (*S)[kFmaLd], int tid) const {
+    load_kcontig(S, tid, 64, k0, H, [&](int c, int k) {
+      const int row = c < 32 ? t.f0 + c : I + t.f0 + (c - 32);
+      return Act<T>::ld(Wgu, (int64_t(t.e) * 2 * I + row) * H + k);
+    });
+  }
+  __device__ void epilogue(const Tile& t, float (&acc)[4][4], int tm, int tn) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = tm + 16 * i;
+      if (m >= t.mc) continue;
+      const int64_t p = t.off + t.m0 + m;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int f = t.f0 + tn + 16 * jj;
+        const float g = Act<T>::round(acc[i][jj]);
+        const float u = Act<T>::round(acc[i][jj + 2]);
+        Act<T>::st(gu, p * 2 * I + f, g);
+        Act<T>::st(gu, p * 2 * I + I + f, u);
+        Act<T>::st(a, p * I + f, silu_f(g) * u);
+      }
+    }
+  }
+};
+
+// down forward: ybuf[p, :] = a[p, :] * W_d[e]^T  (fp32, expert-major rows)
+template <class T>
+struct DownFwd {
+  const T* a; const T* Wd; const int32_t* offsets; float* ybuf;
+  int H, E, I;
+  struct Tile { int e, m0, mc, n0, off; };
+  __device__ bool get_tile(int bx, int by, int, Tile& t) const {
+    if (!find_mtile(offsets, E, bx, 64, t.e, t.m0, t.mc)) return false;
+    t.off = offsets[t.e];
+    t.n0 = by * 64;
+    return true;
+  }
+  __device__ int kbeg(const Tile&) const { return 0; }
+  __device__ int kend(const Tile&) const { return I; }
+  __device__ void load_a(const Tile& t, int k0, float (*S)[kFmaLd], int tid) const {
+    load_kcontig(S, tid, t.mc, k0, I, [&](int r, int k) { return Act<T>::ld(a, int64_t(t.off + t.m0 + r) * I + k); });
+  }
+  __device__ void load_b(const Tile& t, int k0, float (*S)[kFmaLd], int tid) const {
+    load_kcontig(S, tid, 64, k0, I, [&](int r, int k) { return Act<T>::ld(Wd, (int64_t(t.e) * H + t.n0 + r) * I + k); });
+  }
+  __device__ void epilogue(const Tile& t, float (&acc)[4][4], int tm, int tn) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = tm + 16 * i;
+      if (m >= t.mc) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ybuf[int64_t(t.off + t.m0 + m) * H + t.n0 + tn + 16 * j] = acc[i][j];
+    }
+  }
+};
+
+// dA backward: U = dY[tokens of e] * W_d[e]; epilogue forms dGU (SwiGLU
+// derivative, scaled by the routing weight) and per-tile partial dw sums.
+template <class T>
+struct DaBwd {
+  const T* dY; const T* Wd; const int32_t* offsets; const int32_t* perm; const float* topk_w;
+  const T* gu; const T* a; T* dgu; float* dwpart;
+  int H, E, K, I, NT;
+  struct Tile { int e, m0, mc, n0, nc, off, nt; };
+  __device__ bool get_tile(int bx, int by, int, Tile& t) const {
+    if (!find_mtile(offsets, E, bx, 64, t.e, t.m0, t.mc)) return false;
+    t.off = offsets[t.e];
+    t.n0 = by * 64;
+    t.nc = min(64, I - t.n0);
+    t.nt = by;
+    return true;
+  }
+  __device__ int kbeg(const Tile&) const { return 0; }
+  __device__ int kend(const Tile&) const { return H; }
+  __device__ void load_a(const Tile& t, int k0, float (*S)[kFmaLd], int tid) const {
+    load_kcontig(S, tid, t.mc, k0, H, [&](int r, int k) {
+      const int tok = perm[t.off + t.m0 + r] / K;
+      return Act<T>::ld(dY, int64_t(tok) * H + k);
+    });
+  }
+  __device__ void load_b(const Tile& t, int k0, float (*S)[kFmaLd], int tid) const {
+    load_rcontig(S, tid, t.nc, k0, H, [&](int n, int k) { return Act<T>::ld(Wd, (int64_t(t.e) * H + k) * I + t.n0 + n); });
+  }
+  __device__ void epilogue(const Tile& t, float (&acc)[4][4], int tm, int tn) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = tm + 16 * i;
+      const bool valid = m < t.mc;
+      const int64_t p = t.off + t.m0 + (valid ? m : 0);
+      const float wt = valid ? topk_w[perm[p]] : 0.f;
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = tn + 16 * j;
+        if (valid && n < t.nc) {
+          const int f = t.n0 + n;
+          const float U = acc[i][j];
+          part = fmaf(U, Act<T>::ld(a, p * I + f), part);
+          const float da = wt * U;
+          const float g = Act<T>::ld(gu, p * 2 * I + f);
+          const float u = Act<T>::ld(gu, p * 2 * I + I + f);
+          const float sg = sigmoid_f(g);
+          Act<T>::st(dgu, p * 2 * I + f, da * u * sg * (1.f + g * (1.f - sg)));
+          Act<T>::st(dgu, p * 2 * I + I + f, da * g * sg);
+        }
+      }
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) part += __shfl_xor(part, off, 16);
+      if (tn == 0 && valid) dwpart[p * NT + t.nt] = part;
+    }
+  }
+};
+
+// dX backward: vbuf[p, :] = dGU[p, :] * W_gu[e]   (fp32, expert-major rows)
+template <class T>
+struct DxBwd {
+  const T* dgu; const T* Wgu; const int32_t* offsets; float* vbuf;
+  int H, E, I;
+  struct Tile { int e, m0, mc, n0, off; };
+  __device__ bool get_tile(int bx, int by, int, Tile& t) const {
+    if (!find_mtile(offsets, E, bx, 64, t.e, t.m0, t.mc)) return false;
+    t.off = offsets[t.e];
+    t.n0 = by * 64;
+    return true;
+  }
+  __device__ int kbeg(const Tile&) const { return 0; }
+  __device__ int kend(const Tile&) const { return 2 * I; }
+  __device__ void load_a(const Tile& t, int k0, float (*S)[kFmaLd], int tid) const {
+    load_kcontig(S, tid, t.mc, k0, 2 * I, [&](int r, int k) { return Act<T>::ld(dgu, int64_t(t.off + t.m0 + r) * 2 * I + k); });
+  }
+  __device__ void load_b(const Tile& t, int k0, float (*S)[kFmaLd], int tid) const {
+    load_rcontig(S, tid, 64, k0, 2 * I, [&](int n, int k) { return Act<T>::ld(Wgu, (int64_t(t.e) * 2 * I + k) * H + t.n0 + n); });
+  }
+  __device__ void epilogue(const Tile& t, float (&acc)[4][4], int tm, int tn) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = tm + 16 * i;
+      if (m >= t.mc) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vbuf[int64_t(t.off + t.m0 + m) * H + t.n0 + tn + 16 * j] = acc[i][j];
+    }
+  }
+};
+
+// Dense gate_up weight gradient of expert e: dW[r, c] = sum_p dGU[p, r] X[t(p), c]
+template <class T>
+struct DenseDwGu {
+  const T* dgu; const T* X; const int32_t* offsets; const int32_t* perm; float* dW;
+  int H, E, K, I;
+  struct Tile { int e, r0, n0, off, ne; };
+  __device__ bool get_tile(int bx, int by, int bz, Tile& t) const {
+    t.e = bz; t.n0 = bx * 64; t.r0 = by * 64;
+    t.off = offsets[t.e]; t.ne = offsets[t.e + 1] - t.off;
+    return true;
+  }
+  __device__ int kbeg(const Tile&) const { return 0; }
+  __device__ int kend(const Tile& t) const { return t.ne; }
+  __device__ void load_a(const Tile& t, int k0, float (*S)[kFmaLd], int tid) const {
+    load_rcontig(S, tid, 64, k0, t.ne, [&](int r, int k) { return Act<T>::ld(dgu, int64_t(t.off + k) * 2 * I + t.r0 + r); });
+  }
+  __device__ void load_b(const Tile& t, int k0, float (*S)[kFmaLd], int tid) const {
+    load_rcontig(S, tid, 64, k0, t.ne, [&](int c, int k) {
+      const int tok = perm[t.off + k] / K;
+      return Act<T>::ld(X, int64_t(tok) * H + t.n0 + c);
+    });
+  }
+  __device__ void epilogue(const Tile& t, float (&acc)[4][4], int tm, int tn) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dW[(int64_t(t.e) * 2 * I + t.r0 + tm + 16 * i) * H + t.n0 + tn + 16 * j] = acc[i][j];
+  }
+};
+
+// Dense down weight gradient of expert e: dW[r, c] = sum_p w_p dY[t(p), r] a[p, c]
+template <class T>
+struct DenseDwD {
+  const T* dY; const float* topk_w; const T* a; const int32_t* offsets; const int32_t* perm;
+  float* dW;
+  int H, E, K, I;
+  int64_t ngu;
+  struct Tile { int e, r0, n0, nc, off, ne; };
+  __device__ bool get_tile(int bx, int by, int bz, Tile& t) const {
+    t.e = bz; t.n0 = bx * 64; t.r0 = by * 64; t.nc = min(64, I - t.n0);
+    t.off = offsets[t.e]; t.ne = offsets[t.e + 1] - t.off;
+    return true;
+  }
+  __device__ int kbeg(const Tile&) const { return 0; }
+  __device__ int kend(const Tile& t) const { return t.ne; }
+  __device__ void load_a(const Tile& t, int k0, float (*S)[kFmaLd], int tid) const {
+    load_rcontig(S, tid, 64, k0, t.ne, [&](int r, int k) {
+      const int s = perm[t.off + k];
+      return topk_w[s] * Act<T>::ld(dY, int64_t(s / K) * H + t.r0 + r);
+    });
+  }
+  __device__ void load_b(const Tile& t, int k0, float (*S)[kFmaLd], int tid) const {
+    load_rcontig(S, tid, t.nc, k0, t.ne, [&](int c, int k) { return Act<T>::ld(a, int64_t(t.off + k) * I + t.n0 + c); });
+  }
+  __device__ void epilogue(const Tile& t, float (&acc)[4][4], int tm, int tn) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = tn + 16 * j;
+        if (n < t.nc) dW[ngu + (int64_t(t.e) * H + t.r0 + tm + 16 * i) * I + t.n0 + n] = acc[i][j];
+      }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Combines, router backward, masked dW, loss
+// ---------------------------------------------------------------------------
+
+// Y[t, :] = sum_{j=0..K-1} w[t, j] * y[slot t*K+j]   (fixed j order)
+template <class T>
+__global__ __launch_bounds__(256) void combine_y_kernel(const float* __restrict__ ybuf,
+                                                        const float* __restrict__ topk_w,
+                                                        const int32_t* __restrict__ slot_pos, int H,
+                                                        int K, T* __restrict__ Y) {
+  const int t = blockIdx.x;
+  for (int h = threadIdx.x; h < H; h += blockDim.x) {
+    float acc = 0.f;
+    for (int j = 0; j < K; ++j) {
+      const int s = t * K + j;
+      acc = fmaf(topk_w[s], ybuf[int64_t(slot_pos[s]) * H + h], acc);
+    }
+    Act<T>::st(Y, int64_t(t) * H + h, acc);
+  }
+}
+
+// Per token: dw[s] = sum of the dA tiles' partial dot products (fixed
+// order), then dlogits of the chosen experts: w_j (dw_j - sum_m w_m dw_m).
+__global__ __launch_bounds__(256) void dw_router_kernel(const float* __restrict__ dwpart, int NT,
+                                                        const float* __restrict__ topk_w,
+                                                        const int32_t* __restrict__ slot_pos,
+                                                        int T, int K, float* __restrict__ dw,
+                                                        float* __restrict__ dl) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  float sw = 0.f;
+  for (int j = 0; j < K; ++j) {
+    const int s = t * K + j;
+    const int64_t p = slot_pos[s];
+    float d = 0.f;
+    for (int nt = 0; nt < NT; ++nt) d += dwpart[p * NT + nt];
+    dw[s] = d;
+    sw = fmaf(topk_w[s], d, sw);
+  }
+  for (int j = 0; j < K; ++j) {
+    const int s = t * K + j;
+    dl[s] = topk_w[s] * (dw[s] - sw);
+  }
+}
+
+// Dense fp32 router gradient dWr[e, h] = sum over slots p of e of
+// dlogits[s(p)] * X[t(p), h] (dlogits is zero off the chosen experts).
+template <class T>
+__global__ __launch_bounds__(256) void dwr_kernel(const float* __restrict__ dl,
+                                                  const T* __restrict__ X,
+                                                  const int32_t* __restrict__ offsets,
+                                                  const int32_t* __restrict__ perm, int H, int K,
+                                                  float* __restrict__ dWr,
+                                                  int32_t* __restrict__ nonfinite) {
+  const int e = blockIdx.x;
+  const int h = blockIdx.y * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  const int p0 = offsets[e], p1 = offsets[e + 1];
+  float acc = 0.f;
+  for (int p = p0; p < p1; ++p) {
+    const int s = perm[p];
+    acc = fmaf(dl[s], Act<T>::ld(X, int64_t(s / K) * H + h), acc);
+  }
+  dWr[int64_t(e) * H + h] = acc;
+  if (nonfinite && !finite_f(acc)) atomicAdd(nonfinite, 1);
+}
+
+// dX[t, :] = sum_j v[slot t*K+j] + sum_j dlogits[t, j] * Wr'[e_j, :]
+template <class T>
+__global__ __launch_bounds__(256) void combine_dx_kernel(const float* __restrict__ vbuf,
+                                                         const float* __restrict__ dl,
+                                                         const int32_t* __restrict__ ids,
+                                                         const float* __restrict__ Wr,
+                                                         const int32_t* __restrict__ slot_pos,
+                                                         int H, int K, T* __restrict__ dX) {
+  const int t = blockIdx.x;
+  for (int h = threadIdx.x; h < H; h += blockDim.x) {
+    float acc = 0.f;
+    for (int j = 0; j < K; ++j) acc += vbuf[int64_t(slot_pos[t * K + j]) * H + h];
+    for (int j = 0; j < K; ++j) {
+      const int s = t * K + j;
+      acc = fmaf(dl[s], router_w<T>(Wr, int64_t(ids[s]) * H + h), acc);
+    }
+    Act<T>::st(dX, int64_t(t) * H + h, acc);
+  }
+}
+
+// Expert-weight gradient at each listed flat index (one thread per entry).
+template <class T>
+__global__ __launch_bounds__(256) void masked_dw_kernel(
+    const uint32_t* __restrict__ idx, int64_t nnz, const T* __restrict__ X,
+    const T* __restrict__ dY, const T* __restrict__ dgu, const T* __restrict__ a,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ perm, int H, int K, int I, uint32_t ngu, int64_t N,
+    float* __restrict__ dW, int32_t* __restrict__ nonfinite) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= nnz) return;
+  const uint32_t f = idx[i];
+  if (int64_t(f) >= N) {  // not a valid flat index: flag it instead of reading out of range
+    dW[i] = __int_as_float(0x7fc00000);
+    if (nonfinite) atomicAdd(nonfinite, 1);
+    return;
+  }
+  float acc = 0.f;
+  if (f < ngu) {
+    const uint32_t per = uint32_t(2 * I) * uint32_t(H);
+    const int e = int(f / per);
+    const uint32_t rem = f - uint32_t(e) * per;
+    const int r = int(rem / uint32_t(H)), c = int(rem % uint32_t(H));
+    for (int p = offsets[e]; p < offsets[e + 1]; ++p) {
+      const int tok = perm[p] / K;
+      acc = fmaf(Act<T>::ld(dgu, int64_t(p) * 2 * I + r), Act<T>::ld(X, int64_t(tok) * H + c), acc);
+    }
+  } else {
+    const uint32_t g = f - ngu, per = uint32_t(H) * uint32_t(I);
+    const int e = int(g / per);
+    const uint32_t rem = g - uint32_t(e) * per;
+    const int r = int(rem / uint32_t(I)), c = int(rem % uint32_t(I));
+    for (int p = offsets[e]; p < offsets[e + 1]; ++p) {
+      const int s = perm[p];
+      const float l = topk_w[s] * Act<T>::ld(dY, int64_t(s / K) * H + r);
+      acc = fmaf(l, Act<T>::ld(a, int64_t(p) * I + c), acc);
+    }
+  }
+  dW[i] = acc;
+  if (nonfinite && !finite_f(acc)) atomicAdd(nonfinite, 1);
+}
+
+// Loss: per-block partial sums of (Y - tgt)^2 over 4096 elements, dY written.
+template <class T>
+__global__ __launch_bounds__(256) void mse_partial_kernel(const T* __restrict__ Y,
+                                                          const T* __restrict__ tgt, int64_t n,
+                                                          float scale, T* __restrict__ dY,
+                                                          float* __restrict__ part) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int64_t base = int64_t(blockIdx.x) * 4096;
+  float acc = 0.f;
+#pragma unroll 4
+  for (int r = 0; r < 16; ++r) {
+    const int64_t i = base + r * 256 + tid;
+    if (i < n) {
+      const float d = Act<T>::ld(Y, i) - Act<T>::ld(tgt, i);
+      acc = fmaf(d, d, acc);
+      Act<T>::st(dY, i, scale * d);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = acc;
+  __syncthreads();
+  if (tid == 0) part[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ __launch_bounds__(256) void mse_final_kernel(const float* __restrict__ part, int nb,
+                                                        float inv_n, float* __restrict__ loss,
+                                                        int32_t* __restrict__ nonfinite) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  float acc = 0.f;
+  for (int b = tid; b < nb; b += 256) acc += part[b];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    const float l = ((red[0] + red[1]) + (red[2] + red[3])) * inv_n;
+    *loss = l;
+    if (nonfinite && !finite_f(l)) atomicAdd(nonfinite, 1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+template <class P>
+static usaf_status launch_fma(const P& p, dim3 grid, hipStream_t st, int kclass) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return USAF_OK;
+  timer_begin(kclass, st);
+  hipLaunchKernelGGL(gemm_fma_kernel<P>, grid, dim3(256), 0, st, p);
+  timer_end(kclass, st);
+  USAF_LAUNCH_CHECK();
+  return USAF_OK;
+}
+
+static inline unsigned mtiles_bound(const usaf_moe_shape& s) {
+  return unsigned(ceil_div(int64_t(s.T) * s.K, 64) + s.E);
+}
+
+template <class T>
+static usaf_status route_impl(const usaf_moe_shape& s, const float* logits,
+                              const usaf_moe_state& st, hipStream_t stream) {
+  const int S = s.T * s.K;
+  timer_begin(USAF_K_ROUTE, stream);
+  hipLaunchKernelGGL(route_topk_kernel, dim3(unsigned(ceil_div(s.T, 4))), dim3(256), 0, stream,
+                     logits, s.T, s.E, s.K, st.topk_ids, st.topk_w);
+  USAF_LAUNCH_CHECK();
+  hipLaunchKernelGGL(expert_sort_kernel, dim3(unsigned(s.E)), dim3(256), 0, stream, st.topk_ids, S,
+                     s.E, st.offsets, st.perm, st.slot_pos);
+  timer_end(USAF_K_ROUTE, stream);
+  USAF_LAUNCH_CHECK();
+  return USAF_OK;
+}
+
+template <class T>
+static usaf_status forward_impl(const usaf_moe_shape& s, const T* X, const float* Wr, const T* W,
+                                T* Y, const usaf_moe_state& st, char* ws, hipStream_t stream) {
+  const WsForward L = ws_forward(s);
+  float* ybuf = reinterpret_cast<float*>(ws + L.ybuf);
+  const T* Wgu = W;
+  const T* Wd = W + int64_t(s.E) * 2 * s.I * s.H;
+  // router logits
+  RouterGemm<T> rg{X, Wr, st.logits, s.T, s.H, s.E};
+  USAF_TRY(launch_fma(rg, dim3(unsigned(ceil_div(s.T, 64)), unsigned(ceil_div(s.E, 64))), stream, USAF_K_ROUTER_GEMM));
+  USAF_TRY(route_impl<T>(s, st.logits, st, stream));
+  // experts
+  GateUpFwd<T> gp{X, Wgu, st.offsets, st.perm, static_cast<T*>(st.gu), static_cast<T*>(st.a),
+                  s.H, s.E, s.K, s.I};
+  USAF_TRY(launch_fma(gp, dim3(mtiles_bound(s), unsigned(s.I / 32)), stream, USAF_K_GATE_UP));
+  DownFwd<T> dp{static_cast<const T*>(st.a), Wd, st.offsets, ybuf, s.H, s.E, s.I};
+  USAF_TRY(launch_fma(dp, dim3(mtiles_bound(s), unsigned(s.H / 64)), stream, USAF_K_DOWN));
+  timer_begin(USAF_K_COMBINE_Y, stream);
+  hipLaunchKernelGGL(combine_y_kernel<T>, dim3(unsigned(s.T)), dim3(256), 0, stream, ybuf,
+                     st.topk_w, st.slot_pos, s.H, s.K, Y);
+  timer_end(USAF_K_COMBINE_Y, stream);
+  USAF_LAUNCH_CHECK();
+  return USAF_OK;
+}
+
+template <class T>
+static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const float* Wr, const T* W,
+                                 const usaf_moe_state& st, const T* dY, const uint32_t* idx,
+                                 int64_t nnz, float* dW, float* dWr, T* dX, int32_t* nonfinite,
+                                 char* ws, hipStream_t stream) {
+  const WsBackward L = ws_backward(s);
+  float* vbuf = reinterpret_cast<float*>(ws + L.vbuf);
+  float* dwpart = reinterpret_cast<float*>(ws + L.dwpart);
+  float* dl = reinterpret_cast<float*>(ws + L.dl);
+  const int NT = L.nt;
+  const T* Wgu = W;
+  const T* Wd = W + int64_t(s.E) * 2 * s.I * s.H;
+  T* dgu = static_cast<T*>(st.dgu);
+  const T* gu = static_cast<const T*>(st.gu);
+  const T* a = static_cast<const T*>(st.a);
+
+  DaBwd<T> da{dY, Wd, st.offsets, st.perm, st.topk_w, gu, a, dgu, dwpart, s.H, s.E, s.K, s.I, NT};
+  USAF_TRY(launch_fma(da, dim3(mtiles_bound(s), unsigned(NT)), stream, USAF_K_DA));
+  timer_begin(USAF_K_ROUTER_BWD, stream);
+  hipLaunchKernelGGL(dw_router_kernel, dim3(unsigned(ceil_div(s.T, 256))), dim3(256), 0, stream,
+                     dwpart, NT, st.topk_w, st.slot_pos, s.T, s.K, st.dw, dl);
+  USAF_LAUNCH_CHECK();
+  hipLaunchKernelGGL(dwr_kernel<T>, dim3(unsigned(s.E), unsigned(ceil_div(s.H, 256))), dim3(256),
+                     0, stream, dl, X, st.offsets, st.perm, s.H, s.K, dWr,
+                     idx ? nonfinite : nullptr);
+  timer_end(USAF_K_ROUTER_BWD, stream);
+  USAF_LAUNCH_CHECK();
+  if (dX) {
+    DxBwd<T> dx{dgu, Wgu, st.offsets, vbuf, s.H, s.E, s.I};
+    USAF_TRY(launch_fma(dx, dim3(mtiles_bound(s), unsigned(s.H / 64)), stream, USAF_K_DX));
+    timer_begin(USAF_K_COMBINE_DX, stream);
+    hipLaunchKernelGGL(combine_dx_kernel<T>, dim3(unsigned(s.T)), dim3(256), 0, stream, vbuf, dl,
+                       st.topk_ids, Wr, st.slot_pos, s.H, s.K, dX);
+    timer_end(USAF_K_COMBINE_DX, stream);
+    USAF_LAUNCH_CHECK();
+  }
+  const int64_t ngu = int64_t(s.E) * 2 * s.I * s.H;
+  if (idx) {
+    if (nnz > 0) {
+      timer_begin(USAF_K_MASKED_DW, stream);
+      hipLaunchKernelGGL(masked_dw_kernel<T>, dim3(unsigned(ceil_div(nnz, 256))), dim3(256), 0,
+                         stream, idx, nnz, X, dY, dgu, a, st.topk_w, st.offsets, st.perm, s.H, s.K,
+                         s.I, uint32_t(ngu), n_weights(s), dW, nonfinite);
+      timer_end(USAF_K_MASKED_DW, stream);
+      USAF_LAUNCH_CHECK();
+    }
+  } else {
+    DenseDwGu<T> g1{dgu, X, st.offsets, st.perm, dW, s.H, s.E, s.K, s.I};
+    USAF_TRY(launch_fma(g1, dim3(unsigned(s.H / 64), unsigned(2 * s.I / 64), unsigned(s.E)), stream, USAF_K_DENSE_DW));
+    DenseDwD<T> g2{dY, st.topk_w, a, st.offsets, st.perm, dW, s.H, s.E, s.K, s.I, ngu};
+    USAF_TRY(launch_fma(g2, dim3(unsigned(ceil_div(s.I, 64)), unsigned(s.H / 64), unsigned(s.E)), stream, USAF_K_DENSE_DW));
+  }
+  return USAF_OK;
+}
+
+template <class T>
+static usaf_status mse_impl(const usaf_moe_shape& s, const T* Y, const T* tgt, T* dY, float* loss,
+                            int32_t* nonfinite, char* ws, hipStream_t stream) {
+  const int64_t n = int64_t(s.T) * s.H;
+  const int nb = int(ceil_div(n, 4096));
+  float* part = reinterpret_cast<float*>(ws);
+  timer_begin(USAF_K_MSE, stream);
+  hipLaunchKernelGGL(mse_partial_kernel<T>, dim3(unsigned(nb)), dim3(256), 0, stream, Y, tgt, n,
+                     float(2.0 / double(n)), dY, part);
+  USAF_LAUNCH_CHECK();
+  hipLaunchKernelGGL(mse_final_kernel, dim3(1), dim3(256), 0, stream, part, nb,
+                     float(1.0 / double(n)), loss, nonfinite);
+  timer_end(USAF_K_MSE, stream);
+  USAF_LAUNCH_CHECK();
+  return USAF_OK;
+}
+
+}  // namespace usaf
+
+using namespace usaf;
+
+static bool state_ok(const usaf_moe_state* st, bool bwd) {
+  if (!st || !st->logits || !st->topk_ids || !st->topk_w || !st->offsets || !st->perm ||
+      !st->slot_pos || !st->gu || !st->a)
+    return false;
+  if (bwd && (!st->dgu || !st->dw)) return false;
+  return true;
+}
+
+extern "C" usaf_status usaf_moe_forward(const usaf_moe_shape* shape, const void* X, const float* Wr,
+                                        const void* Wflat, void* Y, const usaf_moe_state* state,
+                                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  USAF_TRY(check_shape(shape));
+  if (!X || !Wr || !Wflat || !Y || !state_ok(state, false)) return USAF_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < ws_forward(*shape).total) return USAF_ERR_WORKSPACE;
+  if (shape->act == USAF_BF16)
+    return forward_impl<bf16_t>(*shape, static_cast<const bf16_t*>(X), Wr,
+                                static_cast<const bf16_t*>(Wflat), static_cast<bf16_t*>(Y), *state,
+                                static_cast<char*>(ws), stream);
+  return forward_impl<float>(*shape, static_cast<const float*>(X), Wr,
+                             static_cast<const float*>(Wflat), static_cast<float*>(Y), *state,
+                             static_cast<char*>(ws), stream);
+}
+
+extern "C" usaf_status usaf_masked_backward(const usaf_moe_shape* shape, const void* X,
+                                            const float* Wr, const void* Wflat,
+                                            const usaf_moe_state* state, const void* dY,
+                                            const uint32_t* idx, int64_t nnz, float* dW,
+                                            float* dWr, void* dX, int32_t* nonfinite, void* ws,
+                                            size_t ws_bytes, hipStream_t stream) {
+  USAF_TRY(check_shape(shape));
+  if (!X || !Wr || !Wflat || !dY || !dWr || !state_ok(state, true)) return USAF_ERR_INVALID_ARG;
+  const int64_t N = n_weights(*shape);
+  if (nnz < 0 || nnz > N) return USAF_ERR_INVALID_ARG;
+  if (!idx && nnz != N) return USAF_ERR_INVALID_ARG;
+  if (nnz > 0 && !dW) return USAF_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < ws_backward(*shape).total) return USAF_ERR_WORKSPACE;
+  if (shape->act == USAF_BF16)
+    return backward_impl<bf16_t>(*shape, static_cast<const bf16_t*>(X), Wr,
+                                 static_cast<const bf16_t*>(Wflat), *state,
+                                 static_cast<const bf16_t*>(dY), idx, nnz, dW, dWr,
+                                 static_cast<bf16_t*>(dX), nonfinite, static_cast<char*>(ws), stream);
+  return backward_impl<float>(*shape, static_cast<const float*>(X), Wr,
+                              static_cast<const float*>(Wflat), *state,
+                              static_cast<const float*>(dY), idx, nnz, dW, dWr,
+                              static_cast<float*>(dX), nonfinite, static_cast<char*>(ws), stream);
+}
+
+extern "C" usaf_status usaf_mse_grad(const usaf_moe_shape* shape, const void* Y, const void* tgt,
+                                     void* dY, float* loss, int32_t* nonfinite, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  USAF_TRY(check_shape(shape));
+  if (!Y || !tgt || !dY || !loss) return USAF_ERR_INVALID_ARG;
+  const int64_t n = int64_t(shape->T) * shape->H;
+  if (!ws || ws_bytes < size_t(ceil_div(n, 4096)) * 4 + 64) return USAF_ERR_WORKSPACE;
+  if (shape->act == USAF_BF16)
+    return mse_impl<bf16_t>(*shape, static_cast<const bf16_t*>(Y), static_cast<const bf16_t*>(tgt),
+                            static_cast<bf16_t*>(dY), loss, nonfinite, static_cast<char*>(ws),
+                            stream);
+  return mse_impl<float>(*shape, static_cast<const float*>(Y), static_cast<const float*>(tgt),
+                         static_cast<float*>(dY), loss, nonfinite, static_cast<char*>(ws), stream);
+}
+
+extern "C" usaf_status usaf_route(const usaf_moe_shape* shape, const float* logits,
+                                  const usaf_moe_state* state, hipStream_t stream) {
+  USAF_TRY(check_shape(shape));
+  if (!logits || !state || !state->topk_ids || !state->topk_w || !state->offsets ||
+      !state->perm || !state->slot_pos)
+    return USAF_ERR_INVALID_ARG;
+  return route_impl<float>(*shape, logits, *state, stream);
+}

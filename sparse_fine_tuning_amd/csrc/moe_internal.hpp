@@ -1,0 +1,67 @@
+// Host-side shape validation and workspace layouts shared by the entry points.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "usaf.h"
+
+namespace usaf {
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline int64_t n_weights(const usaf_moe_shape& s) {
+  return int64_t(3) * s.E * int64_t(s.H) * s.I;
+}
+
+// Shapes the kernels handle (see usaf_moe_shape in usaf.h).
+inline usaf_status check_shape(const usaf_moe_shape* s) {
+  if (!s) return USAF_ERR_INVALID_ARG;
+  if (s->T < 1 || s->H < 1 || s->E < 1 || s->K < 1 || s->I < 1) return USAF_ERR_INVALID_ARG;
+  if (s->K > s->E) return USAF_ERR_INVALID_ARG;
+  if (s->act != USAF_F32 && s->act != USAF_BF16) return USAF_ERR_INVALID_ARG;
+  if (s->E > 1024 || s->K > 64) return USAF_ERR_UNSUPPORTED;
+  if (s->H % 64 != 0 || s->I % 32 != 0) return USAF_ERR_UNSUPPORTED;
+  if (n_weights(*s) >= (int64_t(1) << 32)) return USAF_ERR_UNSUPPORTED;
+  if (int64_t(s->T) * s->K >= (int64_t(1) << 31)) return USAF_ERR_UNSUPPORTED;
+  return USAF_OK;
+}
+
+// Forward workspace: fp32 expert outputs before the combine, [S, H].
+struct WsForward {
+  size_t ybuf, total;
+};
+inline WsForward ws_forward(const usaf_moe_shape& s) {
+  WsForward L;
+  const size_t S = size_t(s.T) * s.K;
+  L.ybuf = 0;
+  size_t mse = ((size_t(s.T) * s.H + 4095) / 4096) * 4 + 64;
+  size_t y = S * s.H * 4;
+  L.total = align256(y > mse ? y : mse);
+  return L;
+}
+
+// Backward workspace: fp32 dX contributions [S, H], partial dw sums
+// [S, NT] (NT = dA column tiles), dlogits of the chosen experts [S].
+struct WsBackward {
+  size_t vbuf, dwpart, dl, total;
+  int nt;
+};
+inline WsBackward ws_backward(const usaf_moe_shape& s) {
+  WsBackward L;
+  const size_t S = size_t(s.T) * s.K;
+  L.nt = (s.I + 63) / 64;
+  L.vbuf = 0;
+  L.dwpart = align256(S * s.H * 4);
+  L.dl = L.dwpart + align256(S * L.nt * 4);
+  L.total = L.dl + align256(S * 4);
+  return L;
+}
+
+}  // namespace usaf
+
+namespace usaf {
+// Workspace of one top-k selection over n keys / one RigL reselection.
+size_t topk_ws_bytes(int64_t n);
+size_t rigl_ws_bytes(int64_t N, int64_t k);
+}  // namespace usaf
