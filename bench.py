@@ -190,7 +190,7 @@ def main():
     ap.add_argument("--scan-tokens", type=int, default=8192)
     ap.add_argument("--no-scan", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not "

@@ -184,14 +184,17 @@ USAF_API usaf_status usaf_rigl_reselect(const usaf_moe_shape *shape, const float
  * W (w_dtype: USAF_BF16 updated with one round-to-nearest-even, or USAF_F32)
  * is updated in place at idx[i] (idx NULL = dense: entry i is W[i]); g, m, v
  * are [n] fp32 aligned with idx; m, v are updated in place.  step >= 1 is the
- * step number after incrementing.  skip_if_nonzero (nullable, device int32):
+ * step number after incrementing.  The hyper-parameters are taken in double:
+ * 1-beta and the bias corrections 1-beta^step are formed in double on the
+ * host and rounded once to fp32 (a float beta2 = 0.999f would shift 1-beta2
+ * by 1.3e-5 relative).  skip_if_nonzero (nullable, device int32):
  * when it holds a non-zero value the kernel changes nothing (the NaN-step
  * skip of the README's results table); the caller then does not advance its
  * step counter.  idx entries must be distinct.  Errors: INVALID_ARG for
  * n < 0, step < 1, null W/g/m/v. */
 USAF_API usaf_status usaf_sparse_adam(int32_t w_dtype, void *W, const uint32_t *idx, int64_t n,
-                             const float *g, float *m, float *v, int64_t step, float lr,
-                             float beta1, float beta2, float eps,
+                             const float *g, float *m, float *v, int64_t step, double lr,
+                             double beta1, double beta2, double eps,
                              const int32_t *skip_if_nonzero, hipStream_t stream);
 
 /* Resident dequantisation (README "how it works": caching bullet; dequant

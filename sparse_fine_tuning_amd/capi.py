@@ -82,8 +82,8 @@ def _load():
         "usaf_masked_backward": [vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp],
         "usaf_importance_topk": [vp, i64, i64, vp, i64, vp, vp, vp, sz, vp],
         "usaf_rigl_reselect": [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
-        "usaf_sparse_adam": [i32, vp, vp, i64, vp, vp, vp, i64, C.c_float, C.c_float, C.c_float,
-                             C.c_float, vp, vp],
+        "usaf_sparse_adam": [i32, vp, vp, i64, vp, vp, vp, i64, C.c_double, C.c_double,
+                             C.c_double, C.c_double, vp, vp],
         "usaf_dequant_resident": [vp, vp, i64, i64, i32, vp, vp],
         "usaf_mse_grad": [vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "usaf_route": [vp, vp, vp, vp],

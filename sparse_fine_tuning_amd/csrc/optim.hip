@@ -71,25 +71,27 @@ static unsigned grid_for(int64_t n, int64_t per_block = 256, int64_t cap = 256 *
 using namespace usaf;
 
 extern "C" usaf_status usaf_sparse_adam(int32_t w_dtype, void* W, const uint32_t* idx, int64_t n,
-                                        const float* g, float* m, float* v, int64_t step, float lr,
-                                        float beta1, float beta2, float eps,
+                                        const float* g, float* m, float* v, int64_t step, double lr,
+                                        double beta1, double beta2, double eps,
                                         const int32_t* skip_if_nonzero, hipStream_t stream) {
   if (n < 0 || step < 1) return USAF_ERR_INVALID_ARG;
   if (w_dtype != USAF_F32 && w_dtype != USAF_BF16) return USAF_ERR_INVALID_ARG;
   if (n == 0) return USAF_OK;
   if (!W || !g || !m || !v) return USAF_ERR_INVALID_ARG;
-  const double bc1 = 1.0 - pow(double(beta1), double(step));
-  const double bc2 = 1.0 - pow(double(beta2), double(step));
-  const float omb1 = float(1.0 - double(beta1)), omb2 = float(1.0 - double(beta2));
+  const double bc1 = 1.0 - pow(beta1, double(step));
+  const double bc2 = 1.0 - pow(beta2, double(step));
+  const float omb1 = float(1.0 - beta1), omb2 = float(1.0 - beta2);
   timer_begin(USAF_K_ADAM, stream);
   if (w_dtype == USAF_BF16)
     hipLaunchKernelGGL(adam_kernel<bf16_t>, dim3(grid_for(n)), dim3(256), 0, stream,
-                       static_cast<bf16_t*>(W), idx, n, g, m, v, lr, beta1, beta2, omb1, omb2,
-                       float(bc1), float(bc2), eps, skip_if_nonzero);
+                       static_cast<bf16_t*>(W), idx, n, g, m, v, float(lr), float(beta1),
+                       float(beta2), omb1, omb2, float(bc1), float(bc2), float(eps),
+                       skip_if_nonzero);
   else
     hipLaunchKernelGGL(adam_kernel<float>, dim3(grid_for(n)), dim3(256), 0, stream,
-                       static_cast<float*>(W), idx, n, g, m, v, lr, beta1, beta2, omb1, omb2,
-                       float(bc1), float(bc2), eps, skip_if_nonzero);
+                       static_cast<float*>(W), idx, n, g, m, v, float(lr), float(beta1),
+                       float(beta2), omb1, omb2, float(bc1), float(bc2), float(eps),
+                       skip_if_nonzero);
   timer_end(USAF_K_ADAM, stream);
   USAF_LAUNCH_CHECK();
   return USAF_OK;

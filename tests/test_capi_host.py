@@ -100,7 +100,7 @@ def test_entry_points_refuse_bad_arguments_before_launch():
     assert L.usaf_rigl_reselect(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, N + 1, 1, FAKE, FAKE,
                                 FAKE, None, FAKE, 1 << 30, None) == 1
     # adam: step < 1, bad dtype, n == 0 no-op
-    f = C.c_float
+    f = C.c_double
     assert L.usaf_sparse_adam(1, FAKE, None, 10, FAKE, FAKE, FAKE, 0, f(1e-3), f(.9), f(.999), f(1e-8), None, None) == 1
     assert L.usaf_sparse_adam(5, FAKE, None, 10, FAKE, FAKE, FAKE, 1, f(1e-3), f(.9), f(.999), f(1e-8), None, None) == 1
     assert L.usaf_sparse_adam(1, None, None, 0, None, None, None, 1, f(1e-3), f(.9), f(.999), f(1e-8), None, None) == 0
