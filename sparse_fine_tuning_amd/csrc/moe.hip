@@ -6,6 +6,7 @@
 // per-operation table).  The expert MLP is SwiGLU over the fused gate_up /
 // down tensors of the README's quantisation recipe.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "gemm_fma.hpp"
@@ -606,16 +607,28 @@ static usaf_status forward_impl(const usaf_moe_shape& s, const T* X, const float
   float* ybuf = reinterpret_cast<float*>(ws + L.ybuf);
   const T* Wgu = W;
   const T* Wd = W + int64_t(s.E) * 2 * s.I * s.H;
+  constexpr bool kMfma = std::is_same<T, bf16_t>::value;
   // router logits
-  RouterGemm<T> rg{X, Wr, st.logits, s.T, s.H, s.E};
-  USAF_TRY(launch_fma(rg, dim3(unsigned(ceil_div(s.T, 64)), unsigned(ceil_div(s.E, 64))), stream, USAF_K_ROUTER_GEMM));
+  if constexpr (kMfma) {
+    USAF_TRY(mfma_router(s, X, Wr, st.logits, stream));
+  } else {
+    RouterGemm<T> rg{X, Wr, st.logits, s.T, s.H, s.E};
+    USAF_TRY(launch_fma(rg, dim3(unsigned(ceil_div(s.T, 64)), unsigned(ceil_div(s.E, 64))), stream,
+                        USAF_K_ROUTER_GEMM));
+  }
   USAF_TRY(route_impl<T>(s, st.logits, st, stream));
   // experts
-  GateUpFwd<T> gp{X, Wgu, st.offsets, st.perm, static_cast<T*>(st.gu), static_cast<T*>(st.a),
-                  s.H, s.E, s.K, s.I};
-  USAF_TRY(launch_fma(gp, dim3(mtiles_bound(s), unsigned(s.I / 32)), stream, USAF_K_GATE_UP));
-  DownFwd<T> dp{static_cast<const T*>(st.a), Wd, st.offsets, ybuf, s.H, s.E, s.I};
-  USAF_TRY(launch_fma(dp, dim3(mtiles_bound(s), unsigned(s.H / 64)), stream, USAF_K_DOWN));
+  if constexpr (kMfma) {
+    USAF_TRY(mfma_gate_up(s, X, Wgu, st.offsets, st.perm, static_cast<T*>(st.gu),
+                          static_cast<T*>(st.a), stream));
+    USAF_TRY(mfma_down(s, static_cast<const T*>(st.a), Wd, st.offsets, ybuf, stream));
+  } else {
+    GateUpFwd<T> gp{X, Wgu, st.offsets, st.perm, static_cast<T*>(st.gu), static_cast<T*>(st.a),
+                    s.H, s.E, s.K, s.I};
+    USAF_TRY(launch_fma(gp, dim3(mtiles_bound(s), unsigned(s.I / 32)), stream, USAF_K_GATE_UP));
+    DownFwd<T> dp{static_cast<const T*>(st.a), Wd, st.offsets, ybuf, s.H, s.E, s.I};
+    USAF_TRY(launch_fma(dp, dim3(mtiles_bound(s), unsigned(s.H / 64)), stream, USAF_K_DOWN));
+  }
   timer_begin(USAF_K_COMBINE_Y, stream);
   hipLaunchKernelGGL(combine_y_kernel<T>, dim3(unsigned(s.T)), dim3(256), 0, stream, ybuf,
                      st.topk_w, st.slot_pos, s.H, s.K, Y);
@@ -633,15 +646,20 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
   float* vbuf = reinterpret_cast<float*>(ws + L.vbuf);
   float* dwpart = reinterpret_cast<float*>(ws + L.dwpart);
   float* dl = reinterpret_cast<float*>(ws + L.dl);
-  const int NT = L.nt;
+  constexpr bool kMfma = std::is_same<T, bf16_t>::value;
+  const int NT = kMfma ? mfma_dw_partials(s) : int(ceil_div(s.I, 64));
   const T* Wgu = W;
   const T* Wd = W + int64_t(s.E) * 2 * s.I * s.H;
   T* dgu = static_cast<T*>(st.dgu);
   const T* gu = static_cast<const T*>(st.gu);
   const T* a = static_cast<const T*>(st.a);
 
-  DaBwd<T> da{dY, Wd, st.offsets, st.perm, st.topk_w, gu, a, dgu, dwpart, s.H, s.E, s.K, s.I, NT};
-  USAF_TRY(launch_fma(da, dim3(mtiles_bound(s), unsigned(NT)), stream, USAF_K_DA));
+  if constexpr (kMfma) {
+    USAF_TRY(mfma_da(s, dY, Wd, st.offsets, st.perm, st.topk_w, gu, a, dgu, dwpart, stream));
+  } else {
+    DaBwd<T> da{dY, Wd, st.offsets, st.perm, st.topk_w, gu, a, dgu, dwpart, s.H, s.E, s.K, s.I, NT};
+    USAF_TRY(launch_fma(da, dim3(mtiles_bound(s), unsigned(NT)), stream, USAF_K_DA));
+  }
   timer_begin(USAF_K_ROUTER_BWD, stream);
   hipLaunchKernelGGL(dw_router_kernel, dim3(unsigned(ceil_div(s.T, 256))), dim3(256), 0, stream,
                      dwpart, NT, st.topk_w, st.slot_pos, s.T, s.K, st.dw, dl);
@@ -652,8 +670,12 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
   timer_end(USAF_K_ROUTER_BWD, stream);
   USAF_LAUNCH_CHECK();
   if (dX) {
-    DxBwd<T> dx{dgu, Wgu, st.offsets, vbuf, s.H, s.E, s.I};
-    USAF_TRY(launch_fma(dx, dim3(mtiles_bound(s), unsigned(s.H / 64)), stream, USAF_K_DX));
+    if constexpr (kMfma) {
+      USAF_TRY(mfma_dx(s, dgu, Wgu, st.offsets, vbuf, stream));
+    } else {
+      DxBwd<T> dx{dgu, Wgu, st.offsets, vbuf, s.H, s.E, s.I};
+      USAF_TRY(launch_fma(dx, dim3(mtiles_bound(s), unsigned(s.H / 64)), stream, USAF_K_DX));
+    }
     timer_begin(USAF_K_COMBINE_DX, stream);
     hipLaunchKernelGGL(combine_dx_kernel<T>, dim3(unsigned(s.T)), dim3(256), 0, stream, vbuf, dl,
                        st.topk_ids, Wr, st.slot_pos, s.H, s.K, dX);
@@ -671,6 +693,9 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
       USAF_LAUNCH_CHECK();
     }
   } else {
+    if constexpr (kMfma) {
+      return mfma_dense_dw(s, X, dY, dgu, a, st.offsets, st.perm, st.topk_w, dW, stream);
+    }
     DenseDwGu<T> g1{dgu, X, st.offsets, st.perm, dW, s.H, s.E, s.K, s.I};
     USAF_TRY(launch_fma(g1, dim3(unsigned(s.H / 64), unsigned(2 * s.I / 64), unsigned(s.E)), stream, USAF_K_DENSE_DW));
     DenseDwD<T> g2{dY, st.topk_w, a, st.offsets, st.perm, dW, s.H, s.E, s.K, s.I, ngu};

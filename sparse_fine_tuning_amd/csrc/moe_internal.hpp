@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_runtime_api.h>
+
 #include "usaf.h"
 
 namespace usaf {
@@ -50,7 +52,7 @@ struct WsBackward {
 inline WsBackward ws_backward(const usaf_moe_shape& s) {
   WsBackward L;
   const size_t S = size_t(s.T) * s.K;
-  L.nt = (s.I + 63) / 64;
+  L.nt = 2 * ((s.I + 127) / 128);  // >= ceil(I/64): enough for either GEMM path
   L.vbuf = 0;
   L.dwpart = align256(S * s.H * 4);
   L.dl = L.dwpart + align256(S * L.nt * 4);
@@ -61,6 +63,25 @@ inline WsBackward ws_backward(const usaf_moe_shape& s) {
 }  // namespace usaf
 
 namespace usaf {
+// bf16 MFMA GEMMs of the layer (moe_mfma.hip).
+usaf_status mfma_router(const usaf_moe_shape& s, const uint16_t* X, const float* Wr, float* logits,
+                        hipStream_t st);
+usaf_status mfma_gate_up(const usaf_moe_shape& s, const uint16_t* X, const uint16_t* Wgu,
+                         const int32_t* offsets, const int32_t* perm, uint16_t* gu, uint16_t* a,
+                         hipStream_t st);
+usaf_status mfma_down(const usaf_moe_shape& s, const uint16_t* a, const uint16_t* Wd,
+                      const int32_t* offsets, float* ybuf, hipStream_t st);
+int mfma_dw_partials(const usaf_moe_shape& s);
+usaf_status mfma_da(const usaf_moe_shape& s, const uint16_t* dY, const uint16_t* Wd,
+                    const int32_t* offsets, const int32_t* perm, const float* topk_w,
+                    const uint16_t* gu, const uint16_t* a, uint16_t* dgu, float* dwpart,
+                    hipStream_t st);
+usaf_status mfma_dx(const usaf_moe_shape& s, const uint16_t* dgu, const uint16_t* Wgu,
+                    const int32_t* offsets, float* vbuf, hipStream_t st);
+usaf_status mfma_dense_dw(const usaf_moe_shape& s, const uint16_t* X, const uint16_t* dY,
+                          const uint16_t* dgu, const uint16_t* a, const int32_t* offsets,
+                          const int32_t* perm, const float* topk_w, float* dW, hipStream_t st);
+
 // Workspace of one top-k selection over n keys / one RigL reselection.
 size_t topk_ws_bytes(int64_t n);
 size_t rigl_ws_bytes(int64_t N, int64_t k);

@@ -18,11 +18,11 @@ KernelTimer& timer();
 
 inline void timer_begin(int kclass, hipStream_t s) {
   KernelTimer& t = timer();
-  if (t.armed == kclass && t.n < t.cap) (void)hipEventRecord(t.start[t.n], s);
+  if (kclass >= 0 && t.armed == kclass && t.n < t.cap) (void)hipEventRecord(t.start[t.n], s);
 }
 inline void timer_end(int kclass, hipStream_t s) {
   KernelTimer& t = timer();
-  if (t.armed == kclass && t.n < t.cap) {
+  if (kclass >= 0 && t.armed == kclass && t.n < t.cap) {
     (void)hipEventRecord(t.stop[t.n], s);
     ++t.n;
   }
