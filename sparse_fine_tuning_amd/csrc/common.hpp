@@ -46,6 +46,11 @@ __device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + expf
 
 __device__ __forceinline__ bool finite_f(float v) { return (__float_as_uint(v) & 0x7f800000u) != 0x7f800000u; }
 
+// Blocks are dealt round-robin to the 8 XCDs (each with its own L2); remap
+// so that each XCD owns a contiguous range of logical block ids.  nb must be
+// a multiple of 8.
+__device__ __forceinline__ int xcd_remap_blocks(int b, int nb) { return (b & 7) * (nb >> 3) + (b >> 3); }
+
 // Wave-wide helpers (64 lanes).
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

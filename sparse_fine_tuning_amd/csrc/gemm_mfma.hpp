@@ -38,10 +38,8 @@ struct MTile {
   int nt;      // column-tile index
 };
 
-// Blocks are dealt round-robin to the 8 XCDs; remap so that each XCD owns a
-// contiguous range of logical tiles (tiles that share weights or rows then
-// share that XCD's L2).  nb must be a multiple of 8.
-__device__ __forceinline__ int xcd_remap(int b, int nb) { return (b & 7) * (nb >> 3) + (b >> 3); }
+// Logical tile ids are XCD-remapped (xcd_remap_blocks) so tiles that share
+// weights or rows run on one XCD and share its L2.
 
 // Logical tile L -> (expert, column tile, row tile) for groups whose row
 // counts come from device offsets[E+1]; tiles ordered expert-major, then
@@ -233,7 +231,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(P p) {
   __shared__ __attribute__((aligned(16))) bf16_t As[2][kMB * kLdsRow];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kNB * kLdsRow];
   MTile t;
-  if (!p.tile(xcd_remap(blockIdx.x, gridDim.x), t)) return;
+  if (!p.tile(xcd_remap_blocks(blockIdx.x, gridDim.x), t)) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   typename P::ALoader la;

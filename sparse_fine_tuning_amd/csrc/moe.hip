@@ -684,6 +684,10 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
   }
   const int64_t ngu = int64_t(s.E) * 2 * s.I * s.H;
   if (idx) {
+    if constexpr (kMfma) {
+      return masked_dw_bf16(s, idx, nnz, X, dY, dgu, a, st.topk_w, st.offsets, st.perm, dW,
+                            nonfinite, stream);
+    }
     if (nnz > 0) {
       timer_begin(USAF_K_MASKED_DW, stream);
       hipLaunchKernelGGL(masked_dw_kernel<T>, dim3(unsigned(ceil_div(nnz, 256))), dim3(256), 0,

@@ -82,6 +82,11 @@ usaf_status mfma_dense_dw(const usaf_moe_shape& s, const uint16_t* X, const uint
                           const uint16_t* dgu, const uint16_t* a, const int32_t* offsets,
                           const int32_t* perm, const float* topk_w, float* dW, hipStream_t st);
 
+usaf_status masked_dw_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64_t nnz,
+                           const uint16_t* X, const uint16_t* dY, const uint16_t* dgu,
+                           const uint16_t* a, const float* topk_w, const int32_t* offsets,
+                           const int32_t* perm, float* dW, int32_t* nonfinite, hipStream_t st);
+
 // Workspace of one top-k selection over n keys / one RigL reselection.
 size_t topk_ws_bytes(int64_t n);
 size_t rigl_ws_bytes(int64_t N, int64_t k);

@@ -149,6 +149,9 @@ CASES = [
     ("empty_experts_fp32", (8, 64, 16, 1, 32), 0, (40, 41, 42, 43, 44)),
     ("ragged_bf16", (200, 128, 8, 2, 96), 1, (50, 51, 52, 53, 54)),
     ("wide_bf16", (333, 256, 16, 4, 160), 1, (60, 61, 62, 63, 64)),
+    # column-tiled masked gradient: gate_up has H > 2048 columns, down has I > 2048
+    ("coltiled_gate_up_bf16", (64, 4096, 4, 2, 64), 1, (70, 71, 72, 73, 74)),
+    ("coltiled_down_bf16", (48, 128, 3, 2, 2560), 1, (80, 81, 82, 83, 84)),
 ]
 
 
@@ -185,6 +188,19 @@ def test_layer_forward_backward(capi, name, dims, act, seeds):
     assert rel(npf(lay.dW), ref["g"]) <= tol
     assert rel(npf(dense), ref["gd"]) <= tol
     assert int(lay.nonfinite.item()) == 0
+
+
+def test_masked_at_full_density_equals_dense(capi):
+    say("masked dW at 100% density")
+    dims = (64, 2048, 2, 1, 64)
+    d = synth.moe_layer(*dims, bf16=True, seeds=(90, 91, 92, 93, 94))
+    N = 3 * 2 * 2048 * 64
+    idx = np.arange(N, dtype=np.uint32)
+    lay, dense = run_layer(capi, d, dims, 1, idx, dense=True)
+    g = npf(lay.dW)
+    ref = oracle_layer(d, dims, 1, idx[:1])["gd"]
+    assert rel(g, ref) <= TOL_BF16
+    assert rel(g, npf(dense)) <= TOL_BF16
 
 
 def test_repeat_runs_are_bit_identical(capi):
