@@ -24,6 +24,7 @@ constexpr int kSlots = 8;        // slots per staged chunk
 constexpr int kMaxEnt = 16;      // entries per thread per batch
 constexpr int kMaxRB = 512;      // max rows per block
 constexpr int kMaxCB = 1536;     // max columns per block (kMaxCB/8 + kMaxRB/8 <= 256)
+constexpr int kTokTab = 2048;    // slots per token-table window
 constexpr int kLsBytes = kMaxRB * kSlots * 4;
 constexpr int kRsBytes = kMaxCB * kSlots * 2;
 
@@ -38,7 +39,40 @@ struct MaskedArgs {
   int E;
   int64_t base;           // flat index of expert 0's (0,0) entry for this tensor
   float* dW; int32_t* nonfinite;
+  const uint32_t* seg;    // plan: start in idx of every (expert, row, column tile) segment
+  int64_t qbase;          // first segment id of this tensor
 };
+
+// Segments of the plan: tensor-major, then expert, row, column tile, so
+// that segment q+1 starts where q ends (the flat order of the list).
+struct SegLayout {
+  int R0, C0, nct0, R1, C1, nct1, CB0, CB1, E;
+  int64_t ngu, q1, Q;  // flat start of down, first down segment, segment count
+};
+
+__global__ __launch_bounds__(256) void masked_plan_kernel(const uint32_t* __restrict__ idx,
+                                                          int64_t nnz, SegLayout Lq,
+                                                          uint32_t* __restrict__ seg) {
+  const int64_t q = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q > Lq.Q) return;
+  int64_t key;  // flat index where segment q begins
+  if (q == Lq.Q) {
+    key = int64_t(1) << 40;
+  } else if (q < Lq.q1) {
+    const int64_t row = q / Lq.nct0, ct = q - row * Lq.nct0;  // row = e*R0 + r
+    key = row * Lq.C0 + ct * Lq.CB0;
+  } else {
+    const int64_t qq = q - Lq.q1;
+    const int64_t row = qq / Lq.nct1, ct = qq - row * Lq.nct1;
+    key = Lq.ngu + row * Lq.C1 + ct * Lq.CB1;
+  }
+  int64_t lo = 0, hi = nnz;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (int64_t(idx[mid]) < key) lo = mid + 1; else hi = mid;
+  }
+  seg[q] = uint32_t(lo);
+}
 
 __device__ __forceinline__ int64_t lb_idx(const uint32_t* a, int64_t lo, int64_t hi, int64_t v) {
   while (lo < hi) {
@@ -83,7 +117,10 @@ struct StageRegs {
 
 template <bool kDown>
 __device__ __forceinline__ void stage_fetch(const MaskedArgs& A, int b, int nblk_r, int p0,
-                                            int ne, int off, int r_lo, int c0, StageRegs& sr) {
+                                            int pend, int slot0, int r_lo, int c0,
+                                            const int* tok_tab, const float* w_tab,
+                                            StageRegs& sr) {
+  // p0 indexes the token table window; slot0 + p is the expert-major slot row
   const bool isR = b < nblk_r;
   const int j0 = (isR ? b : b - nblk_r) * 8;
 #pragma unroll
@@ -91,16 +128,15 @@ __device__ __forceinline__ void stage_fetch(const MaskedArgs& A, int b, int nblk
     const int p = p0 + t;
     sr.v[t] = make_uint4(0, 0, 0, 0);
     sr.w[t] = 0.f;
-    if (p < ne) {
-      const int slot = off + p;
+    if (p < pend) {
       const bf16_t* src;
       if (isR) {
-        src = kDown ? A.Rm + int64_t(slot) * A.C + c0
-                    : A.Rm + int64_t(A.perm[slot] / A.K) * A.C + c0;
+        src = kDown ? A.Rm + int64_t(slot0 + p) * A.C + c0
+                    : A.Rm + int64_t(tok_tab[p]) * A.C + c0;
       } else {
-        const int s_id = kDown ? A.perm[slot] : 0;
-        src = kDown ? A.L + int64_t(s_id / A.K) * A.R + r_lo : A.L + int64_t(slot) * A.R + r_lo;
-        if (kDown) sr.w[t] = A.topk_w[s_id];
+        src = kDown ? A.L + int64_t(tok_tab[p]) * A.R + r_lo
+                    : A.L + int64_t(slot0 + p) * A.R + r_lo;
+        if (kDown) sr.w[t] = w_tab[p];
       }
       sr.v[t] = *reinterpret_cast<const uint4*>(src + j0);
     }
@@ -141,7 +177,9 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_l[kLsBytes];
   __shared__ __attribute__((aligned(16))) unsigned char lds_r[kRsBytes];
   __shared__ int rowpre[kMaxRB + 1];
-  __shared__ int64_t rng[2];
+  __shared__ uint32_t rstart[kMaxRB];
+  __shared__ int tok_tab[kTokTab];
+  __shared__ float w_tab[kDown ? kTokTab : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int per_e = A.nrt * A.nct;
@@ -153,22 +191,15 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
   const int r_lo = rt * A.RB, r_hi = min(A.R, r_lo + A.RB), nr = r_hi - r_lo;
   const int c0 = ct * A.CB, c1 = min(A.C, c0 + A.CB), ncol = c1 - c0;
   const int64_t ebase = A.base + int64_t(e) * A.R * A.C;
+  (void)ebase;
 
-  // entries of this tile: per row r, the run of idx in [row r, c0) .. [row r, c1)
-  if (tid < 2) {
-    const int64_t key = tid == 0 ? ebase + int64_t(r_lo) * A.C + c0
-                                 : ebase + int64_t(r_hi - 1) * A.C + c1;
-    rng[tid] = lb_idx(A.idx, 0, A.nnz, key);
-  }
-  __syncthreads();
-  const int64_t g0 = rng[0], g1 = rng[1];
-  if (g0 >= g1) return;  // nothing selected in this tile (uniform)
-  // per-row counts -> exclusive prefix in rowpre[0..nr]
+  // entries of this tile: per row r, the plan segment (e, r, ct)
+  const int64_t q_r0 = A.qbase + (int64_t(e) * A.R + r_lo) * A.nct + ct;
   for (int r = tid; r < nr; r += 256) {
-    const int64_t rb = ebase + int64_t(r_lo + r) * A.C;
-    const int64_t s = lb_idx(A.idx, g0, g1, rb + c0);
-    const int64_t t = lb_idx(A.idx, s, g1, rb + c1);
-    rowpre[r + 1] = int(t - s);
+    const int64_t q = q_r0 + int64_t(r) * A.nct;
+    const uint32_t s0 = A.seg[q];
+    rstart[r] = s0;
+    rowpre[r + 1] = int(A.seg[q + 1] - s0);
   }
   if (tid == 0) rowpre[0] = 0;
   __syncthreads();
@@ -187,6 +218,7 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
   }
   __syncthreads();
   const int nent = rowpre[nr];
+  if (nent == 0) return;  // nothing selected in this tile (uniform)
 
   const int off = A.offsets[e];
   const int ne = A.offsets[e + 1] - off;
@@ -204,8 +236,7 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
         const int mid = (lo + hi + 1) >> 1;
         if (rowpre[mid] <= q) lo = mid; else hi = mid - 1;
       }
-      int r = lo, rcur = -1;
-      int64_t rb = 0, rowstart = 0;
+      int r = lo;
 #pragma unroll
       for (int i = 0; i < kMaxEnt; ++i) {
         acc[i] = 0.f;
@@ -213,27 +244,32 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
         const int qi = q + i;
         if (qi < nent) {
           while (rowpre[r + 1] <= qi) ++r;
-          if (r != rcur) {
-            rcur = r;
-            rb = ebase + int64_t(r_lo + r) * A.C;
-            rowstart = lb_idx(A.idx, g0, g1, rb + c0) - rowpre[r];
-          }
-          const int c = int(int64_t(A.idx[rowstart + qi]) - rb);
+          const int64_t rb = A.base + (int64_t(e) * A.R + r_lo + r) * A.C;
+          const int c = int(int64_t(A.idx[rstart[r] + (qi - rowpre[r])]) - rb);
           coord[i] = (uint32_t(r) << 16) | uint32_t(c - c0);
         }
       }
     }
-    // stream the expert's slots: chunk k+1 is fetched into registers while
-    // chunk k is consumed from LDS
+    // stream the expert's slots, a token-table window at a time; chunk k+1
+    // is fetched into registers while chunk k is consumed from LDS
     const bool stager = tid < nblk_r + nblk_l;  // <= 256 staging blocks: one per thread
-    StageRegs sr;
-    if (stager) stage_fetch<kDown>(A, tid, nblk_r, 0, ne, off, r_lo, c0, sr);
-    for (int p0 = 0; p0 < ne; p0 += kSlots) {
-      __syncthreads();  // previous chunk fully consumed
-      if (stager) stage_store<kDown>(tid, nblk_r, sr, lds_l, lds_r);
+    for (int w0 = 0; w0 < ne; w0 += kTokTab) {
+      const int wn = min(kTokTab, ne - w0);
+      __syncthreads();  // previous window fully consumed
+      for (int p = tid; p < wn; p += 256) {
+        const int sid = A.perm[off + w0 + p];
+        tok_tab[p] = sid / A.K;
+        if (kDown) w_tab[p] = A.topk_w[sid];
+      }
       __syncthreads();
-      if (stager && p0 + kSlots < ne)
-        stage_fetch<kDown>(A, tid, nblk_r, p0 + kSlots, ne, off, r_lo, c0, sr);
+      StageRegs sr;
+      if (stager) stage_fetch<kDown>(A, tid, nblk_r, 0, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr);
+      for (int p0 = 0; p0 < wn; p0 += kSlots) {
+        __syncthreads();  // previous chunk fully consumed
+        if (stager) stage_store<kDown>(tid, nblk_r, sr, lds_l, lds_r);
+        __syncthreads();
+        if (stager && p0 + kSlots < wn)
+          stage_fetch<kDown>(A, tid, nblk_r, p0 + kSlots, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr);
       uint32_t prow = 0xffffffffu;
       uint4 lb16 = make_uint4(0, 0, 0, 0);
       float lf[8];
@@ -274,26 +310,20 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
         }
         acc[i] = a;
       }
+      }
     }
     // write this thread's entries (contiguous positions in idx within a row run;
     // recompute positions row by row)
     {
       const int q = q0 + tid * kMaxEnt;
-      int r = -1;
-      int64_t rowstart = 0;
       int nbad = 0;
 #pragma unroll
       for (int i = 0; i < kMaxEnt; ++i) {
         const uint32_t cd = coord[i];
         if (cd == 0xffffffffu) continue;
         const int ri = int(cd >> 16);
-        if (ri != r) {
-          r = ri;
-          const int64_t rb = ebase + int64_t(r_lo + r) * A.C;
-          rowstart = lb_idx(A.idx, g0, g1, rb + c0) - rowpre[r];
-        }
         const float v = acc[i];
-        A.dW[rowstart + q + i] = v;
+        A.dW[int64_t(rstart[ri]) + (q + i - rowpre[ri])] = v;
         nbad += !finite_f(v);
       }
       if (A.nonfinite && nbad) atomicAdd(A.nonfinite, nbad);
@@ -301,37 +331,62 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
   }
 }
 
-// Tile sizes for one tensor of the masked gradient.
-static void masked_tiles(int R, int C, double density, int& RB, int& CB) {
-  const int nct = int(ceil_div(C, kMaxCB));
-  CB = int(ceil_div(ceil_div(C, nct), 8) * 8);  // balanced column tiles, multiple of 8
-  double target = 3000.0 / (double(CB) * (density > 0 ? density : 1e-9));
+// Column tiling of one tensor: balanced tiles of at most kMaxCB columns
+// (a multiple of 8); depends on the shape only.
+static void col_tiles(int C, int& CB, int& nct) {
+  nct = int(ceil_div(C, kMaxCB));
+  CB = int(ceil_div(ceil_div(C, nct), 8) * 8);
+  nct = int(ceil_div(C, CB));
+}
+
+int64_t masked_plan_segments(const usaf_moe_shape& s) {
+  int CB0, nct0, CB1, nct1;
+  col_tiles(s.H, CB0, nct0);
+  col_tiles(s.I, CB1, nct1);
+  return int64_t(s.E) * 2 * s.I * nct0 + int64_t(s.E) * s.H * nct1;
+}
+
+// Row tile: about 3000 selected entries per block at this density.
+static int row_tile(int R, int CB, double density) {
+  const double target = 3000.0 / (double(CB) * (density > 0 ? density : 1e-9));
   int rb = 32;
   while (rb * 2 <= kMaxRB && rb * 2 <= target) rb *= 2;
-  RB = rb < R ? rb : R;
-  if (RB > kMaxRB) RB = kMaxRB;
+  return rb < R ? rb : R;
 }
 
 usaf_status masked_dw_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64_t nnz,
                            const bf16_t* X, const bf16_t* dY, const bf16_t* dgu, const bf16_t* a,
                            const float* topk_w, const int32_t* offsets, const int32_t* perm,
-                           float* dW, int32_t* nonfinite, hipStream_t st) {
+                           float* dW, int32_t* nonfinite, uint32_t* seg, hipStream_t st) {
   if (nnz == 0) return USAF_OK;
   const double density = double(nnz) / double(n_weights(s));
+  SegLayout Lq;
+  Lq.E = s.E;
+  Lq.R0 = 2 * s.I; Lq.C0 = s.H;
+  Lq.R1 = s.H; Lq.C1 = s.I;
+  col_tiles(Lq.C0, Lq.CB0, Lq.nct0);
+  col_tiles(Lq.C1, Lq.CB1, Lq.nct1);
+  Lq.ngu = int64_t(s.E) * 2 * s.I * s.H;
+  Lq.q1 = int64_t(s.E) * Lq.R0 * Lq.nct0;
+  Lq.Q = Lq.q1 + int64_t(s.E) * Lq.R1 * Lq.nct1;
   timer_begin(USAF_K_MASKED_DW, st);
+  hipLaunchKernelGGL(masked_plan_kernel, dim3(unsigned(ceil_div(Lq.Q + 1, 256))), dim3(256), 0, st,
+                     idx, nnz, Lq, seg);
+  USAF_LAUNCH_CHECK();
   for (int tensor = 0; tensor < 2; ++tensor) {
     MaskedArgs A;
     A.idx = idx; A.nnz = nnz;
     A.offsets = offsets; A.perm = perm; A.topk_w = topk_w; A.K = s.K; A.E = s.E;
-    A.dW = dW; A.nonfinite = nonfinite;
+    A.dW = dW; A.nonfinite = nonfinite; A.seg = seg;
     if (tensor == 0) {
-      A.L = dgu; A.Rm = X; A.R = 2 * s.I; A.C = s.H; A.base = 0;
+      A.L = dgu; A.Rm = X; A.R = Lq.R0; A.C = Lq.C0; A.base = 0;
+      A.CB = Lq.CB0; A.nct = Lq.nct0; A.qbase = 0;
     } else {
-      A.L = dY; A.Rm = a; A.R = s.H; A.C = s.I; A.base = int64_t(s.E) * 2 * s.I * s.H;
+      A.L = dY; A.Rm = a; A.R = Lq.R1; A.C = Lq.C1; A.base = Lq.ngu;
+      A.CB = Lq.CB1; A.nct = Lq.nct1; A.qbase = Lq.q1;
     }
-    masked_tiles(A.R, A.C, density, A.RB, A.CB);
+    A.RB = row_tile(A.R, A.CB, density);
     A.nrt = int(ceil_div(A.R, A.RB));
-    A.nct = int(ceil_div(A.C, A.CB));
     const int64_t blocks = (int64_t(s.E) * A.nrt * A.nct + 7) / 8 * 8;
     if (tensor == 0)
       hipLaunchKernelGGL(masked_dw_sddmm_kernel<false>, dim3(unsigned(blocks)), dim3(256), 0, st, A);

@@ -686,7 +686,7 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
   if (idx) {
     if constexpr (kMfma) {
       return masked_dw_bf16(s, idx, nnz, X, dY, dgu, a, st.topk_w, st.offsets, st.perm, dW,
-                            nonfinite, stream);
+                            nonfinite, reinterpret_cast<uint32_t*>(ws + L.seg), stream);
     }
     if (nnz > 0) {
       timer_begin(USAF_K_MASKED_DW, stream);

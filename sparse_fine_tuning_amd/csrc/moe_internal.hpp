@@ -10,6 +10,8 @@
 
 namespace usaf {
 
+int64_t masked_plan_segments(const usaf_moe_shape& s);
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline int64_t n_weights(const usaf_moe_shape& s) {
@@ -44,9 +46,10 @@ inline WsForward ws_forward(const usaf_moe_shape& s) {
 }
 
 // Backward workspace: fp32 dX contributions [S, H], partial dw sums
-// [S, NT] (NT = dA column tiles), dlogits of the chosen experts [S].
+// [S, NT] (NT = dA column tiles), dlogits of the chosen experts [S], and
+// the masked-gradient plan (segment starts, u32).
 struct WsBackward {
-  size_t vbuf, dwpart, dl, total;
+  size_t vbuf, dwpart, dl, seg, total;
   int nt;
 };
 inline WsBackward ws_backward(const usaf_moe_shape& s) {
@@ -56,7 +59,8 @@ inline WsBackward ws_backward(const usaf_moe_shape& s) {
   L.vbuf = 0;
   L.dwpart = align256(S * s.H * 4);
   L.dl = L.dwpart + align256(S * L.nt * 4);
-  L.total = L.dl + align256(S * 4);
+  L.seg = L.dl + align256(S * 4);
+  L.total = L.seg + align256(size_t(masked_plan_segments(s) + 1) * 4);
   return L;
 }
 
@@ -85,7 +89,10 @@ usaf_status mfma_dense_dw(const usaf_moe_shape& s, const uint16_t* X, const uint
 usaf_status masked_dw_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64_t nnz,
                            const uint16_t* X, const uint16_t* dY, const uint16_t* dgu,
                            const uint16_t* a, const float* topk_w, const int32_t* offsets,
-                           const int32_t* perm, float* dW, int32_t* nonfinite, hipStream_t st);
+                           const int32_t* perm, float* dW, int32_t* nonfinite, uint32_t* seg,
+                           hipStream_t st);
+// Segments (expert, row, column tile) of the masked-gradient plan.
+int64_t masked_plan_segments(const usaf_moe_shape& s);
 
 // Workspace of one top-k selection over n keys / one RigL reselection.
 size_t topk_ws_bytes(int64_t n);
