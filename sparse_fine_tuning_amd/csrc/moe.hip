@@ -30,19 +30,37 @@ __device__ __forceinline__ uint32_t logit_key(float v) {
 
 // One wave per token: K rounds of a wave-wide max over (key, -expert id),
 // then softmax over the K chosen logits.  E <= 1024, K <= 64.
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
-                                                         int E, int K, int32_t* __restrict__ ids,
+// With nparts > 1 the logits arrive as split-K partial sums [nparts][T][E];
+// they are added in fixed part order and the sums written to `logits`.
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ parts,
+                                                         int nparts, float* __restrict__ logits,
+                                                         int T, int E, int K,
+                                                         int32_t* __restrict__ ids,
                                                          float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
   const float* lt = logits + int64_t(t) * E;
   uint64_t comp[16];
+  float val[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int e = lane + 64 * i;
-    comp[i] = (e < E) ? ((uint64_t(logit_key(lt[e])) << 32) | uint64_t(0xffffffffu - uint32_t(e)))
-                      : 0ull;
+    val[i] = 0.f;
+    if (e < E) {
+      float v;
+      if (nparts > 1) {
+        v = parts[int64_t(t) * E + e];
+        for (int q = 1; q < nparts; ++q) v += parts[(int64_t(q) * T + t) * E + e];
+        logits[int64_t(t) * E + e] = v;
+      } else {
+        v = lt[e];
+      }
+      val[i] = v;
+      comp[i] = (uint64_t(logit_key(v)) << 32) | uint64_t(0xffffffffu - uint32_t(e));
+    } else {
+      comp[i] = 0ull;
+    }
   }
   int my_id = 0;
   float my_l = 0.f;
@@ -56,12 +74,18 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
       best = o > best ? o : best;
     }
     const int e = int(0xffffffffu - uint32_t(best & 0xffffffffull));
+    // the owner lane (e % 64) retires the expert and broadcasts its logit
+    float le = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (lane + 64 * i == e) comp[i] = 0;
+      if (lane + 64 * i == e) {
+        comp[i] = 0;
+        le = val[i];
+      }
+    le = __shfl(le, e & 63, 64);
     if (lane == j) {
       my_id = e;
-      my_l = lt[e];
+      my_l = le;
     }
   }
   const float l0 = __shfl(my_l, 0, 64);
@@ -75,55 +99,52 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   }
 }
 
-// Stable grouping of slots by expert.  Block e counts the slots routed to
-// experts < e (its offset) and == e, then writes its slots in ascending slot
-// order with a block-wide ballot scan.
-__global__ __launch_bounds__(256) void expert_sort_kernel(const int32_t* __restrict__ ids, int S,
-                                                          int E, int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ perm,
-                                                          int32_t* __restrict__ slot_pos) {
-  __shared__ int red[2][4];
-  __shared__ int wtot[4];
+// Stable grouping of slots by expert.  Block e (1024 threads) counts the
+// slots routed to experts < e (its offset) and == e, each thread over a
+// contiguous run of slots; one block-wide scan of the per-thread matches then
+// places every thread's matches in ascending slot order.
+__global__ __launch_bounds__(1024) void expert_sort_kernel(const int32_t* __restrict__ ids, int S,
+                                                           int E, int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ perm,
+                                                           int32_t* __restrict__ slot_pos) {
+  __shared__ int red_lt[16];
+  __shared__ int wscan[16];
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int per = (S + 1023) / 1024;
+  const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
   int lt = 0, eq = 0;
-  for (int s = tid; s < S; s += 256) {
+  for (int s = s0; s < s1; ++s) {
     const int id = ids[s];
     lt += id < e;
     eq += id == e;
   }
+  int inc = eq;  // wave inclusive scan of the matches
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    lt += __shfl_xor(lt, off, 64);
-    eq += __shfl_xor(eq, off, 64);
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += v;
   }
-  if (lane == 0) {
-    red[0][wid] = lt;
-    red[1][wid] = eq;
-  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lt += __shfl_xor(lt, off, 64);
+  if (lane == 63) wscan[wid] = inc;
+  if (lane == 0) red_lt[wid] = lt;
   __syncthreads();
-  const int off_e = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  int off_e = 0, wbase = 0;
+  for (int w = 0; w < 16; ++w) {
+    off_e += red_lt[w];
+    if (w < wid) wbase += wscan[w];
+  }
   if (tid == 0) {
     offsets[e] = off_e;
     if (e == E - 1) offsets[E] = S;
   }
-  int run = off_e;
-  for (int base = 0; base < S; base += 256) {
-    const int s = base + tid;
-    const bool f = s < S && ids[s] == e;
-    const uint64_t b = __ballot(f);
-    const int pre = __popcll(b & ((1ull << lane) - 1ull));
-    if (lane == 0) wtot[wid] = __popcll(b);
-    __syncthreads();
-    int wbase = 0;
-    for (int w = 0; w < wid; ++w) wbase += wtot[w];
-    const int tot = wtot[0] + wtot[1] + wtot[2] + wtot[3];
-    if (f) {
-      const int p = run + wbase + pre;
+  int p = off_e + wbase + inc - eq;
+  for (int s = s0; s < s1; ++s) {
+    if (ids[s] == e) {
       perm[p] = s;
       slot_pos[s] = p;
+      ++p;
     }
-    run += tot;
-    __syncthreads();
   }
 }
 
@@ -400,49 +421,74 @@ struct DenseDwD {
 // Combines, router backward, masked dW, loss
 // ---------------------------------------------------------------------------
 
-// Y[t, :] = sum_{j=0..K-1} w[t, j] * y[slot t*K+j]   (fixed j order)
+template <class T>
+__device__ __forceinline__ void store4(T* p, int64_t i, float4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, int64_t i, float4 v) {
+  *reinterpret_cast<float4*>(p + i) = v;
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, int64_t i, float4 v) {
+  *reinterpret_cast<uint2*>(p + i) = make_uint2(uint32_t(f2bf(v.x)) | (uint32_t(f2bf(v.y)) << 16),
+                                                uint32_t(f2bf(v.z)) | (uint32_t(f2bf(v.w)) << 16));
+}
+
+// Y[t, :] = sum_{j=0..K-1} w[t, j] * y[slot t*K+j]   (fixed j order); four
+// columns per thread (H % 64 == 0).
 template <class T>
 __global__ __launch_bounds__(256) void combine_y_kernel(const float* __restrict__ ybuf,
                                                         const float* __restrict__ topk_w,
                                                         const int32_t* __restrict__ slot_pos, int H,
                                                         int K, T* __restrict__ Y) {
   const int t = blockIdx.x;
-  for (int h = threadIdx.x; h < H; h += blockDim.x) {
-    float acc = 0.f;
+  for (int h = 4 * threadIdx.x; h < H; h += 4 * blockDim.x) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < K; ++j) {
       const int s = t * K + j;
-      acc = fmaf(topk_w[s], ybuf[int64_t(slot_pos[s]) * H + h], acc);
+      const float wj = topk_w[s];
+      const float4 y = *reinterpret_cast<const float4*>(ybuf + int64_t(slot_pos[s]) * H + h);
+      acc.x = fmaf(wj, y.x, acc.x);
+      acc.y = fmaf(wj, y.y, acc.y);
+      acc.z = fmaf(wj, y.z, acc.z);
+      acc.w = fmaf(wj, y.w, acc.w);
     }
-    Act<T>::st(Y, int64_t(t) * H + h, acc);
+    store4<T>(Y, int64_t(t) * H + h, acc);
   }
 }
 
-// Per token: dw[s] = sum of the dA tiles' partial dot products (fixed
-// order), then dlogits of the chosen experts: w_j (dw_j - sum_m w_m dw_m).
+// Per slot: dw[s] = sum of the dA tiles' partial dot products (fixed order).
+// A block covers whole tokens (floor(256/K) of them); per token, dlogits of
+// the chosen experts: w_j (dw_j - sum_m w_m dw_m), the sum in fixed m order.
 __global__ __launch_bounds__(256) void dw_router_kernel(const float* __restrict__ dwpart, int NT,
                                                         const float* __restrict__ topk_w,
                                                         const int32_t* __restrict__ slot_pos,
                                                         int T, int K, float* __restrict__ dw,
                                                         float* __restrict__ dl) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
-  float sw = 0.f;
-  for (int j = 0; j < K; ++j) {
-    const int s = t * K + j;
+  __shared__ float swd[256];
+  const int tpb = 256 / K;
+  const int lt = threadIdx.x / K, j = threadIdx.x - lt * K;
+  const int t = blockIdx.x * tpb + lt;
+  const bool live = lt < tpb && t < T;
+  const int s = t * K + j;
+  float d = 0.f, wj = 0.f;
+  if (live) {
     const int64_t p = slot_pos[s];
-    float d = 0.f;
     for (int nt = 0; nt < NT; ++nt) d += dwpart[p * NT + nt];
     dw[s] = d;
-    sw = fmaf(topk_w[s], d, sw);
+    wj = topk_w[s];
   }
-  for (int j = 0; j < K; ++j) {
-    const int s = t * K + j;
-    dl[s] = topk_w[s] * (dw[s] - sw);
+  swd[threadIdx.x] = wj * d;
+  __syncthreads();
+  if (live) {
+    float sw = 0.f;
+    for (int m = 0; m < K; ++m) sw += swd[lt * K + m];
+    dl[s] = wj * (d - sw);
   }
 }
 
 // Dense fp32 router gradient dWr[e, h] = sum over slots p of e of
-// dlogits[s(p)] * X[t(p), h] (dlogits is zero off the chosen experts).
+// dlogits[s(p)] * X[t(p), h] (dlogits is zero off the chosen experts).  The
+// expert's slot tokens and dlogits are staged in LDS; two columns per thread.
 template <class T>
 __global__ __launch_bounds__(256) void dwr_kernel(const float* __restrict__ dl,
                                                   const T* __restrict__ X,
@@ -450,20 +496,54 @@ __global__ __launch_bounds__(256) void dwr_kernel(const float* __restrict__ dl,
                                                   const int32_t* __restrict__ perm, int H, int K,
                                                   float* __restrict__ dWr,
                                                   int32_t* __restrict__ nonfinite) {
+  __shared__ int tok[1024];
+  __shared__ float dls[1024];
   const int e = blockIdx.x;
-  const int h = blockIdx.y * blockDim.x + threadIdx.x;
-  if (h >= H) return;
+  const int h = 2 * (blockIdx.y * blockDim.x + threadIdx.x);
   const int p0 = offsets[e], p1 = offsets[e + 1];
-  float acc = 0.f;
-  for (int p = p0; p < p1; ++p) {
-    const int s = perm[p];
-    acc = fmaf(dl[s], Act<T>::ld(X, int64_t(s / K) * H + h), acc);
+  float a0 = 0.f, a1 = 0.f;
+  for (int w0 = p0; w0 < p1; w0 += 1024) {
+    const int wn = min(1024, p1 - w0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < wn; i += blockDim.x) {
+      const int s = perm[w0 + i];
+      tok[i] = s / K;
+      dls[i] = dl[s];
+    }
+    __syncthreads();
+    if (h < H) {
+      int i = 0;
+      for (; i + 4 <= wn; i += 4) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t base = int64_t(tok[i + u]) * H + h;
+          x[2 * u] = Act<T>::ld(X, base);
+          x[2 * u + 1] = Act<T>::ld(X, base + 1);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a0 = fmaf(dls[i + u], x[2 * u], a0);
+          a1 = fmaf(dls[i + u], x[2 * u + 1], a1);
+        }
+      }
+      for (; i < wn; ++i) {
+        const int64_t base = int64_t(tok[i]) * H + h;
+        a0 = fmaf(dls[i], Act<T>::ld(X, base), a0);
+        a1 = fmaf(dls[i], Act<T>::ld(X, base + 1), a1);
+      }
+    }
   }
-  dWr[int64_t(e) * H + h] = acc;
-  if (nonfinite && !finite_f(acc)) atomicAdd(nonfinite, 1);
+  if (h < H) {
+    dWr[int64_t(e) * H + h] = a0;
+    dWr[int64_t(e) * H + h + 1] = a1;
+    const int bad = !finite_f(a0) + !finite_f(a1);
+    if (nonfinite && bad) atomicAdd(nonfinite, bad);
+  }
 }
 
-// dX[t, :] = sum_j v[slot t*K+j] + sum_j dlogits[t, j] * Wr'[e_j, :]
+// dX[t, :] = sum_j v[slot t*K+j] + sum_j dlogits[t, j] * Wr'[e_j, :]; four
+// columns per thread.
 template <class T>
 __global__ __launch_bounds__(256) void combine_dx_kernel(const float* __restrict__ vbuf,
                                                          const float* __restrict__ dl,
@@ -472,14 +552,22 @@ __global__ __launch_bounds__(256) void combine_dx_kernel(const float* __restrict
                                                          const int32_t* __restrict__ slot_pos,
                                                          int H, int K, T* __restrict__ dX) {
   const int t = blockIdx.x;
-  for (int h = threadIdx.x; h < H; h += blockDim.x) {
-    float acc = 0.f;
-    for (int j = 0; j < K; ++j) acc += vbuf[int64_t(slot_pos[t * K + j]) * H + h];
+  for (int h = 4 * threadIdx.x; h < H; h += 4 * blockDim.x) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < K; ++j) {
+      const float4 v = *reinterpret_cast<const float4*>(vbuf + int64_t(slot_pos[t * K + j]) * H + h);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
     for (int j = 0; j < K; ++j) {
       const int s = t * K + j;
-      acc = fmaf(dl[s], router_w<T>(Wr, int64_t(ids[s]) * H + h), acc);
+      const float d = dl[s];
+      const int64_t wb = int64_t(ids[s]) * H + h;
+      acc.x = fmaf(d, router_w<T>(Wr, wb), acc.x);
+      acc.y = fmaf(d, router_w<T>(Wr, wb + 1), acc.y);
+      acc.z = fmaf(d, router_w<T>(Wr, wb + 2), acc.z);
+      acc.w = fmaf(d, router_w<T>(Wr, wb + 3), acc.w);
     }
-    Act<T>::st(dX, int64_t(t) * H + h, acc);
+    store4<T>(dX, int64_t(t) * H + h, acc);
   }
 }
 
@@ -585,16 +673,18 @@ static inline unsigned mtiles_bound(const usaf_moe_shape& s) {
   return unsigned(ceil_div(int64_t(s.T) * s.K, 64) + s.E);
 }
 
-template <class T>
-static usaf_status route_impl(const usaf_moe_shape& s, const float* logits,
+// Routing from logits: `parts` holds nparts split-K partial sums (summed
+// into st.logits) or, with nparts == 1, the logits themselves.
+static usaf_status route_impl(const usaf_moe_shape& s, const float* parts, int nparts,
                               const usaf_moe_state& st, hipStream_t stream) {
   const int S = s.T * s.K;
   timer_begin(USAF_K_ROUTE, stream);
   hipLaunchKernelGGL(route_topk_kernel, dim3(unsigned(ceil_div(s.T, 4))), dim3(256), 0, stream,
-                     logits, s.T, s.E, s.K, st.topk_ids, st.topk_w);
+                     parts, nparts, nparts > 1 ? st.logits : const_cast<float*>(parts), s.T, s.E,
+                     s.K, st.topk_ids, st.topk_w);
   USAF_LAUNCH_CHECK();
-  hipLaunchKernelGGL(expert_sort_kernel, dim3(unsigned(s.E)), dim3(256), 0, stream, st.topk_ids, S,
-                     s.E, st.offsets, st.perm, st.slot_pos);
+  hipLaunchKernelGGL(expert_sort_kernel, dim3(unsigned(s.E)), dim3(1024), 0, stream, st.topk_ids,
+                     S, s.E, st.offsets, st.perm, st.slot_pos);
   timer_end(USAF_K_ROUTE, stream);
   USAF_LAUNCH_CHECK();
   return USAF_OK;
@@ -608,15 +698,19 @@ static usaf_status forward_impl(const usaf_moe_shape& s, const T* X, const float
   const T* Wgu = W;
   const T* Wd = W + int64_t(s.E) * 2 * s.I * s.H;
   constexpr bool kMfma = std::is_same<T, bf16_t>::value;
-  // router logits
+  // router logits (bf16: split-K partial sums in the workspace, summed by
+  // the routing kernel in fixed order)
   if constexpr (kMfma) {
-    USAF_TRY(mfma_router(s, X, Wr, st.logits, stream));
+    float* parts = reinterpret_cast<float*>(ws + L.ybuf);
+    const int nparts = mfma_router_splits(s);
+    USAF_TRY(mfma_router(s, X, Wr, parts, nparts, stream));
+    USAF_TRY(route_impl(s, parts, nparts, st, stream));
   } else {
     RouterGemm<T> rg{X, Wr, st.logits, s.T, s.H, s.E};
     USAF_TRY(launch_fma(rg, dim3(unsigned(ceil_div(s.T, 64)), unsigned(ceil_div(s.E, 64))), stream,
                         USAF_K_ROUTER_GEMM));
+    USAF_TRY(route_impl(s, st.logits, 1, st, stream));
   }
-  USAF_TRY(route_impl<T>(s, st.logits, st, stream));
   // experts
   if constexpr (kMfma) {
     USAF_TRY(mfma_gate_up(s, X, Wgu, st.offsets, st.perm, static_cast<T*>(st.gu),
@@ -661,10 +755,10 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
     USAF_TRY(launch_fma(da, dim3(mtiles_bound(s), unsigned(NT)), stream, USAF_K_DA));
   }
   timer_begin(USAF_K_ROUTER_BWD, stream);
-  hipLaunchKernelGGL(dw_router_kernel, dim3(unsigned(ceil_div(s.T, 256))), dim3(256), 0, stream,
-                     dwpart, NT, st.topk_w, st.slot_pos, s.T, s.K, st.dw, dl);
+  hipLaunchKernelGGL(dw_router_kernel, dim3(unsigned(ceil_div(s.T, 256 / s.K))), dim3(256), 0,
+                     stream, dwpart, NT, st.topk_w, st.slot_pos, s.T, s.K, st.dw, dl);
   USAF_LAUNCH_CHECK();
-  hipLaunchKernelGGL(dwr_kernel<T>, dim3(unsigned(s.E), unsigned(ceil_div(s.H, 256))), dim3(256),
+  hipLaunchKernelGGL(dwr_kernel<T>, dim3(unsigned(s.E), unsigned(ceil_div(s.H, 512))), dim3(256),
                      0, stream, dl, X, st.offsets, st.perm, s.H, s.K, dWr,
                      idx ? nonfinite : nullptr);
   timer_end(USAF_K_ROUTER_BWD, stream);
@@ -797,5 +891,5 @@ extern "C" usaf_status usaf_route(const usaf_moe_shape* shape, const float* logi
   if (!logits || !state || !state->topk_ids || !state->topk_w || !state->offsets ||
       !state->perm || !state->slot_pos)
     return USAF_ERR_INVALID_ARG;
-  return route_impl<float>(*shape, logits, *state, stream);
+  return route_impl(*shape, logits, 1, *state, stream);
 }

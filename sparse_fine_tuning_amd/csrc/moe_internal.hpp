@@ -41,7 +41,9 @@ inline WsForward ws_forward(const usaf_moe_shape& s) {
   L.ybuf = 0;
   size_t mse = ((size_t(s.T) * s.H + 4095) / 4096) * 4 + 64;
   size_t y = S * s.H * 4;
-  L.total = align256(y > mse ? y : mse);
+  size_t parts = size_t(8) * s.T * s.E * 4;  // router split-K partials (consumed before y)
+  size_t m = y > mse ? y : mse;
+  L.total = align256(m > parts ? m : parts);
   return L;
 }
 
@@ -68,8 +70,15 @@ inline WsBackward ws_backward(const usaf_moe_shape& s) {
 
 namespace usaf {
 // bf16 MFMA GEMMs of the layer (moe_mfma.hip).
-usaf_status mfma_router(const usaf_moe_shape& s, const uint16_t* X, const float* Wr, float* logits,
-                        hipStream_t st);
+usaf_status mfma_router(const usaf_moe_shape& s, const uint16_t* X, const float* Wr, float* parts,
+                        int nparts, hipStream_t st);
+// Split-K factor of the router GEMM (partial sums [nparts][T][E]).
+inline int mfma_router_splits(const usaf_moe_shape& s) {
+  const int tiles = ((s.T + 127) / 128) * ((s.E + 127) / 128);
+  int ks = 1;
+  while (ks < 8 && tiles * ks < 256 && s.H / (64 * ks * 2) >= 1) ks *= 2;
+  return ks;
+}
 usaf_status mfma_gate_up(const usaf_moe_shape& s, const uint16_t* X, const uint16_t* Wgu,
                          const int32_t* offsets, const int32_t* perm, uint16_t* gu, uint16_t* a,
                          hipStream_t st);

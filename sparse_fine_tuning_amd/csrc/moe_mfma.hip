@@ -277,25 +277,29 @@ struct MDenseDw {
   }
 };
 
-// Router logits[T, E] = X bf16(Wr)^T.
+// Router logits[T, E] = X bf16(Wr)^T, split over K into KS partial sums
+// parts[ks][T][E] (k-range ks*Kc .. (ks+1)*Kc), summed later in fixed order.
 struct MRouter {
-  const bf16_t* X; const float* Wr; float* logits;
-  int T, H, E, MT, NT;
+  const bf16_t* X; const float* Wr; float* parts;
+  int T, H, E, MT, NT, KS, Kc;
   using ALoader = KcLoader<bf16_t>;
   using BLoader = KcLoader<float>;
   __device__ bool tile(int L, MTile& t) const {
-    if (L >= MT * NT) return false;
-    t.nt = L / MT;
-    t.m0 = (L - t.nt * MT) * kMB;
+    if (L >= MT * NT * KS) return false;
+    const int ks = L / (MT * NT);
+    const int rem = L - ks * MT * NT;
+    t.nt = rem / MT;
+    t.m0 = (rem - t.nt * MT) * kMB;
     t.n0 = t.nt * kNB;
     t.mc = min(kMB, T - t.m0);
     t.nc = min(kNB, E - t.n0);
-    t.kb = 0; t.ke = H; t.e = 0; t.off = 0;
+    t.kb = ks * Kc; t.ke = min(H, t.kb + Kc); t.e = ks; t.off = 0;
     return true;
   }
-  __device__ PlainRows a_src(const MTile& t) const { return PlainRows{X + int64_t(t.m0) * H, H, t.mc, H}; }
-  __device__ RouterRows b_src(const MTile& t) const { return RouterRows{Wr + int64_t(t.n0) * H, H, t.nc, H}; }
+  __device__ PlainRows a_src(const MTile& t) const { return PlainRows{X + int64_t(t.m0) * H, H, t.mc, t.ke}; }
+  __device__ RouterRows b_src(const MTile& t) const { return RouterRows{Wr + int64_t(t.n0) * H, H, t.nc, t.ke}; }
   __device__ void epilogue(const MTile& t, f32x16_t (&acc)[2][2], int wm, int wn, int lane) const {
+    float* logits = parts + int64_t(t.e) * T * E;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -330,11 +334,12 @@ static int64_t grouped_tiles_bound(const usaf_moe_shape& s, int NT) {
   return (ceil_div(int64_t(s.T) * s.K, kMB) + s.E) * NT;
 }
 
-usaf_status mfma_router(const usaf_moe_shape& s, const bf16_t* X, const float* Wr, float* logits,
-                        hipStream_t st) {
+usaf_status mfma_router(const usaf_moe_shape& s, const bf16_t* X, const float* Wr, float* parts,
+                        int nparts, hipStream_t st) {
   const int MT = int(ceil_div(s.T, kMB)), NT = int(ceil_div(s.E, kNB));
-  return launch_mfma(MRouter{X, Wr, logits, s.T, s.H, s.E, MT, NT}, int64_t(MT) * NT, st,
-                     USAF_K_ROUTER_GEMM);
+  const int Kc = int(ceil_div(ceil_div(s.H, nparts), kKB) * kKB);
+  return launch_mfma(MRouter{X, Wr, parts, s.T, s.H, s.E, MT, NT, nparts, Kc},
+                     int64_t(MT) * NT * nparts, st, USAF_K_ROUTER_GEMM);
 }
 
 usaf_status mfma_gate_up(const usaf_moe_shape& s, const bf16_t* X, const bf16_t* Wgu,
