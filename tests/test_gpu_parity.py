@@ -249,9 +249,12 @@ def test_topk_exact(capi, n, k, mode):
     assert np.array_equal(val.cpu().numpy(), g[ref])
 
 
-@pytest.mark.parametrize("act", [1, 0])
-def test_rigl_exact(capi, act):
-    say(f"rigl act={act}")
+@pytest.mark.parametrize("act,old_is_top", [(1, False), (0, False), (1, True)])
+def test_rigl_exact(capi, act, old_is_top):
+    """old_is_top: the old set holds the largest |g|, so fewer than r entries of
+    a fresh top-k are new and the grow set must come from the full selection
+    that excludes the old set."""
+    say(f"rigl act={act} old_is_top={old_is_top}")
     T, H, E, K, I = 16, 64, 4, 2, 32
     N = 3 * E * H * I
     k = 1000
@@ -260,6 +263,8 @@ def test_rigl_exact(capi, act):
     g = (rng.integers(-4, 5, N) * 0.125).astype(np.float32)
     w = (rng.integers(-6, 7, N) * 0.0078125).astype(np.float32)  # exact in bf16, many ties
     S_old = synth.random_mask(N, k, 3)
+    if old_is_top:
+        g[S_old] = np.float32(4.0) * np.sign(g[S_old] + 0.01)
     m = rng.standard_normal(k).astype(np.float32)
     v = rng.random(k).astype(np.float32)
     shape = capi.Shape(T, H, E, K, I, act)
@@ -282,6 +287,7 @@ def test_rigl_exact(capi, act):
     assert np.array_equal(new_v.cpu().numpy(), ref["v"].astype(np.float32))
     s = stats.cpu().numpy()
     assert s[0] == r and s[1] == r and s[2] == ref["topk_new_vs_old"]
+    assert (ref["topk_new_vs_old"] < r) == old_is_top
 
 
 # --------------------------------------------------------------------------
