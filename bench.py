@@ -191,6 +191,8 @@ def main():
     ap.add_argument("--no-scan", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not "
@@ -199,6 +201,17 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        # a plain copy of known size: scales rocprofv3's FETCH_SIZE / WRITE_SIZE
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": nbytes, "copies": 3}), flush=True)
+        return
 
     import usaf_synth as synth
     from sparse_fine_tuning_amd import capi

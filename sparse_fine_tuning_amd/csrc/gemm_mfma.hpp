@@ -106,31 +106,45 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 template <class E>
 struct KcLoader;
 
+// Loads are branch-free: rows past the tile and k past the end read a
+// clamped, valid address and are zeroed by a select, so the compiler can
+// count outstanding loads exactly (no exec-masked load blocks).
 template <>
 struct KcLoader<bf16_t> {
   const bf16_t* rp[4];
+  uint32_t ok;  // bit i: row i of this thread is inside the tile
   int c, kend;
   uint4 v[4];
   template <class Src>
   __device__ __forceinline__ void init(const Src& s, int tid) {
     c = tid & 7;
     kend = s.kend;
+    ok = 0;
+    const bf16_t* safe = s.row(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = (tid >> 3) + 32 * i;
-      rp[i] = r < s.rows ? s.row(r) : nullptr;
+      const bf16_t* p = r < s.rows ? s.row(r) : nullptr;
+      ok |= p ? (1u << i) : 0u;
+      rp[i] = p ? p : safe;
     }
   }
+  int klive;
   __device__ __forceinline__ void load(int k0) {
     const int k = k0 + 8 * c;
+    const int kk = min(k, kend - 8);
+    klive = k < kend;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      v[i] = (rp[i] && k < kend) ? *reinterpret_cast<const uint4*>(rp[i] + k) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const uint4*>(rp[i] + kk);
   }
   __device__ __forceinline__ void store(bf16_t* S, int tid) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(&S[((tid >> 3) + 32 * i) * kLdsRow + 8 * c]) = v[i];
+    for (int i = 0; i < 4; ++i) {
+      const bool live = ((ok >> i) & 1u) && klive;
+      const uint4 x = v[i];
+      const uint4 y = make_uint4(live ? x.x : 0u, live ? x.y : 0u, live ? x.z : 0u, live ? x.w : 0u);
+      *reinterpret_cast<uint4*>(&S[((tid >> 3) + 32 * i) * kLdsRow + 8 * c]) = y;
+    }
   }
 };
 
@@ -138,36 +152,44 @@ struct KcLoader<bf16_t> {
 template <>
 struct KcLoader<float> {
   const float* rp[4];
+  uint32_t ok;
   int c, kend;
-  uint4 v[4];
+  float4 x[4], y[4];
   template <class Src>
   __device__ __forceinline__ void init(const Src& s, int tid) {
     c = tid & 7;
     kend = s.kend;
+    ok = 0;
+    const float* safe = s.row(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = (tid >> 3) + 32 * i;
-      rp[i] = r < s.rows ? s.row(r) : nullptr;
+      const float* p = r < s.rows ? s.row(r) : nullptr;
+      ok |= p ? (1u << i) : 0u;
+      rp[i] = p ? p : safe;
     }
   }
+  int klive;
   __device__ __forceinline__ void load(int k0) {
     const int k = k0 + 8 * c;
+    const int kk = min(k, kend - 8);
+    klive = k < kend;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (rp[i] && k < kend) {
-        const float4 x = *reinterpret_cast<const float4*>(rp[i] + k);
-        const float4 y = *reinterpret_cast<const float4*>(rp[i] + k + 4);
-        v[i] = make_uint4(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w), pack_bf16x2(y.x, y.y),
-                          pack_bf16x2(y.z, y.w));
-      } else {
-        v[i] = make_uint4(0, 0, 0, 0);
-      }
+      x[i] = *reinterpret_cast<const float4*>(rp[i] + kk);
+      y[i] = *reinterpret_cast<const float4*>(rp[i] + kk + 4);
     }
   }
   __device__ __forceinline__ void store(bf16_t* S, int tid) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(&S[((tid >> 3) + 32 * i) * kLdsRow + 8 * c]) = v[i];
+    for (int i = 0; i < 4; ++i) {
+      const bool live = ((ok >> i) & 1u) && klive;
+      const uint4 v = make_uint4(live ? pack_bf16x2(x[i].x, x[i].y) : 0u,
+                                 live ? pack_bf16x2(x[i].z, x[i].w) : 0u,
+                                 live ? pack_bf16x2(y[i].x, y[i].y) : 0u,
+                                 live ? pack_bf16x2(y[i].z, y[i].w) : 0u);
+      *reinterpret_cast<uint4*>(&S[((tid >> 3) + 32 * i) * kLdsRow + 8 * c]) = v;
+    }
   }
 };
 
@@ -180,6 +202,7 @@ struct RcLoader {
   int mq, kq;
   bool live;
   uint2 v[8];
+  float sc[8];
   __device__ __forceinline__ void init(const Src& src, int tid) {
     s = src;
     mq = tid & 31;
@@ -187,31 +210,37 @@ struct RcLoader {
     live = 4 * mq < s.rows;
   }
   __device__ __forceinline__ void load(int k0) {
+    const int col = live ? 4 * mq : 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int k = k0 + 8 * kq + i;
-      if (live && k < s.kend) {
-        uint2 x = *reinterpret_cast<const uint2*>(s.kptr(k) + 4 * mq);
-        if constexpr (Src::kScaled) {
-          const float sc = s.scale(k);
-          x.x = pack_bf16x2(bf2f(bf16_t(x.x & 0xffffu)) * sc, bf2f(bf16_t(x.x >> 16)) * sc);
-          x.y = pack_bf16x2(bf2f(bf16_t(x.y & 0xffffu)) * sc, bf2f(bf16_t(x.y >> 16)) * sc);
-        }
-        v[i] = x;
-      } else {
-        v[i] = make_uint2(0, 0);
-      }
+      const int k = min(k0 + 8 * kq + i, s.kend - 1);
+      v[i] = *reinterpret_cast<const uint2*>(s.kptr(k) + col);
+      if constexpr (Src::kScaled) sc[i] = s.scale(k);
     }
+    kbase = k0 + 8 * kq;
   }
+  int kbase;
   __device__ __forceinline__ void store(bf16_t* S, int) const {
-    // element j of k-row i: 16-bit half (j&1) of word (j>>1) of v[i]
+    // k-row i is live when inside [.., kend) and the thread's rows are live
+    uint2 u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint2 x = v[i];
+      if constexpr (Src::kScaled) {
+        x.x = pack_bf16x2(bf2f(bf16_t(x.x & 0xffffu)) * sc[i], bf2f(bf16_t(x.x >> 16)) * sc[i]);
+        x.y = pack_bf16x2(bf2f(bf16_t(x.y & 0xffffu)) * sc[i], bf2f(bf16_t(x.y >> 16)) * sc[i]);
+      }
+      const bool ok = live && kbase + i < s.kend;
+      u[i] = make_uint2(ok ? x.x : 0u, ok ? x.y : 0u);
+    }
+    // element j of k-row i: 16-bit half (j&1) of word (j>>1) of u[i]
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t w[4];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const uint32_t a = (j < 2) ? v[2 * d].x : v[2 * d].y;
-        const uint32_t b = (j < 2) ? v[2 * d + 1].x : v[2 * d + 1].y;
+        const uint32_t a = (j < 2) ? u[2 * d].x : u[2 * d].y;
+        const uint32_t b = (j < 2) ? u[2 * d + 1].x : u[2 * d + 1].y;
         w[d] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
       }
       *reinterpret_cast<uint4*>(&S[(4 * mq + j) * kLdsRow + 8 * kq]) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -234,10 +263,13 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(P p) {
   if (!p.tile(xcd_remap_blocks(blockIdx.x, gridDim.x), t)) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
-  typename P::ALoader la;
-  typename P::BLoader lb;
-  la.init(p.a_src(t), tid);
-  lb.init(p.b_src(t), tid);
+  // two register stages: k-tile kt+2 is in flight while kt is multiplied
+  typename P::ALoader la0, la1;
+  typename P::BLoader lb0, lb1;
+  la0.init(p.a_src(t), tid);
+  lb0.init(p.b_src(t), tid);
+  la1 = la0;
+  lb1 = lb0;
   f32x16_t acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -247,21 +279,22 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(P p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = (t.ke - t.kb + kKB - 1) / kKB;
   if (nk > 0) {
-    la.load(t.kb);
-    lb.load(t.kb);
-    la.store(As[0], tid);
-    lb.store(Bs[0], tid);
+    la0.load(t.kb);
+    lb0.load(t.kb);
+    if (nk > 1) {
+      la1.load(t.kb + kKB);
+      lb1.load(t.kb + kKB);
+    }
+    la0.store(As[0], tid);
+    lb0.store(Bs[0], tid);
+    if (nk > 2) {
+      la0.load(t.kb + 2 * kKB);
+      lb0.load(t.kb + 2 * kKB);
+    }
   }
   __syncthreads();
   const int lrow = lane & 31, lk = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      la.load(t.kb + (kt + 1) * kKB);
-      lb.load(t.kb + (kt + 1) * kKB);
-    }
-    const bf16_t* Ab = As[cur];
-    const bf16_t* Bb = Bs[cur];
+  auto mma = [&](const bf16_t* Ab, const bf16_t* Bb) {
 #pragma unroll
     for (int kc = 0; kc < kKB / 16; ++kc) {
       bf16x8_t af[2], bfr[2];
@@ -277,12 +310,30 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(P p) {
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) {
-      la.store(As[cur ^ 1], tid);
-      lb.store(Bs[cur ^ 1], tid);
+  };
+  // iterations in pairs so each register stage has a fixed name
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    mma(As[0], Bs[0]);
+    la1.store(As[1], tid);  // stage kt+1
+    lb1.store(Bs[1], tid);
+    if (kt + 3 < nk) {
+      la1.load(t.kb + (kt + 3) * kKB);
+      lb1.load(t.kb + (kt + 3) * kKB);
+    }
+    __syncthreads();
+    mma(As[1], Bs[1]);
+    if (kt + 2 < nk) {
+      la0.store(As[0], tid);  // stage kt+2
+      lb0.store(Bs[0], tid);
+      if (kt + 4 < nk) {
+        la0.load(t.kb + (kt + 4) * kKB);
+        lb0.load(t.kb + (kt + 4) * kKB);
+      }
     }
     __syncthreads();
   }
+  if (kt < nk) mma(As[0], Bs[0]);  // odd count: last tile sits in buffer 0
   p.epilogue(t, acc, wm, wn, lane);
 }
 
