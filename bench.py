@@ -31,6 +31,50 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 FP32_VEC_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, TFLOP/s
 
+# HBM traffic per launch from rocprofv3 counter runs (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch, median over the step's launches) at the
+# default workload, with the sources the kernel is built from at that time.
+# Counters are scaled by what they read for a plain 1 GiB device copy.  A
+# figure whose sources have changed since is reported as null.
+FETCH_SCALE = 2.0   # a 1 GiB copy reads 524,300 KiB of FETCH_SIZE
+WRITE_SCALE = 1.0   # and 1,048,576 KiB of WRITE_SIZE
+# kernel class -> (fetch KiB, write KiB, sources hash); masked_dw and adam sum
+# the launches of one step (plan + two SDDMM launches; expert + router Adam)
+COUNTER_TRAFFIC = {
+    "router_gemm": (8846, 16384, "c0729b3485a0e65d"),
+    "gate_up": (497397, 147458, "c0729b3485a0e65d"),
+    "down": (226652, 262144, "c0729b3485a0e65d"),
+    "da": (374458, 100618, "c0729b3485a0e65d"),
+    "dx": (477064, 262144, "c0729b3485a0e65d"),
+    "masked_dw": (110258 + 71967 + 7317, 7870 + 3932 + 2560, "a607433f3e1ce9ed"),
+    "adam": (185598 + 2060, 114540 + 3072, "26f53ce5cbbb540f"),
+}
+KERNEL_SOURCES = {
+    c: ("gemm_mfma.hpp", "moe_mfma.hip", "common.hpp", "moe_internal.hpp")
+    for c in ("router_gemm", "gate_up", "down", "da", "dx", "dense_dw")
+}
+KERNEL_SOURCES.update(masked_dw=("masked_dw.hip", "common.hpp", "moe_internal.hpp"),
+                      adam=("optim.hip", "common.hpp"))
+
+
+def sources_sha(kclass):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kclass, ()):
+        with open(os.path.join(ROOT, "sparse_fine_tuning_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kclass):
+    """Scaled HBM bytes per launch, or None when unmeasured or stale."""
+    if kclass not in COUNTER_TRAFFIC or kclass not in KERNEL_SOURCES:
+        return None
+    fetch_kib, write_kib, sha = COUNTER_TRAFFIC[kclass]
+    if sha != sources_sha(kclass):
+        return None
+    return (fetch_kib * FETCH_SCALE + write_kib * WRITE_SCALE) * 1024.0
+
 
 def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
@@ -51,7 +95,7 @@ def algorithmic_work(shape, k):
         "da": (2.0 * S * H * I, W_d + X + gu + a + gu),
         "dx": (2.0 * S * 2 * I * H, W_gu + gu + X),
         "masked_dw": (2.0 * k * S / E, 2 * X + gu + a + 8 * k),
-        "adam": (0.0, 28 * k),
+        "adam": (0.0, 28 * k + 28 * E * H),
         "router_gemm": (2.0 * T * H * E, X + E * H * 4 + T * E * 4),
     }
 
@@ -76,8 +120,9 @@ def make_layer(lay_cls, dims, d, idx, act):
 
 
 def time_kernel_classes(capi, lay, classes, lr):
-    """Average launch time (ms) of each kernel class over one step, events
-    recorded on the launch stream by the library's timing hook."""
+    """Time (ms) of each kernel class in one step (summed over its launches
+    in the step), events recorded on the launch stream by the library's
+    timing hook."""
     import torch
     out = {}
     for c in classes:
@@ -85,7 +130,7 @@ def time_kernel_classes(capi, lay, classes, lr):
         lay.train_step(lr=lr, check_skip=False)
         torch.cuda.synchronize()
         ms = capi.timer_read(8)
-        out[capi.KERNEL_CLASS_NAMES[c]] = sum(ms) / len(ms) if ms else 0.0
+        out[capi.KERNEL_CLASS_NAMES[c]] = sum(ms)
     capi.timer_arm(-1)
     return out
 
@@ -190,6 +235,10 @@ def main():
     ap.add_argument("--scan-tokens", type=int, default=8192)
     ap.add_argument("--no-scan", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--scan-only", action="store_true",
+                    help="skip the timed train steps; run only the RigL scan (profiling)")
+    ap.add_argument("--print-sha", action="store_true",
+                    help="print the source hash of each counter-measured kernel class and exit")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
@@ -198,6 +247,10 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not "
               f"sharded across GPUs in this build.", file=sys.stderr)
         sys.exit(2)
+
+    if args.print_sha:
+        print(json.dumps({c: sources_sha(c) for c in KERNEL_SOURCES}))
+        return
 
     import numpy as np
     import torch
@@ -225,6 +278,11 @@ def main():
     log("generating the seeded Qwen3-shaped layer")
     d = synth.moe_layer(*dims, bf16=True, seeds=(0, 1, 2, 3, 4))
     idx = synth.random_mask(N, k, 5)
+    if args.scan_only:
+        log("rigl scan only")
+        print(json.dumps({"rigl": rigl_scan(capi, synth, layer_mod, d, idx, dims,
+                                            args.scan_tokens)}), flush=True)
+        return
     lay = make_layer(layer_mod.SparseMoELayer, dims, d, idx, capi.BF16)
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -237,7 +295,7 @@ def main():
     work = algorithmic_work(dims, k)
     dominant = max((c for c in per_class if c in work), key=lambda c: per_class[c])
     dom_class = capi.KERNEL_CLASS_NAMES.index(dominant)
-    launches_per_step = 2 if dominant == "adam" else 1
+    launches_per_step = {"adam": 2, "masked_dw": 1}.get(dominant, 1)
     log(f"per-class ms {json.dumps({c: round(v, 4) for c, v in per_class.items()})}; dominant {dominant}")
 
     capi.timer_arm(dom_class, args.steps * launches_per_step)
@@ -253,13 +311,16 @@ def main():
     nonfinite = int(lay.nonfinite.item())
     ms_step = (t1 - t0) * 1e3 / args.steps
     value = T / (ms_step * 1e-3)
-    kern_ms = sum(kms) / len(kms)
+    kern_ms = sum(kms) / args.steps  # per step: one launch for every GEMM class
     fl, by = work[dominant]
     roof = roofline_entry(dominant, fl, by, kern_ms)
     roof.update(kernel_ms=kern_ms, launches=len(kms), algorithmic_flops=fl,
-                algorithmic_bytes=by, traffic=None)
+                algorithmic_bytes=by, traffic=counter_traffic(dominant),
+                traffic_note="rocprofv3 FETCH_SIZE x%.1f + WRITE_SIZE x%.1f per launch"
+                             % (FETCH_SCALE, WRITE_SCALE))
     log(f"step {ms_step:.3f} ms -> {value:.0f} tokens/s; {dominant} {kern_ms:.3f} ms")
-    step_kernels = {c: dict(ms=per_class[c], **roofline_entry(c, *work[c], per_class[c]))
+    step_kernels = {c: dict(ms=per_class[c], traffic=counter_traffic(c),
+                            **roofline_entry(c, *work[c], per_class[c]))
                     for c in per_class if c in work and per_class[c] > 0}
     del lay
     torch.cuda.empty_cache()
