@@ -50,7 +50,7 @@ COUNTER_TRAFFIC = {
     "adam": (185598 + 2060, 114540 + 3072, "26f53ce5cbbb540f"),
 }
 KERNEL_SOURCES = {
-    c: ("gemm_mfma.hpp", "moe_mfma.hip", "common.hpp", "moe_internal.hpp")
+    c: ("gemm_mfma.hpp", "gemm_v2.hpp", "moe_mfma.hip", "common.hpp", "moe_internal.hpp")
     for c in ("router_gemm", "gate_up", "down", "da", "dx", "dense_dw")
 }
 KERNEL_SOURCES.update(masked_dw=("masked_dw.hip", "common.hpp", "moe_internal.hpp"),

@@ -792,7 +792,8 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
     }
   } else {
     if constexpr (kMfma) {
-      return mfma_dense_dw(s, X, dY, dgu, a, st.offsets, st.perm, st.topk_w, dW, stream);
+      return mfma_dense_dw(s, X, dY, dgu, a, st.offsets, st.perm, st.topk_w,
+                           reinterpret_cast<bf16_t*>(vbuf), dW, stream);
     }
     DenseDwGu<T> g1{dgu, X, st.offsets, st.perm, dW, s.H, s.E, s.K, s.I};
     USAF_TRY(launch_fma(g1, dim3(unsigned(s.H / 64), unsigned(2 * s.I / 64), unsigned(s.E)), stream, USAF_K_DENSE_DW));

@@ -91,9 +91,12 @@ usaf_status mfma_da(const usaf_moe_shape& s, const uint16_t* dY, const uint16_t*
                     hipStream_t st);
 usaf_status mfma_dx(const usaf_moe_shape& s, const uint16_t* dgu, const uint16_t* Wgu,
                     const int32_t* offsets, float* vbuf, hipStream_t st);
+// stage: S*H*2 bf16 scratch (the backward workspace's vbuf) for the
+// expert-major gathered X and w*dY operands.
 usaf_status mfma_dense_dw(const usaf_moe_shape& s, const uint16_t* X, const uint16_t* dY,
                           const uint16_t* dgu, const uint16_t* a, const int32_t* offsets,
-                          const int32_t* perm, const float* topk_w, float* dW, hipStream_t st);
+                          const int32_t* perm, const float* topk_w, uint16_t* stage, float* dW,
+                          hipStream_t st);
 
 usaf_status masked_dw_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64_t nnz,
                            const uint16_t* X, const uint16_t* dY, const uint16_t* dgu,

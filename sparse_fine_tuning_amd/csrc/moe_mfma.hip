@@ -7,6 +7,7 @@
 // the importance / RigL scan.
 #include "common.hpp"
 #include "gemm_mfma.hpp"
+#include "gemm_v2.hpp"
 #include "moe_internal.hpp"
 #include "timing.hpp"
 
@@ -316,6 +317,319 @@ struct MRouter {
 };
 
 // ---------------------------------------------------------------------------
+// Problems on the direct-to-LDS kernel (gemm_v2.hpp).  Row sources clamp to a
+// valid row so every copy reads mapped memory; the epilogues store only rows
+// and columns inside the tile.
+// ---------------------------------------------------------------------------
+namespace g2 {
+
+// k-major rows gathered by token: row r -> act[tok(perm[base + min(r, n-1)])]
+struct TokRowsC {
+  const bf16_t* act; const int32_t* perm; int K; int base; int n; int64_t ld;
+  __device__ __forceinline__ const bf16_t* row(int r) const {
+    return act + int64_t(perm[base + min(r, n - 1)] / K) * ld;
+  }
+};
+// k-major plain rows: row r -> base + min(r, n-1) * ld
+struct PlainRowsC {
+  const bf16_t* base; int64_t ld; int n;
+  __device__ __forceinline__ const bf16_t* row(int r) const { return base + int64_t(min(r, n - 1)) * ld; }
+};
+// mn-major: element (col, k) at base + k*ld + col, ncols valid columns
+struct StridedKC {
+  const bf16_t* base; int64_t ld; int ncols;
+  __device__ __forceinline__ const bf16_t* kptr(int k) const { return base + int64_t(k) * ld; }
+};
+// gate_up weight rows for a tile of BN columns holding BN/2 features: wave
+// column-half wn holds features F0 + (BN/4) wn + [0, BN/4); its 32-column
+// blocks alternate gate, up, gate, up over consecutive 32-feature groups.
+template <int BN>
+struct GateUpRowsC {
+  const bf16_t* We; int F0; int I; int64_t H;
+  __device__ __forceinline__ const bf16_t* row(int c) const {
+    const int wn = c / (BN / 2), j = (c % (BN / 2)) >> 5;
+    const int f = min(F0 + (BN / 4) * wn + 32 * (j >> 1) + (c & 31), I - 1);
+    return We + int64_t((j & 1) ? I + f : f) * H;
+  }
+};
+
+template <int BN_, int NS_>
+struct MGateUp {
+  static constexpr int BN = BN_, NS = NS_, NJ = BN_ / 64;
+  using AOp = KMajor<kBM>;
+  using BOp = KMajor<BN>;
+  const bf16_t* X; const bf16_t* Wgu; const int32_t* offsets; const int32_t* perm;
+  bf16_t* gu; bf16_t* a;
+  int H, E, K, I, NT;
+  __device__ __forceinline__ bool tile(int L, MTile& t) const {
+    if (!grouped_m_tile(offsets, E, NT, L, t)) return false;
+    t.kb = 0; t.ke = H; t.n0 = t.nt * (BN / 2); t.nc = 0;
+    return true;
+  }
+  __device__ __forceinline__ TokRowsC a_src(const MTile& t) const { return TokRowsC{X, perm, K, t.off + t.m0, t.mc, H}; }
+  __device__ __forceinline__ GateUpRowsC<BN> b_src(const MTile& t) const {
+    return GateUpRowsC<BN>{Wgu + int64_t(t.e) * 2 * I * H, t.n0, I, H};
+  }
+  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[2][NJ], int wm, int wn, int lane) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = out_row(wm, i, lane);
+      if (row >= t.mc) continue;
+      const int64_t p = t.off + t.m0 + row;
+#pragma unroll
+      for (int jp = 0; jp < NJ / 2; ++jp)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int f = t.n0 + (BN / 4) * wn + 32 * jp + 8 * g + 4 * (lane >> 5);
+          if (f >= I) continue;
+          uint32_t gw[2], uw[2], aw[2];
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const float g0 = bf2f(f2bf(acc[i][2 * jp][4 * g + e]));
+            const float g1 = bf2f(f2bf(acc[i][2 * jp][4 * g + e + 1]));
+            const float u0 = bf2f(f2bf(acc[i][2 * jp + 1][4 * g + e]));
+            const float u1 = bf2f(f2bf(acc[i][2 * jp + 1][4 * g + e + 1]));
+            gw[e / 2] = pack_bf16x2(g0, g1);
+            uw[e / 2] = pack_bf16x2(u0, u1);
+            aw[e / 2] = pack_bf16x2(silu_f(g0) * u0, silu_f(g1) * u1);
+          }
+          *reinterpret_cast<uint2*>(gu + p * 2 * I + f) = make_uint2(gw[0], gw[1]);
+          *reinterpret_cast<uint2*>(gu + p * 2 * I + I + f) = make_uint2(uw[0], uw[1]);
+          *reinterpret_cast<uint2*>(a + p * I + f) = make_uint2(aw[0], aw[1]);
+        }
+    }
+  }
+};
+
+template <int BN_, int NS_>
+struct MDown {
+  static constexpr int BN = BN_, NS = NS_, NJ = BN_ / 64;
+  using AOp = KMajor<kBM>;
+  using BOp = KMajor<BN>;
+  const bf16_t* a; const bf16_t* Wd; const int32_t* offsets; float* ybuf;
+  int H, E, I, NT;
+  __device__ __forceinline__ bool tile(int L, MTile& t) const {
+    if (!grouped_m_tile(offsets, E, NT, L, t)) return false;
+    t.kb = 0; t.ke = I; t.n0 = t.nt * BN; t.nc = min(BN, H - t.n0);
+    return true;
+  }
+  __device__ __forceinline__ PlainRowsC a_src(const MTile& t) const {
+    return PlainRowsC{a + int64_t(t.off + t.m0) * I, I, t.mc};
+  }
+  __device__ __forceinline__ PlainRowsC b_src(const MTile& t) const {
+    return PlainRowsC{Wd + (int64_t(t.e) * H + t.n0) * I, I, t.nc};
+  }
+  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[2][NJ], int wm, int wn, int lane) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = out_row(wm, i, lane);
+      if (row >= t.mc) continue;
+      float* yr = ybuf + int64_t(t.off + t.m0 + row) * H + t.n0;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = out_col(BN, wn, j, g, lane);
+          if (col < t.nc)
+            *reinterpret_cast<float4*>(yr + col) =
+                make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        }
+    }
+  }
+};
+
+template <int BN_, int NS_>
+struct MDa {
+  static constexpr int BN = BN_, NS = NS_, NJ = BN_ / 64;
+  using AOp = KMajor<kBM>;
+  using BOp = MNMajor<BN>;
+  const bf16_t* dY; const bf16_t* Wd; const int32_t* offsets; const int32_t* perm;
+  const float* topk_w; const bf16_t* gu; const bf16_t* a; bf16_t* dgu; float* dwpart;
+  int H, E, K, I, NT, NTP;
+  __device__ __forceinline__ bool tile(int L, MTile& t) const {
+    if (!grouped_m_tile(offsets, E, NT, L, t)) return false;
+    t.kb = 0; t.ke = H; t.n0 = t.nt * BN; t.nc = min(BN, I - t.n0);
+    return true;
+  }
+  __device__ __forceinline__ TokRowsC a_src(const MTile& t) const { return TokRowsC{dY, perm, K, t.off + t.m0, t.mc, H}; }
+  __device__ __forceinline__ StridedKC b_src(const MTile& t) const {
+    return StridedKC{Wd + int64_t(t.e) * H * I + t.n0, I, t.nc};
+  }
+  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[2][NJ], int wm, int wn, int lane) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = out_row(wm, i, lane);
+      const bool vrow = row < t.mc;
+      const int64_t p = t.off + t.m0 + (vrow ? row : 0);
+      const float wt = topk_w[perm[p]];
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = out_col(BN, wn, j, g, lane);
+          if (!vrow || col >= t.nc) continue;
+          const int f = t.n0 + col;
+          const uint2 av = *reinterpret_cast<const uint2*>(a + p * I + f);
+          const uint2 gv = *reinterpret_cast<const uint2*>(gu + p * 2 * I + f);
+          const uint2 uv = *reinterpret_cast<const uint2*>(gu + p * 2 * I + I + f);
+          const uint32_t aw[2] = {av.x, av.y}, gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y};
+          uint32_t dg[2], du[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float dgs[2], dus[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const float U = acc[i][j][4 * g + 2 * h + q];
+              const float av1 = q ? bf2f(bf16_t(aw[h] >> 16)) : bf2f(bf16_t(aw[h] & 0xffffu));
+              const float g1 = q ? bf2f(bf16_t(gw[h] >> 16)) : bf2f(bf16_t(gw[h] & 0xffffu));
+              const float u1 = q ? bf2f(bf16_t(uw[h] >> 16)) : bf2f(bf16_t(uw[h] & 0xffffu));
+              part = fmaf(U, av1, part);
+              const float da = wt * U;
+              const float sg = sigmoid_f(g1);
+              dgs[q] = da * u1 * sg * (1.f + g1 * (1.f - sg));
+              dus[q] = da * g1 * sg;
+            }
+            dg[h] = pack_bf16x2(dgs[0], dgs[1]);
+            du[h] = pack_bf16x2(dus[0], dus[1]);
+          }
+          *reinterpret_cast<uint2*>(dgu + p * 2 * I + f) = make_uint2(dg[0], dg[1]);
+          *reinterpret_cast<uint2*>(dgu + p * 2 * I + I + f) = make_uint2(du[0], du[1]);
+        }
+      // lanes l and l + 32 hold the same row
+      part += __shfl_xor(part, 32, 64);
+      if (lane < 32 && vrow) dwpart[p * NTP + 2 * t.nt + wn] = part;
+    }
+  }
+};
+
+template <int BN_, int NS_>
+struct MDx {
+  static constexpr int BN = BN_, NS = NS_, NJ = BN_ / 64;
+  using AOp = KMajor<kBM>;
+  using BOp = MNMajor<BN>;
+  const bf16_t* dgu; const bf16_t* Wgu; const int32_t* offsets; float* vbuf;
+  int H, E, I, NT;
+  __device__ __forceinline__ bool tile(int L, MTile& t) const {
+    if (!grouped_m_tile(offsets, E, NT, L, t)) return false;
+    t.kb = 0; t.ke = 2 * I; t.n0 = t.nt * BN; t.nc = min(BN, H - t.n0);
+    return true;
+  }
+  __device__ __forceinline__ PlainRowsC a_src(const MTile& t) const {
+    return PlainRowsC{dgu + int64_t(t.off + t.m0) * 2 * I, 2 * I, t.mc};
+  }
+  __device__ __forceinline__ StridedKC b_src(const MTile& t) const {
+    return StridedKC{Wgu + int64_t(t.e) * 2 * I * H + t.n0, H, t.nc};
+  }
+  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[2][NJ], int wm, int wn, int lane) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = out_row(wm, i, lane);
+      if (row >= t.mc) continue;
+      float* vr = vbuf + int64_t(t.off + t.m0 + row) * H + t.n0;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = out_col(BN, wn, j, g, lane);
+          if (col < t.nc)
+            *reinterpret_cast<float4*>(vr + col) =
+                make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        }
+    }
+  }
+};
+
+// Dense weight gradients of one expert, contraction over its slots p, with
+// both operands expert-major slot rows (mn-major):
+//   gate_up: dW[r, c] = sum_p dGU[p, r] Xg[p, c]    (rows 2I, cols H)
+//   down:    dW[r, c] = sum_p wdYg[p, r] a[p, c]    (rows H,  cols I)
+// Xg = X gathered by token and wdYg = bf16(w_p dY[tok(p)]) are staged first.
+template <bool kDown, int BN_, int NS_>
+struct MDenseDw {
+  static constexpr int BN = BN_, NS = NS_, NJ = BN_ / 64;
+  using AOp = MNMajor<kBM>;
+  using BOp = MNMajor<BN>;
+  const bf16_t* L; const bf16_t* R; const int32_t* offsets; float* dW;
+  int H, E, I, MT, NT;
+  int64_t ngu;
+  __device__ __forceinline__ int rows_total() const { return kDown ? H : 2 * I; }
+  __device__ __forceinline__ int cols_total() const { return kDown ? I : H; }
+  __device__ __forceinline__ bool tile(int Lt, MTile& t) const {
+    const int per = MT * NT;
+    t.e = Lt / per;
+    if (t.e >= E) return false;
+    const int rem = Lt - t.e * per;
+    t.nt = rem / MT;
+    t.m0 = (rem - t.nt * MT) * kBM;
+    t.n0 = t.nt * BN;
+    t.mc = min(kBM, rows_total() - t.m0);
+    t.nc = min(BN, cols_total() - t.n0);
+    t.off = offsets[t.e];
+    t.kb = 0;
+    t.ke = offsets[t.e + 1] - t.off;
+    return true;
+  }
+  __device__ __forceinline__ StridedKC a_src(const MTile& t) const {
+    const int ld = rows_total();
+    return StridedKC{L + int64_t(t.off) * ld + t.m0, ld, t.mc};
+  }
+  __device__ __forceinline__ StridedKC b_src(const MTile& t) const {
+    const int ld = cols_total();
+    return StridedKC{R + int64_t(t.off) * ld + t.n0, ld, t.nc};
+  }
+  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[2][NJ], int wm, int wn, int lane) const {
+    const int64_t base = kDown ? ngu + int64_t(t.e) * H * I : int64_t(t.e) * 2 * I * H;
+    const int ldo = cols_total();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = out_row(wm, i, lane);
+      if (row >= t.mc) continue;
+      float* dr = dW + base + int64_t(t.m0 + row) * ldo + t.n0;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = out_col(BN, wn, j, g, lane);
+          if (col < t.nc)
+            *reinterpret_cast<float4*>(dr + col) =
+                make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        }
+    }
+  }
+};
+
+// Expert-major operands of the dense gradient: Xg[p] = X[tok(p)],
+// wdYg[p] = bf16(w_p dY[tok(p)]); 8 elements per thread.
+__global__ __launch_bounds__(256) void stage_dense_kernel(const bf16_t* __restrict__ X,
+                                                          const bf16_t* __restrict__ dY,
+                                                          const int32_t* __restrict__ perm,
+                                                          const float* __restrict__ topk_w,
+                                                          int S, int H, int K,
+                                                          bf16_t* __restrict__ Xg,
+                                                          bf16_t* __restrict__ wdYg) {
+  const int per_row = H / 8;
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= int64_t(S) * per_row) return;
+  const int p = int(i / per_row), c = int(i - int64_t(p) * per_row) * 8;
+  const int slot = perm[p];
+  const int64_t src = int64_t(slot / K) * H + c;
+  const float w = topk_w[slot];
+  *reinterpret_cast<uint4*>(Xg + int64_t(p) * H + c) = *reinterpret_cast<const uint4*>(X + src);
+  const uint4 v = *reinterpret_cast<const uint4*>(dY + src);
+  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float lo = w * bf2f(bf16_t(in[q] & 0xffffu)), hi = w * bf2f(bf16_t(in[q] >> 16));
+    o[q] = pack_bf16x2(lo, hi);
+  }
+  *reinterpret_cast<uint4*>(wdYg + int64_t(p) * H + c) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+}  // namespace g2
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 template <class P>
@@ -325,6 +639,18 @@ static usaf_status launch_mfma(const P& p, int64_t tiles, hipStream_t st, int kc
   if (blocks >= (int64_t(1) << 31)) return USAF_ERR_UNSUPPORTED;
   timer_begin(kclass, st);
   hipLaunchKernelGGL(gemm_mfma_kernel<P>, dim3(unsigned(blocks)), dim3(256), 0, st, p);
+  timer_end(kclass, st);
+  USAF_LAUNCH_CHECK();
+  return USAF_OK;
+}
+
+template <class P>
+static usaf_status launch_v2(const P& p, int64_t tiles, hipStream_t st, int kclass) {
+  if (tiles <= 0) return USAF_OK;
+  const int64_t blocks = (tiles + 7) / 8 * 8;
+  if (blocks >= (int64_t(1) << 31)) return USAF_ERR_UNSUPPORTED;
+  timer_begin(kclass, st);
+  hipLaunchKernelGGL(g2::gemm2_kernel<P>, dim3(unsigned(blocks)), dim3(256), 0, st, p);
   timer_end(kclass, st);
   USAF_LAUNCH_CHECK();
   return USAF_OK;
@@ -342,54 +668,68 @@ usaf_status mfma_router(const usaf_moe_shape& s, const bf16_t* X, const float* W
                      int64_t(MT) * NT * nparts, st, USAF_K_ROUTER_GEMM);
 }
 
+// Tile widths and LDS ring depths of the direct-to-LDS GEMMs.
+constexpr int kFwdBN = 256, kFwdNS = 3;   // gate_up, down, dA, dX: 144 KiB LDS, 1 block / CU
+constexpr int kDwBN = 128, kDwNS = 2;     // dense dW: 64 KiB LDS, 2 blocks / CU
+
 usaf_status mfma_gate_up(const usaf_moe_shape& s, const bf16_t* X, const bf16_t* Wgu,
                          const int32_t* offsets, const int32_t* perm, bf16_t* gu, bf16_t* a,
                          hipStream_t st) {
-  const int NT = int(ceil_div(s.I, 64));
-  return launch_mfma(MGateUp{X, Wgu, offsets, perm, gu, a, s.H, s.E, s.K, s.I, NT},
-                     grouped_tiles_bound(s, NT), st, USAF_K_GATE_UP);
+  const int NT = int(ceil_div(s.I, kFwdBN / 2));
+  return launch_v2(g2::MGateUp<kFwdBN, kFwdNS>{X, Wgu, offsets, perm, gu, a, s.H, s.E, s.K, s.I, NT},
+                   grouped_tiles_bound(s, NT), st, USAF_K_GATE_UP);
 }
 
 usaf_status mfma_down(const usaf_moe_shape& s, const bf16_t* a, const bf16_t* Wd,
                       const int32_t* offsets, float* ybuf, hipStream_t st) {
-  const int NT = int(ceil_div(s.H, kNB));
-  return launch_mfma(MDown{a, Wd, offsets, ybuf, s.H, s.E, s.I, NT}, grouped_tiles_bound(s, NT),
-                     st, USAF_K_DOWN);
+  const int NT = int(ceil_div(s.H, kFwdBN));
+  return launch_v2(g2::MDown<kFwdBN, kFwdNS>{a, Wd, offsets, ybuf, s.H, s.E, s.I, NT},
+                   grouped_tiles_bound(s, NT), st, USAF_K_DOWN);
 }
 
-int mfma_dw_partials(const usaf_moe_shape& s) { return 2 * int(ceil_div(s.I, kNB)); }
+int mfma_dw_partials(const usaf_moe_shape& s) { return 2 * int(ceil_div(s.I, kFwdBN)); }
 
 usaf_status mfma_da(const usaf_moe_shape& s, const bf16_t* dY, const bf16_t* Wd,
                     const int32_t* offsets, const int32_t* perm, const float* topk_w,
                     const bf16_t* gu, const bf16_t* a, bf16_t* dgu, float* dwpart,
                     hipStream_t st) {
-  const int NT = int(ceil_div(s.I, kNB));
-  return launch_mfma(MDa{dY, Wd, offsets, perm, topk_w, gu, a, dgu, dwpart, s.H, s.E, s.K, s.I, NT,
-                         2 * NT},
-                     grouped_tiles_bound(s, NT), st, USAF_K_DA);
+  const int NT = int(ceil_div(s.I, kFwdBN));
+  return launch_v2(g2::MDa<kFwdBN, kFwdNS>{dY, Wd, offsets, perm, topk_w, gu, a, dgu, dwpart, s.H,
+                                           s.E, s.K, s.I, NT, 2 * NT},
+                   grouped_tiles_bound(s, NT), st, USAF_K_DA);
 }
 
 usaf_status mfma_dx(const usaf_moe_shape& s, const bf16_t* dgu, const bf16_t* Wgu,
                     const int32_t* offsets, float* vbuf, hipStream_t st) {
-  const int NT = int(ceil_div(s.H, kNB));
-  return launch_mfma(MDx{dgu, Wgu, offsets, vbuf, s.H, s.E, s.I, NT}, grouped_tiles_bound(s, NT),
-                     st, USAF_K_DX);
+  const int NT = int(ceil_div(s.H, kFwdBN));
+  return launch_v2(g2::MDx<kFwdBN, kFwdNS>{dgu, Wgu, offsets, vbuf, s.H, s.E, s.I, NT},
+                   grouped_tiles_bound(s, NT), st, USAF_K_DX);
 }
 
 usaf_status mfma_dense_dw(const usaf_moe_shape& s, const bf16_t* X, const bf16_t* dY,
                           const bf16_t* dgu, const bf16_t* a, const int32_t* offsets,
-                          const int32_t* perm, const float* topk_w, float* dW, hipStream_t st) {
+                          const int32_t* perm, const float* topk_w, bf16_t* stage, float* dW,
+                          hipStream_t st) {
   const int64_t ngu = int64_t(s.E) * 2 * s.I * s.H;
+  const int64_t S = int64_t(s.T) * s.K;
+  bf16_t* Xg = stage;
+  bf16_t* wdYg = stage + S * s.H;
   timer_begin(USAF_K_DENSE_DW, st);
   {
-    const int MT = int(ceil_div(2 * s.I, kMB)), NT = int(ceil_div(s.H, kNB));
-    MDenseDw<false> p{dgu, X, offsets, perm, topk_w, dW, s.H, s.E, s.K, s.I, MT, NT, ngu};
-    USAF_TRY(launch_mfma(p, int64_t(MT) * NT * s.E, st, -1));
+    const int64_t n = S * (s.H / 8);
+    hipLaunchKernelGGL(g2::stage_dense_kernel, dim3(unsigned(ceil_div(n, 256))), dim3(256), 0, st,
+                       X, dY, perm, topk_w, int(S), s.H, s.K, Xg, wdYg);
+    USAF_LAUNCH_CHECK();
   }
   {
-    const int MT = int(ceil_div(s.H, kMB)), NT = int(ceil_div(s.I, kNB));
-    MDenseDw<true> p{dY, a, offsets, perm, topk_w, dW, s.H, s.E, s.K, s.I, MT, NT, ngu};
-    USAF_TRY(launch_mfma(p, int64_t(MT) * NT * s.E, st, -1));
+    const int MT = int(ceil_div(2 * s.I, g2::kBM)), NT = int(ceil_div(s.H, kDwBN));
+    g2::MDenseDw<false, kDwBN, kDwNS> p{dgu, Xg, offsets, dW, s.H, s.E, s.I, MT, NT, ngu};
+    USAF_TRY(launch_v2(p, int64_t(MT) * NT * s.E, st, -1));
+  }
+  {
+    const int MT = int(ceil_div(s.H, g2::kBM)), NT = int(ceil_div(s.I, kDwBN));
+    g2::MDenseDw<true, kDwBN, kDwNS> p{wdYg, a, offsets, dW, s.H, s.E, s.I, MT, NT, ngu};
+    USAF_TRY(launch_v2(p, int64_t(MT) * NT * s.E, st, -1));
   }
   timer_end(USAF_K_DENSE_DW, st);
   return USAF_OK;
