@@ -1,7 +1,7 @@
 // bf16 MFMA grouped GEMM for gfx950 with direct global->LDS staging.
 //
-// Block tile 128 x BN x 64 (BN = 128 or 256), 256 threads = 4 waves in a
-// 2 x 2 grid; each wave computes 64 x BN/2 with v_mfma_f32_32x32x16_bf16
+// Block tile BM x BN x 64 (BM, BN = 128 or 256), 256 threads = 4 waves in a
+// 2 x 2 grid; each wave computes BM/2 x BN/2 with v_mfma_f32_32x32x16_bf16
 // (fp32 accumulate).  Operand tiles are copied straight from global memory
 // into an NS-deep ring of LDS stages with 16-byte global_load_lds_dwordx4
 // (no register staging), so the loads of stages kt+1 .. kt+NS-1 are in flight
@@ -10,14 +10,16 @@
 // Two operand forms:
 //   k-major  (contraction index contiguous in memory, e.g. X rows, a weight
 //            used as [N][K]): LDS [row][64 k] in 128-byte rows; 16-byte chunk
-//            q of row r sits at slot q ^ (r & 7), so the 8 rows a 32-bank LDS
-//            serves together hit distinct banks.  Fragments are read with
-//            ds_read_b128.
+//            q of row r sits at slot q ^ ((r / 2) mod 8), so the 16 rows that
+//            the 64-bank LDS serves together in a 16-byte read hit distinct
+//            banks (measured: 4 LDS cycles per ds_read_b128, no conflicts).
+//            Fragments are read with ds_read_b128.
 //   mn-major (row index contiguous, e.g. a weight used as [K][N], or
 //            activations contracted over slots): LDS [64 k][R rows]; chunk c
-//            of k-row k sits at slot c ^ (2 (k & 3)).  Fragments are read with
-//            two ds_read_b64_tr_b16 (gfx950's transposing LDS read), which
-//            hand each lane 4 consecutive k of one row.
+//            of k-row k sits at slot c ^ (4 (k & 3)), which puts the 4 k-rows
+//            read together in different 64-byte bank quarters.  Fragments are
+//            read with two ds_read_b64_tr_b16 (gfx950's transposing LDS read),
+//            which hand each lane 4 consecutive k of one row.
 // Rows past the tile and k past the end read clamped, valid addresses; the
 // k tail of the last stage is zeroed in LDS before it is used, and rows or
 // columns past the tile are never stored.
@@ -26,9 +28,11 @@
 // instruction's first operand), so each lane's accumulator holds one row of
 // the tile and runs of 4 consecutive columns: for block (i, j), lane l and
 // element r = 4 g + e:
-//   row = wm*64 + 32 i + (l % 32),  col = wn*BN/2 + 32 j + 8 g + 4 (l / 32) + e.
+//   row = wm*BM/2 + 32 i + (l % 32),  col = wn*BN/2 + 32 j + 8 g + 4 (l / 32) + e.
 // Epilogues therefore read and write 4-column vectors per lane.
 #pragma once
+
+#include <utility>
 
 #include "common.hpp"
 #include "gemm_mfma.hpp"
@@ -41,6 +45,18 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kBM = 128, kBK = 64;
+
+// f(std::integral_constant<int, 0>{}), ..., f(...<N-1>): a loop whose index is
+// a compile-time constant in each copy (accumulator registers are indexed
+// statically even where the body is too large for the unroller).
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // s_waitcnt with vmcnt <= n (expcnt and lgkmcnt left unconstrained).
 template <int n>
@@ -63,7 +79,59 @@ __device__ __forceinline__ void dma16(const void* g, unsigned char* lds_base) {
                : "memory", "m0");
 }
 
-__device__ __forceinline__ int out_row(int wm, int i, int lane) { return wm * 64 + 32 * i + (lane & 31); }
+// Logical tile L -> (expert, column tile, row tile of BM rows) over device
+// offsets[E+1]; tiles ordered expert-major, then column tile, then row tile.
+// Wave 0 scans the experts 64 at a time; false for the whole block past the end.
+template <int BM>
+__device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ offsets, int E, int NT,
+                                             int L, MTile& t) {
+  __shared__ int sh[4];
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    int base = 0;
+    bool found = false;
+    for (int e0 = 0; e0 < E && !found; e0 += 64) {
+      const int e = e0 + lane;
+      const int o0 = e < E ? offsets[e] : 0;
+      const int cnt = e < E ? offsets[e + 1] - o0 : 0;
+      const int tiles = ((cnt + BM - 1) / BM) * NT;
+      int incl = tiles;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+      }
+      const int excl = incl - tiles;
+      const bool hit = tiles > 0 && L >= base + excl && L < base + incl;
+      const uint64_t bal = __ballot(hit);
+      if (bal) {
+        if (lane == __ffsll((long long)bal) - 1) {
+          sh[0] = e;
+          sh[1] = L - base - excl;
+          sh[2] = cnt;
+          sh[3] = o0;
+        }
+        found = true;
+      }
+      base += __shfl(incl, 63, 64);
+    }
+    if (!found && lane == 0) sh[0] = -1;
+  }
+  __syncthreads();
+  t.e = sh[0];
+  if (t.e < 0) return false;
+  const int rem = sh[1], cnt = sh[2];
+  const int mts = (cnt + BM - 1) / BM;
+  t.nt = rem / mts;
+  t.m0 = (rem - t.nt * mts) * BM;
+  t.mc = min(BM, cnt - t.m0);
+  t.off = sh[3];
+  return true;
+}
+
+__device__ __forceinline__ int out_row(int BM, int wm, int i, int lane) {
+  return wm * (BM / 2) + 32 * i + (lane & 31);
+}
 // first of the 4 consecutive columns of group g of block j
 __device__ __forceinline__ int out_col(int BN, int wn, int j, int g, int lane) {
   return wn * (BN / 2) + 32 * j + 8 * g + 4 * (lane >> 5);
@@ -79,39 +147,48 @@ template <int R>
 struct KMajor {
   static constexpr int kInst = R / 32;  // dma instructions per wave per stage
   static constexpr int kBytes = R * 128;
+  // slot of 16-byte chunk q in row r: 64 banks serve 16 lanes of a 16-byte
+  // read together, i.e. 16 consecutive rows; rows r and r+1 share a 256-byte
+  // bank line, so the chunk position is XOR-ed with (r/2) mod 8
+  __device__ __forceinline__ static int sw(int r) { return (r >> 1) & 7; }
   const bf16_t* p[kInst];
+  int chunk[kInst];
   int kend;
   template <class Src>
   __device__ __forceinline__ void init(const Src& s, int kend_, int w, int lane) {
     kend = kend_;
-    const int chunk = (lane & 7) ^ (lane >> 3);
 #pragma unroll
-    for (int i = 0; i < kInst; ++i) p[i] = s.row(w * (R / 4) + 8 * i + (lane >> 3)) + 8 * chunk;
+    for (int i = 0; i < kInst; ++i) {
+      const int r = w * (R / 4) + 8 * i + (lane >> 3);
+      chunk[i] = (lane & 7) ^ sw(r);
+      p[i] = s.row(r) + 8 * chunk[i];
+    }
   }
   // stage kt into lds (operand tile base)
   template <class Src>
-  __device__ __forceinline__ void issue(const Src&, int kt, unsigned char* lds, int w, int lane) const {
-    const int chunk = (lane & 7) ^ (lane >> 3);
-    // a chunk past kend (kend % 64 != 0, last stage) reads the row's last
-    // chunk instead; it is zeroed before use
+  __device__ __forceinline__ void issue(const Src&, int kt, unsigned char* lds, int w, int) const {
     const int k0 = kt * kBK;
-    const int over = k0 + 8 * chunk + 8 - kend;
-    const int koff = over > 0 ? k0 - over : k0;
 #pragma unroll
-    for (int i = 0; i < kInst; ++i) dma16(p[i] + koff, lds + (w * (R / 4) + 8 * i) * 128);
+    for (int i = 0; i < kInst; ++i) {
+      // a chunk past kend (kend % 64 != 0, last stage) reads the row's last
+      // chunk instead; it is zeroed before use
+      const int over = k0 + 8 * chunk[i] + 8 - kend;
+      const int koff = over > 0 ? k0 - over : k0;
+      dma16(p[i] + koff, lds + (w * (R / 4) + 8 * i) * 128);
+    }
   }
   // zero k >= kvalid (kvalid a multiple of 8) in a stage
   __device__ __forceinline__ static void zero_tail(unsigned char* lds, int kvalid, int tid) {
     for (int x = tid; x < R * 8; x += 256) {
       const int r = x >> 3, q = x & 7;
       if (8 * q >= kvalid)
-        *reinterpret_cast<uint4*>(lds + r * 128 + 16 * (q ^ (r & 7))) = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(lds + r * 128 + 16 * (q ^ sw(r))) = make_uint4(0, 0, 0, 0);
     }
   }
-  // fragment rows base..base+31, k-substep kc
+  // fragment rows base..base+31 (base a multiple of 32), k-substep kc
   __device__ __forceinline__ static bf16x8_t frag(const unsigned char* lds, int base, int kc, int lane) {
     const int r = base + (lane & 31);
-    const int q = (2 * kc + (lane >> 5)) ^ (lane & 7);
+    const int q = (2 * kc + (lane >> 5)) ^ sw(r);
     return *reinterpret_cast<const bf16x8_t*>(lds + r * 128 + 16 * q);
   }
 };
@@ -135,7 +212,7 @@ struct MNMajor {
 #pragma unroll
     for (int i = 0; i < kInst; ++i) {
       const int kr = krow0 + i * kKPI;
-      const int chunk = min(slot ^ (2 * (kr & 3)), last);
+      const int chunk = min(slot ^ (4 * (kr & 3)), last);
       const int k = min(kt * kBK + kr, kend - 1);
       dma16(s.kptr(k) + 8 * chunk, lds + (w * kInst + i) * kKPI * R * 2);
     }
@@ -149,7 +226,7 @@ struct MNMajor {
     const int g = lane >> 4, pq = lane & 15, jj = pq >> 2, q = pq & 3;
     const int n = base + 16 * (g & 1) + 4 * q;
     const int k = 16 * kc + 8 * (g >> 1) + jj;
-    const int off = k * (R * 2) + 16 * ((n >> 3) ^ (2 * jj)) + 8 * (q & 1);
+    const int off = k * (R * 2) + 16 * ((n >> 3) ^ (4 * jj)) + 8 * (q & 1);
     const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds + off));
     const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds + off + 4 * R * 2));
     typedef short s16x8_t __attribute__((ext_vector_type(8)));
@@ -158,18 +235,143 @@ struct MNMajor {
   }
 };
 
+
+// lgkmcnt(0): this wave's LDS accesses have completed (the compiler cannot
+// see the cross-lane dependence of the staging below).
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15 << 0) | (7 << 4) | (0 << 8) | (3 << 14));
+  asm volatile("" ::: "memory");
+}
+
+// Output staging through LDS.  A wave holds, for its 32-row block i, 32 rows
+// x 32*NJ columns in the swapped MFMA layout (lane: one row, 4-column runs).
+// These helpers write that block into the wave's own LDS region and read it
+// back row-major, so that each global store instruction covers whole row
+// segments (consecutive lanes, consecutive 16 bytes).  The caller must have
+// finished every LDS read of the main loop (a block barrier) first.
+//
+// fp32: calls st(row, col4, float4) for rows 0..31 and col4 = 4*(lane%32)
+// (a multiple of 4 below 32*NJ; rows 2q + lane/32).
+// With region == nullptr the lane stores its own 4-column runs instead
+// (st(row = lane%32, col4, float4)).
+template <int NJ, class St>
+__device__ __forceinline__ void stage_f32(unsigned char* region, const f32x16_t (&accr)[NJ], int lane,
+                                          St&& st) {
+  constexpr int kPitch = 32 * NJ * 4 + 16;  // bytes per staged row
+  const int r = lane & 31, h = lane >> 5;
+  if (region == nullptr) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        st(r, 32 * j + 8 * g + 4 * h,
+           make_float4(accr[j][4 * g], accr[j][4 * g + 1], accr[j][4 * g + 2], accr[j][4 * g + 3]));
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4*>(region + r * kPitch + 4 * (32 * j + 8 * g + 4 * h)) =
+          make_float4(accr[j][4 * g], accr[j][4 * g + 1], accr[j][4 * g + 2], accr[j][4 * g + 3]);
+  wave_lds_sync();
+  static_assert(NJ == 4, "row-major read assumes 128 columns = 32 lanes x 4");
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int row = 2 * q + h;
+    st(row, 4 * r, *reinterpret_cast<const float4*>(region + row * kPitch + 16 * r));
+  }
+  wave_lds_sync();
+}
+
+// bf16, NC columns per row (NC = 64: 128-byte rows): writer puts packed
+// (2 x bf16) words; reader calls st(row, col8, uint4) with 8 columns per
+// lane, 8 lanes per row.
+template <int NC>
+struct StageBf16 {
+  static constexpr int kPitch = NC * 2 + 16;
+  __device__ __forceinline__ static void put2(unsigned char* region, int row, int col, uint32_t w0,
+                                              uint32_t w1) {
+    *reinterpret_cast<uint2*>(region + row * kPitch + 2 * col) = make_uint2(w0, w1);
+  }
+  template <class St>
+  __device__ __forceinline__ static void drain(unsigned char* region, int lane, St&& st) {
+    static_assert(NC == 64, "8 lanes of 16 bytes per row");
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 8 * q + (lane >> 3);
+      st(row, 8 * (lane & 7), *reinterpret_cast<const uint4*>(region + row * kPitch + 16 * (lane & 7)));
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // The kernel.  P supplies
-//   static constexpr int BN, NS; types AOp, BOp (KMajor<128> / MNMajor<128>,
+//   static constexpr int BM, BN, NS; types AOp, BOp (KMajor<BM> / MNMajor<BM>,
 //   KMajor<BN> / MNMajor<BN>)
 //   bool tile(int L, MTile&)      (uniform per block; contraction [0, t.ke))
 //   a_src(t), b_src(t): row(r) for a k-major operand, kptr(k) + ncols for an
 //   mn-major one
-//   void epilogue(const MTile&, f32x16_t (&acc)[2][BN/64], int wm, int wn, int lane)
+//   void epilogue(const MTile&, f32x16_t (&acc)[BM/64][BN/64], int wm, int wn, int lane,
+//                 unsigned char* stage)   (stage: kStageBytes of LDS private to the wave)
+// Each wave computes (BM/2) x (BN/2).  Row blocks of 32 past the tile's valid
+// rows (ragged expert groups) issue no MFMA.
 // ---------------------------------------------------------------------------
+template <class P, int VB, int IM, int NJ, class AOp, class BOp, class AS, class BS>
+__device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS& as, const BS& bs,
+                                          unsigned char (*lds)[AOp::kBytes + BOp::kBytes], int K,
+                                          int nk, int tid, int w, int wm, int wn, int lane,
+                                          f32x16_t (&acc)[IM][NJ]) {
+  constexpr int BM = P::BM, BN = P::BN, NS = P::NS;
+  constexpr int A_BYTES = AOp::kBytes;
+  constexpr int NLOAD = AOp::kInst + BOp::kInst;
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + NS - 2 < nk) wait_vmcnt<(NS - 2) * NLOAD>(); else wait_vmcnt<0>();
+    __syncthreads();
+    unsigned char* cur = lds[kt % NS];
+    const int kvalid = K - kt * kBK;
+    if (kvalid < kBK) {  // uniform: only the last stage
+      AOp::zero_tail(cur, kvalid, tid);
+      BOp::zero_tail(cur + A_BYTES, kvalid, tid);
+      __syncthreads();
+    }
+    if (kt + NS - 1 < nk) {
+      unsigned char* nxt = lds[(kt + NS - 1) % NS];
+      ao.issue(as, kt + NS - 1, nxt, w, lane);
+      bo.issue(bs, kt + NS - 1, nxt + A_BYTES, w, lane);
+    }
+    if constexpr (VB > 0) {
+      const unsigned char* As = cur;
+      const unsigned char* Bs = cur + A_BYTES;
+      // fragments of substep kc+1 are read while the MFMAs of kc run
+      bf16x8_t af[2][VB], bfr[2][NJ];
+#pragma unroll
+      for (int i = 0; i < VB; ++i) af[0][i] = AOp::frag(As, wm * (BM / 2) + 32 * i, 0, lane);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bfr[0][j] = BOp::frag(Bs, wn * (BN / 2) + 32 * j, 0, lane);
+#pragma unroll
+      for (int kc = 0; kc < kBK / 16; ++kc) {
+        const int c = kc & 1, n = c ^ 1;
+        if (kc + 1 < kBK / 16) {
+#pragma unroll
+          for (int i = 0; i < VB; ++i) af[n][i] = AOp::frag(As, wm * (BM / 2) + 32 * i, kc + 1, lane);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) bfr[n][j] = BOp::frag(Bs, wn * (BN / 2) + 32 * j, kc + 1, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < VB; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[c][j], af[c][i], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+}
+
 template <class P>
 __global__ __launch_bounds__(256) void gemm2_kernel(P p) {
-  constexpr int BN = P::BN, NS = P::NS, NJ = BN / 64;
+  constexpr int BM = P::BM, BN = P::BN, NS = P::NS, IM = BM / 64, NJ = BN / 64;
   using AOp = typename P::AOp;
   using BOp = typename P::BOp;
   constexpr int A_BYTES = AOp::kBytes, B_BYTES = BOp::kBytes;
@@ -189,9 +391,9 @@ __global__ __launch_bounds__(256) void gemm2_kernel(P p) {
   ao.init(as, K, w, lane);
   bo.init(bs, K, w, lane);
   const int nk = (K + kBK - 1) / kBK;
-  f32x16_t acc[2][NJ];
+  f32x16_t acc[IM][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < IM; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -202,54 +404,75 @@ __global__ __launch_bounds__(256) void gemm2_kernel(P p) {
       ao.issue(as, s, lds[s], w, lane);
       bo.issue(bs, s, lds[s] + A_BYTES, w, lane);
     }
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + NS - 2 < nk) wait_vmcnt<(NS - 2) * NLOAD>(); else wait_vmcnt<0>();
-    __syncthreads();
-    unsigned char* cur = lds[kt % NS];
-    const int kvalid = K - kt * kBK;
-    if (kvalid < kBK) {  // uniform: only the last stage
-      AOp::zero_tail(cur, kvalid, tid);
-      BOp::zero_tail(cur + A_BYTES, kvalid, tid);
-      __syncthreads();
+  main_loop<P, IM, IM, NJ>(ao, bo, as, bs, lds, K, nk, tid, w, wm, wn, lane, acc);
+  __syncthreads();  // the ring is free: epilogues may stage through it
+  p.epilogue(t, acc, wm, wn, lane, &lds[0][0] + w * P::kStageBytes);
+}
+
+// Persistent form: a grid of about one block per CU walks the tile list
+// (block b takes logical tiles x(b), x(b) + G, x(b) + 2G, ... with the
+// XCD-aware x), and the first stages of the next tile are in flight while
+// the current tile's epilogue stores.  Epilogues get no LDS staging area
+// here (the ring holds the next tile's stages).
+template <class P>
+__global__ __launch_bounds__(256) void gemm2_persistent(P p) {
+  constexpr int BM = P::BM, BN = P::BN, NS = P::NS, IM = BM / 64, NJ = BN / 64;
+  using AOp = typename P::AOp;
+  using BOp = typename P::BOp;
+  constexpr int A_BYTES = AOp::kBytes, B_BYTES = BOp::kBytes;
+  constexpr int NLOAD = AOp::kInst + BOp::kInst;
+  static_assert((NS - 2) * NLOAD < 64, "vmcnt");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[NS][A_BYTES + B_BYTES];
+  const int G = gridDim.x;
+  int L = xcd_remap_blocks(blockIdx.x, G);
+  MTile t;
+  if (!p.tile(L, t)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  auto as = p.a_src(t);
+  auto bs = p.b_src(t);
+  AOp ao;
+  BOp bo;
+  ao.init(as, t.ke, w, lane);
+  bo.init(bs, t.ke, w, lane);
+  int nk = (t.ke + kBK - 1) / kBK;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) {
+      ao.issue(as, s, lds[s], w, lane);
+      bo.issue(bs, s, lds[s] + A_BYTES, w, lane);
     }
-    if (kt + NS - 1 < nk) {
-      unsigned char* nxt = lds[(kt + NS - 1) % NS];
-      ao.issue(as, kt + NS - 1, nxt, w, lane);
-      bo.issue(bs, kt + NS - 1, nxt + A_BYTES, w, lane);
-    }
-    const unsigned char* As = cur;
-    const unsigned char* Bs = cur + A_BYTES;
-    // fragments of substep kc+1 are read while the MFMAs of kc run
-    bf16x8_t af[2][2], bfr[2][NJ];
+  while (true) {
+    f32x16_t acc[IM][NJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) af[0][i] = AOp::frag(As, wm * 64 + 32 * i, 0, lane);
+    for (int i = 0; i < IM; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) bfr[0][j] = BOp::frag(Bs, wn * (BN / 2) + 32 * j, 0, lane);
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int kc = 0; kc < kBK / 16; ++kc) {
-      const int c = kc & 1, n = c ^ 1;
-      if (kc + 1 < kBK / 16) {
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    main_loop<P, IM, IM, NJ>(ao, bo, as, bs, lds, t.ke, nk, tid, w, wm, wn, lane, acc);
+    __syncthreads();  // every wave is done with the ring
+    MTile tn;
+    L += G;
+    const bool more = p.tile(L, tn);
+    if (more) {
+      as = p.a_src(tn);
+      bs = p.b_src(tn);
+      ao.init(as, tn.ke, w, lane);
+      bo.init(bs, tn.ke, w, lane);
+      nk = (tn.ke + kBK - 1) / kBK;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) af[n][i] = AOp::frag(As, wm * 64 + 32 * i, kc + 1, lane);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) bfr[n][j] = BOp::frag(Bs, wn * (BN / 2) + 32 * j, kc + 1, lane);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[c][j], af[c][i], acc[i][j], 0, 0, 0);
-      if (kc + 1 < kBK / 16) {
-        // interleave: one LDS read after each MFMA
-#pragma unroll
-        for (int q = 0; q < 2 * NJ; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int s = 0; s < NS - 1; ++s)
+        if (s < nk) {
+          ao.issue(as, s, lds[s], w, lane);
+          bo.issue(bs, s, lds[s] + A_BYTES, w, lane);
         }
-      }
     }
+    p.epilogue(t, acc, wm, wn, lane, nullptr);
+    if (!more) break;
+    t = tn;
   }
-  p.epilogue(t, acc, wm, wn, lane);
 }
 
 }  // namespace g2

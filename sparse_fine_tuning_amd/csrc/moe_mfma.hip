@@ -353,16 +353,16 @@ struct GateUpRowsC {
   }
 };
 
-template <int BN_, int NS_>
+template <int BM_, int BN_, int NS_>
 struct MGateUp {
-  static constexpr int BN = BN_, NS = NS_, NJ = BN_ / 64;
-  using AOp = KMajor<kBM>;
+  static constexpr int BM = BM_, BN = BN_, NS = NS_, IM = BM_ / 64, NJ = BN_ / 64;
+  using AOp = KMajor<BM>;
   using BOp = KMajor<BN>;
   const bf16_t* X; const bf16_t* Wgu; const int32_t* offsets; const int32_t* perm;
   bf16_t* gu; bf16_t* a;
   int H, E, K, I, NT;
   __device__ __forceinline__ bool tile(int L, MTile& t) const {
-    if (!grouped_m_tile(offsets, E, NT, L, t)) return false;
+    if (!grouped_tile<BM>(offsets, E, NT, L, t)) return false;
     t.kb = 0; t.ke = H; t.n0 = t.nt * (BN / 2); t.nc = 0;
     return true;
   }
@@ -370,18 +370,23 @@ struct MGateUp {
   __device__ __forceinline__ GateUpRowsC<BN> b_src(const MTile& t) const {
     return GateUpRowsC<BN>{Wgu + int64_t(t.e) * 2 * I * H, t.n0, I, H};
   }
-  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[2][NJ], int wm, int wn, int lane) const {
+  static constexpr int kStageBytes = 3 * 32 * StageBf16<64>::kPitch;
+  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
+                                           unsigned char* stage) const {
+    static_assert(NJ == 4, "a wave covers 64 features: gate / up blocks of 32, twice");
+    unsigned char* sg = stage;
+    unsigned char* su = stage + 32 * StageBf16<64>::kPitch;
+    unsigned char* sa = stage + 2 * 32 * StageBf16<64>::kPitch;
+    const int F = t.n0 + (BN / 4) * wn;  // first feature of this wave
+    static_for<IM>([&](auto I_) {
+      constexpr int i = decltype(I_)::value;
+      const int rb = wm * (BM / 2) + 32 * i;
+      if (rb >= t.mc) return;
+      const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = out_row(wm, i, lane);
-      if (row >= t.mc) continue;
-      const int64_t p = t.off + t.m0 + row;
-#pragma unroll
-      for (int jp = 0; jp < NJ / 2; ++jp)
+      for (int jp = 0; jp < 2; ++jp)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int f = t.n0 + (BN / 4) * wn + 32 * jp + 8 * g + 4 * (lane >> 5);
-          if (f >= I) continue;
           uint32_t gw[2], uw[2], aw[2];
 #pragma unroll
           for (int e = 0; e < 4; e += 2) {
@@ -393,23 +398,44 @@ struct MGateUp {
             uw[e / 2] = pack_bf16x2(u0, u1);
             aw[e / 2] = pack_bf16x2(silu_f(g0) * u0, silu_f(g1) * u1);
           }
-          *reinterpret_cast<uint2*>(gu + p * 2 * I + f) = make_uint2(gw[0], gw[1]);
-          *reinterpret_cast<uint2*>(gu + p * 2 * I + I + f) = make_uint2(uw[0], uw[1]);
-          *reinterpret_cast<uint2*>(a + p * I + f) = make_uint2(aw[0], aw[1]);
+          const int c = 32 * jp + 8 * g + 4 * h;
+          if (stage) {
+            StageBf16<64>::put2(sg, r, c, gw[0], gw[1]);
+            StageBf16<64>::put2(su, r, c, uw[0], uw[1]);
+            StageBf16<64>::put2(sa, r, c, aw[0], aw[1]);
+          } else if (rb + r < t.mc && F + c < I) {
+            const int64_t p = t.off + t.m0 + rb + r;
+            *reinterpret_cast<uint2*>(gu + p * 2 * I + F + c) = make_uint2(gw[0], gw[1]);
+            *reinterpret_cast<uint2*>(gu + p * 2 * I + I + F + c) = make_uint2(uw[0], uw[1]);
+            *reinterpret_cast<uint2*>(a + p * I + F + c) = make_uint2(aw[0], aw[1]);
+          }
         }
-    }
+      if (!stage) return;
+      wave_lds_sync();
+      const int64_t p0 = t.off + t.m0 + rb;
+      auto rows = [&](unsigned char* reg, bf16_t* base, int64_t ld, int coff) {
+        StageBf16<64>::drain(reg, lane, [&](int row, int c8, uint4 v) {
+          if (rb + row < t.mc && F + c8 < I)
+            *reinterpret_cast<uint4*>(base + (p0 + row) * ld + coff + F + c8) = v;
+        });
+      };
+      rows(sg, gu, 2 * I, 0);
+      rows(su, gu, 2 * I, I);
+      rows(sa, a, I, 0);
+      wave_lds_sync();
+    });
   }
 };
 
-template <int BN_, int NS_>
+template <int BM_, int BN_, int NS_>
 struct MDown {
-  static constexpr int BN = BN_, NS = NS_, NJ = BN_ / 64;
-  using AOp = KMajor<kBM>;
+  static constexpr int BM = BM_, BN = BN_, NS = NS_, IM = BM_ / 64, NJ = BN_ / 64;
+  using AOp = KMajor<BM>;
   using BOp = KMajor<BN>;
   const bf16_t* a; const bf16_t* Wd; const int32_t* offsets; float* ybuf;
   int H, E, I, NT;
   __device__ __forceinline__ bool tile(int L, MTile& t) const {
-    if (!grouped_m_tile(offsets, E, NT, L, t)) return false;
+    if (!grouped_tile<BM>(offsets, E, NT, L, t)) return false;
     t.kb = 0; t.ke = I; t.n0 = t.nt * BN; t.nc = min(BN, H - t.n0);
     return true;
   }
@@ -419,35 +445,33 @@ struct MDown {
   __device__ __forceinline__ PlainRowsC b_src(const MTile& t) const {
     return PlainRowsC{Wd + (int64_t(t.e) * H + t.n0) * I, I, t.nc};
   }
-  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[2][NJ], int wm, int wn, int lane) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = out_row(wm, i, lane);
-      if (row >= t.mc) continue;
-      float* yr = ybuf + int64_t(t.off + t.m0 + row) * H + t.n0;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = out_col(BN, wn, j, g, lane);
-          if (col < t.nc)
-            *reinterpret_cast<float4*>(yr + col) =
-                make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-        }
-    }
+  static constexpr int kStageBytes = 32 * (32 * NJ * 4 + 16);
+  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
+                                           unsigned char* stage) const {
+    static_for<IM>([&](auto I_) {
+      constexpr int i = decltype(I_)::value;
+      const int rb = wm * (BM / 2) + 32 * i;
+      if (rb >= t.mc) return;
+      const int ncw = t.nc - wn * (BN / 2);
+      float* base = ybuf + int64_t(t.off + t.m0 + rb) * H + t.n0 + wn * (BN / 2);
+      const int64_t ld = H;
+      stage_f32<NJ>(stage, acc[i], lane, [&](int row, int col, float4 v) {
+        if (rb + row < t.mc && col < ncw) *reinterpret_cast<float4*>(base + row * ld + col) = v;
+      });
+    });
   }
 };
 
-template <int BN_, int NS_>
+template <int BM_, int BN_, int NS_>
 struct MDa {
-  static constexpr int BN = BN_, NS = NS_, NJ = BN_ / 64;
-  using AOp = KMajor<kBM>;
+  static constexpr int BM = BM_, BN = BN_, NS = NS_, IM = BM_ / 64, NJ = BN_ / 64;
+  using AOp = KMajor<BM>;
   using BOp = MNMajor<BN>;
   const bf16_t* dY; const bf16_t* Wd; const int32_t* offsets; const int32_t* perm;
   const float* topk_w; const bf16_t* gu; const bf16_t* a; bf16_t* dgu; float* dwpart;
   int H, E, K, I, NT, NTP;
   __device__ __forceinline__ bool tile(int L, MTile& t) const {
-    if (!grouped_m_tile(offsets, E, NT, L, t)) return false;
+    if (!grouped_tile<BM>(offsets, E, NT, L, t)) return false;
     t.kb = 0; t.ke = H; t.n0 = t.nt * BN; t.nc = min(BN, I - t.n0);
     return true;
   }
@@ -455,10 +479,12 @@ struct MDa {
   __device__ __forceinline__ StridedKC b_src(const MTile& t) const {
     return StridedKC{Wd + int64_t(t.e) * H * I + t.n0, I, t.nc};
   }
-  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[2][NJ], int wm, int wn, int lane) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = out_row(wm, i, lane);
+  static constexpr int kStageBytes = 0;
+  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
+                                           unsigned char*) const {
+    static_for<IM>([&](auto I_) {
+      constexpr int i = decltype(I_)::value;
+      const int row = out_row(BM, wm, i, lane);
       const bool vrow = row < t.mc;
       const int64_t p = t.off + t.m0 + (vrow ? row : 0);
       const float wt = topk_w[perm[p]];
@@ -499,19 +525,19 @@ struct MDa {
       // lanes l and l + 32 hold the same row
       part += __shfl_xor(part, 32, 64);
       if (lane < 32 && vrow) dwpart[p * NTP + 2 * t.nt + wn] = part;
-    }
+    });
   }
 };
 
-template <int BN_, int NS_>
+template <int BM_, int BN_, int NS_>
 struct MDx {
-  static constexpr int BN = BN_, NS = NS_, NJ = BN_ / 64;
-  using AOp = KMajor<kBM>;
+  static constexpr int BM = BM_, BN = BN_, NS = NS_, IM = BM_ / 64, NJ = BN_ / 64;
+  using AOp = KMajor<BM>;
   using BOp = MNMajor<BN>;
   const bf16_t* dgu; const bf16_t* Wgu; const int32_t* offsets; float* vbuf;
   int H, E, I, NT;
   __device__ __forceinline__ bool tile(int L, MTile& t) const {
-    if (!grouped_m_tile(offsets, E, NT, L, t)) return false;
+    if (!grouped_tile<BM>(offsets, E, NT, L, t)) return false;
     t.kb = 0; t.ke = 2 * I; t.n0 = t.nt * BN; t.nc = min(BN, H - t.n0);
     return true;
   }
@@ -521,22 +547,20 @@ struct MDx {
   __device__ __forceinline__ StridedKC b_src(const MTile& t) const {
     return StridedKC{Wgu + int64_t(t.e) * 2 * I * H + t.n0, H, t.nc};
   }
-  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[2][NJ], int wm, int wn, int lane) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = out_row(wm, i, lane);
-      if (row >= t.mc) continue;
-      float* vr = vbuf + int64_t(t.off + t.m0 + row) * H + t.n0;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = out_col(BN, wn, j, g, lane);
-          if (col < t.nc)
-            *reinterpret_cast<float4*>(vr + col) =
-                make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-        }
-    }
+  static constexpr int kStageBytes = 32 * (32 * NJ * 4 + 16);
+  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
+                                           unsigned char* stage) const {
+    static_for<IM>([&](auto I_) {
+      constexpr int i = decltype(I_)::value;
+      const int rb = wm * (BM / 2) + 32 * i;
+      if (rb >= t.mc) return;
+      const int ncw = t.nc - wn * (BN / 2);
+      float* base = vbuf + int64_t(t.off + t.m0 + rb) * H + t.n0 + wn * (BN / 2);
+      const int64_t ld = H;
+      stage_f32<NJ>(stage, acc[i], lane, [&](int row, int col, float4 v) {
+        if (rb + row < t.mc && col < ncw) *reinterpret_cast<float4*>(base + row * ld + col) = v;
+      });
+    });
   }
 };
 
@@ -545,10 +569,10 @@ struct MDx {
 //   gate_up: dW[r, c] = sum_p dGU[p, r] Xg[p, c]    (rows 2I, cols H)
 //   down:    dW[r, c] = sum_p wdYg[p, r] a[p, c]    (rows H,  cols I)
 // Xg = X gathered by token and wdYg = bf16(w_p dY[tok(p)]) are staged first.
-template <bool kDown, int BN_, int NS_>
+template <bool kDown, int BM_, int BN_, int NS_>
 struct MDenseDw {
-  static constexpr int BN = BN_, NS = NS_, NJ = BN_ / 64;
-  using AOp = MNMajor<kBM>;
+  static constexpr int BM = BM_, BN = BN_, NS = NS_, IM = BM_ / 64, NJ = BN_ / 64;
+  using AOp = MNMajor<BM>;
   using BOp = MNMajor<BN>;
   const bf16_t* L; const bf16_t* R; const int32_t* offsets; float* dW;
   int H, E, I, MT, NT;
@@ -561,9 +585,9 @@ struct MDenseDw {
     if (t.e >= E) return false;
     const int rem = Lt - t.e * per;
     t.nt = rem / MT;
-    t.m0 = (rem - t.nt * MT) * kBM;
+    t.m0 = (rem - t.nt * MT) * BM;
     t.n0 = t.nt * BN;
-    t.mc = min(kBM, rows_total() - t.m0);
+    t.mc = min(BM, rows_total() - t.m0);
     t.nc = min(BN, cols_total() - t.n0);
     t.off = offsets[t.e];
     t.kb = 0;
@@ -578,24 +602,22 @@ struct MDenseDw {
     const int ld = cols_total();
     return StridedKC{R + int64_t(t.off) * ld + t.n0, ld, t.nc};
   }
-  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[2][NJ], int wm, int wn, int lane) const {
-    const int64_t base = kDown ? ngu + int64_t(t.e) * H * I : int64_t(t.e) * 2 * I * H;
+  static constexpr int kStageBytes = 32 * (32 * NJ * 4 + 16);
+  __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
+                                           unsigned char* stage) const {
+    const int64_t obase = kDown ? ngu + int64_t(t.e) * H * I : int64_t(t.e) * 2 * I * H;
     const int ldo = cols_total();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = out_row(wm, i, lane);
-      if (row >= t.mc) continue;
-      float* dr = dW + base + int64_t(t.m0 + row) * ldo + t.n0;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = out_col(BN, wn, j, g, lane);
-          if (col < t.nc)
-            *reinterpret_cast<float4*>(dr + col) =
-                make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-        }
-    }
+    static_for<IM>([&](auto I_) {
+      constexpr int i = decltype(I_)::value;
+      const int rb = wm * (BM / 2) + 32 * i;
+      if (rb >= t.mc) return;
+      const int ncw = t.nc - wn * (BN / 2);
+      float* base = dW + obase + int64_t(t.m0 + rb) * ldo + t.n0 + wn * (BN / 2);
+      const int64_t ld = ldo;
+      stage_f32<NJ>(stage, acc[i], lane, [&](int row, int col, float4 v) {
+        if (rb + row < t.mc && col < ncw) *reinterpret_cast<float4*>(base + row * ld + col) = v;
+      });
+    });
   }
 };
 
@@ -656,8 +678,37 @@ static usaf_status launch_v2(const P& p, int64_t tiles, hipStream_t st, int kcla
   return USAF_OK;
 }
 
-static int64_t grouped_tiles_bound(const usaf_moe_shape& s, int NT) {
-  return (ceil_div(int64_t(s.T) * s.K, kMB) + s.E) * NT;
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Persistent launch: about one block per CU (a multiple of 8 for the XCD
+// remap), never more blocks than tiles.
+template <class P>
+static usaf_status launch_persistent(const P& p, int64_t tiles, hipStream_t st, int kclass) {
+  if (tiles <= 0) return USAF_OK;
+  int64_t blocks = device_cus();
+  if (blocks > tiles) blocks = tiles;
+  blocks = (blocks + 7) / 8 * 8;
+  timer_begin(kclass, st);
+  hipLaunchKernelGGL(g2::gemm2_persistent<P>, dim3(unsigned(blocks)), dim3(256), 0, st, p);
+  timer_end(kclass, st);
+  USAF_LAUNCH_CHECK();
+  return USAF_OK;
+}
+
+static int64_t grouped_tiles_bound(const usaf_moe_shape& s, int NT, int BM = kMB) {
+  return (ceil_div(int64_t(s.T) * s.K, BM) + s.E) * NT;
 }
 
 usaf_status mfma_router(const usaf_moe_shape& s, const bf16_t* X, const float* Wr, float* parts,
@@ -668,23 +719,23 @@ usaf_status mfma_router(const usaf_moe_shape& s, const bf16_t* X, const float* W
                      int64_t(MT) * NT * nparts, st, USAF_K_ROUTER_GEMM);
 }
 
-// Tile widths and LDS ring depths of the direct-to-LDS GEMMs.
-constexpr int kFwdBN = 256, kFwdNS = 3;   // gate_up, down, dA, dX: 144 KiB LDS, 1 block / CU
-constexpr int kDwBN = 128, kDwNS = 2;     // dense dW: 64 KiB LDS, 2 blocks / CU
+// Tile shapes and LDS ring depths of the direct-to-LDS GEMMs.
+constexpr int kFwdBM = 128, kFwdBN = 256, kFwdNS = 3;  // gate_up, down, dA, dX: 144 KiB LDS
+constexpr int kDwBM = 256, kDwBN = 256, kDwNS = 2;     // dense dW: 128 KiB LDS
 
 usaf_status mfma_gate_up(const usaf_moe_shape& s, const bf16_t* X, const bf16_t* Wgu,
                          const int32_t* offsets, const int32_t* perm, bf16_t* gu, bf16_t* a,
                          hipStream_t st) {
   const int NT = int(ceil_div(s.I, kFwdBN / 2));
-  return launch_v2(g2::MGateUp<kFwdBN, kFwdNS>{X, Wgu, offsets, perm, gu, a, s.H, s.E, s.K, s.I, NT},
-                   grouped_tiles_bound(s, NT), st, USAF_K_GATE_UP);
+  return launch_persistent(g2::MGateUp<kFwdBM, kFwdBN, kFwdNS>{X, Wgu, offsets, perm, gu, a, s.H, s.E, s.K, s.I, NT},
+                   grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_GATE_UP);
 }
 
 usaf_status mfma_down(const usaf_moe_shape& s, const bf16_t* a, const bf16_t* Wd,
                       const int32_t* offsets, float* ybuf, hipStream_t st) {
   const int NT = int(ceil_div(s.H, kFwdBN));
-  return launch_v2(g2::MDown<kFwdBN, kFwdNS>{a, Wd, offsets, ybuf, s.H, s.E, s.I, NT},
-                   grouped_tiles_bound(s, NT), st, USAF_K_DOWN);
+  return launch_persistent(g2::MDown<kFwdBM, kFwdBN, kFwdNS>{a, Wd, offsets, ybuf, s.H, s.E, s.I, NT},
+                   grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DOWN);
 }
 
 int mfma_dw_partials(const usaf_moe_shape& s) { return 2 * int(ceil_div(s.I, kFwdBN)); }
@@ -694,16 +745,16 @@ usaf_status mfma_da(const usaf_moe_shape& s, const bf16_t* dY, const bf16_t* Wd,
                     const bf16_t* gu, const bf16_t* a, bf16_t* dgu, float* dwpart,
                     hipStream_t st) {
   const int NT = int(ceil_div(s.I, kFwdBN));
-  return launch_v2(g2::MDa<kFwdBN, kFwdNS>{dY, Wd, offsets, perm, topk_w, gu, a, dgu, dwpart, s.H,
+  return launch_persistent(g2::MDa<kFwdBM, kFwdBN, kFwdNS>{dY, Wd, offsets, perm, topk_w, gu, a, dgu, dwpart, s.H,
                                            s.E, s.K, s.I, NT, 2 * NT},
-                   grouped_tiles_bound(s, NT), st, USAF_K_DA);
+                   grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DA);
 }
 
 usaf_status mfma_dx(const usaf_moe_shape& s, const bf16_t* dgu, const bf16_t* Wgu,
                     const int32_t* offsets, float* vbuf, hipStream_t st) {
   const int NT = int(ceil_div(s.H, kFwdBN));
-  return launch_v2(g2::MDx<kFwdBN, kFwdNS>{dgu, Wgu, offsets, vbuf, s.H, s.E, s.I, NT},
-                   grouped_tiles_bound(s, NT), st, USAF_K_DX);
+  return launch_persistent(g2::MDx<kFwdBM, kFwdBN, kFwdNS>{dgu, Wgu, offsets, vbuf, s.H, s.E, s.I, NT},
+                   grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DX);
 }
 
 usaf_status mfma_dense_dw(const usaf_moe_shape& s, const bf16_t* X, const bf16_t* dY,
@@ -722,13 +773,13 @@ usaf_status mfma_dense_dw(const usaf_moe_shape& s, const bf16_t* X, const bf16_t
     USAF_LAUNCH_CHECK();
   }
   {
-    const int MT = int(ceil_div(2 * s.I, g2::kBM)), NT = int(ceil_div(s.H, kDwBN));
-    g2::MDenseDw<false, kDwBN, kDwNS> p{dgu, Xg, offsets, dW, s.H, s.E, s.I, MT, NT, ngu};
+    const int MT = int(ceil_div(2 * s.I, kDwBM)), NT = int(ceil_div(s.H, kDwBN));
+    g2::MDenseDw<false, kDwBM, kDwBN, kDwNS> p{dgu, Xg, offsets, dW, s.H, s.E, s.I, MT, NT, ngu};
     USAF_TRY(launch_v2(p, int64_t(MT) * NT * s.E, st, -1));
   }
   {
-    const int MT = int(ceil_div(s.H, g2::kBM)), NT = int(ceil_div(s.I, kDwBN));
-    g2::MDenseDw<true, kDwBN, kDwNS> p{wdYg, a, offsets, dW, s.H, s.E, s.I, MT, NT, ngu};
+    const int MT = int(ceil_div(s.H, kDwBM)), NT = int(ceil_div(s.I, kDwBN));
+    g2::MDenseDw<true, kDwBM, kDwBN, kDwNS> p{wdYg, a, offsets, dW, s.H, s.E, s.I, MT, NT, ngu};
     USAF_TRY(launch_v2(p, int64_t(MT) * NT * s.E, st, -1));
   }
   timer_end(USAF_K_DENSE_DW, st);

@@ -129,6 +129,22 @@ def compare_forward_backward(g, fw, bw, ref_loss, ref_dY, dims):
     return bad_e
 
 
+def check_adam_weights(w_gpu, w_ref, g_ref, w_old):
+    """Weights after one Adam step.  At t = 1 the update is lr * g/(|g| + eps),
+    about lr * sign(g), so where |g| lies within the gradient tolerance of
+    zero the two sides may move the weight in opposite directions: there
+    the bound is |dW| <= 2 lr plus one bf16 rounding of each side.  Elsewhere
+    the usual relative bound applies."""
+    g_ref = np.asarray(g_ref, np.float64)
+    sure = np.abs(g_ref) > TOL_BF16 * np.abs(g_ref).max()
+    err = rel(w_gpu[sure], w_ref[sure])
+    say(f"  W after Adam ({sure.mean():.4f} of entries with a clear gradient sign): {err:.2e}")
+    assert err <= TOL_BF16
+    ulp = np.abs(np.asarray(w_old, np.float64)) * 2.0 ** -7 + 1e-30
+    loose = np.abs(w_gpu[~sure] - w_ref[~sure]) <= 2 * LR * (1 + 1e-3) + 2 * ulp[~sure]
+    assert loose.all()
+
+
 def entries_of_experts(idx, dims, experts):
     """Mask of flat indices that belong to any of ``experts``."""
     T, H, E, K, I = dims
@@ -160,10 +176,9 @@ def test_qwen3_layer_step_full_size(capi):
         err = rel(gv[keep], rv[keep])
         say(f"  {name}: {err:.2e}")
         assert err <= TOL_BF16, name
-    w_new = g["W_at"](idx)
-    err = rel(w_new[keep], ref["W_flat"][idx.astype(np.int64)][keep])
-    say(f"  W[idx] after Adam: {err:.2e}")
-    assert err <= TOL_BF16
+    i64 = idx.astype(np.int64)
+    w_old = np.concatenate([d["W_gu"].ravel(), d["W_d"].ravel()])[i64]
+    check_adam_weights(g["W_at"](idx)[keep], ref["W_flat"][i64][keep], ref["g"][keep], w_old[keep])
     for name in ("Wr", "mr", "vr"):
         assert rel(g[name], ref[name]) <= TOL_BF16, name
     # only listed weights may change
@@ -185,8 +200,10 @@ def test_mixtral_layer_step_full_size(capi):
     lay = g["layer"]
     # masked gradient equals the dense gradient at the listed entries (any size)
     dense = torch.empty(N, dtype=torch.float32, device=DEV)
+    # back to the step's starting weights (Adam has moved W and the router)
     lay.W.copy_(torch.from_numpy(np.concatenate([d["W_gu"].ravel(), d["W_d"].ravel()]))
                 .to(DEV).to(torch.bfloat16))
+    lay.Wr.copy_(torch.from_numpy(d["Wr"]).to(DEV))
     lay.dense_scan(out=dense)
     torch.cuda.synchronize()
     dense_at = npf(dense[torch.from_numpy(idx.astype(np.int64)).to(DEV)])
@@ -212,11 +229,11 @@ def test_mixtral_layer_step_full_size(capi):
     flat_at = np.concatenate([d["W_gu"].ravel(), d["W_d"].ravel()])[sample.astype(np.int64)]
     zs = np.zeros(sample.size)
     w_ref, m_ref, v_ref = O.adam_update(flat_at, ref_g, zs, zs, 1, LR, 0.9, 0.999, 1e-8, O.BF16, R)
-    for name, gv, rv in (("m", g["m"][pick], m_ref), ("v", g["v"][pick], v_ref),
-                         ("W", g["W_at"](sample), w_ref)):
+    for name, gv, rv in (("m", g["m"][pick], m_ref), ("v", g["v"][pick], v_ref)):
         err = rel(gv, rv)
         say(f"  {name} sample: {err:.2e}")
         assert err <= TOL_BF16, name
+    check_adam_weights(g["W_at"](sample), w_ref, ref_g, flat_at)
     assert np.isin(g["changed"], idx.astype(np.int64)).all()
 
 
@@ -283,48 +300,101 @@ def test_scan_dense_gradient_and_selection_full_size(capi):
         err = rel(g_host, ref["g"])
     say(f"  dense gradient: {err:.2e}")
     assert err <= TOL_BF16
-    sel_ref = O.importance_topk(ref["g"], k)
-    overlap = np.intersect1d(sel_gpu, sel_ref, assume_unique=True).size / k
+    # the oracle's top-k of its own gradient, from its k-th key: entries of
+    # larger fp32 |g|, then ties by lowest index
+    bits = np.abs(ref["g"].astype(np.float32)).view(np.uint32)
+    kth = np.partition(bits, bits.size - k)[bits.size - k]
+    n_gt = int(np.count_nonzero(bits > kth))
+    tie_idx = np.nonzero(bits == kth)[0][: k - n_gt]
+    cut = tie_idx[-1] if tie_idx.size else -1
+    sg = sel_gpu.astype(np.int64)
+    inside = (bits[sg] > kth) | ((bits[sg] == kth) & (sg <= cut))
+    overlap = np.count_nonzero(inside) / k
     say(f"  self-computed selection overlap {overlap:.5f}")
     assert overlap >= 0.999
 
 
-def test_topk_and_rigl_exact_full_size(capi):
-    from sparse_fine_tuning_amd.layer import topk
+def topk_set_is_exact(g, sel, k):
+    """sel (ascending u32) is the top-k of |g| under (|g| desc, index asc):
+    exactly k distinct ascending indices, and every selected entry ranks
+    above every unselected one.  Ranking is unique, so this fixes the set."""
+    sel = np.asarray(sel, np.int64)
+    assert sel.size == k and np.all(np.diff(sel) > 0)
+    bits = np.abs(np.asarray(g, np.float32)).view(np.uint32)
+    mask = np.zeros(bits.size, dtype=bool)
+    mask[sel] = True
+    sb = bits[sel]
+    lo = sb.min()
+    lo_idx = sel[sb == lo].max()            # lowest-ranked selected entry
+    ub = bits[~mask]
+    if ub.size == 0:
+        return
+    hi = ub.max()
+    hi_idx = np.nonzero(~mask & (bits == hi))[0].min()  # highest-ranked unselected entry
+    assert (lo > hi) or (lo == hi and lo_idx < hi_idx), "selection is not the top-k"
+
+
+def test_topk_and_rigl_full_size(capi):
+    """Global top-k and RigL at N = 603,979,776 on a seeded gradient, checked
+    by the properties that define them (the oracle's own functions are run
+    against the kernels at smaller sizes)."""
+    from sparse_fine_tuning_amd.layer import SparseMoELayer, rigl, topk
     dims = (4096, 2048, 128, 8, 768)
     T, H, E, K, I = dims
     N = 3 * E * H * I
     k = O.select_count(N, 5, 1000)
     r = (3 * k) // 10
     say(f"top-k and RigL at N={N}, k={k}, r={r}")
-    d = synth.moe_layer(*dims, bf16=True, seeds=(0, 1, 2, 3, 4))
-    w_flat = np.concatenate([d["W_gu"].ravel(), d["W_d"].ravel()])
-    del d
-    # an identical seeded gradient for both sides, at the scan's magnitude
+    w_flat = synth.to_bf16_values(synth.normal((N,), 0.02, 33))
     grad = synth.normal((N,), 1e-6, 30)
     S_old = synth.random_mask(N, k, 5)
     m_old = synth.normal((k,), 1e-7, 31)
     v_old = np.abs(synth.normal((k,), 1e-13, 32))
     g_dev = torch.from_numpy(grad).to(DEV)
     sel = topk(g_dev, k).cpu().numpy().view(np.uint32)
-    from sparse_fine_tuning_amd.layer import SparseMoELayer, rigl
+    say("  top-k properties")
+    topk_set_is_exact(grad, sel, k)
     lay = SparseMoELayer(8, H, E, K, I, act=capi.BF16, device=DEV)
     lay.W = torch.from_numpy(w_flat).to(DEV).to(torch.bfloat16)
     lay.set_active(S_old)
     lay.m.copy_(torch.from_numpy(m_old))
-    lay.v.copy_(torch.from_numpy(v_old.astype(np.float32)))
+    lay.v.copy_(torch.from_numpy(v_old))
     stats = rigl(lay, g_dev, r).cpu().numpy()
-    S_new = lay.idx.cpu().numpy().view(np.uint32)
+    S_new = lay.idx.cpu().numpy().view(np.uint32).astype(np.int64)
     m_new, v_new = lay.m.cpu().numpy(), lay.v.cpu().numpy()
     del lay, g_dev
     torch.cuda.empty_cache()
-    say("  oracle top-k")
-    ref_sel = O.importance_topk(grad, k)
-    assert np.array_equal(sel, ref_sel), "top-k set differs"
-    say("  oracle RigL")
-    ref = O.rigl_reselect(grad, w_flat, S_old, m_old, v_old, k, r)
-    assert np.array_equal(S_new, ref["S_new"]), "RigL set differs"
-    assert np.array_equal(m_new.astype(np.float64), ref["m"])
-    assert np.array_equal(v_new.astype(np.float64), ref["v"].astype(np.float32).astype(np.float64))
-    assert int(stats[0]) == ref["n_drop"] and int(stats[1]) == ref["n_grow"]
-    assert int(stats[2]) == ref["topk_new_vs_old"]
+    say("  RigL properties")
+    S_old64 = S_old.astype(np.int64)
+    assert S_new.size == k and np.all(np.diff(S_new) > 0)
+    kept = np.intersect1d(S_new, S_old64, assume_unique=True)
+    dropped = np.setdiff1d(S_old64, kept, assume_unique=True)
+    grown = np.setdiff1d(S_new, kept, assume_unique=True)
+    assert dropped.size == r and grown.size == r
+    # drop: the r active entries of smallest |w| (ties: lowest index)
+    wb = np.abs(w_flat.astype(np.float32)).view(np.uint32)
+    dk = wb[dropped].max()
+    dk_idx = dropped[wb[dropped] == dk].max()
+    kk = wb[kept].min()
+    kk_idx = kept[wb[kept] == kk].min()
+    assert dk < kk or (dk == kk and dk_idx < kk_idx), "drop set is not the r smallest |w|"
+    # grow: the top-r of |g| outside S_old
+    gb = np.abs(grad).view(np.uint32)
+    outside = np.ones(N, dtype=bool)
+    outside[S_old64] = False
+    outside[grown] = False
+    lo = gb[grown].min()
+    lo_idx = grown[gb[grown] == lo].max()
+    hi = gb[outside].max()
+    hi_idx = np.nonzero(outside & (gb == hi))[0].min()
+    assert lo > hi or (lo == hi and lo_idx < hi_idx), "grow set is not the top-r outside S_old"
+    # moments: kept entries carry theirs, grown entries start at zero
+    pos_old = np.searchsorted(S_old64, kept)
+    pos_new = np.searchsorted(S_new, kept)
+    assert np.array_equal(m_new[pos_new], m_old[pos_old])
+    assert np.array_equal(v_new[pos_new], v_old[pos_old])
+    pos_g = np.searchsorted(S_new, grown)
+    assert not m_new[pos_g].any() and not v_new[pos_g].any()
+    assert int(stats[0]) == r and int(stats[1]) == r
+    novelty = np.setdiff1d(sel.astype(np.int64), S_old64, assume_unique=True).size
+    assert int(stats[2]) == novelty
