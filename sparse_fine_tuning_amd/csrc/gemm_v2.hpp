@@ -1,7 +1,7 @@
 // bf16 MFMA grouped GEMM for gfx950 with direct global->LDS staging.
 //
-// Block tile BM x BN x 64 (BM, BN = 128 or 256), 256 threads = 4 waves in a
-// 2 x 2 grid; each wave computes BM/2 x BN/2 with v_mfma_f32_32x32x16_bf16
+// Block tile BM x BN x 64, WM x WN waves (4 or 8); each wave computes
+// BM/WM x BN/WN with v_mfma_f32_32x32x16_bf16
 // (fp32 accumulate).  Operand tiles are copied straight from global memory
 // into an NS-deep ring of LDS stages with 16-byte global_load_lds_dwordx4
 // (no register staging), so the loads of stages kt+1 .. kt+NS-1 are in flight
@@ -28,7 +28,7 @@
 // instruction's first operand), so each lane's accumulator holds one row of
 // the tile and runs of 4 consecutive columns: for block (i, j), lane l and
 // element r = 4 g + e:
-//   row = wm*BM/2 + 32 i + (l % 32),  col = wn*BN/2 + 32 j + 8 g + 4 (l / 32) + e.
+//   row = wm*RW + 32 i + (l % 32),  col = wn*CW + 32 j + 8 g + 4 (l / 32) + e.
 // Epilogues therefore read and write 4-column vectors per lane.
 #pragma once
 
@@ -129,12 +129,13 @@ __device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ offsets
   return true;
 }
 
-__device__ __forceinline__ int out_row(int BM, int wm, int i, int lane) {
-  return wm * (BM / 2) + 32 * i + (lane & 31);
+// RW / CW: rows / columns of the tile held by one wave
+__device__ __forceinline__ int out_row(int RW, int wm, int i, int lane) {
+  return wm * RW + 32 * i + (lane & 31);
 }
 // first of the 4 consecutive columns of group g of block j
-__device__ __forceinline__ int out_col(int BN, int wn, int j, int g, int lane) {
-  return wn * (BN / 2) + 32 * j + 8 * g + 4 * (lane >> 5);
+__device__ __forceinline__ int out_col(int CW, int wn, int j, int g, int lane) {
+  return wn * CW + 32 * j + 8 * g + 4 * (lane >> 5);
 }
 
 // ---------------------------------------------------------------------------
@@ -143,9 +144,10 @@ __device__ __forceinline__ int out_col(int BN, int wn, int j, int g, int lane) {
 // kptr(k) (element (row 0, k); k < kend, always valid) and ncols (valid rows,
 // a multiple of 8).
 // ---------------------------------------------------------------------------
-template <int R>
+template <int R, int NW = 4>
 struct KMajor {
-  static constexpr int kInst = R / 32;  // dma instructions per wave per stage
+  static constexpr int kRW = R / NW;     // rows copied by one wave
+  static constexpr int kInst = kRW / 8;  // dma instructions per wave per stage
   static constexpr int kBytes = R * 128;
   // slot of 16-byte chunk q in row r: 64 banks serve 16 lanes of a 16-byte
   // read together, i.e. 16 consecutive rows; rows r and r+1 share a 256-byte
@@ -159,7 +161,7 @@ struct KMajor {
     kend = kend_;
 #pragma unroll
     for (int i = 0; i < kInst; ++i) {
-      const int r = w * (R / 4) + 8 * i + (lane >> 3);
+      const int r = w * kRW + 8 * i + (lane >> 3);
       chunk[i] = (lane & 7) ^ sw(r);
       p[i] = s.row(r) + 8 * chunk[i];
     }
@@ -174,12 +176,12 @@ struct KMajor {
       // chunk instead; it is zeroed before use
       const int over = k0 + 8 * chunk[i] + 8 - kend;
       const int koff = over > 0 ? k0 - over : k0;
-      dma16(p[i] + koff, lds + (w * (R / 4) + 8 * i) * 128);
+      dma16(p[i] + koff, lds + (w * kRW + 8 * i) * 128);
     }
   }
   // zero k >= kvalid (kvalid a multiple of 8) in a stage
   __device__ __forceinline__ static void zero_tail(unsigned char* lds, int kvalid, int tid) {
-    for (int x = tid; x < R * 8; x += 256) {
+    for (int x = tid; x < R * 8; x += 64 * NW) {
       const int r = x >> 3, q = x & 7;
       if (8 * q >= kvalid)
         *reinterpret_cast<uint4*>(lds + r * 128 + 16 * (q ^ sw(r))) = make_uint4(0, 0, 0, 0);
@@ -193,11 +195,11 @@ struct KMajor {
   }
 };
 
-template <int R>
+template <int R, int NW = 4>
 struct MNMajor {
   static constexpr int kCPR = R / 8;         // 16-byte chunks per k-row
   static constexpr int kKPI = 64 / kCPR;     // k-rows per dma instruction
-  static constexpr int kInst = kCPR / 4;     // dma instructions per wave per stage
+  static constexpr int kInst = kCPR / NW;    // dma instructions per wave per stage
   static constexpr int kBytes = kBK * R * 2;
   int kend, slot, last, krow0;
   template <class Src>
@@ -218,7 +220,7 @@ struct MNMajor {
     }
   }
   __device__ __forceinline__ static void zero_tail(unsigned char* lds, int kvalid, int tid) {
-    for (int x = tid + kvalid * kCPR; x < kBK * kCPR; x += 256)
+    for (int x = tid + kvalid * kCPR; x < kBK * kCPR; x += 64 * NW)
       *reinterpret_cast<uint4*>(lds + x * 16) = make_uint4(0, 0, 0, 0);
   }
   // fragment rows base..base+31 (the contiguous dimension), k-substep kc
@@ -260,7 +262,7 @@ __device__ __forceinline__ void stage_f32(unsigned char* region, const f32x16_t 
                                           St&& st) {
   constexpr int kPitch = 32 * NJ * 4 + 16;  // bytes per staged row
   const int r = lane & 31, h = lane >> 5;
-  if (region == nullptr) {
+  if (NJ != 4 || region == nullptr) {  // staging needs 128 columns = 32 lanes x 4
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -276,7 +278,6 @@ __device__ __forceinline__ void stage_f32(unsigned char* region, const f32x16_t 
       *reinterpret_cast<float4*>(region + r * kPitch + 4 * (32 * j + 8 * g + 4 * h)) =
           make_float4(accr[j][4 * g], accr[j][4 * g + 1], accr[j][4 * g + 2], accr[j][4 * g + 3]);
   wave_lds_sync();
-  static_assert(NJ == 4, "row-major read assumes 128 columns = 32 lanes x 4");
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int row = 2 * q + h;
@@ -308,22 +309,22 @@ struct StageBf16 {
 
 // ---------------------------------------------------------------------------
 // The kernel.  P supplies
-//   static constexpr int BM, BN, NS; types AOp, BOp (KMajor<BM> / MNMajor<BM>,
-//   KMajor<BN> / MNMajor<BN>)
+//   static constexpr int BM, BN, NS, WM, WN (wave grid), NTHR = 64 WM WN,
+//   RW = BM/WM, CW = BN/WN, IM = RW/32, NJ = CW/32; types AOp, BOp
+//   (KMajor<BM, NW> / MNMajor<BM, NW>, KMajor<BN, NW> / MNMajor<BN, NW>)
 //   bool tile(int L, MTile&)      (uniform per block; contraction [0, t.ke))
 //   a_src(t), b_src(t): row(r) for a k-major operand, kptr(k) + ncols for an
 //   mn-major one
-//   void epilogue(const MTile&, f32x16_t (&acc)[BM/64][BN/64], int wm, int wn, int lane,
+//   void epilogue(const MTile&, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
 //                 unsigned char* stage)   (stage: kStageBytes of LDS private to the wave)
-// Each wave computes (BM/2) x (BN/2).  Row blocks of 32 past the tile's valid
-// rows (ragged expert groups) issue no MFMA.
+// Each wave computes RW x CW.
 // ---------------------------------------------------------------------------
 template <class P, int VB, int IM, int NJ, class AOp, class BOp, class AS, class BS>
 __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS& as, const BS& bs,
                                           unsigned char (*lds)[AOp::kBytes + BOp::kBytes], int K,
                                           int nk, int tid, int w, int wm, int wn, int lane,
                                           f32x16_t (&acc)[IM][NJ]) {
-  constexpr int BM = P::BM, BN = P::BN, NS = P::NS;
+  constexpr int NS = P::NS, RW = P::RW, CW = P::CW;
   constexpr int A_BYTES = AOp::kBytes;
   constexpr int NLOAD = AOp::kInst + BOp::kInst;
   for (int kt = 0; kt < nk; ++kt) {
@@ -347,17 +348,17 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
       // fragments of substep kc+1 are read while the MFMAs of kc run
       bf16x8_t af[2][VB], bfr[2][NJ];
 #pragma unroll
-      for (int i = 0; i < VB; ++i) af[0][i] = AOp::frag(As, wm * (BM / 2) + 32 * i, 0, lane);
+      for (int i = 0; i < VB; ++i) af[0][i] = AOp::frag(As, wm * RW + 32 * i, 0, lane);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) bfr[0][j] = BOp::frag(Bs, wn * (BN / 2) + 32 * j, 0, lane);
+      for (int j = 0; j < NJ; ++j) bfr[0][j] = BOp::frag(Bs, wn * CW + 32 * j, 0, lane);
 #pragma unroll
       for (int kc = 0; kc < kBK / 16; ++kc) {
         const int c = kc & 1, n = c ^ 1;
         if (kc + 1 < kBK / 16) {
 #pragma unroll
-          for (int i = 0; i < VB; ++i) af[n][i] = AOp::frag(As, wm * (BM / 2) + 32 * i, kc + 1, lane);
+          for (int i = 0; i < VB; ++i) af[n][i] = AOp::frag(As, wm * RW + 32 * i, kc + 1, lane);
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) bfr[n][j] = BOp::frag(Bs, wn * (BN / 2) + 32 * j, kc + 1, lane);
+          for (int j = 0; j < NJ; ++j) bfr[n][j] = BOp::frag(Bs, wn * CW + 32 * j, kc + 1, lane);
         }
 #pragma unroll
         for (int i = 0; i < VB; ++i)
@@ -370,8 +371,8 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
 }
 
 template <class P>
-__global__ __launch_bounds__(256) void gemm2_kernel(P p) {
-  constexpr int BM = P::BM, BN = P::BN, NS = P::NS, IM = BM / 64, NJ = BN / 64;
+__global__ __launch_bounds__(P::NTHR) void gemm2_kernel(P p) {
+  constexpr int NS = P::NS, IM = P::IM, NJ = P::NJ;
   using AOp = typename P::AOp;
   using BOp = typename P::BOp;
   constexpr int A_BYTES = AOp::kBytes, B_BYTES = BOp::kBytes;
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(P p) {
   if (!p.tile(xcd_remap_blocks(blockIdx.x, gridDim.x), t)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / P::WN, wn = w % P::WN;
   const int K = t.ke;  // contraction range [0, ke)
   const auto as = p.a_src(t);
   const auto bs = p.b_src(t);
@@ -415,8 +416,8 @@ __global__ __launch_bounds__(256) void gemm2_kernel(P p) {
 // the current tile's epilogue stores.  Epilogues get no LDS staging area
 // here (the ring holds the next tile's stages).
 template <class P>
-__global__ __launch_bounds__(256) void gemm2_persistent(P p) {
-  constexpr int BM = P::BM, BN = P::BN, NS = P::NS, IM = BM / 64, NJ = BN / 64;
+__global__ __launch_bounds__(P::NTHR) void gemm2_persistent(P p) {
+  constexpr int NS = P::NS, IM = P::IM, NJ = P::NJ;
   using AOp = typename P::AOp;
   using BOp = typename P::BOp;
   constexpr int A_BYTES = AOp::kBytes, B_BYTES = BOp::kBytes;
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(256) void gemm2_persistent(P p) {
   if (!p.tile(L, t)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / P::WN, wn = w % P::WN;
   auto as = p.a_src(t);
   auto bs = p.b_src(t);
   AOp ao;

@@ -57,7 +57,7 @@ struct WsBackward {
 inline WsBackward ws_backward(const usaf_moe_shape& s) {
   WsBackward L;
   const size_t S = size_t(s.T) * s.K;
-  L.nt = 2 * ((s.I + 127) / 128);  // >= ceil(I/64): enough for either GEMM path
+  L.nt = 4 * ((s.I + 127) / 128);  // >= ceil(I/64) and >= WN * ceil(I/BN) for WN <= 4, BN >= 128
   L.vbuf = 0;
   L.dwpart = align256(S * s.H * 4);
   L.dl = L.dwpart + align256(S * L.nt * 4);

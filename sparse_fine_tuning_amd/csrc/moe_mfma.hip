@@ -340,24 +340,25 @@ struct StridedKC {
   const bf16_t* base; int64_t ld; int ncols;
   __device__ __forceinline__ const bf16_t* kptr(int k) const { return base + int64_t(k) * ld; }
 };
-// gate_up weight rows for a tile of BN columns holding BN/2 features: wave
-// column-half wn holds features F0 + (BN/4) wn + [0, BN/4); its 32-column
-// blocks alternate gate, up, gate, up over consecutive 32-feature groups.
-template <int BN>
+// gate_up weight rows for a tile holding half as many features as columns:
+// wave column wn (CW columns) holds features F0 + (CW/2) wn + [0, CW/2); its
+// 32-column blocks alternate gate, up, gate, up over 32-feature groups.
+template <int CW>
 struct GateUpRowsC {
   const bf16_t* We; int F0; int I; int64_t H;
   __device__ __forceinline__ const bf16_t* row(int c) const {
-    const int wn = c / (BN / 2), j = (c % (BN / 2)) >> 5;
-    const int f = min(F0 + (BN / 4) * wn + 32 * (j >> 1) + (c & 31), I - 1);
+    const int wn = c / CW, j = (c % CW) >> 5;
+    const int f = min(F0 + (CW / 2) * wn + 32 * (j >> 1) + (c & 31), I - 1);
     return We + int64_t((j & 1) ? I + f : f) * H;
   }
 };
 
-template <int BM_, int BN_, int NS_>
+template <int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2>
 struct MGateUp {
-  static constexpr int BM = BM_, BN = BN_, NS = NS_, IM = BM_ / 64, NJ = BN_ / 64;
-  using AOp = KMajor<BM>;
-  using BOp = KMajor<BN>;
+  static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
+  static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
+  using AOp = KMajor<BM, WM_ * WN_>;
+  using BOp = KMajor<BN, WM_ * WN_>;
   const bf16_t* X; const bf16_t* Wgu; const int32_t* offsets; const int32_t* perm;
   bf16_t* gu; bf16_t* a;
   int H, E, K, I, NT;
@@ -367,24 +368,24 @@ struct MGateUp {
     return true;
   }
   __device__ __forceinline__ TokRowsC a_src(const MTile& t) const { return TokRowsC{X, perm, K, t.off + t.m0, t.mc, H}; }
-  __device__ __forceinline__ GateUpRowsC<BN> b_src(const MTile& t) const {
-    return GateUpRowsC<BN>{Wgu + int64_t(t.e) * 2 * I * H, t.n0, I, H};
+  __device__ __forceinline__ GateUpRowsC<CW> b_src(const MTile& t) const {
+    return GateUpRowsC<CW>{Wgu + int64_t(t.e) * 2 * I * H, t.n0, I, H};
   }
   static constexpr int kStageBytes = 3 * 32 * StageBf16<64>::kPitch;
   __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
                                            unsigned char* stage) const {
-    static_assert(NJ == 4, "a wave covers 64 features: gate / up blocks of 32, twice");
+    static_assert(NJ % 2 == 0, "gate / up blocks of 32 features alternate");
     unsigned char* sg = stage;
     unsigned char* su = stage + 32 * StageBf16<64>::kPitch;
     unsigned char* sa = stage + 2 * 32 * StageBf16<64>::kPitch;
-    const int F = t.n0 + (BN / 4) * wn;  // first feature of this wave
+    const int F = t.n0 + (CW / 2) * wn;  // first feature of this wave
     static_for<IM>([&](auto I_) {
       constexpr int i = decltype(I_)::value;
-      const int rb = wm * (BM / 2) + 32 * i;
+      const int rb = wm * RW + 32 * i;
       if (rb >= t.mc) return;
       const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-      for (int jp = 0; jp < 2; ++jp)
+      for (int jp = 0; jp < NJ / 2; ++jp)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           uint32_t gw[2], uw[2], aw[2];
@@ -427,11 +428,12 @@ struct MGateUp {
   }
 };
 
-template <int BM_, int BN_, int NS_>
+template <int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2>
 struct MDown {
-  static constexpr int BM = BM_, BN = BN_, NS = NS_, IM = BM_ / 64, NJ = BN_ / 64;
-  using AOp = KMajor<BM>;
-  using BOp = KMajor<BN>;
+  static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
+  static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
+  using AOp = KMajor<BM, WM_ * WN_>;
+  using BOp = KMajor<BN, WM_ * WN_>;
   const bf16_t* a; const bf16_t* Wd; const int32_t* offsets; float* ybuf;
   int H, E, I, NT;
   __device__ __forceinline__ bool tile(int L, MTile& t) const {
@@ -450,10 +452,10 @@ struct MDown {
                                            unsigned char* stage) const {
     static_for<IM>([&](auto I_) {
       constexpr int i = decltype(I_)::value;
-      const int rb = wm * (BM / 2) + 32 * i;
+      const int rb = wm * RW + 32 * i;
       if (rb >= t.mc) return;
-      const int ncw = t.nc - wn * (BN / 2);
-      float* base = ybuf + int64_t(t.off + t.m0 + rb) * H + t.n0 + wn * (BN / 2);
+      const int ncw = t.nc - wn * CW;
+      float* base = ybuf + int64_t(t.off + t.m0 + rb) * H + t.n0 + wn * CW;
       const int64_t ld = H;
       stage_f32<NJ>(stage, acc[i], lane, [&](int row, int col, float4 v) {
         if (rb + row < t.mc && col < ncw) *reinterpret_cast<float4*>(base + row * ld + col) = v;
@@ -462,11 +464,12 @@ struct MDown {
   }
 };
 
-template <int BM_, int BN_, int NS_>
+template <int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2>
 struct MDa {
-  static constexpr int BM = BM_, BN = BN_, NS = NS_, IM = BM_ / 64, NJ = BN_ / 64;
-  using AOp = KMajor<BM>;
-  using BOp = MNMajor<BN>;
+  static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
+  static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
+  using AOp = KMajor<BM, WM_ * WN_>;
+  using BOp = MNMajor<BN, WM_ * WN_>;
   const bf16_t* dY; const bf16_t* Wd; const int32_t* offsets; const int32_t* perm;
   const float* topk_w; const bf16_t* gu; const bf16_t* a; bf16_t* dgu; float* dwpart;
   int H, E, K, I, NT, NTP;
@@ -484,7 +487,7 @@ struct MDa {
                                            unsigned char*) const {
     static_for<IM>([&](auto I_) {
       constexpr int i = decltype(I_)::value;
-      const int row = out_row(BM, wm, i, lane);
+      const int row = out_row(RW, wm, i, lane);
       const bool vrow = row < t.mc;
       const int64_t p = t.off + t.m0 + (vrow ? row : 0);
       const float wt = topk_w[perm[p]];
@@ -493,7 +496,7 @@ struct MDa {
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int col = out_col(BN, wn, j, g, lane);
+          const int col = out_col(CW, wn, j, g, lane);
           if (!vrow || col >= t.nc) continue;
           const int f = t.n0 + col;
           const uint2 av = *reinterpret_cast<const uint2*>(a + p * I + f);
@@ -524,16 +527,17 @@ struct MDa {
         }
       // lanes l and l + 32 hold the same row
       part += __shfl_xor(part, 32, 64);
-      if (lane < 32 && vrow) dwpart[p * NTP + 2 * t.nt + wn] = part;
+      if (lane < 32 && vrow) dwpart[p * NTP + WN * t.nt + wn] = part;
     });
   }
 };
 
-template <int BM_, int BN_, int NS_>
+template <int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2>
 struct MDx {
-  static constexpr int BM = BM_, BN = BN_, NS = NS_, IM = BM_ / 64, NJ = BN_ / 64;
-  using AOp = KMajor<BM>;
-  using BOp = MNMajor<BN>;
+  static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
+  static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
+  using AOp = KMajor<BM, WM_ * WN_>;
+  using BOp = MNMajor<BN, WM_ * WN_>;
   const bf16_t* dgu; const bf16_t* Wgu; const int32_t* offsets; float* vbuf;
   int H, E, I, NT;
   __device__ __forceinline__ bool tile(int L, MTile& t) const {
@@ -552,10 +556,10 @@ struct MDx {
                                            unsigned char* stage) const {
     static_for<IM>([&](auto I_) {
       constexpr int i = decltype(I_)::value;
-      const int rb = wm * (BM / 2) + 32 * i;
+      const int rb = wm * RW + 32 * i;
       if (rb >= t.mc) return;
-      const int ncw = t.nc - wn * (BN / 2);
-      float* base = vbuf + int64_t(t.off + t.m0 + rb) * H + t.n0 + wn * (BN / 2);
+      const int ncw = t.nc - wn * CW;
+      float* base = vbuf + int64_t(t.off + t.m0 + rb) * H + t.n0 + wn * CW;
       const int64_t ld = H;
       stage_f32<NJ>(stage, acc[i], lane, [&](int row, int col, float4 v) {
         if (rb + row < t.mc && col < ncw) *reinterpret_cast<float4*>(base + row * ld + col) = v;
@@ -569,11 +573,12 @@ struct MDx {
 //   gate_up: dW[r, c] = sum_p dGU[p, r] Xg[p, c]    (rows 2I, cols H)
 //   down:    dW[r, c] = sum_p wdYg[p, r] a[p, c]    (rows H,  cols I)
 // Xg = X gathered by token and wdYg = bf16(w_p dY[tok(p)]) are staged first.
-template <bool kDown, int BM_, int BN_, int NS_>
+template <bool kDown, int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2>
 struct MDenseDw {
-  static constexpr int BM = BM_, BN = BN_, NS = NS_, IM = BM_ / 64, NJ = BN_ / 64;
-  using AOp = MNMajor<BM>;
-  using BOp = MNMajor<BN>;
+  static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
+  static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
+  using AOp = MNMajor<BM, WM_ * WN_>;
+  using BOp = MNMajor<BN, WM_ * WN_>;
   const bf16_t* L; const bf16_t* R; const int32_t* offsets; float* dW;
   int H, E, I, MT, NT;
   int64_t ngu;
@@ -609,10 +614,10 @@ struct MDenseDw {
     const int ldo = cols_total();
     static_for<IM>([&](auto I_) {
       constexpr int i = decltype(I_)::value;
-      const int rb = wm * (BM / 2) + 32 * i;
+      const int rb = wm * RW + 32 * i;
       if (rb >= t.mc) return;
-      const int ncw = t.nc - wn * (BN / 2);
-      float* base = dW + obase + int64_t(t.m0 + rb) * ldo + t.n0 + wn * (BN / 2);
+      const int ncw = t.nc - wn * CW;
+      float* base = dW + obase + int64_t(t.m0 + rb) * ldo + t.n0 + wn * CW;
       const int64_t ld = ldo;
       stage_f32<NJ>(stage, acc[i], lane, [&](int row, int col, float4 v) {
         if (rb + row < t.mc && col < ncw) *reinterpret_cast<float4*>(base + row * ld + col) = v;
@@ -672,7 +677,7 @@ static usaf_status launch_v2(const P& p, int64_t tiles, hipStream_t st, int kcla
   const int64_t blocks = (tiles + 7) / 8 * 8;
   if (blocks >= (int64_t(1) << 31)) return USAF_ERR_UNSUPPORTED;
   timer_begin(kclass, st);
-  hipLaunchKernelGGL(g2::gemm2_kernel<P>, dim3(unsigned(blocks)), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(g2::gemm2_kernel<P>, dim3(unsigned(blocks)), dim3(P::NTHR), 0, st, p);
   timer_end(kclass, st);
   USAF_LAUNCH_CHECK();
   return USAF_OK;
@@ -701,7 +706,7 @@ static usaf_status launch_persistent(const P& p, int64_t tiles, hipStream_t st, 
   if (blocks > tiles) blocks = tiles;
   blocks = (blocks + 7) / 8 * 8;
   timer_begin(kclass, st);
-  hipLaunchKernelGGL(g2::gemm2_persistent<P>, dim3(unsigned(blocks)), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(g2::gemm2_persistent<P>, dim3(unsigned(blocks)), dim3(P::NTHR), 0, st, p);
   timer_end(kclass, st);
   USAF_LAUNCH_CHECK();
   return USAF_OK;
@@ -721,39 +726,41 @@ usaf_status mfma_router(const usaf_moe_shape& s, const bf16_t* X, const float* W
 
 // Tile shapes and LDS ring depths of the direct-to-LDS GEMMs.
 constexpr int kFwdBM = 128, kFwdBN = 256, kFwdNS = 3;  // gate_up, down, dA, dX: 144 KiB LDS
+constexpr int kFwdWM = 2, kFwdWN = 4;                  // 8 waves: 2 per SIMD
+constexpr int kDaWN = 2;                               // dA: 4 waves (its epilogue prefers them)
 constexpr int kDwBM = 256, kDwBN = 256, kDwNS = 2;     // dense dW: 128 KiB LDS
 
 usaf_status mfma_gate_up(const usaf_moe_shape& s, const bf16_t* X, const bf16_t* Wgu,
                          const int32_t* offsets, const int32_t* perm, bf16_t* gu, bf16_t* a,
                          hipStream_t st) {
   const int NT = int(ceil_div(s.I, kFwdBN / 2));
-  return launch_persistent(g2::MGateUp<kFwdBM, kFwdBN, kFwdNS>{X, Wgu, offsets, perm, gu, a, s.H, s.E, s.K, s.I, NT},
+  return launch_persistent(g2::MGateUp<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN>{X, Wgu, offsets, perm, gu, a, s.H, s.E, s.K, s.I, NT},
                    grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_GATE_UP);
 }
 
 usaf_status mfma_down(const usaf_moe_shape& s, const bf16_t* a, const bf16_t* Wd,
                       const int32_t* offsets, float* ybuf, hipStream_t st) {
   const int NT = int(ceil_div(s.H, kFwdBN));
-  return launch_persistent(g2::MDown<kFwdBM, kFwdBN, kFwdNS>{a, Wd, offsets, ybuf, s.H, s.E, s.I, NT},
+  return launch_persistent(g2::MDown<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN>{a, Wd, offsets, ybuf, s.H, s.E, s.I, NT},
                    grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DOWN);
 }
 
-int mfma_dw_partials(const usaf_moe_shape& s) { return 2 * int(ceil_div(s.I, kFwdBN)); }
+int mfma_dw_partials(const usaf_moe_shape& s) { return kDaWN * int(ceil_div(s.I, kFwdBN)); }
 
 usaf_status mfma_da(const usaf_moe_shape& s, const bf16_t* dY, const bf16_t* Wd,
                     const int32_t* offsets, const int32_t* perm, const float* topk_w,
                     const bf16_t* gu, const bf16_t* a, bf16_t* dgu, float* dwpart,
                     hipStream_t st) {
   const int NT = int(ceil_div(s.I, kFwdBN));
-  return launch_persistent(g2::MDa<kFwdBM, kFwdBN, kFwdNS>{dY, Wd, offsets, perm, topk_w, gu, a, dgu, dwpart, s.H,
-                                           s.E, s.K, s.I, NT, 2 * NT},
+  return launch_persistent(g2::MDa<kFwdBM, kFwdBN, kFwdNS, 2, kDaWN>{dY, Wd, offsets, perm, topk_w, gu, a, dgu, dwpart, s.H,
+                                           s.E, s.K, s.I, NT, kDaWN * NT},
                    grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DA);
 }
 
 usaf_status mfma_dx(const usaf_moe_shape& s, const bf16_t* dgu, const bf16_t* Wgu,
                     const int32_t* offsets, float* vbuf, hipStream_t st) {
   const int NT = int(ceil_div(s.H, kFwdBN));
-  return launch_persistent(g2::MDx<kFwdBM, kFwdBN, kFwdNS>{dgu, Wgu, offsets, vbuf, s.H, s.E, s.I, NT},
+  return launch_persistent(g2::MDx<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN>{dgu, Wgu, offsets, vbuf, s.H, s.E, s.I, NT},
                    grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DX);
 }
 
