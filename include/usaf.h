@@ -192,12 +192,24 @@ USAF_API usaf_status usaf_rigl_reselect(const usaf_moe_shape *shape, const float
  * by 1.3e-5 relative).  skip_if_nonzero (nullable, device int32):
  * when it holds a non-zero value the kernel changes nothing (the NaN-step
  * skip of the README's results table); the caller then does not advance its
- * step counter.  idx entries must be distinct.  Errors: INVALID_ARG for
- * n < 0, step < 1, null W/g/m/v. */
+ * step counter.  idx entries must be distinct.
+ * w_list (nullable, w_dtype, [n]): a compact copy of W[idx[i]].  When given
+ * (idx must be too) the weights are read from w_list[i] instead of the
+ * scattered W[idx[i]] and written to both, so the list stays equal to W at
+ * idx; build it with usaf_gather and rebuild it after the list changes.
+ * Errors: INVALID_ARG for n < 0, step < 1, null W/g/m/v, w_list without idx. */
 USAF_API usaf_status usaf_sparse_adam(int32_t w_dtype, void *W, const uint32_t *idx, int64_t n,
-                             const float *g, float *m, float *v, int64_t step, double lr,
-                             double beta1, double beta2, double eps,
+                             void *w_list, const float *g, float *m, float *v, int64_t step,
+                             double lr, double beta1, double beta2, double eps,
                              const int32_t *skip_if_nonzero, hipStream_t stream);
+
+/* out[i] = W[idx[i]] for i < n (w_dtype elements): the compact weight list
+ * of usaf_sparse_adam.  Errors: INVALID_ARG for n < 0 or null pointers with
+ * n > 0, or an unknown w_dtype. */
+USAF_API usaf_status usaf_gather(int32_t w_dtype, const void *W, const uint32_t *idx, int64_t n,
+                        void *out, hipStream_t stream);
+
+
 
 /* Resident dequantisation (README "how it works": caching bullet; dequant
  * once, keep the working copy).  Symmetric int4: q [rows, cols/2] bytes,

@@ -25,6 +25,7 @@ EXPORTS = (
     "usaf_workspace_size", "usaf_moe_forward", "usaf_masked_backward", "usaf_importance_topk",
     "usaf_rigl_reselect", "usaf_sparse_adam", "usaf_dequant_resident", "usaf_mse_grad",
     "usaf_route", "usaf_status_string", "usaf_version", "usaf_timer_arm", "usaf_timer_read",
+    "usaf_gather",
 )
 
 # Kernel classes of the timing hook (usaf_kernel_class).
@@ -82,8 +83,9 @@ def _load():
         "usaf_masked_backward": [vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp],
         "usaf_importance_topk": [vp, i64, i64, vp, i64, vp, vp, vp, sz, vp],
         "usaf_rigl_reselect": [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
-        "usaf_sparse_adam": [i32, vp, vp, i64, vp, vp, vp, i64, C.c_double, C.c_double,
+        "usaf_sparse_adam": [i32, vp, vp, i64, vp, vp, vp, vp, i64, C.c_double, C.c_double,
                              C.c_double, C.c_double, vp, vp],
+        "usaf_gather": [i32, vp, vp, i64, vp, vp],
         "usaf_dequant_resident": [vp, vp, i64, i64, i32, vp, vp],
         "usaf_mse_grad": [vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "usaf_route": [vp, vp, vp, vp],
@@ -181,11 +183,17 @@ def rigl_reselect(shape, grad, Wflat, old_idx, old_m, old_v, k, r, new_idx, new_
            "usaf_rigl_reselect")
 
 
-def sparse_adam(w_dtype, W, idx, n, g, m, v, step, lr, beta1, beta2, eps, skip=None, stream=None):
-    _check(lib.usaf_sparse_adam(int(w_dtype), _p(W), _p(idx), int(n), _p(g), _p(m), _p(v),
-                                int(step), float(lr), float(beta1), float(beta2), float(eps),
-                                _p(skip), _stream(stream)),
+def sparse_adam(w_dtype, W, idx, n, g, m, v, step, lr, beta1, beta2, eps, skip=None, stream=None,
+                w_list=None):
+    _check(lib.usaf_sparse_adam(int(w_dtype), _p(W), _p(idx), int(n), _p(w_list), _p(g), _p(m),
+                                _p(v), int(step), float(lr), float(beta1), float(beta2),
+                                float(eps), _p(skip), _stream(stream)),
            "usaf_sparse_adam")
+
+
+def gather(w_dtype, W, idx, n, out, stream=None):
+    _check(lib.usaf_gather(int(w_dtype), _p(W), _p(idx), int(n), _p(out), _stream(stream)),
+           "usaf_gather")
 
 
 def dequant_resident(q, scale_f16, rows, cols, group, out_bf16, stream=None):

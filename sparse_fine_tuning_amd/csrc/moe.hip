@@ -107,44 +107,47 @@ __global__ __launch_bounds__(1024) void expert_sort_kernel(const int32_t* __rest
                                                            int E, int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ perm,
                                                            int32_t* __restrict__ slot_pos) {
-  __shared__ int red_lt[16];
-  __shared__ int wscan[16];
+  // Block e reads the ids twice, 1024 consecutive slots per round: first
+  // counting the slots of lower experts (the group's offset), then placing
+  // its own slots in slot order (ballot prefix within a wave, LDS prefix
+  // over the 16 waves, a running base across rounds).
+  __shared__ int red[16];
+  __shared__ int wcnt[16];
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int per = (S + 1023) / 1024;
-  const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
-  int lt = 0, eq = 0;
-  for (int s = s0; s < s1; ++s) {
-    const int id = ids[s];
-    lt += id < e;
-    eq += id == e;
-  }
-  int inc = eq;  // wave inclusive scan of the matches
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(inc, d, 64);
-    if (lane >= d) inc += v;
-  }
+  int lt = 0;
+  for (int s = tid; s < S; s += 1024) lt += ids[s] < e;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lt += __shfl_xor(lt, off, 64);
-  if (lane == 63) wscan[wid] = inc;
-  if (lane == 0) red_lt[wid] = lt;
+  if (lane == 0) red[wid] = lt;
   __syncthreads();
-  int off_e = 0, wbase = 0;
-  for (int w = 0; w < 16; ++w) {
-    off_e += red_lt[w];
-    if (w < wid) wbase += wscan[w];
-  }
+  int base = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) base += red[w];
   if (tid == 0) {
-    offsets[e] = off_e;
+    offsets[e] = base;
     if (e == E - 1) offsets[E] = S;
   }
-  int p = off_e + wbase + inc - eq;
-  for (int s = s0; s < s1; ++s) {
-    if (ids[s] == e) {
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  for (int s0 = 0; s0 < S; s0 += 1024) {
+    const int s = s0 + tid;
+    const bool mine = s < S && ids[s] == e;
+    const uint64_t m = __ballot(mine);
+    if (lane == 0) wcnt[wid] = __popcll(m);
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int c = wcnt[w];
+      before += w < wid ? c : 0;
+      total += c;
+    }
+    if (mine) {
+      const int p = base + before + __popcll(m & below);
       perm[p] = s;
       slot_pos[s] = p;
-      ++p;
     }
+    base += total;
+    __syncthreads();  // wcnt is rewritten next round
   }
 }
 
@@ -440,13 +443,21 @@ __global__ __launch_bounds__(256) void combine_y_kernel(const float* __restrict_
                                                         const float* __restrict__ topk_w,
                                                         const int32_t* __restrict__ slot_pos, int H,
                                                         int K, T* __restrict__ Y) {
+  __shared__ const float* rows[64];
+  __shared__ float wts[64];
   const int t = blockIdx.x;
+  if (threadIdx.x < K) {
+    const int s = t * K + threadIdx.x;
+    rows[threadIdx.x] = ybuf + int64_t(slot_pos[s]) * H;
+    wts[threadIdx.x] = topk_w[s];
+  }
+  __syncthreads();
   for (int h = 4 * threadIdx.x; h < H; h += 4 * blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
     for (int j = 0; j < K; ++j) {
-      const int s = t * K + j;
-      const float wj = topk_w[s];
-      const float4 y = *reinterpret_cast<const float4*>(ybuf + int64_t(slot_pos[s]) * H + h);
+      const float wj = wts[j];
+      const float4 y = *reinterpret_cast<const float4*>(rows[j] + h);
       acc.x = fmaf(wj, y.x, acc.x);
       acc.y = fmaf(wj, y.y, acc.y);
       acc.z = fmaf(wj, y.z, acc.z);
@@ -551,21 +562,34 @@ __global__ __launch_bounds__(256) void combine_dx_kernel(const float* __restrict
                                                          const float* __restrict__ Wr,
                                                          const int32_t* __restrict__ slot_pos,
                                                          int H, int K, T* __restrict__ dX) {
+  __shared__ const float* vrows[64];
+  __shared__ const float* wrows[64];
+  __shared__ float dls[64];
   const int t = blockIdx.x;
+  if (threadIdx.x < K) {
+    const int s = t * K + threadIdx.x;
+    vrows[threadIdx.x] = vbuf + int64_t(slot_pos[s]) * H;
+    wrows[threadIdx.x] = Wr + int64_t(ids[s]) * H;
+    dls[threadIdx.x] = dl[s];
+  }
+  __syncthreads();
   for (int h = 4 * threadIdx.x; h < H; h += 4 * blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
     for (int j = 0; j < K; ++j) {
-      const float4 v = *reinterpret_cast<const float4*>(vbuf + int64_t(slot_pos[t * K + j]) * H + h);
+      const float4 v = *reinterpret_cast<const float4*>(vrows[j] + h);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
+#pragma unroll 8
     for (int j = 0; j < K; ++j) {
-      const int s = t * K + j;
-      const float d = dl[s];
-      const int64_t wb = int64_t(ids[s]) * H + h;
-      acc.x = fmaf(d, router_w<T>(Wr, wb), acc.x);
-      acc.y = fmaf(d, router_w<T>(Wr, wb + 1), acc.y);
-      acc.z = fmaf(d, router_w<T>(Wr, wb + 2), acc.z);
-      acc.w = fmaf(d, router_w<T>(Wr, wb + 3), acc.w);
+      const float d = dls[j];
+      float4 w = *reinterpret_cast<const float4*>(wrows[j] + h);
+      w.x = Act<T>::round(w.x); w.y = Act<T>::round(w.y);
+      w.z = Act<T>::round(w.z); w.w = Act<T>::round(w.w);
+      acc.x = fmaf(d, w.x, acc.x);
+      acc.y = fmaf(d, w.y, acc.y);
+      acc.z = fmaf(d, w.z, acc.z);
+      acc.w = fmaf(d, w.w, acc.w);
     }
     store4<T>(dX, int64_t(t) * H + h, acc);
   }

@@ -37,6 +37,65 @@ __global__ __launch_bounds__(256) void adam_kernel(W* __restrict__ w, const uint
   }
 }
 
+// Adam over a list with a compact weight copy: entries 4i..4i+3 per thread
+// (16-byte reads of g, m, v, idx), the weights read from the list and
+// written to the list and to W at idx.
+template <class W>
+__global__ __launch_bounds__(256) void adam_list_kernel(W* __restrict__ w, const uint32_t* __restrict__ idx,
+                                                        int64_t n, W* __restrict__ wl,
+                                                        const float* __restrict__ g,
+                                                        float* __restrict__ m, float* __restrict__ v,
+                                                        float lr, float b1, float b2, float omb1,
+                                                        float omb2, float bc1, float bc2, float eps,
+                                                        const int32_t* __restrict__ skip) {
+  if (skip && *skip != 0) return;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  const int64_t n4 = n / 4;
+  for (int64_t q = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; q < n4; q += stride) {
+    const float4 gq = reinterpret_cast<const float4*>(g)[q];
+    float4 mq = reinterpret_cast<const float4*>(m)[q];
+    float4 vq = reinterpret_cast<const float4*>(v)[q];
+    const uint4 iq = reinterpret_cast<const uint4*>(idx)[q];
+    const float gi[4] = {gq.x, gq.y, gq.z, gq.w};
+    float mi[4] = {mq.x, mq.y, mq.z, mq.w}, vi[4] = {vq.x, vq.y, vq.z, vq.w};
+    const uint32_t ii[4] = {iq.x, iq.y, iq.z, iq.w};
+    float wv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      mi[u] = fmaf(b1, mi[u], omb1 * gi[u]);
+      vi[u] = fmaf(b2, vi[u], omb2 * gi[u] * gi[u]);
+      wv[u] = Act<W>::ld(wl, 4 * q + u) - lr * (mi[u] / bc1) / (sqrtf(vi[u] / bc2) + eps);
+    }
+    reinterpret_cast<float4*>(m)[q] = make_float4(mi[0], mi[1], mi[2], mi[3]);
+    reinterpret_cast<float4*>(v)[q] = make_float4(vi[0], vi[1], vi[2], vi[3]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      Act<W>::st(wl, 4 * q + u, wv[u]);
+      Act<W>::st(w, int64_t(ii[u]), wv[u]);
+    }
+  }
+  // tail (n % 4 entries)
+  const int64_t i = 4 * n4 + int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const float gi = g[i];
+    const float mi = fmaf(b1, m[i], omb1 * gi);
+    const float vi = fmaf(b2, v[i], omb2 * gi * gi);
+    m[i] = mi;
+    v[i] = vi;
+    const float wv = Act<W>::ld(wl, i) - lr * (mi / bc1) / (sqrtf(vi / bc2) + eps);
+    Act<W>::st(wl, i, wv);
+    Act<W>::st(w, int64_t(idx[i]), wv);
+  }
+}
+
+template <class W>
+__global__ __launch_bounds__(256) void gather_kernel(const W* __restrict__ w, const uint32_t* __restrict__ idx,
+                                                     int64_t n, W* __restrict__ out) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    out[i] = w[idx[i]];
+}
+
 // int4 -> bf16: one thread per 8 outputs (one 32-bit word of codes).
 __global__ __launch_bounds__(256) void dequant_int4_kernel(const uint32_t* __restrict__ q,
                                                            const uint16_t* __restrict__ scale,
@@ -71,18 +130,38 @@ static unsigned grid_for(int64_t n, int64_t per_block = 256, int64_t cap = 256 *
 using namespace usaf;
 
 extern "C" usaf_status usaf_sparse_adam(int32_t w_dtype, void* W, const uint32_t* idx, int64_t n,
-                                        const float* g, float* m, float* v, int64_t step, double lr,
-                                        double beta1, double beta2, double eps,
-                                        const int32_t* skip_if_nonzero, hipStream_t stream) {
+                                        void* w_list, const float* g, float* m, float* v,
+                                        int64_t step, double lr, double beta1, double beta2,
+                                        double eps, const int32_t* skip_if_nonzero,
+                                        hipStream_t stream) {
   if (n < 0 || step < 1) return USAF_ERR_INVALID_ARG;
   if (w_dtype != USAF_F32 && w_dtype != USAF_BF16) return USAF_ERR_INVALID_ARG;
+  if (w_list && !idx) return USAF_ERR_INVALID_ARG;
   if (n == 0) return USAF_OK;
   if (!W || !g || !m || !v) return USAF_ERR_INVALID_ARG;
   const double bc1 = 1.0 - pow(beta1, double(step));
   const double bc2 = 1.0 - pow(beta2, double(step));
   const float omb1 = float(1.0 - beta1), omb2 = float(1.0 - beta2);
   timer_begin(USAF_K_ADAM, stream);
-  if (w_dtype == USAF_BF16)
+  if (w_list) {
+    const bool aligned = ((reinterpret_cast<uintptr_t>(g) | reinterpret_cast<uintptr_t>(m) |
+                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(idx)) & 15) == 0;
+    if (!aligned) {
+      timer_end(USAF_K_ADAM, stream);
+      return USAF_ERR_UNSUPPORTED;
+    }
+    const unsigned grid = grid_for(ceil_div(n, 4));
+    if (w_dtype == USAF_BF16)
+      hipLaunchKernelGGL(adam_list_kernel<bf16_t>, dim3(grid), dim3(256), 0, stream,
+                         static_cast<bf16_t*>(W), idx, n, static_cast<bf16_t*>(w_list), g, m, v,
+                         float(lr), float(beta1), float(beta2), omb1, omb2, float(bc1),
+                         float(bc2), float(eps), skip_if_nonzero);
+    else
+      hipLaunchKernelGGL(adam_list_kernel<float>, dim3(grid), dim3(256), 0, stream,
+                         static_cast<float*>(W), idx, n, static_cast<float*>(w_list), g, m, v,
+                         float(lr), float(beta1), float(beta2), omb1, omb2, float(bc1),
+                         float(bc2), float(eps), skip_if_nonzero);
+  } else if (w_dtype == USAF_BF16)
     hipLaunchKernelGGL(adam_kernel<bf16_t>, dim3(grid_for(n)), dim3(256), 0, stream,
                        static_cast<bf16_t*>(W), idx, n, g, m, v, float(lr), float(beta1),
                        float(beta2), omb1, omb2, float(bc1), float(bc2), float(eps),
@@ -93,6 +172,21 @@ extern "C" usaf_status usaf_sparse_adam(int32_t w_dtype, void* W, const uint32_t
                        float(beta2), omb1, omb2, float(bc1), float(bc2), float(eps),
                        skip_if_nonzero);
   timer_end(USAF_K_ADAM, stream);
+  USAF_LAUNCH_CHECK();
+  return USAF_OK;
+}
+
+extern "C" usaf_status usaf_gather(int32_t w_dtype, const void* W, const uint32_t* idx, int64_t n,
+                                   void* out, hipStream_t stream) {
+  if (n < 0 || (w_dtype != USAF_F32 && w_dtype != USAF_BF16)) return USAF_ERR_INVALID_ARG;
+  if (n == 0) return USAF_OK;
+  if (!W || !idx || !out) return USAF_ERR_INVALID_ARG;
+  if (w_dtype == USAF_BF16)
+    hipLaunchKernelGGL(gather_kernel<bf16_t>, dim3(grid_for(n)), dim3(256), 0, stream,
+                       static_cast<const bf16_t*>(W), idx, n, static_cast<bf16_t*>(out));
+  else
+    hipLaunchKernelGGL(gather_kernel<float>, dim3(grid_for(n)), dim3(256), 0, stream,
+                       static_cast<const float*>(W), idx, n, static_cast<float*>(out));
   USAF_LAUNCH_CHECK();
   return USAF_OK;
 }

@@ -78,6 +78,14 @@ class SparseMoELayer:
         self.m = torch.zeros(k, dtype=torch.float32, device=self.device)
         self.v = torch.zeros(k, dtype=torch.float32, device=self.device)
         self.dW = torch.empty(k, dtype=torch.float32, device=self.device)
+        self.refresh_list()
+
+    def refresh_list(self):
+        """Compact copy of the active weights (W at idx) that SparseAdam reads
+        instead of the scattered entries; rebuilt whenever the list changes."""
+        k = self.idx.numel()
+        self.w_list = torch.empty(k, dtype=_dt(self.act), device=self.device)
+        capi.gather(self.act, self.W, self.idx, k, self.w_list)
 
     # ---- the step ------------------------------------------------------------
     def forward(self, stream=None):
@@ -102,7 +110,7 @@ class SparseMoELayer:
     def adam(self, step, lr, betas=(0.9, 0.999), eps=1e-8, stream=None):
         b1, b2 = betas
         capi.sparse_adam(self.act, self.W, self.idx, self.idx.numel(), self.dW, self.m, self.v,
-                         step, lr, b1, b2, eps, self.nonfinite, stream)
+                         step, lr, b1, b2, eps, self.nonfinite, stream, w_list=self.w_list)
         capi.sparse_adam(F32, self.Wr, None, self.Wr.numel(), self.dWr, self.mr, self.vr, step,
                          lr, b1, b2, eps, self.nonfinite, stream)
 
@@ -159,4 +167,5 @@ def rigl(layer: SparseMoELayer, grad: torch.Tensor, r: int, stream=None, ws=None
     capi.rigl_reselect(layer.shape, grad, layer.W, layer.idx, layer.m, layer.v, k, r, new_idx,
                        new_m, new_v, stats, ws, stream)
     layer.idx, layer.m, layer.v = new_idx, new_m, new_v
+    layer.refresh_list()
     return stats

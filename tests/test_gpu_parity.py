@@ -293,11 +293,11 @@ def test_rigl_exact(capi, act, old_is_top):
 # --------------------------------------------------------------------------
 # a12 Adam and the NaN skip
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("act", [1, 0])
-def test_sparse_adam(capi, act):
-    say(f"adam act={act}")
+@pytest.mark.parametrize("act,use_list", [(1, False), (0, False), (1, True), (0, True)])
+def test_sparse_adam(capi, act, use_list):
+    say(f"adam act={act} list={use_list}")
     rng = np.random.default_rng(5 + act)
-    N, k = 50000, 4000
+    N, k = 50000, (4001 if use_list else 4000)  # 4001: the list kernel's 4-wide tail
     w = synth.normal(N, 0.02, 9)
     if act:
         w = synth.to_bf16_values(w)
@@ -309,11 +309,15 @@ def test_sparse_adam(capi, act):
         Wt = Wt.to(torch.bfloat16)
     mt = torch.zeros(k, device=DEV); vt = torch.zeros(k, device=DEV)
     it = torch.from_numpy(idx.view(np.int32)).to(DEV)
+    wl = None
+    if use_list:
+        wl = torch.empty(k, dtype=Wt.dtype, device=DEV)
+        capi.gather(act, Wt, it, k, wl)
     wref = w.astype(np.float64)
     for step in range(1, 4):
         g = (rng.standard_normal(k) * 10.0 ** rng.integers(-8, -3, k)).astype(np.float32)
         capi.sparse_adam(act, Wt, it, k, torch.from_numpy(g).to(DEV), mt, vt, step, 1e-3, 0.9,
-                         0.999, 1e-8)
+                         0.999, 1e-8, w_list=wl)
         wsel, m, v = O.adam_update(wref[idx], g, m, v, step, 1e-3, 0.9, 0.999, 1e-8,
                                    R.act_dtype, R)
         wref[idx] = wsel
@@ -326,6 +330,8 @@ def test_sparse_adam(capi, act):
     assert rel(got, wref) <= (TOL_BF16 if act else TOL_F32)
     # the touched entries moved by ~lr per step
     assert np.median(np.abs(got[idx] - w[idx])) > 1e-3
+    if use_list:  # the compact copy still equals W at idx
+        assert torch.equal(wl, Wt[it.long()])
 
 
 def test_nan_step_is_skipped(capi):
