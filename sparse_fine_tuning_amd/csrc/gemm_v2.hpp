@@ -452,7 +452,16 @@ __global__ __launch_bounds__(P::NTHR) void gemm2_persistent(P p) {
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    main_loop<P, IM, IM, NJ>(ao, bo, as, bs, lds, t.ke, nk, tid, w, wm, wn, lane, acc);
+    // 32-row blocks of this wave inside the tile's valid rows: a ragged
+    // group's last tile issues MFMAs only for its valid row blocks
+    const int vb = __builtin_amdgcn_readfirstlane(min(IM, max(0, (t.mc - wm * P::RW + 31) / 32)));
+    if constexpr (IM == 2) {
+      if (vb == 2) main_loop<P, 2, IM, NJ>(ao, bo, as, bs, lds, t.ke, nk, tid, w, wm, wn, lane, acc);
+      else if (vb == 1) main_loop<P, 1, IM, NJ>(ao, bo, as, bs, lds, t.ke, nk, tid, w, wm, wn, lane, acc);
+      else main_loop<P, 0, IM, NJ>(ao, bo, as, bs, lds, t.ke, nk, tid, w, wm, wn, lane, acc);
+    } else {
+      main_loop<P, IM, IM, NJ>(ao, bo, as, bs, lds, t.ke, nk, tid, w, wm, wn, lane, acc);
+    }
     __syncthreads();  // every wave is done with the ring
     MTile tn;
     L += G;

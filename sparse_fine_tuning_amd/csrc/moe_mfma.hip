@@ -499,10 +499,11 @@ struct MDa {
           const int col = out_col(CW, wn, j, g, lane);
           if (!vrow || col >= t.nc) continue;
           const int f = t.n0 + col;
-          const uint2 av = *reinterpret_cast<const uint2*>(a + p * I + f);
+          // a = bf16(silu(g) u) is recomputed from the saved g|u exactly as the
+          // forward epilogue rounded it, instead of being read back
           const uint2 gv = *reinterpret_cast<const uint2*>(gu + p * 2 * I + f);
           const uint2 uv = *reinterpret_cast<const uint2*>(gu + p * 2 * I + I + f);
-          const uint32_t aw[2] = {av.x, av.y}, gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y};
+          const uint32_t gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y};
           uint32_t dg[2], du[2];
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
@@ -510,12 +511,12 @@ struct MDa {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
               const float U = acc[i][j][4 * g + 2 * h + q];
-              const float av1 = q ? bf2f(bf16_t(aw[h] >> 16)) : bf2f(bf16_t(aw[h] & 0xffffu));
               const float g1 = q ? bf2f(bf16_t(gw[h] >> 16)) : bf2f(bf16_t(gw[h] & 0xffffu));
               const float u1 = q ? bf2f(bf16_t(uw[h] >> 16)) : bf2f(bf16_t(uw[h] & 0xffffu));
+              const float sg = sigmoid_f(g1);
+              const float av1 = bf2f(f2bf(g1 * sg * u1));
               part = fmaf(U, av1, part);
               const float da = wt * U;
-              const float sg = sigmoid_f(g1);
               dgs[q] = da * u1 * sg * (1.f + g1 * (1.f - sg));
               dus[q] = da * g1 * sg;
             }
