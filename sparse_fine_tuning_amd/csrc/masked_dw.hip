@@ -224,12 +224,14 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
   const int ne = A.offsets[e + 1] - off;
   const int nblk_r = (ncol + 7) >> 3, nblk_l = (nr + 7) >> 3;
 
-  for (int q0 = 0; q0 < nent; q0 += 256 * kMaxEnt) {
-    // this thread's entries: q0 + tid*kMaxEnt + i
+  for (int q0 = 0, per = 0; q0 < nent; q0 += 256 * per) {
+    // this pass: per entries for every thread (spread evenly, at most
+    // kMaxEnt), thread tid taking q0 + tid*per + i
+    per = min(kMaxEnt, (nent - q0 + 255) / 256);
     uint32_t coord[kMaxEnt];  // (row - r_lo) << 16 | (col - c0), or ~0 when unused
     float acc[kMaxEnt];
     {
-      const int q = q0 + tid * kMaxEnt;
+      const int q = q0 + tid * per;
       // row of entry q: last r with rowpre[r] <= q
       int lo = 0, hi = nr;
       while (lo < hi) {
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
         acc[i] = 0.f;
         coord[i] = 0xffffffffu;
         const int qi = q + i;
-        if (qi < nent) {
+        if (i < per && qi < nent) {
           while (rowpre[r + 1] <= qi) ++r;
           const int64_t rb = A.base + (int64_t(e) * A.R + r_lo + r) * A.C;
           const int c = int(int64_t(A.idx[rstart[r] + (qi - rowpre[r])]) - rb);
@@ -250,8 +252,8 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
         }
       }
     }
-    // stream the expert's slots, a token-table window at a time; chunk k+1
-    // is fetched into registers while chunk k is consumed from LDS
+    // stream the expert's slots, a token-table window at a time, in chunks
+    // of kSlots staged through LDS
     const bool stager = tid < nblk_r + nblk_l;  // <= 256 staging blocks: one per thread
     for (int w0 = 0; w0 < ne; w0 += kTokTab) {
       const int wn = min(kTokTab, ne - w0);
@@ -262,60 +264,76 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
         if (kDown) w_tab[p] = A.topk_w[sid];
       }
       __syncthreads();
-      StageRegs sr;
-      if (stager) stage_fetch<kDown>(A, tid, nblk_r, 0, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr);
-      for (int p0 = 0; p0 < wn; p0 += kSlots) {
-        __syncthreads();  // previous chunk fully consumed
-        if (stager) stage_store<kDown>(tid, nblk_r, sr, lds_l, lds_r);
-        __syncthreads();
-        if (stager && p0 + kSlots < wn)
-          stage_fetch<kDown>(A, tid, nblk_r, p0 + kSlots, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr);
-      uint32_t prow = 0xffffffffu;
-      uint4 lb16 = make_uint4(0, 0, 0, 0);
-      float lf[8];
+      // two chunks in flight: chunk c+2 is fetched into the register stage
+      // that chunk c just left, so each fetch has two chunks of work to land
+      auto compute = [&]() {
+        uint32_t prow = 0xffffffffu;
+        uint4 lb16 = make_uint4(0, 0, 0, 0);
+        float lf[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) lf[t] = 0.f;
+        for (int t = 0; t < 8; ++t) lf[t] = 0.f;
 #pragma unroll
-      for (int i = 0; i < kMaxEnt; ++i) {
-        const uint32_t cd = coord[i];
-        if (cd == 0xffffffffu) continue;
-        const uint32_t lr = cd >> 16, lc = cd & 0xffffu;
-        if (lr != prow) {
-          prow = lr;
-          if (kDown) {
-            const float4* src = reinterpret_cast<const float4*>(lds_l + size_t(sw32(lr)) * 32);
-            const float4 x = src[0], y = src[1];
-            lf[0] = x.x; lf[1] = x.y; lf[2] = x.z; lf[3] = x.w;
-            lf[4] = y.x; lf[5] = y.y; lf[6] = y.z; lf[7] = y.w;
-          } else {
-            lb16 = *reinterpret_cast<const uint4*>(lds_l + size_t(sw16(lr)) * 16);
+        for (int i = 0; i < kMaxEnt; ++i) {
+          const uint32_t cd = coord[i];
+          if (cd == 0xffffffffu) continue;
+          const uint32_t lr = cd >> 16, lc = cd & 0xffffu;
+          if (lr != prow) {
+            prow = lr;
+            if (kDown) {
+              const float4* src = reinterpret_cast<const float4*>(lds_l + size_t(sw32(lr)) * 32);
+              const float4 x = src[0], y = src[1];
+              lf[0] = x.x; lf[1] = x.y; lf[2] = x.z; lf[3] = x.w;
+              lf[4] = y.x; lf[5] = y.y; lf[6] = y.z; lf[7] = y.w;
+            } else {
+              lb16 = *reinterpret_cast<const uint4*>(lds_l + size_t(sw16(lr)) * 16);
+            }
           }
+          const uint4 rv = *reinterpret_cast<const uint4*>(lds_r + size_t(sw16(lc)) * 16);
+          float a = acc[i];
+          if (kDown) {
+            a = fmaf(lf[0], bflo(rv.x), a); a = fmaf(lf[1], bfhi(rv.x), a);
+            a = fmaf(lf[2], bflo(rv.y), a); a = fmaf(lf[3], bfhi(rv.y), a);
+            a = fmaf(lf[4], bflo(rv.z), a); a = fmaf(lf[5], bfhi(rv.z), a);
+            a = fmaf(lf[6], bflo(rv.w), a); a = fmaf(lf[7], bfhi(rv.w), a);
+          } else {
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb16.x),
+                                                __builtin_bit_cast(bf16x2_t, rv.x), a, false);
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb16.y),
+                                                __builtin_bit_cast(bf16x2_t, rv.y), a, false);
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb16.z),
+                                                __builtin_bit_cast(bf16x2_t, rv.z), a, false);
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb16.w),
+                                                __builtin_bit_cast(bf16x2_t, rv.w), a, false);
+          }
+          acc[i] = a;
         }
-        const uint4 rv = *reinterpret_cast<const uint4*>(lds_r + size_t(sw16(lc)) * 16);
-        float a = acc[i];
-        if (kDown) {
-          a = fmaf(lf[0], bflo(rv.x), a); a = fmaf(lf[1], bfhi(rv.x), a);
-          a = fmaf(lf[2], bflo(rv.y), a); a = fmaf(lf[3], bfhi(rv.y), a);
-          a = fmaf(lf[4], bflo(rv.z), a); a = fmaf(lf[5], bfhi(rv.z), a);
-          a = fmaf(lf[6], bflo(rv.w), a); a = fmaf(lf[7], bfhi(rv.w), a);
-        } else {
-          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb16.x),
-                                              __builtin_bit_cast(bf16x2_t, rv.x), a, false);
-          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb16.y),
-                                              __builtin_bit_cast(bf16x2_t, rv.y), a, false);
-          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb16.z),
-                                              __builtin_bit_cast(bf16x2_t, rv.z), a, false);
-          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb16.w),
-                                              __builtin_bit_cast(bf16x2_t, rv.w), a, false);
-        }
-        acc[i] = a;
+      };
+      StageRegs sr0, sr1;
+      if (stager) {
+        stage_fetch<kDown>(A, tid, nblk_r, 0, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr0);
+        if (kSlots < wn)
+          stage_fetch<kDown>(A, tid, nblk_r, kSlots, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr1);
       }
+      for (int p0 = 0; p0 < wn; p0 += 2 * kSlots) {
+        __syncthreads();  // previous chunk fully consumed
+        if (stager) stage_store<kDown>(tid, nblk_r, sr0, lds_l, lds_r);
+        __syncthreads();
+        if (stager && p0 + 2 * kSlots < wn)
+          stage_fetch<kDown>(A, tid, nblk_r, p0 + 2 * kSlots, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr0);
+        compute();
+        if (p0 + kSlots >= wn) break;
+        __syncthreads();
+        if (stager) stage_store<kDown>(tid, nblk_r, sr1, lds_l, lds_r);
+        __syncthreads();
+        if (stager && p0 + 3 * kSlots < wn)
+          stage_fetch<kDown>(A, tid, nblk_r, p0 + 3 * kSlots, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr1);
+        compute();
       }
     }
     // write this thread's entries (contiguous positions in idx within a row run;
     // recompute positions row by row)
     {
-      const int q = q0 + tid * kMaxEnt;
+      const int q = q0 + tid * per;
       int nbad = 0;
 #pragma unroll
       for (int i = 0; i < kMaxEnt; ++i) {
