@@ -327,6 +327,18 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
   constexpr int NS = P::NS, RW = P::RW, CW = P::CW;
   constexpr int A_BYTES = AOp::kBytes;
   constexpr int NLOAD = AOp::kInst + BOp::kInst;
+  constexpr int KC = kBK / 16;
+  // The MFMAs of a stage's last substep are issued after the next stage's
+  // barrier, from fragments already in registers, so they cover the barrier
+  // and the latency of the next stage's first LDS reads.
+  bf16x8_t pa[VB > 0 ? VB : 1], pb[NJ];
+  auto mfmas = [&](const bf16x8_t* a, const bf16x8_t* b) {
+#pragma unroll
+    for (int i = 0; i < VB; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+  };
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + NS - 2 < nk) wait_vmcnt<(NS - 2) * NLOAD>(); else wait_vmcnt<0>();
     __syncthreads();
@@ -351,22 +363,25 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
       for (int i = 0; i < VB; ++i) af[0][i] = AOp::frag(As, wm * RW + 32 * i, 0, lane);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bfr[0][j] = BOp::frag(Bs, wn * CW + 32 * j, 0, lane);
+      if (kt > 0) mfmas(pa, pb);  // the previous stage's last substep
 #pragma unroll
-      for (int kc = 0; kc < kBK / 16; ++kc) {
+      for (int kc = 0; kc < KC - 1; ++kc) {
         const int c = kc & 1, n = c ^ 1;
-        if (kc + 1 < kBK / 16) {
 #pragma unroll
-          for (int i = 0; i < VB; ++i) af[n][i] = AOp::frag(As, wm * RW + 32 * i, kc + 1, lane);
+        for (int i = 0; i < VB; ++i) af[n][i] = AOp::frag(As, wm * RW + 32 * i, kc + 1, lane);
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) bfr[n][j] = BOp::frag(Bs, wn * CW + 32 * j, kc + 1, lane);
-        }
-#pragma unroll
-        for (int i = 0; i < VB; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[c][j], af[c][i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NJ; ++j) bfr[n][j] = BOp::frag(Bs, wn * CW + 32 * j, kc + 1, lane);
+        mfmas(af[c], bfr[c]);
       }
+      constexpr int last = (KC - 1) & 1;
+#pragma unroll
+      for (int i = 0; i < VB; ++i) pa[i] = af[last][i];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) pb[j] = bfr[last][j];
     }
+  }
+  if constexpr (VB > 0) {
+    if (nk > 0) mfmas(pa, pb);
   }
 }
 
