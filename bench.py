@@ -202,6 +202,80 @@ def rigl_scan(capi, synth, layer_mod, d, idx, dims, scan_tokens, repeats=2):
                 rigl_k=int(k), rigl_r=int(r))
 
 
+def mixtral_layer(capi, synth, layer_mod, steps, lr):
+    """The Mixtral-8x7B-shaped layer (T=4096, H=4096, E=8, K=2, I=14336, bf16,
+    seeded 0.5% mask): step throughput with per-class rooflines, and one RigL
+    scan (dense gradient, global top-0.5%, drop/grow at 30%) on the same
+    4096 tokens.  Inputs are drawn on the device with a seeded generator
+    (same distributions as the other workloads); the mask is the seeded
+    uniform one."""
+    import numpy as np
+    import torch
+    dims = (4096, 4096, 8, 2, 14336)
+    T, H, E, K, I = dims
+    N = 3 * E * H * I
+    k = (N * 5) // 1000
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20)
+    lay = layer_mod.SparseMoELayer(*dims, act=capi.BF16, device=dev)
+    lay.X = torch.randn(T, H, generator=gen, device=dev).to(torch.bfloat16)
+    lay.tgt = torch.randn(T, H, generator=gen, device=dev).to(torch.bfloat16)
+    lay.Wr = torch.randn(E, H, generator=gen, device=dev) * 0.02
+    lay.W = (torch.randn(N, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    lay.mr = torch.zeros_like(lay.Wr)
+    lay.vr = torch.zeros_like(lay.Wr)
+    idx = synth.random_mask(N, k, 25)
+    lay.set_active(idx)
+    for _ in range(3):
+        lay.train_step(lr=lr, check_skip=False)
+    torch.cuda.synchronize()
+    classes = [capi.K_ROUTER_GEMM, capi.K_ROUTE, capi.K_GATE_UP, capi.K_DOWN, capi.K_COMBINE_Y,
+               capi.K_MSE, capi.K_DA, capi.K_ROUTER_BWD, capi.K_DX, capi.K_COMBINE_DX,
+               capi.K_MASKED_DW, capi.K_ADAM]
+    per_class = time_kernel_classes(capi, lay, classes, lr)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        lay.train_step(lr=lr, check_skip=False)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    work = algorithmic_work(dims, k)
+    kern = {c: dict(ms=per_class[c], **roofline_entry(c, *work[c], per_class[c]))
+            for c in per_class if c in work and per_class[c] > 0}
+    gemm_fl = sum(work[c][0] for c in ("gate_up", "down", "da", "dx"))
+    gemm_ms = sum(per_class[c] for c in ("gate_up", "down", "da", "dx"))
+    log(f"mixtral: step {ms:.3f} ms -> {T / (ms * 1e-3):.0f} tokens/s; grouped GEMMs "
+        f"{gemm_fl / (gemm_ms * 1e-3) / 1e12:.0f} TFLOP/s")
+    # one RigL scan on the step batch
+    r = (3 * k) // 10
+    grad = torch.empty(N, dtype=torch.float32, device=dev)
+    ws = torch.empty(capi.workspace_size(capi.WS_RIGL, None, N, k), dtype=torch.uint8, device=dev)
+    scans = []
+    for rep in range(3):
+        lay.set_active(idx)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        lay.dense_scan(out=grad)
+        st = layer_mod.rigl(lay, grad, r, ws=ws)
+        torch.cuda.synchronize()
+        if rep:
+            scans.append((time.perf_counter() - t0) * 1e3)
+    stats = st.cpu().numpy()
+    log(f"mixtral: rigl scan {np.median(scans):.2f} ms")
+    out = dict(workload="Mixtral-8x7B-shaped single MoE layer sparse train step",
+               tokens=T, hidden=H, experts=E, top_k=K, intermediate=I, active_entries=k,
+               value=T / (ms * 1e-3), unit="tokens/s", ms_per_step=ms,
+               grouped_gemm_tflops=gemm_fl / (gemm_ms * 1e-3) / 1e12,
+               grouped_gemm_mfma_frac=gemm_fl / (gemm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+               step_kernels=kern, rigl_scan_ms=float(np.median(scans)), rigl_k=int(k),
+               rigl_r=int(r), turnover_applied=float(stats[1]) / k,
+               turnover_topk_vs_old=float(stats[2]) / k)
+    del lay, grad, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(d, idx, dims, sample_tokens):
     """The CPU oracle, as it stands, on one train step over a sample of the
     layer's tokens (same weights and mask); tokens/s."""
@@ -235,6 +309,7 @@ def main():
     ap.add_argument("--scan-tokens", type=int, default=8192)
     ap.add_argument("--no-scan", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-mixtral", action="store_true")
     ap.add_argument("--scan-only", action="store_true",
                     help="skip the timed train steps; run only the RigL scan (profiling)")
     ap.add_argument("--print-sha", action="store_true",
@@ -341,6 +416,9 @@ def main():
         out["rigl"] = rigl_scan(capi, synth, layer_mod, d, idx, dims, args.scan_tokens)
         out["rigl_scan_ms"] = out["rigl"]["rigl_scan_ms"]
         torch.cuda.empty_cache()
+    if not args.no_mixtral and not args.scan_only:
+        log("mixtral-shaped layer")
+        out["mixtral"] = mixtral_layer(capi, synth, layer_mod, 10, lr)
     if not args.no_cpu:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
         out["cpu_baseline"] = cpu_baseline(d, idx, dims, args.cpu_tokens)
