@@ -10,16 +10,19 @@
 // drop), i.e. magnitude descending, then index ascending.  Composites are
 // unique, so the top-k set is unique.
 //
-// Selection is an exact radix select done with three full reads:
+// Selection is an exact radix select done with two full reads:
 //   A  histogram of the top 11 key bits (64 privatised global copies, so the
 //      few hot bins do not serialise every block's atomics) -> the bin b0
 //      holding the k-th element;
-//   B  per 4096-key chunk: how many keys lie above b0, and the indices of
-//      the keys in b0 (the candidates) in the chunk's own buffer region;
-//   -  the remaining 52 composite bits are resolved on the candidates alone
-//      (five histogram/select rounds) -> the exact k-th composite;
-//   C  ordered compaction of every selected index, chunk by chunk, at
-//      offsets from a scan of the per-chunk selected counts.
+//   B  per 4096-key chunk, in the chunk's own buffer regions: the indices of
+//      the keys above b0 (all selected) and the indices and keys of the keys
+//      in b0 (the candidates);
+//   -  the remaining 52 composite bits are resolved on the stored candidate
+//      keys alone (five histogram/select rounds) -> the exact k-th composite;
+//   C  per chunk, the selected indices (the above list and the candidates at
+//      or above the k-th composite) are merged in index order through a
+//      4096-bit LDS mask and written at offsets from a scan of the per-chunk
+//      counts.
 // Output indices are therefore ascending.
 #include "common.hpp"
 #include "moe_internal.hpp"
@@ -149,7 +152,10 @@ struct TopkWs {
   uint32_t* st;     // [ST_WORDS]
   uint32_t* cnt;    // [nchunks] selected per wave chunk (then exclusive offsets)
   uint32_t* ccnt;   // [nchunks] candidates per wave chunk
+  uint32_t* acnt;   // [nchunks] keys above b0 per wave chunk
   uint32_t* cand;   // [n] candidate indices, chunk c's at [c*kChunk, c*kChunk + ccnt[c])
+  uint32_t* ckey;   // [n] their keys, same layout
+  uint32_t* above;  // [n] indices above b0, chunk c's at [c*kChunk, c*kChunk + acnt[c])
   int64_t nchunks;
 };
 
@@ -157,7 +163,7 @@ static size_t al(size_t x) { return align256(x); }
 size_t topk_ws_bytes(int64_t n) {
   const int64_t nt = ceil_div(n > 0 ? n : 1, kChunk);
   return al(size_t(kHistCopies) * kTopkBins * 4) + al(kTopkBins * 4) + al(ST_WORDS * 4) +
-         2 * al(size_t(nt) * 4) + al(size_t(nt) * kChunk * 4);
+         3 * al(size_t(nt) * 4) + 3 * al(size_t(nt) * kChunk * 4);
 }
 static TopkWs topk_ws(char* w, int64_t n) {
   const int64_t nt = ceil_div(n > 0 ? n : 1, kChunk);
@@ -172,7 +178,13 @@ static TopkWs topk_ws(char* w, int64_t n) {
   w += al(size_t(nt) * 4);
   t.ccnt = reinterpret_cast<uint32_t*>(w);
   w += al(size_t(nt) * 4);
+  t.acnt = reinterpret_cast<uint32_t*>(w);
+  w += al(size_t(nt) * 4);
   t.cand = reinterpret_cast<uint32_t*>(w);
+  w += al(size_t(nt) * kChunk * 4);
+  t.ckey = reinterpret_cast<uint32_t*>(w);
+  w += al(size_t(nt) * kChunk * 4);
+  t.above = reinterpret_cast<uint32_t*>(w);
   t.nchunks = nt;
   return t;
 }
@@ -300,9 +312,9 @@ __device__ __forceinline__ uint32_t wave_excl(uint32_t v, uint32_t& total) {
   return inc - v;
 }
 
-// Pass B: per wave chunk, the count of eligible keys above b0 (cnt) and the
-// candidates in b0, stored in the chunk's own region of the buffer (ccnt of
-// them, in index order) -- no shared counter.
+// Pass B: per wave chunk, the indices of the eligible keys above b0 and the
+// indices and keys of those in b0 (the candidates), each in the chunk's own
+// region of its buffer, in index order -- no shared counter.
 template <class KF>
 __global__ __launch_bounds__(256) void topk_pass_b_kernel(KF key, int64_t n, const uint32_t* ex,
                                                           int64_t nex, TopkWs w,
@@ -317,32 +329,42 @@ __global__ __launch_bounds__(256) void topk_pass_b_kernel(KF key, int64_t n, con
   if (i0 + lbase >= n) return;  // uniform per wave; no block barrier follows
   const int64_t chunk = int64_t(blockIdx.x) * 4 + wid;
   uint32_t* cdst = w.cand + chunk * kChunk;
-  uint32_t gt = 0, pos = 0;
+  uint32_t* kdst = w.ckey + chunk * kChunk;
+  uint32_t* adst = w.above + chunk * kChunk;
+  uint32_t apos = 0, pos = 0;
   for (int r = 0; r < kChunk / 256; ++r) {
     const int l = lbase + r * 256 + lane * 4;
     uint32_t kv[4];
     bool ok[4];
     keys4(key, i0 + l, n, bm, l, kv, ok);
-    bool c[4];
-    uint32_t mine = 0;
+    bool c[4], a[4];
+    uint32_t mine = 0, mina = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const uint32_t d = kv[u] >> 20;
-      gt += ok[u] && d > b0;
+      a[u] = ok[u] && d > b0;
       c[u] = ok[u] && d == b0;
       mine += c[u];
+      mina += a[u];
     }
-    uint32_t tot;
+    uint32_t tot, tota;
     uint32_t p = pos + wave_excl(mine, tot);
+    uint32_t q = apos + wave_excl(mina, tota);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (c[u]) cdst[p++] = uint32_t(i0 + l + u);
+    for (int u = 0; u < 4; ++u) {
+      if (c[u]) {
+        cdst[p] = uint32_t(i0 + l + u);
+        kdst[p] = kv[u];
+        ++p;
+      }
+      if (a[u]) adst[q++] = uint32_t(i0 + l + u);
+    }
     pos += tot;
+    apos += tota;
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) gt += __shfl_xor(gt, off, 64);
   if (lane == 0) {
-    w.cnt[chunk] = gt;
+    w.cnt[chunk] = apos;
+    w.acnt[chunk] = apos;
     w.ccnt[chunk] = pos;
   }
 }
@@ -363,11 +385,9 @@ __global__ __launch_bounds__(256) void topk_cand_hist_kernel(KF key, TopkWs w, i
   for (int64_t c = int64_t(blockIdx.x) * 4 + wid; c < w.nchunks; c += int64_t(gridDim.x) * 4) {
     const uint32_t m = w.ccnt[c];
     const uint32_t* src = w.cand + c * kChunk;
+    const uint32_t* ksrc = w.ckey + c * kChunk;
     for (uint32_t j = lane; j < m; j += 64) {
-      const uint32_t i = src[j];
-      uint32_t kv;
-      key(i, kv);
-      const uint64_t cp = composite(kv, i);
+      const uint64_t cp = composite(ksrc[j], src[j]);
       if ((cp >> top) == (prefix >> top)) atomicAdd(&h[uint32_t(cp >> shift) & dmask], 1u);
     }
   }
@@ -402,16 +422,12 @@ __global__ __launch_bounds__(256) void topk_cand_count_kernel(KF key, TopkWs w, 
     const uint32_t m = w.ccnt[c];
     if (m == 0) continue;
     const uint32_t* src = w.cand + c * kChunk;
+    const uint32_t* ksrc = w.ckey + c * kChunk;
     uint32_t nsel = 0;
     for (uint32_t j0 = 0; j0 < m; j0 += 64) {
       const uint32_t j = j0 + lane;
       bool sel = false;
-      if (j < m) {
-        const uint32_t i = src[j];
-        uint32_t kv;
-        key(i, kv);
-        sel = composite(kv, i) >= theta;
-      }
+      if (j < m) sel = composite(ksrc[j], src[j]) >= theta;
       nsel += __popcll(__ballot(sel));
     }
     if (lane == 0) w.cnt[c] += nsel;
@@ -452,47 +468,50 @@ __global__ __launch_bounds__(1024) void scan_u32_kernel(uint32_t* __restrict__ a
   }
 }
 
-// Pass C: ordered compaction of the selected indices of each wave chunk.
-template <class KF>
-__global__ __launch_bounds__(256) void topk_pass_c_kernel(KF key, int64_t n, const uint32_t* ex,
-                                                          int64_t nex, TopkWs w,
-                                                          uint32_t* __restrict__ out_idx,
+// Pass C: per wave chunk, the above-b0 indices and the candidates at or
+// above the k-th composite are marked in a 4096-bit LDS mask (chunk-local
+// offsets) and emitted in index order at the chunk's scanned offset.
+__global__ __launch_bounds__(256) void topk_pass_c_kernel(TopkWs w, uint32_t* __restrict__ out_idx,
                                                           float* __restrict__ out_val,
                                                           const float* __restrict__ valsrc,
                                                           const uint32_t* gate) {
   if (gated_off(gate)) return;
-  __shared__ uint32_t bm[kTopkTile / 32];
-  const int64_t i0 = int64_t(blockIdx.x) * kTopkTile;
-  mark_excluded(bm, ex, nex, i0);
-  const uint32_t b0 = w.st[ST_B0];
-  const uint64_t theta = (uint64_t(w.st[ST_PHI]) << 32) | w.st[ST_PLO];
+  __shared__ uint64_t mask[4][kChunk / 64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int lbase = wid * kChunk;
-  if (i0 + lbase >= n) return;
-  uint32_t pos = w.cnt[int64_t(blockIdx.x) * 4 + wid];
-  for (int r = 0; r < kChunk / 256; ++r) {
-    const int l = lbase + r * 256 + lane * 4;
-    uint32_t kv[4];
-    bool ok[4];
-    keys4(key, i0 + l, n, bm, l, kv, ok);
-    bool sel[4];
-    uint32_t mine = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t d = kv[u] >> 20;
-      sel[u] = ok[u] && (d > b0 || (d == b0 && composite(kv[u], uint32_t(i0 + l + u)) >= theta));
-      mine += sel[u];
+  const int64_t c = int64_t(blockIdx.x) * 4 + wid;
+  if (c >= w.nchunks) return;  // uniform per wave; no block barrier follows
+  uint64_t* mk = mask[wid];
+  mk[lane] = 0;
+  const uint64_t theta = (uint64_t(w.st[ST_PHI]) << 32) | w.st[ST_PLO];
+  const uint32_t base = uint32_t(c * kChunk);
+  const uint32_t na = w.acnt[c], nc = w.ccnt[c];
+  const uint32_t* asrc = w.above + c * kChunk;
+  const uint32_t* csrc = w.cand + c * kChunk;
+  const uint32_t* ksrc = w.ckey + c * kChunk;
+  __builtin_amdgcn_wave_barrier();
+  for (uint32_t j = lane; j < na; j += 64) {
+    const uint32_t l = asrc[j] - base;
+    atomicOr(reinterpret_cast<unsigned long long*>(&mk[l >> 6]), 1ull << (l & 63));
+  }
+  for (uint32_t j = lane; j < nc; j += 64) {
+    const uint32_t i = csrc[j];
+    if (composite(ksrc[j], i) >= theta) {
+      const uint32_t l = i - base;
+      atomicOr(reinterpret_cast<unsigned long long*>(&mk[l >> 6]), 1ull << (l & 63));
     }
-    uint32_t tot;
-    uint32_t p = pos + wave_excl(mine, tot);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (sel[u]) {
-        out_idx[p] = uint32_t(i0 + l + u);
-        if (out_val) out_val[p] = valsrc[i0 + l + u];
-        ++p;
-      }
-    pos += tot;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0);
+  uint64_t bits = mk[lane];
+  uint32_t tot;
+  uint32_t p = w.cnt[c] + wave_excl(uint32_t(__popcll(bits)), tot);
+  while (bits) {
+    const int b = __builtin_ctzll(bits);
+    bits &= bits - 1;
+    const uint32_t i = base + uint32_t(lane) * 64u + uint32_t(b);
+    out_idx[p] = i;
+    if (out_val) out_val[p] = valsrc[i];
+    ++p;
   }
 }
 
@@ -521,8 +540,7 @@ usaf_status topk_run(KF key, int64_t n, int64_t k, const uint32_t* ex, int64_t n
   }
   hipLaunchKernelGGL(topk_cand_count_kernel<KF>, dim3(cgrid), blk, 0, st, key, w, gate);
   hipLaunchKernelGGL(scan_u32_kernel, dim3(1), dim3(1024), 0, st, w.cnt, w.nchunks, gate);
-  hipLaunchKernelGGL(topk_pass_c_kernel<KF>, grid, blk, 0, st, key, n, ex, nex, w, out_idx,
-                     out_val, valsrc, gate);
+  hipLaunchKernelGGL(topk_pass_c_kernel, grid, blk, 0, st, w, out_idx, out_val, valsrc, gate);
   timer_end(USAF_K_TOPK, st);
   USAF_LAUNCH_CHECK();
   return USAF_OK;
