@@ -310,6 +310,8 @@ def main():
     ap.add_argument("--no-scan", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-mixtral", action="store_true")
+    ap.add_argument("--mixtral-only", action="store_true",
+                    help="only the Mixtral-shaped layer leg (prints its JSON object)")
     ap.add_argument("--scan-only", action="store_true",
                     help="skip the timed train steps; run only the RigL scan (profiling)")
     ap.add_argument("--print-sha", action="store_true",
@@ -350,6 +352,9 @@ def main():
     N = 3 * E * H * I
     k = (N * 5) // 1000
     lr = 1e-3
+    if args.mixtral_only:
+        print(json.dumps({"mixtral": mixtral_layer(capi, synth, layer_mod, 10, lr)}), flush=True)
+        return
     log("generating the seeded Qwen3-shaped layer")
     d = synth.moe_layer(*dims, bf16=True, seeds=(0, 1, 2, 3, 4))
     idx = synth.random_mask(N, k, 5)

@@ -731,19 +731,36 @@ constexpr int kFwdWM = 2, kFwdWN = 4;                  // 8 waves: 2 per SIMD
 constexpr int kDaWN = 2;                               // dA: 4 waves (its epilogue prefers them)
 constexpr int kDwBM = 256, kDwBN = 256, kDwNS = 2;     // dense dW: 128 KiB LDS
 
+// Groups of at least kBigRows rows on average (few large experts) take
+// 256-row tiles: twice the MFMA work per staged byte, and little ragged waste.
+constexpr int kBigRows = 512;
+constexpr int kBigBM = 256, kBigNS = 2;  // 2 x 64 KiB LDS stages, 8 waves of 128 x 64
+static bool big_groups(const usaf_moe_shape& s) {
+  return int64_t(s.T) * s.K >= int64_t(kBigRows) * s.E;
+}
+
+template <template <int, int, int, int, int> class M, class... Args>
+static usaf_status launch_fwd(const usaf_moe_shape& s, int NT, hipStream_t st, int kclass,
+                              Args... args) {
+  if (big_groups(s))
+    return launch_persistent(M<kBigBM, kFwdBN, kBigNS, kFwdWM, kFwdWN>{args...},
+                             grouped_tiles_bound(s, NT, kBigBM), st, kclass);
+  return launch_persistent(M<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN>{args...},
+                           grouped_tiles_bound(s, NT, kFwdBM), st, kclass);
+}
+
 usaf_status mfma_gate_up(const usaf_moe_shape& s, const bf16_t* X, const bf16_t* Wgu,
                          const int32_t* offsets, const int32_t* perm, bf16_t* gu, bf16_t* a,
                          hipStream_t st) {
   const int NT = int(ceil_div(s.I, kFwdBN / 2));
-  return launch_persistent(g2::MGateUp<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN>{X, Wgu, offsets, perm, gu, a, s.H, s.E, s.K, s.I, NT},
-                   grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_GATE_UP);
+  return launch_fwd<g2::MGateUp>(s, NT, st, USAF_K_GATE_UP, X, Wgu, offsets, perm, gu, a, s.H,
+                                 s.E, s.K, s.I, NT);
 }
 
 usaf_status mfma_down(const usaf_moe_shape& s, const bf16_t* a, const bf16_t* Wd,
                       const int32_t* offsets, float* ybuf, hipStream_t st) {
   const int NT = int(ceil_div(s.H, kFwdBN));
-  return launch_persistent(g2::MDown<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN>{a, Wd, offsets, ybuf, s.H, s.E, s.I, NT},
-                   grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DOWN);
+  return launch_fwd<g2::MDown>(s, NT, st, USAF_K_DOWN, a, Wd, offsets, ybuf, s.H, s.E, s.I, NT);
 }
 
 int mfma_dw_partials(const usaf_moe_shape& s) { return kDaWN * int(ceil_div(s.I, kFwdBN)); }
@@ -753,6 +770,11 @@ usaf_status mfma_da(const usaf_moe_shape& s, const bf16_t* dY, const bf16_t* Wd,
                     const bf16_t* gu, const bf16_t* a, bf16_t* dgu, float* dwpart,
                     hipStream_t st) {
   const int NT = int(ceil_div(s.I, kFwdBN));
+  if (big_groups(s))  // 8 waves of 64 x 128 on 256-row tiles
+    return launch_persistent(g2::MDa<kBigBM, kFwdBN, kBigNS, 4, kDaWN>{dY, Wd, offsets, perm, topk_w, gu,
+                                                                       a, dgu, dwpart, s.H, s.E, s.K,
+                                                                       s.I, NT, kDaWN * NT},
+                             grouped_tiles_bound(s, NT, kBigBM), st, USAF_K_DA);
   return launch_persistent(g2::MDa<kFwdBM, kFwdBN, kFwdNS, 2, kDaWN>{dY, Wd, offsets, perm, topk_w, gu, a, dgu, dwpart, s.H,
                                            s.E, s.K, s.I, NT, kDaWN * NT},
                    grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DA);
@@ -761,8 +783,7 @@ usaf_status mfma_da(const usaf_moe_shape& s, const bf16_t* dY, const bf16_t* Wd,
 usaf_status mfma_dx(const usaf_moe_shape& s, const bf16_t* dgu, const bf16_t* Wgu,
                     const int32_t* offsets, float* vbuf, hipStream_t st) {
   const int NT = int(ceil_div(s.H, kFwdBN));
-  return launch_persistent(g2::MDx<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN>{dgu, Wgu, offsets, vbuf, s.H, s.E, s.I, NT},
-                   grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DX);
+  return launch_fwd<g2::MDx>(s, NT, st, USAF_K_DX, dgu, Wgu, offsets, vbuf, s.H, s.E, s.I, NT);
 }
 
 usaf_status mfma_dense_dw(const usaf_moe_shape& s, const bf16_t* X, const bf16_t* dY,

@@ -152,6 +152,8 @@ CASES = [
     # column-tiled masked gradient: gate_up has H > 2048 columns, down has I > 2048
     ("coltiled_gate_up_bf16", (64, 4096, 4, 2, 64), 1, (70, 71, 72, 73, 74)),
     ("coltiled_down_bf16", (48, 128, 3, 2, 2560), 1, (80, 81, 82, 83, 84)),
+    # >= 512 rows per expert on average: the 256-row GEMM tiles, ragged
+    ("big_groups_bf16", (1100, 256, 4, 2, 96), 1, (85, 86, 87, 88, 89)),
 ]
 
 
