@@ -21,9 +21,10 @@ namespace usaf {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kSlots = 8;        // slots per staged chunk
-constexpr int kMaxEnt = 16;      // entries per thread per batch
-constexpr int kMaxRB = 512;      // max rows per block
-constexpr int kMaxCB = 1536;     // max columns per block (kMaxCB/8 + kMaxRB/8 <= 256)
+constexpr int kThreads = 512;    // 8 waves per block, one block per CU
+constexpr int kMaxEnt = 24;      // entries per thread per pass
+constexpr int kMaxRB = 1024;     // max rows per block
+constexpr int kMaxCB = 2048;     // max columns per block (kMaxCB/8 + kMaxRB/8 <= kThreads)
 constexpr int kTokTab = 2048;    // slots per token-table window
 constexpr int kLsBytes = kMaxRB * kSlots * 4;
 constexpr int kRsBytes = kMaxCB * kSlots * 2;
@@ -173,7 +174,7 @@ __device__ __forceinline__ void stage_store(int b, int nblk_r, const StageRegs& 
 }
 
 template <bool kDown>
-__global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
+__global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_l[kLsBytes];
   __shared__ __attribute__((aligned(16))) unsigned char lds_r[kRsBytes];
   __shared__ int rowpre[kMaxRB + 1];
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
 
   // entries of this tile: per row r, the plan segment (e, r, ct)
   const int64_t q_r0 = A.qbase + (int64_t(e) * A.R + r_lo) * A.nct + ct;
-  for (int r = tid; r < nr; r += 256) {
+  for (int r = tid; r < nr; r += kThreads) {
     const int64_t q = q_r0 + int64_t(r) * A.nct;
     const uint32_t s0 = A.seg[q];
     rstart[r] = s0;
@@ -224,10 +225,10 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
   const int ne = A.offsets[e + 1] - off;
   const int nblk_r = (ncol + 7) >> 3, nblk_l = (nr + 7) >> 3;
 
-  for (int q0 = 0, per = 0; q0 < nent; q0 += 256 * per) {
+  for (int q0 = 0, per = 0; q0 < nent; q0 += kThreads * per) {
     // this pass: per entries for every thread (spread evenly, at most
     // kMaxEnt), thread tid taking q0 + tid*per + i
-    per = min(kMaxEnt, (nent - q0 + 255) / 256);
+    per = min(kMaxEnt, (nent - q0 + kThreads - 1) / kThreads);
     uint32_t coord[kMaxEnt];  // (row - r_lo) << 16 | (col - c0), or ~0 when unused
     float acc[kMaxEnt];
     {
@@ -254,18 +255,17 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
     }
     // stream the expert's slots, a token-table window at a time, in chunks
     // of kSlots staged through LDS
-    const bool stager = tid < nblk_r + nblk_l;  // <= 256 staging blocks: one per thread
+    const bool stager = tid < nblk_r + nblk_l;  // <= kThreads staging blocks: one per thread
     for (int w0 = 0; w0 < ne; w0 += kTokTab) {
       const int wn = min(kTokTab, ne - w0);
       __syncthreads();  // previous window fully consumed
-      for (int p = tid; p < wn; p += 256) {
+      for (int p = tid; p < wn; p += kThreads) {
         const int sid = A.perm[off + w0 + p];
         tok_tab[p] = sid / A.K;
         if (kDown) w_tab[p] = A.topk_w[sid];
       }
       __syncthreads();
-      // two chunks in flight: chunk c+2 is fetched into the register stage
-      // that chunk c just left, so each fetch has two chunks of work to land
+      // chunk c+1 is fetched into registers while chunk c is consumed
       auto compute = [&]() {
         uint32_t prow = 0xffffffffu;
         uint4 lb16 = make_uint4(0, 0, 0, 0);
@@ -308,25 +308,14 @@ __global__ __launch_bounds__(256) void masked_dw_sddmm_kernel(MaskedArgs A) {
           acc[i] = a;
         }
       };
-      StageRegs sr0, sr1;
-      if (stager) {
-        stage_fetch<kDown>(A, tid, nblk_r, 0, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr0);
-        if (kSlots < wn)
-          stage_fetch<kDown>(A, tid, nblk_r, kSlots, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr1);
-      }
-      for (int p0 = 0; p0 < wn; p0 += 2 * kSlots) {
+      StageRegs sr;
+      if (stager) stage_fetch<kDown>(A, tid, nblk_r, 0, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr);
+      for (int p0 = 0; p0 < wn; p0 += kSlots) {
         __syncthreads();  // previous chunk fully consumed
-        if (stager) stage_store<kDown>(tid, nblk_r, sr0, lds_l, lds_r);
+        if (stager) stage_store<kDown>(tid, nblk_r, sr, lds_l, lds_r);
         __syncthreads();
-        if (stager && p0 + 2 * kSlots < wn)
-          stage_fetch<kDown>(A, tid, nblk_r, p0 + 2 * kSlots, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr0);
-        compute();
-        if (p0 + kSlots >= wn) break;
-        __syncthreads();
-        if (stager) stage_store<kDown>(tid, nblk_r, sr1, lds_l, lds_r);
-        __syncthreads();
-        if (stager && p0 + 3 * kSlots < wn)
-          stage_fetch<kDown>(A, tid, nblk_r, p0 + 3 * kSlots, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr1);
+        if (stager && p0 + kSlots < wn)
+          stage_fetch<kDown>(A, tid, nblk_r, p0 + kSlots, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr);
         compute();
       }
     }
@@ -364,9 +353,9 @@ int64_t masked_plan_segments(const usaf_moe_shape& s) {
   return int64_t(s.E) * 2 * s.I * nct0 + int64_t(s.E) * s.H * nct1;
 }
 
-// Row tile: about 3000 selected entries per block at this density.
+// Row tile: about 12 selected entries per thread of a block at this density.
 static int row_tile(int R, int CB, double density) {
-  const double target = 3000.0 / (double(CB) * (density > 0 ? density : 1e-9));
+  const double target = 20.0 * kThreads / (double(CB) * (density > 0 ? density : 1e-9));
   int rb = 32;
   while (rb * 2 <= kMaxRB && rb * 2 <= target) rb *= 2;
   return rb < R ? rb : R;
@@ -407,9 +396,9 @@ usaf_status masked_dw_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64_t
     A.nrt = int(ceil_div(A.R, A.RB));
     const int64_t blocks = (int64_t(s.E) * A.nrt * A.nct + 7) / 8 * 8;
     if (tensor == 0)
-      hipLaunchKernelGGL(masked_dw_sddmm_kernel<false>, dim3(unsigned(blocks)), dim3(256), 0, st, A);
+      hipLaunchKernelGGL(masked_dw_sddmm_kernel<false>, dim3(unsigned(blocks)), dim3(kThreads), 0, st, A);
     else
-      hipLaunchKernelGGL(masked_dw_sddmm_kernel<true>, dim3(unsigned(blocks)), dim3(256), 0, st, A);
+      hipLaunchKernelGGL(masked_dw_sddmm_kernel<true>, dim3(unsigned(blocks)), dim3(kThreads), 0, st, A);
     USAF_LAUNCH_CHECK();
   }
   timer_end(USAF_K_MASKED_DW, st);
