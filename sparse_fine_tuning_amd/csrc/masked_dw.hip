@@ -12,6 +12,8 @@
 // a contiguous run of the block's entries (consecutive entries mostly share
 // a row, whose staged values stay in registers).  gate_up uses bf16 dot2
 // (fp32 accumulate); down stages w_p * dY in fp32 and uses fp32 FMA.
+#include <cmath>
+
 #include "common.hpp"
 #include "moe_internal.hpp"
 #include "timing.hpp"
@@ -353,12 +355,17 @@ int64_t masked_plan_segments(const usaf_moe_shape& s) {
   return int64_t(s.E) * 2 * s.I * nct0 + int64_t(s.E) * s.H * nct1;
 }
 
-// Row tile: about 12 selected entries per thread of a block at this density.
+// Row tiling: as few row tiles as the LDS staging allows (the expert's slot
+// stream is re-read once per tile), but enough that each block's entries
+// fit one pass of about 20 per thread.  Returns the tile height (a multiple
+// of 8).
 static int row_tile(int R, int CB, double density) {
-  const double target = 20.0 * kThreads / (double(CB) * (density > 0 ? density : 1e-9));
-  int rb = 32;
-  while (rb * 2 <= kMaxRB && rb * 2 <= target) rb *= 2;
-  return rb < R ? rb : R;
+  const double per_row = double(CB) * (density > 0 ? density : 1e-9);
+  int64_t nrt = ceil_div(int64_t(R), int64_t(kMaxRB));
+  const int64_t by_entries = int64_t(std::ceil(double(R) * per_row / (20.0 * kThreads)));
+  if (by_entries > nrt) nrt = by_entries;
+  const int64_t rb = ceil_div(ceil_div(int64_t(R), nrt), int64_t(8)) * 8;
+  return int(rb < R ? rb : R);
 }
 
 usaf_status masked_dw_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64_t nnz,
