@@ -41,13 +41,13 @@ WRITE_SCALE = 1.0   # and 1,048,576 KiB of WRITE_SIZE
 # kernel class -> (fetch KiB, write KiB, sources hash); masked_dw and adam sum
 # the launches of one step (plan + two SDDMM launches; expert + router Adam)
 COUNTER_TRAFFIC = {
-    "router_gemm": (8846, 16384, "c0729b3485a0e65d"),
-    "gate_up": (497397, 147458, "c0729b3485a0e65d"),
-    "down": (226652, 262144, "c0729b3485a0e65d"),
-    "da": (374458, 100618, "c0729b3485a0e65d"),
-    "dx": (477064, 262144, "c0729b3485a0e65d"),
-    "masked_dw": (110258 + 71967 + 7317, 7870 + 3932 + 2560, "a607433f3e1ce9ed"),
-    "adam": (185598 + 2060, 114540 + 3072, "26f53ce5cbbb540f"),
+    "router_gemm": (8847, 16384, "602634fc2a2e897c"),
+    "gate_up": (549330, 149286, "602634fc2a2e897c"),
+    "down": (249243, 263079, "602634fc2a2e897c"),
+    "da": (454863, 153460, "602634fc2a2e897c"),
+    "dx": (717044, 262820, "602634fc2a2e897c"),
+    "masked_dw": (176810, 13592, "d133da227a39acf8"),
+    "adam": (28637, 128691, "b67b67111d5b8531"),
 }
 KERNEL_SOURCES = {
     c: ("gemm_mfma.hpp", "gemm_v2.hpp", "moe_mfma.hip", "common.hpp", "moe_internal.hpp")
@@ -322,7 +322,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not "
-              f"sharded across GPUs in this build.", file=sys.stderr)
+              f"sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
 
     if args.print_sha:
