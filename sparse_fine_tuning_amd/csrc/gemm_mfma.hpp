@@ -1,17 +1,15 @@
-// bf16 MFMA grouped GEMM skeleton for gfx950 (CDNA4, wave64).
+// bf16 MFMA GEMM skeleton for gfx950 (CDNA4, wave64), used by the router
+// logits GEMM (split over the contraction, fp32 master weights rounded to
+// bf16 while staging).  The expert GEMMs use the direct-to-LDS kernel in
+// gemm_v2.hpp, which includes this header for its tile and vector types.
 //
 // Block tile 128 x 128 x 64, 256 threads = 4 waves in a 2 x 2 grid, each wave
 // computing 64 x 64 with v_mfma_f32_32x32x16_bf16 (fp32 accumulate).  Both
 // operand tiles are staged in LDS as [row][k] (k contiguous, rows padded to
 // 144 B so the 16 rows a quarter-wave reads land in distinct banks), double
 // buffered: the next k-tile is fetched into registers while the current one
-// feeds the matrix cores.
-//
-// An operand whose contraction index is contiguous in memory ("k-contiguous")
-// is copied with 16-byte loads and stores.  An operand whose row index is
-// contiguous ("row-contiguous", e.g. a weight used as [K][N], or token-major
-// activations contracted over tokens) is loaded as 8 k-rows x 4 elements per
-// thread and transposed in registers before the 16-byte LDS store.
+// feeds the matrix cores.  Both operands are k-contiguous and are copied
+// with 16-byte loads and stores.
 //
 // MFMA 32x32 output layout (per lane l, accumulator element r = 0..15):
 //   row = 8*(r/4) + 4*(l/32) + (r%4),  col = l%32.
@@ -41,63 +39,10 @@ struct MTile {
 // Logical tile ids are XCD-remapped (xcd_remap_blocks) so tiles that share
 // weights or rows run on one XCD and share its L2.
 
-// Logical tile L -> (expert, column tile, row tile) for groups whose row
-// counts come from device offsets[E+1]; tiles ordered expert-major, then
-// column tile, then row tile.  Wave 0 scans the experts 64 at a time and
-// broadcasts through LDS; returns false (for the whole block) past the end.
-__device__ __forceinline__ bool grouped_m_tile(const int32_t* __restrict__ offsets, int E, int NT,
-                                               int L, MTile& t) {
-  __shared__ int sh[4];
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x < 64) {
-    int base = 0;
-    bool found = false;
-    for (int e0 = 0; e0 < E && !found; e0 += 64) {
-      const int e = e0 + lane;
-      const int o0 = e < E ? offsets[e] : 0;
-      const int cnt = e < E ? offsets[e + 1] - o0 : 0;
-      const int tiles = ((cnt + kMB - 1) / kMB) * NT;
-      int incl = tiles;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int v = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += v;
-      }
-      const int excl = incl - tiles;
-      const bool hit = tiles > 0 && L >= base + excl && L < base + incl;
-      const uint64_t bal = __ballot(hit);
-      if (bal) {
-        if (lane == __ffsll((long long)bal) - 1) {
-          sh[0] = e;
-          sh[1] = L - base - excl;
-          sh[2] = cnt;
-          sh[3] = o0;
-        }
-        found = true;
-      }
-      base += __shfl(incl, 63, 64);
-    }
-    if (!found && lane == 0) sh[0] = -1;
-  }
-  __syncthreads();
-  t.e = sh[0];
-  if (t.e < 0) return false;
-  const int rem = sh[1], cnt = sh[2];
-  const int mts = (cnt + kMB - 1) / kMB;
-  t.nt = rem / mts;
-  t.m0 = (rem - t.nt * mts) * kMB;
-  t.mc = min(kMB, cnt - t.m0);
-  t.off = sh[3];
-  return true;
-}
-
 // ---------------------------------------------------------------------------
 // Operand loaders.  Src supplies:
 //   k-contiguous:   int rows;  const E* row(int r) (row r's element 0), or
 //                   nullptr for rows past the end; int kend.
-//   row-contiguous: int rows (multiple of 4); int kend;
-//                   const bf16_t* kptr(int k) (element (row 0, k));
-//                   float scale(int k) when Src::kScaled.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
@@ -189,61 +134,6 @@ struct KcLoader<float> {
                                  live ? pack_bf16x2(y[i].x, y[i].y) : 0u,
                                  live ? pack_bf16x2(y[i].z, y[i].w) : 0u);
       *reinterpret_cast<uint4*>(&S[((tid >> 3) + 32 * i) * kLdsRow + 8 * c]) = v;
-    }
-  }
-};
-
-// Row-contiguous source: thread (mq = tid%32, kq = tid/32) loads k-rows
-// kq*8 .. kq*8+7 of rows 4*mq .. 4*mq+3, then writes those 4 rows' 8 k-values
-// as one 16-byte LDS store each.
-template <class Src>
-struct RcLoader {
-  Src s;
-  int mq, kq;
-  bool live;
-  uint2 v[8];
-  float sc[8];
-  __device__ __forceinline__ void init(const Src& src, int tid) {
-    s = src;
-    mq = tid & 31;
-    kq = tid >> 5;
-    live = 4 * mq < s.rows;
-  }
-  __device__ __forceinline__ void load(int k0) {
-    const int col = live ? 4 * mq : 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = min(k0 + 8 * kq + i, s.kend - 1);
-      v[i] = *reinterpret_cast<const uint2*>(s.kptr(k) + col);
-      if constexpr (Src::kScaled) sc[i] = s.scale(k);
-    }
-    kbase = k0 + 8 * kq;
-  }
-  int kbase;
-  __device__ __forceinline__ void store(bf16_t* S, int) const {
-    // k-row i is live when inside [.., kend) and the thread's rows are live
-    uint2 u[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint2 x = v[i];
-      if constexpr (Src::kScaled) {
-        x.x = pack_bf16x2(bf2f(bf16_t(x.x & 0xffffu)) * sc[i], bf2f(bf16_t(x.x >> 16)) * sc[i]);
-        x.y = pack_bf16x2(bf2f(bf16_t(x.y & 0xffffu)) * sc[i], bf2f(bf16_t(x.y >> 16)) * sc[i]);
-      }
-      const bool ok = live && kbase + i < s.kend;
-      u[i] = make_uint2(ok ? x.x : 0u, ok ? x.y : 0u);
-    }
-    // element j of k-row i: 16-bit half (j&1) of word (j>>1) of u[i]
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t w[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t a = (j < 2) ? u[2 * d].x : u[2 * d].y;
-        const uint32_t b = (j < 2) ? u[2 * d + 1].x : u[2 * d + 1].y;
-        w[d] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-      }
-      *reinterpret_cast<uint4*>(&S[(4 * mq + j) * kLdsRow + 8 * kq]) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 };

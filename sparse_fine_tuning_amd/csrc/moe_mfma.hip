@@ -16,14 +16,6 @@ namespace usaf {
 // ---------------------------------------------------------------------------
 // Operand sources
 // ---------------------------------------------------------------------------
-// Rows gathered by token: row r of the tile is act[tok(perm[base_row + r])].
-struct TokRows {
-  typedef bf16_t elem_t;
-  const bf16_t* act; const int32_t* perm; int K; int base_row; int rows; int ld; int kend;
-  __device__ __forceinline__ const bf16_t* row(int r) const {
-    return act + int64_t(perm[base_row + r] / K) * ld;
-  }
-};
 // Plain rows: row r at base + r*ld.
 struct PlainRows {
   typedef bf16_t elem_t;
@@ -36,248 +28,9 @@ struct RouterRows {
   const float* base; int64_t ld; int rows; int kend;
   __device__ __forceinline__ const float* row(int r) const { return base + int64_t(r) * ld; }
 };
-// gate_up weight rows for a 128-column tile holding 64 features: columns
-// [64w, 64w+32) are gate features F0+32w.., [64w+32, 64w+64) the same up
-// features, so each wave column-half holds matching (gate, up) pairs.
-struct GateUpRows {
-  typedef bf16_t elem_t;
-  const bf16_t* We; int F0; int I; int H; int rows; int kend;
-  __device__ __forceinline__ const bf16_t* row(int c) const {
-    const int w = c & 63;
-    const int f = F0 + 32 * (c >> 6) + (w & 31);
-    if (f >= I) return nullptr;
-    return We + int64_t(w < 32 ? f : I + f) * H;
-  }
-};
-// Row-contiguous operands: element (row, k) at kptr(k)[row].
-struct StridedK {
-  static constexpr bool kScaled = false;
-  const bf16_t* base; int64_t ld; int rows; int kend;
-  __device__ __forceinline__ const bf16_t* kptr(int k) const { return base + int64_t(k) * ld; }
-  __device__ __forceinline__ float scale(int) const { return 1.f; }
-};
-// k = a slot of expert e (expert-major row off+k); element (row, k) at
-// act[row_of(k)*ld + col0 + row], optionally scaled by the slot's routing weight.
-template <bool kTok, bool kScale>
-struct SlotK {
-  static constexpr bool kScaled = kScale;
-  const bf16_t* act; const int32_t* perm; const float* topk_w;
-  int K; int off; int64_t ld; int col0; int rows; int kend;
-  __device__ __forceinline__ const bf16_t* kptr(int k) const {
-    const int64_t r = kTok ? int64_t(perm[off + k] / K) : int64_t(off + k);
-    return act + r * ld + col0;
-  }
-  __device__ __forceinline__ float scale(int k) const { return topk_w[perm[off + k]]; }
-};
-
 // ---------------------------------------------------------------------------
 // Problems
 // ---------------------------------------------------------------------------
-// gate_up forward + SwiGLU: per expert, [g|u] = X[tokens] W_gu[e]^T.
-struct MGateUp {
-  const bf16_t* X; const bf16_t* Wgu; const int32_t* offsets; const int32_t* perm;
-  bf16_t* gu; bf16_t* a;
-  int H, E, K, I, NT;
-  using ALoader = KcLoader<bf16_t>;
-  using BLoader = KcLoader<bf16_t>;
-  __device__ bool tile(int L, MTile& t) const {
-    if (!grouped_m_tile(offsets, E, NT, L, t)) return false;
-    t.kb = 0; t.ke = H; t.n0 = t.nt * 64; t.nc = 0;
-    return true;
-  }
-  __device__ TokRows a_src(const MTile& t) const { return TokRows{X, perm, K, t.off + t.m0, t.mc, H, H}; }
-  __device__ GateUpRows b_src(const MTile& t) const {
-    return GateUpRows{Wgu + int64_t(t.e) * 2 * I * H, t.n0, I, H, kNB, H};
-  }
-  __device__ void epilogue(const MTile& t, f32x16_t (&acc)[2][2], int wm, int wn, int lane) const {
-    const int f = t.n0 + 32 * wn + (lane & 31);
-    if (f >= I) return;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = acc_row(wm, i, r, lane);
-        if (row >= t.mc) continue;
-        const int64_t p = t.off + t.m0 + row;
-        const float g = bf2f(f2bf(acc[i][0][r]));
-        const float u = bf2f(f2bf(acc[i][1][r]));
-        gu[p * 2 * I + f] = f2bf(g);
-        gu[p * 2 * I + I + f] = f2bf(u);
-        a[p * I + f] = f2bf(silu_f(g) * u);
-      }
-  }
-};
-
-// down forward: ybuf[p, :] = a[p, :] W_d[e]^T (fp32 rows, expert-major).
-struct MDown {
-  const bf16_t* a; const bf16_t* Wd; const int32_t* offsets; float* ybuf;
-  int H, E, I, NT;
-  using ALoader = KcLoader<bf16_t>;
-  using BLoader = KcLoader<bf16_t>;
-  __device__ bool tile(int L, MTile& t) const {
-    if (!grouped_m_tile(offsets, E, NT, L, t)) return false;
-    t.kb = 0; t.ke = I; t.n0 = t.nt * kNB; t.nc = min(kNB, H - t.n0);
-    return true;
-  }
-  __device__ PlainRows a_src(const MTile& t) const {
-    return PlainRows{a + int64_t(t.off + t.m0) * I, I, t.mc, I};
-  }
-  __device__ PlainRows b_src(const MTile& t) const {
-    return PlainRows{Wd + (int64_t(t.e) * H + t.n0) * I, I, t.nc, I};
-  }
-  __device__ void epilogue(const MTile& t, f32x16_t (&acc)[2][2], int wm, int wn, int lane) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = acc_col(wn, j, lane);
-        if (col >= t.nc) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = acc_row(wm, i, r, lane);
-          if (row < t.mc) ybuf[int64_t(t.off + t.m0 + row) * H + t.n0 + col] = acc[i][j][r];
-        }
-      }
-  }
-};
-
-// dA backward: U = dY[tokens] W_d[e]; epilogue forms dGU and per-(row,
-// column-half) partial dot products <U, a> for the routing-weight gradient.
-struct MDa {
-  const bf16_t* dY; const bf16_t* Wd; const int32_t* offsets; const int32_t* perm;
-  const float* topk_w; const bf16_t* gu; const bf16_t* a; bf16_t* dgu; float* dwpart;
-  int H, E, K, I, NT, NTP;
-  using ALoader = KcLoader<bf16_t>;
-  using BLoader = RcLoader<StridedK>;
-  __device__ bool tile(int L, MTile& t) const {
-    if (!grouped_m_tile(offsets, E, NT, L, t)) return false;
-    t.kb = 0; t.ke = H; t.n0 = t.nt * kNB; t.nc = min(kNB, I - t.n0);
-    return true;
-  }
-  __device__ TokRows a_src(const MTile& t) const { return TokRows{dY, perm, K, t.off + t.m0, t.mc, H, H}; }
-  __device__ StridedK b_src(const MTile& t) const {
-    return StridedK{Wd + int64_t(t.e) * H * I + t.n0, I, t.nc, H};
-  }
-  __device__ void epilogue(const MTile& t, f32x16_t (&acc)[2][2], int wm, int wn, int lane) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = acc_row(wm, i, r, lane);
-        const bool vrow = row < t.mc;
-        const int64_t p = t.off + t.m0 + (vrow ? row : 0);
-        const float wt = vrow ? topk_w[perm[p]] : 0.f;
-        float part = 0.f;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = acc_col(wn, j, lane);
-          if (vrow && col < t.nc) {
-            const int f = t.n0 + col;
-            const float U = acc[i][j][r];
-            part = fmaf(U, bf2f(a[p * I + f]), part);
-            const float da = wt * U;
-            const float g = bf2f(gu[p * 2 * I + f]);
-            const float u = bf2f(gu[p * 2 * I + I + f]);
-            const float sg = sigmoid_f(g);
-            dgu[p * 2 * I + f] = f2bf(da * u * sg * (1.f + g * (1.f - sg)));
-            dgu[p * 2 * I + I + f] = f2bf(da * g * sg);
-          }
-        }
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-        if ((lane & 31) == 0 && vrow) dwpart[p * NTP + 2 * t.nt + wn] = part;
-      }
-  }
-};
-
-// dX backward: vbuf[p, :] = dGU[p, :] W_gu[e]  (fp32 rows, expert-major).
-struct MDx {
-  const bf16_t* dgu; const bf16_t* Wgu; const int32_t* offsets; float* vbuf;
-  int H, E, I, NT;
-  using ALoader = KcLoader<bf16_t>;
-  using BLoader = RcLoader<StridedK>;
-  __device__ bool tile(int L, MTile& t) const {
-    if (!grouped_m_tile(offsets, E, NT, L, t)) return false;
-    t.kb = 0; t.ke = 2 * I; t.n0 = t.nt * kNB; t.nc = min(kNB, H - t.n0);
-    return true;
-  }
-  __device__ PlainRows a_src(const MTile& t) const {
-    return PlainRows{dgu + int64_t(t.off + t.m0) * 2 * I, 2 * I, t.mc, 2 * I};
-  }
-  __device__ StridedK b_src(const MTile& t) const {
-    return StridedK{Wgu + int64_t(t.e) * 2 * I * H + t.n0, H, t.nc, 2 * I};
-  }
-  __device__ void epilogue(const MTile& t, f32x16_t (&acc)[2][2], int wm, int wn, int lane) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = acc_col(wn, j, lane);
-        if (col >= t.nc) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = acc_row(wm, i, r, lane);
-          if (row < t.mc) vbuf[int64_t(t.off + t.m0 + row) * H + t.n0 + col] = acc[i][j][r];
-        }
-      }
-  }
-};
-
-// Dense weight gradients of one expert, contraction over its slots:
-//   gate_up: dW[r, c] = sum_p dGU[p, r] X[tok(p), c]      (rows 2I, cols H)
-//   down:    dW[r, c] = sum_p w_p dY[tok(p), r] a[p, c]   (rows H,  cols I)
-// (w_p dY is rounded to bf16 while staging for the matrix cores.)
-template <bool kDown>
-struct MDenseDw {
-  const bf16_t* L; const bf16_t* R; const int32_t* offsets; const int32_t* perm;
-  const float* topk_w; float* dW;
-  int H, E, K, I, MT, NT;
-  int64_t ngu;
-  using ALoader = RcLoader<SlotK<kDown, kDown>>;
-  using BLoader = RcLoader<SlotK<!kDown, false>>;
-  __device__ int rows_total() const { return kDown ? H : 2 * I; }
-  __device__ int cols_total() const { return kDown ? I : H; }
-  __device__ bool tile(int Lt, MTile& t) const {
-    const int per = MT * NT;
-    t.e = Lt / per;
-    if (t.e >= E) return false;
-    const int rem = Lt - t.e * per;
-    t.nt = rem / MT;
-    t.m0 = (rem - t.nt * MT) * kMB;
-    t.n0 = t.nt * kNB;
-    t.mc = min(kMB, rows_total() - t.m0);
-    t.nc = min(kNB, cols_total() - t.n0);
-    t.off = offsets[t.e];
-    t.kb = 0;
-    t.ke = offsets[t.e + 1] - t.off;
-    return true;
-  }
-  __device__ SlotK<kDown, kDown> a_src(const MTile& t) const {
-    // gate_up: dGU rows (slot-major, ld 2I); down: dY rows by token, scaled by w
-    return SlotK<kDown, kDown>{L, perm, topk_w, K, t.off, kDown ? H : 2 * I, t.m0, t.mc, t.ke};
-  }
-  __device__ SlotK<!kDown, false> b_src(const MTile& t) const {
-    // gate_up: X rows by token (ld H); down: a rows (slot-major, ld I)
-    return SlotK<!kDown, false>{R, perm, topk_w, K, t.off, kDown ? I : H, t.n0, t.nc, t.ke};
-  }
-  __device__ void epilogue(const MTile& t, f32x16_t (&acc)[2][2], int wm, int wn, int lane) const {
-    const int64_t base = kDown ? ngu + int64_t(t.e) * H * I : int64_t(t.e) * 2 * I * H;
-    const int ldo = cols_total();
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = acc_col(wn, j, lane);
-        if (col >= t.nc) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = acc_row(wm, i, r, lane);
-          if (row < t.mc) dW[base + int64_t(t.m0 + row) * ldo + t.n0 + col] = acc[i][j][r];
-        }
-      }
-  }
-};
-
 // Router logits[T, E] = X bf16(Wr)^T, split over K into KS partial sums
 // parts[ks][T][E] (k-range ks*Kc .. (ks+1)*Kc), summed later in fixed order.
 struct MRouter {
