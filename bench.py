@@ -50,7 +50,7 @@ COUNTER_TRAFFIC = {
     "adam": (28637, 128691, "b67b67111d5b8531"),
 }
 KERNEL_SOURCES = {
-    c: ("gemm_mfma.hpp", "gemm_v2.hpp", "moe_mfma.hip", "common.hpp", "moe_internal.hpp")
+    c: ("gemm_mfma.hpp", "gemm_v2.hpp", "lds_dma.hpp", "moe_mfma.hip", "common.hpp", "moe_internal.hpp")
     for c in ("router_gemm", "gate_up", "down", "da", "dx", "dense_dw")
 }
 KERNEL_SOURCES.update(masked_dw=("masked_dw.hip", "common.hpp", "moe_internal.hpp"),

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "usaf.h"
 
 namespace usaf {
@@ -13,6 +16,18 @@ using bf16_t = uint16_t;  // bf16 storage (upper half of an fp32 word)
 constexpr int kWave = 64;
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// f(std::integral_constant<int, 0>{}), ..., f(...<N-1>): a loop whose index is
+// a compile-time constant in each copy (accumulator registers are indexed
+// statically even where the body is too large for the unroller).
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // bf16 -> fp32 is exact: the bf16 bits are the fp32 word's upper half.
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(uint32_t(h) << 16); }

@@ -32,52 +32,31 @@
 // Epilogues therefore read and write 4-column vectors per lane.
 #pragma once
 
+#include <type_traits>
 #include <utility>
 
 #include "common.hpp"
 #include "gemm_mfma.hpp"
+#include "lds_dma.hpp"
 
 namespace usaf {
 namespace g2 {
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-constexpr int kBM = 128, kBK = 64;
+constexpr int kBM = 128;
 
-// f(std::integral_constant<int, 0>{}), ..., f(...<N-1>): a loop whose index is
-// a compile-time constant in each copy (accumulator registers are indexed
-// statically even where the body is too large for the unroller).
-template <class F, int... Is>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
-  (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// s_waitcnt with vmcnt <= n (expcnt and lgkmcnt left unconstrained).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// One wave-wide 16-byte-per-lane copy: lane l's 16 bytes land at
-// lds_base + 16 l.  lds_base must be the same for the whole wave.  Issued as
-// inline assembly: completion is tracked only by the explicit vmcnt waits of
-// the pipeline (the compiler's own tracking would wait for every copy in
-// flight before each LDS read).  M0 holds the LDS address; one wait state
-// separates its write from the copy.
-__device__ __forceinline__ void dma16(const void* g, unsigned char* lds_base) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane(uint32_t(size_t((lds_void_t*)lds_base)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(l)
-               : "memory", "m0");
-}
+// Blocks per CU and waves per SIMD of a BM x BN tile with NS stages of BK
+// and NW waves: two blocks share a CU when both rings fit the 160 KiB LDS and
+// each block has at most 4 waves (so one block's epilogue overlaps the other's
+// main loop); otherwise one.
+template <int BM, int BN, int BK, int NS, int NW>
+struct Occupancy {
+  static constexpr int kLds = NS * (BM + BN) * BK * 2;
+  static constexpr int kBlocksPerCU = (2 * kLds + 1024 <= 160 * 1024 && NW <= 4) ? 2 : 1;
+  static constexpr int kWavesPerEU = (kBlocksPerCU * NW + 3) / 4;
+};
 
 // Logical tile L -> (expert, column tile, row tile of BM rows) over device
 // offsets[E+1]; tiles ordered expert-major, then column tile, then row tile.
@@ -144,15 +123,23 @@ __device__ __forceinline__ int out_col(int CW, int wn, int j, int g, int lane) {
 // kptr(k) (element (row 0, k); k < kend, always valid) and ncols (valid rows,
 // a multiple of 8).
 // ---------------------------------------------------------------------------
-template <int R, int NW = 4>
+template <int R, int NW = 4, int BK = 64>
 struct KMajor {
-  static constexpr int kRW = R / NW;     // rows copied by one wave
-  static constexpr int kInst = kRW / 8;  // dma instructions per wave per stage
-  static constexpr int kBytes = R * 128;
+  static_assert(BK == 32 || BK == 64, "64- or 128-byte rows");
+  static constexpr int kBK = BK;
+  static constexpr int kRowB = BK * 2;       // bytes per staged row
+  static constexpr int kCh = BK / 8;         // 16-byte chunks per row
+  static constexpr int kRPI = 64 / kCh;      // rows per dma instruction
+  static constexpr int kRW = R / NW;         // rows copied by one wave
+  static constexpr int kFragReads = 1;       // LDS read instructions per fragment
+  static constexpr int kInst = kRW / kRPI;   // dma instructions per wave per stage
+  static constexpr int kBytes = R * kRowB;
+  static_assert(kInst * kRPI == kRW, "rows per wave");
   // slot of 16-byte chunk q in row r: 64 banks serve 16 lanes of a 16-byte
-  // read together, i.e. 16 consecutive rows; rows r and r+1 share a 256-byte
-  // bank line, so the chunk position is XOR-ed with (r/2) mod 8
-  __device__ __forceinline__ static int sw(int r) { return (r >> 1) & 7; }
+  // read together, i.e. 16 consecutive rows; 256 / kRowB consecutive rows
+  // share a 256-byte bank line, so the chunk position is XOR-ed with the
+  // line index mod kCh
+  __device__ __forceinline__ static int sw(int r) { return (r / (256 / kRowB)) & (kCh - 1); }
   const bf16_t* p[kInst];
   int chunk[kInst];
   int kend;
@@ -161,46 +148,49 @@ struct KMajor {
     kend = kend_;
 #pragma unroll
     for (int i = 0; i < kInst; ++i) {
-      const int r = w * kRW + 8 * i + (lane >> 3);
-      chunk[i] = (lane & 7) ^ sw(r);
+      const int r = w * kRW + kRPI * i + lane / kCh;
+      chunk[i] = (lane % kCh) ^ sw(r);
       p[i] = s.row(r) + 8 * chunk[i];
     }
   }
   // stage kt into lds (operand tile base)
   template <class Src>
   __device__ __forceinline__ void issue(const Src&, int kt, unsigned char* lds, int w, int) const {
-    const int k0 = kt * kBK;
+    const int k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < kInst; ++i) {
-      // a chunk past kend (kend % 64 != 0, last stage) reads the row's last
+      // a chunk past kend (kend % BK != 0, last stage) reads the row's last
       // chunk instead; it is zeroed before use
       const int over = k0 + 8 * chunk[i] + 8 - kend;
       const int koff = over > 0 ? k0 - over : k0;
-      dma16(p[i] + koff, lds + (w * kRW + 8 * i) * 128);
+      dma16(p[i] + koff, lds + (w * kRW + kRPI * i) * kRowB);
     }
   }
   // zero k >= kvalid (kvalid a multiple of 8) in a stage
   __device__ __forceinline__ static void zero_tail(unsigned char* lds, int kvalid, int tid) {
-    for (int x = tid; x < R * 8; x += 64 * NW) {
-      const int r = x >> 3, q = x & 7;
+    for (int x = tid; x < R * kCh; x += 64 * NW) {
+      const int r = x / kCh, q = x % kCh;
       if (8 * q >= kvalid)
-        *reinterpret_cast<uint4*>(lds + r * 128 + 16 * (q ^ sw(r))) = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(lds + r * kRowB + 16 * (q ^ sw(r))) = make_uint4(0, 0, 0, 0);
     }
   }
   // fragment rows base..base+31 (base a multiple of 32), k-substep kc
   __device__ __forceinline__ static bf16x8_t frag(const unsigned char* lds, int base, int kc, int lane) {
     const int r = base + (lane & 31);
     const int q = (2 * kc + (lane >> 5)) ^ sw(r);
-    return *reinterpret_cast<const bf16x8_t*>(lds + r * 128 + 16 * q);
+    return *reinterpret_cast<const bf16x8_t*>(lds + r * kRowB + 16 * q);
   }
 };
 
-template <int R, int NW = 4>
+template <int R, int NW = 4, int BK = 64>
 struct MNMajor {
+  static constexpr int kBK = BK;
   static constexpr int kCPR = R / 8;         // 16-byte chunks per k-row
   static constexpr int kKPI = 64 / kCPR;     // k-rows per dma instruction
-  static constexpr int kInst = kCPR / NW;    // dma instructions per wave per stage
-  static constexpr int kBytes = kBK * R * 2;
+  static constexpr int kFragReads = 2;       // LDS read instructions per fragment
+  static constexpr int kInst = BK * kCPR / (64 * NW);  // dma instructions per wave per stage
+  static constexpr int kBytes = BK * R * 2;
+  static_assert(kInst * 64 * NW == BK * kCPR, "k-rows per wave");
   int kend, slot, last, krow0;
   template <class Src>
   __device__ __forceinline__ void init(const Src& s, int kend_, int w, int lane) {
@@ -215,12 +205,12 @@ struct MNMajor {
     for (int i = 0; i < kInst; ++i) {
       const int kr = krow0 + i * kKPI;
       const int chunk = min(slot ^ (4 * (kr & 3)), last);
-      const int k = min(kt * kBK + kr, kend - 1);
+      const int k = min(kt * BK + kr, kend - 1);
       dma16(s.kptr(k) + 8 * chunk, lds + (w * kInst + i) * kKPI * R * 2);
     }
   }
   __device__ __forceinline__ static void zero_tail(unsigned char* lds, int kvalid, int tid) {
-    for (int x = tid + kvalid * kCPR; x < kBK * kCPR; x += 64 * NW)
+    for (int x = tid + kvalid * kCPR; x < BK * kCPR; x += 64 * NW)
       *reinterpret_cast<uint4*>(lds + x * 16) = make_uint4(0, 0, 0, 0);
   }
   // fragment rows base..base+31 (the contiguous dimension), k-substep kc
@@ -319,6 +309,19 @@ struct StageBf16 {
 //                 unsigned char* stage)   (stage: kStageBytes of LDS private to the wave)
 // Each wave computes RW x CW.
 // ---------------------------------------------------------------------------
+// Scheduling request for one substep of the main loop: its NM MFMAs, each
+// followed by a share of the NR LDS fragment reads of the next substep, so
+// every fragment is read about one substep before its MFMA needs it.
+template <int NM, int NR>
+__device__ __forceinline__ void interleave_mfma_reads() {
+  static_for<NM>([&](auto m) {
+    constexpr int mm = decltype(m)::value;
+    constexpr int r = (NR * (mm + 1)) / NM - (NR * mm) / NM;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // r LDS reads
+  });
+}
+
 template <class P, int VB, int IM, int NJ, class AOp, class BOp, class AS, class BS>
 __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS& as, const BS& bs,
                                           unsigned char (*lds)[AOp::kBytes + BOp::kBytes], int K,
@@ -327,10 +330,15 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
   constexpr int NS = P::NS, RW = P::RW, CW = P::CW;
   constexpr int A_BYTES = AOp::kBytes;
   constexpr int NLOAD = AOp::kInst + BOp::kInst;
-  constexpr int KC = kBK / 16;
+  constexpr int BK = AOp::kBK;
+  static_assert(BOp::kBK == BK, "operands share the stage depth");
+  constexpr int KC = BK / 16;
+  constexpr int NM = VB * NJ;                                       // MFMAs per substep
+  constexpr int NR = VB * AOp::kFragReads + NJ * BOp::kFragReads;   // LDS reads per substep
   // The MFMAs of a stage's last substep are issued after the next stage's
   // barrier, from fragments already in registers, so they cover the barrier
-  // and the latency of the next stage's first LDS reads.
+  // and the latency of the next stage's first LDS reads.  Stage 0 is peeled
+  // (it has no such MFMAs), which keeps every stage body one basic block.
   bf16x8_t pa[VB > 0 ? VB : 1], pb[NJ];
   auto mfmas = [&](const bf16x8_t* a, const bf16x8_t* b) {
 #pragma unroll
@@ -339,12 +347,13 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
       for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
   };
-  for (int kt = 0; kt < nk; ++kt) {
+  auto stage = [&](int kt, auto first) {
+    constexpr bool kFirst = decltype(first)::value;
     if (kt + NS - 2 < nk) wait_vmcnt<(NS - 2) * NLOAD>(); else wait_vmcnt<0>();
     __syncthreads();
     unsigned char* cur = lds[kt % NS];
-    const int kvalid = K - kt * kBK;
-    if (kvalid < kBK) {  // uniform: only the last stage
+    const int kvalid = K - kt * BK;
+    if (kvalid < BK) {  // uniform: only the last stage
       AOp::zero_tail(cur, kvalid, tid);
       BOp::zero_tail(cur + A_BYTES, kvalid, tid);
       __syncthreads();
@@ -363,7 +372,10 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
       for (int i = 0; i < VB; ++i) af[0][i] = AOp::frag(As, wm * RW + 32 * i, 0, lane);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bfr[0][j] = BOp::frag(Bs, wn * CW + 32 * j, 0, lane);
-      if (kt > 0) mfmas(pa, pb);  // the previous stage's last substep
+      if constexpr (!kFirst) {
+        mfmas(pa, pb);  // the previous stage's last substep
+        interleave_mfma_reads<NM, NR>();
+      }
 #pragma unroll
       for (int kc = 0; kc < KC - 1; ++kc) {
         const int c = kc & 1, n = c ^ 1;
@@ -372,6 +384,7 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
 #pragma unroll
         for (int j = 0; j < NJ; ++j) bfr[n][j] = BOp::frag(Bs, wn * CW + 32 * j, kc + 1, lane);
         mfmas(af[c], bfr[c]);
+        interleave_mfma_reads<NM, NR>();
       }
       constexpr int last = (KC - 1) & 1;
 #pragma unroll
@@ -379,14 +392,16 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
 #pragma unroll
       for (int j = 0; j < NJ; ++j) pb[j] = bfr[last][j];
     }
-  }
-  if constexpr (VB > 0) {
-    if (nk > 0) mfmas(pa, pb);
+  };
+  if (nk > 0) {
+    stage(0, std::true_type{});
+    for (int kt = 1; kt < nk; ++kt) stage(kt, std::false_type{});
+    if constexpr (VB > 0) mfmas(pa, pb);
   }
 }
 
 template <class P>
-__global__ __launch_bounds__(P::NTHR) void gemm2_kernel(P p) {
+__global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_kernel(P p) {
   constexpr int NS = P::NS, IM = P::IM, NJ = P::NJ;
   using AOp = typename P::AOp;
   using BOp = typename P::BOp;
@@ -406,7 +421,7 @@ __global__ __launch_bounds__(P::NTHR) void gemm2_kernel(P p) {
   BOp bo;
   ao.init(as, K, w, lane);
   bo.init(bs, K, w, lane);
-  const int nk = (K + kBK - 1) / kBK;
+  const int nk = (K + AOp::kBK - 1) / AOp::kBK;
   f32x16_t acc[IM][NJ];
 #pragma unroll
   for (int i = 0; i < IM; ++i)
@@ -431,7 +446,7 @@ __global__ __launch_bounds__(P::NTHR) void gemm2_kernel(P p) {
 // the current tile's epilogue stores.  Epilogues get no LDS staging area
 // here (the ring holds the next tile's stages).
 template <class P>
-__global__ __launch_bounds__(P::NTHR) void gemm2_persistent(P p) {
+__global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_persistent(P p) {
   constexpr int NS = P::NS, IM = P::IM, NJ = P::NJ;
   using AOp = typename P::AOp;
   using BOp = typename P::BOp;
@@ -452,7 +467,7 @@ __global__ __launch_bounds__(P::NTHR) void gemm2_persistent(P p) {
   BOp bo;
   ao.init(as, t.ke, w, lane);
   bo.init(bs, t.ke, w, lane);
-  int nk = (t.ke + kBK - 1) / kBK;
+  int nk = (t.ke + AOp::kBK - 1) / AOp::kBK;
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) {
@@ -486,7 +501,7 @@ __global__ __launch_bounds__(P::NTHR) void gemm2_persistent(P p) {
       bs = p.b_src(tn);
       ao.init(as, tn.ke, w, lane);
       bo.init(bs, tn.ke, w, lane);
-      nk = (tn.ke + kBK - 1) / kBK;
+      nk = (tn.ke + AOp::kBK - 1) / AOp::kBK;
 #pragma unroll
       for (int s = 0; s < NS - 1; ++s)
         if (s < nk) {

@@ -106,12 +106,14 @@ struct GateUpRowsC {
   }
 };
 
-template <int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2>
+template <int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2, int BK_ = 64>
 struct MGateUp {
   static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
+  static constexpr int kBlocksPerCU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kBlocksPerCU;
+  static constexpr int kWavesPerEU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kWavesPerEU;
   static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
-  using AOp = KMajor<BM, WM_ * WN_>;
-  using BOp = KMajor<BN, WM_ * WN_>;
+  using AOp = KMajor<BM, WM_ * WN_, BK_>;
+  using BOp = KMajor<BN, WM_ * WN_, BK_>;
   const bf16_t* X; const bf16_t* Wgu; const int32_t* offsets; const int32_t* perm;
   bf16_t* gu; bf16_t* a;
   int H, E, K, I, NT;
@@ -181,12 +183,14 @@ struct MGateUp {
   }
 };
 
-template <int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2>
+template <int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2, int BK_ = 64>
 struct MDown {
   static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
+  static constexpr int kBlocksPerCU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kBlocksPerCU;
+  static constexpr int kWavesPerEU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kWavesPerEU;
   static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
-  using AOp = KMajor<BM, WM_ * WN_>;
-  using BOp = KMajor<BN, WM_ * WN_>;
+  using AOp = KMajor<BM, WM_ * WN_, BK_>;
+  using BOp = KMajor<BN, WM_ * WN_, BK_>;
   const bf16_t* a; const bf16_t* Wd; const int32_t* offsets; float* ybuf;
   int H, E, I, NT;
   __device__ __forceinline__ bool tile(int L, MTile& t) const {
@@ -217,12 +221,14 @@ struct MDown {
   }
 };
 
-template <int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2>
+template <int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2, int BK_ = 64>
 struct MDa {
   static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
+  static constexpr int kBlocksPerCU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kBlocksPerCU;
+  static constexpr int kWavesPerEU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kWavesPerEU;
   static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
-  using AOp = KMajor<BM, WM_ * WN_>;
-  using BOp = MNMajor<BN, WM_ * WN_>;
+  using AOp = KMajor<BM, WM_ * WN_, BK_>;
+  using BOp = MNMajor<BN, WM_ * WN_, BK_>;
   const bf16_t* dY; const bf16_t* Wd; const int32_t* offsets; const int32_t* perm;
   const float* topk_w; const bf16_t* gu; const bf16_t* a; bf16_t* dgu; float* dwpart;
   int H, E, K, I, NT, NTP;
@@ -286,12 +292,14 @@ struct MDa {
   }
 };
 
-template <int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2>
+template <int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2, int BK_ = 64>
 struct MDx {
   static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
+  static constexpr int kBlocksPerCU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kBlocksPerCU;
+  static constexpr int kWavesPerEU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kWavesPerEU;
   static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
-  using AOp = KMajor<BM, WM_ * WN_>;
-  using BOp = MNMajor<BN, WM_ * WN_>;
+  using AOp = KMajor<BM, WM_ * WN_, BK_>;
+  using BOp = MNMajor<BN, WM_ * WN_, BK_>;
   const bf16_t* dgu; const bf16_t* Wgu; const int32_t* offsets; float* vbuf;
   int H, E, I, NT;
   __device__ __forceinline__ bool tile(int L, MTile& t) const {
@@ -327,12 +335,14 @@ struct MDx {
 //   gate_up: dW[r, c] = sum_p dGU[p, r] Xg[p, c]    (rows 2I, cols H)
 //   down:    dW[r, c] = sum_p wdYg[p, r] a[p, c]    (rows H,  cols I)
 // Xg = X gathered by token and wdYg = bf16(w_p dY[tok(p)]) are staged first.
-template <bool kDown, int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2>
+template <bool kDown, int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2, int BK_ = 64>
 struct MDenseDw {
   static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
+  static constexpr int kBlocksPerCU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kBlocksPerCU;
+  static constexpr int kWavesPerEU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kWavesPerEU;
   static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
-  using AOp = MNMajor<BM, WM_ * WN_>;
-  using BOp = MNMajor<BN, WM_ * WN_>;
+  using AOp = MNMajor<BM, WM_ * WN_, BK_>;
+  using BOp = MNMajor<BN, WM_ * WN_, BK_>;
   const bf16_t* L; const bf16_t* R; const int32_t* offsets; float* dW;
   int H, E, I, MT, NT;
   int64_t ngu;
@@ -451,12 +461,12 @@ static int device_cus() {
   return cus[dev];
 }
 
-// Persistent launch: about one block per CU (a multiple of 8 for the XCD
-// remap), never more blocks than tiles.
+// Persistent launch: about P::kBlocksPerCU blocks per CU (a multiple of 8
+// for the XCD remap), never more blocks than tiles.
 template <class P>
 static usaf_status launch_persistent(const P& p, int64_t tiles, hipStream_t st, int kclass) {
   if (tiles <= 0) return USAF_OK;
-  int64_t blocks = device_cus();
+  int64_t blocks = int64_t(P::kBlocksPerCU) * device_cus();
   if (blocks > tiles) blocks = tiles;
   blocks = (blocks + 7) / 8 * 8;
   timer_begin(kclass, st);
@@ -481,6 +491,7 @@ usaf_status mfma_router(const usaf_moe_shape& s, const bf16_t* X, const float* W
 // Tile shapes and LDS ring depths of the direct-to-LDS GEMMs.
 constexpr int kFwdBM = 128, kFwdBN = 256, kFwdNS = 3;  // gate_up, down, dA, dX: 144 KiB LDS
 constexpr int kFwdWM = 2, kFwdWN = 4;                  // 8 waves: 2 per SIMD
+constexpr int kFwdBK = 64;                             // contraction depth of a stage
 constexpr int kDaWN = 2;                               // dA: 4 waves (its epilogue prefers them)
 constexpr int kDwBM = 256, kDwBN = 256, kDwNS = 2;     // dense dW: 128 KiB LDS
 
@@ -492,13 +503,13 @@ static bool big_groups(const usaf_moe_shape& s) {
   return int64_t(s.T) * s.K >= int64_t(kBigRows) * s.E;
 }
 
-template <template <int, int, int, int, int> class M, class... Args>
+template <template <int, int, int, int, int, int> class M, class... Args>
 static usaf_status launch_fwd(const usaf_moe_shape& s, int NT, hipStream_t st, int kclass,
                               Args... args) {
   if (big_groups(s))
-    return launch_persistent(M<kBigBM, kFwdBN, kBigNS, kFwdWM, kFwdWN>{args...},
+    return launch_persistent(M<kBigBM, kFwdBN, kBigNS, kFwdWM, kFwdWN, 64>{args...},
                              grouped_tiles_bound(s, NT, kBigBM), st, kclass);
-  return launch_persistent(M<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN>{args...},
+  return launch_persistent(M<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN, kFwdBK>{args...},
                            grouped_tiles_bound(s, NT, kFwdBM), st, kclass);
 }
 
@@ -528,7 +539,7 @@ usaf_status mfma_da(const usaf_moe_shape& s, const bf16_t* dY, const bf16_t* Wd,
                                                                        a, dgu, dwpart, s.H, s.E, s.K,
                                                                        s.I, NT, kDaWN * NT},
                              grouped_tiles_bound(s, NT, kBigBM), st, USAF_K_DA);
-  return launch_persistent(g2::MDa<kFwdBM, kFwdBN, kFwdNS, 2, kDaWN>{dY, Wd, offsets, perm, topk_w, gu, a, dgu, dwpart, s.H,
+  return launch_persistent(g2::MDa<kFwdBM, kFwdBN, kFwdNS, 2, kDaWN, kFwdBK>{dY, Wd, offsets, perm, topk_w, gu, a, dgu, dwpart, s.H,
                                            s.E, s.K, s.I, NT, kDaWN * NT},
                    grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DA);
 }
