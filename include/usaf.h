@@ -233,6 +233,18 @@ USAF_API usaf_status usaf_mse_grad(const usaf_moe_shape *shape, const void *Y, c
                           void *dY, float *loss, int32_t *nonfinite, void *ws,
                           size_t ws_bytes, hipStream_t stream);
 
+/* Residual stream of a stack of layers (the stacked-layer workload's
+ * composition reading: no attention or norm between the MoE layers, so the
+ * next layer's input is the sum of a layer's input and output, and in the
+ * backward the gradient of a layer's input is the sum of the gradient of
+ * the next layer's input and the layer's own dX): out[i] = round_act(a[i] +
+ * b[i]) for i < n, act USAF_BF16 (round to nearest even) or USAF_F32.  a, b,
+ * out: device arrays of n elements; out may alias a or b.  Asynchronous on
+ * `stream`.  Errors: INVALID_ARG for n < 0, an unknown act, or null pointers
+ * with n > 0. */
+USAF_API usaf_status usaf_residual_add(int32_t act, const void *a, const void *b, void *out,
+                              int64_t n, hipStream_t stream);
+
 /* Routing alone, from given fp32 logits [T, E]: writes state->topk_ids,
  * topk_w, offsets, perm, slot_pos exactly as usaf_moe_forward does. */
 USAF_API usaf_status usaf_route(const usaf_moe_shape *shape, const float *logits,

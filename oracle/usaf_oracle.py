@@ -572,3 +572,112 @@ def dense_scan(X, tgt, Wr, W_gu, W_d, K, R: Rounding) -> dict:
     bw = moe_backward(fw, X, Wr, W_gu, W_d, dY, R)
     g = weight_grads_dense(fw, bw, X, dY, shape, R)
     return dict(fw=fw, bw=bw, loss=loss, dY=dY, g=g)
+
+
+# ----------------------------------------------------------------------------
+# The stacked-layer workload: the trainer loop around the step
+# ----------------------------------------------------------------------------
+# Readings (the pages train a stack of real model layers; the stacked
+# workload keeps only the MoE layers):
+# * composition: a residual stream with no attention or norm, so layer l+1
+#   reads X_{l+1} = round_act(X_l + Y_l); the loss is the MSE of the last
+#   output; in the backward the gradient of X_l is round_act(G_{l+1} + dX_l),
+#   where dX_l is layer l's own input gradient for output gradient G_{l+1};
+# * the learning rate follows the README's cosine decay from LR_PEAK
+#   (environment-variable table) over the run's steps, without warm-up, to 0;
+# * every layer's active set is chosen from that layer's own gradients, with
+#   k = floor(frac * N) per layer (README intro and "how it works": the
+#   importance phase; RigL every RESELECT_EVERY steps).
+
+
+def residual_add(a, b, R: Rounding) -> np.ndarray:
+    """The residual stream: round_act(a + b), the sum taken in float64."""
+    return R.act(np.asarray(a, dtype=np.float64) + np.asarray(b, dtype=np.float64))
+
+
+def cosine_lr(step: int, total: int, peak: float) -> float:
+    """Cosine decay from ``peak`` at step 0 towards 0 at step ``total`` (README
+    environment-variable table: LR_PEAK, cosine decay), no warm-up."""
+    return 0.5 * peak * (1.0 + math.cos(math.pi * step / total))
+
+
+def stack_forward(X0, layers: list, K: int, R: Rounding) -> dict:
+    """Forward through the stack.  ``layers[l]`` holds W_gu, W_d and Wr.
+    Returns the per-layer forward records and the inputs X_0 .. X_L."""
+    Xs = [np.asarray(X0, dtype=np.float64)]
+    fws = []
+    for lay in layers:
+        fw = moe_forward(Xs[-1], lay["Wr"], lay["W_gu"], lay["W_d"], K, R)
+        fws.append(fw)
+        Xs.append(residual_add(Xs[-1], fw["Y"], R))
+    return dict(fws=fws, Xs=Xs)
+
+
+def stack_backward(fwd: dict, layers: list, GL, R: Rounding) -> dict:
+    """Backward from the gradient GL of the last output X_L.  Returns, per
+    layer, the backward record and the output gradient dY_l = G_{l+1} that
+    layer l's weight gradients are taken against, and the gradient G_0."""
+    n = len(layers)
+    bws, dYs = [None] * n, [None] * n
+    G = np.asarray(GL, dtype=np.float64)
+    for l in range(n - 1, -1, -1):
+        lay = layers[l]
+        bw = moe_backward(fwd["fws"][l], fwd["Xs"][l], lay["Wr"], lay["W_gu"], lay["W_d"], G, R)
+        bws[l], dYs[l] = bw, G
+        G = residual_add(G, bw["dX"], R)
+    return dict(bws=bws, dYs=dYs, G0=G)
+
+
+def stack_scan_grads(X0, tgt, layers: list, K: int, R: Rounding) -> dict:
+    """Dense pass over the stack: every expert-weight gradient of every layer
+    (the importance / RigL scan of each layer, taken in one backward)."""
+    fwd = stack_forward(X0, layers, K, R)
+    loss, GL = mse_loss_grad(fwd["Xs"][-1], tgt, R)
+    bwd = stack_backward(fwd, layers, GL, R)
+    grads = []
+    for l, lay in enumerate(layers):
+        shape = Shape(np.shape(X0)[0], np.shape(X0)[1], lay["W_gu"].shape[0], K, lay["W_d"].shape[2])
+        grads.append(weight_grads_dense(fwd["fws"][l], bwd["bws"][l], fwd["Xs"][l], bwd["dYs"][l],
+                                        shape, R))
+    return dict(loss=loss, grads=grads, fwd=fwd, bwd=bwd)
+
+
+def stack_train_step(X0, tgt, layers: list, K: int, t: int, lr, beta1, beta2, eps,
+                     R: Rounding) -> dict:
+    """One sparse step of the whole stack.  ``layers[l]`` also holds its active
+    list idx and its moments m, v, mr, vr.  Every layer's gradients are taken
+    first; if the loss, the last output's gradient, or any layer's listed or
+    router gradient is non-finite, no layer is updated and the step count
+    stays (README results table: NaN steps are skipped).  Otherwise each
+    layer takes SparseAdam on its list and dense Adam on its router with the
+    shared step count t + 1."""
+    fwd = stack_forward(X0, layers, K, R)
+    loss, GL = mse_loss_grad(fwd["Xs"][-1], tgt, R)
+    bwd = stack_backward(fwd, layers, GL, R)
+    gs = []
+    finite = is_finite_all([loss], GL)
+    for l, lay in enumerate(layers):
+        shape = Shape(np.shape(X0)[0], np.shape(X0)[1], lay["W_gu"].shape[0], K, lay["W_d"].shape[2])
+        g = weight_grads_at(fwd["fws"][l], bwd["bws"][l], fwd["Xs"][l], bwd["dYs"][l], lay["idx"],
+                            shape, R)
+        gs.append(g)
+        finite = finite and is_finite_all(g, bwd["bws"][l]["dWr"])
+    out = dict(loss=loss, fwd=fwd, bwd=bwd, g=gs, skipped=not finite)
+    if not finite:
+        out.update(layers=[dict(lay) for lay in layers], t=t)
+        return out
+    new_layers = []
+    for l, lay in enumerate(layers):
+        shape = Shape(np.shape(X0)[0], np.shape(X0)[1], lay["W_gu"].shape[0], K, lay["W_d"].shape[2])
+        flat = np.concatenate([np.asarray(lay["W_gu"], np.float64).ravel(),
+                               np.asarray(lay["W_d"], np.float64).ravel()])
+        idx64 = np.asarray(lay["idx"], dtype=np.int64)
+        w_sel, m_new, v_new = adam_update(flat[idx64], gs[l], lay["m"], lay["v"], t + 1, lr, beta1,
+                                          beta2, eps, R.act_dtype, R)
+        flat[idx64] = w_sel
+        W_gu, W_d = unflatten(flat, shape)
+        Wr, mr, vr = adam_update(lay["Wr"], bwd["bws"][l]["dWr"], lay["mr"], lay["vr"], t + 1, lr,
+                                 beta1, beta2, eps, F32, R)
+        new_layers.append(dict(lay, W_gu=W_gu, W_d=W_d, Wr=Wr, m=m_new, v=v_new, mr=mr, vr=vr))
+    out.update(layers=new_layers, t=t + 1)
+    return out

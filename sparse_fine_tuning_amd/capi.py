@@ -25,7 +25,7 @@ EXPORTS = (
     "usaf_workspace_size", "usaf_moe_forward", "usaf_masked_backward", "usaf_importance_topk",
     "usaf_rigl_reselect", "usaf_sparse_adam", "usaf_dequant_resident", "usaf_mse_grad",
     "usaf_route", "usaf_status_string", "usaf_version", "usaf_timer_arm", "usaf_timer_read",
-    "usaf_gather",
+    "usaf_gather", "usaf_residual_add",
 )
 
 # Kernel classes of the timing hook (usaf_kernel_class).
@@ -89,6 +89,7 @@ def _load():
         "usaf_dequant_resident": [vp, vp, i64, i64, i32, vp, vp],
         "usaf_mse_grad": [vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "usaf_route": [vp, vp, vp, vp],
+        "usaf_residual_add": [i32, vp, vp, vp, i64, vp],
         "usaf_status_string": [i32],
         "usaf_version": [],
         "usaf_timer_arm": [i32, i32],
@@ -206,6 +207,11 @@ def mse_grad(shape, Y, tgt, dY, loss, nonfinite, ws, stream=None):
     _check(lib.usaf_mse_grad(C.byref(shape), _p(Y), _p(tgt), _p(dY), _p(loss), _p(nonfinite),
                              _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "usaf_mse_grad")
+
+
+def residual_add(act, a, b, out, n, stream=None):
+    _check(lib.usaf_residual_add(int(act), _p(a), _p(b), _p(out), int(n), _stream(stream)),
+           "usaf_residual_add")
 
 
 def route(shape, logits, state: State, stream=None):

@@ -636,6 +636,24 @@ __global__ __launch_bounds__(256) void masked_dw_kernel(
   if (nonfinite && !finite_f(acc)) atomicAdd(nonfinite, 1);
 }
 
+// Residual stream of stacked layers: out = round(a + b) elementwise.  For
+// bf16 operands the fp32 sum is exact unless the exponents differ by more
+// than 15, and then b lies far below half an ulp of a, so rounding the fp32
+// sum to bf16 gives the correctly rounded sum either way.  Eight elements per
+// thread (16-byte bf16 / 2 x 16-byte fp32 accesses), scalar tail.
+template <class T>
+__global__ __launch_bounds__(256) void residual_add_kernel(const T* __restrict__ a,
+                                                           const T* __restrict__ b, T* __restrict__ out,
+                                                           int64_t n) {
+  const int64_t i0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i0 + 8 <= n) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Act<T>::st(out, i0 + j, Act<T>::ld(a, i0 + j) + Act<T>::ld(b, i0 + j));
+  } else {
+    for (int64_t i = i0; i < n; ++i) Act<T>::st(out, i, Act<T>::ld(a, i) + Act<T>::ld(b, i));
+  }
+}
+
 // Loss: per-block partial sums of (Y - tgt)^2 over 4096 elements, dY written.
 template <class T>
 __global__ __launch_bounds__(256) void mse_partial_kernel(const T* __restrict__ Y,
@@ -908,6 +926,25 @@ extern "C" usaf_status usaf_mse_grad(const usaf_moe_shape* shape, const void* Y,
                             stream);
   return mse_impl<float>(*shape, static_cast<const float*>(Y), static_cast<const float*>(tgt),
                          static_cast<float*>(dY), loss, nonfinite, static_cast<char*>(ws), stream);
+}
+
+extern "C" usaf_status usaf_residual_add(int32_t act, const void* a, const void* b, void* out,
+                                         int64_t n, hipStream_t stream) {
+  if (n < 0 || (act != USAF_BF16 && act != USAF_F32)) return USAF_ERR_INVALID_ARG;
+  if (n == 0) return USAF_OK;
+  if (!a || !b || !out) return USAF_ERR_INVALID_ARG;
+  const int64_t blocks = ceil_div(ceil_div(n, 8), 256);
+  if (blocks >= (int64_t(1) << 31)) return USAF_ERR_UNSUPPORTED;
+  if (act == USAF_BF16)
+    hipLaunchKernelGGL(residual_add_kernel<bf16_t>, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b),
+                       static_cast<bf16_t*>(out), n);
+  else
+    hipLaunchKernelGGL(residual_add_kernel<float>, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                       static_cast<const float*>(a), static_cast<const float*>(b),
+                       static_cast<float*>(out), n);
+  USAF_LAUNCH_CHECK();
+  return USAF_OK;
 }
 
 extern "C" usaf_status usaf_route(const usaf_moe_shape* shape, const float* logits,

@@ -1,0 +1,224 @@
+"""A stack of MoE layers trained sparsely through the C ABI: the trainer loop
+around the layer step.
+
+The usaf README trains the expert weights of a deep model's MoE layers
+("how it works": native sparse fine-tuning with the router trained densely;
+environment-variable table: STEPS, LR_PEAK with cosine decay, FRAC,
+RESELECT_EVERY).  Here the stack keeps only the MoE layers, joined by a
+residual stream:
+
+  forward   X_{l+1} = round(X_l + Y_l)                      (usaf_residual_add)
+  loss      MSE of X_L against the target                    (usaf_mse_grad)
+  backward  G_l = round(G_{l+1} + dX_l), layer l's weight gradients taken
+            against output gradient G_{l+1}                  (usaf_masked_backward)
+  update    every layer's SparseAdam + router Adam, one shared step count,
+            all skipped together when any gradient is non-finite
+
+and the importance pass / RigL reselection scan the dense gradient of every
+layer in one backward, selecting each layer's list from its own gradient
+before the next layer's backward reuses the dense buffer.
+
+PyTorch only owns device memory; every step runs in libusaf.so's kernels.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import capi
+from .capi import BF16, F32
+
+
+def _dt(act: int):
+    return torch.bfloat16 if act == BF16 else torch.float32
+
+
+def cosine_lr(step: int, total: int, peak: float) -> float:
+    """README cosine decay from LR_PEAK at step 0 towards 0 at ``total``."""
+    return 0.5 * peak * (1.0 + math.cos(math.pi * step / total))
+
+
+class _Layer:
+    """Parameters, optimiser state and saved forward state of one layer."""
+
+    def __init__(self, shape: capi.Shape, shared: dict, dev: torch.device):
+        T, H, E, K, I, act = shape.T, shape.H, shape.E, shape.K, shape.I, shape.act
+        dt = _dt(act)
+        S = T * K
+        z = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=dev)
+        self.st = dict(
+            logits=z(T, E), topk_ids=z(T, K, dtype=torch.int32), topk_w=z(T, K),
+            offsets=z(E + 1, dtype=torch.int32), perm=z(S, dtype=torch.int32),
+            slot_pos=z(S, dtype=torch.int32), gu=z(S, 2 * I, dtype=dt), a=z(S, I, dtype=dt),
+            dgu=shared["dgu"], dw=shared["dw"])
+        self.state = capi.make_state(self.st)
+        self.W = z(shape.N, dtype=dt)
+        self.Wr = z(E, H)
+        self.mr = torch.zeros(E, H, dtype=torch.float32, device=dev)
+        self.vr = torch.zeros(E, H, dtype=torch.float32, device=dev)
+        self.dWr = z(E, H)
+        self.idx = self.m = self.v = self.dW = self.w_list = None
+
+    def set_active(self, idx: torch.Tensor, act: int):
+        """Active list (int32 tensor of ascending uint32 flat indices) with
+        fresh moments."""
+        k = idx.numel()
+        dev = idx.device
+        self.idx = idx
+        self.m = torch.zeros(k, dtype=torch.float32, device=dev)
+        self.v = torch.zeros(k, dtype=torch.float32, device=dev)
+        self.dW = torch.empty(k, dtype=torch.float32, device=dev)
+        self.refresh_list(act)
+
+    def refresh_list(self, act: int):
+        k = self.idx.numel()
+        self.w_list = torch.empty(k, dtype=_dt(act), device=self.idx.device)
+        capi.gather(act, self.W, self.idx, k, self.w_list)
+
+
+class MoEStack:
+    """``n_layers`` MoE layers of one shape on one device."""
+
+    def __init__(self, n_layers, T, H, E, K, I, act=BF16, device="cuda"):
+        self.shape = capi.Shape(T, H, E, K, I, act)
+        self.act = act
+        self.n_layers = n_layers
+        self.device = dev = torch.device(device)
+        dt = _dt(act)
+        z = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=dev)
+        shared = dict(dgu=z(T * K, 2 * I, dtype=dt), dw=z(T, K))
+        self.layers = [_Layer(self.shape, shared, dev) for _ in range(n_layers)]
+        self.ws_fwd = z(capi.workspace_size(capi.WS_FORWARD, self.shape), dtype=torch.uint8)
+        self.ws_bwd = z(capi.workspace_size(capi.WS_BACKWARD, self.shape), dtype=torch.uint8)
+        self.Xs = [z(T, H, dtype=dt) for _ in range(n_layers + 1)]  # X_0 .. X_L
+        self.tgt = z(T, H, dtype=dt)
+        self.Y = z(T, H, dtype=dt)
+        self.dXl = z(T, H, dtype=dt)
+        self.G = [z(T, H, dtype=dt), z(T, H, dtype=dt)]
+        self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.nonfinite = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.t = 0
+        self.skipped = 0
+        self._dense = None
+        self._ws_topk = None
+        self._ws_rigl = None
+
+    # ---- parameters and data -----------------------------------------------
+    def load_layer(self, l, W_gu, W_d, Wr):
+        """Upload one layer's numpy weights (values representable in act)."""
+        lay, dev, dt = self.layers[l], self.device, _dt(self.act)
+        flat = np.concatenate([np.asarray(W_gu, np.float32).ravel(), np.asarray(W_d, np.float32).ravel()])
+        lay.W.copy_(torch.from_numpy(flat).to(dev).to(dt))
+        lay.Wr.copy_(torch.from_numpy(np.ascontiguousarray(Wr, dtype=np.float32)).to(dev))
+
+    def set_batch(self, X, tgt):
+        """X_0 and the target: numpy arrays or device tensors."""
+        for dst, src in ((self.Xs[0], X), (self.tgt, tgt)):
+            if isinstance(src, torch.Tensor):
+                dst.copy_(src)
+            else:
+                dst.copy_(torch.from_numpy(np.ascontiguousarray(src, dtype=np.float32)).to(self.device))
+
+    # ---- the step ------------------------------------------------------------
+    def forward(self, stream=None):
+        n = self.shape.T * self.shape.H
+        for l, lay in enumerate(self.layers):
+            capi.moe_forward(self.shape, self.Xs[l], lay.Wr, lay.W, self.Y, lay.state, self.ws_fwd,
+                             stream)
+            capi.residual_add(self.act, self.Xs[l], self.Y, self.Xs[l + 1], n, stream)
+
+    def backward(self, select=None, stream=None):
+        """Backward from the loss of the last output.  With ``select`` (a
+        callable (l, dense_grad)), every layer's dense expert-weight gradient
+        is formed instead of the listed one and handed to it at once."""
+        n = self.shape.T * self.shape.H
+        capi.mse_grad(self.shape, self.Xs[-1], self.tgt, self.G[0], self.loss, self.nonfinite,
+                      self.ws_fwd, stream)
+        cur = 0
+        for l in range(self.n_layers - 1, -1, -1):
+            lay = self.layers[l]
+            G, Gn = self.G[cur], self.G[cur ^ 1]
+            if select is None:
+                capi.masked_backward(self.shape, self.Xs[l], lay.Wr, lay.W, lay.state, G, lay.idx,
+                                     lay.idx.numel(), lay.dW, lay.dWr, self.dXl, self.nonfinite,
+                                     self.ws_bwd, stream)
+            else:
+                dense = self._dense_buffer()
+                capi.masked_backward(self.shape, self.Xs[l], lay.Wr, lay.W, lay.state, G, None,
+                                     self.shape.N, dense, lay.dWr, self.dXl, None, self.ws_bwd,
+                                     stream)
+                select(l, dense)
+            if l > 0:
+                capi.residual_add(self.act, G, self.dXl, Gn, n, stream)
+                cur ^= 1
+
+    def adam(self, step, lr, betas=(0.9, 0.999), eps=1e-8, stream=None):
+        b1, b2 = betas
+        for lay in self.layers:
+            capi.sparse_adam(self.act, lay.W, lay.idx, lay.idx.numel(), lay.dW, lay.m, lay.v, step,
+                             lr, b1, b2, eps, self.nonfinite, stream, w_list=lay.w_list)
+            capi.sparse_adam(F32, lay.Wr, None, lay.Wr.numel(), lay.dWr, lay.mr, lay.vr, step, lr,
+                             b1, b2, eps, self.nonfinite, stream)
+
+    def train_step(self, lr, betas=(0.9, 0.999), eps=1e-8, stream=None, check_skip=True):
+        """Forward, loss, backward through every layer, then every layer's
+        update with the shared step count (skipped together when any gradient
+        is non-finite; checking that costs one 4-byte device->host read)."""
+        self.nonfinite.zero_()
+        self.forward(stream)
+        self.backward(stream=stream)
+        self.adam(self.t + 1, lr, betas, eps, stream)
+        if check_skip and int(self.nonfinite.item()) != 0:
+            self.skipped += 1
+        else:
+            self.t += 1
+
+    # ---- importance / RigL ---------------------------------------------------
+    def _dense_buffer(self):
+        if self._dense is None:
+            self._dense = torch.empty(self.shape.N, dtype=torch.float32, device=self.device)
+        return self._dense
+
+    def _topk_ws(self):
+        if self._ws_topk is None:
+            self._ws_topk = torch.empty(capi.workspace_size(capi.WS_TOPK, None, self.shape.N),
+                                        dtype=torch.uint8, device=self.device)
+        return self._ws_topk
+
+    def importance(self, k: int, stream=None):
+        """The importance pass: every layer's active list is the top-k of its
+        own dense gradient on the current batch."""
+        ws = self._topk_ws()
+
+        def pick(l, grad):
+            out = torch.empty(k, dtype=torch.int32, device=self.device)
+            capi.importance_topk(grad, self.shape.N, k, None, 0, out, None, ws, stream)
+            self.layers[l].set_active(out, self.act)
+
+        self.forward(stream)
+        self.backward(select=pick, stream=stream)
+
+    def rigl(self, r: int, stream=None) -> torch.Tensor:
+        """RigL reselection of every layer on the current batch; returns the
+        device stats [n_layers, 3] (int64) of usaf_rigl_reselect."""
+        k = self.layers[0].idx.numel()
+        if self._ws_rigl is None:
+            self._ws_rigl = torch.empty(capi.workspace_size(capi.WS_RIGL, None, self.shape.N, k),
+                                        dtype=torch.uint8, device=self.device)
+        stats = torch.zeros(self.n_layers, 3, dtype=torch.int64, device=self.device)
+
+        def reselect(l, grad):
+            lay = self.layers[l]
+            new_idx = torch.empty_like(lay.idx)
+            new_m = torch.empty_like(lay.m)
+            new_v = torch.empty_like(lay.v)
+            capi.rigl_reselect(self.shape, grad, lay.W, lay.idx, lay.m, lay.v, k, r, new_idx,
+                               new_m, new_v, stats[l], self._ws_rigl, stream)
+            lay.idx, lay.m, lay.v = new_idx, new_m, new_v
+            lay.refresh_list(self.act)
+
+        self.forward(stream)
+        self.backward(select=reselect, stream=stream)
+        return stats
