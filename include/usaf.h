@@ -71,7 +71,8 @@ typedef enum {
   USAF_WS_FORWARD = 0,
   USAF_WS_BACKWARD = 1,
   USAF_WS_TOPK = 2,
-  USAF_WS_RIGL = 3
+  USAF_WS_RIGL = 3,
+  USAF_WS_MASKED_PLAN = 4
 } usaf_ws_kind;
 
 /* One MoE layer: T tokens, hidden H, E experts, top-K routing, expert
@@ -108,7 +109,8 @@ typedef struct {
                             /* are not in the old set (the README's "turnover")     */
 } usaf_rigl_stats;
 
-/* Bytes of workspace `kind` needs for `shape` (FORWARD, BACKWARD) or for a
+/* Bytes of workspace `kind` needs for `shape` (FORWARD, BACKWARD,
+ * MASKED_PLAN: the plan of usaf_masked_plan for any list) or for a
  * selection over n keys picking k (TOPK: n = N, k; RIGL: n = N, k = active
  * count).  `shape` may be NULL for TOPK / RIGL.  Result goes to HOST *bytes.
  * Returns USAF_ERR_INVALID_ARG for a bad kind, size or null `bytes`. */
@@ -129,6 +131,20 @@ USAF_API usaf_status usaf_moe_forward(const usaf_moe_shape *shape, const void *X
                              const void *Wflat, void *Y, const usaf_moe_state *state,
                              void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Plan of the masked gradient for one active list idx[nnz] (strictly
+ * ascending): where every (expert, row, column tile) segment starts in the
+ * list, and the list's work cut into tiles of balanced entry counts.  It
+ * depends on idx and the shape only (not on routing or data), so a caller
+ * that keeps the list for many steps builds it once per list (README "how it
+ * works": the active set changes only at RigL reselection) and passes it to
+ * usaf_masked_backward.  plan: device buffer of usaf_workspace_size
+ * (USAF_WS_MASKED_PLAN) bytes, written; its layout is private to the library.
+ * fp32 layers need no plan (returns OK, writes nothing).  Errors:
+ * INVALID_ARG for nnz < 0, nnz > N or idx == NULL with nnz > 0; WORKSPACE
+ * for a short buffer. */
+USAF_API usaf_status usaf_masked_plan(const usaf_moe_shape *shape, const uint32_t *idx, int64_t nnz,
+                             void *plan, size_t plan_bytes, hipStream_t stream);
+
 /* Masked backward (README intro and A100 table: gradients only for the
  * selected subset of expert weights; the router gradient is dense).
  * Reads the forward's state and dY [T,H] (act).  Writes
@@ -138,6 +154,8 @@ USAF_API usaf_status usaf_moe_forward(const usaf_moe_shape *shape, const void *X
  *   dW: for a sparse list idx[nnz] (strictly ascending flat indices) dW[i] is
  *       the fp32 gradient at idx[i]; in dense mode (idx == NULL and
  *       nnz == N) dW[f] is the gradient of every expert weight f.
+ * plan (nullable): usaf_masked_plan's plan of this very idx[nnz]; with NULL
+ * the plan is rebuilt inside ws on every call.  Ignored in dense mode.
  * nonfinite (nullable, device int32): incremented when any dW value or dWr
  * is NaN/Inf (sparse mode); the caller zeroes it before the step.
  * ws: USAF_WS_BACKWARD bytes.  Errors: INVALID_ARG for nnz < 0, nnz > N, a
@@ -145,8 +163,8 @@ USAF_API usaf_status usaf_moe_forward(const usaf_moe_shape *shape, const void *X
 USAF_API usaf_status usaf_masked_backward(const usaf_moe_shape *shape, const void *X, const float *Wr,
                                  const void *Wflat, const usaf_moe_state *state,
                                  const void *dY, const uint32_t *idx, int64_t nnz,
-                                 float *dW, float *dWr, void *dX, int32_t *nonfinite,
-                                 void *ws, size_t ws_bytes, hipStream_t stream);
+                                 const void *plan, float *dW, float *dWr, void *dX,
+                                 int32_t *nonfinite, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Importance selection (README "how it works": the 0.5% of weights with the
  * largest gradient magnitude).  Ranks grad[0..n) by (|grad| descending, index

@@ -18,14 +18,14 @@ LIB_PATH = os.path.join(_PKG, "libusaf.so")
 USAF_OK, USAF_ERR_INVALID_ARG, USAF_ERR_UNSUPPORTED, USAF_ERR_WORKSPACE, USAF_ERR_HIP, \
     USAF_ERR_NOT_IMPLEMENTED = range(6)
 F32, BF16 = 0, 1
-WS_FORWARD, WS_BACKWARD, WS_TOPK, WS_RIGL = range(4)
+WS_FORWARD, WS_BACKWARD, WS_TOPK, WS_RIGL, WS_MASKED_PLAN = range(5)
 
 # Every symbol include/usaf.h declares.
 EXPORTS = (
     "usaf_workspace_size", "usaf_moe_forward", "usaf_masked_backward", "usaf_importance_topk",
     "usaf_rigl_reselect", "usaf_sparse_adam", "usaf_dequant_resident", "usaf_mse_grad",
     "usaf_route", "usaf_status_string", "usaf_version", "usaf_timer_arm", "usaf_timer_read",
-    "usaf_gather", "usaf_residual_add",
+    "usaf_gather", "usaf_residual_add", "usaf_masked_plan",
 )
 
 # Kernel classes of the timing hook (usaf_kernel_class).
@@ -80,7 +80,8 @@ def _load():
     sig = {
         "usaf_workspace_size": [i32, vp, i64, i64, C.POINTER(sz)],
         "usaf_moe_forward": [vp, vp, vp, vp, vp, vp, vp, sz, vp],
-        "usaf_masked_backward": [vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, sz, vp],
+        "usaf_masked_backward": [vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp],
+        "usaf_masked_plan": [vp, vp, i64, vp, sz, vp],
         "usaf_importance_topk": [vp, i64, i64, vp, i64, vp, vp, vp, sz, vp],
         "usaf_rigl_reselect": [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
         "usaf_sparse_adam": [i32, vp, vp, i64, vp, vp, vp, vp, i64, C.c_double, C.c_double,
@@ -159,12 +160,18 @@ def moe_forward(shape, X, Wr, Wflat, Y, state: State, ws, stream=None):
 
 
 def masked_backward(shape, X, Wr, Wflat, state: State, dY, idx, nnz, dW, dWr, dX, nonfinite, ws,
-                    stream=None):
+                    stream=None, plan=None):
     _check(lib.usaf_masked_backward(C.byref(shape), _p(X), _p(Wr), _p(Wflat), C.byref(state),
-                                    _p(dY), _p(idx), int(nnz), _p(dW), _p(dWr), _p(dX),
+                                    _p(dY), _p(idx), int(nnz), _p(plan), _p(dW), _p(dWr), _p(dX),
                                     _p(nonfinite), _p(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)),
            "usaf_masked_backward")
+
+
+def masked_plan(shape, idx, nnz, plan, stream=None):
+    _check(lib.usaf_masked_plan(C.byref(shape), _p(idx), int(nnz), _p(plan),
+                                plan.numel() * plan.element_size(), _stream(stream)),
+           "usaf_masked_plan")
 
 
 def importance_topk(grad, n, k, exclude, n_exclude, out_idx, out_val, ws, stream=None):

@@ -5,13 +5,21 @@
 // For one (tensor, expert) the selected entries are a sampled subset of
 //   gate_up: G[r, c] = sum_p dGU[p, r] * X[tok(p), c]          (r < 2I, c < H)
 //   down:    G[r, c] = sum_p (w_p dY[tok(p), r]) * a[p, c]     (r < H,  c < I)
-// over the expert's slots p.  A block owns a (row tile x column tile) of one
-// expert and streams the expert's slots through LDS in chunks of 8, staged
-// slot-contiguous ([row][8 slots]) by 8x8 register transposes, so that one
-// 16-byte LDS read yields an entry's 8 slot values.  Each thread accumulates
-// a contiguous run of the block's entries (consecutive entries mostly share
-// a row, whose staged values stay in registers).  gate_up uses bf16 dot2
+// over the expert's slots p.  The work is cut into tiles of one expert's
+// rows [r_lo, r_hi) x one column tile: a builder kernel walks each (expert,
+// column tile)'s rows and closes a tile before it would exceed a row limit
+// (set from the list's average density) or one block's pass of entries, so
+// the tiles stay balanced however the selected entries cluster (an
+// importance-selected list is far from uniform: a few rows carry hundreds of
+// entries).  A block takes one
+// tile and streams the expert's slots in chunks of 8: the staging threads
+// load chunk c+2 into registers and transpose chunk c+1 into one of two
+// slot-contiguous LDS buffers ([element][8 slots], one 16-byte read yields
+// an entry's 8 slot values) while every thread multiplies chunk c from the
+// other, one barrier per chunk.  Each thread accumulates a contiguous run of
+// the tile's entries in branch-free groups of 4.  gate_up uses bf16 dot2
 // (fp32 accumulate); down stages w_p * dY in fp32 and uses fp32 FMA.
+#include <algorithm>
 #include <cmath>
 
 #include "common.hpp"
@@ -23,13 +31,19 @@ namespace usaf {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kSlots = 8;        // slots per staged chunk
-constexpr int kThreads = 512;    // 8 waves per block, one block per CU
-constexpr int kMaxEnt = 24;      // entries per thread per pass
-constexpr int kMaxRB = 1024;     // max rows per block
-constexpr int kMaxCB = 2048;     // max columns per block (kMaxCB/8 + kMaxRB/8 <= kThreads)
+constexpr int kThreads = 512;    // 8 waves per block
+constexpr int kMaxEnt = 24;      // entries per thread per pass (gate_up; down: kMaxEntDown)
+constexpr int kMaxEntDown = 16;  // down's fp32 rows leave fewer registers
+constexpr int kMaxRB = 1024;     // max rows per tile
+constexpr int kMaxCB = 2048;     // max columns per tile ((kMaxCB + kMaxRB + 8)/8 <= kThreads)
+template <bool kDown>
+constexpr int kEnt = kDown ? kMaxEntDown : kMaxEnt;  // entries per thread per pass
+template <bool kDown>
+constexpr int kCap = kThreads * kEnt<kDown>;          // entries of one tile: one pass of a block
 constexpr int kTokTab = 2048;    // slots per token-table window
-constexpr int kLsBytes = kMaxRB * kSlots * 4;
+constexpr int kLsBytes = (kMaxRB + 8) * kSlots * 4;  // rows from r_lo rounded down to 8
 constexpr int kRsBytes = kMaxCB * kSlots * 2;
+static_assert(kMaxCB <= kThreads * kMaxEntDown, "a single row fits a tile");
 
 struct MaskedArgs {
   const uint32_t* idx; int64_t nnz;
@@ -38,7 +52,7 @@ struct MaskedArgs {
   const int32_t* offsets; const int32_t* perm; const float* topk_w;
   int K;
   int R, C;               // rows / columns of the per-expert gradient
-  int RB, CB, nrt, nct;   // tiling
+  int CB, nct;            // column tiling
   int E;
   int64_t base;           // flat index of expert 0's (0,0) entry for this tensor
   float* dW; int32_t* nonfinite;
@@ -55,8 +69,10 @@ struct SegLayout {
 
 __global__ __launch_bounds__(256) void masked_plan_kernel(const uint32_t* __restrict__ idx,
                                                           int64_t nnz, SegLayout Lq,
-                                                          uint32_t* __restrict__ seg) {
+                                                          uint32_t* __restrict__ seg,
+                                                          int* __restrict__ tile_counters) {
   const int64_t q = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q < 2) tile_counters[q] = 0;  // the tile builders append after this kernel
   if (q > Lq.Q) return;
   int64_t key;  // flat index where segment q begins
   if (q == Lq.Q) {
@@ -175,26 +191,123 @@ __device__ __forceinline__ void stage_store(int b, int nblk_r, const StageRegs& 
   }
 }
 
+// Tiles of one tensor.  Group g = (expert e, column tile ct), e-major; its
+// rows' entry counts come from the plan's segment starts (per group fewer
+// than 2^31 entries).  One wave per group walks the rows 64 at a time and
+// cuts greedily: row r joins the open tile [open_r, r) unless the tile would
+// then exceed RB rows or cap entries; then the open tile is closed (listed
+// if it holds entries) and r opens the next.  A single row never exceeds cap
+// (at most kMaxCB entries), so every tile is one pass of a block.  On a
+// uniform list the row limit decides and the tiles are the plain geometric
+// ones; clustered rows are cut into more, smaller tiles.  A group's tiles
+// are appended together at an atomically reserved position: the order of
+// the groups in the list changes no result, since every tile's entries are
+// computed the same way by whichever block takes it.
+// Tile: x = e | ct << 16, y = r_lo | r_hi << 16.
+__global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __restrict__ seg,
+                                                           int64_t qbase, int E, int R, int nct,
+                                                           int RB, int cap, uint2* __restrict__ tiles,
+                                                           int* __restrict__ ntiles) {
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g >= E * nct) return;  // uniform per wave
+  const int e = g / nct, ct = g - e * nct;
+  const uint32_t tx = uint32_t(e) | (uint32_t(ct) << 16);
+  // segment of row r: q0 + r*nct; its entries: seg[q+1] - seg[q]
+  const int64_t q0 = qbase + int64_t(e) * R * nct + ct;
+  // two walks over the rows: the first counts the group's tiles and
+  // reserves them at once (a group's tiles stay consecutive in the list), the
+  // second writes them; each walk loads the counts of 16 chunks of 64 rows at
+  // once (independent loads), then scans them chunk by chunk
+  int base = 0;
+  constexpr int kSpan = 16;  // 64-row chunks whose counts are loaded together
+  for (int walk = 0; walk < 2; ++walk) {
+    int open_r = 0, open_x = 0;  // first row of the open tile, its exclusive prefix
+    int carry = 0;               // exclusive prefix of the chunk's first row
+    int n = 0;                   // tiles with entries so far
+    for (int s0 = 0; s0 < R; s0 += 64 * kSpan) {
+      int cnts[kSpan];
+#pragma unroll
+      for (int j = 0; j < kSpan; ++j) {
+        const int r = s0 + 64 * j + lane;
+        cnts[j] = 0;
+        if (r < R) {
+          const int64_t q = q0 + int64_t(r) * nct;
+          cnts[j] = int(seg[q + 1] - seg[q]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kSpan; ++j) {
+        const int r0 = s0 + 64 * j;
+        if (r0 >= R) break;  // uniform
+        const int r = r0 + lane;
+        const int cnt = cnts[j];
+        int incl = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int v = __shfl_up(incl, d, 64);
+          if (lane >= d) incl += v;
+        }
+        const int excl = carry + incl - cnt;
+        // at most one cut per row, taken in row order
+        while (true) {
+          const bool cut = r < R && r > open_r && (r - open_r >= RB || excl + cnt - open_x > cap);
+          const uint64_t m = __ballot(cut);
+          if (!m) break;
+          const int c = __ffsll((long long)m) - 1;
+          const int cr = r0 + c;
+          const int cx = __shfl(excl, c, 64);
+          if (cx > open_x) {
+            if (walk == 1 && lane == 0)
+              tiles[base + n] = make_uint2(tx, uint32_t(open_r) | (uint32_t(cr) << 16));
+            ++n;
+          }
+          open_r = cr;
+          open_x = cx;
+        }
+        carry += __shfl(incl, 63, 64);
+      }
+    }
+    if (carry > open_x) {
+      if (walk == 1 && lane == 0) tiles[base + n] = make_uint2(tx, uint32_t(open_r) | (uint32_t(R) << 16));
+      ++n;
+    }
+    if (walk == 0) {
+      if (n == 0) return;  // uniform
+      if (lane == 0) base = atomicAdd(ntiles, n);
+      base = __shfl(base, 0, 64);
+    }
+  }
+}
+
+// Tiles of the list, one at a time per block: the rows [r_lo, r_hi) of
+// expert e in column tile ct, all the tile's entries in one pass (at most
+// kCap<kDown>).
 template <bool kDown>
-__global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds_l[kLsBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_r[kRsBytes];
+__global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A, const uint2* __restrict__ tiles,
+                                                                  const int* __restrict__ ntiles) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds_l[2][kDown ? kLsBytes : kLsBytes / 2];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_r[2][kRsBytes];
   __shared__ int rowpre[kMaxRB + 1];
   __shared__ uint32_t rstart[kMaxRB];
   __shared__ int tok_tab[kTokTab];
   __shared__ float w_tab[kDown ? kTokTab : 1];
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int per_e = A.nrt * A.nct;
-  const int L = xcd_remap_blocks(blockIdx.x, gridDim.x);
-  const int e = L / per_e;
-  if (e >= A.E) return;
-  const int rem = L - e * per_e;
-  const int rt = rem / A.nct, ct = rem - rt * A.nct;
-  const int r_lo = rt * A.RB, r_hi = min(A.R, r_lo + A.RB), nr = r_hi - r_lo;
+  constexpr int kE = kEnt<kDown>;
+  const int tid = threadIdx.x;
+  const int nt = *ntiles;
+  // persistent: block b takes tiles x(b), x(b) + G, ... (x: the XCD-aware
+  // order, so that a group's consecutive tiles share an XCD's L2)
+  for (int L = xcd_remap_blocks(blockIdx.x, gridDim.x); L < nt; L += gridDim.x) {
+  __syncthreads();  // the previous tile's tables are no longer read
+  const uint2 td = tiles[L];
+  const int e = int(td.x & 0xffffu), ct = int(td.x >> 16);
+  const int r_lo = int(td.y & 0xffffu), r_hi = int(td.y >> 16), nr = r_hi - r_lo;
+  // rows are staged from r_al (16-byte aligned loads); an entry of local
+  // row i (from r_lo) sits at staged row i + shift
+  const int r_al = r_lo & ~7, shift = r_lo - r_al;
   const int c0 = ct * A.CB, c1 = min(A.C, c0 + A.CB), ncol = c1 - c0;
-  const int64_t ebase = A.base + int64_t(e) * A.R * A.C;
-  (void)ebase;
+  const int lane = tid & 63;
 
   // entries of this tile: per row r, the plan segment (e, r, ct)
   const int64_t q_r0 = A.qbase + (int64_t(e) * A.R + r_lo) * A.nct + ct;
@@ -221,18 +334,18 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A)
   }
   __syncthreads();
   const int nent = rowpre[nr];
-  if (nent == 0) return;  // nothing selected in this tile (uniform)
+  if (nent == 0) continue;  // uniform
 
   const int off = A.offsets[e];
   const int ne = A.offsets[e + 1] - off;
-  const int nblk_r = (ncol + 7) >> 3, nblk_l = (nr + 7) >> 3;
+  const int nblk_r = (ncol + 7) >> 3, nblk_l = (nr + shift + 7) >> 3;
 
   for (int q0 = 0, per = 0; q0 < nent; q0 += kThreads * per) {
     // this pass: per entries for every thread (spread evenly, at most
-    // kMaxEnt), thread tid taking q0 + tid*per + i
-    per = min(kMaxEnt, (nent - q0 + kThreads - 1) / kThreads);
-    uint32_t coord[kMaxEnt];  // (row - r_lo) << 16 | (col - c0), or ~0 when unused
-    float acc[kMaxEnt];
+    // kE), thread tid taking q0 + tid*per + i
+    per = min(kE, (nent - q0 + kThreads - 1) / kThreads);
+    uint32_t coord[kE];  // (row - r_lo) << 16 | (col - c0), or ~0 when unused
+    float acc[kE];
     {
       const int q = q0 + tid * per;
       // row of entry q: last r with rowpre[r] <= q
@@ -241,93 +354,127 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A)
         const int mid = (lo + hi + 1) >> 1;
         if (rowpre[mid] <= q) lo = mid; else hi = mid - 1;
       }
+      // rows (kept in the coordinate words) and list positions from LDS
+      // first, then every list load at once (independent registers), then
+      // the columns
       int r = lo;
+      uint32_t pos[kE];
 #pragma unroll
-      for (int i = 0; i < kMaxEnt; ++i) {
-        acc[i] = 0.f;
-        coord[i] = 0xffffffffu;
+      for (int i = 0; i < kE; ++i) {
         const int qi = q + i;
+        coord[i] = 0xffffffffu;
+        pos[i] = rstart[0];
         if (i < per && qi < nent) {
           while (rowpre[r + 1] <= qi) ++r;
-          const int64_t rb = A.base + (int64_t(e) * A.R + r_lo + r) * A.C;
-          const int c = int(int64_t(A.idx[rstart[r] + (qi - rowpre[r])]) - rb);
-          coord[i] = (uint32_t(r) << 16) | uint32_t(c - c0);
+          coord[i] = uint32_t(r) << 16;
+          pos[i] = rstart[r] + uint32_t(qi - rowpre[r]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kE; ++i) pos[i] = A.idx[pos[i]];
+      const int64_t rb0 = A.base + (int64_t(e) * A.R + r_lo) * A.C + c0;
+#pragma unroll
+      for (int i = 0; i < kE; ++i) {
+        acc[i] = 0.f;
+        if (coord[i] != 0xffffffffu) {
+          const int ri = int(coord[i] >> 16);
+          coord[i] |= uint32_t(int64_t(pos[i]) - (rb0 + int64_t(ri) * A.C));
         }
       }
     }
-    // stream the expert's slots, a token-table window at a time, in chunks
-    // of kSlots staged through LDS
-    const bool stager = tid < nblk_r + nblk_l;  // <= kThreads staging blocks: one per thread
+    // Products over one staged chunk, entries in branch-free groups (4, or 2
+    // for down): the LDS reads of a group (an unused entry reads row 0 and
+    // column 0) are all issued before its products.
+    auto compute = [&](const unsigned char* Ls, const unsigned char* Rs) {
+      constexpr int kG = kDown ? 2 : 4;  // entries per group (down rows are 32-byte fp32)
+      static_for<kE / kG>([&](auto G_) {
+        constexpr int g0 = kG * decltype(G_)::value;
+        if (g0 >= per) return;
+        uint32_t lr[kG], lc[kG];
+#pragma unroll
+        for (int k = 0; k < kG; ++k) {
+          const uint32_t cd = coord[g0 + k];
+          lr[k] = cd == 0xffffffffu ? 0u : (cd >> 16) + uint32_t(shift);
+          lc[k] = cd == 0xffffffffu ? 0u : cd & 0xffffu;
+        }
+        uint4 rv[kG];
+#pragma unroll
+        for (int k = 0; k < kG; ++k) rv[k] = *reinterpret_cast<const uint4*>(Rs + size_t(sw16(lc[k])) * 16);
+        if constexpr (kDown) {
+          float4 lx[kG], ly[kG];
+#pragma unroll
+          for (int k = 0; k < kG; ++k) {
+            const float4* src = reinterpret_cast<const float4*>(Ls + size_t(sw32(lr[k])) * 32);
+            lx[k] = src[0];
+            ly[k] = src[1];
+          }
+#pragma unroll
+          for (int k = 0; k < kG; ++k) {
+            float a = acc[g0 + k];
+            a = fmaf(lx[k].x, bflo(rv[k].x), a); a = fmaf(lx[k].y, bfhi(rv[k].x), a);
+            a = fmaf(lx[k].z, bflo(rv[k].y), a); a = fmaf(lx[k].w, bfhi(rv[k].y), a);
+            a = fmaf(ly[k].x, bflo(rv[k].z), a); a = fmaf(ly[k].y, bfhi(rv[k].z), a);
+            a = fmaf(ly[k].z, bflo(rv[k].w), a); a = fmaf(ly[k].w, bfhi(rv[k].w), a);
+            acc[g0 + k] = a;
+          }
+        } else {
+          uint4 lb[kG];
+#pragma unroll
+          for (int k = 0; k < kG; ++k) lb[k] = *reinterpret_cast<const uint4*>(Ls + size_t(sw16(lr[k])) * 16);
+#pragma unroll
+          for (int k = 0; k < kG; ++k) {
+            float a = acc[g0 + k];
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb[k].x),
+                                                __builtin_bit_cast(bf16x2_t, rv[k].x), a, false);
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb[k].y),
+                                                __builtin_bit_cast(bf16x2_t, rv[k].y), a, false);
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb[k].z),
+                                                __builtin_bit_cast(bf16x2_t, rv[k].z), a, false);
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb[k].w),
+                                                __builtin_bit_cast(bf16x2_t, rv[k].w), a, false);
+            acc[g0 + k] = a;
+          }
+        }
+      });
+    };
+    // stream the expert's slots, a token-table window at a time
+    const bool stager = tid < nblk_r + nblk_l;  // one staging block per thread
     for (int w0 = 0; w0 < ne; w0 += kTokTab) {
       const int wn = min(kTokTab, ne - w0);
-      __syncthreads();  // previous window fully consumed
+      __syncthreads();  // previous window's tables and buffers consumed
       for (int p = tid; p < wn; p += kThreads) {
         const int sid = A.perm[off + w0 + p];
         tok_tab[p] = sid / A.K;
         if (kDown) w_tab[p] = A.topk_w[sid];
       }
       __syncthreads();
-      // chunk c+1 is fetched into registers while chunk c is consumed
-      auto compute = [&]() {
-        uint32_t prow = 0xffffffffu;
-        uint4 lb16 = make_uint4(0, 0, 0, 0);
-        float lf[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) lf[t] = 0.f;
-#pragma unroll
-        for (int i = 0; i < kMaxEnt; ++i) {
-          const uint32_t cd = coord[i];
-          if (cd == 0xffffffffu) continue;
-          const uint32_t lr = cd >> 16, lc = cd & 0xffffu;
-          if (lr != prow) {
-            prow = lr;
-            if (kDown) {
-              const float4* src = reinterpret_cast<const float4*>(lds_l + size_t(sw32(lr)) * 32);
-              const float4 x = src[0], y = src[1];
-              lf[0] = x.x; lf[1] = x.y; lf[2] = x.z; lf[3] = x.w;
-              lf[4] = y.x; lf[5] = y.y; lf[6] = y.z; lf[7] = y.w;
-            } else {
-              lb16 = *reinterpret_cast<const uint4*>(lds_l + size_t(sw16(lr)) * 16);
-            }
-          }
-          const uint4 rv = *reinterpret_cast<const uint4*>(lds_r + size_t(sw16(lc)) * 16);
-          float a = acc[i];
-          if (kDown) {
-            a = fmaf(lf[0], bflo(rv.x), a); a = fmaf(lf[1], bfhi(rv.x), a);
-            a = fmaf(lf[2], bflo(rv.y), a); a = fmaf(lf[3], bfhi(rv.y), a);
-            a = fmaf(lf[4], bflo(rv.z), a); a = fmaf(lf[5], bfhi(rv.z), a);
-            a = fmaf(lf[6], bflo(rv.w), a); a = fmaf(lf[7], bfhi(rv.w), a);
-          } else {
-            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb16.x),
-                                                __builtin_bit_cast(bf16x2_t, rv.x), a, false);
-            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb16.y),
-                                                __builtin_bit_cast(bf16x2_t, rv.y), a, false);
-            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb16.z),
-                                                __builtin_bit_cast(bf16x2_t, rv.z), a, false);
-            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb16.w),
-                                                __builtin_bit_cast(bf16x2_t, rv.w), a, false);
-          }
-          acc[i] = a;
-        }
-      };
+      const int nch = (wn + kSlots - 1) / kSlots;
+      // chunk c is multiplied from buffer c & 1; while it is, the staging
+      // threads write chunk c+1 (loaded during chunk c-1) into the other
+      // buffer and load chunk c+2
       StageRegs sr;
-      if (stager) stage_fetch<kDown>(A, tid, nblk_r, 0, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr);
-      for (int p0 = 0; p0 < wn; p0 += kSlots) {
-        __syncthreads();  // previous chunk fully consumed
-        if (stager) stage_store<kDown>(tid, nblk_r, sr, lds_l, lds_r);
-        __syncthreads();
-        if (stager && p0 + kSlots < wn)
-          stage_fetch<kDown>(A, tid, nblk_r, p0 + kSlots, wn, off + w0, r_lo, c0, tok_tab, w_tab, sr);
-        compute();
+      if (stager) {
+        stage_fetch<kDown>(A, tid, nblk_r, 0, wn, off + w0, r_al, c0, tok_tab, w_tab, sr);
+        stage_store<kDown>(tid, nblk_r, sr, lds_l[0], lds_r[0]);
+        if (nch > 1) stage_fetch<kDown>(A, tid, nblk_r, kSlots, wn, off + w0, r_al, c0, tok_tab, w_tab, sr);
+      }
+      for (int c = 0; c < nch; ++c) {
+        __syncthreads();  // buffer c & 1 written; buffer (c+1) & 1 no longer read
+        if (stager && c + 1 < nch) {
+          stage_store<kDown>(tid, nblk_r, sr, lds_l[(c + 1) & 1], lds_r[(c + 1) & 1]);
+          if (c + 2 < nch)
+            stage_fetch<kDown>(A, tid, nblk_r, (c + 2) * kSlots, wn, off + w0, r_al, c0, tok_tab,
+                               w_tab, sr);
+        }
+        compute(lds_l[c & 1], lds_r[c & 1]);
       }
     }
-    // write this thread's entries (contiguous positions in idx within a row run;
-    // recompute positions row by row)
+    // write this thread's entries
     {
       const int q = q0 + tid * per;
       int nbad = 0;
 #pragma unroll
-      for (int i = 0; i < kMaxEnt; ++i) {
+      for (int i = 0; i < kE; ++i) {
         const uint32_t cd = coord[i];
         if (cd == 0xffffffffu) continue;
         const int ri = int(cd >> 16);
@@ -337,6 +484,7 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A)
       }
       if (A.nonfinite && nbad) atomicAdd(A.nonfinite, nbad);
     }
+  }
   }
 }
 
@@ -348,33 +496,42 @@ static void col_tiles(int C, int& CB, int& nct) {
   nct = int(ceil_div(C, CB));
 }
 
-int64_t masked_plan_segments(const usaf_moe_shape& s) {
-  int CB0, nct0, CB1, nct1;
-  col_tiles(s.H, CB0, nct0);
-  col_tiles(s.I, CB1, nct1);
-  return int64_t(s.E) * 2 * s.I * nct0 + int64_t(s.E) * s.H * nct1;
-}
-
-// Row tiling: as few row tiles as the LDS staging allows (the expert's slot
-// stream is re-read once per tile), but enough that each block's entries
-// fit one pass of about 20 per thread.  Returns the tile height (a multiple
-// of 8).
-static int row_tile(int R, int CB, double density) {
+// Row limit of the tiles: as few row tiles as the LDS staging allows (the
+// expert's slot stream is re-read once per tile), but enough that a tile of
+// the list's average density fills at most one pass; the tile builder cuts
+// where the local density is higher.  A multiple of 8.
+static int row_tile(int R, int CB, double density, int ent) {
   const double per_row = double(CB) * (density > 0 ? density : 1e-9);
   int64_t nrt = ceil_div(int64_t(R), int64_t(kMaxRB));
-  const int64_t by_entries = int64_t(std::ceil(double(R) * per_row / (20.0 * kThreads)));
+  const int64_t by_entries = int64_t(std::ceil(double(R) * per_row / (double(ent) * kThreads)));
   if (by_entries > nrt) nrt = by_entries;
   const int64_t rb = ceil_div(ceil_div(int64_t(R), nrt), int64_t(8)) * 8;
   return int(rb < R ? rb : R);
 }
 
-usaf_status masked_dw_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64_t nnz,
-                           const bf16_t* X, const bf16_t* dY, const bf16_t* dgu, const bf16_t* a,
-                           const float* topk_w, const int32_t* offsets, const int32_t* perm,
-                           float* dW, int32_t* nonfinite, uint32_t* seg, hipStream_t st) {
-  if (nnz == 0) return USAF_OK;
-  const double density = double(nnz) / double(n_weights(s));
+// Upper bound on the tiles of one tensor (R rows, C columns per expert)
+// holding at most nnz entries, for row limit RB >= 1: per group one tile per
+// RB rows plus one per entry cut; two consecutive entry-cut tiles hold more
+// than kCap entries together, so entry cuts number at most 2 nnz / kCap + 1
+// per group.
+static int64_t tile_bound(const usaf_moe_shape& s, int R, int C, int64_t nnz, int RB, int cap) {
+  int CB, nct;
+  col_tiles(C, CB, nct);
+  return int64_t(s.E) * nct * (2 + ceil_div(R, RB)) + ceil_div(2 * nnz, cap);
+}
+
+// Plan layout (bytes): segment starts [Q+1] u32 (256-aligned), two tile
+// counters (256 bytes), the gate_up tile list, the down tile list.
+struct PlanLayout {
   SegLayout Lq;
+  int RB0, RB1;
+  int64_t b0, b1;   // tile bounds for this nnz (block counts)
+  size_t counters, tiles0, tiles1, total;
+};
+
+static PlanLayout plan_layout(const usaf_moe_shape& s, int64_t nnz) {
+  PlanLayout P;
+  SegLayout& Lq = P.Lq;
   Lq.E = s.E;
   Lq.R0 = 2 * s.I; Lq.C0 = s.H;
   Lq.R1 = s.H; Lq.C1 = s.I;
@@ -383,29 +540,85 @@ usaf_status masked_dw_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64_t
   Lq.ngu = int64_t(s.E) * 2 * s.I * s.H;
   Lq.q1 = int64_t(s.E) * Lq.R0 * Lq.nct0;
   Lq.Q = Lq.q1 + int64_t(s.E) * Lq.R1 * Lq.nct1;
-  timer_begin(USAF_K_MASKED_DW, st);
-  hipLaunchKernelGGL(masked_plan_kernel, dim3(unsigned(ceil_div(Lq.Q + 1, 256))), dim3(256), 0, st,
-                     idx, nnz, Lq, seg);
+  const int64_t N = n_weights(s);
+  const double density = double(nnz) / double(N);
+  P.RB0 = row_tile(Lq.R0, Lq.CB0, density, kEnt<false>);
+  P.RB1 = row_tile(Lq.R1, Lq.CB1, density, kEnt<true>);
+  P.b0 = tile_bound(s, Lq.R0, Lq.C0, std::min<int64_t>(nnz, Lq.ngu), P.RB0, kCap<false>);
+  P.b1 = tile_bound(s, Lq.R1, Lq.C1, std::min<int64_t>(nnz, N - Lq.ngu), P.RB1, kCap<true>);
+  P.counters = ((size_t(Lq.Q + 1) * 4 + 255) / 256) * 256;
+  P.tiles0 = P.counters + 256;
+  P.tiles1 = P.tiles0 + 8 * size_t(tile_bound(s, Lq.R0, Lq.C0, Lq.ngu, 8, kCap<false>));
+  P.total = P.tiles1 + 8 * size_t(tile_bound(s, Lq.R1, Lq.C1, N - Lq.ngu, 8, kCap<true>));
+  return P;
+}
+
+int64_t masked_plan_bytes(const usaf_moe_shape& s) { return int64_t(plan_layout(s, 1).total); }
+
+// The plan of a list: segment starts, then each tensor's tiles.  Depends on
+// idx and the shape only, so one plan serves every step until the list
+// changes.
+usaf_status masked_plan_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64_t nnz, void* plan,
+                             hipStream_t st) {
+  if (nnz == 0) return USAF_OK;
+  const PlanLayout P = plan_layout(s, nnz);
+  if (P.b0 >= (int64_t(1) << 31) || P.b1 >= (int64_t(1) << 31)) return USAF_ERR_UNSUPPORTED;
+  unsigned char* base = static_cast<unsigned char*>(plan);
+  uint32_t* seg = reinterpret_cast<uint32_t*>(base);
+  int* counters = reinterpret_cast<int*>(base + P.counters);
+  hipLaunchKernelGGL(masked_plan_kernel, dim3(unsigned(ceil_div(P.Lq.Q + 1, 256))), dim3(256), 0, st,
+                     idx, nnz, P.Lq, seg, counters);
   USAF_LAUNCH_CHECK();
+  for (int tensor = 0; tensor < 2; ++tensor) {
+    const int nct = tensor == 0 ? P.Lq.nct0 : P.Lq.nct1;
+    const int groups = s.E * nct;
+    hipLaunchKernelGGL(masked_tiles_kernel, dim3(unsigned(ceil_div(groups, 4))), dim3(256), 0, st,
+                       seg, tensor == 0 ? int64_t(0) : P.Lq.q1, s.E, tensor == 0 ? P.Lq.R0 : P.Lq.R1, nct,
+                       tensor == 0 ? P.RB0 : P.RB1, tensor == 0 ? kCap<false> : kCap<true>,
+                       reinterpret_cast<uint2*>(base + (tensor == 0 ? P.tiles0 : P.tiles1)),
+                       counters + tensor);
+    USAF_LAUNCH_CHECK();
+  }
+  return USAF_OK;
+}
+
+usaf_status masked_dw_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64_t nnz,
+                           const bf16_t* X, const bf16_t* dY, const bf16_t* dgu, const bf16_t* a,
+                           const float* topk_w, const int32_t* offsets, const int32_t* perm,
+                           float* dW, int32_t* nonfinite, const void* plan, void* ws_plan,
+                           hipStream_t st) {
+  if (nnz == 0) return USAF_OK;
+  const PlanLayout P = plan_layout(s, nnz);
+  if (P.b0 >= (int64_t(1) << 31) || P.b1 >= (int64_t(1) << 31)) return USAF_ERR_UNSUPPORTED;
+  timer_begin(USAF_K_MASKED_DW, st);
+  if (!plan) {  // no plan kept by the caller: build one in the workspace
+    USAF_TRY(masked_plan_bf16(s, idx, nnz, ws_plan, st));
+    plan = ws_plan;
+  }
+  const unsigned char* base = static_cast<const unsigned char*>(plan);
+  const uint32_t* seg = reinterpret_cast<const uint32_t*>(base);
+  const int* counters = reinterpret_cast<const int*>(base + P.counters);
   for (int tensor = 0; tensor < 2; ++tensor) {
     MaskedArgs A;
     A.idx = idx; A.nnz = nnz;
     A.offsets = offsets; A.perm = perm; A.topk_w = topk_w; A.K = s.K; A.E = s.E;
     A.dW = dW; A.nonfinite = nonfinite; A.seg = seg;
     if (tensor == 0) {
-      A.L = dgu; A.Rm = X; A.R = Lq.R0; A.C = Lq.C0; A.base = 0;
-      A.CB = Lq.CB0; A.nct = Lq.nct0; A.qbase = 0;
+      A.L = dgu; A.Rm = X; A.R = P.Lq.R0; A.C = P.Lq.C0; A.base = 0;
+      A.CB = P.Lq.CB0; A.nct = P.Lq.nct0; A.qbase = 0;
     } else {
-      A.L = dY; A.Rm = a; A.R = Lq.R1; A.C = Lq.C1; A.base = Lq.ngu;
-      A.CB = Lq.CB1; A.nct = Lq.nct1; A.qbase = Lq.q1;
+      A.L = dY; A.Rm = a; A.R = P.Lq.R1; A.C = P.Lq.C1; A.base = P.Lq.ngu;
+      A.CB = P.Lq.CB1; A.nct = P.Lq.nct1; A.qbase = P.Lq.q1;
     }
-    A.RB = row_tile(A.R, A.CB, density);
-    A.nrt = int(ceil_div(A.R, A.RB));
-    const int64_t blocks = (int64_t(s.E) * A.nrt * A.nct + 7) / 8 * 8;
+    const uint2* tl = reinterpret_cast<const uint2*>(base + (tensor == 0 ? P.tiles0 : P.tiles1));
+    const int64_t bound = tensor == 0 ? P.b0 : P.b1;
+    const int64_t blocks = (std::min<int64_t>(bound, device_cus()) + 7) / 8 * 8;
     if (tensor == 0)
-      hipLaunchKernelGGL(masked_dw_sddmm_kernel<false>, dim3(unsigned(blocks)), dim3(kThreads), 0, st, A);
+      hipLaunchKernelGGL(masked_dw_sddmm_kernel<false>, dim3(unsigned(blocks)), dim3(kThreads), 0, st, A, tl,
+                         counters);
     else
-      hipLaunchKernelGGL(masked_dw_sddmm_kernel<true>, dim3(unsigned(blocks)), dim3(kThreads), 0, st, A);
+      hipLaunchKernelGGL(masked_dw_sddmm_kernel<true>, dim3(unsigned(blocks)), dim3(kThreads), 0, st, A, tl,
+                         counters + 1);
     USAF_LAUNCH_CHECK();
   }
   timer_end(USAF_K_MASKED_DW, st);

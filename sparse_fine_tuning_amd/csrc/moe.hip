@@ -776,8 +776,8 @@ static usaf_status forward_impl(const usaf_moe_shape& s, const T* X, const float
 template <class T>
 static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const float* Wr, const T* W,
                                  const usaf_moe_state& st, const T* dY, const uint32_t* idx,
-                                 int64_t nnz, float* dW, float* dWr, T* dX, int32_t* nonfinite,
-                                 char* ws, hipStream_t stream) {
+                                 int64_t nnz, const void* plan, float* dW, float* dWr, T* dX,
+                                 int32_t* nonfinite, char* ws, hipStream_t stream) {
   const WsBackward L = ws_backward(s);
   float* vbuf = reinterpret_cast<float*>(ws + L.vbuf);
   float* dwpart = reinterpret_cast<float*>(ws + L.dwpart);
@@ -822,7 +822,7 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
   if (idx) {
     if constexpr (kMfma) {
       return masked_dw_bf16(s, idx, nnz, X, dY, dgu, a, st.topk_w, st.offsets, st.perm, dW,
-                            nonfinite, reinterpret_cast<uint32_t*>(ws + L.seg), stream);
+                            nonfinite, plan, ws + L.seg, stream);
     }
     if (nnz > 0) {
       timer_begin(USAF_K_MASKED_DW, stream);
@@ -892,9 +892,9 @@ extern "C" usaf_status usaf_moe_forward(const usaf_moe_shape* shape, const void*
 extern "C" usaf_status usaf_masked_backward(const usaf_moe_shape* shape, const void* X,
                                             const float* Wr, const void* Wflat,
                                             const usaf_moe_state* state, const void* dY,
-                                            const uint32_t* idx, int64_t nnz, float* dW,
-                                            float* dWr, void* dX, int32_t* nonfinite, void* ws,
-                                            size_t ws_bytes, hipStream_t stream) {
+                                            const uint32_t* idx, int64_t nnz, const void* plan,
+                                            float* dW, float* dWr, void* dX, int32_t* nonfinite,
+                                            void* ws, size_t ws_bytes, hipStream_t stream) {
   USAF_TRY(check_shape(shape));
   if (!X || !Wr || !Wflat || !dY || !dWr || !state_ok(state, true)) return USAF_ERR_INVALID_ARG;
   const int64_t N = n_weights(*shape);
@@ -905,12 +905,23 @@ extern "C" usaf_status usaf_masked_backward(const usaf_moe_shape* shape, const v
   if (shape->act == USAF_BF16)
     return backward_impl<bf16_t>(*shape, static_cast<const bf16_t*>(X), Wr,
                                  static_cast<const bf16_t*>(Wflat), *state,
-                                 static_cast<const bf16_t*>(dY), idx, nnz, dW, dWr,
-                                 static_cast<bf16_t*>(dX), nonfinite, static_cast<char*>(ws), stream);
+                                 static_cast<const bf16_t*>(dY), idx, nnz, idx ? plan : nullptr, dW,
+                                 dWr, static_cast<bf16_t*>(dX), nonfinite, static_cast<char*>(ws),
+                                 stream);
   return backward_impl<float>(*shape, static_cast<const float*>(X), Wr,
                               static_cast<const float*>(Wflat), *state,
-                              static_cast<const float*>(dY), idx, nnz, dW, dWr,
+                              static_cast<const float*>(dY), idx, nnz, nullptr, dW, dWr,
                               static_cast<float*>(dX), nonfinite, static_cast<char*>(ws), stream);
+}
+
+extern "C" usaf_status usaf_masked_plan(const usaf_moe_shape* shape, const uint32_t* idx,
+                                        int64_t nnz, void* plan, size_t plan_bytes,
+                                        hipStream_t stream) {
+  USAF_TRY(check_shape(shape));
+  if (nnz < 0 || nnz > n_weights(*shape) || (nnz > 0 && !idx)) return USAF_ERR_INVALID_ARG;
+  if (shape->act != USAF_BF16) return USAF_OK;  // fp32 layers need no plan
+  if (!plan || plan_bytes < size_t(masked_plan_bytes(*shape))) return USAF_ERR_WORKSPACE;
+  return masked_plan_bf16(*shape, idx, nnz, plan, stream);
 }
 
 extern "C" usaf_status usaf_mse_grad(const usaf_moe_shape* shape, const void* Y, const void* tgt,

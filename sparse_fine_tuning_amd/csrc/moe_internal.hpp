@@ -10,7 +10,10 @@
 
 namespace usaf {
 
-int64_t masked_plan_segments(const usaf_moe_shape& s);
+// Bytes of a masked-gradient plan (segment starts and tile lists).
+int64_t masked_plan_bytes(const usaf_moe_shape& s);
+// Compute units of the current device (cached per device).
+int device_cus();
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -49,7 +52,7 @@ inline WsForward ws_forward(const usaf_moe_shape& s) {
 
 // Backward workspace: fp32 dX contributions [S, H], partial dw sums
 // [S, NT] (NT = dA column tiles), dlogits of the chosen experts [S], and
-// the masked-gradient plan (segment starts, u32).
+// a masked-gradient plan built per call when the caller keeps none.
 struct WsBackward {
   size_t vbuf, dwpart, dl, seg, total;
   int nt;
@@ -62,7 +65,7 @@ inline WsBackward ws_backward(const usaf_moe_shape& s) {
   L.dwpart = align256(S * s.H * 4);
   L.dl = L.dwpart + align256(S * L.nt * 4);
   L.seg = L.dl + align256(S * 4);
-  L.total = L.seg + align256(size_t(masked_plan_segments(s) + 1) * 4);
+  L.total = L.seg + align256(size_t(masked_plan_bytes(s)));
   return L;
 }
 
@@ -98,13 +101,15 @@ usaf_status mfma_dense_dw(const usaf_moe_shape& s, const uint16_t* X, const uint
                           const int32_t* perm, const float* topk_w, uint16_t* stage, float* dW,
                           hipStream_t st);
 
+// Masked gradient of a bf16 layer at idx: with plan == NULL a plan is built
+// in ws_plan (masked_plan_bytes) first.
 usaf_status masked_dw_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64_t nnz,
                            const uint16_t* X, const uint16_t* dY, const uint16_t* dgu,
                            const uint16_t* a, const float* topk_w, const int32_t* offsets,
-                           const int32_t* perm, float* dW, int32_t* nonfinite, uint32_t* seg,
-                           hipStream_t st);
-// Segments (expert, row, column tile) of the masked-gradient plan.
-int64_t masked_plan_segments(const usaf_moe_shape& s);
+                           const int32_t* perm, float* dW, int32_t* nonfinite, const void* plan,
+                           void* ws_plan, hipStream_t st);
+usaf_status masked_plan_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64_t nnz, void* plan,
+                             hipStream_t st);
 
 // Workspace of one top-k selection over n keys / one RigL reselection.
 size_t topk_ws_bytes(int64_t n);

@@ -448,7 +448,7 @@ static usaf_status launch_v2(const P& p, int64_t tiles, hipStream_t st, int kcla
 }
 
 // Compute units of the current device (cached per device).
-static int device_cus() {
+int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

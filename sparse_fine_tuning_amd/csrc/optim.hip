@@ -230,6 +230,10 @@ extern "C" usaf_status usaf_workspace_size(int32_t kind, const usaf_moe_shape* s
       if (n < 0 || k < 0 || k > n || n >= (int64_t(1) << 32)) return USAF_ERR_INVALID_ARG;
       *bytes = rigl_ws_bytes(n, k);
       return USAF_OK;
+    case USAF_WS_MASKED_PLAN:
+      USAF_TRY(check_shape(shape));
+      *bytes = shape->act == USAF_BF16 ? size_t(masked_plan_bytes(*shape)) : 256;
+      return USAF_OK;
     default:
       return USAF_ERR_INVALID_ARG;
   }

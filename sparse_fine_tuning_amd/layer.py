@@ -81,11 +81,16 @@ class SparseMoELayer:
         self.refresh_list()
 
     def refresh_list(self):
-        """Compact copy of the active weights (W at idx) that SparseAdam reads
-        instead of the scattered entries; rebuilt whenever the list changes."""
+        """Per-list state rebuilt whenever the list changes: the compact copy
+        of the active weights (W at idx) that SparseAdam reads instead of the
+        scattered entries, and the masked gradient's plan."""
         k = self.idx.numel()
         self.w_list = torch.empty(k, dtype=_dt(self.act), device=self.device)
         capi.gather(self.act, self.W, self.idx, k, self.w_list)
+        if getattr(self, "plan", None) is None:
+            self.plan = torch.empty(capi.workspace_size(capi.WS_MASKED_PLAN, self.shape),
+                                    dtype=torch.uint8, device=self.device)
+        capi.masked_plan(self.shape, self.idx, k, self.plan)
 
     # ---- the step ------------------------------------------------------------
     def forward(self, stream=None):
@@ -105,7 +110,7 @@ class SparseMoELayer:
             capi.masked_backward(self.shape, self.X, self.Wr, self.W, self.state, self.dY,
                                  self.idx, self.idx.numel(), self.dW, self.dWr,
                                  self.dX if want_dx else None, self.nonfinite, self.ws_bwd,
-                                 stream)
+                                 stream, plan=self.plan)
 
     def adam(self, step, lr, betas=(0.9, 0.999), eps=1e-8, stream=None):
         b1, b2 = betas

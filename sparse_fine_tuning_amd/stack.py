@@ -59,7 +59,8 @@ class _Layer:
         self.mr = torch.zeros(E, H, dtype=torch.float32, device=dev)
         self.vr = torch.zeros(E, H, dtype=torch.float32, device=dev)
         self.dWr = z(E, H)
-        self.idx = self.m = self.v = self.dW = self.w_list = None
+        self.shape = shape
+        self.idx = self.m = self.v = self.dW = self.w_list = self.plan = None
 
     def set_active(self, idx: torch.Tensor, act: int):
         """Active list (int32 tensor of ascending uint32 flat indices) with
@@ -73,9 +74,15 @@ class _Layer:
         self.refresh_list(act)
 
     def refresh_list(self, act: int):
+        """The compact weight list SparseAdam reads and the masked gradient's
+        plan, both rebuilt whenever the list changes."""
         k = self.idx.numel()
         self.w_list = torch.empty(k, dtype=_dt(act), device=self.idx.device)
         capi.gather(act, self.W, self.idx, k, self.w_list)
+        if self.plan is None:
+            self.plan = torch.empty(capi.workspace_size(capi.WS_MASKED_PLAN, self.shape),
+                                    dtype=torch.uint8, device=self.idx.device)
+        capi.masked_plan(self.shape, self.idx, k, self.plan)
 
 
 class MoEStack:
@@ -143,7 +150,7 @@ class MoEStack:
             if select is None:
                 capi.masked_backward(self.shape, self.Xs[l], lay.Wr, lay.W, lay.state, G, lay.idx,
                                      lay.idx.numel(), lay.dW, lay.dWr, self.dXl, self.nonfinite,
-                                     self.ws_bwd, stream)
+                                     self.ws_bwd, stream, plan=lay.plan)
             else:
                 dense = self._dense_buffer()
                 capi.masked_backward(self.shape, self.Xs[l], lay.Wr, lay.W, lay.state, G, None,

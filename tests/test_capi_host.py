@@ -84,11 +84,21 @@ def test_entry_points_refuse_bad_arguments_before_launch():
     # backward: dense mode needs nnz == N; nnz range; state needs dgu/dw
     N = sh.N
     assert L.usaf_masked_backward(C.byref(sh), FAKE, FAKE, FAKE, C.byref(st), FAKE, None, N - 1,
-                                  FAKE, FAKE, None, None, FAKE, 1 << 30, None) == 1
+                                  None, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == 1
     assert L.usaf_masked_backward(C.byref(sh), FAKE, FAKE, FAKE, C.byref(st), FAKE, FAKE, N + 1,
-                                  FAKE, FAKE, None, None, FAKE, 1 << 30, None) == 1
+                                  None, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == 1
     assert L.usaf_masked_backward(C.byref(sh), FAKE, FAKE, FAKE, C.byref(bad_state), FAKE, FAKE, 5,
-                                  FAKE, FAKE, None, None, FAKE, 1 << 30, None) == 1
+                                  None, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == 1
+    # masked plan: nnz range, a list pointer, the plan's size (bf16 layers)
+    shb = capi.Shape(128, 64, 8, 2, 32, 1)
+    need = capi.workspace_size(capi.WS_MASKED_PLAN, shb)
+    assert L.usaf_masked_plan(C.byref(shb), FAKE, -1, FAKE, need, None) == 1
+    assert L.usaf_masked_plan(C.byref(shb), FAKE, N + 1, FAKE, need, None) == 1
+    assert L.usaf_masked_plan(C.byref(shb), None, 5, FAKE, need, None) == 1
+    assert L.usaf_masked_plan(C.byref(shb), FAKE, 5, FAKE, need - 1, None) == 3
+    assert L.usaf_masked_plan(C.byref(shb), FAKE, 5, None, need, None) == 3
+    assert L.usaf_masked_plan(C.byref(shb), None, 0, FAKE, need, None) == 0  # empty list: nothing to plan
+    assert L.usaf_masked_plan(C.byref(sh), FAKE, 5, None, 0, None) == 0      # fp32 layers need no plan
     # top-k: k larger than the candidates; k == 0 is a no-op
     assert L.usaf_importance_topk(FAKE, 100, 101, None, 0, FAKE, None, FAKE, 1 << 20, None) == 1
     assert L.usaf_importance_topk(FAKE, 100, 91, FAKE, 10, FAKE, None, FAKE, 1 << 20, None) == 1

@@ -205,6 +205,66 @@ def test_masked_at_full_density_equals_dense(capi):
     assert rel(g, npf(dense)) <= TOL_BF16
 
 
+def skewed_mask(kind, dims, gd):
+    """Clustered active lists: an importance selection (top-2% of the dense
+    gradient: a few rows carry most entries), whole rows at unaligned
+    positions over sparse entries, or every entry in one expert."""
+    T, H, E, K, I = dims
+    N = 3 * E * H * I
+    ngu = E * 2 * I * H
+    rng = np.random.default_rng(11)
+    if kind == "importance":
+        return O.importance_topk(gd, N // 50)
+    if kind == "rows":
+        rows = [(1, 3), (1, 4), (1, 5), (1, 1001), (2, 2 * I - 1), (0, 517)]  # (expert, gate_up row)
+        full = [np.arange(H, dtype=np.int64) + (e * 2 * I + r) * H for e, r in rows]
+        down_rows = [(3, 9), (3, 10)]
+        full += [ngu + np.arange(I, dtype=np.int64) + (e * H + r) * I for e, r in down_rows]
+        sparse = rng.choice(N, N // 500, replace=False)
+        return np.unique(np.concatenate(full + [sparse])).astype(np.uint32)
+    if kind == "one_expert":
+        e = 2
+        gu = np.arange(e * 2 * I * H, (e + 1) * 2 * I * H, dtype=np.int64)
+        dn = ngu + np.arange(e * H * I, (e + 1) * H * I, dtype=np.int64)
+        pool = np.concatenate([gu, dn])
+        return np.sort(rng.choice(pool, pool.size * 3 // 10, replace=False)).astype(np.uint32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["importance", "rows", "one_expert"])
+def test_masked_dw_clustered_lists(capi, kind):
+    """The masked gradient on lists far from uniform: the tiles follow the
+    entry counts, so heavy rows and experts are split and empty ones skipped."""
+    dims = (256, 2048, 4, 2, 256)
+    say(f"masked dW clustered list {kind} dims={dims}")
+    d = synth.moe_layer(*dims, bf16=True, seeds=(120, 121, 122, 123, 124))
+    gd = oracle_layer(d, dims, 1, np.zeros(1, np.uint32))["gd"]
+    idx = skewed_mask(kind, dims, gd)
+    lay, _ = run_layer(capi, d, dims, 1, idx, dense=False)
+    got = npf(lay.dW)
+    want = gd[idx.astype(np.int64)]
+    assert rel(got, want) <= TOL_BF16
+    assert int(lay.nonfinite.item()) == 0
+
+
+def test_kept_plan_equals_plan_per_call(capi):
+    """usaf_masked_backward with the plan usaf_masked_plan kept for the list
+    gives the same bits as with the plan rebuilt inside the call, also after
+    the list (and so the plan) changes."""
+    dims = (256, 2048, 4, 2, 256)
+    say(f"kept masked plan dims={dims}")
+    d = synth.moe_layer(*dims, bf16=True, seeds=(120, 121, 122, 123, 124))
+    N = 3 * 4 * 2048 * 256
+    for mask_seed in (3, 4):
+        idx = synth.random_mask(N, N // 100, mask_seed)
+        lay, _ = run_layer(capi, d, dims, 1, idx, dense=False)  # the layer keeps a plan
+        kept = lay.dW.clone()
+        capi.masked_backward(lay.shape, lay.X, lay.Wr, lay.W, lay.state, lay.dY, lay.idx,
+                             lay.idx.numel(), lay.dW, lay.dWr, None, None, lay.ws_bwd)
+        torch.cuda.synchronize()
+        assert torch.equal(kept, lay.dW)
+
+
 def test_repeat_runs_are_bit_identical(capi):
     say("determinism ragged_bf16")
     dims = (200, 128, 8, 2, 96)
