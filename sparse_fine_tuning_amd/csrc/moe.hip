@@ -640,17 +640,41 @@ __global__ __launch_bounds__(256) void masked_dw_kernel(
 // bf16 operands the fp32 sum is exact unless the exponents differ by more
 // than 15, and then b lies far below half an ulp of a, so rounding the fp32
 // sum to bf16 gives the correctly rounded sum either way.  Eight elements per
-// thread (16-byte bf16 / 2 x 16-byte fp32 accesses), scalar tail.
-template <class T>
+// thread: 16-byte vector accesses when every pointer is 16-byte aligned and
+// n is a multiple of 8 (kVec), element accesses otherwise.
+template <class T, bool kVec>
 __global__ __launch_bounds__(256) void residual_add_kernel(const T* __restrict__ a,
                                                            const T* __restrict__ b, T* __restrict__ out,
                                                            int64_t n) {
   const int64_t i0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
-  if (i0 + 8 <= n) {
+  if (i0 >= n) return;
+  if constexpr (kVec) {
+    constexpr int kU = 16 / sizeof(T);  // elements per 16-byte vector
 #pragma unroll
-    for (int j = 0; j < 8; ++j) Act<T>::st(out, i0 + j, Act<T>::ld(a, i0 + j) + Act<T>::ld(b, i0 + j));
+    for (int v = 0; v < 8 / kU; ++v) {
+      const uint4 x = *reinterpret_cast<const uint4*>(a + i0 + v * kU);
+      const uint4 y = *reinterpret_cast<const uint4*>(b + i0 + v * kU);
+      uint4 z;
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+        uint32_t zs[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = __uint_as_float(xs[q] << 16) + __uint_as_float(ys[q] << 16);
+          const float hi = __uint_as_float(xs[q] & 0xffff0000u) + __uint_as_float(ys[q] & 0xffff0000u);
+          zs[q] = uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+        }
+        z = make_uint4(zs[0], zs[1], zs[2], zs[3]);
+      } else {
+        z = make_uint4(__float_as_uint(__uint_as_float(x.x) + __uint_as_float(y.x)),
+                       __float_as_uint(__uint_as_float(x.y) + __uint_as_float(y.y)),
+                       __float_as_uint(__uint_as_float(x.z) + __uint_as_float(y.z)),
+                       __float_as_uint(__uint_as_float(x.w) + __uint_as_float(y.w)));
+      }
+      *reinterpret_cast<uint4*>(out + i0 + v * kU) = z;
+    }
   } else {
-    for (int64_t i = i0; i < n; ++i) Act<T>::st(out, i, Act<T>::ld(a, i) + Act<T>::ld(b, i));
+    for (int64_t i = i0; i < n && i < i0 + 8; ++i) Act<T>::st(out, i, Act<T>::ld(a, i) + Act<T>::ld(b, i));
   }
 }
 
@@ -946,14 +970,17 @@ extern "C" usaf_status usaf_residual_add(int32_t act, const void* a, const void*
   if (!a || !b || !out) return USAF_ERR_INVALID_ARG;
   const int64_t blocks = ceil_div(ceil_div(n, 8), 256);
   if (blocks >= (int64_t(1) << 31)) return USAF_ERR_UNSUPPORTED;
-  if (act == USAF_BF16)
-    hipLaunchKernelGGL(residual_add_kernel<bf16_t>, dim3(unsigned(blocks)), dim3(256), 0, stream,
-                       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b),
-                       static_cast<bf16_t*>(out), n);
-  else
-    hipLaunchKernelGGL(residual_add_kernel<float>, dim3(unsigned(blocks)), dim3(256), 0, stream,
-                       static_cast<const float*>(a), static_cast<const float*>(b),
-                       static_cast<float*>(out), n);
+  const bool vec = n % 8 == 0 && ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
+                                    reinterpret_cast<uintptr_t>(out)) & 15) == 0;
+  if (act == USAF_BF16) {
+    auto* k = vec ? residual_add_kernel<bf16_t, true> : residual_add_kernel<bf16_t, false>;
+    hipLaunchKernelGGL(k, dim3(unsigned(blocks)), dim3(256), 0, stream, static_cast<const bf16_t*>(a),
+                       static_cast<const bf16_t*>(b), static_cast<bf16_t*>(out), n);
+  } else {
+    auto* k = vec ? residual_add_kernel<float, true> : residual_add_kernel<float, false>;
+    hipLaunchKernelGGL(k, dim3(unsigned(blocks)), dim3(256), 0, stream, static_cast<const float*>(a),
+                       static_cast<const float*>(b), static_cast<float*>(out), n);
+  }
   USAF_LAUNCH_CHECK();
   return USAF_OK;
 }

@@ -53,9 +53,11 @@ def to_dev(x, dtype):
 # the residual stream
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("act", [0, 1])
-@pytest.mark.parametrize("n", [0, 5, 1000003])
-def test_residual_add_bit_exact(capi, act, n):
-    say(f"residual_add act={act} n={n}")
+@pytest.mark.parametrize("n,shift", [(0, 0), (5, 0), (1000003, 0), (1 << 20, 0), (1 << 20, 1)])
+def test_residual_add_bit_exact(capi, act, n, shift):
+    """Vector path (n a multiple of 8, 16-byte aligned) and element path
+    (ragged n, or operands one element off alignment)."""
+    say(f"residual_add act={act} n={n} shift={shift}")
     dt = torch.bfloat16 if act == capi.BF16 else torch.float32
     R = O.Rounding(O.BF16 if act == capi.BF16 else O.F32, O.CONTRACT)
     rng = np.random.default_rng(n + 3)
@@ -63,8 +65,9 @@ def test_residual_add_bit_exact(capi, act, n):
     # round, and some are dominated entirely by one side
     a = R.act(rng.standard_normal(n) * 2.0 ** rng.integers(-30, 10, n))
     b = R.act(rng.standard_normal(n) * 2.0 ** rng.integers(-30, 10, n))
-    ta, tb = to_dev(a, dt), to_dev(b, dt)
-    out = torch.empty(n, dtype=dt, device=DEV)
+    ta = to_dev(np.concatenate([np.zeros(shift), a]), dt)[shift:]
+    tb = to_dev(np.concatenate([np.zeros(shift), b]), dt)[shift:]
+    out = torch.empty(n + shift, dtype=dt, device=DEV)[shift:]
     capi.residual_add(act, ta, tb, out, n)
     want = O.residual_add(a, b, R)
     assert np.array_equal(npf(out), want)
