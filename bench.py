@@ -276,6 +276,83 @@ def mixtral_layer(capi, synth, layer_mod, steps, lr):
     return out
 
 
+def stack_run(capi, layers=48, steps=180, reselect_every=50, peak_lr=2e-4):
+    """The stacked workload: 48 Qwen3-shaped layers (T=4096 as 8 x 512
+    tokens, bf16 experts, fp32 routers and Adam state), a fresh batch every
+    step, the importance pass before step 0 and RigL (30%) before steps 50,
+    100 and 150, the README's cosine decay from LR_PEAK.  Weights come from
+    the workload's per-layer seeds and the batches from its per-step seeds,
+    drawn on the device (same distributions as the other workloads); all
+    batches are resident before the timed region.  Reports tokens/s over the
+    whole run and over the train steps alone, and the reselection costs."""
+    import torch
+    from sparse_fine_tuning_amd.stack import MoEStack, cosine_lr
+    dims = (4096, 2048, 128, 8, 768)
+    T, H, E, K, I = dims
+    dev = "cuda"
+    stk = MoEStack(layers, *dims, act=capi.BF16, device=dev)
+    N = stk.shape.N
+    k = (N * 5) // 1000
+    r = (k * 3) // 10
+    ngu = E * 2 * I * H
+    g = torch.Generator(device=dev)
+    log(f"stack: {layers} layers, drawing weights")
+    for l, lay in enumerate(stk.layers):
+        g.manual_seed(1000 * (l + 1) + 1)
+        lay.W[:ngu].copy_(torch.randn(ngu, generator=g, device=dev) * 0.02)
+        g.manual_seed(1000 * (l + 1) + 2)
+        lay.W[ngu:].copy_(torch.randn(N - ngu, generator=g, device=dev) * 0.02)
+        g.manual_seed(1000 * (l + 1) + 3)
+        lay.Wr.copy_(torch.randn(E, H, generator=g, device=dev) * 0.02)
+    batches = []
+    for t in range(steps):
+        g.manual_seed(100 + t)
+        X = torch.randn(T, H, generator=g, device=dev).to(torch.bfloat16)
+        g.manual_seed(10000 + t)
+        batches.append((X, torch.randn(T, H, generator=g, device=dev).to(torch.bfloat16)))
+    torch.cuda.synchronize()
+    log(f"stack: {steps} steps")
+    reselect_ms, turnover, novelty, losses = [], [], [], []
+    t0 = time.perf_counter()
+    for t in range(steps):
+        stk.set_batch(*batches[t])
+        if t % reselect_every == 0:
+            torch.cuda.synchronize()
+            r0 = time.perf_counter()
+            if t == 0:
+                stk.importance(k)
+            else:
+                st = stk.rigl(r)
+            torch.cuda.synchronize()
+            reselect_ms.append((time.perf_counter() - r0) * 1e3)
+            if t > 0:
+                st = st.cpu().numpy()
+                turnover.append(float(st[:, 1].mean()) / k)
+                novelty.append(float(st[:, 2].mean()) / k)
+        stk.train_step(cosine_lr(t, steps, peak_lr))
+        if t % 10 == 0 or t == steps - 1:
+            losses.append(float(stk.loss.item()))
+    torch.cuda.synchronize()
+    total_s = time.perf_counter() - t0
+    train_s = total_s - sum(reselect_ms) * 1e-3
+    res = dict(
+        workload=f"stack of {layers} Qwen3-30B-A3B-shaped MoE layers, {steps} steps",
+        layers=layers, steps=steps, tokens_per_step=T,
+        tokens_per_s_including_reselection=T * steps / total_s,
+        tokens_per_s_train_steps=T * steps / train_s,
+        ms_per_step_train=train_s * 1e3 / steps, total_s=total_s,
+        reselect_ms=reselect_ms, reselect_ms_per_layer=[m / layers for m in reselect_ms],
+        rigl_k=k, rigl_r=r, turnover_applied=turnover, turnover_topk_vs_old=novelty,
+        steps_taken=stk.t, skipped_steps=stk.skipped, loss_every_10_steps=losses,
+        lr="cosine from 2e-4 to 0 over the run")
+    log(f"stack: {res['tokens_per_s_including_reselection']:.0f} tokens/s with reselection, "
+        f"{res['tokens_per_s_train_steps']:.0f} without; {res['ms_per_step_train']:.2f} ms per step; "
+        f"reselect ms {[round(m, 1) for m in reselect_ms]}")
+    del stk, batches
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(d, idx, dims, sample_tokens):
     """The CPU oracle, as it stands, on one train step over a sample of the
     layer's tokens (same weights and mask); tokens/s."""
@@ -310,6 +387,9 @@ def main():
     ap.add_argument("--no-scan", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-mixtral", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--stack-only", action="store_true",
+                    help="only the 48-layer stacked workload (prints its JSON object)")
     ap.add_argument("--mixtral-only", action="store_true",
                     help="only the Mixtral-shaped layer leg (prints its JSON object)")
     ap.add_argument("--scan-only", action="store_true",
@@ -354,6 +434,9 @@ def main():
     lr = 1e-3
     if args.mixtral_only:
         print(json.dumps({"mixtral": mixtral_layer(capi, synth, layer_mod, 10, lr)}), flush=True)
+        return
+    if args.stack_only:
+        print(json.dumps({"stack": stack_run(capi)}), flush=True)
         return
     log("generating the seeded Qwen3-shaped layer")
     d = synth.moe_layer(*dims, bf16=True, seeds=(0, 1, 2, 3, 4))
@@ -424,6 +507,9 @@ def main():
     if not args.no_mixtral and not args.scan_only:
         log("mixtral-shaped layer")
         out["mixtral"] = mixtral_layer(capi, synth, layer_mod, 10, lr)
+    if not args.no_stack and not args.scan_only:
+        log("stacked workload")
+        out["stack"] = stack_run(capi)
     if not args.no_cpu:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
         out["cpu_baseline"] = cpu_baseline(d, idx, dims, args.cpu_tokens)
