@@ -388,6 +388,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-mixtral", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--stack-steps", type=int, default=180,
+                    help="steps of the stacked workload (reselection every 50)")
     ap.add_argument("--stack-only", action="store_true",
                     help="only the 48-layer stacked workload (prints its JSON object)")
     ap.add_argument("--mixtral-only", action="store_true",
@@ -436,7 +438,7 @@ def main():
         print(json.dumps({"mixtral": mixtral_layer(capi, synth, layer_mod, 10, lr)}), flush=True)
         return
     if args.stack_only:
-        print(json.dumps({"stack": stack_run(capi)}), flush=True)
+        print(json.dumps({"stack": stack_run(capi, steps=args.stack_steps)}), flush=True)
         return
     log("generating the seeded Qwen3-shaped layer")
     d = synth.moe_layer(*dims, bf16=True, seeds=(0, 1, 2, 3, 4))
@@ -509,7 +511,7 @@ def main():
         out["mixtral"] = mixtral_layer(capi, synth, layer_mod, 10, lr)
     if not args.no_stack and not args.scan_only:
         log("stacked workload")
-        out["stack"] = stack_run(capi)
+        out["stack"] = stack_run(capi, steps=args.stack_steps)
     if not args.no_cpu:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
         out["cpu_baseline"] = cpu_baseline(d, idx, dims, args.cpu_tokens)
