@@ -39,15 +39,16 @@ FP32_VEC_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, TFLOP/s
 FETCH_SCALE = 2.0   # a 1 GiB copy reads 524,300 KiB of FETCH_SIZE
 WRITE_SCALE = 1.0   # and 1,048,576 KiB of WRITE_SIZE
 # kernel class -> (fetch KiB, write KiB, sources hash); masked_dw and adam sum
-# the launches of one step (plan + two SDDMM launches; expert + router Adam)
+# the launches of one step (the two SDDMM launches, the plan being kept per
+# list; expert + router Adam)
 COUNTER_TRAFFIC = {
-    "router_gemm": (8847, 16384, "602634fc2a2e897c"),
-    "gate_up": (549330, 149286, "602634fc2a2e897c"),
-    "down": (249243, 263079, "602634fc2a2e897c"),
-    "da": (454863, 153460, "602634fc2a2e897c"),
-    "dx": (717044, 262820, "602634fc2a2e897c"),
-    "masked_dw": (176810, 13592, "d133da227a39acf8"),
-    "adam": (28637, 128691, "b67b67111d5b8531"),
+    "router_gemm": (8847, 16384, "b6d3d88e9a00f8ca"),
+    "gate_up": (554951, 149774, "b6d3d88e9a00f8ca"),
+    "down": (250550, 262195, "b6d3d88e9a00f8ca"),
+    "da": (448368, 140913, "b6d3d88e9a00f8ca"),
+    "dx": (652395, 262259, "b6d3d88e9a00f8ca"),
+    "masked_dw": (169609, 11804, "02e0356039740389"),
+    "adam": (28637, 128683, "a1e0c9fd5b07a9f0"),
 }
 KERNEL_SOURCES = {
     c: ("gemm_mfma.hpp", "gemm_v2.hpp", "lds_dma.hpp", "moe_mfma.hip", "common.hpp", "moe_internal.hpp")
