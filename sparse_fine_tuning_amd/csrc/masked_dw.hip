@@ -34,14 +34,25 @@ constexpr int kSlots = 8;        // slots per staged chunk
 constexpr int kThreads = 512;    // 8 waves per block
 constexpr int kMaxEnt = 24;      // entries per thread per pass (gate_up; down: kMaxEntDown)
 constexpr int kMaxEntDown = 16;  // down's fp32 rows leave fewer registers
-constexpr int kMaxRB = 1024;     // max rows per tile
-constexpr int kMaxCB = 2048;     // max columns per tile ((kMaxCB + kMaxRB + 8)/8 <= kThreads)
+constexpr int kMaxCB = 2048;     // max columns per tile
 template <bool kDown>
 constexpr int kEnt = kDown ? kMaxEntDown : kMaxEnt;  // entries per thread per pass
 template <bool kDown>
 constexpr int kCap = kThreads * kEnt<kDown>;          // entries of one tile: one pass of a block
 constexpr int kTokTab = 2048;    // slots per token-table window
-constexpr int kLsBytes = (kMaxRB + 8) * kSlots * 4;  // rows from r_lo rounded down to 8
+// staged chunks whose loads are in flight (register sets of the staging threads)
+constexpr int kPreGateUp = 2;
+constexpr int kPreDown = 2;
+template <bool kDown>
+constexpr int kPre = kDown ? kPreDown : kPreGateUp;
+// max rows per tile: what the row operand's two LDS buffers allow (bf16 for
+// gate_up, fp32 w*dY for down), staged from r_lo rounded down to 8
+template <bool kDown>
+constexpr int kMaxRows = kDown ? 1024 : 1536;
+template <bool kDown>
+constexpr int kLsBytes = (kMaxRows<kDown> + 8) * kSlots * (kDown ? 4 : 2);
+static_assert((kMaxCB + kMaxRows<false> + 16) / 8 <= kThreads &&
+              (kMaxCB + kMaxRows<true> + 16) / 8 <= kThreads, "one staging block per thread");
 constexpr int kRsBytes = kMaxCB * kSlots * 2;
 static_assert(kMaxCB <= kThreads * kMaxEntDown, "a single row fits a tile");
 
@@ -193,15 +204,19 @@ __device__ __forceinline__ void stage_store(int b, int nblk_r, const StageRegs& 
 
 // Tiles of one tensor.  Group g = (expert e, column tile ct), e-major; its
 // rows' entry counts come from the plan's segment starts (per group fewer
-// than 2^31 entries).  One wave per group walks the rows 64 at a time and
-// cuts greedily: row r joins the open tile [open_r, r) unless the tile would
-// then exceed RB rows or cap entries; then the open tile is closed (listed
-// if it holds entries) and r opens the next.  A single row never exceeds cap
-// (at most kMaxCB entries), so every tile is one pass of a block.  On a
-// uniform list the row limit decides and the tiles are the plain geometric
-// ones; clustered rows are cut into more, smaller tiles.  A group's tiles
-// are appended together at an atomically reserved position: the order of
-// the groups in the list changes no result, since every tile's entries are
+// than 2^31 entries).  The group is split into nt = max(ceil(R / RB),
+// ceil(n / cap)) tiles of about n / nt entries each (n: the group's
+// entries): one wave per group walks the rows 64 at a time and closes the
+// open tile [open_r, r) before row r when it holds RB rows, when row r would
+// take it past cap entries, or when the entries before r reach the next
+// multiple of n / nt and the rows from r on fit in the tiles still planned
+// (so that a row-limited split is not followed by a sliver).  A single row never exceeds cap (at most kMaxCB
+// entries), so every tile is one pass of a block.  Splitting at the
+// quantiles keeps the tiles of a group even however its entries cluster (an
+// importance-selected list puts hundreds of entries in a few rows and leaves
+// others empty) and gives a light expert a single tile.  A group's tiles are
+// appended together at an atomically reserved position: the order of the
+// groups in the list changes no result, since every tile's entries are
 // computed the same way by whichever block takes it.
 // Tile: x = e | ct << 16, y = r_lo | r_hi << 16.
 __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __restrict__ seg,
@@ -215,6 +230,21 @@ __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __res
   const uint32_t tx = uint32_t(e) | (uint32_t(ct) << 16);
   // segment of row r: q0 + r*nct; its entries: seg[q+1] - seg[q]
   const int64_t q0 = qbase + int64_t(e) * R * nct + ct;
+  int total;
+  if (nct == 1) {
+    total = int(seg[q0 + R] - seg[q0]);  // the group's rows are consecutive segments
+  } else {
+    int part = 0;
+    for (int r = lane; r < R; r += 64) {
+      const int64_t q = q0 + int64_t(r) * nct;
+      part += int(seg[q + 1] - seg[q]);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) part += __shfl_xor(part, d, 64);
+    total = part;
+  }
+  if (total == 0) return;  // uniform
+  const int nt = max(int((R + RB - 1) / RB), int((int64_t(total) + cap - 1) / cap));
   // two walks over the rows: the first counts the group's tiles and
   // reserves them at once (a group's tiles stay consecutive in the list), the
   // second writes them; each walk loads the counts of 16 chunks of 64 rows at
@@ -225,6 +255,7 @@ __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __res
     int open_r = 0, open_x = 0;  // first row of the open tile, its exclusive prefix
     int carry = 0;               // exclusive prefix of the chunk's first row
     int n = 0;                   // tiles with entries so far
+    int ncut = 0;                // cuts so far
     for (int s0 = 0; s0 < R; s0 += 64 * kSpan) {
       int cnts[kSpan];
 #pragma unroll
@@ -251,7 +282,13 @@ __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __res
         const int excl = carry + incl - cnt;
         // at most one cut per row, taken in row order
         while (true) {
-          const bool cut = r < R && r > open_r && (r - open_r >= RB || excl + cnt - open_x > cap);
+          // the first multiple of total / nt beyond the open tile's start;
+          // a cut there only once the rows after it fit the tiles left
+          const int64_t k = int64_t(open_x) * nt / total + 1;
+          const int64_t quant = (k * total + nt - 1) / nt;
+          const bool cut = r < R && r > open_r &&
+                           (r - open_r >= RB || excl + cnt - open_x > cap ||
+                            (int64_t(excl) >= quant && int64_t(R - r) <= int64_t(nt - ncut - 1) * RB));
           const uint64_t m = __ballot(cut);
           if (!m) break;
           const int c = __ffsll((long long)m) - 1;
@@ -264,6 +301,7 @@ __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __res
           }
           open_r = cr;
           open_x = cx;
+          ++ncut;
         }
         carry += __shfl(incl, 63, 64);
       }
@@ -273,7 +311,6 @@ __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __res
       ++n;
     }
     if (walk == 0) {
-      if (n == 0) return;  // uniform
       if (lane == 0) base = atomicAdd(ntiles, n);
       base = __shfl(base, 0, 64);
     }
@@ -286,10 +323,10 @@ __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __res
 template <bool kDown>
 __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A, const uint2* __restrict__ tiles,
                                                                   const int* __restrict__ ntiles) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds_l[2][kDown ? kLsBytes : kLsBytes / 2];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_l[2][kLsBytes<kDown>];
   __shared__ __attribute__((aligned(16))) unsigned char lds_r[2][kRsBytes];
-  __shared__ int rowpre[kMaxRB + 1];
-  __shared__ uint32_t rstart[kMaxRB];
+  __shared__ int rowpre[kMaxRows<kDown> + 1];
+  __shared__ uint32_t rstart[kMaxRows<kDown>];
   __shared__ int tok_tab[kTokTab];
   __shared__ float w_tab[kDown ? kTokTab : 1];
 
@@ -341,100 +378,143 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
   const int nblk_r = (ncol + 7) >> 3, nblk_l = (nr + shift + 7) >> 3;
 
   for (int q0 = 0, per = 0; q0 < nent; q0 += kThreads * per) {
-    // this pass: per entries for every thread (spread evenly, at most
-    // kE), thread tid taking q0 + tid*per + i
+    // this pass: per entries for every thread (spread evenly, at most kE).
+    // Wave w takes the 64*per entries from q0 + 64*per*w, lane-interleaved:
+    // lane l's i-th entry is that base + 64 i + l, so the lanes of a wave
+    // read neighbouring entries at once (mostly one row: one broadcast LDS
+    // read of the row operand; coalesced list loads and gradient stores).
     per = min(kE, (nent - q0 + kThreads - 1) / kThreads);
-    uint32_t coord[kE];  // (row - r_lo) << 16 | (col - c0), or ~0 when unused
+    uint32_t offs[kE];  // LDS byte offsets of the entry's row (high half) and column (low half)
+    uint32_t opos[kE];  // list position of the entry, ~0 when unused
     float acc[kE];
     {
-      const int q = q0 + tid * per;
-      // row of entry q: last r with rowpre[r] <= q
-      int lo = 0, hi = nr;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (rowpre[mid] <= q) lo = mid; else hi = mid - 1;
-      }
-      // rows (kept in the coordinate words) and list positions from LDS
-      // first, then every list load at once (independent registers), then
-      // the columns
-      int r = lo;
-      uint32_t pos[kE];
-#pragma unroll
-      for (int i = 0; i < kE; ++i) {
-        const int qi = q + i;
-        coord[i] = 0xffffffffu;
-        pos[i] = rstart[0];
-        if (i < per && qi < nent) {
-          while (rowpre[r + 1] <= qi) ++r;
-          coord[i] = uint32_t(r) << 16;
-          pos[i] = rstart[r] + uint32_t(qi - rowpre[r]);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kE; ++i) pos[i] = A.idx[pos[i]];
+      const int qw = q0 + (tid >> 6) * 64 * per + lane;
+      uint32_t rows[kE], val[kE];
       const int64_t rb0 = A.base + (int64_t(e) * A.R + r_lo) * A.C + c0;
+      if (A.nct == 1) {
+        // one column tile: the tile's rows are one run of the list from
+        // rstart[0], and an entry's row follows from its flat index
+        // (offset x < nr*C < 2^24 from the tile's first row; the float
+        // quotient is off by at most one and corrected exactly)
+#pragma unroll
+        for (int i = 0; i < kE; ++i) {
+          const int qi = qw + 64 * i;
+          const bool used = i < per && qi < nent;
+          opos[i] = used ? rstart[0] + uint32_t(qi) : 0xffffffffu;
+          val[i] = used ? opos[i] : rstart[0];
+        }
+#pragma unroll
+        for (int i = 0; i < kE; ++i) val[i] = A.idx[val[i]];
+        const uint32_t C = uint32_t(A.C);
+        const float invC = 1.0f / float(A.C);
+#pragma unroll
+        for (int i = 0; i < kE; ++i) {
+          const uint32_t x = opos[i] != 0xffffffffu ? uint32_t(int64_t(val[i]) - rb0) : 0u;
+          uint32_t rr = uint32_t(float(x) * invC);
+          if (rr * C > x) --rr; else if ((rr + 1) * C <= x) ++rr;
+          rows[i] = rr;
+        }
+      } else {
+        // rows by binary search over the row prefix (the lane's entries
+        // ascend, so each search starts at the previous row), list
+        // positions, then every list load at once
+        int r = 0;
+#pragma unroll
+        for (int i = 0; i < kE; ++i) {
+          const int qi = qw + 64 * i;
+          opos[i] = 0xffffffffu;
+          rows[i] = 0;
+          val[i] = rstart[0];
+          if (i < per && qi < nent) {
+            int hi = nr - 1;
+            while (r < hi) {  // last row with rowpre <= qi
+              const int mid = (r + hi + 1) >> 1;
+              if (rowpre[mid] <= qi) r = mid; else hi = mid - 1;
+            }
+            rows[i] = uint32_t(r);
+            opos[i] = rstart[r] + uint32_t(qi - rowpre[r]);
+            val[i] = opos[i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < kE; ++i) val[i] = A.idx[val[i]];
+      }
 #pragma unroll
       for (int i = 0; i < kE; ++i) {
         acc[i] = 0.f;
-        if (coord[i] != 0xffffffffu) {
-          const int ri = int(coord[i] >> 16);
-          coord[i] |= uint32_t(int64_t(pos[i]) - (rb0 + int64_t(ri) * A.C));
+        offs[i] = 0;  // unused: row 0, column 0
+        if (opos[i] != 0xffffffffu) {
+          const uint32_t col = uint32_t(int64_t(val[i]) - (rb0 + int64_t(rows[i]) * A.C));
+          const uint32_t lrow = rows[i] + uint32_t(shift);
+          const uint32_t loff = kDown ? sw32(lrow) * 32 : sw16(lrow) * 16;
+          offs[i] = (loff << 16) | (sw16(col) * 16);
         }
       }
     }
     // Products over one staged chunk, entries in branch-free groups (4, or 2
-    // for down): the LDS reads of a group (an unused entry reads row 0 and
-    // column 0) are all issued before its products.
-    auto compute = [&](const unsigned char* Ls, const unsigned char* Rs) {
-      constexpr int kG = kDown ? 2 : 4;  // entries per group (down rows are 32-byte fp32)
-      static_for<kE / kG>([&](auto G_) {
-        constexpr int g0 = kG * decltype(G_)::value;
-        if (g0 >= per) return;
-        uint32_t lr[kG], lc[kG];
+    // for down; an unused entry reads row 0 and column 0).  The LDS reads of
+    // group g+1 are issued before the products of group g and no further
+    // ahead (a scheduling barrier after each group), which keeps the
+    // operands of two groups in registers.
+    constexpr int kG = kDown ? 2 : 4;  // entries per group (down rows are 32-byte fp32)
+    constexpr int kNG = kE / kG;
+    struct Ops {
+      uint4 rv[kG];
+      uint4 l0[kG];  // gate_up: 8 bf16 slots; down: slots 0-3 as fp32
+      uint4 l1[kG];  // down: slots 4-7
+    };
+    auto load_group = [&](auto G_, const unsigned char* Ls, const unsigned char* Rs, Ops& o) {
+      constexpr int g0 = kG * decltype(G_)::value;
 #pragma unroll
-        for (int k = 0; k < kG; ++k) {
-          const uint32_t cd = coord[g0 + k];
-          lr[k] = cd == 0xffffffffu ? 0u : (cd >> 16) + uint32_t(shift);
-          lc[k] = cd == 0xffffffffu ? 0u : cd & 0xffffu;
-        }
-        uint4 rv[kG];
-#pragma unroll
-        for (int k = 0; k < kG; ++k) rv[k] = *reinterpret_cast<const uint4*>(Rs + size_t(sw16(lc[k])) * 16);
+      for (int k = 0; k < kG; ++k) {
+        const uint32_t lo = offs[g0 + k] >> 16, ro = offs[g0 + k] & 0xffffu;
+        o.rv[k] = *reinterpret_cast<const uint4*>(Rs + ro);
         if constexpr (kDown) {
-          float4 lx[kG], ly[kG];
-#pragma unroll
-          for (int k = 0; k < kG; ++k) {
-            const float4* src = reinterpret_cast<const float4*>(Ls + size_t(sw32(lr[k])) * 32);
-            lx[k] = src[0];
-            ly[k] = src[1];
-          }
-#pragma unroll
-          for (int k = 0; k < kG; ++k) {
-            float a = acc[g0 + k];
-            a = fmaf(lx[k].x, bflo(rv[k].x), a); a = fmaf(lx[k].y, bfhi(rv[k].x), a);
-            a = fmaf(lx[k].z, bflo(rv[k].y), a); a = fmaf(lx[k].w, bfhi(rv[k].y), a);
-            a = fmaf(ly[k].x, bflo(rv[k].z), a); a = fmaf(ly[k].y, bfhi(rv[k].z), a);
-            a = fmaf(ly[k].z, bflo(rv[k].w), a); a = fmaf(ly[k].w, bfhi(rv[k].w), a);
-            acc[g0 + k] = a;
-          }
+          const uint4* src = reinterpret_cast<const uint4*>(Ls + lo);
+          o.l0[k] = src[0];
+          o.l1[k] = src[1];
         } else {
-          uint4 lb[kG];
-#pragma unroll
-          for (int k = 0; k < kG; ++k) lb[k] = *reinterpret_cast<const uint4*>(Ls + size_t(sw16(lr[k])) * 16);
-#pragma unroll
-          for (int k = 0; k < kG; ++k) {
-            float a = acc[g0 + k];
-            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb[k].x),
-                                                __builtin_bit_cast(bf16x2_t, rv[k].x), a, false);
-            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb[k].y),
-                                                __builtin_bit_cast(bf16x2_t, rv[k].y), a, false);
-            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb[k].z),
-                                                __builtin_bit_cast(bf16x2_t, rv[k].z), a, false);
-            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb[k].w),
-                                                __builtin_bit_cast(bf16x2_t, rv[k].w), a, false);
-            acc[g0 + k] = a;
-          }
+          o.l0[k] = *reinterpret_cast<const uint4*>(Ls + lo);
         }
+      }
+    };
+    auto math_group = [&](auto G_, const Ops& o) {
+      constexpr int g0 = kG * decltype(G_)::value;
+#pragma unroll
+      for (int k = 0; k < kG; ++k) {
+        float a = acc[g0 + k];
+        const uint4 rv = o.rv[k];
+        if constexpr (kDown) {
+          const uint4 lx = o.l0[k], ly = o.l1[k];
+          a = fmaf(__uint_as_float(lx.x), bflo(rv.x), a); a = fmaf(__uint_as_float(lx.y), bfhi(rv.x), a);
+          a = fmaf(__uint_as_float(lx.z), bflo(rv.y), a); a = fmaf(__uint_as_float(lx.w), bfhi(rv.y), a);
+          a = fmaf(__uint_as_float(ly.x), bflo(rv.z), a); a = fmaf(__uint_as_float(ly.y), bfhi(rv.z), a);
+          a = fmaf(__uint_as_float(ly.z), bflo(rv.w), a); a = fmaf(__uint_as_float(ly.w), bfhi(rv.w), a);
+        } else {
+          const uint4 lb = o.l0[k];
+          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb.x),
+                                              __builtin_bit_cast(bf16x2_t, rv.x), a, false);
+          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb.y),
+                                              __builtin_bit_cast(bf16x2_t, rv.y), a, false);
+          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb.z),
+                                              __builtin_bit_cast(bf16x2_t, rv.z), a, false);
+          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb.w),
+                                              __builtin_bit_cast(bf16x2_t, rv.w), a, false);
+        }
+        acc[g0 + k] = a;
+      }
+    };
+    auto compute = [&](const unsigned char* Ls, const unsigned char* Rs) {
+      Ops o[2];
+      load_group(std::integral_constant<int, 0>{}, Ls, Rs, o[0]);  // per >= 1
+      static_for<kNG>([&](auto G_) {
+        constexpr int g = decltype(G_)::value;
+        if (kG * g >= per) return;
+        if constexpr (g + 1 < kNG) {
+          if (kG * (g + 1) < per) load_group(std::integral_constant<int, g + 1>{}, Ls, Rs, o[(g + 1) & 1]);
+        }
+        math_group(G_, o[g & 1]);
+        __builtin_amdgcn_sched_barrier(0);
       });
     };
     // stream the expert's slots, a token-table window at a time
@@ -449,38 +529,48 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
       }
       __syncthreads();
       const int nch = (wn + kSlots - 1) / kSlots;
-      // chunk c is multiplied from buffer c & 1; while it is, the staging
-      // threads write chunk c+1 (loaded during chunk c-1) into the other
-      // buffer and load chunk c+2
-      StageRegs sr;
+      // chunk c is multiplied from buffer c & 1.  The staging threads hold
+      // the loads of kPre chunks in registers (chunk m in set m % kPre):
+      // while chunk c is multiplied they write chunk c+1 into the other
+      // buffer and reuse its registers to load chunk c+1+kPre, so every
+      // load has kPre chunk steps to arrive
+      constexpr int kP = kPre<kDown>;
+      StageRegs sr[kP];
       if (stager) {
-        stage_fetch<kDown>(A, tid, nblk_r, 0, wn, off + w0, r_al, c0, tok_tab, w_tab, sr);
-        stage_store<kDown>(tid, nblk_r, sr, lds_l[0], lds_r[0]);
-        if (nch > 1) stage_fetch<kDown>(A, tid, nblk_r, kSlots, wn, off + w0, r_al, c0, tok_tab, w_tab, sr);
+        stage_fetch<kDown>(A, tid, nblk_r, 0, wn, off + w0, r_al, c0, tok_tab, w_tab, sr[0]);
+        stage_store<kDown>(tid, nblk_r, sr[0], lds_l[0], lds_r[0]);
+        static_for<kP>([&](auto J) {
+          constexpr int m = decltype(J)::value + 1;
+          if (m < nch)
+            stage_fetch<kDown>(A, tid, nblk_r, m * kSlots, wn, off + w0, r_al, c0, tok_tab, w_tab,
+                               sr[m % kP]);
+        });
       }
-      for (int c = 0; c < nch; ++c) {
-        __syncthreads();  // buffer c & 1 written; buffer (c+1) & 1 no longer read
-        if (stager && c + 1 < nch) {
-          stage_store<kDown>(tid, nblk_r, sr, lds_l[(c + 1) & 1], lds_r[(c + 1) & 1]);
-          if (c + 2 < nch)
-            stage_fetch<kDown>(A, tid, nblk_r, (c + 2) * kSlots, wn, off + w0, r_al, c0, tok_tab,
-                               w_tab, sr);
-        }
-        compute(lds_l[c & 1], lds_r[c & 1]);
+      for (int cb = 0; cb < nch; cb += kP) {
+        static_for<kP>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          constexpr int s = (j + 1) % kP;  // set of chunk c + 1 (cb is a multiple of kP)
+          const int c = cb + j;
+          if (c >= nch) return;  // uniform
+          __syncthreads();  // buffer c & 1 written; buffer (c+1) & 1 no longer read
+          if (stager && c + 1 < nch) {
+            stage_store<kDown>(tid, nblk_r, sr[s], lds_l[(c + 1) & 1], lds_r[(c + 1) & 1]);
+            if (c + 1 + kP < nch)
+              stage_fetch<kDown>(A, tid, nblk_r, (c + 1 + kP) * kSlots, wn, off + w0, r_al, c0,
+                                 tok_tab, w_tab, sr[s]);
+          }
+          compute(lds_l[c & 1], lds_r[c & 1]);
+        });
       }
     }
     // write this thread's entries
     {
-      const int q = q0 + tid * per;
       int nbad = 0;
 #pragma unroll
       for (int i = 0; i < kE; ++i) {
-        const uint32_t cd = coord[i];
-        if (cd == 0xffffffffu) continue;
-        const int ri = int(cd >> 16);
-        const float v = acc[i];
-        A.dW[int64_t(rstart[ri]) + (q + i - rowpre[ri])] = v;
-        nbad += !finite_f(v);
+        if (opos[i] == 0xffffffffu) continue;
+        A.dW[opos[i]] = acc[i];
+        nbad += !finite_f(acc[i]);
       }
       if (A.nonfinite && nbad) atomicAdd(A.nonfinite, nbad);
     }
@@ -496,28 +586,17 @@ static void col_tiles(int C, int& CB, int& nct) {
   nct = int(ceil_div(C, CB));
 }
 
-// Row limit of the tiles: as few row tiles as the LDS staging allows (the
-// expert's slot stream is re-read once per tile), but enough that a tile of
-// the list's average density fills at most one pass; the tile builder cuts
-// where the local density is higher.  A multiple of 8.
-static int row_tile(int R, int CB, double density, int ent) {
-  const double per_row = double(CB) * (density > 0 ? density : 1e-9);
-  int64_t nrt = ceil_div(int64_t(R), int64_t(kMaxRB));
-  const int64_t by_entries = int64_t(std::ceil(double(R) * per_row / (double(ent) * kThreads)));
-  if (by_entries > nrt) nrt = by_entries;
-  const int64_t rb = ceil_div(ceil_div(int64_t(R), nrt), int64_t(8)) * 8;
-  return int(rb < R ? rb : R);
-}
-
 // Upper bound on the tiles of one tensor (R rows, C columns per expert)
-// holding at most nnz entries, for row limit RB >= 1: per group one tile per
-// RB rows plus one per entry cut; two consecutive entry-cut tiles hold more
-// than kCap entries together, so entry cuts number at most 2 nnz / kCap + 1
-// per group.
+// holding at most nnz entries, for row limit RB.  A group of n entries has
+// at most R/RB row cuts, 2n/cap + 1 entry cuts (two consecutive entry-cut
+// tiles hold more than cap entries together) and at most one quantile cut
+// per multiple of n/nt, nt <= ceil(R/RB) + ceil(n/cap) of them, so at most
+// 2 ceil(R/RB) + 3 ceil(n/cap) + 2 tiles; summed over the groups with
+// sum ceil(n/cap) <= nnz/cap + groups.
 static int64_t tile_bound(const usaf_moe_shape& s, int R, int C, int64_t nnz, int RB, int cap) {
   int CB, nct;
   col_tiles(C, CB, nct);
-  return int64_t(s.E) * nct * (2 + ceil_div(R, RB)) + ceil_div(2 * nnz, cap);
+  return int64_t(s.E) * nct * (2 * ceil_div(R, RB) + 5) + 3 * ceil_div(nnz, cap);
 }
 
 // Plan layout (bytes): segment starts [Q+1] u32 (256-aligned), two tile
@@ -541,15 +620,14 @@ static PlanLayout plan_layout(const usaf_moe_shape& s, int64_t nnz) {
   Lq.q1 = int64_t(s.E) * Lq.R0 * Lq.nct0;
   Lq.Q = Lq.q1 + int64_t(s.E) * Lq.R1 * Lq.nct1;
   const int64_t N = n_weights(s);
-  const double density = double(nnz) / double(N);
-  P.RB0 = row_tile(Lq.R0, Lq.CB0, density, kEnt<false>);
-  P.RB1 = row_tile(Lq.R1, Lq.CB1, density, kEnt<true>);
+  P.RB0 = std::min(Lq.R0, kMaxRows<false>);
+  P.RB1 = std::min(Lq.R1, kMaxRows<true>);
   P.b0 = tile_bound(s, Lq.R0, Lq.C0, std::min<int64_t>(nnz, Lq.ngu), P.RB0, kCap<false>);
   P.b1 = tile_bound(s, Lq.R1, Lq.C1, std::min<int64_t>(nnz, N - Lq.ngu), P.RB1, kCap<true>);
   P.counters = ((size_t(Lq.Q + 1) * 4 + 255) / 256) * 256;
   P.tiles0 = P.counters + 256;
-  P.tiles1 = P.tiles0 + 8 * size_t(tile_bound(s, Lq.R0, Lq.C0, Lq.ngu, 8, kCap<false>));
-  P.total = P.tiles1 + 8 * size_t(tile_bound(s, Lq.R1, Lq.C1, N - Lq.ngu, 8, kCap<true>));
+  P.tiles1 = P.tiles0 + 8 * size_t(tile_bound(s, Lq.R0, Lq.C0, Lq.ngu, P.RB0, kCap<false>));
+  P.total = P.tiles1 + 8 * size_t(tile_bound(s, Lq.R1, Lq.C1, N - Lq.ngu, P.RB1, kCap<true>));
   return P;
 }
 
