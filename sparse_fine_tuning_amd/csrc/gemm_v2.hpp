@@ -485,13 +485,10 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_persistent(P p)
     // 32-row blocks of this wave inside the tile's valid rows: a ragged
     // group's last tile issues MFMAs only for its valid row blocks
     const int vb = __builtin_amdgcn_readfirstlane(min(IM, max(0, (t.mc - wm * P::RW + 31) / 32)));
-    if constexpr (IM == 2) {
-      if (vb == 2) main_loop<P, 2, IM, NJ>(ao, bo, as, bs, lds, t.ke, nk, tid, w, wm, wn, lane, acc);
-      else if (vb == 1) main_loop<P, 1, IM, NJ>(ao, bo, as, bs, lds, t.ke, nk, tid, w, wm, wn, lane, acc);
-      else main_loop<P, 0, IM, NJ>(ao, bo, as, bs, lds, t.ke, nk, tid, w, wm, wn, lane, acc);
-    } else {
-      main_loop<P, IM, IM, NJ>(ao, bo, as, bs, lds, t.ke, nk, tid, w, wm, wn, lane, acc);
-    }
+    static_for<IM + 1>([&](auto V_) {
+      constexpr int v = decltype(V_)::value;
+      if (vb == v) main_loop<P, v, IM, NJ>(ao, bo, as, bs, lds, t.ke, nk, tid, w, wm, wn, lane, acc);
+    });
     __syncthreads();  // every wave is done with the ring
     MTile tn;
     L += G;

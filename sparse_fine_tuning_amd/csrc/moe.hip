@@ -29,9 +29,11 @@ __device__ __forceinline__ uint32_t logit_key(float v) {
 }
 
 // One wave per token: K rounds of a wave-wide max over (key, -expert id),
-// then softmax over the K chosen logits.  E <= 1024, K <= 64.
+// then softmax over the K chosen logits.  E <= 64 NV, K <= 64: lane l holds
+// experts l, l + 64, ... in NV registers.
 // With nparts > 1 the logits arrive as split-K partial sums [nparts][T][E];
 // they are added in fixed part order and the sums written to `logits`.
+template <int NV>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ parts,
                                                          int nparts, float* __restrict__ logits,
                                                          int T, int E, int K,
@@ -41,10 +43,10 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
   const float* lt = logits + int64_t(t) * E;
-  uint64_t comp[16];
-  float val[16];
+  uint64_t comp[NV];
+  float val[NV];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
     val[i] = 0.f;
     if (e < E) {
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   for (int j = 0; j < K; ++j) {
     uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) best = comp[i] > best ? comp[i] : best;
+    for (int i = 0; i < NV; ++i) best = comp[i] > best ? comp[i] : best;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       uint64_t o = __shfl_xor(best, off, 64);
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     // the owner lane (e % 64) retires the expert and broadcasts its logit
     float le = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < NV; ++i)
       if (lane + 64 * i == e) {
         comp[i] = 0;
         le = val[i];
@@ -149,6 +151,99 @@ __global__ __launch_bounds__(1024) void expert_sort_kernel(const int32_t* __rest
     base += total;
     __syncthreads();  // wcnt is rewritten next round
   }
+}
+
+// The same stable grouping in three launches of constant depth, for S >=
+// ceil(S / 1024) * E (the per-chunk counts borrow perm as scratch):
+//  1. chunk b of 1024 slots ranks each slot among the chunk's earlier slots
+//     of its expert (wave peers from one ballot per id bit, then the counts
+//     of the chunk's earlier waves) into slot_pos, and its per-expert counts
+//     into perm[b*E + e];
+//  2. every chunk derives the expert offsets and its own per-expert base
+//     from all chunks' counts, and turns its ranks into final positions;
+//  3. perm[slot_pos[s]] = s.
+constexpr int kSortChunk = 1024;
+__global__ __launch_bounds__(kSortChunk) void expert_rank_kernel(const int32_t* __restrict__ ids,
+                                                                 int S, int E, int nbits,
+                                                                 int32_t* __restrict__ cnt_out,
+                                                                 int32_t* __restrict__ rank) {
+  extern __shared__ int wc[];  // [16 waves][E]
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  for (int i = tid; i < 16 * E; i += kSortChunk) wc[i] = 0;
+  const int s = blockIdx.x * kSortChunk + tid;
+  const bool live = s < S;
+  const int id = live ? ids[s] : 0;
+  uint64_t peers = __ballot(live);
+  if (!live) peers = 0;
+  for (int b = 0; b < nbits; ++b) {
+    const uint64_t m = __ballot(live && ((id >> b) & 1));
+    peers &= ((id >> b) & 1) ? m : ~m;
+  }
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  const int rw = __popcll(peers & below);
+  __syncthreads();  // table zeroed
+  if (live && rw == 0) wc[wid * E + id] = __popcll(peers);
+  __syncthreads();
+  for (int e = tid; e < E; e += kSortChunk) {  // exclusive scan over the waves
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int c = wc[w * E + e];
+      wc[w * E + e] = run;
+      run += c;
+    }
+    cnt_out[int64_t(blockIdx.x) * E + e] = run;
+  }
+  __syncthreads();
+  if (live) rank[s] = wc[wid * E + id] + rw;
+}
+
+__global__ __launch_bounds__(kSortChunk) void expert_place_kernel(const int32_t* __restrict__ ids,
+                                                                  int S, int E, int nchunk,
+                                                                  const int32_t* __restrict__ cnt,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ slot_pos) {
+  extern __shared__ int base[];  // [E] then wave sums [16]
+  int* wsum = base + E;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // per expert: total over all chunks and the chunks before this one; the
+  // offsets are the exclusive scan of the totals over the experts, taken
+  // 1024 experts at a time (E <= 1024)
+  int total = 0, before = 0;
+  if (tid < E) {
+    for (int b = 0; b < nchunk; ++b) {
+      const int c = cnt[int64_t(b) * E + tid];
+      total += c;
+      before += b < int(blockIdx.x) ? c : 0;
+    }
+  }
+  int incl = total;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < wid; ++w) wbase += wsum[w];
+  const int off = wbase + incl - total;
+  if (tid < E) {
+    base[tid] = off + before;
+    if (blockIdx.x == 0) {
+      offsets[tid] = off;
+      if (tid == E - 1) offsets[E] = S;
+    }
+  }
+  __syncthreads();
+  const int s = blockIdx.x * kSortChunk + tid;
+  if (s < S) slot_pos[s] = base[ids[s]] + slot_pos[s];
+}
+
+__global__ __launch_bounds__(256) void expert_scatter_kernel(const int32_t* __restrict__ slot_pos,
+                                                             int S, int32_t* __restrict__ perm) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s < S) perm[slot_pos[s]] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -745,12 +840,38 @@ static usaf_status route_impl(const usaf_moe_shape& s, const float* parts, int n
                               const usaf_moe_state& st, hipStream_t stream) {
   const int S = s.T * s.K;
   timer_begin(USAF_K_ROUTE, stream);
-  hipLaunchKernelGGL(route_topk_kernel, dim3(unsigned(ceil_div(s.T, 4))), dim3(256), 0, stream,
-                     parts, nparts, nparts > 1 ? st.logits : const_cast<float*>(parts), s.T, s.E,
-                     s.K, st.topk_ids, st.topk_w);
+  const dim3 tg(unsigned(ceil_div(s.T, 4)));
+  float* lg = nparts > 1 ? st.logits : const_cast<float*>(parts);
+  const int nv = int(ceil_div(s.E, 64));
+  if (nv <= 1)
+    hipLaunchKernelGGL(route_topk_kernel<1>, tg, dim3(256), 0, stream, parts, nparts, lg, s.T, s.E, s.K, st.topk_ids, st.topk_w);
+  else if (nv <= 2)
+    hipLaunchKernelGGL(route_topk_kernel<2>, tg, dim3(256), 0, stream, parts, nparts, lg, s.T, s.E, s.K, st.topk_ids, st.topk_w);
+  else if (nv <= 4)
+    hipLaunchKernelGGL(route_topk_kernel<4>, tg, dim3(256), 0, stream, parts, nparts, lg, s.T, s.E, s.K, st.topk_ids, st.topk_w);
+  else if (nv <= 8)
+    hipLaunchKernelGGL(route_topk_kernel<8>, tg, dim3(256), 0, stream, parts, nparts, lg, s.T, s.E, s.K, st.topk_ids, st.topk_w);
+  else
+    hipLaunchKernelGGL(route_topk_kernel<16>, tg, dim3(256), 0, stream, parts, nparts, lg, s.T, s.E, s.K, st.topk_ids, st.topk_w);
   USAF_LAUNCH_CHECK();
-  hipLaunchKernelGGL(expert_sort_kernel, dim3(unsigned(s.E)), dim3(1024), 0, stream, st.topk_ids,
-                     S, s.E, st.offsets, st.perm, st.slot_pos);
+  const int nchunk = int(ceil_div(S, kSortChunk));
+  if (int64_t(nchunk) * s.E <= S) {
+    int nbits = 0;
+    while ((1 << nbits) < s.E) ++nbits;
+    hipLaunchKernelGGL(expert_rank_kernel, dim3(unsigned(nchunk)), dim3(kSortChunk),
+                       size_t(16) * s.E * sizeof(int), stream, st.topk_ids, S, s.E, nbits, st.perm,
+                       st.slot_pos);
+    USAF_LAUNCH_CHECK();
+    hipLaunchKernelGGL(expert_place_kernel, dim3(unsigned(nchunk)), dim3(kSortChunk),
+                       size_t(s.E + 16) * sizeof(int), stream, st.topk_ids, S, s.E, nchunk, st.perm,
+                       st.offsets, st.slot_pos);
+    USAF_LAUNCH_CHECK();
+    hipLaunchKernelGGL(expert_scatter_kernel, dim3(unsigned(ceil_div(S, 256))), dim3(256), 0, stream,
+                       st.slot_pos, S, st.perm);
+  } else {
+    hipLaunchKernelGGL(expert_sort_kernel, dim3(unsigned(s.E)), dim3(1024), 0, stream, st.topk_ids,
+                       S, s.E, st.offsets, st.perm, st.slot_pos);
+  }
   timer_end(USAF_K_ROUTE, stream);
   USAF_LAUNCH_CHECK();
   return USAF_OK;

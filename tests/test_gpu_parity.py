@@ -84,7 +84,9 @@ def route_state(T, E, K):
 
 
 @pytest.mark.parametrize("T,E,K,ties", [(300, 128, 8, False), (300, 128, 8, True),
-                                        (77, 8, 2, True), (50, 5, 5, False), (5, 1024, 64, True)])
+                                        (77, 8, 2, True), (50, 5, 5, False), (5, 1024, 64, True),
+                                        (4096, 128, 8, True), (2048, 1024, 8, False),
+                                        (100, 1, 1, False), (1500, 200, 3, True)])
 def test_route_exact_given_logits(capi, T, E, K, ties):
     say(f"route T={T} E={E} K={K} ties={ties}")
     rng = np.random.default_rng(T * E + K)
