@@ -617,7 +617,29 @@ __global__ __launch_bounds__(256) void dwr_kernel(const float* __restrict__ dl,
       dls[i] = dl[s];
     }
     __syncthreads();
-    if (h < H) {
+    if constexpr (std::is_same<T, bf16_t>::value) {
+      // both columns in one 4-byte load (h even, H a multiple of 64), 16
+      // slots' loads in flight; the same fma order as the generic loop
+      if (h < H) {
+        int i = 0;
+        for (; i + 16 <= wn; i += 16) {
+          uint32_t xv[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            xv[u] = *reinterpret_cast<const uint32_t*>(X + int64_t(tok[i + u]) * H + h);
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            a0 = fmaf(dls[i + u], __uint_as_float(xv[u] << 16), a0);
+            a1 = fmaf(dls[i + u], __uint_as_float(xv[u] & 0xffff0000u), a1);
+          }
+        }
+        for (; i < wn; ++i) {
+          const uint32_t xv = *reinterpret_cast<const uint32_t*>(X + int64_t(tok[i]) * H + h);
+          a0 = fmaf(dls[i], __uint_as_float(xv << 16), a0);
+          a1 = fmaf(dls[i], __uint_as_float(xv & 0xffff0000u), a1);
+        }
+      }
+    } else if (h < H) {
       int i = 0;
       for (; i + 4 <= wn; i += 4) {
         float x[8];
@@ -774,7 +796,8 @@ __global__ __launch_bounds__(256) void residual_add_kernel(const T* __restrict__
 }
 
 // Loss: per-block partial sums of (Y - tgt)^2 over 4096 elements, dY written.
-template <class T>
+// kVec: bf16 operands 16-byte aligned, accessed 8 elements at a time.
+template <class T, bool kVec>
 __global__ __launch_bounds__(256) void mse_partial_kernel(const T* __restrict__ Y,
                                                           const T* __restrict__ tgt, int64_t n,
                                                           float scale, T* __restrict__ dY,
@@ -783,13 +806,36 @@ __global__ __launch_bounds__(256) void mse_partial_kernel(const T* __restrict__ 
   const int tid = threadIdx.x;
   const int64_t base = int64_t(blockIdx.x) * 4096;
   float acc = 0.f;
+  if constexpr (kVec) {
+    // 8 elements per thread and step in 16-byte accesses (n is a multiple of 8)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int64_t i = base + r * 2048 + tid * 8;
+      if (i < n) {
+        const uint4 y = *reinterpret_cast<const uint4*>(Y + i);
+        const uint4 g = *reinterpret_cast<const uint4*>(tgt + i);
+        const uint32_t yw[4] = {y.x, y.y, y.z, y.w}, gw[4] = {g.x, g.y, g.z, g.w};
+        uint32_t ow[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float d0 = __uint_as_float(yw[q] << 16) - __uint_as_float(gw[q] << 16);
+          const float d1 = __uint_as_float(yw[q] & 0xffff0000u) - __uint_as_float(gw[q] & 0xffff0000u);
+          acc = fmaf(d0, d0, acc);
+          acc = fmaf(d1, d1, acc);
+          ow[q] = uint32_t(f2bf(scale * d0)) | (uint32_t(f2bf(scale * d1)) << 16);
+        }
+        *reinterpret_cast<uint4*>(dY + i) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      }
+    }
+  } else {
 #pragma unroll 4
-  for (int r = 0; r < 16; ++r) {
-    const int64_t i = base + r * 256 + tid;
-    if (i < n) {
-      const float d = Act<T>::ld(Y, i) - Act<T>::ld(tgt, i);
-      acc = fmaf(d, d, acc);
-      Act<T>::st(dY, i, scale * d);
+    for (int r = 0; r < 16; ++r) {
+      const int64_t i = base + r * 256 + tid;
+      if (i < n) {
+        const float d = Act<T>::ld(Y, i) - Act<T>::ld(tgt, i);
+        acc = fmaf(d, d, acc);
+        Act<T>::st(dY, i, scale * d);
+      }
     }
   }
 #pragma unroll
@@ -997,8 +1043,15 @@ static usaf_status mse_impl(const usaf_moe_shape& s, const T* Y, const T* tgt, T
   const int nb = int(ceil_div(n, 4096));
   float* part = reinterpret_cast<float*>(ws);
   timer_begin(USAF_K_MSE, stream);
-  hipLaunchKernelGGL(mse_partial_kernel<T>, dim3(unsigned(nb)), dim3(256), 0, stream, Y, tgt, n,
-                     float(2.0 / double(n)), dY, part);
+  const bool vec = std::is_same<T, bf16_t>::value && n % 8 == 0 &&
+                   ((reinterpret_cast<uintptr_t>(Y) | reinterpret_cast<uintptr_t>(tgt) |
+                     reinterpret_cast<uintptr_t>(dY)) & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL((mse_partial_kernel<T, std::is_same<T, bf16_t>::value>), dim3(unsigned(nb)), dim3(256), 0,
+                       stream, Y, tgt, n, float(2.0 / double(n)), dY, part);
+  else
+    hipLaunchKernelGGL((mse_partial_kernel<T, false>), dim3(unsigned(nb)), dim3(256), 0, stream, Y, tgt, n,
+                       float(2.0 / double(n)), dY, part);
   USAF_LAUNCH_CHECK();
   hipLaunchKernelGGL(mse_final_kernel, dim3(1), dim3(256), 0, stream, part, nb,
                      float(1.0 / double(n)), loss, nonfinite);

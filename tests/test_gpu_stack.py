@@ -50,6 +50,43 @@ def to_dev(x, dtype):
 
 
 # --------------------------------------------------------------------------
+# the loss gradient: 16-byte path and element path
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T,H", [(64, 192), (33, 64)])
+def test_mse_grad_vector_and_element_paths(capi, T, H):
+    """Aligned bf16 operands take the 16-byte path, operands one element off
+    alignment the element path; dY is the same element-wise arithmetic on
+    both (bit-identical), the loss differs only in summation order.  Both
+    against the oracle's loss and gradient."""
+    say(f"mse_grad T={T} H={H}")
+    n = T * H
+    Y = synth.to_bf16_values(synth.normal((T, H), 1.0, 900 + T))
+    tgt = synth.to_bf16_values(synth.normal((T, H), 1.0, 901 + T))
+    shape = capi.Shape(T, H, 4, 2, 32, capi.BF16)
+    ws = torch.empty(capi.workspace_size(capi.WS_FORWARD, shape), dtype=torch.uint8, device=DEV)
+    out = {}
+    for shift in (0, 1):
+        yb = torch.zeros(n + 8, dtype=torch.bfloat16, device=DEV)
+        tb = torch.zeros(n + 8, dtype=torch.bfloat16, device=DEV)
+        db = torch.zeros(n + 8, dtype=torch.bfloat16, device=DEV)
+        yb[shift:shift + n] = to_dev(Y, torch.bfloat16).reshape(-1)
+        tb[shift:shift + n] = to_dev(tgt, torch.bfloat16).reshape(-1)
+        loss = torch.zeros(1, dtype=torch.float32, device=DEV)
+        nf = torch.zeros(1, dtype=torch.int32, device=DEV)
+        capi.mse_grad(shape, yb[shift:], tb[shift:], db[shift:], loss, nf, ws)
+        torch.cuda.synchronize()
+        out[shift] = (float(loss.item()), db[shift:shift + n].clone(), int(nf.item()))
+    ref_loss, ref_dY = O.mse_loss_grad(Y, tgt, O.Rounding(O.BF16, O.CONTRACT))
+    assert np.array_equal(out[0][1].view(torch.int16).cpu().numpy(),
+                          out[1][1].view(torch.int16).cpu().numpy())
+    for shift in (0, 1):
+        lo, dY, nf = out[shift]
+        assert nf == 0
+        assert abs(lo - ref_loss) <= 1e-5 * ref_loss
+        assert rel(npf(dY).reshape(T, H), ref_dY) <= TOL_BF16
+
+
+# --------------------------------------------------------------------------
 # the residual stream
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("act", [0, 1])
