@@ -116,18 +116,22 @@ __device__ __forceinline__ float bflo(uint32_t w) { return __uint_as_float(w << 
 __device__ __forceinline__ float bfhi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Transpose 8 rows (slots) x 8 bf16 (one uint4 per slot) into 8 uint4 of
-// 8 slot values each (one per element).
+// 8 slot values each (one per element).  Output word d of element j pairs
+// element j of slots 2d (low half) and 2d+1 (high half); both sit in word
+// j/2 of their slot, in its low half for even j, high half for odd j.  One
+// byte permute per output word: v_perm_b32 indexes the bytes of {S0, S1}
+// with S1 as bytes 0-3 and S0 as bytes 4-7.
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int w) {
+  return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+}
 __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
     uint32_t w[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint4 a4 = in[2 * d], b4 = in[2 * d + 1];
-      const uint32_t a = (j < 2) ? a4.x : (j < 4) ? a4.y : (j < 6) ? a4.z : a4.w;
-      const uint32_t b = (j < 2) ? b4.x : (j < 4) ? b4.y : (j < 6) ? b4.z : b4.w;
-      w[d] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
+    for (int d = 0; d < 4; ++d)
+      w[d] = __builtin_amdgcn_perm(word_of(in[2 * d + 1], j >> 1), word_of(in[2 * d], j >> 1), sel);
     out[j] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
