@@ -32,13 +32,17 @@ __device__ __forceinline__ void static_for(F&& f) {
 // bf16 -> fp32 is exact: the bf16 bits are the fp32 word's upper half.
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return bf16_t(u >> 16);
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a NaN.  gfx950's
+// v_cvt_pk_bf16_f32 converts two values per instruction; on every finite
+// fp32 input (subnormals and infinities included) it gives the same bits as
+// adding 0x7fff plus the kept lsb to the word and truncating.
+typedef __bf16 hw_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float hw_f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+  const hw_f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, hw_bf16x2_t));
 }
+__device__ __forceinline__ bf16_t f2bf(float f) { return bf16_t(f2bf2(f, 0.f) & 0xffffu); }
 
 // Activation element access, fp32 or bf16 storage.
 template <class T> struct Act;

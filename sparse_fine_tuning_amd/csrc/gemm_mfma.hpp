@@ -44,9 +44,7 @@ struct MTile {
 //   k-contiguous:   int rows;  const E* row(int r) (row r's element 0), or
 //                   nullptr for rows past the end; int kend.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
-}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) { return f2bf2(lo, hi); }
 
 template <class E>
 struct KcLoader;

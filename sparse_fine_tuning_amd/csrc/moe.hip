@@ -527,8 +527,8 @@ __device__ __forceinline__ void store4<float>(float* p, int64_t i, float4 v) {
 }
 template <>
 __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, int64_t i, float4 v) {
-  *reinterpret_cast<uint2*>(p + i) = make_uint2(uint32_t(f2bf(v.x)) | (uint32_t(f2bf(v.y)) << 16),
-                                                uint32_t(f2bf(v.z)) | (uint32_t(f2bf(v.w)) << 16));
+  *reinterpret_cast<uint2*>(p + i) = make_uint2(f2bf2(v.x, v.y),
+                                                f2bf2(v.z, v.w));
 }
 
 // Y[t, :] = sum_{j=0..K-1} w[t, j] * y[slot t*K+j]   (fixed j order); four
@@ -779,7 +779,7 @@ __global__ __launch_bounds__(256) void residual_add_kernel(const T* __restrict__
         for (int q = 0; q < 4; ++q) {
           const float lo = __uint_as_float(xs[q] << 16) + __uint_as_float(ys[q] << 16);
           const float hi = __uint_as_float(xs[q] & 0xffff0000u) + __uint_as_float(ys[q] & 0xffff0000u);
-          zs[q] = uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+          zs[q] = f2bf2(lo, hi);
         }
         z = make_uint4(zs[0], zs[1], zs[2], zs[3]);
       } else {
@@ -822,7 +822,7 @@ __global__ __launch_bounds__(256) void mse_partial_kernel(const T* __restrict__ 
           const float d1 = __uint_as_float(yw[q] & 0xffff0000u) - __uint_as_float(gw[q] & 0xffff0000u);
           acc = fmaf(d0, d0, acc);
           acc = fmaf(d1, d1, acc);
-          ow[q] = uint32_t(f2bf(scale * d0)) | (uint32_t(f2bf(scale * d1)) << 16);
+          ow[q] = f2bf2(scale * d0, scale * d1);
         }
         *reinterpret_cast<uint4*>(dY + i) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
       }

@@ -146,12 +146,12 @@ struct MGateUp {
           uint32_t gw[2], uw[2], aw[2];
 #pragma unroll
           for (int e = 0; e < 4; e += 2) {
-            const float g0 = bf2f(f2bf(acc[i][2 * jp][4 * g + e]));
-            const float g1 = bf2f(f2bf(acc[i][2 * jp][4 * g + e + 1]));
-            const float u0 = bf2f(f2bf(acc[i][2 * jp + 1][4 * g + e]));
-            const float u1 = bf2f(f2bf(acc[i][2 * jp + 1][4 * g + e + 1]));
-            gw[e / 2] = pack_bf16x2(g0, g1);
-            uw[e / 2] = pack_bf16x2(u0, u1);
+            const uint32_t gp = pack_bf16x2(acc[i][2 * jp][4 * g + e], acc[i][2 * jp][4 * g + e + 1]);
+            const uint32_t up = pack_bf16x2(acc[i][2 * jp + 1][4 * g + e], acc[i][2 * jp + 1][4 * g + e + 1]);
+            const float g0 = __uint_as_float(gp << 16), g1 = __uint_as_float(gp & 0xffff0000u);
+            const float u0 = __uint_as_float(up << 16), u1 = __uint_as_float(up & 0xffff0000u);
+            gw[e / 2] = gp;
+            uw[e / 2] = up;
             aw[e / 2] = pack_bf16x2(silu_f(g0) * u0, silu_f(g1) * u1);
           }
           const int c = 32 * jp + 8 * g + 4 * h;

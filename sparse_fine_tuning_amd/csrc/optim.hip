@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void dequant_int4_kernel(const uint32_t* __res
       const int n0 = int((word >> (8 * j)) & 0xfu), n1 = int((word >> (8 * j + 4)) & 0xfu);
       const float v0 = float(n0 - ((n0 & 8) << 1)) * s;
       const float v1 = float(n1 - ((n1 & 8) << 1)) * s;
-      o[j] = uint32_t(f2bf(v0)) | (uint32_t(f2bf(v1)) << 16);
+      o[j] = f2bf2(v0, v1);
     }
     out[i] = make_uint4(o[0], o[1], o[2], o[3]);
   }
