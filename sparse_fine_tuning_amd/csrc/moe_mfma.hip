@@ -251,6 +251,23 @@ struct MDa {
       const int64_t p = t.off + t.m0 + (vrow ? row : 0);
       const float wt = topk_w[perm[p]];
       float part = 0.f;
+      // With 8 waves (two per SIMD) every saved g|u word of this row block
+      // is loaded before the first dGU store, which could otherwise alias
+      // them and serialise the loads (measured: 17% faster there, 4% slower
+      // with one wave per SIMD, where they are loaded next to their use).
+      constexpr bool kBatch = WM_ * WN_ >= 8;
+      uint2 gvs[NJ][4], uvs[NJ][4];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = out_col(CW, wn, j, g, lane);
+          gvs[j][g] = uvs[j][g] = make_uint2(0u, 0u);
+          if (!kBatch || !vrow || col >= t.nc) continue;
+          const int f = t.n0 + col;
+          gvs[j][g] = *reinterpret_cast<const uint2*>(gu + p * 2 * I + f);
+          uvs[j][g] = *reinterpret_cast<const uint2*>(gu + p * 2 * I + I + f);
+        }
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -260,8 +277,8 @@ struct MDa {
           const int f = t.n0 + col;
           // a = bf16(silu(g) u) is recomputed from the saved g|u exactly as the
           // forward epilogue rounded it, instead of being read back
-          const uint2 gv = *reinterpret_cast<const uint2*>(gu + p * 2 * I + f);
-          const uint2 uv = *reinterpret_cast<const uint2*>(gu + p * 2 * I + I + f);
+          const uint2 gv = kBatch ? gvs[j][g] : *reinterpret_cast<const uint2*>(gu + p * 2 * I + f);
+          const uint2 uv = kBatch ? uvs[j][g] : *reinterpret_cast<const uint2*>(gu + p * 2 * I + I + f);
           const uint32_t gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y};
           uint32_t dg[2], du[2];
 #pragma unroll
@@ -492,13 +509,14 @@ usaf_status mfma_router(const usaf_moe_shape& s, const bf16_t* X, const float* W
 constexpr int kFwdBM = 128, kFwdBN = 256, kFwdNS = 3;  // gate_up, down, dA, dX: 144 KiB LDS
 constexpr int kFwdWM = 2, kFwdWN = 4;                  // 8 waves: 2 per SIMD
 constexpr int kFwdBK = 64;                             // contraction depth of a stage
-constexpr int kDaWN = 2;                               // dA: 4 waves (its epilogue prefers them)
+constexpr int kDaWN = 4;                               // dA: 8 waves of 64 x 64
 constexpr int kDwBM = 256, kDwBN = 256, kDwNS = 2;     // dense dW: 128 KiB LDS
 
 // Groups of at least kBigRows rows on average (few large experts) take
 // 256-row tiles: twice the MFMA work per staged byte, and little ragged waste.
 constexpr int kBigRows = 512;
 constexpr int kBigBM = 256, kBigNS = 2;  // 2 x 64 KiB LDS stages, 8 waves of 128 x 64
+constexpr int kBigDaWN = 2;               // dA on 256-row tiles: 8 waves of 64 x 128
 static bool big_groups(const usaf_moe_shape& s) {
   return int64_t(s.T) * s.K >= int64_t(kBigRows) * s.E;
 }
@@ -527,7 +545,9 @@ usaf_status mfma_down(const usaf_moe_shape& s, const bf16_t* a, const bf16_t* Wd
   return launch_fwd<g2::MDown>(s, NT, st, USAF_K_DOWN, a, Wd, offsets, ybuf, s.H, s.E, s.I, NT);
 }
 
-int mfma_dw_partials(const usaf_moe_shape& s) { return kDaWN * int(ceil_div(s.I, kFwdBN)); }
+int mfma_dw_partials(const usaf_moe_shape& s) {
+  return (big_groups(s) ? kBigDaWN : kDaWN) * int(ceil_div(s.I, kFwdBN));
+}
 
 usaf_status mfma_da(const usaf_moe_shape& s, const bf16_t* dY, const bf16_t* Wd,
                     const int32_t* offsets, const int32_t* perm, const float* topk_w,
@@ -535,9 +555,9 @@ usaf_status mfma_da(const usaf_moe_shape& s, const bf16_t* dY, const bf16_t* Wd,
                     hipStream_t st) {
   const int NT = int(ceil_div(s.I, kFwdBN));
   if (big_groups(s))  // 8 waves of 64 x 128 on 256-row tiles
-    return launch_persistent(g2::MDa<kBigBM, kFwdBN, kBigNS, 4, kDaWN>{dY, Wd, offsets, perm, topk_w, gu,
-                                                                       a, dgu, dwpart, s.H, s.E, s.K,
-                                                                       s.I, NT, kDaWN * NT},
+    return launch_persistent(g2::MDa<kBigBM, kFwdBN, kBigNS, 4, kBigDaWN>{dY, Wd, offsets, perm, topk_w, gu,
+                                                                          a, dgu, dwpart, s.H, s.E, s.K,
+                                                                          s.I, NT, kBigDaWN * NT},
                              grouped_tiles_bound(s, NT, kBigBM), st, USAF_K_DA);
   return launch_persistent(g2::MDa<kFwdBM, kFwdBN, kFwdNS, 2, kDaWN, kFwdBK>{dY, Wd, offsets, perm, topk_w, gu, a, dgu, dwpart, s.H,
                                            s.E, s.K, s.I, NT, kDaWN * NT},
