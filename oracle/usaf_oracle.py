@@ -255,6 +255,10 @@ def moe_forward(X, Wr, W_gu, W_d, K: int, R: Rounding) -> dict:
     [g | u] = x W_gu^T, a = silu(g) * u, y = a W_d^T.  The layer output is
     Y[t] = sum_j w[t, j] * y[t*K + j], summed in the fixed order j = 0..K-1.
     Routing is dropless (no capacity limit).
+    Reading (rounding points): each slot's expert output y is a tensor of the
+    activation dtype, as the down projection of a bf16 model outputs bf16;
+    the weighted combine over the K slots is summed in higher precision and
+    rounded once.
 
     Arrays indexed by slot id s = t*K + j: gu [S, 2I], a [S, I].
     """
@@ -281,7 +285,7 @@ def moe_forward(X, Wr, W_gu, W_d, K: int, R: Rounding) -> dict:
         a_e = R.act(g * _sigmoid(g) * u)
         gu[slots] = gu_e
         a[slots] = a_e
-        y[slots] = a_e @ W_d[e].T
+        y[slots] = R.act(a_e @ W_d[e].T)
     y3 = y.reshape(T, K, H)
     Yacc = np.zeros((T, H))
     for j in range(K):
@@ -319,6 +323,10 @@ def moe_backward(fw: dict, X, Wr, W_gu, W_d, dY, R: Rounding) -> dict:
     dlogits[t, e_j] = w_j (dw_j - sum_m w_m dw_m); zero elsewhere.
     dWr = dlogits^T X (dense, fp32);  dX_r = dlogits Wr_used.
     dX[t] = sum_j W_gu[e_j]^T dGU_{t*K+j} + dX_r[t].
+    Reading (rounding points): each slot's input gradient W_gu^T dGU is a
+    tensor of the activation dtype (the gate_up projection's input gradient
+    in a bf16 model); the sum over the K slots and the router term is taken
+    in higher precision and rounded once.
     """
     X = np.asarray(X, dtype=np.float64)
     W_gu = np.asarray(W_gu, dtype=np.float64)
@@ -357,7 +365,7 @@ def moe_backward(fw: dict, X, Wr, W_gu, W_d, dY, R: Rounding) -> dict:
     for e in range(E):
         slots = perm[offsets[e]:offsets[e + 1]].astype(np.int64)
         if slots.size:
-            V[slots] = dgu[slots] @ W_gu[e]
+            V[slots] = R.act(dgu[slots] @ W_gu[e])
     V3 = V.reshape(T, K, H)
     dXacc = np.zeros((T, H))
     for j in range(K):

@@ -330,10 +330,10 @@ struct GateUpFwd {
   }
 };
 
-// down forward: ybuf[p, :] = a[p, :] * W_d[e]^T  (fp32, expert-major rows)
+// down forward: ybuf[p, :] = a[p, :] * W_d[e]^T  (activation dtype, expert-major rows)
 template <class T>
 struct DownFwd {
-  const T* a; const T* Wd; const int32_t* offsets; float* ybuf;
+  const T* a; const T* Wd; const int32_t* offsets; T* ybuf;
   int H, E, I;
   struct Tile { int e, m0, mc, n0, off; };
   __device__ bool get_tile(int bx, int by, int, Tile& t) const {
@@ -356,7 +356,7 @@ struct DownFwd {
       const int m = tm + 16 * i;
       if (m >= t.mc) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ybuf[int64_t(t.off + t.m0 + m) * H + t.n0 + tn + 16 * j] = acc[i][j];
+      for (int j = 0; j < 4; ++j) Act<T>::st(ybuf, int64_t(t.off + t.m0 + m) * H + t.n0 + tn + 16 * j, acc[i][j]);
     }
   }
 };
@@ -418,10 +418,10 @@ struct DaBwd {
   }
 };
 
-// dX backward: vbuf[p, :] = dGU[p, :] * W_gu[e]   (fp32, expert-major rows)
+// dX backward: vbuf[p, :] = dGU[p, :] * W_gu[e]   (activation dtype, expert-major rows)
 template <class T>
 struct DxBwd {
-  const T* dgu; const T* Wgu; const int32_t* offsets; float* vbuf;
+  const T* dgu; const T* Wgu; const int32_t* offsets; T* vbuf;
   int H, E, I;
   struct Tile { int e, m0, mc, n0, off; };
   __device__ bool get_tile(int bx, int by, int, Tile& t) const {
@@ -444,7 +444,7 @@ struct DxBwd {
       const int m = tm + 16 * i;
       if (m >= t.mc) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) vbuf[int64_t(t.off + t.m0 + m) * H + t.n0 + tn + 16 * j] = acc[i][j];
+      for (int j = 0; j < 4; ++j) Act<T>::st(vbuf, int64_t(t.off + t.m0 + m) * H + t.n0 + tn + 16 * j, acc[i][j]);
     }
   }
 };
@@ -531,14 +531,28 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, int64_t i, float4 v) {
                                                 f2bf2(v.z, v.w));
 }
 
+// Four consecutive elements (16 bytes fp32, 8 bytes bf16) as fp32.
+template <class T>
+__device__ __forceinline__ float4 load4(const T* p);
+template <>
+__device__ __forceinline__ float4 load4<float>(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+template <>
+__device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+}
+
 // Y[t, :] = sum_{j=0..K-1} w[t, j] * y[slot t*K+j]   (fixed j order); four
 // columns per thread (H % 64 == 0).
 template <class T>
-__global__ __launch_bounds__(256) void combine_y_kernel(const float* __restrict__ ybuf,
+__global__ __launch_bounds__(256) void combine_y_kernel(const T* __restrict__ ybuf,
                                                         const float* __restrict__ topk_w,
                                                         const int32_t* __restrict__ slot_pos, int H,
                                                         int K, T* __restrict__ Y) {
-  __shared__ const float* rows[64];
+  __shared__ const T* rows[64];
   __shared__ float wts[64];
   const int t = blockIdx.x;
   if (threadIdx.x < K) {
@@ -552,7 +566,7 @@ __global__ __launch_bounds__(256) void combine_y_kernel(const float* __restrict_
 #pragma unroll 8
     for (int j = 0; j < K; ++j) {
       const float wj = wts[j];
-      const float4 y = *reinterpret_cast<const float4*>(rows[j] + h);
+      const float4 y = load4<T>(rows[j] + h);
       acc.x = fmaf(wj, y.x, acc.x);
       acc.y = fmaf(wj, y.y, acc.y);
       acc.z = fmaf(wj, y.z, acc.z);
@@ -673,13 +687,13 @@ __global__ __launch_bounds__(256) void dwr_kernel(const float* __restrict__ dl,
 // dX[t, :] = sum_j v[slot t*K+j] + sum_j dlogits[t, j] * Wr'[e_j, :]; four
 // columns per thread.
 template <class T>
-__global__ __launch_bounds__(256) void combine_dx_kernel(const float* __restrict__ vbuf,
+__global__ __launch_bounds__(256) void combine_dx_kernel(const T* __restrict__ vbuf,
                                                          const float* __restrict__ dl,
                                                          const int32_t* __restrict__ ids,
                                                          const float* __restrict__ Wr,
                                                          const int32_t* __restrict__ slot_pos,
                                                          int H, int K, T* __restrict__ dX) {
-  __shared__ const float* vrows[64];
+  __shared__ const T* vrows[64];
   __shared__ const float* wrows[64];
   __shared__ float dls[64];
   const int t = blockIdx.x;
@@ -694,7 +708,7 @@ __global__ __launch_bounds__(256) void combine_dx_kernel(const float* __restrict
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 8
     for (int j = 0; j < K; ++j) {
-      const float4 v = *reinterpret_cast<const float4*>(vrows[j] + h);
+      const float4 v = load4<T>(vrows[j] + h);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
 #pragma unroll 8
@@ -927,7 +941,7 @@ template <class T>
 static usaf_status forward_impl(const usaf_moe_shape& s, const T* X, const float* Wr, const T* W,
                                 T* Y, const usaf_moe_state& st, char* ws, hipStream_t stream) {
   const WsForward L = ws_forward(s);
-  float* ybuf = reinterpret_cast<float*>(ws + L.ybuf);
+  T* ybuf = reinterpret_cast<T*>(ws + L.ybuf);
   const T* Wgu = W;
   const T* Wd = W + int64_t(s.E) * 2 * s.I * s.H;
   constexpr bool kMfma = std::is_same<T, bf16_t>::value;
@@ -970,7 +984,7 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
                                  int64_t nnz, const void* plan, float* dW, float* dWr, T* dX,
                                  int32_t* nonfinite, char* ws, hipStream_t stream) {
   const WsBackward L = ws_backward(s);
-  float* vbuf = reinterpret_cast<float*>(ws + L.vbuf);
+  T* vbuf = reinterpret_cast<T*>(ws + L.vbuf);
   float* dwpart = reinterpret_cast<float*>(ws + L.dwpart);
   float* dl = reinterpret_cast<float*>(ws + L.dl);
   constexpr bool kMfma = std::is_same<T, bf16_t>::value;

@@ -34,7 +34,8 @@ inline usaf_status check_shape(const usaf_moe_shape* s) {
   return USAF_OK;
 }
 
-// Forward workspace: fp32 expert outputs before the combine, [S, H].
+// Forward workspace: expert outputs before the combine, [S, H] in the
+// activation dtype (sized for fp32; also holds the router split-K partials).
 struct WsForward {
   size_t ybuf, total;
 };
@@ -50,7 +51,8 @@ inline WsForward ws_forward(const usaf_moe_shape& s) {
   return L;
 }
 
-// Backward workspace: fp32 dX contributions [S, H], partial dw sums
+// Backward workspace: dX contributions [S, H] (activation dtype, sized for
+// fp32), partial dw sums
 // [S, NT] (NT = dA column tiles), dlogits of the chosen experts [S], and
 // a masked-gradient plan built per call when the caller keeps none.
 struct WsBackward {
@@ -86,14 +88,14 @@ usaf_status mfma_gate_up(const usaf_moe_shape& s, const uint16_t* X, const uint1
                          const int32_t* offsets, const int32_t* perm, uint16_t* gu, uint16_t* a,
                          hipStream_t st);
 usaf_status mfma_down(const usaf_moe_shape& s, const uint16_t* a, const uint16_t* Wd,
-                      const int32_t* offsets, float* ybuf, hipStream_t st);
+                      const int32_t* offsets, uint16_t* ybuf, hipStream_t st);
 int mfma_dw_partials(const usaf_moe_shape& s);
 usaf_status mfma_da(const usaf_moe_shape& s, const uint16_t* dY, const uint16_t* Wd,
                     const int32_t* offsets, const int32_t* perm, const float* topk_w,
                     const uint16_t* gu, const uint16_t* a, uint16_t* dgu, float* dwpart,
                     hipStream_t st);
 usaf_status mfma_dx(const usaf_moe_shape& s, const uint16_t* dgu, const uint16_t* Wgu,
-                    const int32_t* offsets, float* vbuf, hipStream_t st);
+                    const int32_t* offsets, uint16_t* vbuf, hipStream_t st);
 // stage: S*H*2 bf16 scratch (the backward workspace's vbuf) for the
 // expert-major gathered X and w*dY operands.
 usaf_status mfma_dense_dw(const usaf_moe_shape& s, const uint16_t* X, const uint16_t* dY,

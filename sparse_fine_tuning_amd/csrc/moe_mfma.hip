@@ -191,7 +191,7 @@ struct MDown {
   static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
   using AOp = KMajor<BM, WM_ * WN_, BK_>;
   using BOp = KMajor<BN, WM_ * WN_, BK_>;
-  const bf16_t* a; const bf16_t* Wd; const int32_t* offsets; float* ybuf;
+  const bf16_t* a; const bf16_t* Wd; const int32_t* offsets; bf16_t* ybuf;
   int H, E, I, NT;
   __device__ __forceinline__ bool tile(int L, MTile& t) const {
     if (!grouped_tile<BM>(offsets, E, NT, L, t)) return false;
@@ -212,10 +212,11 @@ struct MDown {
       const int rb = wm * RW + 32 * i;
       if (rb >= t.mc) return;
       const int ncw = t.nc - wn * CW;
-      float* base = ybuf + int64_t(t.off + t.m0 + rb) * H + t.n0 + wn * CW;
+      bf16_t* base = ybuf + int64_t(t.off + t.m0 + rb) * H + t.n0 + wn * CW;
       const int64_t ld = H;
       stage_f32<NJ>(stage, acc[i], lane, [&](int row, int col, float4 v) {
-        if (rb + row < t.mc && col < ncw) *reinterpret_cast<float4*>(base + row * ld + col) = v;
+        if (rb + row < t.mc && col < ncw)
+          *reinterpret_cast<uint2*>(base + row * ld + col) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
       });
     });
   }
@@ -317,7 +318,7 @@ struct MDx {
   static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
   using AOp = KMajor<BM, WM_ * WN_, BK_>;
   using BOp = MNMajor<BN, WM_ * WN_, BK_>;
-  const bf16_t* dgu; const bf16_t* Wgu; const int32_t* offsets; float* vbuf;
+  const bf16_t* dgu; const bf16_t* Wgu; const int32_t* offsets; bf16_t* vbuf;
   int H, E, I, NT;
   __device__ __forceinline__ bool tile(int L, MTile& t) const {
     if (!grouped_tile<BM>(offsets, E, NT, L, t)) return false;
@@ -338,10 +339,11 @@ struct MDx {
       const int rb = wm * RW + 32 * i;
       if (rb >= t.mc) return;
       const int ncw = t.nc - wn * CW;
-      float* base = vbuf + int64_t(t.off + t.m0 + rb) * H + t.n0 + wn * CW;
+      bf16_t* base = vbuf + int64_t(t.off + t.m0 + rb) * H + t.n0 + wn * CW;
       const int64_t ld = H;
       stage_f32<NJ>(stage, acc[i], lane, [&](int row, int col, float4 v) {
-        if (rb + row < t.mc && col < ncw) *reinterpret_cast<float4*>(base + row * ld + col) = v;
+        if (rb + row < t.mc && col < ncw)
+          *reinterpret_cast<uint2*>(base + row * ld + col) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
       });
     });
   }
@@ -540,7 +542,7 @@ usaf_status mfma_gate_up(const usaf_moe_shape& s, const bf16_t* X, const bf16_t*
 }
 
 usaf_status mfma_down(const usaf_moe_shape& s, const bf16_t* a, const bf16_t* Wd,
-                      const int32_t* offsets, float* ybuf, hipStream_t st) {
+                      const int32_t* offsets, bf16_t* ybuf, hipStream_t st) {
   const int NT = int(ceil_div(s.H, kFwdBN));
   return launch_fwd<g2::MDown>(s, NT, st, USAF_K_DOWN, a, Wd, offsets, ybuf, s.H, s.E, s.I, NT);
 }
@@ -565,7 +567,7 @@ usaf_status mfma_da(const usaf_moe_shape& s, const bf16_t* dY, const bf16_t* Wd,
 }
 
 usaf_status mfma_dx(const usaf_moe_shape& s, const bf16_t* dgu, const bf16_t* Wgu,
-                    const int32_t* offsets, float* vbuf, hipStream_t st) {
+                    const int32_t* offsets, bf16_t* vbuf, hipStream_t st) {
   const int NT = int(ceil_div(s.H, kFwdBN));
   return launch_fwd<g2::MDx>(s, NT, st, USAF_K_DX, dgu, Wgu, offsets, vbuf, s.H, s.E, s.I, NT);
 }
