@@ -276,24 +276,32 @@ __device__ __forceinline__ void stage_f32(unsigned char* region, const f32x16_t 
   wave_lds_sync();
 }
 
-// bf16, NC columns per row (NC = 64: 128-byte rows): writer puts packed
-// (2 x bf16) words; reader calls st(row, col8, uint4) with 8 columns per
-// lane, 8 lanes per row.
+// One wave's block of 32 rows x NC bf16 columns (NC = 32 or 64) through a
+// region of LDS private to the wave: the writers put packed words (4 columns)
+// in the MFMA output layout; the block then leaves in 16-byte row pieces,
+// NC/8 lanes per row, so one store instruction covers 64*8/NC whole row
+// segments instead of 32 rows x 8 bytes.
 template <int NC>
-struct StageBf16 {
+struct WaveRows {
+  static_assert(NC == 32 || NC == 64, "16-byte pieces, at most 8 lanes per row");
   static constexpr int kPitch = NC * 2 + 16;
+  static constexpr int kBytes = 32 * kPitch;
+  static constexpr int kLanesPerRow = NC / 8, kRowsPerStore = 64 / kLanesPerRow;
   __device__ __forceinline__ static void put2(unsigned char* region, int row, int col, uint32_t w0,
                                               uint32_t w1) {
     *reinterpret_cast<uint2*>(region + row * kPitch + 2 * col) = make_uint2(w0, w1);
   }
+  // st(row, col8, uint4): 8 columns from col8 of row; every row of the block
   template <class St>
   __device__ __forceinline__ static void drain(unsigned char* region, int lane, St&& st) {
-    static_assert(NC == 64, "8 lanes of 16 bytes per row");
+    wave_lds_sync();  // the wave's puts have landed
+    const int lr = lane / kLanesPerRow, lc = lane % kLanesPerRow;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 8 * q + (lane >> 3);
-      st(row, 8 * (lane & 7), *reinterpret_cast<const uint4*>(region + row * kPitch + 16 * (lane & 7)));
+    for (int q = 0; q < 32 / kRowsPerStore; ++q) {
+      const int row = kRowsPerStore * q + lr;
+      st(row, 8 * lc, *reinterpret_cast<const uint4*>(region + row * kPitch + 16 * lc));
     }
+    wave_lds_sync();  // read back before the region is written again
   }
 };
 
@@ -453,6 +461,7 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_persistent(P p)
   constexpr int A_BYTES = AOp::kBytes, B_BYTES = BOp::kBytes;
   constexpr int NLOAD = AOp::kInst + BOp::kInst;
   static_assert((NS - 2) * NLOAD < 64, "vmcnt");
+  static_assert(P::kPStage * (P::NTHR / 64) <= A_BYTES + B_BYTES, "epilogue staging fits one ring stage");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[NS][A_BYTES + B_BYTES];
   const int G = gridDim.x;
   int L = xcd_remap_blocks(blockIdx.x, G);
@@ -506,7 +515,11 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_persistent(P p)
           bo.issue(bs, s, lds[s] + A_BYTES, w, lane);
         }
     }
-    p.epilogue(t, acc, wm, wn, lane, nullptr);
+    // the epilogue stages through ring stage NS-1, which the next tile's
+    // prologue leaves free (its first stage refills it only after a barrier
+    // every wave reaches after its epilogue)
+    unsigned char* pst = P::kPStage ? &lds[NS - 1][0] + w * P::kPStage : nullptr;
+    p.epilogue(t, acc, wm, wn, lane, pst);
     if (!more) break;
     t = tn;
   }

@@ -126,62 +126,102 @@ struct MGateUp {
   __device__ __forceinline__ GateUpRowsC<CW> b_src(const MTile& t) const {
     return GateUpRowsC<CW>{Wgu + int64_t(t.e) * 2 * I * H, t.n0, I, H};
   }
-  static constexpr int kStageBytes = 3 * 32 * StageBf16<64>::kPitch;
+  // persistent epilogue staging: one tensor's 32-row block (CW/2 features)
+  static constexpr int kPStage = WaveRows<CW / 2>::kBytes;
+  static constexpr int kStageBytes = kPStage;
   __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
                                            unsigned char* stage) const {
     static_assert(NJ % 2 == 0, "gate / up blocks of 32 features alternate");
-    unsigned char* sg = stage;
-    unsigned char* su = stage + 32 * StageBf16<64>::kPitch;
-    unsigned char* sa = stage + 2 * 32 * StageBf16<64>::kPitch;
     const int F = t.n0 + (CW / 2) * wn;  // first feature of this wave
     static_for<IM>([&](auto I_) {
       constexpr int i = decltype(I_)::value;
       const int rb = wm * RW + 32 * i;
       if (rb >= t.mc) return;
       const int r = lane & 31, h = lane >> 5;
+      // g, u (rounded once) and a = bf16(silu(g) u), as packed word pairs
+      uint32_t gw[NJ / 2][4][2], uw[NJ / 2][4][2], aw[NJ / 2][4][2];
 #pragma unroll
       for (int jp = 0; jp < NJ / 2; ++jp)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint32_t gw[2], uw[2], aw[2];
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
           for (int e = 0; e < 4; e += 2) {
             const uint32_t gp = pack_bf16x2(acc[i][2 * jp][4 * g + e], acc[i][2 * jp][4 * g + e + 1]);
             const uint32_t up = pack_bf16x2(acc[i][2 * jp + 1][4 * g + e], acc[i][2 * jp + 1][4 * g + e + 1]);
             const float g0 = __uint_as_float(gp << 16), g1 = __uint_as_float(gp & 0xffff0000u);
             const float u0 = __uint_as_float(up << 16), u1 = __uint_as_float(up & 0xffff0000u);
-            gw[e / 2] = gp;
-            uw[e / 2] = up;
-            aw[e / 2] = pack_bf16x2(silu_f(g0) * u0, silu_f(g1) * u1);
+            gw[jp][g][e / 2] = gp;
+            uw[jp][g][e / 2] = up;
+            aw[jp][g][e / 2] = pack_bf16x2(silu_f(g0) * u0, silu_f(g1) * u1);
           }
-          const int c = 32 * jp + 8 * g + 4 * h;
-          if (stage) {
-            StageBf16<64>::put2(sg, r, c, gw[0], gw[1]);
-            StageBf16<64>::put2(su, r, c, uw[0], uw[1]);
-            StageBf16<64>::put2(sa, r, c, aw[0], aw[1]);
-          } else if (rb + r < t.mc && F + c < I) {
-            const int64_t p = t.off + t.m0 + rb + r;
-            *reinterpret_cast<uint2*>(gu + p * 2 * I + F + c) = make_uint2(gw[0], gw[1]);
-            *reinterpret_cast<uint2*>(gu + p * 2 * I + I + F + c) = make_uint2(uw[0], uw[1]);
-            *reinterpret_cast<uint2*>(a + p * I + F + c) = make_uint2(aw[0], aw[1]);
-          }
-        }
-      if (!stage) return;
-      wave_lds_sync();
       const int64_t p0 = t.off + t.m0 + rb;
-      auto rows = [&](unsigned char* reg, bf16_t* base, int64_t ld, int coff) {
-        StageBf16<64>::drain(reg, lane, [&](int row, int c8, uint4 v) {
-          if (rb + row < t.mc && F + c8 < I)
-            *reinterpret_cast<uint4*>(base + (p0 + row) * ld + coff + F + c8) = v;
-        });
+      auto emit = [&](const uint32_t (&wv)[NJ / 2][4][2], bf16_t* base, int64_t ld, int coff) {
+        if (stage) {
+#pragma unroll
+          for (int jp = 0; jp < NJ / 2; ++jp)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              WaveRows<CW / 2>::put2(stage, r, 32 * jp + 8 * g + 4 * h, wv[jp][g][0], wv[jp][g][1]);
+          WaveRows<CW / 2>::drain(stage, lane, [&](int row, int c8, uint4 v) {
+            if (rb + row < t.mc && F + c8 < I)
+              *reinterpret_cast<uint4*>(base + (p0 + row) * ld + coff + F + c8) = v;
+          });
+        } else {
+#pragma unroll
+          for (int jp = 0; jp < NJ / 2; ++jp)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int c = 32 * jp + 8 * g + 4 * h;
+              if (rb + r < t.mc && F + c < I)
+                *reinterpret_cast<uint2*>(base + (p0 + r) * ld + coff + F + c) = make_uint2(wv[jp][g][0], wv[jp][g][1]);
+            }
+        }
       };
-      rows(sg, gu, 2 * I, 0);
-      rows(su, gu, 2 * I, I);
-      rows(sa, a, I, 0);
-      wave_lds_sync();
+      emit(gw, gu, 2 * I, 0);
+      emit(uw, gu, 2 * I, I);
+      emit(aw, a, I, 0);
     });
   }
 };
+
+// bf16 [32 rows x CW] blocks of a wave's accumulators to rows base + row*ld:
+// staged through the wave's LDS region (CW = 32 or 64), else 8-byte stores.
+template <int IM, int NJ, int CW, int RW>
+__device__ __forceinline__ void store_rows_bf16(const f32x16_t (&acc)[IM][NJ], unsigned char* stage, int wm,
+                                                int lane, int mc, int ncw, bf16_t* base0, int64_t ld) {
+  static_for<IM>([&](auto I_) {
+    constexpr int i = decltype(I_)::value;
+    const int rb = wm * RW + 32 * i;
+    if (rb >= mc) return;
+    bf16_t* base = base0 + int64_t(rb) * ld;
+    const int r = lane & 31, h = lane >> 5;
+    if constexpr (CW == 32 || CW == 64) {
+      if (stage) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            WaveRows<CW>::put2(stage, r, 32 * j + 8 * g + 4 * h,
+                               pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                               pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
+        WaveRows<CW>::drain(stage, lane, [&](int row, int c8, uint4 v) {
+          if (rb + row < mc && c8 < ncw) *reinterpret_cast<uint4*>(base + row * ld + c8) = v;
+        });
+        return;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = 32 * j + 8 * g + 4 * h;
+        if (rb + r < mc && c < ncw)
+          *reinterpret_cast<uint2*>(base + r * ld + c) =
+              make_uint2(pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                         pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
+      }
+  });
+}
 
 template <int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2, int BK_ = 64>
 struct MDown {
@@ -204,21 +244,12 @@ struct MDown {
   __device__ __forceinline__ PlainRowsC b_src(const MTile& t) const {
     return PlainRowsC{Wd + (int64_t(t.e) * H + t.n0) * I, I, t.nc};
   }
-  static constexpr int kStageBytes = 32 * (32 * NJ * 4 + 16);
+  static constexpr int kPStage = (CW == 32 || CW == 64) ? WaveRows<(CW == 32 ? 32 : 64)>::kBytes : 0;
+  static constexpr int kStageBytes = kPStage;
   __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
                                            unsigned char* stage) const {
-    static_for<IM>([&](auto I_) {
-      constexpr int i = decltype(I_)::value;
-      const int rb = wm * RW + 32 * i;
-      if (rb >= t.mc) return;
-      const int ncw = t.nc - wn * CW;
-      bf16_t* base = ybuf + int64_t(t.off + t.m0 + rb) * H + t.n0 + wn * CW;
-      const int64_t ld = H;
-      stage_f32<NJ>(stage, acc[i], lane, [&](int row, int col, float4 v) {
-        if (rb + row < t.mc && col < ncw)
-          *reinterpret_cast<uint2*>(base + row * ld + col) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-      });
-    });
+    store_rows_bf16<IM, NJ, CW, RW>(acc, stage, wm, lane, t.mc, t.nc - wn * CW,
+                                    ybuf + int64_t(t.off + t.m0) * H + t.n0 + wn * CW, H);
   }
 };
 
@@ -242,9 +273,10 @@ struct MDa {
   __device__ __forceinline__ StridedKC b_src(const MTile& t) const {
     return StridedKC{Wd + int64_t(t.e) * H * I + t.n0, I, t.nc};
   }
-  static constexpr int kStageBytes = 0;
+  static constexpr int kPStage = (CW == 32 || CW == 64) ? WaveRows<(CW == 32 ? 32 : 64)>::kBytes : 0;
+  static constexpr int kStageBytes = kPStage;
   __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
-                                           unsigned char*) const {
+                                           unsigned char* stage) const {
     static_for<IM>([&](auto I_) {
       constexpr int i = decltype(I_)::value;
       const int row = out_row(RW, wm, i, lane);
@@ -252,6 +284,11 @@ struct MDa {
       const int64_t p = t.off + t.m0 + (vrow ? row : 0);
       const float wt = topk_w[perm[p]];
       float part = 0.f;
+      uint32_t dgw[NJ][4][2], duw[NJ][4][2];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) dgw[j][g][0] = dgw[j][g][1] = duw[j][g][0] = duw[j][g][1] = 0u;
       // With 8 waves (two per SIMD) every saved g|u word of this row block
       // is loaded before the first dGU store, which could otherwise alias
       // them and serialise the loads (measured: 17% faster there, 4% slower
@@ -300,9 +337,40 @@ struct MDa {
             dg[h] = pack_bf16x2(dgs[0], dgs[1]);
             du[h] = pack_bf16x2(dus[0], dus[1]);
           }
-          *reinterpret_cast<uint2*>(dgu + p * 2 * I + f) = make_uint2(dg[0], dg[1]);
-          *reinterpret_cast<uint2*>(dgu + p * 2 * I + I + f) = make_uint2(du[0], du[1]);
+          dgw[j][g][0] = dg[0]; dgw[j][g][1] = dg[1];
+          duw[j][g][0] = du[0]; duw[j][g][1] = du[1];
         }
+      // dGU: the wave's 32 rows x CW columns of dg, then of du
+      const int rb = wm * RW + 32 * i;
+      const int ncw = t.nc - wn * CW;
+      const int64_t p0 = t.off + t.m0 + rb;
+      auto emit = [&](const uint32_t (&wv)[NJ][4][2], int coff) {
+        bf16_t* base = dgu + p0 * 2 * I + coff + t.n0 + wn * CW;
+        if constexpr (kPStage > 0) {
+          if (stage) {
+            constexpr int NC = CW == 32 ? 32 : 64;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+                WaveRows<NC>::put2(stage, lane & 31, 32 * j + 8 * g + 4 * (lane >> 5), wv[j][g][0], wv[j][g][1]);
+            WaveRows<NC>::drain(stage, lane, [&](int row, int c8, uint4 v) {
+              if (rb + row < t.mc && c8 < ncw) *reinterpret_cast<uint4*>(base + row * 2 * I + c8) = v;
+            });
+            return;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = 32 * j + 8 * g + 4 * (lane >> 5);
+            if (vrow && c < ncw)
+              *reinterpret_cast<uint2*>(base + (lane & 31) * 2 * I + c) = make_uint2(wv[j][g][0], wv[j][g][1]);
+          }
+      };
+      emit(dgw, 0);
+      emit(duw, I);
       // lanes l and l + 32 hold the same row
       part += __shfl_xor(part, 32, 64);
       if (lane < 32 && vrow) dwpart[p * NTP + WN * t.nt + wn] = part;
@@ -331,21 +399,12 @@ struct MDx {
   __device__ __forceinline__ StridedKC b_src(const MTile& t) const {
     return StridedKC{Wgu + int64_t(t.e) * 2 * I * H + t.n0, H, t.nc};
   }
-  static constexpr int kStageBytes = 32 * (32 * NJ * 4 + 16);
+  static constexpr int kPStage = (CW == 32 || CW == 64) ? WaveRows<(CW == 32 ? 32 : 64)>::kBytes : 0;
+  static constexpr int kStageBytes = kPStage;
   __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
                                            unsigned char* stage) const {
-    static_for<IM>([&](auto I_) {
-      constexpr int i = decltype(I_)::value;
-      const int rb = wm * RW + 32 * i;
-      if (rb >= t.mc) return;
-      const int ncw = t.nc - wn * CW;
-      bf16_t* base = vbuf + int64_t(t.off + t.m0 + rb) * H + t.n0 + wn * CW;
-      const int64_t ld = H;
-      stage_f32<NJ>(stage, acc[i], lane, [&](int row, int col, float4 v) {
-        if (rb + row < t.mc && col < ncw)
-          *reinterpret_cast<uint2*>(base + row * ld + col) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-      });
-    });
+    store_rows_bf16<IM, NJ, CW, RW>(acc, stage, wm, lane, t.mc, t.nc - wn * CW,
+                                    vbuf + int64_t(t.off + t.m0) * H + t.n0 + wn * CW, H);
   }
 };
 
