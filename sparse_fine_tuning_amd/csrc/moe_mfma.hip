@@ -293,7 +293,11 @@ struct MDa {
       // is loaded before the first dGU store, which could otherwise alias
       // them and serialise the loads (measured: 17% faster there, 4% slower
       // with one wave per SIMD, where they are loaded next to their use).
+      // With a staging region the block's g and u rows come in as 16-byte
+      // row pieces (8 rows per load) and are read back from LDS in the
+      // output layout.
       constexpr bool kBatch = WM_ * WN_ >= 8;
+      const bool staged = kPStage > 0 && stage != nullptr;
       uint2 gvs[NJ][4], uvs[NJ][4];
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
@@ -301,11 +305,45 @@ struct MDa {
         for (int g = 0; g < 4; ++g) {
           const int col = out_col(CW, wn, j, g, lane);
           gvs[j][g] = uvs[j][g] = make_uint2(0u, 0u);
-          if (!kBatch || !vrow || col >= t.nc) continue;
+          if (staged || !kBatch || !vrow || col >= t.nc) continue;
           const int f = t.n0 + col;
           gvs[j][g] = *reinterpret_cast<const uint2*>(gu + p * 2 * I + f);
           uvs[j][g] = *reinterpret_cast<const uint2*>(gu + p * 2 * I + I + f);
         }
+      if constexpr (kPStage > 0) {
+        if (staged) {
+          constexpr int NC = CW == 32 ? 32 : 64;
+          using WR = WaveRows<NC>;
+          const int rb0 = wm * RW + 32 * i, ncw0 = t.nc - wn * CW;
+          const int lr = lane / WR::kLanesPerRow, lc = lane % WR::kLanesPerRow;
+          const bf16_t* gbase = gu + int64_t(t.off + t.m0 + rb0) * 2 * I + t.n0 + wn * CW;
+          uint4 gq[32 / WR::kRowsPerStore], uq[32 / WR::kRowsPerStore];
+#pragma unroll
+          for (int q = 0; q < 32 / WR::kRowsPerStore; ++q) {
+            const int row = WR::kRowsPerStore * q + lr;
+            gq[q] = uq[q] = make_uint4(0u, 0u, 0u, 0u);
+            if (rb0 + row < t.mc && 8 * lc < ncw0) {
+              gq[q] = *reinterpret_cast<const uint4*>(gbase + int64_t(row) * 2 * I + 8 * lc);
+              uq[q] = *reinterpret_cast<const uint4*>(gbase + int64_t(row) * 2 * I + I + 8 * lc);
+            }
+          }
+          auto back = [&](const uint4 (&rows)[32 / WR::kRowsPerStore], uint2 (&out)[NJ][4]) {
+#pragma unroll
+            for (int q = 0; q < 32 / WR::kRowsPerStore; ++q)
+              *reinterpret_cast<uint4*>(stage + (WR::kRowsPerStore * q + lr) * WR::kPitch + 16 * lc) = rows[q];
+            wave_lds_sync();
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+                out[j][g] = *reinterpret_cast<const uint2*>(stage + (lane & 31) * WR::kPitch +
+                                                            2 * (32 * j + 8 * g + 4 * (lane >> 5)));
+            wave_lds_sync();
+          };
+          back(gq, gvs);
+          back(uq, uvs);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -315,8 +353,8 @@ struct MDa {
           const int f = t.n0 + col;
           // a = bf16(silu(g) u) is recomputed from the saved g|u exactly as the
           // forward epilogue rounded it, instead of being read back
-          const uint2 gv = kBatch ? gvs[j][g] : *reinterpret_cast<const uint2*>(gu + p * 2 * I + f);
-          const uint2 uv = kBatch ? uvs[j][g] : *reinterpret_cast<const uint2*>(gu + p * 2 * I + I + f);
+          const uint2 gv = (kBatch || staged) ? gvs[j][g] : *reinterpret_cast<const uint2*>(gu + p * 2 * I + f);
+          const uint2 uv = (kBatch || staged) ? uvs[j][g] : *reinterpret_cast<const uint2*>(gu + p * 2 * I + I + f);
           const uint32_t gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y};
           uint32_t dg[2], du[2];
 #pragma unroll
