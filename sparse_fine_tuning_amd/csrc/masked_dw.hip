@@ -6,19 +6,19 @@
 //   gate_up: G[r, c] = sum_p dGU[p, r] * X[tok(p), c]          (r < 2I, c < H)
 //   down:    G[r, c] = sum_p (w_p dY[tok(p), r]) * a[p, c]     (r < H,  c < I)
 // over the expert's slots p.  The work is cut into tiles of one expert's
-// rows [r_lo, r_hi) x one column tile: a builder kernel walks each (expert,
-// column tile)'s rows and closes a tile before it would exceed a row limit
-// (set from the list's average density) or one block's pass of entries, so
-// the tiles stay balanced however the selected entries cluster (an
-// importance-selected list is far from uniform: a few rows carry hundreds of
-// entries).  A block takes one
-// tile and streams the expert's slots in chunks of 8: the staging threads
-// load chunk c+2 into registers and transpose chunk c+1 into one of two
-// slot-contiguous LDS buffers ([element][8 slots], one 16-byte read yields
-// an entry's 8 slot values) while every thread multiplies chunk c from the
-// other, one barrier per chunk.  Each thread accumulates a contiguous run of
-// the tile's entries in branch-free groups of 4.  gate_up uses bf16 dot2
-// (fp32 accumulate); down stages w_p * dY in fp32 and uses fp32 FMA.
+// rows [r_lo, r_hi) x one column tile: a builder kernel splits each
+// (expert, column tile)'s rows at quantiles of its entries, within the LDS
+// row limit, so the tiles stay balanced however the selected entries cluster
+// (an importance-selected list is far from uniform: a few rows carry hundreds
+// of entries).  A block takes tiles in turn and streams the expert's slots in
+// chunks of 8: the staging threads keep the loads of the next chunks in
+// registers and transpose chunk c+1 into one of two slot-contiguous LDS
+// buffers ([element][8 slots] bf16, one 16-byte read yields an entry's 8
+// slot values) while every thread multiplies chunk c from the other, one
+// barrier per chunk.  Entries are interleaved over the lanes of a wave;
+// each thread accumulates its entries in branch-free groups of 4 with bf16
+// dot2 (fp32 accumulation).  down stages bf16(w_p * dY), the product rounded
+// once, as a bf16 autograd forms the down projection's output gradient.
 #include <algorithm>
 #include <cmath>
 
@@ -32,29 +32,28 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kSlots = 8;        // slots per staged chunk
 constexpr int kThreads = 512;    // 8 waves per block
-constexpr int kMaxEnt = 24;      // entries per thread per pass (gate_up; down: kMaxEntDown)
-constexpr int kMaxEntDown = 16;  // down's fp32 rows leave fewer registers
+constexpr int kMaxEnt = 24;      // entries per thread per pass
 constexpr int kMaxCB = 2048;     // max columns per tile
 template <bool kDown>
-constexpr int kEnt = kDown ? kMaxEntDown : kMaxEnt;  // entries per thread per pass
+constexpr int kEnt = kMaxEnt;  // entries per thread per pass
 template <bool kDown>
 constexpr int kCap = kThreads * kEnt<kDown>;          // entries of one tile: one pass of a block
 constexpr int kTokTab = 2048;    // slots per token-table window
 // staged chunks whose loads are in flight (register sets of the staging threads)
 constexpr int kPreGateUp = 2;
-constexpr int kPreDown = 2;
+constexpr int kPreDown = 1;
 template <bool kDown>
 constexpr int kPre = kDown ? kPreDown : kPreGateUp;
-// max rows per tile: what the row operand's two LDS buffers allow (bf16 for
-// gate_up, fp32 w*dY for down), staged from r_lo rounded down to 8
+// max rows per tile: what the row operand's two LDS buffers allow (bf16,
+// staged from r_lo rounded down to 8)
 template <bool kDown>
 constexpr int kMaxRows = kDown ? 1024 : 1536;
 template <bool kDown>
-constexpr int kLsBytes = (kMaxRows<kDown> + 8) * kSlots * (kDown ? 4 : 2);
+constexpr int kLsBytes = (kMaxRows<kDown> + 8) * kSlots * 2;
 static_assert((kMaxCB + kMaxRows<false> + 16) / 8 <= kThreads &&
               (kMaxCB + kMaxRows<true> + 16) / 8 <= kThreads, "one staging block per thread");
 constexpr int kRsBytes = kMaxCB * kSlots * 2;
-static_assert(kMaxCB <= kThreads * kMaxEntDown, "a single row fits a tile");
+static_assert(kMaxCB <= kThreads * kMaxEnt, "a single row fits a tile");
 
 struct MaskedArgs {
   const uint32_t* idx; int64_t nnz;
@@ -141,7 +140,6 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[
 // low 3 bits spreads those lanes over all 16 bank groups of a 256-byte window.
 // 32-byte units (fp32 staging) are 8 apart in the same way.
 __device__ __forceinline__ uint32_t sw16(uint32_t u) { return u ^ ((u >> 4) & 7u); }
-__device__ __forceinline__ uint32_t sw32(uint32_t u) { return u ^ ((u >> 3) & 7u); }
 
 // One staging block: 8 slots x 8 consecutive elements of one operand row.
 struct StageRegs {
@@ -182,28 +180,29 @@ __device__ __forceinline__ void stage_store(int b, int nblk_r, const StageRegs& 
                                             unsigned char* lds_l, unsigned char* lds_r) {
   const bool isR = b < nblk_r;
   const int j0 = (isR ? b : b - nblk_r) * 8;
+  uint4 out[8];
   if (isR || !kDown) {
-    uint4 out[8];
     transpose8x8(sr.v, out);
-    unsigned char* dst = isR ? lds_r : lds_l;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<uint4*>(dst + size_t(sw16(uint32_t(j0 + j))) * 16) = out[j];
   } else {
-    // down: w_p * dY in fp32, [row][8 slots]
+    // down: bf16(w_p * dY) for the 8 slots of each element, slots 2d and
+    // 2d+1 in word d (the product rounded once, as a bf16 autograd forms
+    // the down projection's output gradient)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float v[8];
+      uint32_t w[4];
 #pragma unroll
-      for (int t = 0; t < kSlots; ++t) {
-        const uint32_t wd = (j < 2) ? sr.v[t].x : (j < 4) ? sr.v[t].y : (j < 6) ? sr.v[t].z : sr.v[t].w;
-        v[t] = sr.w[t] * ((j & 1) ? bfhi(wd) : bflo(wd));
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t a = word_of(sr.v[2 * d], j >> 1), c = word_of(sr.v[2 * d + 1], j >> 1);
+        const float x0 = (j & 1) ? bfhi(a) : bflo(a), x1 = (j & 1) ? bfhi(c) : bflo(c);
+        w[d] = f2bf2(sr.w[2 * d] * x0, sr.w[2 * d + 1] * x1);
       }
-      float4* dst = reinterpret_cast<float4*>(lds_l + size_t(sw32(uint32_t(j0 + j))) * 32);
-      dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-      dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+      out[j] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
+  unsigned char* dst = isR ? lds_r : lds_l;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    *reinterpret_cast<uint4*>(dst + size_t(sw16(uint32_t(j0 + j))) * 16) = out[j];
 }
 
 // Tiles of one tensor.  Group g = (expert e, column tile ct), e-major; its
@@ -450,22 +449,21 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
         if (opos[i] != 0xffffffffu) {
           const uint32_t col = uint32_t(int64_t(val[i]) - (rb0 + int64_t(rows[i]) * A.C));
           const uint32_t lrow = rows[i] + uint32_t(shift);
-          const uint32_t loff = kDown ? sw32(lrow) * 32 : sw16(lrow) * 16;
+          const uint32_t loff = sw16(lrow) * 16;
           offs[i] = (loff << 16) | (sw16(col) * 16);
         }
       }
     }
-    // Products over one staged chunk, entries in branch-free groups (4, or 2
-    // for down; an unused entry reads row 0 and column 0).  The LDS reads of
-    // group g+1 are issued before the products of group g and no further
-    // ahead (a scheduling barrier after each group), which keeps the
-    // operands of two groups in registers.
-    constexpr int kG = kDown ? 2 : 4;  // entries per group (down rows are 32-byte fp32)
+    // Products over one staged chunk, entries in branch-free groups of 4 (an
+    // unused entry reads row 0 and column 0): bf16 dot2 with fp32
+    // accumulation.  The LDS reads of group g+1 are issued before the
+    // products of group g and no further ahead (a scheduling barrier after
+    // each group), which keeps the operands of two groups in registers.
+    constexpr int kG = 4;
     constexpr int kNG = kE / kG;
     struct Ops {
       uint4 rv[kG];
-      uint4 l0[kG];  // gate_up: 8 bf16 slots; down: slots 0-3 as fp32
-      uint4 l1[kG];  // down: slots 4-7
+      uint4 lv[kG];
     };
     auto load_group = [&](auto G_, const unsigned char* Ls, const unsigned char* Rs, Ops& o) {
       constexpr int g0 = kG * decltype(G_)::value;
@@ -473,13 +471,7 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
       for (int k = 0; k < kG; ++k) {
         const uint32_t lo = offs[g0 + k] >> 16, ro = offs[g0 + k] & 0xffffu;
         o.rv[k] = *reinterpret_cast<const uint4*>(Rs + ro);
-        if constexpr (kDown) {
-          const uint4* src = reinterpret_cast<const uint4*>(Ls + lo);
-          o.l0[k] = src[0];
-          o.l1[k] = src[1];
-        } else {
-          o.l0[k] = *reinterpret_cast<const uint4*>(Ls + lo);
-        }
+        o.lv[k] = *reinterpret_cast<const uint4*>(Ls + lo);
       }
     };
     auto math_group = [&](auto G_, const Ops& o) {
@@ -487,24 +479,15 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
 #pragma unroll
       for (int k = 0; k < kG; ++k) {
         float a = acc[g0 + k];
-        const uint4 rv = o.rv[k];
-        if constexpr (kDown) {
-          const uint4 lx = o.l0[k], ly = o.l1[k];
-          a = fmaf(__uint_as_float(lx.x), bflo(rv.x), a); a = fmaf(__uint_as_float(lx.y), bfhi(rv.x), a);
-          a = fmaf(__uint_as_float(lx.z), bflo(rv.y), a); a = fmaf(__uint_as_float(lx.w), bfhi(rv.y), a);
-          a = fmaf(__uint_as_float(ly.x), bflo(rv.z), a); a = fmaf(__uint_as_float(ly.y), bfhi(rv.z), a);
-          a = fmaf(__uint_as_float(ly.z), bflo(rv.w), a); a = fmaf(__uint_as_float(ly.w), bfhi(rv.w), a);
-        } else {
-          const uint4 lb = o.l0[k];
-          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb.x),
-                                              __builtin_bit_cast(bf16x2_t, rv.x), a, false);
-          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb.y),
-                                              __builtin_bit_cast(bf16x2_t, rv.y), a, false);
-          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb.z),
-                                              __builtin_bit_cast(bf16x2_t, rv.z), a, false);
-          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb.w),
-                                              __builtin_bit_cast(bf16x2_t, rv.w), a, false);
-        }
+        const uint4 rv = o.rv[k], lb = o.lv[k];
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb.x),
+                                            __builtin_bit_cast(bf16x2_t, rv.x), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb.y),
+                                            __builtin_bit_cast(bf16x2_t, rv.y), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb.z),
+                                            __builtin_bit_cast(bf16x2_t, rv.z), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lb.w),
+                                            __builtin_bit_cast(bf16x2_t, rv.w), a, false);
         acc[g0 + k] = a;
       }
     };
