@@ -42,13 +42,13 @@ WRITE_SCALE = 1.0   # and 1,048,576 KiB of WRITE_SIZE
 # the launches of one step (the two SDDMM launches, the plan being kept per
 # list; expert + router Adam)
 COUNTER_TRAFFIC = {
-    "router_gemm": (8847, 16384, "b6d3d88e9a00f8ca"),
-    "gate_up": (554951, 149774, "b6d3d88e9a00f8ca"),
-    "down": (250550, 262195, "b6d3d88e9a00f8ca"),
-    "da": (448368, 140913, "b6d3d88e9a00f8ca"),
-    "dx": (652395, 262259, "b6d3d88e9a00f8ca"),
-    "masked_dw": (169609, 11804, "02e0356039740389"),
-    "adam": (28637, 128683, "a1e0c9fd5b07a9f0"),
+    "router_gemm": (8788, 16384, "285f7d840e47e0fd"),
+    "gate_up": (536745, 147459, "285f7d840e47e0fd"),
+    "down": (242851, 131072, "285f7d840e47e0fd"),
+    "da": (385419, 100382, "285f7d840e47e0fd"),
+    "dx": (642156, 131072, "285f7d840e47e0fd"),
+    "masked_dw": (169503, 11803, "9e57c1de124f2a6e"),
+    "adam": (28632, 124889, "e3d368e223881c40"),
 }
 KERNEL_SOURCES = {
     c: ("gemm_mfma.hpp", "gemm_v2.hpp", "lds_dma.hpp", "moe_mfma.hip", "common.hpp", "moe_internal.hpp")
