@@ -38,21 +38,32 @@ template <bool kDown>
 constexpr int kEnt = kMaxEnt;  // entries per thread per pass
 template <bool kDown>
 constexpr int kCap = kThreads * kEnt<kDown>;          // entries of one tile: one pass of a block
-constexpr int kTokTab = 2048;    // slots per token-table window
+template <bool kDown>
+constexpr int kTokTab = kDown ? 1024 : 2048;  // slots per token-table window (down: LDS for 2048 rows)
 // staged chunks whose loads are in flight (register sets of the staging threads)
 constexpr int kPreGateUp = 2;
 constexpr int kPreDown = 1;
 template <bool kDown>
 constexpr int kPre = kDown ? kPreDown : kPreGateUp;
 // max rows per tile: what the row operand's two LDS buffers allow (bf16,
-// staged from r_lo rounded down to 8)
+// staged from r_lo rounded down to 8); down holds all 2048 rows of a
+// Qwen3-sized expert, so a light expert takes one tile.  The host lowers the
+// limit where rows and columns together would need more staging blocks than
+// threads.
 template <bool kDown>
-constexpr int kMaxRows = kDown ? 1024 : 1536;
+constexpr int kMaxRows = kDown ? 2048 : 1536;
 template <bool kDown>
 constexpr int kLsBytes = (kMaxRows<kDown> + 8) * kSlots * 2;
-static_assert((kMaxCB + kMaxRows<false> + 16) / 8 <= kThreads &&
-              (kMaxCB + kMaxRows<true> + 16) / 8 <= kThreads, "one staging block per thread");
+// row limit for CB columns: LDS and one staging block per thread
+// ((CB + RB + 16) / 8 <= kThreads, rows staged from r_lo rounded down to 8)
+template <bool kDown>
+constexpr int row_limit(int CB) {
+  const int by_threads = (8 * kThreads - 16 - CB) & ~7;
+  return kMaxRows<kDown> < by_threads ? kMaxRows<kDown> : by_threads;
+}
+static_assert(row_limit<false>(kMaxCB) >= 8 && row_limit<true>(kMaxCB) >= 8, "rows per tile");
 constexpr int kRsBytes = kMaxCB * kSlots * 2;
+constexpr int kMaxCUs = 1024;  // bound on the CU count in plan sizes
 static_assert(kMaxCB <= kThreads * kMaxEnt, "a single row fits a tile");
 
 struct MaskedArgs {
@@ -205,33 +216,15 @@ __device__ __forceinline__ void stage_store(int b, int nblk_r, const StageRegs& 
     *reinterpret_cast<uint4*>(dst + size_t(sw16(uint32_t(j0 + j))) * 16) = out[j];
 }
 
-// Tiles of one tensor.  Group g = (expert e, column tile ct), e-major; its
-// rows' entry counts come from the plan's segment starts (per group fewer
-// than 2^31 entries).  The group is split into nt = max(ceil(R / RB),
-// ceil(n / cap)) tiles of about n / nt entries each (n: the group's
-// entries): one wave per group walks the rows 64 at a time and closes the
-// open tile [open_r, r) before row r when it holds RB rows, when row r would
-// take it past cap entries, or when the entries before r reach the next
-// multiple of n / nt and the rows from r on fit in the tiles still planned
-// (so that a row-limited split is not followed by a sliver).  A single row never exceeds cap (at most kMaxCB
-// entries), so every tile is one pass of a block.  Splitting at the
-// quantiles keeps the tiles of a group even however its entries cluster (an
-// importance-selected list puts hundreds of entries in a few rows and leaves
-// others empty) and gives a light expert a single tile.  A group's tiles are
-// appended together at an atomically reserved position: the order of the
-// groups in the list changes no result, since every tile's entries are
-// computed the same way by whichever block takes it.
-// Tile: x = e | ct << 16, y = r_lo | r_hi << 16.
-__global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __restrict__ seg,
-                                                           int64_t qbase, int E, int R, int nct,
-                                                           int RB, int cap, uint2* __restrict__ tiles,
-                                                           int* __restrict__ ntiles) {
+// Entries of each group g = (expert e, column tile ct) of one tensor, one
+// wave per group.
+__global__ __launch_bounds__(256) void masked_group_totals_kernel(const uint32_t* __restrict__ seg,
+                                                                  int64_t qbase, int E, int R, int nct,
+                                                                  int* __restrict__ ng) {
   const int lane = threadIdx.x & 63;
   const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (g >= E * nct) return;  // uniform per wave
   const int e = g / nct, ct = g - e * nct;
-  const uint32_t tx = uint32_t(e) | (uint32_t(ct) << 16);
-  // segment of row r: q0 + r*nct; its entries: seg[q+1] - seg[q]
   const int64_t q0 = qbase + int64_t(e) * R * nct + ct;
   int total;
   if (nct == 1) {
@@ -246,8 +239,81 @@ __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __res
     for (int d = 32; d >= 1; d >>= 1) part += __shfl_xor(part, d, 64);
     total = part;
   }
+  if (lane == 0) ng[g] = total;
+}
+
+// The tensor-wide entry target of a tile: the smallest t <= cap with
+// sum over groups of max(ceil(R/RB), ceil(n_g / t)) <= cus (or cap when even
+// cap leaves more tiles than CUs).  A light list then takes one tile per
+// row range and expert while a heavy expert's entries are spread over the
+// CUs the light ones leave idle.  One block.
+__global__ __launch_bounds__(256) void masked_target_kernel(const int* __restrict__ ng, int G, int R,
+                                                            int RB, int cap, int cus,
+                                                            int* __restrict__ target) {
+  __shared__ int red[4];
+  const int tid = threadIdx.x;
+  const int nr = (R + RB - 1) / RB;
+  auto tiles_at = [&](int t) {
+    int c = 0;
+    for (int g = tid; g < G; g += 256) {
+      const int n = ng[g];
+      if (n > 0) c += max(nr, int((int64_t(n) + t - 1) / t));
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
+    __syncthreads();  // red is free
+    if ((tid & 63) == 0) red[tid >> 6] = c;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+  };
+  int lo = 1, hi = cap;  // invariant: tiles_at(hi) <= cus, or hi == cap
+  if (tiles_at(cap) > cus) {
+    lo = cap;
+  } else {
+    while (lo < hi) {
+      const int mid = lo + (hi - lo) / 2;
+      if (tiles_at(mid) <= cus) hi = mid; else lo = mid + 1;
+    }
+  }
+  if (tid == 0) *target = lo;
+}
+
+// Tiles of one tensor.  Group g = (expert e, column tile ct), e-major; its
+// rows' entry counts come from the plan's segment starts (per group fewer
+// than 2^31 entries).  The group is split into nt = max(ceil(R / RB),
+// ceil(n / min(cap, target))) tiles of about n / nt entries each (n: the
+// group's entries, target: the tensor-wide entry target): one wave per group walks the rows 64 at a time and closes the
+// open tile [open_r, r) before row r when it holds RB rows, when row r would
+// take it past cap entries, or when the entries before r reach the next
+// multiple of n / nt and the rows from r on fit in the tiles still planned
+// (so that a row-limited split is not followed by a sliver).  A single row never exceeds cap (at most kMaxCB
+// entries), so every tile is one pass of a block.  Splitting at the
+// quantiles keeps the tiles of a group even however its entries cluster (an
+// importance-selected list puts hundreds of entries in a few rows and leaves
+// others empty) and gives a light expert a single tile.  A group's tiles are
+// appended together at an atomically reserved position: the order of the
+// groups in the list changes no result, since every tile's entries are
+// computed the same way by whichever block takes it.
+// Tile: x = e | ct << 16, y = r_lo | r_hi << 16.
+__global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __restrict__ seg,
+                                                           int64_t qbase, int E, int R, int nct,
+                                                           int RB, int cap, const int* __restrict__ ng,
+                                                           const int* __restrict__ target,
+                                                           uint2* __restrict__ tiles,
+                                                           int* __restrict__ ntiles) {
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g >= E * nct) return;  // uniform per wave
+  const int e = g / nct, ct = g - e * nct;
+  const uint32_t tx = uint32_t(e) | (uint32_t(ct) << 16);
+  // segment of row r: q0 + r*nct; its entries: seg[q+1] - seg[q]
+  const int64_t q0 = qbase + int64_t(e) * R * nct + ct;
+  const int total = ng[g];
   if (total == 0) return;  // uniform
-  const int nt = max(int((R + RB - 1) / RB), int((int64_t(total) + cap - 1) / cap));
+  // tiles of about total / nt entries: at most cap (one pass of a block) and
+  // at most the tensor-wide target, which spreads the work over the CUs
+  const int tcap = min(cap, *target);
+  const int nt = max(int((R + RB - 1) / RB), int((int64_t(total) + tcap - 1) / tcap));
   // two walks over the rows: the first counts the group's tiles and
   // reserves them at once (a group's tiles stay consecutive in the list), the
   // second writes them; each walk loads the counts of 16 chunks of 64 rows at
@@ -330,8 +396,8 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
   __shared__ __attribute__((aligned(16))) unsigned char lds_r[2][kRsBytes];
   __shared__ int rowpre[kMaxRows<kDown> + 1];
   __shared__ uint32_t rstart[kMaxRows<kDown>];
-  __shared__ int tok_tab[kTokTab];
-  __shared__ float w_tab[kDown ? kTokTab : 1];
+  __shared__ int tok_tab[kTokTab<kDown>];
+  __shared__ float w_tab[kDown ? kTokTab<kDown> : 1];
 
   constexpr int kE = kEnt<kDown>;
   const int tid = threadIdx.x;
@@ -506,8 +572,8 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
     };
     // stream the expert's slots, a token-table window at a time
     const bool stager = tid < nblk_r + nblk_l;  // one staging block per thread
-    for (int w0 = 0; w0 < ne; w0 += kTokTab) {
-      const int wn = min(kTokTab, ne - w0);
+    for (int w0 = 0; w0 < ne; w0 += kTokTab<kDown>) {
+      const int wn = min(kTokTab<kDown>, ne - w0);
       __syncthreads();  // previous window's tables and buffers consumed
       for (int p = tid; p < wn; p += kThreads) {
         const int sid = A.perm[off + w0 + p];
@@ -579,20 +645,22 @@ static void col_tiles(int C, int& CB, int& nct) {
 // tiles hold more than cap entries together) and at most one quantile cut
 // per multiple of n/nt, nt <= ceil(R/RB) + ceil(n/cap) of them, so at most
 // 2 ceil(R/RB) + 3 ceil(n/cap) + 2 tiles; summed over the groups with
-// sum ceil(n/cap) <= nnz/cap + groups.
+// sum ceil(n/cap) <= nnz/cap + groups; a target below cap adds at most
+// kMaxCUs (it is chosen so that the quantile tiles number at most the CUs).
 static int64_t tile_bound(const usaf_moe_shape& s, int R, int C, int64_t nnz, int RB, int cap) {
   int CB, nct;
   col_tiles(C, CB, nct);
-  return int64_t(s.E) * nct * (2 * ceil_div(R, RB) + 5) + 3 * ceil_div(nnz, cap);
+  return int64_t(s.E) * nct * (2 * ceil_div(R, RB) + 5) + 3 * ceil_div(nnz, cap) + kMaxCUs;
 }
 
-// Plan layout (bytes): segment starts [Q+1] u32 (256-aligned), two tile
-// counters (256 bytes), the gate_up tile list, the down tile list.
+// Plan layout (bytes): segment starts [Q+1] u32 (256-aligned), 256 bytes of
+// counters (the two tensors' tile counts, then their entry targets), the
+// gate_up tile list, the down tile list, the groups' entry counts.
 struct PlanLayout {
   SegLayout Lq;
   int RB0, RB1;
   int64_t b0, b1;   // tile bounds for this nnz (block counts)
-  size_t counters, tiles0, tiles1, total;
+  size_t counters, tiles0, tiles1, ngrp, total;
 };
 
 static PlanLayout plan_layout(const usaf_moe_shape& s, int64_t nnz) {
@@ -607,14 +675,15 @@ static PlanLayout plan_layout(const usaf_moe_shape& s, int64_t nnz) {
   Lq.q1 = int64_t(s.E) * Lq.R0 * Lq.nct0;
   Lq.Q = Lq.q1 + int64_t(s.E) * Lq.R1 * Lq.nct1;
   const int64_t N = n_weights(s);
-  P.RB0 = std::min(Lq.R0, kMaxRows<false>);
-  P.RB1 = std::min(Lq.R1, kMaxRows<true>);
+  P.RB0 = std::min(Lq.R0, row_limit<false>(Lq.CB0));
+  P.RB1 = std::min(Lq.R1, row_limit<true>(Lq.CB1));
   P.b0 = tile_bound(s, Lq.R0, Lq.C0, std::min<int64_t>(nnz, Lq.ngu), P.RB0, kCap<false>);
   P.b1 = tile_bound(s, Lq.R1, Lq.C1, std::min<int64_t>(nnz, N - Lq.ngu), P.RB1, kCap<true>);
   P.counters = ((size_t(Lq.Q + 1) * 4 + 255) / 256) * 256;
   P.tiles0 = P.counters + 256;
   P.tiles1 = P.tiles0 + 8 * size_t(tile_bound(s, Lq.R0, Lq.C0, Lq.ngu, P.RB0, kCap<false>));
-  P.total = P.tiles1 + 8 * size_t(tile_bound(s, Lq.R1, Lq.C1, N - Lq.ngu, P.RB1, kCap<true>));
+  P.ngrp = P.tiles1 + ((8 * size_t(tile_bound(s, Lq.R1, Lq.C1, N - Lq.ngu, P.RB1, kCap<true>)) + 255) / 256) * 256;
+  P.total = P.ngrp + ((size_t(s.E) * (Lq.nct0 + Lq.nct1) * 4 + 255) / 256) * 256;
   return P;
 }
 
@@ -634,12 +703,23 @@ usaf_status masked_plan_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64
   hipLaunchKernelGGL(masked_plan_kernel, dim3(unsigned(ceil_div(P.Lq.Q + 1, 256))), dim3(256), 0, st,
                      idx, nnz, P.Lq, seg, counters);
   USAF_LAUNCH_CHECK();
+  int* ng = reinterpret_cast<int*>(base + P.ngrp);
+  const int cus = std::min(device_cus(), kMaxCUs);
   for (int tensor = 0; tensor < 2; ++tensor) {
     const int nct = tensor == 0 ? P.Lq.nct0 : P.Lq.nct1;
     const int groups = s.E * nct;
+    const int64_t qb = tensor == 0 ? int64_t(0) : P.Lq.q1;
+    const int R = tensor == 0 ? P.Lq.R0 : P.Lq.R1, RB = tensor == 0 ? P.RB0 : P.RB1;
+    const int cap = tensor == 0 ? kCap<false> : kCap<true>;
+    int* ngt = ng + (tensor == 0 ? 0 : s.E * P.Lq.nct0);
+    hipLaunchKernelGGL(masked_group_totals_kernel, dim3(unsigned(ceil_div(groups, 4))), dim3(256), 0, st,
+                       seg, qb, s.E, R, nct, ngt);
+    USAF_LAUNCH_CHECK();
+    hipLaunchKernelGGL(masked_target_kernel, dim3(1), dim3(256), 0, st, ngt, groups, R, RB, cap, cus,
+                       counters + 2 + tensor);
+    USAF_LAUNCH_CHECK();
     hipLaunchKernelGGL(masked_tiles_kernel, dim3(unsigned(ceil_div(groups, 4))), dim3(256), 0, st,
-                       seg, tensor == 0 ? int64_t(0) : P.Lq.q1, s.E, tensor == 0 ? P.Lq.R0 : P.Lq.R1, nct,
-                       tensor == 0 ? P.RB0 : P.RB1, tensor == 0 ? kCap<false> : kCap<true>,
+                       seg, qb, s.E, R, nct, RB, cap, ngt, counters + 2 + tensor,
                        reinterpret_cast<uint2*>(base + (tensor == 0 ? P.tiles0 : P.tiles1)),
                        counters + tensor);
     USAF_LAUNCH_CHECK();
