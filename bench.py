@@ -102,15 +102,22 @@ def algorithmic_work(shape, k):
 
 
 def roofline_entry(name, flops, nbytes, ms):
+    """The binding roofline of a kernel class; for classes with MFMA work also
+    its MFMA utilisation next to the ceiling its arithmetic intensity allows
+    (min(1, AI / ridge))."""
     ai = flops / nbytes if nbytes else 0.0
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    extra = {}
+    if flops:
+        extra = dict(mfma_frac=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                     mfma_ceiling=min(1.0, ai / ridge))
     if flops and ai >= ridge:
         ach = flops / (ms * 1e-3) / 1e12
         return dict(kernel=name, bound="mfma", achieved=ach, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=ach / BF16_PEAK_TFLOPS)
+                    frac=ach / BF16_PEAK_TFLOPS, **extra)
     ach = nbytes / (ms * 1e-3) / 1e9
     return dict(kernel=name, bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=ach / HBM_PEAK_GBS)
+                frac=ach / HBM_PEAK_GBS, **extra)
 
 
 def make_layer(lay_cls, dims, d, idx, act):
