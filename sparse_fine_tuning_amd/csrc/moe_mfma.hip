@@ -614,7 +614,8 @@ constexpr int kDwBM = 256, kDwBN = 256, kDwNS = 2;     // dense dW: 128 KiB LDS
 // Groups of at least kBigRows rows on average (few large experts) take
 // 256-row tiles: twice the MFMA work per staged byte, and little ragged waste.
 constexpr int kBigRows = 512;
-constexpr int kBigBM = 256, kBigNS = 2;  // 2 x 64 KiB LDS stages, 8 waves of 128 x 64
+constexpr int kBigBM = 256, kBigNS = 2;  // 2 x 64 KiB LDS stages
+constexpr int kBigWM = 2, kBigWN = 4;    // 8 waves of 128 x 64
 constexpr int kBigDaWN = 2;               // dA on 256-row tiles: 8 waves of 64 x 128
 static bool big_groups(const usaf_moe_shape& s) {
   return int64_t(s.T) * s.K >= int64_t(kBigRows) * s.E;
@@ -624,7 +625,7 @@ template <template <int, int, int, int, int, int> class M, class... Args>
 static usaf_status launch_fwd(const usaf_moe_shape& s, int NT, hipStream_t st, int kclass,
                               Args... args) {
   if (big_groups(s))
-    return launch_persistent(M<kBigBM, kFwdBN, kBigNS, kFwdWM, kFwdWN, 64>{args...},
+    return launch_persistent(M<kBigBM, kFwdBN, kBigNS, kBigWM, kBigWN, 64>{args...},
                              grouped_tiles_bound(s, NT, kBigBM), st, kclass);
   return launch_persistent(M<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN, kFwdBK>{args...},
                            grouped_tiles_bound(s, NT, kFwdBM), st, kclass);
