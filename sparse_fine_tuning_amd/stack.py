@@ -18,6 +18,12 @@ and the importance pass / RigL reselection scan the dense gradient of every
 layer in one backward, selecting each layer's list from its own gradient
 before the next layer's backward reuses the dense buffer.
 
+Around the step (README environment-variable table: STEPS, RESELECT_EVERY,
+the NaN-skip count of the results): a checkpoint holds what a resume needs
+on top of the base weights (every layer's list, moments, router and its
+moments, the weights at every index ever selected, the step and skip
+counts), and the expert load of the last forward is readable per layer.
+
 PyTorch only owns device memory; every step runs in libusaf.so's kernels.
 """
 from __future__ import annotations
@@ -61,6 +67,14 @@ class _Layer:
         self.dWr = z(E, H)
         self.shape = shape
         self.idx = self.m = self.v = self.dW = self.w_list = self.plan = None
+        self.touched = None  # int64 ascending: every index selected so far
+
+    def note_touched(self):
+        """Adds the current list to the touched set (its weights may differ
+        from the base weights from now on: RigL keeps the values of dropped
+        entries)."""
+        cur = self.idx.long() & 0xFFFFFFFF
+        self.touched = cur.clone() if self.touched is None else torch.unique(torch.cat([self.touched, cur]))
 
     def set_active(self, idx: torch.Tensor, act: int):
         """Active list (int32 tensor of ascending uint32 flat indices) with
@@ -71,6 +85,7 @@ class _Layer:
         self.m = torch.zeros(k, dtype=torch.float32, device=dev)
         self.v = torch.zeros(k, dtype=torch.float32, device=dev)
         self.dW = torch.empty(k, dtype=torch.float32, device=dev)
+        self.note_touched()
         self.refresh_list(act)
 
     def refresh_list(self, act: int):
@@ -224,8 +239,65 @@ class MoEStack:
             capi.rigl_reselect(self.shape, grad, lay.W, lay.idx, lay.m, lay.v, k, r, new_idx,
                                new_m, new_v, stats[l], self._ws_rigl, stream)
             lay.idx, lay.m, lay.v = new_idx, new_m, new_v
+            lay.note_touched()
             lay.refresh_list(self.act)
 
         self.forward(stream)
         self.backward(select=reselect, stream=stream)
         return stats
+
+    # ---- monitoring, checkpoint / resume --------------------------------------
+    def expert_load(self) -> torch.Tensor:
+        """Slots routed to each expert in every layer's last forward: int32
+        [n_layers, E] (each row sums to T*K)."""
+        return torch.stack([torch.diff(lay.st["offsets"]) for lay in self.layers])
+
+    def state_dict(self) -> dict:
+        """Host tensors of a resume point: the step and skip counts and, per
+        layer, the list, its moments, the router and its moments, and the
+        touched indices with their current weights.  The weights outside the
+        touched set are the base weights, which the resuming stack loads
+        itself (a 48-layer Qwen3-shaped stack holds 58 GB of them)."""
+        sd = {"t": torch.tensor([self.t], dtype=torch.int64),
+              "skipped": torch.tensor([self.skipped], dtype=torch.int64)}
+        for l, lay in enumerate(self.layers):
+            p = f"layer{l}."
+            sd[p + "idx"] = lay.idx.cpu()
+            sd[p + "m"] = lay.m.cpu()
+            sd[p + "v"] = lay.v.cpu()
+            sd[p + "Wr"] = lay.Wr.cpu()
+            sd[p + "mr"] = lay.mr.cpu()
+            sd[p + "vr"] = lay.vr.cpu()
+            sd[p + "touched"] = lay.touched.cpu()
+            sd[p + "touched_w"] = lay.W[lay.touched].cpu()
+        return sd
+
+    def load_state_dict(self, sd: dict):
+        """Restores a resume point onto a stack of the same shape whose base
+        weights are loaded; the following steps then repeat, bit for bit, the
+        steps of the run that saved it."""
+        dev = self.device
+        self.t = int(sd["t"][0])
+        self.skipped = int(sd["skipped"][0])
+        for l, lay in enumerate(self.layers):
+            p = f"layer{l}."
+            touched = sd[p + "touched"].to(dev)
+            lay.W[touched] = sd[p + "touched_w"].to(dev)
+            lay.Wr.copy_(sd[p + "Wr"].to(dev))
+            lay.mr.copy_(sd[p + "mr"].to(dev))
+            lay.vr.copy_(sd[p + "vr"].to(dev))
+            lay.idx = sd[p + "idx"].to(dev).clone()
+            lay.m = sd[p + "m"].to(dev).clone()
+            lay.v = sd[p + "v"].to(dev).clone()
+            lay.dW = torch.empty_like(lay.m)
+            lay.touched = touched
+            lay.refresh_list(self.act)
+
+    def save(self, path: str):
+        """The state dict as a safetensors file."""
+        from safetensors.torch import save_file
+        save_file(self.state_dict(), path)
+
+    def load(self, path: str):
+        from safetensors.torch import load_file
+        self.load_state_dict(load_file(path))

@@ -133,6 +133,63 @@ def make_layers(L, dims, seed0, bf16):
     return layers
 
 
+def test_stack_checkpoint_resume_bit_exact(capi, tmp_path):
+    """A stack saved after the importance pass, two steps, a RigL pass and one
+    more step, then resumed from the file onto a fresh stack holding only the
+    base weights, repeats the next two steps bit for bit (losses, touched
+    weights, lists, moments, router); the expert load of a forward sums to
+    T*K per layer."""
+    from sparse_fine_tuning_amd.stack import MoEStack, cosine_lr
+    dims = (200, 256, 8, 2, 96)
+    T, H, E, K, I = dims
+    L = 3
+    say(f"stack checkpoint L={L} dims={dims}")
+    layers = make_layers(L, dims, 7, bf16=True)
+    N = 3 * E * H * I
+    k = O.select_count(N, 5, 1000)
+    r = (3 * k) // 10
+
+    def fresh():
+        stk = MoEStack(L, *dims, act=capi.BF16, device=DEV)
+        for l, lay in enumerate(layers):
+            stk.load_layer(l, lay["W_gu"], lay["W_d"], lay["Wr"])
+        return stk
+
+    def batch(t):
+        return (synth.to_bf16_values(synth.normal((T, H), 1.0, 300 + t)),
+                synth.to_bf16_values(synth.normal((T, H), 1.0, 30000 + t)))
+
+    total = 6
+    a = fresh()
+    a.set_batch(*batch(0))
+    a.importance(k)
+    for t in range(4):
+        a.set_batch(*batch(t))
+        if t == 2:
+            a.rigl(r)
+        a.train_step(cosine_lr(t, total, 2e-4))
+    load = a.expert_load()
+    assert load.shape == (L, E) and bool((load.sum(dim=1) == T * K).all())
+    ck = str(tmp_path / "stack.safetensors")
+    a.save(ck)
+    assert all(lay.touched.numel() > k for lay in a.layers)  # RigL grew new entries
+    b = fresh()
+    b.load(ck)
+    assert b.t == a.t == 4
+    for t in range(4, total):
+        for stk in (a, b):
+            stk.set_batch(*batch(t))
+            stk.train_step(cosine_lr(t, total, 2e-4))
+        torch.cuda.synchronize()
+        assert float(a.loss.item()) == float(b.loss.item()), t
+    assert a.t == b.t == total
+    for la, lb in zip(a.layers, b.layers):
+        assert torch.equal(la.W.view(torch.int16), lb.W.view(torch.int16))
+        for x, y in ((la.idx, lb.idx), (la.m, lb.m), (la.v, lb.v), (la.Wr, lb.Wr), (la.mr, lb.mr),
+                     (la.vr, lb.vr), (la.touched, lb.touched)):
+            assert torch.equal(x, y)
+
+
 def test_bf16_stack_steps_vs_oracle(capi):
     """Three layers, fixed 0.5% masks, three steps with the cosine schedule."""
     from sparse_fine_tuning_amd.stack import MoEStack, cosine_lr
