@@ -614,7 +614,7 @@ constexpr int kDwBM = 256, kDwBN = 256, kDwNS = 2;     // dense dW: 128 KiB LDS
 // Groups of at least kBigRows rows on average (few large experts) take
 // 256-row tiles: twice the MFMA work per staged byte, and little ragged waste.
 constexpr int kBigRows = 512;
-constexpr int kBigBM = 256, kBigNS = 2;  // 2 x 64 KiB LDS stages
+constexpr int kBigBM = 256, kBigNS = 2, kBigBK = 64;  // 2 x 64 KiB LDS stages
 constexpr int kBigWM = 2, kBigWN = 4;    // 8 waves of 128 x 64
 constexpr int kBigDaWN = 2;               // dA on 256-row tiles: 8 waves of 64 x 128
 static bool big_groups(const usaf_moe_shape& s) {
@@ -625,7 +625,7 @@ template <template <int, int, int, int, int, int> class M, class... Args>
 static usaf_status launch_fwd(const usaf_moe_shape& s, int NT, hipStream_t st, int kclass,
                               Args... args) {
   if (big_groups(s))
-    return launch_persistent(M<kBigBM, kFwdBN, kBigNS, kBigWM, kBigWN, 64>{args...},
+    return launch_persistent(M<kBigBM, kFwdBN, kBigNS, kBigWM, kBigWN, kBigBK>{args...},
                              grouped_tiles_bound(s, NT, kBigBM), st, kclass);
   return launch_persistent(M<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN, kFwdBK>{args...},
                            grouped_tiles_bound(s, NT, kFwdBM), st, kclass);
@@ -655,7 +655,7 @@ usaf_status mfma_da(const usaf_moe_shape& s, const bf16_t* dY, const bf16_t* Wd,
                     hipStream_t st) {
   const int NT = int(ceil_div(s.I, kFwdBN));
   if (big_groups(s))  // 8 waves of 64 x 128 on 256-row tiles
-    return launch_persistent(g2::MDa<kBigBM, kFwdBN, kBigNS, 4, kBigDaWN>{dY, Wd, offsets, perm, topk_w, gu,
+    return launch_persistent(g2::MDa<kBigBM, kFwdBN, kBigNS, 4, kBigDaWN, kBigBK>{dY, Wd, offsets, perm, topk_w, gu,
                                                                           a, dgu, dwpart, s.H, s.E, s.K,
                                                                           s.I, NT, kBigDaWN * NT},
                              grouped_tiles_bound(s, NT, kBigBM), st, USAF_K_DA);
