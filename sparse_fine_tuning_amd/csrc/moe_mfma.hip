@@ -127,7 +127,8 @@ struct MGateUp {
     return GateUpRowsC<CW>{Wgu + int64_t(t.e) * 2 * I * H, t.n0, I, H};
   }
   // persistent epilogue staging: one tensor's 32-row block (CW/2 features)
-  static constexpr int kPStage = WaveRows<CW / 2>::kBytes;
+  static constexpr int kPStage =
+      WaveRows<CW / 2>::kBytes * WM_ * WN_ <= (BM_ + BN_) * BK_ * 2 ? WaveRows<CW / 2>::kBytes : 0;
   static constexpr int kStageBytes = kPStage;
   __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
                                            unsigned char* stage) const {
@@ -244,7 +245,10 @@ struct MDown {
   __device__ __forceinline__ PlainRowsC b_src(const MTile& t) const {
     return PlainRowsC{Wd + (int64_t(t.e) * H + t.n0) * I, I, t.nc};
   }
-  static constexpr int kPStage = (CW == 32 || CW == 64) ? WaveRows<(CW == 32 ? 32 : 64)>::kBytes : 0;
+  // staging through one ring stage, where the wave's block fits there
+  static constexpr int kPStage = ((CW == 32 || CW == 64) &&
+                                  WaveRows<(CW == 32 ? 32 : 64)>::kBytes * WM_ * WN_ <= (BM_ + BN_) * BK_ * 2)
+                                     ? WaveRows<(CW == 32 ? 32 : 64)>::kBytes : 0;
   static constexpr int kStageBytes = kPStage;
   __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
                                            unsigned char* stage) const {
@@ -273,7 +277,10 @@ struct MDa {
   __device__ __forceinline__ StridedKC b_src(const MTile& t) const {
     return StridedKC{Wd + int64_t(t.e) * H * I + t.n0, I, t.nc};
   }
-  static constexpr int kPStage = (CW == 32 || CW == 64) ? WaveRows<(CW == 32 ? 32 : 64)>::kBytes : 0;
+  // staging through one ring stage, where the wave's block fits there
+  static constexpr int kPStage = ((CW == 32 || CW == 64) &&
+                                  WaveRows<(CW == 32 ? 32 : 64)>::kBytes * WM_ * WN_ <= (BM_ + BN_) * BK_ * 2)
+                                     ? WaveRows<(CW == 32 ? 32 : 64)>::kBytes : 0;
   static constexpr int kStageBytes = kPStage;
   __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
                                            unsigned char* stage) const {
@@ -437,7 +444,10 @@ struct MDx {
   __device__ __forceinline__ StridedKC b_src(const MTile& t) const {
     return StridedKC{Wgu + int64_t(t.e) * 2 * I * H + t.n0, H, t.nc};
   }
-  static constexpr int kPStage = (CW == 32 || CW == 64) ? WaveRows<(CW == 32 ? 32 : 64)>::kBytes : 0;
+  // staging through one ring stage, where the wave's block fits there
+  static constexpr int kPStage = ((CW == 32 || CW == 64) &&
+                                  WaveRows<(CW == 32 ? 32 : 64)>::kBytes * WM_ * WN_ <= (BM_ + BN_) * BK_ * 2)
+                                     ? WaveRows<(CW == 32 ? 32 : 64)>::kBytes : 0;
   static constexpr int kStageBytes = kPStage;
   __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
                                            unsigned char* stage) const {
