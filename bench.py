@@ -42,13 +42,13 @@ WRITE_SCALE = 1.0   # and 1,048,576 KiB of WRITE_SIZE
 # the launches of one step (the two SDDMM launches, the plan being kept per
 # list; expert + router Adam)
 COUNTER_TRAFFIC = {
-    "router_gemm": (8788, 16384, "285f7d840e47e0fd"),
-    "gate_up": (536745, 147459, "285f7d840e47e0fd"),
-    "down": (242851, 131072, "285f7d840e47e0fd"),
-    "da": (385419, 100382, "285f7d840e47e0fd"),
-    "dx": (642156, 131072, "285f7d840e47e0fd"),
-    "masked_dw": (169503, 11803, "9e57c1de124f2a6e"),
-    "adam": (28632, 124889, "e3d368e223881c40"),
+    "router_gemm": (8788, 16384, "577764dd3a9fdc69"),
+    "gate_up": (532485, 147458, "577764dd3a9fdc69"),
+    "down": (243579, 131072, "577764dd3a9fdc69"),
+    "da": (382455, 100370, "577764dd3a9fdc69"),
+    "dx": (629936, 131072, "577764dd3a9fdc69"),
+    "masked_dw": (169607, 11803, "2c8a87e7202209f0"),
+    "adam": (28632, 124890, "e3d368e223881c40"),
 }
 KERNEL_SOURCES = {
     c: ("gemm_mfma.hpp", "gemm_v2.hpp", "lds_dma.hpp", "moe_mfma.hip", "common.hpp", "moe_internal.hpp")
