@@ -60,7 +60,16 @@ struct Occupancy {
 
 // Logical tile L -> (expert, column tile, row tile of BM rows) over device
 // offsets[E+1]; tiles ordered expert-major, then column tile, then row tile.
+// When BM is an odd number of 32-row blocks, a group of cnt rows takes
+// ceil(cnt / BM) row tiles of equal size in whole blocks (the last one
+// shorter): 256 rows under BM = 160 make two tiles of 128, not 160 + 96.
 // Wave 0 scans the experts 64 at a time; false for the whole block past the end.
+template <int BM>
+__device__ __forceinline__ int row_tile(int cnt) {
+  if constexpr ((BM / 32) % 2 == 0) return BM;
+  const int n = (cnt + BM - 1) / BM;
+  return n > 0 ? ((cnt + n - 1) / n + 31) / 32 * 32 : BM;
+}
 template <int BM>
 __device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ offsets, int E, int NT,
                                              int L, MTile& t) {
@@ -73,7 +82,7 @@ __device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ offsets
       const int e = e0 + lane;
       const int o0 = e < E ? offsets[e] : 0;
       const int cnt = e < E ? offsets[e + 1] - o0 : 0;
-      const int tiles = ((cnt + BM - 1) / BM) * NT;
+      const int tiles = ((cnt + row_tile<BM>(cnt) - 1) / row_tile<BM>(cnt)) * NT;
       int incl = tiles;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
@@ -100,21 +109,33 @@ __device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ offsets
   t.e = sh[0];
   if (t.e < 0) return false;
   const int rem = sh[1], cnt = sh[2];
-  const int mts = (cnt + BM - 1) / BM;
+  const int q = row_tile<BM>(cnt), mts = (cnt + q - 1) / q;
   t.nt = rem / mts;
-  t.m0 = (rem - t.nt * mts) * BM;
-  t.mc = min(BM, cnt - t.m0);
+  t.m0 = (rem - t.nt * mts) * q;
+  t.mc = min(q, cnt - t.m0);
   t.off = sh[3];
   return true;
 }
 
-// RW / CW: rows / columns of the tile held by one wave
-__device__ __forceinline__ int out_row(int RW, int wm, int i, int lane) {
-  return wm * RW + 32 * i + (lane & 31);
-}
+// CW: columns of the tile held by one wave
 // first of the 4 consecutive columns of group g of block j
 __device__ __forceinline__ int out_col(int CW, int wn, int j, int g, int lane) {
   return wn * CW + 32 * j + 8 * g + 4 * (lane >> 5);
+}
+// First tile row r0 and valid 32-row blocks vb of wave-row wm for a tile of
+// mc rows.  kSplit (two wave-rows): the tile's blocks are shared evenly,
+// wave-row 0 taking the odd one, so a 128-row tile under RW = 96 runs 2 + 2
+// blocks; otherwise wave-row wm holds rows [wm RW, (wm + 1) RW).
+template <bool kSplit, int RW, int IM>
+__device__ __forceinline__ void wave_rows(int mc, int wm, int& r0, int& vb) {
+  if constexpr (kSplit) {
+    const int nb = (mc + 31) / 32, h = (nb + 1) / 2;
+    r0 = wm ? 32 * h : 0;
+    vb = min(IM, wm ? nb - h : h);
+  } else {
+    r0 = wm * RW;
+    vb = min(IM, max(0, (mc - r0 + 31) / 32));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -130,11 +151,23 @@ struct KMajor {
   static constexpr int kRowB = BK * 2;       // bytes per staged row
   static constexpr int kCh = BK / 8;         // 16-byte chunks per row
   static constexpr int kRPI = 64 / kCh;      // rows per dma instruction
-  static constexpr int kRW = R / NW;         // rows copied by one wave
+  static constexpr int kGroups = R / kRPI;   // dma instructions per stage (all waves)
   static constexpr int kFragReads = 1;       // LDS read instructions per fragment
-  static constexpr int kInst = kRW / kRPI;   // dma instructions per wave per stage
+  // dma instructions per wave per stage: when the waves cannot share the
+  // row groups evenly, group g = i NW + w goes to wave w, and the first
+  // kGroups % NW waves issue one more than the rest (kInstMin)
+  static constexpr bool kEven = kGroups % NW == 0;
+  static constexpr int kInst = (kGroups + NW - 1) / NW;
+  static constexpr int kInstMin = kGroups / NW;
   static constexpr int kBytes = R * kRowB;
-  static_assert(kInst * kRPI == kRW, "rows per wave");
+  static_assert(kGroups * kRPI == R && kInstMin > 0, "row groups");
+  // first row of the wave's i-th instruction
+  __device__ __forceinline__ static int group_row(int w, int i) {
+    return kRPI * (kEven ? w * kInst + i : i * NW + w);
+  }
+  __device__ __forceinline__ static bool has_inst(int w, int i) {
+    return kEven || i < kInstMin || w < kGroups - kInstMin * NW;
+  }
   // slot of 16-byte chunk q in row r: 64 banks serve 16 lanes of a 16-byte
   // read together, i.e. 16 consecutive rows; 256 / kRowB consecutive rows
   // share a 256-byte bank line, so the chunk position is XOR-ed with the
@@ -148,7 +181,7 @@ struct KMajor {
     kend = kend_;
 #pragma unroll
     for (int i = 0; i < kInst; ++i) {
-      const int r = w * kRW + kRPI * i + lane / kCh;
+      const int r = (kEven ? group_row(w, i) : min(group_row(w, i), R - kRPI)) + lane / kCh;
       chunk[i] = (lane % kCh) ^ sw(r);
       p[i] = s.row(r) + 8 * chunk[i];
     }
@@ -159,11 +192,12 @@ struct KMajor {
     const int k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < kInst; ++i) {
+      if (!has_inst(w, i)) break;  // wave-uniform
       // a chunk past kend (kend % BK != 0, last stage) reads the row's last
       // chunk instead; it is zeroed before use
       const int over = k0 + 8 * chunk[i] + 8 - kend;
       const int koff = over > 0 ? k0 - over : k0;
-      dma16(p[i] + koff, lds + (w * kRW + kRPI * i) * kRowB);
+      dma16(p[i] + koff, lds + group_row(w, i) * kRowB);
     }
   }
   // zero k >= kvalid (kvalid a multiple of 8) in a stage
@@ -189,6 +223,7 @@ struct MNMajor {
   static constexpr int kKPI = 64 / kCPR;     // k-rows per dma instruction
   static constexpr int kFragReads = 2;       // LDS read instructions per fragment
   static constexpr int kInst = BK * kCPR / (64 * NW);  // dma instructions per wave per stage
+  static constexpr int kInstMin = kInst;
   static constexpr int kBytes = BK * R * 2;
   static_assert(kInst * 64 * NW == BK * kCPR, "k-rows per wave");
   int kend, slot, last, krow0;
@@ -333,11 +368,11 @@ __device__ __forceinline__ void interleave_mfma_reads() {
 template <class P, int VB, int IM, int NJ, class AOp, class BOp, class AS, class BS>
 __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS& as, const BS& bs,
                                           unsigned char (*lds)[AOp::kBytes + BOp::kBytes], int K,
-                                          int nk, int tid, int w, int wm, int wn, int lane,
+                                          int nk, int tid, int w, int r0, int wn, int lane,
                                           f32x16_t (&acc)[IM][NJ]) {
-  constexpr int NS = P::NS, RW = P::RW, CW = P::CW;
+  constexpr int NS = P::NS, CW = P::CW;
   constexpr int A_BYTES = AOp::kBytes;
-  constexpr int NLOAD = AOp::kInst + BOp::kInst;
+  constexpr int NLOAD = AOp::kInstMin + BOp::kInstMin;  // the fewest any wave issues per stage
   constexpr int BK = AOp::kBK;
   static_assert(BOp::kBK == BK, "operands share the stage depth");
   constexpr int KC = BK / 16;
@@ -377,7 +412,7 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
       // fragments of substep kc+1 are read while the MFMAs of kc run
       bf16x8_t af[2][VB], bfr[2][NJ];
 #pragma unroll
-      for (int i = 0; i < VB; ++i) af[0][i] = AOp::frag(As, wm * RW + 32 * i, 0, lane);
+      for (int i = 0; i < VB; ++i) af[0][i] = AOp::frag(As, r0 + 32 * i, 0, lane);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bfr[0][j] = BOp::frag(Bs, wn * CW + 32 * j, 0, lane);
       if constexpr (!kFirst) {
@@ -388,7 +423,7 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
       for (int kc = 0; kc < KC - 1; ++kc) {
         const int c = kc & 1, n = c ^ 1;
 #pragma unroll
-        for (int i = 0; i < VB; ++i) af[n][i] = AOp::frag(As, wm * RW + 32 * i, kc + 1, lane);
+        for (int i = 0; i < VB; ++i) af[n][i] = AOp::frag(As, r0 + 32 * i, kc + 1, lane);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) bfr[n][j] = BOp::frag(Bs, wn * CW + 32 * j, kc + 1, lane);
         mfmas(af[c], bfr[c]);
@@ -414,7 +449,7 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_kernel(P p) {
   using AOp = typename P::AOp;
   using BOp = typename P::BOp;
   constexpr int A_BYTES = AOp::kBytes, B_BYTES = BOp::kBytes;
-  constexpr int NLOAD = AOp::kInst + BOp::kInst;
+  constexpr int NLOAD = AOp::kInstMin + BOp::kInstMin;  // the fewest any wave issues per stage
   static_assert((NS - 2) * NLOAD < 64, "vmcnt");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[NS][A_BYTES + B_BYTES];
   MTile t;
@@ -443,7 +478,7 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_kernel(P p) {
       ao.issue(as, s, lds[s], w, lane);
       bo.issue(bs, s, lds[s] + A_BYTES, w, lane);
     }
-  main_loop<P, IM, IM, NJ>(ao, bo, as, bs, lds, K, nk, tid, w, wm, wn, lane, acc);
+  main_loop<P, IM, IM, NJ>(ao, bo, as, bs, lds, K, nk, tid, w, wm * P::RW, wn, lane, acc);
   __syncthreads();  // the ring is free: epilogues may stage through it
   p.epilogue(t, acc, wm, wn, lane, &lds[0][0] + w * P::kStageBytes);
 }
@@ -459,7 +494,7 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_persistent(P p)
   using AOp = typename P::AOp;
   using BOp = typename P::BOp;
   constexpr int A_BYTES = AOp::kBytes, B_BYTES = BOp::kBytes;
-  constexpr int NLOAD = AOp::kInst + BOp::kInst;
+  constexpr int NLOAD = AOp::kInstMin + BOp::kInstMin;  // the fewest any wave issues per stage
   static_assert((NS - 2) * NLOAD < 64, "vmcnt");
   static_assert(P::kPStage * (P::NTHR / 64) <= A_BYTES + B_BYTES, "epilogue staging fits one ring stage");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[NS][A_BYTES + B_BYTES];
@@ -493,10 +528,17 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_persistent(P p)
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     // 32-row blocks of this wave inside the tile's valid rows: a ragged
     // group's last tile issues MFMAs only for its valid row blocks
-    const int vb = __builtin_amdgcn_readfirstlane(min(IM, max(0, (t.mc - wm * P::RW + 31) / 32)));
+    int r0 = wm * P::RW, vb;
+    if constexpr (P::kSplit) {
+      wave_rows<true, P::RW, IM>(t.mc, wm, r0, vb);
+      r0 = __builtin_amdgcn_readfirstlane(r0);
+    } else {
+      vb = min(IM, max(0, (t.mc - r0 + 31) / 32));
+    }
+    vb = __builtin_amdgcn_readfirstlane(vb);
     static_for<IM + 1>([&](auto V_) {
       constexpr int v = decltype(V_)::value;
-      if (vb == v) main_loop<P, v, IM, NJ>(ao, bo, as, bs, lds, t.ke, nk, tid, w, wm, wn, lane, acc);
+      if (vb == v) main_loop<P, v, IM, NJ>(ao, bo, as, bs, lds, t.ke, nk, tid, w, r0, wn, lane, acc);
     });
     __syncthreads();  // every wave is done with the ring
     MTile tn;

@@ -111,7 +111,9 @@ struct MGateUp {
   static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
   static constexpr int kBlocksPerCU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kBlocksPerCU;
   static constexpr int kWavesPerEU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kWavesPerEU;
-  static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
+  static constexpr int RW = (BM / WM + 31) / 32 * 32, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
+  // two wave-rows share an odd number of row blocks evenly at run time
+  static constexpr bool kSplit = WM_ == 2 && (BM_ / 32) % 2 == 1;
   using AOp = KMajor<BM, WM_ * WN_, BK_>;
   using BOp = KMajor<BN, WM_ * WN_, BK_>;
   const bf16_t* X; const bf16_t* Wgu; const int32_t* offsets; const int32_t* perm;
@@ -134,10 +136,12 @@ struct MGateUp {
                                            unsigned char* stage) const {
     static_assert(NJ % 2 == 0, "gate / up blocks of 32 features alternate");
     const int F = t.n0 + (CW / 2) * wn;  // first feature of this wave
+    int r0, vb;
+    wave_rows<kSplit, RW, IM>(t.mc, wm, r0, vb);
     static_for<IM>([&](auto I_) {
       constexpr int i = decltype(I_)::value;
-      const int rb = wm * RW + 32 * i;
-      if (rb >= t.mc) return;
+      const int rb = r0 + 32 * i;
+      if (kSplit ? i >= vb : rb >= t.mc) return;
       const int r = lane & 31, h = lane >> 5;
       // g, u (rounded once) and a = bf16(silu(g) u), as packed word pairs
       uint32_t gw[NJ / 2][4][2], uw[NJ / 2][4][2], aw[NJ / 2][4][2];
@@ -187,13 +191,14 @@ struct MGateUp {
 
 // bf16 [32 rows x CW] blocks of a wave's accumulators to rows base + row*ld:
 // staged through the wave's LDS region (CW = 32 or 64), else 8-byte stores.
-template <int IM, int NJ, int CW, int RW>
-__device__ __forceinline__ void store_rows_bf16(const f32x16_t (&acc)[IM][NJ], unsigned char* stage, int wm,
-                                                int lane, int mc, int ncw, bf16_t* base0, int64_t ld) {
+template <int IM, int NJ, int CW>
+__device__ __forceinline__ void store_rows_bf16(const f32x16_t (&acc)[IM][NJ], unsigned char* stage, int r0,
+                                                int vb, int lane, int mc, int ncw, bf16_t* base0,
+                                                int64_t ld) {
   static_for<IM>([&](auto I_) {
     constexpr int i = decltype(I_)::value;
-    const int rb = wm * RW + 32 * i;
-    if (rb >= mc) return;
+    const int rb = r0 + 32 * i;
+    if (i >= vb) return;
     bf16_t* base = base0 + int64_t(rb) * ld;
     const int r = lane & 31, h = lane >> 5;
     if constexpr (CW == 32 || CW == 64) {
@@ -229,7 +234,9 @@ struct MDown {
   static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
   static constexpr int kBlocksPerCU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kBlocksPerCU;
   static constexpr int kWavesPerEU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kWavesPerEU;
-  static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
+  static constexpr int RW = (BM / WM + 31) / 32 * 32, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
+  // two wave-rows share an odd number of row blocks evenly at run time
+  static constexpr bool kSplit = WM_ == 2 && (BM_ / 32) % 2 == 1;
   using AOp = KMajor<BM, WM_ * WN_, BK_>;
   using BOp = KMajor<BN, WM_ * WN_, BK_>;
   const bf16_t* a; const bf16_t* Wd; const int32_t* offsets; bf16_t* ybuf;
@@ -252,8 +259,10 @@ struct MDown {
   static constexpr int kStageBytes = kPStage;
   __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
                                            unsigned char* stage) const {
-    store_rows_bf16<IM, NJ, CW, RW>(acc, stage, wm, lane, t.mc, t.nc - wn * CW,
-                                    ybuf + int64_t(t.off + t.m0) * H + t.n0 + wn * CW, H);
+    int r0, vb;
+    wave_rows<kSplit, RW, IM>(t.mc, wm, r0, vb);
+    store_rows_bf16<IM, NJ, CW>(acc, stage, r0, vb, lane, t.mc, t.nc - wn * CW,
+                                ybuf + int64_t(t.off + t.m0) * H + t.n0 + wn * CW, H);
   }
 };
 
@@ -262,7 +271,9 @@ struct MDa {
   static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
   static constexpr int kBlocksPerCU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kBlocksPerCU;
   static constexpr int kWavesPerEU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kWavesPerEU;
-  static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
+  static constexpr int RW = (BM / WM + 31) / 32 * 32, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
+  // two wave-rows share an odd number of row blocks evenly at run time
+  static constexpr bool kSplit = WM_ == 2 && (BM_ / 32) % 2 == 1;
   using AOp = KMajor<BM, WM_ * WN_, BK_>;
   using BOp = MNMajor<BN, WM_ * WN_, BK_>;
   const bf16_t* dY; const bf16_t* Wd; const int32_t* offsets; const int32_t* perm;
@@ -284,9 +295,12 @@ struct MDa {
   static constexpr int kStageBytes = kPStage;
   __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
                                            unsigned char* stage) const {
+    int r0, vb;
+    wave_rows<kSplit, RW, IM>(t.mc, wm, r0, vb);
     static_for<IM>([&](auto I_) {
       constexpr int i = decltype(I_)::value;
-      const int row = out_row(RW, wm, i, lane);
+      if (i >= vb) return;
+      const int row = r0 + 32 * i + (lane & 31);
       const bool vrow = row < t.mc;
       const int64_t p = t.off + t.m0 + (vrow ? row : 0);
       const float wt = topk_w[perm[p]];
@@ -321,7 +335,7 @@ struct MDa {
         if (staged) {
           constexpr int NC = CW == 32 ? 32 : 64;
           using WR = WaveRows<NC>;
-          const int rb0 = wm * RW + 32 * i, ncw0 = t.nc - wn * CW;
+          const int rb0 = r0 + 32 * i, ncw0 = t.nc - wn * CW;
           const int lr = lane / WR::kLanesPerRow, lc = lane % WR::kLanesPerRow;
           const bf16_t* gbase = gu + int64_t(t.off + t.m0 + rb0) * 2 * I + t.n0 + wn * CW;
           uint4 gq[32 / WR::kRowsPerStore], uq[32 / WR::kRowsPerStore];
@@ -386,7 +400,7 @@ struct MDa {
           duw[j][g][0] = du[0]; duw[j][g][1] = du[1];
         }
       // dGU: the wave's 32 rows x CW columns of dg, then of du
-      const int rb = wm * RW + 32 * i;
+      const int rb = r0 + 32 * i;
       const int ncw = t.nc - wn * CW;
       const int64_t p0 = t.off + t.m0 + rb;
       auto emit = [&](const uint32_t (&wv)[NJ][4][2], int coff) {
@@ -428,7 +442,9 @@ struct MDx {
   static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
   static constexpr int kBlocksPerCU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kBlocksPerCU;
   static constexpr int kWavesPerEU = Occupancy<BM_, BN_, BK_, NS_, WM_ * WN_>::kWavesPerEU;
-  static constexpr int RW = BM / WM, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
+  static constexpr int RW = (BM / WM + 31) / 32 * 32, CW = BN / WN, IM = RW / 32, NJ = CW / 32;
+  // two wave-rows share an odd number of row blocks evenly at run time
+  static constexpr bool kSplit = WM_ == 2 && (BM_ / 32) % 2 == 1;
   using AOp = KMajor<BM, WM_ * WN_, BK_>;
   using BOp = MNMajor<BN, WM_ * WN_, BK_>;
   const bf16_t* dgu; const bf16_t* Wgu; const int32_t* offsets; bf16_t* vbuf;
@@ -451,8 +467,10 @@ struct MDx {
   static constexpr int kStageBytes = kPStage;
   __device__ __forceinline__ void epilogue(const MTile& t, f32x16_t (&acc)[IM][NJ], int wm, int wn, int lane,
                                            unsigned char* stage) const {
-    store_rows_bf16<IM, NJ, CW, RW>(acc, stage, wm, lane, t.mc, t.nc - wn * CW,
-                                    vbuf + int64_t(t.off + t.m0) * H + t.n0 + wn * CW, H);
+    int r0, vb;
+    wave_rows<kSplit, RW, IM>(t.mc, wm, r0, vb);
+    store_rows_bf16<IM, NJ, CW>(acc, stage, r0, vb, lane, t.mc, t.nc - wn * CW,
+                                vbuf + int64_t(t.off + t.m0) * H + t.n0 + wn * CW, H);
   }
 };
 
@@ -615,7 +633,7 @@ usaf_status mfma_router(const usaf_moe_shape& s, const bf16_t* X, const float* W
 }
 
 // Tile shapes and LDS ring depths of the direct-to-LDS GEMMs.
-constexpr int kFwdBM = 128, kFwdBN = 256, kFwdNS = 3;  // gate_up, down, dA, dX: 144 KiB LDS
+constexpr int kFwdBM = 160, kFwdBN = 256, kFwdNS = 3;  // gate_up, down, dA, dX: 156 KiB LDS
 constexpr int kFwdWM = 2, kFwdWN = 4;                  // 8 waves: 2 per SIMD
 constexpr int kFwdBK = 64;                             // contraction depth of a stage
 constexpr int kDaWN = 4;                               // dA: 8 waves of 64 x 64

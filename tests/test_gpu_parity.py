@@ -156,6 +156,13 @@ CASES = [
     ("coltiled_down_bf16", (48, 128, 3, 2, 2560), 1, (80, 81, 82, 83, 84)),
     # >= 512 rows per expert on average: the 256-row GEMM tiles, ragged
     ("big_groups_bf16", (1100, 256, 4, 2, 96), 1, (85, 86, 87, 88, 89)),
+    # 160-row GEMM tiles split evenly: groups of ~300 rows take 160 + the
+    # rest, the two wave-rows sharing 5 blocks 3 + 2
+    ("row_tiles_bf16", (600, 128, 4, 2, 96), 1, (95, 96, 97, 98, 99)),
+    # groups of ~350 rows: three tiles of 128, 128 and the rest
+    ("row_tiles_350_bf16", (700, 128, 4, 2, 64), 1, (115, 116, 117, 118, 119)),
+    # groups of 161..192 rows: two tiles of 96 + the rest
+    ("row_tiles_180_bf16", (360, 128, 4, 2, 64), 1, (105, 106, 107, 108, 109)),
 ]
 
 
