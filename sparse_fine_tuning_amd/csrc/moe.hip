@@ -52,8 +52,15 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     if (e < E) {
       float v;
       if (nparts > 1) {
-        v = parts[int64_t(t) * E + e];
-        for (int q = 1; q < nparts; ++q) v += parts[(int64_t(q) * T + t) * E + e];
+        // the parts' loads are issued together, then added in part order
+        float pv[kMaxRouterParts];
+#pragma unroll
+        for (int q = 0; q < kMaxRouterParts; ++q)
+          pv[q] = q < nparts ? parts[(int64_t(q) * T + t) * E + e] : 0.f;
+        v = pv[0];
+#pragma unroll
+        for (int q = 1; q < kMaxRouterParts; ++q)
+          if (q < nparts) v += pv[q];
         logits[int64_t(t) * E + e] = v;
       } else {
         v = lt[e];
@@ -211,6 +218,7 @@ __global__ __launch_bounds__(kSortChunk) void expert_place_kernel(const int32_t*
   // 1024 experts at a time (E <= 1024)
   int total = 0, before = 0;
   if (tid < E) {
+#pragma unroll 8
     for (int b = 0; b < nchunk; ++b) {
       const int c = cnt[int64_t(b) * E + tid];
       total += c;
@@ -898,6 +906,7 @@ static inline unsigned mtiles_bound(const usaf_moe_shape& s) {
 // into st.logits) or, with nparts == 1, the logits themselves.
 static usaf_status route_impl(const usaf_moe_shape& s, const float* parts, int nparts,
                               const usaf_moe_state& st, hipStream_t stream) {
+  if (nparts < 1 || nparts > kMaxRouterParts) return USAF_ERR_INVALID_ARG;
   const int S = s.T * s.K;
   timer_begin(USAF_K_ROUTE, stream);
   const dim3 tg(unsigned(ceil_div(s.T, 4)));

@@ -78,10 +78,11 @@ namespace usaf {
 usaf_status mfma_router(const usaf_moe_shape& s, const uint16_t* X, const float* Wr, float* parts,
                         int nparts, hipStream_t st);
 // Split-K factor of the router GEMM (partial sums [nparts][T][E]).
+constexpr int kMaxRouterParts = 8;
 inline int mfma_router_splits(const usaf_moe_shape& s) {
   const int tiles = ((s.T + 127) / 128) * ((s.E + 127) / 128);
   int ks = 1;
-  while (ks < 8 && tiles * ks < 256 && s.H / (64 * ks * 2) >= 1) ks *= 2;
+  while (ks < kMaxRouterParts && tiles * ks < 256 && s.H / (64 * ks * 2) >= 1) ks *= 2;
   return ks;
 }
 usaf_status mfma_gate_up(const usaf_moe_shape& s, const uint16_t* X, const uint16_t* Wgu,
