@@ -692,6 +692,81 @@ __global__ __launch_bounds__(256) void dwr_kernel(const float* __restrict__ dl,
   }
 }
 
+// bf16 form of dwr_kernel for H % 8 == 0: a block takes 512 columns of one
+// expert, each lane 8 columns (one 16-byte load per slot), and its four
+// waves take every fourth slot of the expert, 8 slots' loads in flight.  The
+// four partial sums are added in wave order, so the result is deterministic.
+__global__ __launch_bounds__(256) void dwr_bf16_kernel(const float* __restrict__ dl,
+                                                       const bf16_t* __restrict__ X,
+                                                       const int32_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ perm, int H,
+                                                       int K, float* __restrict__ dWr,
+                                                       int32_t* __restrict__ nonfinite) {
+  __shared__ int tok[1024];
+  __shared__ float dls[1024];
+  __shared__ float part[3][512];
+  const int e = blockIdx.x, lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int h = 512 * blockIdx.y + 8 * lane;
+  const bool live = h < H;
+  const int p0 = offsets[e], p1 = offsets[e + 1];
+  float acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+  for (int w0 = p0; w0 < p1; w0 += 1024) {
+    const int wn = min(1024, p1 - w0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < wn; i += blockDim.x) {
+      const int s = perm[w0 + i];
+      tok[i] = s / K;
+      dls[i] = dl[s];
+    }
+    __syncthreads();
+    if (!live) continue;
+    int i = wid;
+    for (; i + 28 < wn; i += 32) {
+      uint4 xv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        xv[u] = *reinterpret_cast<const uint4*>(X + int64_t(tok[i + 4 * u]) * H + h);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float d = dls[i + 4 * u];
+        const uint32_t wv[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[2 * c] = fmaf(d, __uint_as_float(wv[c] << 16), acc[2 * c]);
+          acc[2 * c + 1] = fmaf(d, __uint_as_float(wv[c] & 0xffff0000u), acc[2 * c + 1]);
+        }
+      }
+    }
+    for (; i < wn; i += 4) {
+      const uint4 x = *reinterpret_cast<const uint4*>(X + int64_t(tok[i]) * H + h);
+      const float d = dls[i];
+      const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[2 * c] = fmaf(d, __uint_as_float(wv[c] << 16), acc[2 * c]);
+        acc[2 * c + 1] = fmaf(d, __uint_as_float(wv[c] & 0xffff0000u), acc[2 * c + 1]);
+      }
+    }
+  }
+  if (wid > 0) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) part[wid - 1][8 * lane + c] = acc[c];
+  }
+  __syncthreads();
+  if (wid == 0 && live) {
+    int bad = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float v = ((acc[c] + part[0][8 * lane + c]) + part[1][8 * lane + c]) + part[2][8 * lane + c];
+      dWr[int64_t(e) * H + h + c] = v;
+      bad += !finite_f(v);
+    }
+    if (nonfinite && bad) atomicAdd(nonfinite, bad);
+  }
+}
+
 // dX[t, :] = sum_j v[slot t*K+j] + sum_j dlogits[t, j] * Wr'[e_j, :]; four
 // columns per thread.
 template <class T>
@@ -1014,9 +1089,20 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
   hipLaunchKernelGGL(dw_router_kernel, dim3(unsigned(ceil_div(s.T, 256 / s.K))), dim3(256), 0,
                      stream, dwpart, NT, st.topk_w, st.slot_pos, s.T, s.K, st.dw, dl);
   USAF_LAUNCH_CHECK();
-  hipLaunchKernelGGL(dwr_kernel<T>, dim3(unsigned(s.E), unsigned(ceil_div(s.H, 512))), dim3(256),
-                     0, stream, dl, X, st.offsets, st.perm, s.H, s.K, dWr,
-                     idx ? nonfinite : nullptr);
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (s.H % 8 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0)
+      hipLaunchKernelGGL(dwr_bf16_kernel, dim3(unsigned(s.E), unsigned(ceil_div(s.H, 512))), dim3(256),
+                         0, stream, dl, X, st.offsets, st.perm, s.H, s.K, dWr,
+                         idx ? nonfinite : nullptr);
+    else
+      hipLaunchKernelGGL(dwr_kernel<T>, dim3(unsigned(s.E), unsigned(ceil_div(s.H, 512))), dim3(256),
+                         0, stream, dl, X, st.offsets, st.perm, s.H, s.K, dWr,
+                         idx ? nonfinite : nullptr);
+  } else {
+    hipLaunchKernelGGL(dwr_kernel<T>, dim3(unsigned(s.E), unsigned(ceil_div(s.H, 512))), dim3(256),
+                       0, stream, dl, X, st.offsets, st.perm, s.H, s.K, dWr,
+                       idx ? nonfinite : nullptr);
+  }
   timer_end(USAF_K_ROUTER_BWD, stream);
   USAF_LAUNCH_CHECK();
   if (dX) {
