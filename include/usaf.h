@@ -158,8 +158,9 @@ USAF_API usaf_status usaf_masked_plan(const usaf_moe_shape *shape, const uint32_
  * the plan is rebuilt inside ws on every call.  Ignored in dense mode.
  * nonfinite (nullable, device int32): incremented when any dW value or dWr
  * is NaN/Inf (sparse mode); the caller zeroes it before the step.
+ * An empty list (nnz == 0, idx may be NULL) computes everything but dW.
  * ws: USAF_WS_BACKWARD bytes.  Errors: INVALID_ARG for nnz < 0, nnz > N, a
- * null required pointer, or idx == NULL with nnz != N. */
+ * null required pointer, or idx == NULL with 0 < nnz < N. */
 USAF_API usaf_status usaf_masked_backward(const usaf_moe_shape *shape, const void *X, const float *Wr,
                                  const void *Wflat, const usaf_moe_state *state,
                                  const void *dY, const uint32_t *idx, int64_t nnz,

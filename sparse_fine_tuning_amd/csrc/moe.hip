@@ -1068,6 +1068,8 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
                                  int64_t nnz, const void* plan, float* dW, float* dWr, T* dX,
                                  int32_t* nonfinite, char* ws, hipStream_t stream) {
   const WsBackward L = ws_backward(s);
+  // sparse mode: a list of nnz entries, possibly empty (idx may then be NULL)
+  const bool sparse = idx != nullptr || nnz == 0;
   T* vbuf = reinterpret_cast<T*>(ws + L.vbuf);
   float* dwpart = reinterpret_cast<float*>(ws + L.dwpart);
   float* dl = reinterpret_cast<float*>(ws + L.dl);
@@ -1093,15 +1095,15 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
     if (s.H % 8 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0)
       hipLaunchKernelGGL(dwr_bf16_kernel, dim3(unsigned(s.E), unsigned(ceil_div(s.H, 512))), dim3(256),
                          0, stream, dl, X, st.offsets, st.perm, s.H, s.K, dWr,
-                         idx ? nonfinite : nullptr);
+                         sparse ? nonfinite : nullptr);
     else
       hipLaunchKernelGGL(dwr_kernel<T>, dim3(unsigned(s.E), unsigned(ceil_div(s.H, 512))), dim3(256),
                          0, stream, dl, X, st.offsets, st.perm, s.H, s.K, dWr,
-                         idx ? nonfinite : nullptr);
+                         sparse ? nonfinite : nullptr);
   } else {
     hipLaunchKernelGGL(dwr_kernel<T>, dim3(unsigned(s.E), unsigned(ceil_div(s.H, 512))), dim3(256),
                        0, stream, dl, X, st.offsets, st.perm, s.H, s.K, dWr,
-                       idx ? nonfinite : nullptr);
+                       sparse ? nonfinite : nullptr);
   }
   timer_end(USAF_K_ROUTER_BWD, stream);
   USAF_LAUNCH_CHECK();
@@ -1119,7 +1121,7 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
     USAF_LAUNCH_CHECK();
   }
   const int64_t ngu = int64_t(s.E) * 2 * s.I * s.H;
-  if (idx) {
+  if (sparse) {
     if constexpr (kMfma) {
       return masked_dw_bf16(s, idx, nnz, X, dY, dgu, a, st.topk_w, st.offsets, st.perm, dW,
                             nonfinite, plan, ws + L.seg, stream);
@@ -1206,7 +1208,7 @@ extern "C" usaf_status usaf_masked_backward(const usaf_moe_shape* shape, const v
   if (!X || !Wr || !Wflat || !dY || !dWr || !state_ok(state, true)) return USAF_ERR_INVALID_ARG;
   const int64_t N = n_weights(*shape);
   if (nnz < 0 || nnz > N) return USAF_ERR_INVALID_ARG;
-  if (!idx && nnz != N) return USAF_ERR_INVALID_ARG;
+  if (!idx && nnz != N && nnz != 0) return USAF_ERR_INVALID_ARG;
   if (nnz > 0 && !dW) return USAF_ERR_INVALID_ARG;
   if (!ws || ws_bytes < ws_backward(*shape).total) return USAF_ERR_WORKSPACE;
   if (shape->act == USAF_BF16)
