@@ -243,10 +243,12 @@ __global__ __launch_bounds__(256) void masked_group_totals_kernel(const uint32_t
 }
 
 // The tensor-wide entry target of a tile: the smallest t <= cap with
-// sum over groups of max(ceil(R/RB), ceil(n_g / t)) <= cus (or cap when even
-// cap leaves more tiles than CUs).  A light list then takes one tile per
-// row range and expert while a heavy expert's entries are spread over the
-// CUs the light ones leave idle.  One block.
+// sum over groups of max(ceil(R/RB), ceil(n_g / t)) <= rounds * cus, where
+// rounds is the number of CU rounds that full tiles (t = cap) take.  A light
+// list then takes one tile per row range and expert while a heavy expert's
+// entries are spread over the CUs the light ones leave idle, and a list too
+// large for one round fills its last round instead of leaving it part
+// empty.  Either way t < cap adds fewer than cus tiles.  One block.
 __global__ __launch_bounds__(256) void masked_target_kernel(const int* __restrict__ ng, int G, int R,
                                                             int RB, int cap, int cus,
                                                             int* __restrict__ target) {
@@ -266,14 +268,15 @@ __global__ __launch_bounds__(256) void masked_target_kernel(const int* __restric
     __syncthreads();
     return (red[0] + red[1]) + (red[2] + red[3]);
   };
-  int lo = 1, hi = cap;  // invariant: tiles_at(hi) <= cus, or hi == cap
-  if (tiles_at(cap) > cus) {
-    lo = cap;
-  } else {
-    while (lo < hi) {
-      const int mid = lo + (hi - lo) / 2;
-      if (tiles_at(mid) <= cus) hi = mid; else lo = mid + 1;
-    }
+  // whole rounds of the CUs: when even full tiles need more than one round,
+  // the smallest target that still fits the same number of rounds spreads
+  // the entries evenly instead of leaving a part-filled last round
+  const int rounds = max(1, (tiles_at(cap) + cus - 1) / cus);
+  const int bound = rounds * cus;
+  int lo = 1, hi = cap;  // invariant: tiles_at(hi) <= bound
+  while (lo < hi) {
+    const int mid = lo + (hi - lo) / 2;
+    if (tiles_at(mid) <= bound) hi = mid; else lo = mid + 1;
   }
   if (tid == 0) *target = lo;
 }
@@ -645,8 +648,8 @@ static void col_tiles(int C, int& CB, int& nct) {
 // tiles hold more than cap entries together) and at most one quantile cut
 // per multiple of n/nt, nt <= ceil(R/RB) + ceil(n/cap) of them, so at most
 // 2 ceil(R/RB) + 3 ceil(n/cap) + 2 tiles; summed over the groups with
-// sum ceil(n/cap) <= nnz/cap + groups; a target below cap adds at most
-// kMaxCUs (it is chosen so that the quantile tiles number at most the CUs).
+// sum ceil(n/cap) <= nnz/cap + groups; a target below cap adds fewer than
+// cus <= kMaxCUs (the quantile tiles fit the rounds that full tiles take).
 static int64_t tile_bound(const usaf_moe_shape& s, int R, int C, int64_t nnz, int RB, int cap) {
   int CB, nct;
   col_tiles(C, CB, nct);
