@@ -636,7 +636,7 @@ usaf_status mfma_router(const usaf_moe_shape& s, const bf16_t* X, const float* W
 constexpr int kFwdBM = 160, kFwdBN = 256, kFwdNS = 3;  // gate_up, down, dA, dX: 156 KiB LDS
 constexpr int kFwdWM = 2, kFwdWN = 4;                  // 8 waves: 2 per SIMD
 constexpr int kFwdBK = 64;                             // contraction depth of a stage
-constexpr int kDaWN = 4;                               // dA: 8 waves of 64 x 64
+constexpr int kDaWN = 4;                               // dA: 8 waves of 64 columns
 constexpr int kDwBM = 256, kDwBN = 256, kDwNS = 2;     // dense dW: 128 KiB LDS
 
 // Groups of at least kBigRows rows on average (few large experts) take
@@ -644,7 +644,6 @@ constexpr int kDwBM = 256, kDwBN = 256, kDwNS = 2;     // dense dW: 128 KiB LDS
 constexpr int kBigRows = 512;
 constexpr int kBigBM = 256, kBigNS = 2, kBigBK = 64;  // 2 x 64 KiB LDS stages
 constexpr int kBigWM = 2, kBigWN = 4;    // 8 waves of 128 x 64
-constexpr int kBigDaWN = 2;               // dA on 256-row tiles: 8 waves of 64 x 128
 static bool big_groups(const usaf_moe_shape& s) {
   return int64_t(s.T) * s.K >= int64_t(kBigRows) * s.E;
 }
@@ -673,20 +672,15 @@ usaf_status mfma_down(const usaf_moe_shape& s, const bf16_t* a, const bf16_t* Wd
   return launch_fwd<g2::MDown>(s, NT, st, USAF_K_DOWN, a, Wd, offsets, ybuf, s.H, s.E, s.I, NT);
 }
 
-int mfma_dw_partials(const usaf_moe_shape& s) {
-  return (big_groups(s) ? kBigDaWN : kDaWN) * int(ceil_div(s.I, kFwdBN));
-}
+int mfma_dw_partials(const usaf_moe_shape& s) { return kDaWN * int(ceil_div(s.I, kFwdBN)); }
 
 usaf_status mfma_da(const usaf_moe_shape& s, const bf16_t* dY, const bf16_t* Wd,
                     const int32_t* offsets, const int32_t* perm, const float* topk_w,
                     const bf16_t* gu, const bf16_t* a, bf16_t* dgu, float* dwpart,
                     hipStream_t st) {
+  // dA keeps the 160-row tiles for large groups too: its epilogue's g|u
+  // loads spill on 256-row tiles (measured 13% slower at the Mixtral shape)
   const int NT = int(ceil_div(s.I, kFwdBN));
-  if (big_groups(s))  // 8 waves of 64 x 128 on 256-row tiles
-    return launch_persistent(g2::MDa<kBigBM, kFwdBN, kBigNS, 4, kBigDaWN, kBigBK>{dY, Wd, offsets, perm, topk_w, gu,
-                                                                          a, dgu, dwpart, s.H, s.E, s.K,
-                                                                          s.I, NT, kBigDaWN * NT},
-                             grouped_tiles_bound(s, NT, kBigBM), st, USAF_K_DA);
   return launch_persistent(g2::MDa<kFwdBM, kFwdBN, kFwdNS, 2, kDaWN, kFwdBK>{dY, Wd, offsets, perm, topk_w, gu, a, dgu, dwpart, s.H,
                                            s.E, s.K, s.I, NT, kDaWN * NT},
                    grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DA);
