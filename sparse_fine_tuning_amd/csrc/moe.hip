@@ -587,11 +587,22 @@ __global__ __launch_bounds__(256) void combine_y_kernel(const T* __restrict__ yb
 // Per slot: dw[s] = sum of the dA tiles' partial dot products (fixed order).
 // A block covers whole tokens (floor(256/K) of them); per token, dlogits of
 // the chosen experts: w_j (dw_j - sum_m w_m dw_m), the sum in fixed m order.
+// With wrb set it also writes bf16(Wr) [E*H] (the rounded router rows the
+// dX combine multiplies), four elements per thread over the grid.
 __global__ __launch_bounds__(256) void dw_router_kernel(const float* __restrict__ dwpart, int NT,
                                                         const float* __restrict__ topk_w,
                                                         const int32_t* __restrict__ slot_pos,
                                                         int T, int K, float* __restrict__ dw,
-                                                        float* __restrict__ dl) {
+                                                        float* __restrict__ dl,
+                                                        const float* __restrict__ Wr,
+                                                        bf16_t* __restrict__ wrb, int64_t EH) {
+  if (wrb) {
+    for (int64_t i = 4 * (int64_t(blockIdx.x) * 256 + threadIdx.x); i < EH;
+         i += 4 * int64_t(gridDim.x) * 256) {
+      const uint32_t lo = f2bf2(Wr[i], Wr[i + 1]), hi = f2bf2(Wr[i + 2], Wr[i + 3]);
+      *reinterpret_cast<uint2*>(wrb + i) = make_uint2(lo, hi);
+    }
+  }
   __shared__ float swd[256];
   const int tpb = 256 / K;
   const int lt = threadIdx.x / K, j = threadIdx.x - lt * K;
@@ -601,6 +612,7 @@ __global__ __launch_bounds__(256) void dw_router_kernel(const float* __restrict_
   float d = 0.f, wj = 0.f;
   if (live) {
     const int64_t p = slot_pos[s];
+#pragma unroll 4
     for (int nt = 0; nt < NT; ++nt) d += dwpart[p * NT + nt];
     dw[s] = d;
     wj = topk_w[s];
@@ -773,11 +785,11 @@ template <class T>
 __global__ __launch_bounds__(256) void combine_dx_kernel(const T* __restrict__ vbuf,
                                                          const float* __restrict__ dl,
                                                          const int32_t* __restrict__ ids,
-                                                         const float* __restrict__ Wr,
+                                                         const T* __restrict__ Wr,
                                                          const int32_t* __restrict__ slot_pos,
                                                          int H, int K, T* __restrict__ dX) {
   __shared__ const T* vrows[64];
-  __shared__ const float* wrows[64];
+  __shared__ const T* wrows[64];
   __shared__ float dls[64];
   const int t = blockIdx.x;
   if (threadIdx.x < K) {
@@ -797,9 +809,7 @@ __global__ __launch_bounds__(256) void combine_dx_kernel(const T* __restrict__ v
 #pragma unroll 8
     for (int j = 0; j < K; ++j) {
       const float d = dls[j];
-      float4 w = *reinterpret_cast<const float4*>(wrows[j] + h);
-      w.x = Act<T>::round(w.x); w.y = Act<T>::round(w.y);
-      w.z = Act<T>::round(w.z); w.w = Act<T>::round(w.w);
+      const float4 w = load4<T>(wrows[j] + h);
       acc.x = fmaf(d, w.x, acc.x);
       acc.y = fmaf(d, w.y, acc.y);
       acc.z = fmaf(d, w.z, acc.z);
@@ -1088,8 +1098,12 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
     USAF_TRY(launch_fma(da, dim3(mtiles_bound(s), unsigned(NT)), stream, USAF_K_DA));
   }
   timer_begin(USAF_K_ROUTER_BWD, stream);
+  // bf16 layers: the combine reads bf16(Wr), written here once per call
+  bf16_t* wrb = nullptr;
+  if constexpr (kMfma) wrb = reinterpret_cast<bf16_t*>(ws + L.wrb);
   hipLaunchKernelGGL(dw_router_kernel, dim3(unsigned(ceil_div(s.T, 256 / s.K))), dim3(256), 0,
-                     stream, dwpart, NT, st.topk_w, st.slot_pos, s.T, s.K, st.dw, dl);
+                     stream, dwpart, NT, st.topk_w, st.slot_pos, s.T, s.K, st.dw, dl, Wr, wrb,
+                     int64_t(s.E) * s.H);
   USAF_LAUNCH_CHECK();
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (s.H % 8 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0)
@@ -1115,8 +1129,10 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
       USAF_TRY(launch_fma(dx, dim3(mtiles_bound(s), unsigned(s.H / 64)), stream, USAF_K_DX));
     }
     timer_begin(USAF_K_COMBINE_DX, stream);
+    const T* wr_act;
+    if constexpr (kMfma) wr_act = wrb; else wr_act = Wr;
     hipLaunchKernelGGL(combine_dx_kernel<T>, dim3(unsigned(s.T)), dim3(256), 0, stream, vbuf, dl,
-                       st.topk_ids, Wr, st.slot_pos, s.H, s.K, dX);
+                       st.topk_ids, wr_act, st.slot_pos, s.H, s.K, dX);
     timer_end(USAF_K_COMBINE_DX, stream);
     USAF_LAUNCH_CHECK();
   }

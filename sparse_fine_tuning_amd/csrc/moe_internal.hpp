@@ -56,7 +56,7 @@ inline WsForward ws_forward(const usaf_moe_shape& s) {
 // [S, NT] (NT = dA column tiles), dlogits of the chosen experts [S], and
 // a masked-gradient plan built per call when the caller keeps none.
 struct WsBackward {
-  size_t vbuf, dwpart, dl, seg, total;
+  size_t vbuf, dwpart, dl, seg, wrb, total;
   int nt;
 };
 inline WsBackward ws_backward(const usaf_moe_shape& s) {
@@ -67,7 +67,8 @@ inline WsBackward ws_backward(const usaf_moe_shape& s) {
   L.dwpart = align256(S * s.H * 4);
   L.dl = L.dwpart + align256(S * L.nt * 4);
   L.seg = L.dl + align256(S * 4);
-  L.total = L.seg + align256(size_t(masked_plan_bytes(s)));
+  L.wrb = L.seg + align256(size_t(masked_plan_bytes(s)));  // bf16(Wr) [E, H] (bf16 layers)
+  L.total = L.wrb + align256(size_t(s.E) * s.H * 2);
   return L;
 }
 
