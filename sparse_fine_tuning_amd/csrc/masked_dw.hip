@@ -328,6 +328,13 @@ __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __res
     int carry = 0;               // exclusive prefix of the chunk's first row
     int n = 0;                   // tiles with entries so far
     int ncut = 0;                // cuts so far
+    // the first multiple of total / nt beyond the open tile's start (it
+    // changes only at a cut)
+    auto next_quant = [&](int ox) {
+      const int64_t k = int64_t(ox) * nt / total + 1;
+      return (k * total + nt - 1) / nt;
+    };
+    int64_t quant = next_quant(0);
     for (int s0 = 0; s0 < R; s0 += 64 * kSpan) {
       int cnts[kSpan];
 #pragma unroll
@@ -354,10 +361,7 @@ __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __res
         const int excl = carry + incl - cnt;
         // at most one cut per row, taken in row order
         while (true) {
-          // the first multiple of total / nt beyond the open tile's start;
-          // a cut there only once the rows after it fit the tiles left
-          const int64_t k = int64_t(open_x) * nt / total + 1;
-          const int64_t quant = (k * total + nt - 1) / nt;
+          // a cut at the quantile only once the rows after it fit the tiles left
           const bool cut = r < R && r > open_r &&
                            (r - open_r >= RB || excl + cnt - open_x > cap ||
                             (int64_t(excl) >= quant && int64_t(R - r) <= int64_t(nt - ncut - 1) * RB));
@@ -373,6 +377,7 @@ __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __res
           }
           open_r = cr;
           open_x = cx;
+          quant = next_quant(open_x);
           ++ncut;
         }
         carry += __shfl(incl, 63, 64);
