@@ -163,6 +163,28 @@ def split_flat(f, shape: Shape):
 # ----------------------------------------------------------------------------
 # a1: int4 -> resident bf16
 # ----------------------------------------------------------------------------
+def dequant_affine(q_packed: np.ndarray, scale_bits: np.ndarray, zero_bits: np.ndarray,
+                   group: int = 128) -> np.ndarray:
+    """The pages' own 4-bit storage (usaf README, "how it works": experts read
+    in 4-bit HQQ format; its quantisation recipe uses group size 128): an
+    affine code per weight, one fp16 scale s and one fp16 zero z per
+    ``group`` consecutive input-dim elements, w = (q - z) * s.  The pages give
+    no arithmetic precision; the reading taken here: q - z and the product
+    are each formed in fp32 (one rounding each), then rounded once to bf16.
+    q is an unsigned nibble (0..15), element 2i in the low nibble of byte i.
+    Returns float64 values."""
+    q_packed = np.asarray(q_packed, dtype=np.uint8)
+    rows, half = q_packed.shape
+    codes = np.empty((rows, 2 * half), dtype=np.float32)
+    codes[:, 0::2] = q_packed & 0x0F
+    codes[:, 1::2] = q_packed >> 4
+    s = np.repeat(np.asarray(scale_bits, np.uint16).view(np.float16).astype(np.float32), group, axis=1)
+    z = np.repeat(np.asarray(zero_bits, np.uint16).view(np.float16).astype(np.float32), group, axis=1)
+    with np.errstate(over="ignore", invalid="ignore"):
+        prod = (codes - z) * s          # float32 operations, each rounded once
+    return bf16_rne(prod.astype(np.float64))
+
+
 def dequant_int4(q_packed: np.ndarray, scale_bits: np.ndarray, group: int = 64) -> np.ndarray:
     """Resident dequantisation (usaf README, "how it works": caching bullet;
     quantisation recipe), with the storage taken here: symmetric int4 codes,

@@ -99,6 +99,73 @@ def test_dequant_nibble_order_and_groups():
     assert got[0, 64] == 0.5 and got[0, 65] == 3.5
 
 
+def pack_unsigned(codes):
+    c = np.asarray(codes, np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def test_affine_dequant_with_zero_8_is_the_symmetric_format():
+    """Offset-binary codes u = c + 8 with zero 8 give (u - 8) s = c s: the
+    affine dequant must equal the symmetric int4 dequant (pinned above) with
+    the same scale in both of its 64-wide halves."""
+    rng = np.random.default_rng(31)
+    rows, cols = 6, 256
+    c = rng.integers(-8, 8, size=(rows, cols))
+    sc = (10.0 ** rng.uniform(-6, 3, size=(rows, cols // 128)) * rng.choice([-1, 1], (rows, cols // 128))).astype(np.float16)
+    nib = (c & 0xF).astype(np.uint8)
+    sym = O.dequant_int4((nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8),
+                         np.repeat(sc, 2, axis=1).view(np.uint16), group=64)
+    zero = np.full(sc.shape, 8.0, np.float16)
+    aff = O.dequant_affine(pack_unsigned(c + 8), sc.view(np.uint16), zero.view(np.uint16), group=128)
+    assert np.array_equal(aff, sym)
+
+
+def test_affine_dequant_exact_cases_by_hand():
+    # zero 2.5, scale 2^-6: (q - 2.5) / 64 is exact in fp32 and in bf16
+    q = np.tile(np.arange(16), (1, 8))  # 128 columns = one group
+    got = O.dequant_affine(pack_unsigned(q), np.array([[2.0 ** -6]], np.float16).view(np.uint16),
+                           np.array([[2.5]], np.float16).view(np.uint16))
+    assert np.array_equal(got[0, :16], (np.arange(16) - 2.5) / 64.0)
+    # q == zero gives exactly 0 whatever the scale
+    got = O.dequant_affine(pack_unsigned(np.full((1, 128), 7)), np.array([[65504.0]], np.float16).view(np.uint16),
+                           np.array([[7.0]], np.float16).view(np.uint16))
+    assert np.all(got == 0.0)
+
+
+def test_affine_dequant_rounds_in_fp32_first():
+    """The reading's two fp32 roundings, worked by hand: q = 1, z = -2^-24,
+    s = 1 + 2^-8.  In fp32, 1 + 2^-24 is a tie that rounds to 1; 1 * s = 1 + 2^-8
+    is then a bf16 tie that rounds to even: 1.  Exact arithmetic would give
+    1 + 2^-8 + 2^-24 + 2^-32, above the tie: 1 + 2^-7."""
+    codes = np.ones((1, 128), np.uint8)
+    got = O.dequant_affine(pack_unsigned(codes), np.array([[1 + 2.0 ** -8]], np.float16).view(np.uint16),
+                           np.array([[-(2.0 ** -24)]], np.float16).view(np.uint16))
+    assert np.all(got == 1.0)
+    assert float(np.float16(-(2.0 ** -24))) == -(2.0 ** -24)  # the smallest fp16 subnormal
+
+
+def test_affine_dequant_matches_torch_fp32_then_bf16():
+    rng = np.random.default_rng(33)
+    rows, cols = 16, 256
+    q = rng.integers(0, 16, size=(rows, cols))
+    sc = (10.0 ** rng.uniform(-7, 4, size=(rows, 2))).astype(np.float16)
+    zr = rng.uniform(-2, 17, size=(rows, 2)).astype(np.float16)
+    got = O.dequant_affine(pack_unsigned(q), sc.view(np.uint16), zr.view(np.uint16))
+    qt = torch.from_numpy(q.astype(np.float32))
+    st = torch.from_numpy(np.repeat(sc.astype(np.float32), 128, axis=1))
+    zt = torch.from_numpy(np.repeat(zr.astype(np.float32), 128, axis=1))
+    want = ((qt - zt) * st).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, want)
+
+
+def test_affine_roundtrip_of_synthetic_quantizer():
+    w = synth.normal((8, 256), 0.02, 9)
+    q, s, z = synth.quantize_affine_int4(w, 128)
+    back = O.dequant_affine(q, s, z, 128)
+    scale = np.repeat(s.view(np.float16).astype(np.float64), 128, axis=1)
+    assert np.all(np.abs(back - w) <= 0.55 * scale + 2.0 ** -8 * np.abs(w).max())
+
+
 def test_dequant_roundtrip_of_synthetic_quantizer():
     w = synth.normal((8, 128), 0.02, 7)
     q, s = synth.quantize_int4_g64(w)

@@ -106,6 +106,28 @@ def random_mask(N: int, k: int, seed: int) -> np.ndarray:
     return chosen.astype(np.uint32)
 
 
+def quantize_affine_int4(W2d: np.ndarray, group: int = 128):
+    """Min-max affine 4-bit quantiser used only to build the affine-dequant
+    input: per group of ``group`` consecutive input-dim elements,
+    scale = fp16((max - min) / 15) (1 for a constant group), zero =
+    fp16(-min / scale), code = clip(rint(w / scale + zero), 0, 15); element 2i
+    in the low nibble of byte i.  Returns (q_packed uint8 [rows, cols/2],
+    scale_bits, zero_bits uint16 [rows, cols/group])."""
+    rows, cols = W2d.shape
+    if cols % group:
+        raise ValueError("cols must be a multiple of the group size")
+    g = W2d.reshape(rows, cols // group, group).astype(np.float32)
+    lo, hi = g.min(axis=2), g.max(axis=2)
+    span = (hi - lo) / np.float32(15.0)
+    scale16 = np.where(span > 0, span, np.float32(1.0)).astype(np.float16)
+    s = scale16.astype(np.float32)
+    zero16 = (-lo / s).astype(np.float16)
+    z = zero16.astype(np.float32)
+    q = np.clip(np.rint(g / s[..., None] + z[..., None]), 0, 15).astype(np.uint8).reshape(rows, cols)
+    packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scale16.view(np.uint16), zero16.view(np.uint16)
+
+
 def quantize_int4_g64(W2d: np.ndarray, group: int = 64):
     """Symmetric int4 quantiser used only to build the resident-dequant input.
 
