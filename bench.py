@@ -177,6 +177,26 @@ def rigl_scan(capi, synth, layer_mod, d, idx, dims, scan_tokens, repeats=2):
     N = lay.shape.N
     lay.W = torch.empty(N, dtype=torch.bfloat16, device=dev)
     ngu = lay.shape.n_gate_up
+    # the pages' own affine group-128 storage of the same weights, timed on
+    # random codes (the scan below uses the symmetric g64 copy)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(41)
+    qa = [torch.randint(0, 256, (r_, c_ // 2), dtype=torch.uint8, device=dev, generator=gen)
+          for r_, c_ in ((rows_gu, H), (rows_d, I))]
+    sa = [(torch.rand(r_, c_ // 128, device=dev, generator=gen) * 1e-3).to(torch.float16).view(torch.int16)
+          for r_, c_ in ((rows_gu, H), (rows_d, I))]
+    za = [(torch.rand(r_, c_ // 128, device=dev, generator=gen) * 15).to(torch.float16).view(torch.int16)
+          for r_, c_ in ((rows_gu, H), (rows_d, I))]
+    for rep in range(2):
+        torch.cuda.synchronize()
+        capi.timer_arm(capi.K_DEQUANT, 4)
+        capi.dequant_affine(qa[0], sa[0], za[0], rows_gu, H, 128, lay.W[:ngu])
+        capi.dequant_affine(qa[1], sa[1], za[1], rows_d, I, 128, lay.W[ngu:])
+        torch.cuda.synchronize()
+        dqa_ms = capi.timer_read(4)
+        capi.timer_arm(-1)
+    dqa_bytes = sum(x.numel() for x in qa) + 4 * sum(x.numel() for x in sa) + N * 2
+    del qa, sa, za
     # dequant once into the resident bf16 working copy (timed)
     for rep in range(2):
         torch.cuda.synchronize()
@@ -206,6 +226,8 @@ def rigl_scan(capi, synth, layer_mod, d, idx, dims, scan_tokens, repeats=2):
         log(f"rigl: scan {rep} {dt:.2f} ms")
     return dict(rigl_scan_ms=float(np.median(times)), scan_tokens=Ts,
                 dequant_ms=float(sum(dq_ms)), dequant_GBps=dq_bytes / (sum(dq_ms) * 1e-3) / 1e9,
+                dequant_affine_g128_ms=float(sum(dqa_ms)),
+                dequant_affine_g128_GBps=dqa_bytes / (sum(dqa_ms) * 1e-3) / 1e9,
                 turnover_applied=float(stats[1]) / k, turnover_topk_vs_old=float(stats[2]) / k,
                 rigl_k=int(k), rigl_r=int(r))
 

@@ -241,6 +241,20 @@ USAF_API usaf_status usaf_dequant_resident(const uint8_t *q, const uint16_t *sca
                                   int64_t cols, int32_t group, void *out_bf16,
                                   hipStream_t stream);
 
+/* The pages' own 4-bit storage (README "how it works": experts read in 4-bit
+ * HQQ format; its quantisation recipe quantises with group size 128),
+ * dequantised once into resident bf16.  Affine codes: q [rows, cols/2]
+ * bytes, element 2i in the low nibble of byte i, unsigned in [0, 15];
+ * scale_f16 and zero_f16 [rows, cols/group] fp16 bit patterns; out_bf16
+ * [rows, cols] = round_to_nearest_even_bf16(fp32(fp32(q - zero) * scale)):
+ * the difference and the product are each rounded once in fp32.
+ * Supported: group 64 or 128, cols % group == 0, q 4-byte and out 16-byte
+ * aligned.  Errors: INVALID_ARG for rows or cols < 0 or null pointers with a
+ * non-empty shape; UNSUPPORTED otherwise. */
+USAF_API usaf_status usaf_dequant_affine(const uint8_t *q, const uint16_t *scale_f16,
+                                const uint16_t *zero_f16, int64_t rows, int64_t cols,
+                                int32_t group, void *out_bf16, hipStream_t stream);
+
 /* ---- helpers of the step (not method steps of their own) -------------- */
 
 /* Regression loss of a layer output: loss = mean((Y - tgt)^2) over T*H

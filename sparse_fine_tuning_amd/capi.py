@@ -23,7 +23,8 @@ WS_FORWARD, WS_BACKWARD, WS_TOPK, WS_RIGL, WS_MASKED_PLAN = range(5)
 # Every symbol include/usaf.h declares.
 EXPORTS = (
     "usaf_workspace_size", "usaf_moe_forward", "usaf_masked_backward", "usaf_importance_topk",
-    "usaf_rigl_reselect", "usaf_sparse_adam", "usaf_dequant_resident", "usaf_mse_grad",
+    "usaf_rigl_reselect", "usaf_sparse_adam", "usaf_dequant_resident", "usaf_dequant_affine",
+    "usaf_mse_grad",
     "usaf_route", "usaf_status_string", "usaf_version", "usaf_timer_arm", "usaf_timer_read",
     "usaf_gather", "usaf_residual_add", "usaf_masked_plan",
 )
@@ -88,6 +89,7 @@ def _load():
                              C.c_double, C.c_double, vp, vp],
         "usaf_gather": [i32, vp, vp, i64, vp, vp],
         "usaf_dequant_resident": [vp, vp, i64, i64, i32, vp, vp],
+        "usaf_dequant_affine": [vp, vp, vp, i64, i64, i32, vp, vp],
         "usaf_mse_grad": [vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "usaf_route": [vp, vp, vp, vp],
         "usaf_residual_add": [i32, vp, vp, vp, i64, vp],
@@ -202,6 +204,12 @@ def sparse_adam(w_dtype, W, idx, n, g, m, v, step, lr, beta1, beta2, eps, skip=N
 def gather(w_dtype, W, idx, n, out, stream=None):
     _check(lib.usaf_gather(int(w_dtype), _p(W), _p(idx), int(n), _p(out), _stream(stream)),
            "usaf_gather")
+
+
+def dequant_affine(q, scale_f16, zero_f16, rows, cols, group, out_bf16, stream=None):
+    _check(lib.usaf_dequant_affine(_p(q), _p(scale_f16), _p(zero_f16), int(rows), int(cols),
+                                   int(group), _p(out_bf16), _stream(stream)),
+           "usaf_dequant_affine")
 
 
 def dequant_resident(q, scale_f16, rows, cols, group, out_bf16, stream=None):

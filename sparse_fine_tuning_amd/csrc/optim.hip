@@ -191,6 +191,54 @@ extern "C" usaf_status usaf_gather(int32_t w_dtype, const void* W, const uint32_
   return USAF_OK;
 }
 
+// Affine int4 -> bf16 (the HQQ-style storage): w = bf16((q - z) * s) with
+// q - z and the product each rounded once in fp32; q an unsigned nibble.
+// One thread per 8 outputs (one 32-bit word of codes); group % 8 == 0.
+__global__ __launch_bounds__(256) void dequant_affine_kernel(const uint32_t* __restrict__ q,
+                                                             const uint16_t* __restrict__ scale,
+                                                             const uint16_t* __restrict__ zero,
+                                                             int64_t rows, int64_t cols, int group,
+                                                             uint4* __restrict__ out) {
+  const int64_t wpr = cols / 8, gpr = cols / group;
+  const int wpg = group / 8;
+  const int64_t total = rows * wpr;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t row = i / wpr, wc = i - row * wpr;
+    const int64_t gi = row * gpr + wc / wpg;
+    const uint32_t word = q[i];
+    const float s = float(__builtin_bit_cast(_Float16, scale[gi]));
+    const float z = float(__builtin_bit_cast(_Float16, zero[gi]));
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float d0 = float((word >> (8 * j)) & 0xfu) - z;
+      const float d1 = float((word >> (8 * j + 4)) & 0xfu) - z;
+      o[j] = f2bf2(d0 * s, d1 * s);
+    }
+    out[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+extern "C" usaf_status usaf_dequant_affine(const uint8_t* q, const uint16_t* scale_f16,
+                                           const uint16_t* zero_f16, int64_t rows, int64_t cols,
+                                           int32_t group, void* out_bf16, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return USAF_ERR_INVALID_ARG;
+  if ((group != 64 && group != 128) || cols % group != 0) return USAF_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return USAF_OK;
+  if (!q || !scale_f16 || !zero_f16 || !out_bf16) return USAF_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(q) & 3) || (reinterpret_cast<uintptr_t>(out_bf16) & 15))
+    return USAF_ERR_UNSUPPORTED;
+  const int64_t words = rows * (cols / 8);
+  timer_begin(USAF_K_DEQUANT, stream);
+  hipLaunchKernelGGL(dequant_affine_kernel, dim3(grid_for(words)), dim3(256), 0, stream,
+                     reinterpret_cast<const uint32_t*>(q), scale_f16, zero_f16, rows, cols, group,
+                     static_cast<uint4*>(out_bf16));
+  timer_end(USAF_K_DEQUANT, stream);
+  USAF_LAUNCH_CHECK();
+  return USAF_OK;
+}
+
 extern "C" usaf_status usaf_dequant_resident(const uint8_t* q, const uint16_t* scale_f16,
                                              int64_t rows, int64_t cols, int32_t group,
                                              void* out_bf16, hipStream_t stream) {

@@ -122,6 +122,12 @@ def test_entry_points_refuse_bad_arguments_before_launch():
     assert L.usaf_dequant_resident(FAKE, FAKE, 4, 128, 128, FAKE, None) == 2
     assert L.usaf_dequant_resident(FAKE, FAKE, 4, 96, 64, FAKE, None) == 2
     assert L.usaf_dequant_resident(FAKE, FAKE, -1, 128, 64, FAKE, None) == 1
+    # affine dequant: group not 64 / 128, cols % group, negative rows, null zero
+    assert L.usaf_dequant_affine(FAKE, FAKE, FAKE, 4, 256, 32, FAKE, None) == 2
+    assert L.usaf_dequant_affine(FAKE, FAKE, FAKE, 4, 192, 128, FAKE, None) == 2
+    assert L.usaf_dequant_affine(FAKE, FAKE, FAKE, -1, 128, 128, FAKE, None) == 1
+    assert L.usaf_dequant_affine(FAKE, FAKE, None, 4, 128, 128, FAKE, None) == 1
+    assert L.usaf_dequant_affine(None, None, None, 0, 128, 128, None, None) == 0
     assert L.usaf_dequant_resident(FAKE, FAKE, 4, 128, 64, FAKE + 8, None) == 2
     # mse / route: nulls
     assert L.usaf_mse_grad(C.byref(sh), None, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == 1

@@ -73,6 +73,27 @@ def test_dequant_bit_exact(capi, rows, cols):
     assert np.array_equal(got, bf16_bits(ref))
 
 
+@pytest.mark.parametrize("rows,cols,group", [(96, 384, 128), (1, 128, 128), (513, 768, 64),
+                                            (64, 2048, 128)])
+def test_dequant_affine_bit_exact(capi, rows, cols, group):
+    """The HQQ-style affine storage: unsigned codes, fp16 scale and zero per group."""
+    say(f"dequant affine rows={rows} cols={cols} group={group}")
+    rng = np.random.default_rng(rows + cols + group)
+    q = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    ng = (rows, cols // group)
+    mags = np.concatenate([np.array([0.0, 5.96e-8, 6.1e-5, 65504.0]), 10.0 ** rng.uniform(-7, 4, 1000)])
+    sc = (rng.choice(mags, size=ng) * rng.choice([-1, 1], size=ng)).astype(np.float16)
+    zr = np.concatenate([np.array([0.0, -(2.0 ** -24), 7.5, 65504.0]), rng.uniform(-4, 20, 1000)])
+    zr = rng.choice(zr, size=ng).astype(np.float16)
+    out = torch.empty(rows, cols, dtype=torch.bfloat16, device=DEV)
+    capi.dequant_affine(torch.from_numpy(q).to(DEV), torch.from_numpy(sc.view(np.int16)).to(DEV),
+                        torch.from_numpy(zr.view(np.int16)).to(DEV), rows, cols, group, out)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = O.dequant_affine(q, sc.view(np.uint16), zr.view(np.uint16), group)
+    assert np.array_equal(got, bf16_bits(ref))
+
+
 # --------------------------------------------------------------------------
 # a3-a4 routing from given logits
 # --------------------------------------------------------------------------
