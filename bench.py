@@ -42,13 +42,13 @@ WRITE_SCALE = 1.0   # and 1,048,576 KiB of WRITE_SIZE
 # the launches of one step (the two SDDMM launches, the plan being kept per
 # list; expert + router Adam)
 COUNTER_TRAFFIC = {
-    "router_gemm": (8788, 16384, "6a324fe8063957cd"),
-    "gate_up": (470443, 147460, "6a324fe8063957cd"),
-    "down": (221359, 131072, "6a324fe8063957cd"),
-    "da": (321870, 100114, "6a324fe8063957cd"),
-    "dx": (576031, 131072, "6a324fe8063957cd"),
-    "masked_dw": (169824, 11803, "2432d237f5f1f309"),
-    "adam": (28632, 124784, "e3d368e223881c40"),
+    "router_gemm": (8788, 16384, "11dc2d44b399d193"),
+    "gate_up": (470321, 147459, "11dc2d44b399d193"),
+    "down": (221360, 131072, "11dc2d44b399d193"),
+    "da": (338569, 100112, "11dc2d44b399d193"),
+    "dx": (632618, 131072, "11dc2d44b399d193"),
+    "masked_dw": (169865, 11803, "0dc1c49d496d20e3"),
+    "adam": (28636, 124714, "b8332b752cd03a50"),
 }
 KERNEL_SOURCES = {
     c: ("gemm_mfma.hpp", "gemm_v2.hpp", "lds_dma.hpp", "moe_mfma.hip", "common.hpp", "moe_internal.hpp")
