@@ -155,7 +155,13 @@ USAF_API usaf_status usaf_masked_plan(const usaf_moe_shape *shape, const uint32_
  *       the fp32 gradient at idx[i]; in dense mode (idx == NULL and
  *       nnz == N) dW[f] is the gradient of every expert weight f.
  * plan (nullable): usaf_masked_plan's plan of this very idx[nnz]; with NULL
- * the plan is rebuilt inside ws on every call.  Ignored in dense mode.
+ * the plan is rebuilt inside ws on every call.  Ignored in dense mode.  The
+ * plan records the list it was built for (nnz, the idx address, the first and
+ * last entry); when these differ from the call's list the gradient kernels
+ * write no dW value and add 1 to *nonfinite (when given), so that a step
+ * using a stale plan is skipped rather than computed from another list's
+ * tiles.  A list rewritten in place with the same length and end entries is
+ * not detected: rebuild the plan whenever the list changes.
  * nonfinite (nullable, device int32): incremented when any dW value or dWr
  * is NaN/Inf (sparse mode); the caller zeroes it before the step.
  * An empty list (nnz == 0, idx may be NULL) computes everything but dW.

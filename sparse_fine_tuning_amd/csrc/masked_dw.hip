@@ -88,12 +88,28 @@ struct SegLayout {
   int64_t ngu, q1, Q;  // flat start of down, first down segment, segment count
 };
 
+// Words of the plan's 256-byte counter block: the two tensors' tile counts,
+// their entry targets, then what identifies the list the plan was built
+// for (its length, its address, its first and last entry).  The gradient
+// kernel compares these with the list it is given before it reads a tile.
+constexpr int kHdrTiles = 0, kHdrTarget = 2, kHdrNnz = 4, kHdrPtr = 6, kHdrFirst = 8,
+              kHdrLast = 9;
+
 __global__ __launch_bounds__(256) void masked_plan_kernel(const uint32_t* __restrict__ idx,
                                                           int64_t nnz, SegLayout Lq,
                                                           uint32_t* __restrict__ seg,
                                                           int* __restrict__ tile_counters) {
   const int64_t q = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (q < 2) tile_counters[q] = 0;  // the tile builders append after this kernel
+  if (q < 2) tile_counters[kHdrTiles + q] = 0;  // the tile builders append after this kernel
+  if (q == 0) {
+    uint32_t* hdr = reinterpret_cast<uint32_t*>(tile_counters);
+    hdr[kHdrNnz] = uint32_t(uint64_t(nnz));
+    hdr[kHdrNnz + 1] = uint32_t(uint64_t(nnz) >> 32);
+    hdr[kHdrPtr] = uint32_t(reinterpret_cast<uintptr_t>(idx));
+    hdr[kHdrPtr + 1] = uint32_t(uint64_t(reinterpret_cast<uintptr_t>(idx)) >> 32);
+    hdr[kHdrFirst] = idx[0];
+    hdr[kHdrLast] = idx[nnz - 1];
+  }
   if (q > Lq.Q) return;
   int64_t key;  // flat index where segment q begins
   if (q == Lq.Q) {
@@ -397,9 +413,21 @@ __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __res
 // Tiles of the list, one at a time per block: the rows [r_lo, r_hi) of
 // expert e in column tile ct, all the tile's entries in one pass (at most
 // kCap<kDown>).
+// Whether the plan's counter block describes the list the kernel is given
+// (same length, address, first and last entry).  A plan kept across a change
+// of the list would otherwise send the tiles to list positions that hold
+// other entries.
+__device__ __forceinline__ bool plan_matches(const uint32_t* __restrict__ hdr, const MaskedArgs& A) {
+  const uint64_t p = uint64_t(reinterpret_cast<uintptr_t>(A.idx));
+  return hdr[kHdrNnz] == uint32_t(uint64_t(A.nnz)) && hdr[kHdrNnz + 1] == uint32_t(uint64_t(A.nnz) >> 32) &&
+         hdr[kHdrPtr] == uint32_t(p) && hdr[kHdrPtr + 1] == uint32_t(p >> 32) &&
+         hdr[kHdrFirst] == A.idx[0] && hdr[kHdrLast] == A.idx[A.nnz - 1];
+}
+
 template <bool kDown>
 __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A, const uint2* __restrict__ tiles,
-                                                                  const int* __restrict__ ntiles) {
+                                                                  const int* __restrict__ counters,
+                                                                  int tensor) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_l[2][kLsBytes<kDown>];
   __shared__ __attribute__((aligned(16))) unsigned char lds_r[2][kRsBytes];
   __shared__ int rowpre[kMaxRows<kDown> + 1];
@@ -409,7 +437,13 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
 
   constexpr int kE = kEnt<kDown>;
   const int tid = threadIdx.x;
-  const int nt = *ntiles;
+  if (!plan_matches(reinterpret_cast<const uint32_t*>(counters), A)) {
+    // a plan of another list: no gradient is written, and the non-finite
+    // count the optimiser checks is raised so that the step is skipped
+    if (blockIdx.x == 0 && tid == 0 && A.nonfinite) atomicAdd(A.nonfinite, 1);
+    return;
+  }
+  const int nt = counters[kHdrTiles + tensor];
   // persistent: block b takes tiles x(b), x(b) + G, ... (x: the XCD-aware
   // order, so that a group's consecutive tiles share an XCD's L2)
   for (int L = xcd_remap_blocks(blockIdx.x, gridDim.x); L < nt; L += gridDim.x) {
@@ -425,11 +459,12 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
 
   // entries of this tile: per row r, the plan segment (e, r, ct)
   const int64_t q_r0 = A.qbase + (int64_t(e) * A.R + r_lo) * A.nct + ct;
+  const uint32_t nnz32 = uint32_t(A.nnz);  // list positions are below 2^32
   for (int r = tid; r < nr; r += kThreads) {
     const int64_t q = q_r0 + int64_t(r) * A.nct;
-    const uint32_t s0 = A.seg[q];
+    const uint32_t s0 = min(A.seg[q], nnz32);
     rstart[r] = s0;
-    rowpre[r + 1] = int(A.seg[q + 1] - s0);
+    rowpre[r + 1] = int(max(min(A.seg[q + 1], nnz32), s0) - s0);
   }
   if (tid == 0) rowpre[0] = 0;
   __syncthreads();
@@ -724,12 +759,12 @@ usaf_status masked_plan_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64
                        seg, qb, s.E, R, nct, ngt);
     USAF_LAUNCH_CHECK();
     hipLaunchKernelGGL(masked_target_kernel, dim3(1), dim3(256), 0, st, ngt, groups, R, RB, cap, cus,
-                       counters + 2 + tensor);
+                       counters + kHdrTarget + tensor);
     USAF_LAUNCH_CHECK();
     hipLaunchKernelGGL(masked_tiles_kernel, dim3(unsigned(ceil_div(groups, 4))), dim3(256), 0, st,
-                       seg, qb, s.E, R, nct, RB, cap, ngt, counters + 2 + tensor,
+                       seg, qb, s.E, R, nct, RB, cap, ngt, counters + kHdrTarget + tensor,
                        reinterpret_cast<uint2*>(base + (tensor == 0 ? P.tiles0 : P.tiles1)),
-                       counters + tensor);
+                       counters + kHdrTiles + tensor);
     USAF_LAUNCH_CHECK();
   }
   return USAF_OK;
@@ -768,10 +803,10 @@ usaf_status masked_dw_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64_t
     const int64_t blocks = (std::min<int64_t>(bound, device_cus()) + 7) / 8 * 8;
     if (tensor == 0)
       hipLaunchKernelGGL(masked_dw_sddmm_kernel<false>, dim3(unsigned(blocks)), dim3(kThreads), 0, st, A, tl,
-                         counters);
+                         counters, 0);
     else
       hipLaunchKernelGGL(masked_dw_sddmm_kernel<true>, dim3(unsigned(blocks)), dim3(kThreads), 0, st, A, tl,
-                         counters + 1);
+                         counters, 1);
     USAF_LAUNCH_CHECK();
   }
   timer_end(USAF_K_MASKED_DW, st);

@@ -48,12 +48,27 @@ class SparseMoELayer:
         self.dWr = z(E, H)
         self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
         self.nonfinite = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.X = self.Wr = self.W = self.tgt = None
         self.idx = None
+        self.X = self.Wr = self.W = self.tgt = None
         self.t = 0
         self.skipped = 0
 
     # ---- parameters and data -------------------------------------------------
+    @property
+    def W(self):
+        """The flat expert weights [N] (act dtype)."""
+        return self._W
+
+    @W.setter
+    def W(self, value):
+        # SparseAdam reads the active weights from the compact list, so a new
+        # weight buffer must refresh it (else the next update would write the
+        # old active weights back); after writing into W in place, call
+        # refresh_list() for the same reason
+        self._W = value
+        if value is not None and self.idx is not None:
+            self.refresh_list()
+
     def load(self, X, Wr, W_gu, W_d, tgt):
         """Upload numpy inputs (values already representable in the act dtype)."""
         dt, dev = _dt(self.act), self.device

@@ -134,6 +134,8 @@ class MoEStack:
         flat = np.concatenate([np.asarray(W_gu, np.float32).ravel(), np.asarray(W_d, np.float32).ravel()])
         lay.W.copy_(torch.from_numpy(flat).to(dev).to(dt))
         lay.Wr.copy_(torch.from_numpy(np.ascontiguousarray(Wr, dtype=np.float32)).to(dev))
+        if lay.idx is not None:  # SparseAdam's compact copy of the active weights
+            lay.refresh_list(self.act)
 
     def set_batch(self, X, tgt):
         """X_0 and the target: numpy arrays or device tensors."""

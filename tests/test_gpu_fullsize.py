@@ -204,11 +204,12 @@ def test_mixtral_layer_step_full_size(capi):
     lay.W.copy_(torch.from_numpy(np.concatenate([d["W_gu"].ravel(), d["W_d"].ravel()]))
                 .to(DEV).to(torch.bfloat16))
     lay.Wr.copy_(torch.from_numpy(d["Wr"]).to(DEV))
+    lay.refresh_list()  # W was written in place
     lay.dense_scan(out=dense)
     torch.cuda.synchronize()
     dense_at = npf(dense[torch.from_numpy(idx.astype(np.int64)).to(DEV)])
-    # the dense path rounds w * dY to bf16 before the MFMA, the masked one does not
-    assert rel(g["dW"], dense_at) <= 1e-2
+    # both paths stage bf16(w * dY); they differ only in fp32 summation order
+    assert rel(g["dW"], dense_at) <= 1e-4
     del dense
     torch.cuda.empty_cache()
     say("  oracle forward / backward")

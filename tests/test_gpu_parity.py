@@ -419,11 +419,98 @@ def test_sparse_adam(capi, act, use_list):
     got = npf(Wt)
     frozen = np.ones(N, bool); frozen[idx] = False
     assert np.array_equal(got[frozen], w.astype(np.float64)[frozen])
-    assert rel(got, wref) <= (TOL_BF16 if act else TOL_F32)
+    check_update(got[idx], wref[idx], w[idx], act)
     # the touched entries moved by ~lr per step
     assert np.median(np.abs(got[idx] - w[idx])) > 1e-3
     if use_list:  # the compact copy still equals W at idx
         assert torch.equal(wl, Wt[it.long()])
+
+
+def check_update(w_gpu, w_ref, w_old, act):
+    """The update itself, W_new - W_old, against the oracle's.  fp32: within
+    the fp32 tolerance of max|dW|.  bf16: both sides round every step's
+    result once to bf16 (fp32 vs fp64 arithmetic before it), so an entry may
+    differ by at most one bf16 unit in the last place of its value, and only
+    rarely; a wrong step size (half a step, a missing bias correction) moves
+    nearly every entry."""
+    d_gpu = np.asarray(w_gpu, np.float64) - w_old
+    d_ref = np.asarray(w_ref, np.float64) - w_old
+    if not act:
+        assert rel(d_gpu, d_ref) <= TOL_F32
+        return
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(w_ref), 1e-30))) - 7)
+    diff = np.abs(d_gpu - d_ref)
+    assert np.all(diff <= ulp * 1.0001), "an update differs by more than one bf16 ulp"
+    assert np.count_nonzero(diff) <= 0.01 * diff.size, "updates differ in too many entries"
+
+
+def test_new_weights_after_set_active_reach_adam(capi):
+    """Weights loaded after the active list was set: SparseAdam must update
+    the new weights, not the compact copy of the old ones."""
+    say("weights replaced after set_active")
+    from sparse_fine_tuning_amd.layer import SparseMoELayer
+    dims = (200, 128, 8, 2, 96)
+    T, H, E, K, I = dims
+    d_old = synth.moe_layer(*dims, bf16=True, seeds=(40, 41, 42, 43, 44))
+    d = synth.moe_layer(*dims, bf16=True, seeds=(50, 51, 52, 53, 54))
+    N = 3 * E * H * I
+    k = O.select_count(N, 5, 100)
+    idx = synth.random_mask(N, k, 55)
+    lay = SparseMoELayer(*dims, act=1, device=DEV)
+    lay.load(d_old["X"], d_old["Wr"], d_old["W_gu"], d_old["W_d"], d_old["tgt"])
+    lay.set_active(idx)
+    lay.load(d["X"], d["Wr"], d["W_gu"], d["W_d"], d["tgt"])
+    lay.train_step(lr=1e-3)
+    torch.cuda.synchronize()
+    assert lay.t == 1
+    R = O.Rounding(O.BF16, O.CONTRACT)
+    z = np.zeros(k)
+    ref = O.train_step(d["X"], d["tgt"], d["Wr"], d["W_gu"], d["W_d"], K, idx, z, z,
+                       np.zeros_like(d["Wr"]), np.zeros_like(d["Wr"]), 0, 1e-3, 0.9, 0.999,
+                       1e-8, R)
+    i64 = idx.astype(np.int64)
+    w0 = np.concatenate([d["W_gu"].ravel(), d["W_d"].ravel()])
+    got = npf(lay.W)
+    # every entry moved from the new weights by about lr, in the oracle's direction
+    sure = np.abs(ref["g"]) > TOL_BF16 * np.abs(ref["g"]).max()
+    step = got[i64] - w0[i64]
+    assert np.all(np.abs(step) <= 1e-3 * 1.01 + np.abs(w0[i64]) * 2.0 ** -7)
+    assert np.all(np.sign(step[sure]) == np.sign(ref["W_flat"][i64][sure] - w0[i64][sure]))
+    assert rel(got[i64][sure], ref["W_flat"][i64][sure]) <= TOL_BF16
+    frozen = np.ones(N, bool); frozen[i64] = False
+    assert np.array_equal(got[frozen], w0[frozen])
+    assert torch.equal(lay.w_list, lay.W[lay.idx.long() & 0xFFFFFFFF])
+
+
+def test_stale_plan_skips_the_step(capi):
+    """A masked-gradient plan built for another list is recognised on the
+    device: no gradient is written and the step is counted non-finite, so
+    SparseAdam changes nothing."""
+    say("stale plan")
+    from sparse_fine_tuning_amd.layer import SparseMoELayer
+    dims = (200, 128, 8, 2, 96)
+    T, H, E, K, I = dims
+    d = synth.moe_layer(*dims, bf16=True, seeds=(60, 61, 62, 63, 64))
+    N = 3 * E * H * I
+    lay = SparseMoELayer(*dims, act=1, device=DEV)
+    lay.load(d["X"], d["Wr"], d["W_gu"], d["W_d"], d["tgt"])
+    lay.set_active(synth.random_mask(N, 900, 65))
+    old_plan = lay.plan.clone()
+    lay.set_active(synth.random_mask(N, 1000, 66))
+    lay.plan.copy_(old_plan)  # the kept plan now describes the first list
+    W0 = lay.W.clone()
+    lay.dW.fill_(7.0)
+    lay.train_step(lr=1e-3)
+    torch.cuda.synchronize()
+    assert int(lay.nonfinite.item()) == 1
+    assert lay.skipped == 1 and lay.t == 0
+    assert torch.all(lay.dW == 7.0)
+    assert torch.equal(lay.W.view(torch.int16), W0.view(torch.int16))
+    # the right plan again: a normal step
+    lay.refresh_list()
+    lay.train_step(lr=1e-3)
+    torch.cuda.synchronize()
+    assert int(lay.nonfinite.item()) == 0 and lay.t == 1
 
 
 def test_nan_step_is_skipped(capi):
