@@ -1187,6 +1187,16 @@ static usaf_status mse_impl(const usaf_moe_shape& s, const T* Y, const T* tgt, T
   return USAF_OK;
 }
 
+usaf_status mse_launch(const usaf_moe_shape& s, const void* Y, const void* tgt, void* dY,
+                       float* loss, int32_t* nonfinite, float* part, hipStream_t stream) {
+  char* ws = reinterpret_cast<char*>(part);
+  if (s.act == USAF_BF16)
+    return mse_impl<bf16_t>(s, static_cast<const bf16_t*>(Y), static_cast<const bf16_t*>(tgt),
+                            static_cast<bf16_t*>(dY), loss, nonfinite, ws, stream);
+  return mse_impl<float>(s, static_cast<const float*>(Y), static_cast<const float*>(tgt),
+                         static_cast<float*>(dY), loss, nonfinite, ws, stream);
+}
+
 }  // namespace usaf
 
 using namespace usaf;
@@ -1256,12 +1266,7 @@ extern "C" usaf_status usaf_mse_grad(const usaf_moe_shape* shape, const void* Y,
   if (!Y || !tgt || !dY || !loss) return USAF_ERR_INVALID_ARG;
   const int64_t n = int64_t(shape->T) * shape->H;
   if (!ws || ws_bytes < size_t(ceil_div(n, 4096)) * 4 + 64) return USAF_ERR_WORKSPACE;
-  if (shape->act == USAF_BF16)
-    return mse_impl<bf16_t>(*shape, static_cast<const bf16_t*>(Y), static_cast<const bf16_t*>(tgt),
-                            static_cast<bf16_t*>(dY), loss, nonfinite, static_cast<char*>(ws),
-                            stream);
-  return mse_impl<float>(*shape, static_cast<const float*>(Y), static_cast<const float*>(tgt),
-                         static_cast<float*>(dY), loss, nonfinite, static_cast<char*>(ws), stream);
+  return mse_launch(*shape, Y, tgt, dY, loss, nonfinite, static_cast<float*>(ws), stream);
 }
 
 extern "C" usaf_status usaf_residual_add(int32_t act, const void* a, const void* b, void* out,

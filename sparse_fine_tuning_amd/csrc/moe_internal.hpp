@@ -14,6 +14,10 @@ namespace usaf {
 int64_t masked_plan_bytes(const usaf_moe_shape& s);
 // Compute units of the current device (cached per device).
 int device_cus();
+// The loss kernels of usaf_mse_grad with their partial sums in `part`
+// (ceil(T*H / 4096) floats, each written before it is read).
+usaf_status mse_launch(const usaf_moe_shape& s, const void* Y, const void* tgt, void* dY,
+                       float* loss, int32_t* nonfinite, float* part, hipStream_t stream);
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
