@@ -158,7 +158,7 @@ USAF_API usaf_status usaf_masked_plan(const usaf_moe_shape *shape, const uint32_
  * the plan is rebuilt inside ws on every call.  Ignored in dense mode.  The
  * plan records the list it was built for (nnz, the idx address, the first and
  * last entry); when these differ from the call's list the gradient kernels
- * write no dW value and add 1 to *nonfinite (when given), so that a step
+ * write no dW value and raise *nonfinite (when given), so that a step
  * using a stale plan is skipped rather than computed from another list's
  * tiles.  A list rewritten in place with the same length and end entries is
  * not detected: rebuild the plan whenever the list changes.

@@ -37,9 +37,11 @@ __global__ __launch_bounds__(256) void adam_kernel(W* __restrict__ w, const uint
   }
 }
 
-// Adam over a list with a compact weight copy: entries 4i..4i+3 per thread
-// (16-byte reads of g, m, v, idx), the weights read from the list and
-// written to the list and to W at idx.
+// Adam over a list with a compact weight copy: one entry per lane, so the
+// lanes of a wave hold 64 consecutive entries of the ascending list and each
+// of its scattered W stores covers the shortest span of W (list loads and
+// stores are coalesced 4- and 2-byte accesses).  The weight is read from the
+// list and written to the list and to W at idx.
 template <class W>
 __global__ __launch_bounds__(256) void adam_list_kernel(W* __restrict__ w, const uint32_t* __restrict__ idx,
                                                         int64_t n, W* __restrict__ wl,
@@ -50,41 +52,16 @@ __global__ __launch_bounds__(256) void adam_list_kernel(W* __restrict__ w, const
                                                         const int32_t* __restrict__ skip) {
   if (skip && *skip != 0) return;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  const int64_t n4 = n / 4;
-  for (int64_t q = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; q < n4; q += stride) {
-    const float4 gq = reinterpret_cast<const float4*>(g)[q];
-    float4 mq = reinterpret_cast<const float4*>(m)[q];
-    float4 vq = reinterpret_cast<const float4*>(v)[q];
-    const uint4 iq = reinterpret_cast<const uint4*>(idx)[q];
-    const float gi[4] = {gq.x, gq.y, gq.z, gq.w};
-    float mi[4] = {mq.x, mq.y, mq.z, mq.w}, vi[4] = {vq.x, vq.y, vq.z, vq.w};
-    const uint32_t ii[4] = {iq.x, iq.y, iq.z, iq.w};
-    float wv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      mi[u] = fmaf(b1, mi[u], omb1 * gi[u]);
-      vi[u] = fmaf(b2, vi[u], omb2 * gi[u] * gi[u]);
-      wv[u] = Act<W>::ld(wl, 4 * q + u) - lr * (mi[u] / bc1) / (sqrtf(vi[u] / bc2) + eps);
-    }
-    reinterpret_cast<float4*>(m)[q] = make_float4(mi[0], mi[1], mi[2], mi[3]);
-    reinterpret_cast<float4*>(v)[q] = make_float4(vi[0], vi[1], vi[2], vi[3]);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      Act<W>::st(wl, 4 * q + u, wv[u]);
-      Act<W>::st(w, int64_t(ii[u]), wv[u]);
-    }
-  }
-  // tail (n % 4 entries)
-  const int64_t i = 4 * n4 + int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
     const float gi = g[i];
+    const uint32_t f = idx[i];
     const float mi = fmaf(b1, m[i], omb1 * gi);
     const float vi = fmaf(b2, v[i], omb2 * gi * gi);
+    const float wv = Act<W>::ld(wl, i) - lr * (mi / bc1) / (sqrtf(vi / bc2) + eps);
     m[i] = mi;
     v[i] = vi;
-    const float wv = Act<W>::ld(wl, i) - lr * (mi / bc1) / (sqrtf(vi / bc2) + eps);
     Act<W>::st(wl, i, wv);
-    Act<W>::st(w, int64_t(idx[i]), wv);
+    Act<W>::st(w, int64_t(f), wv);
   }
 }
 
@@ -144,13 +121,7 @@ extern "C" usaf_status usaf_sparse_adam(int32_t w_dtype, void* W, const uint32_t
   const float omb1 = float(1.0 - beta1), omb2 = float(1.0 - beta2);
   timer_begin(USAF_K_ADAM, stream);
   if (w_list) {
-    const bool aligned = ((reinterpret_cast<uintptr_t>(g) | reinterpret_cast<uintptr_t>(m) |
-                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(idx)) & 15) == 0;
-    if (!aligned) {
-      timer_end(USAF_K_ADAM, stream);
-      return USAF_ERR_UNSUPPORTED;
-    }
-    const unsigned grid = grid_for(ceil_div(n, 4));
+    const unsigned grid = grid_for(n);
     if (w_dtype == USAF_BF16)
       hipLaunchKernelGGL(adam_list_kernel<bf16_t>, dim3(grid), dim3(256), 0, stream,
                          static_cast<bf16_t*>(W), idx, n, static_cast<bf16_t*>(w_list), g, m, v,

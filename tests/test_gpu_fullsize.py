@@ -335,11 +335,71 @@ def topk_set_is_exact(g, sel, k):
     assert (lo > hi) or (lo == hi and lo_idx < hi_idx), "selection is not the top-k"
 
 
+def check_rigl(grad, w_flat, S_old, m_old, v_old, S_new, m_new, v_new, stats, sel, k, r):
+    """RigL's defining properties on host copies: k ascending entries, r
+    dropped and r grown; the dropped are the r active entries of smallest |w|
+    and the grown the r best |g| outside S_old (ties: lowest index, both
+    compared as fp32 bit patterns); kept moments carried over, grown ones
+    zero; the stats count the fresh top-k ``sel`` outside S_old."""
+    N = grad.size
+    S_old64 = np.asarray(S_old, np.int64)
+    assert S_new.size == k and np.all(np.diff(S_new) > 0)
+    kept = np.intersect1d(S_new, S_old64, assume_unique=True)
+    dropped = np.setdiff1d(S_old64, kept, assume_unique=True)
+    grown = np.setdiff1d(S_new, kept, assume_unique=True)
+    assert dropped.size == r and grown.size == r
+    # drop: the r active entries of smallest |w| (ties: lowest index)
+    wb = np.abs(np.asarray(w_flat, np.float32)).view(np.uint32)
+    dk = wb[dropped].max()
+    dk_idx = dropped[wb[dropped] == dk].max()
+    kk = wb[kept].min()
+    kk_idx = kept[wb[kept] == kk].min()
+    assert dk < kk or (dk == kk and dk_idx < kk_idx), "drop set is not the r smallest |w|"
+    del wb
+    # grow: the top-r of |g| outside S_old
+    gb = np.abs(grad).view(np.uint32)
+    outside = np.ones(N, dtype=bool)
+    outside[S_old64] = False
+    outside[grown] = False
+    lo = gb[grown].min()
+    lo_idx = grown[gb[grown] == lo].max()
+    hi = gb[outside].max()
+    hi_idx = np.nonzero(outside & (gb == hi))[0].min()
+    assert lo > hi or (lo == hi and lo_idx < hi_idx), "grow set is not the top-r outside S_old"
+    del gb, outside
+    # moments: kept entries carry theirs, grown entries start at zero
+    pos_old = np.searchsorted(S_old64, kept)
+    pos_new = np.searchsorted(S_new, kept)
+    assert np.array_equal(m_new[pos_new], m_old[pos_old])
+    assert np.array_equal(v_new[pos_new], v_old[pos_old])
+    pos_g = np.searchsorted(S_new, grown)
+    assert not m_new[pos_g].any() and not v_new[pos_g].any()
+    assert int(stats[0]) == r and int(stats[1]) == r
+    novelty = np.setdiff1d(np.asarray(sel, np.int64), S_old64, assume_unique=True).size
+    assert int(stats[2]) == novelty
+    return novelty
+
+
+def run_rigl(capi, dims, w_dev, g_dev, S_old, m_old, v_old, r):
+    """usaf_rigl_reselect through the layer (list, moments) on device inputs."""
+    from sparse_fine_tuning_amd.layer import SparseMoELayer, rigl
+    lay = SparseMoELayer(*dims, act=capi.BF16, device=DEV)
+    lay.W = w_dev
+    lay.set_active(S_old)
+    lay.m.copy_(torch.from_numpy(np.asarray(m_old, np.float32)))
+    lay.v.copy_(torch.from_numpy(np.asarray(v_old, np.float32)))
+    stats = rigl(lay, g_dev, r).cpu().numpy()
+    out = (lay.idx.cpu().numpy().view(np.uint32).astype(np.int64), lay.m.cpu().numpy(),
+           lay.v.cpu().numpy(), stats)
+    del lay
+    return out
+
+
 def test_topk_and_rigl_full_size(capi):
     """Global top-k and RigL at N = 603,979,776 on a seeded gradient, checked
     by the properties that define them (the oracle's own functions are run
     against the kernels at smaller sizes)."""
-    from sparse_fine_tuning_amd.layer import SparseMoELayer, rigl, topk
+    from sparse_fine_tuning_amd.layer import topk
     dims = (4096, 2048, 128, 8, 768)
     T, H, E, K, I = dims
     N = 3 * E * H * I
@@ -355,47 +415,65 @@ def test_topk_and_rigl_full_size(capi):
     sel = topk(g_dev, k).cpu().numpy().view(np.uint32)
     say("  top-k properties")
     topk_set_is_exact(grad, sel, k)
-    lay = SparseMoELayer(8, H, E, K, I, act=capi.BF16, device=DEV)
-    lay.W = torch.from_numpy(w_flat).to(DEV).to(torch.bfloat16)
-    lay.set_active(S_old)
-    lay.m.copy_(torch.from_numpy(m_old))
-    lay.v.copy_(torch.from_numpy(v_old))
-    stats = rigl(lay, g_dev, r).cpu().numpy()
-    S_new = lay.idx.cpu().numpy().view(np.uint32).astype(np.int64)
-    m_new, v_new = lay.m.cpu().numpy(), lay.v.cpu().numpy()
-    del lay, g_dev
+    w_dev = torch.from_numpy(w_flat).to(DEV).to(torch.bfloat16)
+    S_new, m_new, v_new, stats = run_rigl(capi, (8, H, E, K, I), w_dev, g_dev, S_old, m_old,
+                                          v_old, r)
+    del g_dev, w_dev
     torch.cuda.empty_cache()
     say("  RigL properties")
-    S_old64 = S_old.astype(np.int64)
-    assert S_new.size == k and np.all(np.diff(S_new) > 0)
-    kept = np.intersect1d(S_new, S_old64, assume_unique=True)
-    dropped = np.setdiff1d(S_old64, kept, assume_unique=True)
-    grown = np.setdiff1d(S_new, kept, assume_unique=True)
-    assert dropped.size == r and grown.size == r
-    # drop: the r active entries of smallest |w| (ties: lowest index)
-    wb = np.abs(w_flat.astype(np.float32)).view(np.uint32)
-    dk = wb[dropped].max()
-    dk_idx = dropped[wb[dropped] == dk].max()
-    kk = wb[kept].min()
-    kk_idx = kept[wb[kept] == kk].min()
-    assert dk < kk or (dk == kk and dk_idx < kk_idx), "drop set is not the r smallest |w|"
-    # grow: the top-r of |g| outside S_old
-    gb = np.abs(grad).view(np.uint32)
-    outside = np.ones(N, dtype=bool)
-    outside[S_old64] = False
-    outside[grown] = False
-    lo = gb[grown].min()
-    lo_idx = grown[gb[grown] == lo].max()
-    hi = gb[outside].max()
-    hi_idx = np.nonzero(outside & (gb == hi))[0].min()
-    assert lo > hi or (lo == hi and lo_idx < hi_idx), "grow set is not the top-r outside S_old"
-    # moments: kept entries carry theirs, grown entries start at zero
-    pos_old = np.searchsorted(S_old64, kept)
-    pos_new = np.searchsorted(S_new, kept)
-    assert np.array_equal(m_new[pos_new], m_old[pos_old])
-    assert np.array_equal(v_new[pos_new], v_old[pos_old])
-    pos_g = np.searchsorted(S_new, grown)
-    assert not m_new[pos_g].any() and not v_new[pos_g].any()
-    assert int(stats[0]) == r and int(stats[1]) == r
-    novelty = np.setdiff1d(sel.astype(np.int64), S_old64, assume_unique=True).size
-    assert int(stats[2]) == novelty
+    check_rigl(grad, w_flat, S_old, m_old, v_old, S_new, m_new, v_new, stats, sel, k, r)
+
+
+@pytest.mark.parametrize("grow_from", ["fresh_topk", "exclusion_select"])
+def test_topk_and_rigl_mixtral_size(capi, grow_from):
+    """Top-k and RigL over every expert weight of the Mixtral-shaped layer,
+    N = 1,409,286,144 > 2^30 (k = 7,046,430, r = 2,113,929), by the
+    defining properties.  Two gradients force the two ways RigL finds its
+    grow set: a plain seeded gradient with a random old list (at least r of
+    the fresh top-k lie outside the old list: the grow set comes from the
+    fresh top-k), and one whose top-k is a known seeded set P with the old
+    list holding all of P but r/2 (fewer than r outside: the grow set needs
+    a full selection that excludes the old list)."""
+    from sparse_fine_tuning_amd.layer import topk
+    dims = (8, 4096, 8, 2, 14336)
+    _, H, E, K, I = dims
+    N = 3 * E * H * I
+    k = O.select_count(N, 5, 1000)
+    r = (3 * k) // 10
+    assert (N, k, r) == (1409286144, 7046430, 2113929)
+    say(f"top-k and RigL at N={N}, k={k}, r={r}, grow from {grow_from}")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(80)
+    g_dev = torch.randn(N, generator=gen, device=DEV) * 1e-6
+    if grow_from == "fresh_topk":
+        S_old = synth.random_mask(N, k, 81)
+    else:
+        P = synth.random_mask(N, k, 82)
+        P_dev = torch.from_numpy(P.astype(np.int64)).to(DEV)
+        big = (1.0 + torch.rand(k, generator=gen, device=DEV)) * 1e-3
+        sign = torch.where(torch.rand(k, generator=gen, device=DEV) < 0.5, -1.0, 1.0)
+        g_dev[P_dev] = big * sign
+        del P_dev, big, sign
+        rng = np.random.default_rng(83)
+        out_of_P = np.sort(rng.choice(k, size=r // 2, replace=False))
+        kept_P = np.delete(P, out_of_P)
+        extra = np.setdiff1d(synth.random_mask(N, r, 84), P, assume_unique=True)[: r // 2]
+        S_old = np.sort(np.concatenate([kept_P, extra])).astype(np.uint32)
+        assert S_old.size == k and np.unique(S_old).size == k
+    m_old = synth.normal((k,), 1e-7, 85)
+    v_old = np.abs(synth.normal((k,), 1e-13, 86))
+    w_dev = (torch.randn(N, generator=gen, device=DEV) * 0.02).to(torch.bfloat16)
+    sel = topk(g_dev, k).cpu().numpy().view(np.uint32)
+    grad = g_dev.cpu().numpy()
+    say("  top-k properties")
+    topk_set_is_exact(grad, sel, k)
+    if grow_from == "exclusion_select":
+        assert np.array_equal(sel, P), "the top-k of the planted gradient is P"
+    S_new, m_new, v_new, stats = run_rigl(capi, dims, w_dev, g_dev, S_old, m_old, v_old, r)
+    w_flat = w_dev.float().cpu().numpy()
+    del g_dev, w_dev
+    torch.cuda.empty_cache()
+    say("  RigL properties")
+    novelty = check_rigl(grad, w_flat, S_old, m_old, v_old, S_new, m_new, v_new, stats, sel, k, r)
+    say(f"  fresh top-k outside the old list: {novelty} (r = {r})")
+    assert (novelty >= r) == (grow_from == "fresh_topk")
