@@ -272,6 +272,21 @@ USAF_API usaf_status usaf_mse_grad(const usaf_moe_shape *shape, const void *Y, c
                           void *dY, float *loss, int32_t *nonfinite, void *ws,
                           size_t ws_bytes, hipStream_t stream);
 
+/* The loss above without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses
+ * that forbid allocation).  Same arguments, results and errors as
+ * usaf_mse_grad, bit for bit; its partial sums live in a fixed 256 KiB
+ * device array of the library instead of a workspace, one copy per device,
+ * held until the process ends.  Limit: T*H <= 2^28 elements, else
+ * USAF_ERR_UNSUPPORTED.  Nothing carries over between calls, but every call
+ * on one device uses the same array: calls that overlap on one device (on
+ * different streams, or from different threads) race.  The stream must
+ * belong to the current device.  USAF_ERR_HIP if the array's device address
+ * cannot be obtained. */
+USAF_API usaf_status usaf_mse_grad_noalloc(const usaf_moe_shape *shape, const void *Y,
+                                           const void *tgt, void *dY, float *loss,
+                                           int32_t *nonfinite, hipStream_t stream);
+
 /* Residual stream of a stack of layers (the stacked-layer workload's
  * composition reading: no attention or norm between the MoE layers, so the
  * next layer's input is the sum of a layer's input and output, and in the

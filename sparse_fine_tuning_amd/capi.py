@@ -24,7 +24,7 @@ WS_FORWARD, WS_BACKWARD, WS_TOPK, WS_RIGL, WS_MASKED_PLAN = range(5)
 EXPORTS = (
     "usaf_workspace_size", "usaf_moe_forward", "usaf_masked_backward", "usaf_importance_topk",
     "usaf_rigl_reselect", "usaf_sparse_adam", "usaf_dequant_resident", "usaf_dequant_affine",
-    "usaf_mse_grad",
+    "usaf_mse_grad", "usaf_mse_grad_noalloc",
     "usaf_route", "usaf_status_string", "usaf_version", "usaf_timer_arm", "usaf_timer_read",
     "usaf_gather", "usaf_residual_add", "usaf_masked_plan",
 )
@@ -91,6 +91,7 @@ def _load():
         "usaf_dequant_resident": [vp, vp, i64, i64, i32, vp, vp],
         "usaf_dequant_affine": [vp, vp, vp, i64, i64, i32, vp, vp],
         "usaf_mse_grad": [vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "usaf_mse_grad_noalloc": [vp, vp, vp, vp, vp, vp, vp],
         "usaf_route": [vp, vp, vp, vp],
         "usaf_residual_add": [i32, vp, vp, vp, i64, vp],
         "usaf_status_string": [i32],
@@ -222,6 +223,12 @@ def mse_grad(shape, Y, tgt, dY, loss, nonfinite, ws, stream=None):
     _check(lib.usaf_mse_grad(C.byref(shape), _p(Y), _p(tgt), _p(dY), _p(loss), _p(nonfinite),
                              _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "usaf_mse_grad")
+
+
+def mse_grad_noalloc(shape, Y, tgt, dY, loss, nonfinite, stream=None):
+    _check(lib.usaf_mse_grad_noalloc(C.byref(shape), _p(Y), _p(tgt), _p(dY), _p(loss),
+                                     _p(nonfinite), _stream(stream)),
+           "usaf_mse_grad_noalloc")
 
 
 def residual_add(act, a, b, out, n, stream=None):

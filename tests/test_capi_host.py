@@ -132,3 +132,7 @@ def test_entry_points_refuse_bad_arguments_before_launch():
     # mse / route: nulls
     assert L.usaf_mse_grad(C.byref(sh), None, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == 1
     assert L.usaf_route(C.byref(sh), None, C.byref(st), None) == 1
+    # the no-allocation loss: nulls, and inputs beyond its fixed scratch (2^28 elements)
+    assert L.usaf_mse_grad_noalloc(C.byref(sh), None, FAKE, FAKE, FAKE, None, None) == 1
+    big = capi.Shape(65536, 8192, 8, 2, 32, 1)
+    assert L.usaf_mse_grad_noalloc(C.byref(big), FAKE, FAKE, FAKE, FAKE, None, None) == 2
