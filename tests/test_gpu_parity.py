@@ -313,7 +313,12 @@ def test_repeat_runs_are_bit_identical(capi):
 # --------------------------------------------------------------------------
 TOPK_CASES = [(10000, 500, "normal"), (50000, 12345, "ties"), (4096 * 3 + 17, 4096 * 3 + 17, "normal"),
               (9999, 1, "ties"), (200000, 1000, "exclude"), (100000, 3000, "ties_exclude"),
-              (4096, 4000, "allsame"), (123457, 61728, "exclude")]
+              (4096, 4000, "allsame"), (123457, 61728, "exclude"),
+              # from 2^20 keys on, a whole gradient takes the sampled single pass
+              (3000001, 15000, "normal"), (2500000, 200000, "ties"), (1 << 20, 1 << 20, "normal"),
+              (1500003, 1000, "allsame"), (1 << 21, 3, "normal"),
+              (2097152 + 4093, 100000, "sample_misleads"), (2 ** 21, 5000, "sample_floods"),
+              (2000000, 30000, "exclude")]
 
 
 @pytest.mark.parametrize("n,k,mode", TOPK_CASES)
@@ -325,6 +330,16 @@ def test_topk_exact(capi, n, k, mode):
         g = (rng.integers(-3, 4, n) * 0.25).astype(np.float32)
     if mode == "allsame":
         g = np.full(n, -0.5, np.float32)
+    sampled = np.arange(n) % 256 < 4  # the keys the sampled pass histograms
+    if mode == "sample_misleads":
+        # the sample sees only large keys, so its threshold lets through
+        # fewer than k keys: the pass must run again with every key
+        g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        g[sampled] = np.float32(10.0) + rng.random(np.count_nonzero(sampled)).astype(np.float32)
+    if mode == "sample_floods":
+        # the sample sees only small keys: nearly every key is a candidate
+        g = (rng.standard_normal(n) + 5.0).astype(np.float32)
+        g[sampled] = (rng.standard_normal(np.count_nonzero(sampled)) * 1e-3).astype(np.float32)
     ex = None
     if "exclude" in mode:
         ex = np.sort(rng.choice(n, n // 10, replace=False)).astype(np.uint32)
@@ -341,15 +356,18 @@ def test_topk_exact(capi, n, k, mode):
     assert np.array_equal(val.cpu().numpy(), g[ref])
 
 
-@pytest.mark.parametrize("act,old_is_top", [(1, False), (0, False), (1, True)])
-def test_rigl_exact(capi, act, old_is_top):
+@pytest.mark.parametrize("act,old_is_top,dims", [
+    (1, False, (16, 64, 4, 2, 32)), (0, False, (16, 64, 4, 2, 32)), (1, True, (16, 64, 4, 2, 32)),
+    # N = 12.6M: the sampled fresh top-k and the merges over 31 blocks of the old list
+    (1, False, (16, 1024, 8, 2, 512)), (1, True, (16, 1024, 8, 2, 512))])
+def test_rigl_exact(capi, act, old_is_top, dims):
     """old_is_top: the old set holds the largest |g|, so fewer than r entries of
     a fresh top-k are new and the grow set must come from the full selection
     that excludes the old set."""
-    say(f"rigl act={act} old_is_top={old_is_top}")
-    T, H, E, K, I = 16, 64, 4, 2, 32
+    say(f"rigl act={act} old_is_top={old_is_top} dims={dims}")
+    T, H, E, K, I = dims
     N = 3 * E * H * I
-    k = 1000
+    k = 1000 if N < 100000 else O.select_count(N, 5, 1000)
     r = (3 * k) // 10
     rng = np.random.default_rng(17 + act)
     g = (rng.integers(-4, 5, N) * 0.125).astype(np.float32)
