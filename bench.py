@@ -54,7 +54,8 @@ KERNEL_SOURCES = {
     c: ("gemm_mfma.hpp", "gemm_v2.hpp", "lds_dma.hpp", "moe_mfma.hip", "common.hpp", "moe_internal.hpp")
     for c in ("router_gemm", "gate_up", "down", "da", "dx", "dense_dw")
 }
-KERNEL_SOURCES.update(masked_dw=("masked_dw.hip", "common.hpp", "moe_internal.hpp"),
+KERNEL_SOURCES.update(topk_fresh=("topk.hip", "common.hpp", "moe_internal.hpp"),
+                      masked_dw=("masked_dw.hip", "common.hpp", "moe_internal.hpp"),
                       adam=("optim.hip", "common.hpp"))
 
 
@@ -224,12 +225,56 @@ def rigl_scan(capi, synth, layer_mod, d, idx, dims, scan_tokens, repeats=2):
             times.append(dt)
         stats = st.cpu().numpy()
         log(f"rigl: scan {rep} {dt:.2f} ms")
-    return dict(rigl_scan_ms=float(np.median(times)), scan_tokens=Ts,
+    parts = scan_parts(capi, layer_mod, lay, idx, grad, r, ws, dims, Ts)
+    log(f"rigl: scan parts {json.dumps({c: round(v['ms'], 4) for c, v in parts.items()})}")
+    return dict(rigl_scan_ms=float(np.median(times)), scan_tokens=Ts, scan_kernels=parts,
                 dequant_ms=float(sum(dq_ms)), dequant_GBps=dq_bytes / (sum(dq_ms) * 1e-3) / 1e9,
                 dequant_affine_g128_ms=float(sum(dqa_ms)),
                 dequant_affine_g128_GBps=dqa_bytes / (sum(dqa_ms) * 1e-3) / 1e9,
                 turnover_applied=float(stats[1]) / k, turnover_topk_vs_old=float(stats[2]) / k,
                 rigl_k=int(k), rigl_r=int(r))
+
+
+def scan_parts(capi, layer_mod, lay, idx, grad, r, ws, dims, Ts):
+    """Time per kernel class inside one RigL scan (HIP events on the launch
+    stream, one scan per class): the dense gradient of every expert weight
+    (operand staging and the two GEMMs), the fresh top-k of |g| over all N
+    (the first selection of the scan), every selection of the reselection,
+    and the merges that build the new list.  Each with its roofline: the
+    dense dW against max(MFMA time, HBM time) of its algorithmic flops and
+    bytes (dW written once, operands read once), the top-k against one read
+    of the N fp32 keys."""
+    import torch
+    T, H, E, K, I = dims
+    N = 3 * E * H * I
+    S = Ts * K
+    out = {}
+    for c in (capi.K_DENSE_DW, capi.K_TOPK, capi.K_RIGL_MERGE):
+        lay.set_active(idx)
+        torch.cuda.synchronize()
+        capi.timer_arm(c, 64)
+        lay.dense_scan(out=grad)
+        layer_mod.rigl(lay, grad, r, ws=ws)
+        torch.cuda.synchronize()
+        ms = capi.timer_read(64)
+        capi.timer_arm(-1)
+        name = capi.KERNEL_CLASS_NAMES[c]
+        if c == capi.K_TOPK:
+            out["topk_fresh"] = dict(ms=ms[0], **roofline_entry("topk_fresh", 0.0, 4.0 * N, ms[0]),
+                                     traffic=counter_traffic("topk_fresh"),
+                                     note="one read of the N fp32 keys is the algorithmic bytes")
+            out["topk_all"] = dict(ms=sum(ms), launches=len(ms))
+        else:
+            out[name] = dict(ms=sum(ms), launches=len(ms))
+    fl = 2.0 * S * 3 * I * H
+    by = 4.0 * N + 2.0 * S * (2 * I + I) + 2.0 * 2 * Ts * H
+    ms = out["dense_dw"]["ms"]
+    t_roof = max(fl / (BF16_PEAK_TFLOPS * 1e12), by / (HBM_PEAK_GBS * 1e9)) * 1e3
+    out["dense_dw"].update(algorithmic_flops=fl, algorithmic_bytes=by, roofline_ms=t_roof,
+                           frac=t_roof / ms, mfma_frac=fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                           hbm_frac=by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           traffic=counter_traffic("dense_dw"))
+    return out
 
 
 def mixtral_layer(capi, synth, layer_mod, steps, lr):
@@ -293,12 +338,15 @@ def mixtral_layer(capi, synth, layer_mod, steps, lr):
             scans.append((time.perf_counter() - t0) * 1e3)
     stats = st.cpu().numpy()
     log(f"mixtral: rigl scan {np.median(scans):.2f} ms")
+    parts = scan_parts(capi, layer_mod, lay, idx, grad, r, ws, dims, T)
+    log(f"mixtral: scan parts {json.dumps({c: round(v['ms'], 4) for c, v in parts.items()})}")
     out = dict(workload="Mixtral-8x7B-shaped single MoE layer sparse train step",
                tokens=T, hidden=H, experts=E, top_k=K, intermediate=I, active_entries=k,
                value=T / (ms * 1e-3), unit="tokens/s", ms_per_step=ms,
                grouped_gemm_tflops=gemm_fl / (gemm_ms * 1e-3) / 1e12,
                grouped_gemm_mfma_frac=gemm_fl / (gemm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-               step_kernels=kern, rigl_scan_ms=float(np.median(scans)), rigl_k=int(k),
+               step_kernels=kern, rigl_scan_ms=float(np.median(scans)), scan_kernels=parts,
+               rigl_k=int(k),
                rigl_r=int(r), turnover_applied=float(stats[1]) / k,
                turnover_topk_vs_old=float(stats[2]) / k)
     del lay, grad, ws
@@ -383,29 +431,167 @@ def stack_run(capi, layers=48, steps=180, reselect_every=50, peak_lr=2e-4):
     return res
 
 
-def cpu_baseline(d, idx, dims, sample_tokens):
-    """The CPU oracle, as it stands, on one train step over a sample of the
-    layer's tokens (same weights and mask); tokens/s."""
+def host_info():
+    """CPU model (lscpu), the threads BLAS uses and NumPy's BLAS build."""
+    import subprocess
     import numpy as np
-    from oracle import usaf_oracle as O
-    T, H, E, K, I = dims
-    R = O.Rounding(O.BF16, O.CONTRACT)
-    X = d["X"][:sample_tokens]
-    tgt = d["tgt"][:sample_tokens]
-    z = np.zeros(idx.size)
-    t0 = time.perf_counter()
-    O.train_step(X, tgt, d["Wr"], d["W_gu"], d["W_d"], K, idx, z, z, np.zeros_like(d["Wr"]),
-                 np.zeros_like(d["Wr"]), 0, 1e-3, 0.9, 0.999, 1e-8, R)
-    dt = time.perf_counter() - t0
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+    except Exception:  # pragma: no cover
+        pass
+    cores, blas = len(os.sched_getaffinity(0)), None
     try:
         from threadpoolctl import threadpool_info
-        cores = max(int(p.get("num_threads", 1)) for p in threadpool_info()) or 1
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if info:
+            cores = int(info[0].get("num_threads", cores))
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')} " \
+                   f"({info[0].get('threading_layer')} threads, {cores})"
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
-    return dict(value=sample_tokens / dt, unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"one oracle train step (forward, loss, masked backward, SparseAdam, "
-                       f"router Adam) on {sample_tokens} of the {T} tokens of the same layer; "
-                       f"{dt:.1f} s", seconds=dt)
+        pass
+    if blas is None:
+        try:
+            cfg = np.show_config(mode="dicts")
+            b = cfg.get("Build Dependencies", {}).get("blas", {})
+            blas = f"{b.get('name')} {b.get('version')}"
+        except Exception:  # pragma: no cover
+            blas = "unknown"
+    return dict(cpu_model=model, cores=cores, blas=blas, numpy=np.__version__)
+
+
+def cpu_baseline(d, idx, dims, gpu):
+    """The CPU oracle, as it stands, on each workload (a baseline, not a
+    target; BLAS threads = the process's CPU affinity).  ``gpu`` holds the
+    GPU's figures of the same run for the ratios.  Where the full oracle run
+    would take minutes, a stated sample is timed and scaled linearly in what
+    its cost is proportional to."""
+    import numpy as np
+    import usaf_synth as synth
+    from oracle import usaf_oracle as O
+    T, H, E, K, I = dims
+    Rb = O.Rounding(O.BF16, O.CONTRACT)
+    tim = lambda f: (lambda t0: (f(), time.perf_counter() - t0))(time.perf_counter())
+    out = {}
+    z = lambda n: np.zeros(n)
+
+    # tiny fp32 layer: everything (importance pass, then 3 steps)
+    tiny = (128, 64, 8, 2, 32)
+    td = synth.moe_layer(*tiny, bf16=False)
+    R32 = O.Rounding(O.F32, O.CONTRACT)
+    tk = O.select_count(3 * 8 * 64 * 32, 5, 100)
+    sc, t_imp = tim(lambda: O.importance_topk(
+        O.dense_scan(td["X"], td["tgt"], td["Wr"], td["W_gu"], td["W_d"], 2, R32)["g"], tk))
+    steps = []
+    st = dict(W_gu=td["W_gu"], W_d=td["W_d"], Wr=td["Wr"], m=z(tk), v=z(tk),
+              mr=np.zeros_like(td["Wr"]), vr=np.zeros_like(td["Wr"]), t=0)
+    for _ in range(3):
+        o, dt = tim(lambda: O.train_step(td["X"], td["tgt"], st["Wr"], st["W_gu"], st["W_d"], 2, sc,
+                                         st["m"], st["v"], st["mr"], st["vr"], st["t"], 1e-3, 0.9,
+                                         0.999, 1e-8, R32))
+        gu_, dd_ = O.unflatten(o["W_flat"], O.Shape(*tiny))
+        st.update(W_gu=gu_, W_d=dd_, Wr=o["Wr"], m=o["m"], v=o["v"], mr=o["mr"], vr=o["vr"], t=o["t"])
+        steps.append(dt)
+    out["tiny_fp32"] = dict(importance_pass_s=t_imp, step_s=steps,
+                            tokens_per_s=128 / float(np.median(steps)), sample="all of it")
+    log(f"cpu baseline: tiny layer importance {t_imp:.2f} s, steps {[round(x, 2) for x in steps]}")
+
+    # Qwen3-shaped layer: 3 full steps on the same batch and mask, median
+    steps = []
+    for _ in range(3):
+        _, dt = tim(lambda: O.train_step(d["X"], d["tgt"], d["Wr"], d["W_gu"], d["W_d"], K, idx,
+                                         z(idx.size), z(idx.size), np.zeros_like(d["Wr"]),
+                                         np.zeros_like(d["Wr"]), 0, 1e-3, 0.9, 0.999, 1e-8, Rb))
+        steps.append(dt)
+        log(f"cpu baseline: qwen3 step {dt:.1f} s")
+    med = float(np.median(steps))
+    out["qwen3_step"] = dict(step_s=steps, median_s=med, tokens_per_s=T / med,
+                             gpu_ratio=gpu.get("qwen3_tokens_per_s", 0) / (T / med),
+                             sample="3 full steps (4096 tokens, 3,019,898 listed entries), median")
+
+    # RigL scan inputs: dequant (1/16 of the rows, scaled), the dense scan on
+    # all 8192 tokens, the selection on the first N/8 entries (scaled)
+    N = 3 * E * H * I
+    rows = E * 2 * I
+    q, sc16 = synth.quantize_int4_g64(d["W_gu"].reshape(rows, H)[: rows // 16])
+    _, t_dq = tim(lambda: O.dequant_int4(q, sc16))
+    t_dq *= 16 * (N / (rows * H))  # the sampled rows hold 1/16 of gate_up, scaled to all N
+    Xs = synth.to_bf16_values(synth.normal((8192, H), 1.0, 10))
+    tg = synth.to_bf16_values(synth.normal((8192, H), 1.0, 14))
+    scan, t_scan = tim(lambda: O.dense_scan(Xs, tg, d["Wr"], d["W_gu"], d["W_d"], K, Rb))
+    n8, k8 = N // 8, (N * 5 // 1000) // 8
+    g8 = scan["g"][:n8]
+    del scan
+    _, t_tk = tim(lambda: O.importance_topk(g8, k8))
+    old8 = synth.random_mask(n8, k8, 5)
+    wsel = d["W_gu"].ravel()[:n8]  # N/8 < the gate_up part
+    _, t_rg = tim(lambda: O.rigl_reselect(g8, wsel, old8, z(k8), z(k8), k8, (3 * k8) // 10))
+    del g8, wsel
+    scan_s = t_scan + 8 * (t_tk + t_rg)
+    out["qwen3_dequant_and_scan"] = dict(
+        dequant_s=t_dq, scan_s=scan_s, dense_scan_s=t_scan, topk_s=8 * t_tk, rigl_s=8 * t_rg,
+        gpu_ratio=scan_s * 1e3 / max(gpu.get("rigl_scan_ms", 0) or 1e-9, 1e-9),
+        sample="dequant: 1/16 of the gate_up rows, scaled to all 604M weights; dense scan: all "
+               "8192 tokens; top-k and RigL: the first N/8 gradient entries (k/8, r/8), scaled x8")
+    log(f"cpu baseline: qwen3 dequant {t_dq:.1f} s (scaled), scan {scan_s:.1f} s")
+
+    # Mixtral-shaped layer: the oracle step at 128 and 256 tokens, each part
+    # extrapolated to 4096 tokens along the line through the two (the fixed
+    # part, fp64 copies of 0.94e9 expert weights, does not grow with the
+    # tokens); the listed gradient on a 40,000-entry sample of the 7,046,430
+    # and Adam on the same sample, scaled by entries
+    me, mk2, mi, mh = 8, 2, 14336, 4096
+    md = synth.moe_layer(256, mh, me, mk2, mi, bf16=True, seeds=(20, 21, 22, 23, 24))
+    Nm = 3 * me * mh * mi
+    km = Nm * 5 // 1000
+    samp = synth.random_mask(Nm, 40000, 25)
+    Rm = O.Rounding(O.BF16, O.CONTRACT)
+    parts = {}
+    for mt in (128, 256):
+        Xm, tm = md["X"][:mt], md["tgt"][:mt]
+        fw, t_f = tim(lambda: O.moe_forward(Xm, md["Wr"], md["W_gu"], md["W_d"], mk2, Rm))
+        (_, dYm), t_l = tim(lambda: O.mse_loss_grad(fw["Y"], tm, Rm))
+        bw, t_b = tim(lambda: O.moe_backward(fw, Xm, md["Wr"], md["W_gu"], md["W_d"], dYm, Rm))
+        gm, t_g = tim(lambda: O.weight_grads_at(fw, bw, Xm, dYm, samp,
+                                                O.Shape(mt, mh, me, mk2, mi), Rm))
+        parts[mt] = (t_f + t_l + t_b, t_g)
+        del fw, bw
+    line = lambda a, b: a + (b - a) * (4096 - 128) / (256 - 128)
+    fwbw = line(parts[128][0], parts[256][0])
+    grad = line(parts[128][1], parts[256][1]) * (km / samp.size)
+    ngu = me * 2 * mi * mh
+    f = samp.astype(np.int64)
+    w_at = np.where(f < ngu, md["W_gu"].ravel()[np.minimum(f, ngu - 1)],
+                    md["W_d"].ravel()[np.maximum(f - ngu, 0)])
+    _, t_a = tim(lambda: O.adam_update(w_at, gm, z(samp.size), z(samp.size), 1, 1e-3, 0.9, 0.999,
+                                       1e-8, O.BF16, Rm))
+    del md
+    step_m = fwbw + grad + t_a * (km / samp.size)
+    out["mixtral_step"] = dict(
+        step_s=step_m, tokens_per_s=4096 / step_m, measured_s={str(t): v for t, v in parts.items()},
+        gpu_ratio=(gpu.get("mixtral_tokens_per_s") or 0) / (4096 / step_m),
+        sample="forward, loss and backward timed at 128 and 256 tokens and extrapolated along "
+               "that line to 4096; the listed gradient likewise on 40,000 of the 7,046,430 "
+               "entries, scaled by entries; Adam on the sample, scaled by entries.  The dense RigL "
+               "scan over 1.41e9 weights is not timed on the host (its fp64 gradient alone is 11 GB)")
+    log(f"cpu baseline: mixtral step {step_m:.1f} s (extrapolated)")
+
+    # the 48-layer stack: extrapolated from the single-layer figures
+    per_layer_scan = out["qwen3_dequant_and_scan"]["scan_s"]
+    run_s = 180 * 48 * med + 4 * 48 * per_layer_scan
+    out["stack48_extrapolated"] = dict(
+        extrapolated=True, run_s=run_s, tokens_per_s=180 * 4096 / run_s,
+        how="48 layers x 180 steps x the Qwen3 step median, plus 4 reselections x 48 layers x "
+            "the Qwen3 scan above (8192 tokens: an upper figure for the stack's 4096, since the "
+            "oracle's scan is dominated by its gradient over all N weights); residual adds "
+            "neglected")
+    info = host_info()
+    return dict(value=T / med, unit="tokens/s", cores=info["cores"], kind="oracle",
+                sample="Qwen3-shaped layer: median of 3 full oracle train steps (4096 tokens); "
+                       "the other workloads under configs", seconds=med, host=info, configs=out)
 
 
 def main():
@@ -428,7 +614,6 @@ def main():
                     help="skip the timed train steps; run only the RigL scan (profiling)")
     ap.add_argument("--print-sha", action="store_true",
                     help="print the source hash of each counter-measured kernel class and exit")
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -543,8 +728,10 @@ def main():
         log("stacked workload")
         out["stack"] = stack_run(capi, steps=args.stack_steps)
     if not args.no_cpu:
-        log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
-        out["cpu_baseline"] = cpu_baseline(d, idx, dims, args.cpu_tokens)
+        log("cpu baseline: the oracle on every workload")
+        gpu = dict(qwen3_tokens_per_s=value, rigl_scan_ms=out.get("rigl_scan_ms"),
+                   mixtral_tokens_per_s=(out.get("mixtral") or {}).get("value"))
+        out["cpu_baseline"] = cpu_baseline(d, idx, dims, gpu)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
