@@ -72,7 +72,8 @@ typedef enum {
   USAF_WS_BACKWARD = 1,
   USAF_WS_TOPK = 2,
   USAF_WS_RIGL = 3,
-  USAF_WS_MASKED_PLAN = 4
+  USAF_WS_MASKED_PLAN = 4,
+  USAF_WS_UNION = 5
 } usaf_ws_kind;
 
 /* One MoE layer: T tokens, hidden H, E experts, top-K routing, expert
@@ -112,7 +113,8 @@ typedef struct {
 /* Bytes of workspace `kind` needs for `shape` (FORWARD, BACKWARD,
  * MASKED_PLAN: the plan of usaf_masked_plan for any list) or for a
  * selection over n keys picking k (TOPK: n = N, k; RIGL: n = N, k = active
- * count).  `shape` may be NULL for TOPK / RIGL.  Result goes to HOST *bytes.
+ * count) or for usaf_sorted_union of lists totalling n entries (UNION).
+ * `shape` may be NULL for TOPK / RIGL / UNION.  Result goes to HOST *bytes.
  * Returns USAF_ERR_INVALID_ARG for a bad kind, size or null `bytes`. */
 USAF_API usaf_status usaf_workspace_size(int32_t kind, const usaf_moe_shape *shape, int64_t n,
                                 int64_t k, size_t *bytes /* HOST */);
@@ -298,6 +300,24 @@ USAF_API usaf_status usaf_mse_grad_noalloc(const usaf_moe_shape *shape, const vo
  * with n > 0. */
 USAF_API usaf_status usaf_residual_add(int32_t act, const void *a, const void *b, void *out,
                               int64_t n, hipStream_t stream);
+
+/* Sorted union of two strictly ascending u32 lists a[na] and b[nb] (the
+ * bookkeeping of a training run that keeps every index ever selected, since
+ * RigL keeps the trained values of the entries it drops: README "how it
+ * works", sparsity bullet).  out (capacity na + nb, must not alias a or b)
+ * receives the union, strictly ascending, and *n_out (device int64) its
+ * length.  ws: USAF_WS_UNION bytes for n = na + nb.  Errors: INVALID_ARG for
+ * negative sizes, na + nb >= 2^32 or null pointers where entries exist;
+ * WORKSPACE for a short ws. */
+USAF_API usaf_status usaf_sorted_union(const uint32_t *a, int64_t na, const uint32_t *b, int64_t nb,
+                                       uint32_t *out, int64_t *n_out, void *ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
+/* out[i] = in[i + 1] - in[i] for i < n (int32): the slots each expert
+ * received from the forward's offsets (the router load-balance monitor of a
+ * training run).  Errors: INVALID_ARG for n < 0 or null pointers with n > 0. */
+USAF_API usaf_status usaf_adjacent_diff(const int32_t *in, int64_t n, int32_t *out,
+                                        hipStream_t stream);
 
 /* Routing alone, from given fp32 logits [T, E]: writes state->topk_ids,
  * topk_w, offsets, perm, slot_pos exactly as usaf_moe_forward does. */

@@ -673,20 +673,27 @@ def stack_scan_grads(X0, tgt, layers: list, K: int, R: Rounding) -> dict:
 
 
 def stack_train_step(X0, tgt, layers: list, K: int, t: int, lr, beta1, beta2, eps,
-                     R: Rounding) -> dict:
+                     R: Rounding, train_from: int = 0) -> dict:
     """One sparse step of the whole stack.  ``layers[l]`` also holds its active
     list idx and its moments m, v, mr, vr.  Every layer's gradients are taken
     first; if the loss, the last output's gradient, or any layer's listed or
     router gradient is non-finite, no layer is updated and the step count
     stays (README results table: NaN steps are skipped).  Otherwise each
     layer takes SparseAdam on its list and dense Adam on its router with the
-    shared step count t + 1."""
+    shared step count t + 1.
+
+    ``train_from`` (README environment-variable table: TRAIN_FROM freezes the
+    layers below it): the layers below it are frozen -- they need no list or
+    moments, their gradients are not taken and they are never updated; only
+    the trained layers' gradients enter the NaN rule."""
     fwd = stack_forward(X0, layers, K, R)
     loss, GL = mse_loss_grad(fwd["Xs"][-1], tgt, R)
     bwd = stack_backward(fwd, layers, GL, R)
-    gs = []
+    gs = [None] * train_from
     finite = is_finite_all([loss], GL)
     for l, lay in enumerate(layers):
+        if l < train_from:
+            continue
         shape = Shape(np.shape(X0)[0], np.shape(X0)[1], lay["W_gu"].shape[0], K, lay["W_d"].shape[2])
         g = weight_grads_at(fwd["fws"][l], bwd["bws"][l], fwd["Xs"][l], bwd["dYs"][l], lay["idx"],
                             shape, R)
@@ -696,8 +703,10 @@ def stack_train_step(X0, tgt, layers: list, K: int, t: int, lr, beta1, beta2, ep
     if not finite:
         out.update(layers=[dict(lay) for lay in layers], t=t)
         return out
-    new_layers = []
+    new_layers = [dict(lay) for lay in layers[:train_from]]
     for l, lay in enumerate(layers):
+        if l < train_from:
+            continue
         shape = Shape(np.shape(X0)[0], np.shape(X0)[1], lay["W_gu"].shape[0], K, lay["W_d"].shape[2])
         flat = np.concatenate([np.asarray(lay["W_gu"], np.float64).ravel(),
                                np.asarray(lay["W_d"], np.float64).ravel()])

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libusaf.so")
 USAF_OK, USAF_ERR_INVALID_ARG, USAF_ERR_UNSUPPORTED, USAF_ERR_WORKSPACE, USAF_ERR_HIP, \
     USAF_ERR_NOT_IMPLEMENTED = range(6)
 F32, BF16 = 0, 1
-WS_FORWARD, WS_BACKWARD, WS_TOPK, WS_RIGL, WS_MASKED_PLAN = range(5)
+WS_FORWARD, WS_BACKWARD, WS_TOPK, WS_RIGL, WS_MASKED_PLAN, WS_UNION = range(6)
 
 # Every symbol include/usaf.h declares.
 EXPORTS = (
@@ -26,7 +26,8 @@ EXPORTS = (
     "usaf_rigl_reselect", "usaf_sparse_adam", "usaf_dequant_resident", "usaf_dequant_affine",
     "usaf_mse_grad", "usaf_mse_grad_noalloc",
     "usaf_route", "usaf_status_string", "usaf_version", "usaf_timer_arm", "usaf_timer_read",
-    "usaf_gather", "usaf_residual_add", "usaf_masked_plan",
+    "usaf_gather", "usaf_residual_add", "usaf_masked_plan", "usaf_sorted_union",
+    "usaf_adjacent_diff",
 )
 
 # Kernel classes of the timing hook (usaf_kernel_class).
@@ -94,6 +95,8 @@ def _load():
         "usaf_mse_grad_noalloc": [vp, vp, vp, vp, vp, vp, vp],
         "usaf_route": [vp, vp, vp, vp],
         "usaf_residual_add": [i32, vp, vp, vp, i64, vp],
+        "usaf_sorted_union": [vp, i64, vp, i64, vp, vp, vp, sz, vp],
+        "usaf_adjacent_diff": [vp, i64, vp, vp],
         "usaf_status_string": [i32],
         "usaf_version": [],
         "usaf_timer_arm": [i32, i32],
@@ -234,6 +237,16 @@ def mse_grad_noalloc(shape, Y, tgt, dY, loss, nonfinite, stream=None):
 def residual_add(act, a, b, out, n, stream=None):
     _check(lib.usaf_residual_add(int(act), _p(a), _p(b), _p(out), int(n), _stream(stream)),
            "usaf_residual_add")
+
+
+def sorted_union(a, na, b, nb, out, n_out, ws, stream=None):
+    _check(lib.usaf_sorted_union(_p(a), int(na), _p(b), int(nb), _p(out), _p(n_out), _p(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)),
+           "usaf_sorted_union")
+
+
+def adjacent_diff(inp, n, out, stream=None):
+    _check(lib.usaf_adjacent_diff(_p(inp), int(n), _p(out), _stream(stream)), "usaf_adjacent_diff")
 
 
 def route(shape, logits, state: State, stream=None):

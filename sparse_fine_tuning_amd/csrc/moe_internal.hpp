@@ -122,4 +122,5 @@ usaf_status masked_plan_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64
 // Workspace of one top-k selection over n keys / one RigL reselection.
 size_t topk_ws_bytes(int64_t n);
 size_t rigl_ws_bytes(int64_t N, int64_t k);
+size_t union_ws_bytes(int64_t n);  // usaf_sorted_union of lists totalling n entries
 }  // namespace usaf

@@ -253,9 +253,29 @@ extern "C" usaf_status usaf_workspace_size(int32_t kind, const usaf_moe_shape* s
       USAF_TRY(check_shape(shape));
       *bytes = shape->act == USAF_BF16 ? size_t(masked_plan_bytes(*shape)) : 256;
       return USAF_OK;
+    case USAF_WS_UNION:
+      if (n < 0 || n >= (int64_t(1) << 32)) return USAF_ERR_INVALID_ARG;
+      *bytes = union_ws_bytes(n);
+      return USAF_OK;
     default:
       return USAF_ERR_INVALID_ARG;
   }
+}
+
+__global__ __launch_bounds__(256) void adjacent_diff_kernel(const int32_t* __restrict__ in, int64_t n,
+                                                             int32_t* __restrict__ out) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = in[i + 1] - in[i];
+}
+
+extern "C" usaf_status usaf_adjacent_diff(const int32_t* in, int64_t n, int32_t* out,
+                                          hipStream_t stream) {
+  if (n < 0 || (n > 0 && (!in || !out))) return USAF_ERR_INVALID_ARG;
+  if (n == 0) return USAF_OK;
+  hipLaunchKernelGGL(adjacent_diff_kernel, dim3(unsigned(ceil_div(n, 256))), dim3(256), 0, stream,
+                     in, n, out);
+  USAF_LAUNCH_CHECK();
+  return USAF_OK;
 }
 
 extern "C" const char* usaf_status_string(usaf_status s) {

@@ -1219,6 +1219,83 @@ __global__ __launch_bounds__(256) void rigl_place_kernel(
   }
 }
 
+// Sorted union of two strictly ascending lists a and b.  Block q holds a's
+// entries from q*kPB and the b entries whose values fall in its range
+// (b[bounds[q], bounds[q+1])); b entries equal to an a entry are dropped.
+// Pass 0 writes each block's output count; pass 1 (after their scan) writes
+// the block's entries at its offset, in ascending order.
+template <int kPass>
+__global__ __launch_bounds__(256) void union_merge_kernel(const uint32_t* __restrict__ a, int64_t na,
+                                                          const uint32_t* __restrict__ b,
+                                                          const uint32_t* __restrict__ bounds,
+                                                          uint32_t* __restrict__ cnt,
+                                                          uint32_t* __restrict__ out) {
+  __shared__ uint32_t as[kPB];
+  __shared__ uint32_t adup[kPB + 1];  // a entry present in b, then the count of those before
+  __shared__ uint32_t bs[kPCap];
+  const int tid = threadIdx.x;
+  const int64_t q0 = int64_t(blockIdx.x) * kPB;
+  const int nq = int(min(int64_t(kPB), na - q0));
+  for (int j = tid; j < kPB; j += 256) {
+    as[j] = j < nq ? a[q0 + j] : 0xffffffffu;
+    adup[j] = 0;
+  }
+  const uint32_t b0 = bounds[blockIdx.x], b1 = bounds[blockIdx.x + 1];
+  const int blen = int(b1 - b0);
+  const bool staged = blen <= kPCap;
+  if (staged)
+    for (int j = tid; j < blen; j += 256) bs[j] = b[b0 + j];
+  __syncthreads();
+  // mark the a entries that b also holds (each b value lands on at most one)
+  uint32_t nnew = 0;  // b entries of this thread that a lacks
+  for (int j = tid; j < blen; j += 256) {
+    const uint32_t v = staged ? bs[j] : b[b0 + j];
+    const int p = lds_lower_bound(as, nq, v);
+    if (p < nq && as[p] == v) adup[p] = 1;
+    else ++nnew;
+  }
+  __syncthreads();
+  if (kPass == 0) {
+    uint32_t total;
+    block_excl_256(nnew, total);
+    if (tid == 0) cnt[blockIdx.x] = uint32_t(nq) + total;
+    return;
+  }
+  {  // exclusive scan of the duplicate flags, 8 per thread
+    uint32_t f[8], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      f[j] = adup[tid * 8 + j];
+      sum += f[j];
+    }
+    uint32_t total;
+    uint32_t run = block_excl_256(sum, total);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      adup[tid * 8 + j] = run;
+      run += f[j];
+    }
+    if (tid == 0) adup[kPB] = total;
+  }
+  __syncthreads();
+  const uint32_t base = cnt[blockIdx.x];
+  // an a entry lands after the block's a entries and new b entries below it
+  for (int j = tid; j < nq; j += 256) {
+    const uint32_t v = as[j];
+    const int below = staged ? lds_lower_bound(bs, blen, v) : int(lower_bound_u32(b + b0, blen, v));
+    // b entries below v: the new ones, plus the duplicates of a entries below v
+    out[base + j + (below - adup[j])] = v;
+  }
+  // a new b entry lands after the a entries below it and the new b entries before it
+  for (int j = tid; j < blen; j += 256) {
+    const uint32_t v = staged ? bs[j] : b[b0 + j];
+    const int p = lds_lower_bound(as, nq, v);
+    if (p < nq && as[p] == v) continue;  // already in a
+    // b entries before j: j of them, adup[p] of which are duplicates (of a entries below v)
+    out[base + p + (j - adup[p])] = v;
+  }
+}
+
 // Compact keys of RigL's list-sized selections: the drop key of W at each
 // old entry and (when the fresh top-k is to give the grow set) |g| at each
 // fresh entry.
@@ -1395,4 +1472,41 @@ extern "C" usaf_status usaf_rigl_reselect(const usaf_moe_shape* shape, const flo
 
 namespace usaf {
 size_t rigl_ws_bytes(int64_t N, int64_t k) { return ws_rigl(N, k).total; }
+size_t union_ws_bytes(int64_t na) {
+  const int64_t nblk = na > 0 ? ceil_div(na, kPB) : 0;
+  return 2 * align256(size_t(nblk + 1) * 4) + align256(size_t(ceil_div(nblk + 1, kScanSeg) + 1) * 4) +
+         256;
+}
+__global__ void union_count_kernel(const uint32_t* total, int64_t* n_out) { *n_out = int64_t(*total); }
 }  // namespace usaf
+
+extern "C" usaf_status usaf_sorted_union(const uint32_t* a, int64_t na, const uint32_t* b, int64_t nb,
+                                         uint32_t* out, int64_t* n_out, void* ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+  if (na < 0 || nb < 0 || na + nb >= (int64_t(1) << 32)) return USAF_ERR_INVALID_ARG;
+  if ((na && !a) || (nb && !b) || (na + nb && !out) || !n_out) return USAF_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < usaf::union_ws_bytes(na + nb)) return USAF_ERR_WORKSPACE;
+  if (na == 0) {  // the union is b (a copy) -- as a merge of b with an empty list
+    std::swap(a, b);
+    std::swap(na, nb);
+  }
+  const int64_t nblk = na ? ceil_div(na, kPB) : 0;
+  uint32_t* w = static_cast<uint32_t*>(ws);
+  uint32_t* bounds = w;                                   // [nblk + 1]
+  uint32_t* cnt = w + align256(size_t(nblk + 1) * 4) / 4;  // [nblk] counts, then offsets
+  uint32_t* bsum = cnt + align256(size_t(nblk + 1) * 4) / 4;
+  uint32_t* total = bsum + align256(size_t(ceil_div(nblk + 1, kScanSeg) + 1) * 4) / 4;
+  hipLaunchKernelGGL(rigl_stats_init_kernel, dim3(1), dim3(1), 0, stream, total);
+  if (nblk > 0) {
+    hipLaunchKernelGGL(part_bounds_kernel, dim3(unsigned(ceil_div(nblk + 1, 4))), dim3(256), 0, stream,
+                       a, nblk, b, nb, bounds, nullptr);
+    hipLaunchKernelGGL(union_merge_kernel<0>, dim3(unsigned(nblk)), dim3(256), 0, stream, a, na, b,
+                       bounds, cnt, out);
+    scan_launch(cnt, nblk, bsum, nullptr, total, stream);
+    hipLaunchKernelGGL(union_merge_kernel<1>, dim3(unsigned(nblk)), dim3(256), 0, stream, a, na, b,
+                       bounds, cnt, out);
+  }
+  hipLaunchKernelGGL(union_count_kernel, dim3(1), dim3(1), 0, stream, total, n_out);
+  USAF_LAUNCH_CHECK();
+  return USAF_OK;
+}

@@ -19,10 +19,14 @@ layer in one backward, selecting each layer's list from its own gradient
 before the next layer's backward reuses the dense buffer.
 
 Around the step (README environment-variable table: STEPS, RESELECT_EVERY,
-the NaN-skip count of the results): a checkpoint holds what a resume needs
-on top of the base weights (every layer's list, moments, router and its
-moments, the weights at every index ever selected, the step and skip
-counts), and the expert load of the last forward is readable per layer.
+TRAIN_FROM, the NaN-skip count of the results): the layers below
+``train_from`` are frozen, as the README freezes the lower layers of a
+model -- they run their forward only, since no trainable weight lies below
+them, and hold no list, moments or gradient buffers; a checkpoint holds
+what a resume needs on top of the base weights (every trained layer's list,
+moments, router and its moments, the weights at every index ever selected,
+the step and skip counts); and the expert load of the last forward is
+readable per layer.
 
 PyTorch only owns device memory; every step runs in libusaf.so's kernels.
 """
@@ -47,34 +51,51 @@ def cosine_lr(step: int, total: int, peak: float) -> float:
 
 
 class _Layer:
-    """Parameters, optimiser state and saved forward state of one layer."""
+    """Parameters, optimiser state and saved forward state of one layer.  A
+    frozen layer keeps its own routing state (for the expert-load monitor)
+    but shares the large saved activations with the other frozen layers and
+    has no router moments or gradient."""
 
-    def __init__(self, shape: capi.Shape, shared: dict, dev: torch.device):
+    def __init__(self, shape: capi.Shape, shared: dict, dev: torch.device, frozen: bool = False):
         T, H, E, K, I, act = shape.T, shape.H, shape.E, shape.K, shape.I, shape.act
         dt = _dt(act)
         S = T * K
         z = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=dev)
+        big = shared["frozen_acts"] if frozen else dict(gu=z(S, 2 * I, dtype=dt), a=z(S, I, dtype=dt))
         self.st = dict(
             logits=z(T, E), topk_ids=z(T, K, dtype=torch.int32), topk_w=z(T, K),
             offsets=z(E + 1, dtype=torch.int32), perm=z(S, dtype=torch.int32),
-            slot_pos=z(S, dtype=torch.int32), gu=z(S, 2 * I, dtype=dt), a=z(S, I, dtype=dt),
+            slot_pos=z(S, dtype=torch.int32), gu=big["gu"], a=big["a"],
             dgu=shared["dgu"], dw=shared["dw"])
         self.state = capi.make_state(self.st)
+        self.frozen = frozen
         self.W = z(shape.N, dtype=dt)
         self.Wr = z(E, H)
-        self.mr = torch.zeros(E, H, dtype=torch.float32, device=dev)
-        self.vr = torch.zeros(E, H, dtype=torch.float32, device=dev)
-        self.dWr = z(E, H)
+        if frozen:
+            self.mr = self.vr = self.dWr = None
+        else:
+            self.mr = torch.zeros(E, H, dtype=torch.float32, device=dev)
+            self.vr = torch.zeros(E, H, dtype=torch.float32, device=dev)
+            self.dWr = z(E, H)
         self.shape = shape
         self.idx = self.m = self.v = self.dW = self.w_list = self.plan = None
-        self.touched = None  # int64 ascending: every index selected so far
+        self.touched = None  # int32 tensor of ascending uint32: every index selected so far
 
     def note_touched(self):
         """Adds the current list to the touched set (its weights may differ
         from the base weights from now on: RigL keeps the values of dropped
-        entries)."""
-        cur = self.idx.long() & 0xFFFFFFFF
-        self.touched = cur.clone() if self.touched is None else torch.unique(torch.cat([self.touched, cur]))
+        entries): a sorted-union merge on the device; its length is read
+        back (one small synchronisation, at reselections only)."""
+        if self.touched is None:
+            self.touched = self.idx.clone()
+            return
+        na, nb = self.touched.numel(), self.idx.numel()
+        out = torch.empty(na + nb, dtype=torch.int32, device=self.idx.device)
+        n_out = torch.zeros(1, dtype=torch.int64, device=self.idx.device)
+        ws = torch.empty(capi.workspace_size(capi.WS_UNION, None, na + nb), dtype=torch.uint8,
+                         device=self.idx.device)
+        capi.sorted_union(self.touched, na, self.idx, nb, out, n_out, ws)
+        self.touched = out[: int(n_out.item())].clone()
 
     def set_active(self, idx: torch.Tensor, act: int):
         """Active list (int32 tensor of ascending uint32 flat indices) with
@@ -103,15 +124,21 @@ class _Layer:
 class MoEStack:
     """``n_layers`` MoE layers of one shape on one device."""
 
-    def __init__(self, n_layers, T, H, E, K, I, act=BF16, device="cuda"):
+    def __init__(self, n_layers, T, H, E, K, I, act=BF16, device="cuda", train_from=0):
+        if not 0 <= train_from < n_layers:
+            raise ValueError("train_from must name a layer of the stack")
         self.shape = capi.Shape(T, H, E, K, I, act)
         self.act = act
         self.n_layers = n_layers
+        self.train_from = train_from
         self.device = dev = torch.device(device)
         dt = _dt(act)
         z = lambda *s, dtype=torch.float32: torch.empty(*s, dtype=dtype, device=dev)
         shared = dict(dgu=z(T * K, 2 * I, dtype=dt), dw=z(T, K))
-        self.layers = [_Layer(self.shape, shared, dev) for _ in range(n_layers)]
+        if train_from > 0:
+            shared["frozen_acts"] = dict(gu=z(T * K, 2 * I, dtype=dt), a=z(T * K, I, dtype=dt))
+        self.layers = [_Layer(self.shape, shared, dev, frozen=l < train_from)
+                       for l in range(n_layers)]
         self.ws_fwd = z(capi.workspace_size(capi.WS_FORWARD, self.shape), dtype=torch.uint8)
         self.ws_bwd = z(capi.workspace_size(capi.WS_BACKWARD, self.shape), dtype=torch.uint8)
         self.Xs = [z(T, H, dtype=dt) for _ in range(n_layers + 1)]  # X_0 .. X_L
@@ -154,33 +181,39 @@ class MoEStack:
             capi.residual_add(self.act, self.Xs[l], self.Y, self.Xs[l + 1], n, stream)
 
     def backward(self, select=None, stream=None):
-        """Backward from the loss of the last output.  With ``select`` (a
-        callable (l, dense_grad)), every layer's dense expert-weight gradient
-        is formed instead of the listed one and handed to it at once."""
+        """Backward from the loss of the last output down to the lowest
+        trained layer (nothing below it trains, so it forms no input
+        gradient).  With ``select`` (a callable (l, dense_grad)), every
+        trained layer's dense expert-weight gradient is formed instead of the
+        listed one and handed to it at once."""
         n = self.shape.T * self.shape.H
         capi.mse_grad(self.shape, self.Xs[-1], self.tgt, self.G[0], self.loss, self.nonfinite,
                       self.ws_fwd, stream)
         cur = 0
-        for l in range(self.n_layers - 1, -1, -1):
+        for l in range(self.n_layers - 1, self.train_from - 1, -1):
             lay = self.layers[l]
             G, Gn = self.G[cur], self.G[cur ^ 1]
+            dX = self.dXl if l > self.train_from else None
             if select is None:
                 capi.masked_backward(self.shape, self.Xs[l], lay.Wr, lay.W, lay.state, G, lay.idx,
-                                     lay.idx.numel(), lay.dW, lay.dWr, self.dXl, self.nonfinite,
+                                     lay.idx.numel(), lay.dW, lay.dWr, dX, self.nonfinite,
                                      self.ws_bwd, stream, plan=lay.plan)
             else:
                 dense = self._dense_buffer()
                 capi.masked_backward(self.shape, self.Xs[l], lay.Wr, lay.W, lay.state, G, None,
-                                     self.shape.N, dense, lay.dWr, self.dXl, None, self.ws_bwd,
-                                     stream)
+                                     self.shape.N, dense, lay.dWr, dX, None, self.ws_bwd, stream)
                 select(l, dense)
-            if l > 0:
+            if l > self.train_from:
                 capi.residual_add(self.act, G, self.dXl, Gn, n, stream)
                 cur ^= 1
 
+    def trained(self):
+        """The layers that train (from ``train_from`` up)."""
+        return self.layers[self.train_from:]
+
     def adam(self, step, lr, betas=(0.9, 0.999), eps=1e-8, stream=None):
         b1, b2 = betas
-        for lay in self.layers:
+        for lay in self.trained():
             capi.sparse_adam(self.act, lay.W, lay.idx, lay.idx.numel(), lay.dW, lay.m, lay.v, step,
                              lr, b1, b2, eps, self.nonfinite, stream, w_list=lay.w_list)
             capi.sparse_adam(F32, lay.Wr, None, lay.Wr.numel(), lay.dWr, lay.mr, lay.vr, step, lr,
@@ -212,8 +245,8 @@ class MoEStack:
         return self._ws_topk
 
     def importance(self, k: int, stream=None):
-        """The importance pass: every layer's active list is the top-k of its
-        own dense gradient on the current batch."""
+        """The importance pass: every trained layer's active list is the
+        top-k of its own dense gradient on the current batch."""
         ws = self._topk_ws()
 
         def pick(l, grad):
@@ -225,9 +258,10 @@ class MoEStack:
         self.backward(select=pick, stream=stream)
 
     def rigl(self, r: int, stream=None) -> torch.Tensor:
-        """RigL reselection of every layer on the current batch; returns the
-        device stats [n_layers, 3] (int64) of usaf_rigl_reselect."""
-        k = self.layers[0].idx.numel()
+        """RigL reselection of every trained layer on the current batch;
+        returns the device stats [n_layers, 3] (int64) of usaf_rigl_reselect
+        (zero rows for frozen layers)."""
+        k = self.layers[self.train_from].idx.numel()
         if self._ws_rigl is None:
             self._ws_rigl = torch.empty(capi.workspace_size(capi.WS_RIGL, None, self.shape.N, k),
                                         dtype=torch.uint8, device=self.device)
@@ -251,8 +285,13 @@ class MoEStack:
     # ---- monitoring, checkpoint / resume --------------------------------------
     def expert_load(self) -> torch.Tensor:
         """Slots routed to each expert in every layer's last forward: int32
-        [n_layers, E] (each row sums to T*K)."""
-        return torch.stack([torch.diff(lay.st["offsets"]) for lay in self.layers])
+        [n_layers, E] (each row sums to T*K), the differences of each layer's
+        expert offsets."""
+        E = self.shape.E
+        out = torch.empty(self.n_layers, E, dtype=torch.int32, device=self.device)
+        for l, lay in enumerate(self.layers):
+            capi.adjacent_diff(lay.st["offsets"], E, out[l])
+        return out
 
     def state_dict(self) -> dict:
         """Host tensors of a resume point: the step and skip counts and, per
@@ -261,8 +300,11 @@ class MoEStack:
         touched set are the base weights, which the resuming stack loads
         itself (a 48-layer Qwen3-shaped stack holds 58 GB of them)."""
         sd = {"t": torch.tensor([self.t], dtype=torch.int64),
-              "skipped": torch.tensor([self.skipped], dtype=torch.int64)}
+              "skipped": torch.tensor([self.skipped], dtype=torch.int64),
+              "train_from": torch.tensor([self.train_from], dtype=torch.int64)}
         for l, lay in enumerate(self.layers):
+            if lay.frozen:
+                continue
             p = f"layer{l}."
             sd[p + "idx"] = lay.idx.cpu()
             sd[p + "m"] = lay.m.cpu()
@@ -271,7 +313,7 @@ class MoEStack:
             sd[p + "mr"] = lay.mr.cpu()
             sd[p + "vr"] = lay.vr.cpu()
             sd[p + "touched"] = lay.touched.cpu()
-            sd[p + "touched_w"] = lay.W[lay.touched].cpu()
+            sd[p + "touched_w"] = lay.W[lay.touched.long() & 0xFFFFFFFF].cpu()
         return sd
 
     def load_state_dict(self, sd: dict):
@@ -279,12 +321,16 @@ class MoEStack:
         weights are loaded; the following steps then repeat, bit for bit, the
         steps of the run that saved it."""
         dev = self.device
+        if int(sd.get("train_from", torch.zeros(1, dtype=torch.int64))[0]) != self.train_from:
+            raise ValueError("the checkpoint was saved by a stack with another train_from")
         self.t = int(sd["t"][0])
         self.skipped = int(sd["skipped"][0])
         for l, lay in enumerate(self.layers):
+            if lay.frozen:
+                continue
             p = f"layer{l}."
             touched = sd[p + "touched"].to(dev)
-            lay.W[touched] = sd[p + "touched_w"].to(dev)
+            lay.W[touched.long() & 0xFFFFFFFF] = sd[p + "touched_w"].to(dev)
             lay.Wr.copy_(sd[p + "Wr"].to(dev))
             lay.mr.copy_(sd[p + "mr"].to(dev))
             lay.vr.copy_(sd[p + "vr"].to(dev))

@@ -370,3 +370,156 @@ def test_qwen3_stack_48_layers_full_size(capi):
         assert bool((W_now[listed] != W_init[listed]).any()), l
         # RigL replaced r of the k entries
         assert int((~torch.isin(before[l], idx)).sum()) == r, l
+
+
+# --------------------------------------------------------------------------
+# trainer-loop features: frozen lower layers, expert load, the stack-wide
+# NaN skip, and the bookkeeping merges
+# --------------------------------------------------------------------------
+def test_partial_stack_trains_upper_layers_only(capi):
+    """Four bf16 layers with the two lowest frozen (the README's TRAIN_FROM):
+    losses, the trained layers' gradients, weights, routers and moments
+    against the oracle's stack step with the same train_from, and the frozen
+    layers bit-identical to their initial weights and routers."""
+    from sparse_fine_tuning_amd.stack import MoEStack, cosine_lr
+    dims = (200, 256, 8, 2, 96)
+    T, H, E, K, I = dims
+    L, F, steps, peak = 4, 2, 2, 2e-4
+    say(f"partial stack L={L} train_from={F} dims={dims}")
+    R = O.Rounding(O.BF16, O.CONTRACT)
+    layers = make_layers(L, dims, 11, bf16=True)
+    shape = O.Shape(*dims)
+    k = O.select_count(shape.N, 5, 1000)
+    stk = MoEStack(L, *dims, act=capi.BF16, device=DEV, train_from=F)
+    ref = []
+    for l, lay in enumerate(layers):
+        stk.load_layer(l, lay["W_gu"], lay["W_d"], lay["Wr"])
+        if l < F:
+            assert stk.layers[l].mr is None and stk.layers[l].idx is None
+            ref.append(dict(lay))
+            continue
+        idx = synth.random_mask(shape.N, k, 70 + l)
+        stk.layers[l].set_active(torch.from_numpy(idx.view(np.int32)).to(DEV), capi.BF16)
+        ref.append(dict(lay, idx=idx, m=np.zeros(k), v=np.zeros(k), mr=np.zeros_like(lay["Wr"]),
+                        vr=np.zeros_like(lay["Wr"])))
+    t_ref = 0
+    for step in range(steps):
+        X = synth.to_bf16_values(synth.normal((T, H), 1.0, 120 + step))
+        tgt = synth.to_bf16_values(synth.normal((T, H), 1.0, 12000 + step))
+        lr = cosine_lr(step, steps, peak)
+        stk.set_batch(X, tgt)
+        stk.train_step(lr)
+        out = O.stack_train_step(X, tgt, ref, K, t_ref, lr, 0.9, 0.999, 1e-8, R, train_from=F)
+        ref, t_ref = out["layers"], out["t"]
+        torch.cuda.synchronize()
+        assert abs(float(stk.loss.item()) - out["loss"]) <= TOL_BF16 * out["loss"], step
+        for l in range(F, L):
+            assert rel(npf(stk.layers[l].dW), out["g"][l]) <= TOL_BF16, (step, l)
+    assert stk.t == t_ref == steps
+    for l in range(L):
+        lay, r = stk.layers[l], ref[l]
+        w0 = np.concatenate([layers[l]["W_gu"].ravel(), layers[l]["W_d"].ravel()])
+        if l < F:
+            assert np.array_equal(npf(lay.W), w0)
+            assert np.array_equal(npf(lay.Wr), layers[l]["Wr"].astype(np.float32).astype(np.float64))
+            continue
+        flat = np.concatenate([r["W_gu"].ravel(), r["W_d"].ravel()])
+        assert rel(npf(lay.W), flat) <= TOL_BF16, l
+        for got, want in ((lay.m, r["m"]), (lay.v, r["v"]), (lay.Wr, r["Wr"]), (lay.mr, r["mr"]),
+                          (lay.vr, r["vr"])):
+            assert rel(npf(got), want) <= TOL_BF16, l
+
+
+def test_expert_load_equals_the_oracle_grouping(capi):
+    """expert_load() (the differences of each layer's expert offsets, a HIP
+    kernel) against the oracle's group_by_expert counts of the same routing."""
+    from sparse_fine_tuning_amd.stack import MoEStack
+    dims = (200, 256, 8, 2, 96)
+    T, H, E, K, I = dims
+    L = 3
+    say("expert load")
+    layers = make_layers(L, dims, 13, bf16=True)
+    stk = MoEStack(L, *dims, act=capi.BF16, device=DEV, train_from=1)
+    for l, lay in enumerate(layers):
+        stk.load_layer(l, lay["W_gu"], lay["W_d"], lay["Wr"])
+    X = synth.to_bf16_values(synth.normal((T, H), 1.0, 130))
+    stk.set_batch(X, X)
+    stk.forward()
+    load = stk.expert_load().cpu().numpy()
+    assert load.shape == (L, E)
+    for l in range(L):
+        ids = stk.layers[l].st["topk_ids"].cpu().numpy()
+        counts, _, _ = O.group_by_expert(ids, E)
+        assert np.array_equal(load[l], counts), l
+        assert load[l].sum() == T * K
+
+
+def test_stack_nan_step_skips_every_layer(capi):
+    """A non-finite target poisons the loss: no layer's weights, router or
+    moments change, the step count stays and the skip is counted; the next
+    finite step trains."""
+    from sparse_fine_tuning_amd.stack import MoEStack
+    dims = (200, 256, 8, 2, 96)
+    T, H, E, K, I = dims
+    L = 3
+    say("stack NaN skip")
+    layers = make_layers(L, dims, 17, bf16=True)
+    shape = O.Shape(*dims)
+    k = O.select_count(shape.N, 5, 1000)
+    stk = MoEStack(L, *dims, act=capi.BF16, device=DEV)
+    for l, lay in enumerate(layers):
+        stk.load_layer(l, lay["W_gu"], lay["W_d"], lay["Wr"])
+        stk.layers[l].set_active(torch.from_numpy(synth.random_mask(shape.N, k, 80 + l)
+                                                  .view(np.int32)).to(DEV), capi.BF16)
+        stk.layers[l].m.fill_(0.5)
+        stk.layers[l].v.fill_(0.25)
+    X = synth.to_bf16_values(synth.normal((T, H), 1.0, 140))
+    tgt = synth.to_bf16_values(synth.normal((T, H), 1.0, 141))
+    tgt[3, 5] = np.nan
+    before = [(lay.W.clone(), lay.Wr.clone()) for lay in stk.layers]
+    stk.set_batch(X, tgt)
+    stk.train_step(1e-3)
+    torch.cuda.synchronize()
+    assert stk.skipped == 1 and stk.t == 0
+    for lay, (W0, Wr0) in zip(stk.layers, before):
+        assert torch.equal(lay.W.view(torch.int16), W0.view(torch.int16))
+        assert torch.equal(lay.Wr, Wr0)
+        assert bool((lay.m == 0.5).all()) and bool((lay.v == 0.25).all())
+    tgt[3, 5] = 0.0
+    stk.set_batch(X, tgt)
+    stk.train_step(1e-3)
+    torch.cuda.synchronize()
+    assert stk.skipped == 1 and stk.t == 1
+    assert not torch.equal(stk.layers[0].Wr, before[0][1])
+
+
+@pytest.mark.parametrize("na,nb,overlap", [(0, 0, 0), (0, 1000, 0), (5000, 0, 0), (3000, 7000, 0.3),
+                                           (100000, 90000, 0.5), (2048 * 3, 5, 1.0),
+                                           (10, 300000, 0.0)])
+def test_sorted_union_and_adjacent_diff(capi, na, nb, overlap):
+    """usaf_sorted_union against numpy's union of two ascending lists (with
+    shared entries, empty sides, a list far denser than the other); and
+    usaf_adjacent_diff against numpy's diff."""
+    say(f"sorted union na={na} nb={nb} overlap={overlap}")
+    rng = np.random.default_rng(na + 7 * nb)
+    a = np.sort(rng.choice(4 * (na + nb) + 10, na, replace=False)).astype(np.uint32)
+    shared = rng.choice(a, int(overlap * min(na, nb)), replace=False) if na and nb else np.zeros(0, np.uint32)
+    rest = np.setdiff1d(rng.choice(4 * (na + nb) + 10, 2 * nb + 10, replace=False).astype(np.uint32), a)
+    b = np.sort(np.concatenate([shared, rest[: nb - shared.size]])).astype(np.uint32)
+    want = np.union1d(a, b).astype(np.uint32)
+    dev = lambda x: torch.from_numpy(x.view(np.int32).copy()).to(DEV)
+    out = torch.full((max(na + b.size, 1),), -1, dtype=torch.int32, device=DEV)
+    n_out = torch.zeros(1, dtype=torch.int64, device=DEV)
+    ws = torch.empty(capi.workspace_size(capi.WS_UNION, None, na + b.size), dtype=torch.uint8,
+                     device=DEV)
+    capi.sorted_union(dev(a) if na else None, na, dev(b) if b.size else None, b.size, out, n_out, ws)
+    torch.cuda.synchronize()
+    n = int(n_out.item())
+    assert n == want.size
+    assert np.array_equal(npu32(out[:n]), want)
+    if na > 1:
+        offs = dev(np.sort(rng.integers(0, 1 << 20, na)).astype(np.int32).view(np.uint32))
+        diff = torch.empty(na - 1, dtype=torch.int32, device=DEV)
+        capi.adjacent_diff(offs, na - 1, diff)
+        torch.cuda.synchronize()
+        assert np.array_equal(diff.cpu().numpy(), np.diff(offs.cpu().numpy()))

@@ -187,3 +187,35 @@ def test_cosine_lr_closed_form():
     for t in range(total):
         assert abs(O.cosine_lr(t, total, peak) + O.cosine_lr(total - t, total, peak) - peak) <= 1e-19
         assert O.cosine_lr(t + 1, total, peak) < O.cosine_lr(t, total, peak)
+
+
+def test_frozen_lower_layers_train_as_in_the_full_stack():
+    """With the layers below train_from frozen, each trained layer gets the
+    very update it gets when every layer trains (its gradients come from the
+    layers above it only), the frozen layers are unchanged, bit for bit, and
+    need no list or moments."""
+    R = O.Rounding(O.BF16, O.CONTRACT)
+    dims = (24, 16, 4, 2, 8)
+    T, H, E, K, I = dims
+    layers = []
+    for l in range(4):
+        d = synth.moe_layer(*dims, bf16=True, seeds=tuple(500 + 10 * l + j for j in range(5)))
+        N = 3 * E * H * I
+        k = O.select_count(N, 5, 100)
+        layers.append(dict(W_gu=d["W_gu"] * 10, W_d=d["W_d"] * 10, Wr=d["Wr"] * 10,
+                           idx=synth.random_mask(N, k, 600 + l), m=np.zeros(k), v=np.zeros(k),
+                           mr=np.zeros((E, H)), vr=np.zeros((E, H))))
+    X0 = synth.to_bf16_values(synth.normal((T, H), 1.0, 700))
+    tgt = synth.to_bf16_values(synth.normal((T, H), 1.0, 701))
+    full = O.stack_train_step(X0, tgt, layers, K, 0, 1e-3, 0.9, 0.999, 1e-8, R)
+    part = O.stack_train_step(X0, tgt, layers, K, 0, 1e-3, 0.9, 0.999, 1e-8, R, train_from=2)
+    assert part["t"] == full["t"] == 1
+    for l in range(4):
+        for key in ("W_gu", "W_d", "Wr", "m", "v", "mr", "vr"):
+            want = (full if l >= 2 else dict(layers=layers))["layers"][l][key]
+            assert np.array_equal(part["layers"][l][key], want), (l, key)
+    # frozen layers need no list and no moments
+    bare = [dict(W_gu=lay["W_gu"], W_d=lay["W_d"], Wr=lay["Wr"]) for lay in layers[:2]] + layers[2:]
+    out = O.stack_train_step(X0, tgt, bare, K, 0, 1e-3, 0.9, 0.999, 1e-8, R, train_from=2)
+    for l in range(2, 4):
+        assert np.array_equal(out["layers"][l]["W_gu"], full["layers"][l]["W_gu"])
