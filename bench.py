@@ -197,7 +197,25 @@ def rigl_scan(capi, synth, layer_mod, d, idx, dims, scan_tokens, repeats=2):
         dqa_ms = capi.timer_read(4)
         capi.timer_arm(-1)
     dqa_bytes = sum(x.numel() for x in qa) + 4 * sum(x.numel() for x in sa) + N * 2
-    del qa, sa, za
+    # the forward on the same codes, dequantised as the GEMMs load them,
+    # against the forward on their resident copy (just written above)
+    w4 = capi.q4_experts(qa[0], sa[0], za[0], qa[1], sa[1], za[1], 128)
+    fwd_ms = {}
+    for name, run in (("resident", lambda: lay.forward()),
+                      ("q4_on_load", lambda: capi.moe_forward_q4(lay.shape, lay.X, lay.Wr, w4, lay.Y,
+                                                                 lay.state, lay.ws_fwd))):
+        ts = []
+        for rep in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        fwd_ms[name] = float(np.median(ts[1:]))
+    log(f"rigl: forward at {Ts} tokens, resident {fwd_ms['resident']:.3f} ms, 4-bit on load "
+        f"{fwd_ms['q4_on_load']:.3f} ms")
+    del qa, sa, za, w4
     # dequant once into the resident bf16 working copy (timed)
     for rep in range(2):
         torch.cuda.synchronize()
@@ -229,6 +247,7 @@ def rigl_scan(capi, synth, layer_mod, d, idx, dims, scan_tokens, repeats=2):
     log(f"rigl: scan parts {json.dumps({c: round(v['ms'], 4) for c, v in parts.items()})}")
     return dict(rigl_scan_ms=float(np.median(times)), scan_tokens=Ts, scan_kernels=parts,
                 dequant_ms=float(sum(dq_ms)), dequant_GBps=dq_bytes / (sum(dq_ms) * 1e-3) / 1e9,
+                forward_ms_resident=fwd_ms["resident"], forward_ms_q4_on_load=fwd_ms["q4_on_load"],
                 dequant_affine_g128_ms=float(sum(dqa_ms)),
                 dequant_affine_g128_GBps=dqa_bytes / (sum(dqa_ms) * 1e-3) / 1e9,
                 turnover_applied=float(stats[1]) / k, turnover_topk_vs_old=float(stats[2]) / k,

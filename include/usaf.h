@@ -133,6 +133,33 @@ USAF_API usaf_status usaf_moe_forward(const usaf_moe_shape *shape, const void *X
                              const void *Wflat, void *Y, const usaf_moe_state *state,
                              void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Expert weights of one layer in the pages' own 4-bit storage (README "how
+ * it works": experts kept in 4-bit HQQ form; quantisation recipe: groups
+ * along the input dimension), the affine codes of usaf_dequant_affine:
+ *   gate_up: q_gu [E*2I, H/2] bytes, s_gu and z_gu [E*2I, H/group] fp16 bits
+ *   down:    q_d  [E*H,  I/2] bytes, s_d  and z_d  [E*H,  I/group] fp16 bits
+ * w = bf16(fp32(fp32(q - z) * s)), element 2i in the low nibble of byte i;
+ * rows in the flat order of the resident weights. */
+typedef struct {
+  const uint8_t *q_gu; const uint16_t *s_gu; const uint16_t *z_gu;
+  const uint8_t *q_d;  const uint16_t *s_d;  const uint16_t *z_d;
+  int32_t group;  /* 64 or 128; must divide H and I */
+} usaf_q4_experts;
+
+/* The layer forward of usaf_moe_forward with the expert weights read from
+ * their 4-bit codes and dequantised as the GEMMs load them, no resident
+ * copy (README "how it works": caching bullet -- the pages keep resident
+ * dequantised copies; this is the other side of that trade, for layers that
+ * only run forward, such as the frozen lower layers of a partly trained
+ * stack).  Every output and every field of `state` it writes equals, bit for
+ * bit, usaf_moe_forward on the usaf_dequant_affine copy of the same codes.
+ * bf16 layers only (UNSUPPORTED otherwise); the code arrays must be 4-byte
+ * aligned.  ws: USAF_WS_FORWARD bytes. */
+USAF_API usaf_status usaf_moe_forward_q4(const usaf_moe_shape *shape, const void *X, const float *Wr,
+                                         const usaf_q4_experts *w, void *Y,
+                                         const usaf_moe_state *state, void *ws, size_t ws_bytes,
+                                         hipStream_t stream);
+
 /* Plan of the masked gradient for one active list idx[nnz] (strictly
  * ascending): where every (expert, row, column tile) segment starts in the
  * list, and the list's work cut into tiles of balanced entry counts.  It

@@ -27,7 +27,7 @@ EXPORTS = (
     "usaf_mse_grad", "usaf_mse_grad_noalloc",
     "usaf_route", "usaf_status_string", "usaf_version", "usaf_timer_arm", "usaf_timer_read",
     "usaf_gather", "usaf_residual_add", "usaf_masked_plan", "usaf_sorted_union",
-    "usaf_adjacent_diff",
+    "usaf_adjacent_diff", "usaf_moe_forward_q4",
 )
 
 # Kernel classes of the timing hook (usaf_kernel_class).
@@ -70,6 +70,12 @@ class State(C.Structure):
                 ("gu", C.c_void_p), ("a", C.c_void_p), ("dgu", C.c_void_p), ("dw", C.c_void_p)]
 
 
+class Q4Experts(C.Structure):
+    _fields_ = [("q_gu", C.c_void_p), ("s_gu", C.c_void_p), ("z_gu", C.c_void_p),
+                ("q_d", C.c_void_p), ("s_d", C.c_void_p), ("z_d", C.c_void_p),
+                ("group", C.c_int32)]
+
+
 class RiglStats(C.Structure):
     _fields_ = [("n_drop", C.c_int64), ("n_grow", C.c_int64), ("topk_new_vs_old", C.c_int64)]
 
@@ -82,6 +88,7 @@ def _load():
     sig = {
         "usaf_workspace_size": [i32, vp, i64, i64, C.POINTER(sz)],
         "usaf_moe_forward": [vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "usaf_moe_forward_q4": [vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "usaf_masked_backward": [vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp],
         "usaf_masked_plan": [vp, vp, i64, vp, sz, vp],
         "usaf_importance_topk": [vp, i64, i64, vp, i64, vp, vp, vp, sz, vp],
@@ -163,6 +170,19 @@ def moe_forward(shape, X, Wr, Wflat, Y, state: State, ws, stream=None):
     _check(lib.usaf_moe_forward(C.byref(shape), _p(X), _p(Wr), _p(Wflat), _p(Y), C.byref(state),
                                 _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "usaf_moe_forward")
+
+
+def q4_experts(q_gu, s_gu, z_gu, q_d, s_d, z_d, group) -> Q4Experts:
+    """The 4-bit expert-weight struct from device tensors (codes uint8,
+    scales and zeros as 16-bit fp16 bit patterns)."""
+    return Q4Experts(_p(q_gu), _p(s_gu), _p(z_gu), _p(q_d), _p(s_d), _p(z_d), int(group))
+
+
+def moe_forward_q4(shape, X, Wr, w: Q4Experts, Y, state: State, ws, stream=None):
+    _check(lib.usaf_moe_forward_q4(C.byref(shape), _p(X), _p(Wr), C.byref(w), _p(Y),
+                                   C.byref(state), _p(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)),
+           "usaf_moe_forward_q4")
 
 
 def masked_backward(shape, X, Wr, Wflat, state: State, dY, idx, nnz, dW, dWr, dX, nonfinite, ws,

@@ -1224,6 +1224,40 @@ extern "C" usaf_status usaf_moe_forward(const usaf_moe_shape* shape, const void*
                              static_cast<char*>(ws), stream);
 }
 
+extern "C" usaf_status usaf_moe_forward_q4(const usaf_moe_shape* shape, const void* X,
+                                           const float* Wr, const usaf_q4_experts* w, void* Y,
+                                           const usaf_moe_state* state, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  USAF_TRY(check_shape(shape));
+  if (!X || !Wr || !w || !Y || !state_ok(state, false)) return USAF_ERR_INVALID_ARG;
+  if (!w->q_gu || !w->s_gu || !w->z_gu || !w->q_d || !w->s_d || !w->z_d) return USAF_ERR_INVALID_ARG;
+  const usaf_moe_shape& s = *shape;
+  if (s.act != USAF_BF16) return USAF_ERR_UNSUPPORTED;
+  if ((w->group != 64 && w->group != 128) || s.H % w->group || s.I % w->group)
+    return USAF_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(w->q_gu) | reinterpret_cast<uintptr_t>(w->q_d)) & 3)
+    return USAF_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < ws_forward(s).total) return USAF_ERR_WORKSPACE;
+  const WsForward L = ws_forward(s);
+  char* wsc = static_cast<char*>(ws);
+  bf16_t* ybuf = reinterpret_cast<bf16_t*>(wsc + L.ybuf);
+  const bf16_t* Xb = static_cast<const bf16_t*>(X);
+  const usaf_moe_state& st = *state;
+  float* parts = reinterpret_cast<float*>(wsc + L.ybuf);
+  const int nparts = mfma_router_splits(s);
+  USAF_TRY(mfma_router(s, Xb, Wr, parts, nparts, stream));
+  USAF_TRY(route_impl(s, parts, nparts, st, stream));
+  USAF_TRY(q4_gate_up(s, Xb, *w, st.offsets, st.perm, static_cast<bf16_t*>(st.gu),
+                      static_cast<bf16_t*>(st.a), stream));
+  USAF_TRY(q4_down(s, static_cast<const bf16_t*>(st.a), *w, st.offsets, ybuf, stream));
+  timer_begin(USAF_K_COMBINE_Y, stream);
+  hipLaunchKernelGGL(combine_y_kernel<bf16_t>, dim3(unsigned(s.T)), dim3(256), 0, stream, ybuf,
+                     st.topk_w, st.slot_pos, s.H, s.K, static_cast<bf16_t*>(Y));
+  timer_end(USAF_K_COMBINE_Y, stream);
+  USAF_LAUNCH_CHECK();
+  return USAF_OK;
+}
+
 extern "C" usaf_status usaf_masked_backward(const usaf_moe_shape* shape, const void* X,
                                             const float* Wr, const void* Wflat,
                                             const usaf_moe_state* state, const void* dY,

@@ -123,4 +123,10 @@ usaf_status masked_plan_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64
 size_t topk_ws_bytes(int64_t n);
 size_t rigl_ws_bytes(int64_t N, int64_t k);
 size_t union_ws_bytes(int64_t n);  // usaf_sorted_union of lists totalling n entries
+// Forward expert GEMMs on 4-bit affine codes, dequantised as they load.
+usaf_status q4_gate_up(const usaf_moe_shape& s, const uint16_t* X, const usaf_q4_experts& w,
+                       const int32_t* offsets, const int32_t* perm, uint16_t* gu, uint16_t* a,
+                       hipStream_t st);
+usaf_status q4_down(const usaf_moe_shape& s, const uint16_t* a, const usaf_q4_experts& w,
+                    const int32_t* offsets, uint16_t* ybuf, hipStream_t st);
 }  // namespace usaf

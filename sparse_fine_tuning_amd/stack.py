@@ -69,6 +69,7 @@ class _Layer:
             dgu=shared["dgu"], dw=shared["dw"])
         self.state = capi.make_state(self.st)
         self.frozen = frozen
+        self.q4 = None  # a frozen layer's 4-bit codes (capi.Q4Experts and its tensors), if any
         self.W = z(shape.N, dtype=dt)
         self.Wr = z(E, H)
         if frozen:
@@ -164,6 +165,21 @@ class MoEStack:
         if lay.idx is not None:  # SparseAdam's compact copy of the active weights
             lay.refresh_list(self.act)
 
+    def load_layer_q4(self, l, codes, group, Wr):
+        """A frozen layer whose experts stay in the pages' 4-bit storage (the
+        affine codes of usaf_dequant_affine: q_gu, s_gu, z_gu, q_d, s_d, z_d as
+        numpy arrays, scales and zeros as fp16 bit patterns) and are
+        dequantised as its forward loads them: no resident bf16 copy."""
+        lay = self.layers[l]
+        if not lay.frozen:
+            raise ValueError("only frozen layers (below train_from) keep 4-bit experts")
+        dev = self.device
+        ts = [torch.from_numpy(np.ascontiguousarray(c).view(np.int16 if c.dtype == np.uint16 else c.dtype))
+              .to(dev) for c in codes]
+        lay.q4 = (capi.q4_experts(*ts, group), ts)
+        lay.W = None  # the resident copy is not kept
+        lay.Wr.copy_(torch.from_numpy(np.ascontiguousarray(Wr, dtype=np.float32)).to(dev))
+
     def set_batch(self, X, tgt):
         """X_0 and the target: numpy arrays or device tensors."""
         for dst, src in ((self.Xs[0], X), (self.tgt, tgt)):
@@ -176,8 +192,12 @@ class MoEStack:
     def forward(self, stream=None):
         n = self.shape.T * self.shape.H
         for l, lay in enumerate(self.layers):
-            capi.moe_forward(self.shape, self.Xs[l], lay.Wr, lay.W, self.Y, lay.state, self.ws_fwd,
-                             stream)
+            if lay.q4 is not None:
+                capi.moe_forward_q4(self.shape, self.Xs[l], lay.Wr, lay.q4[0], self.Y, lay.state,
+                                    self.ws_fwd, stream)
+            else:
+                capi.moe_forward(self.shape, self.Xs[l], lay.Wr, lay.W, self.Y, lay.state,
+                                 self.ws_fwd, stream)
             capi.residual_add(self.act, self.Xs[l], self.Y, self.Xs[l + 1], n, stream)
 
     def backward(self, select=None, stream=None):

@@ -598,3 +598,60 @@ def test_tiny_fp32_importance_then_three_steps(capi):
     assert rel(npf(lay.Wr), st["Wr"]) <= TOL_F32
     assert rel(npf(lay.mr), st["mr"]) <= TOL_F32
     assert rel(npf(lay.vr), st["vr"]) <= TOL_F32
+
+
+# --------------------------------------------------------------------------
+# the pages' 4-bit storage, dequantised as the GEMMs load it
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dims,group", [((200, 256, 8, 2, 128), 64), ((333, 512, 16, 4, 384), 128),
+                                        ((1024, 2048, 128, 8, 768), 128)])
+def test_forward_q4_equals_resident_dequant(capi, dims, group):
+    """usaf_moe_forward_q4 on affine 4-bit codes against usaf_moe_forward on
+    the usaf_dequant_affine copy of the same codes: every state tensor and
+    the output bit-identical; and against the oracle's layer on the oracle's
+    dequant of the codes within the bf16 tolerance (routing exact up to
+    near-ties)."""
+    from sparse_fine_tuning_amd.layer import SparseMoELayer
+    T, H, E, K, I = dims
+    say(f"forward q4 dims={dims} group={group}")
+    d = synth.moe_layer(*dims, bf16=True, seeds=(90, 91, 92, 93, 94))
+    qg, sg, zg = synth.quantize_affine_int4(d["W_gu"].reshape(E * 2 * I, H), group)
+    qd, sd, zd = synth.quantize_affine_int4(d["W_d"].reshape(E * H, I), group)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    i16 = lambda a: dev(np.ascontiguousarray(a).view(np.int16))
+    tq = [dev(qg), i16(sg), i16(zg), dev(qd), i16(sd), i16(zd)]
+    # resident: dequantise into the flat weights, then the usual forward
+    res = SparseMoELayer(*dims, act=capi.BF16, device=DEV)
+    res.load(d["X"], d["Wr"], np.zeros_like(d["W_gu"]), np.zeros_like(d["W_d"]), d["tgt"])
+    ngu = E * 2 * I * H
+    capi.dequant_affine(tq[0], tq[1], tq[2], E * 2 * I, H, group, res.W[:ngu])
+    capi.dequant_affine(tq[3], tq[4], tq[5], E * H, I, group, res.W[ngu:])
+    res.forward()
+    # on load: the same codes, no resident copy
+    onl = SparseMoELayer(*dims, act=capi.BF16, device=DEV)
+    onl.X, onl.Wr = res.X, res.Wr
+    capi.moe_forward_q4(onl.shape, onl.X, onl.Wr, capi.q4_experts(*tq, group), onl.Y, onl.state,
+                        onl.ws_fwd)
+    torch.cuda.synchronize()
+    for name in ("logits", "topk_ids", "topk_w", "offsets", "perm", "slot_pos", "gu", "a"):
+        x, y = res.st[name], onl.st[name]
+        if x.dtype == torch.bfloat16:
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        assert torch.equal(x, y), name
+    assert torch.equal(res.Y.view(torch.int16), onl.Y.view(torch.int16))
+    # the oracle: its dequant of the codes, then its layer
+    R = O.Rounding(O.BF16, O.CONTRACT)
+    W_gu = O.dequant_affine(qg, sg, zg, group).reshape(E, 2 * I, H)
+    W_d = O.dequant_affine(qd, sd, zd, group).reshape(E, H, I)
+    assert np.array_equal(bf16_bits(W_gu.ravel()),
+                          res.W[:ngu].view(torch.int16).cpu().numpy().view(np.uint16))
+    fw = O.moe_forward(d["X"], d["Wr"], W_gu, W_d, K, R)
+    ids = onl.st["topk_ids"].cpu().numpy()
+    logits = fw["logits"]
+    bad = np.nonzero(np.any(ids != fw["topk_ids"], axis=1))[0]
+    for t in bad:  # a routing difference must be a near-tie of the oracle's logits
+        srt = np.sort(logits[t])[::-1]
+        assert srt[K - 1] - srt[K] <= 1e-5 * np.abs(logits).max()
+    ok = np.ones(T, bool)
+    ok[bad] = False
+    assert rel(npf(onl.Y)[ok], fw["Y"][ok]) <= TOL_BF16

@@ -523,3 +523,54 @@ def test_sorted_union_and_adjacent_diff(capi, na, nb, overlap):
         capi.adjacent_diff(offs, na - 1, diff)
         torch.cuda.synchronize()
         assert np.array_equal(diff.cpu().numpy(), np.diff(offs.cpu().numpy()))
+
+
+def test_partial_stack_with_4bit_frozen_layers(capi):
+    """Frozen layers kept as affine 4-bit codes (dequantised as their forward
+    loads them) train the upper layers exactly as frozen layers holding the
+    resident dequantised copy of the same codes: losses and every trained
+    tensor bit-identical over two steps."""
+    from sparse_fine_tuning_amd.stack import MoEStack
+    dims = (200, 256, 8, 2, 128)
+    T, H, E, K, I = dims
+    L, F, group = 3, 2, 64
+    say(f"partial stack, 4-bit frozen layers, dims={dims}")
+    layers = make_layers(L, dims, 19, bf16=True)
+    shape = O.Shape(*dims)
+    k = O.select_count(shape.N, 5, 1000)
+    codes = []
+    for l in range(F):
+        qg, sg, zg = synth.quantize_affine_int4(layers[l]["W_gu"].reshape(E * 2 * I, H), group)
+        qd, sd, zd = synth.quantize_affine_int4(layers[l]["W_d"].reshape(E * H, I), group)
+        codes.append((qg, sg, zg, qd, sd, zd))
+    stacks = []
+    for q4 in (False, True):
+        stk = MoEStack(L, *dims, act=capi.BF16, device=DEV, train_from=F)
+        for l, lay in enumerate(layers):
+            if l < F:
+                if q4:
+                    stk.load_layer_q4(l, codes[l], group, lay["Wr"])
+                else:  # the resident copy of the same codes
+                    W_gu = O.dequant_affine(*codes[l][:3], group).reshape(E, 2 * I, H)
+                    W_d = O.dequant_affine(*codes[l][3:], group).reshape(E, H, I)
+                    stk.load_layer(l, W_gu, W_d, lay["Wr"])
+            else:
+                stk.load_layer(l, lay["W_gu"], lay["W_d"], lay["Wr"])
+                stk.layers[l].set_active(torch.from_numpy(synth.random_mask(shape.N, k, 90 + l)
+                                                          .view(np.int32)).to(DEV), capi.BF16)
+        stacks.append(stk)
+    for step in range(2):
+        X = synth.to_bf16_values(synth.normal((T, H), 1.0, 150 + step))
+        tgt = synth.to_bf16_values(synth.normal((T, H), 1.0, 15000 + step))
+        for stk in stacks:
+            stk.set_batch(X, tgt)
+            stk.train_step(1e-3)
+        torch.cuda.synchronize()
+        assert float(stacks[0].loss.item()) == float(stacks[1].loss.item())
+    a, b = stacks
+    assert b.layers[0].W is None and a.t == b.t == 2
+    for l in range(F, L):
+        la, lb = a.layers[l], b.layers[l]
+        assert torch.equal(la.W.view(torch.int16), lb.W.view(torch.int16))
+        for x, y in ((la.m, lb.m), (la.v, lb.v), (la.Wr, lb.Wr), (la.mr, lb.mr), (la.vr, lb.vr)):
+            assert torch.equal(x, y)
