@@ -38,17 +38,40 @@ FP32_VEC_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, TFLOP/s
 # figure whose sources have changed since is reported as null.
 FETCH_SCALE = 2.0   # a 1 GiB copy reads 524,300 KiB of FETCH_SIZE
 WRITE_SCALE = 1.0   # and 1,048,576 KiB of WRITE_SIZE
-# kernel class -> (fetch KiB, write KiB, sources hash); masked_dw and adam sum
-# the launches of one step (the two SDDMM launches, the plan being kept per
-# list; expert + router Adam)
+# workload -> kernel class -> (fetch KiB, write KiB, sources hash).  masked_dw
+# and adam sum the launches of one step (the two SDDMM launches, the plan
+# being kept per list; expert + router Adam); dense_dw sums the operand
+# staging and the two GEMMs of one scan; topk_fresh sums every launch of the
+# scan's first selection (sample, full read, compaction, candidate rounds,
+# emit).
+G = "40a2f9c78d31f644"  # the GEMM sources
 COUNTER_TRAFFIC = {
-    "router_gemm": (8788, 16384, "11dc2d44b399d193"),
-    "gate_up": (470321, 147459, "11dc2d44b399d193"),
-    "down": (221360, 131072, "11dc2d44b399d193"),
-    "da": (338569, 100112, "11dc2d44b399d193"),
-    "dx": (632618, 131072, "11dc2d44b399d193"),
-    "masked_dw": (169865, 11803, "0dc1c49d496d20e3"),
-    "adam": (28636, 124714, "b8332b752cd03a50"),
+    "qwen3_step": {
+        "router_gemm": (8788, 16384, G),
+        "gate_up": (470370, 147459, G),
+        "down": (221388, 131072, G),
+        "da": (336108, 100110, G),
+        "dx": (628052, 131072, G),
+        "masked_dw": (169551, 11803, "92ef7fede1db8c9f"),
+        "adam": (28614, 123523, "e0a95258367d5586"),
+    },
+    "qwen3_scan": {
+        "dense_dw": (876683, 2883584, G),
+        "topk_fresh": (1338682, 90728, "49b97a47907be4cd"),
+    },
+    "mixtral_step": {
+        "router_gemm": (16518, 1024, G),
+        "gate_up": (1920774, 702978, G),
+        "down": (1161307, 68064, G),
+        "da": (2295388, 468116, G),
+        "dx": (2454283, 78256, G),
+        "masked_dw": (754271, 45258, "92ef7fede1db8c9f"),
+        "adam": (62211, 281417, "e0a95258367d5586"),
+    },
+    "mixtral_scan": {
+        "dense_dw": (4903818, 5636096, G),
+        "topk_fresh": (3122501, 193401, "49b97a47907be4cd"),
+    },
 }
 KERNEL_SOURCES = {
     c: ("gemm_mfma.hpp", "gemm_v2.hpp", "lds_dma.hpp", "moe_mfma.hip", "common.hpp", "moe_internal.hpp")
@@ -68,11 +91,13 @@ def sources_sha(kclass):
     return h.hexdigest()[:16]
 
 
-def counter_traffic(kclass):
-    """Scaled HBM bytes per launch, or None when unmeasured or stale."""
-    if kclass not in COUNTER_TRAFFIC or kclass not in KERNEL_SOURCES:
+def counter_traffic(workload, kclass):
+    """Scaled HBM bytes per launch of a kernel class in a workload, or None
+    when unmeasured or stale."""
+    table = COUNTER_TRAFFIC.get(workload, {})
+    if kclass not in table or kclass not in KERNEL_SOURCES:
         return None
-    fetch_kib, write_kib, sha = COUNTER_TRAFFIC[kclass]
+    fetch_kib, write_kib, sha = table[kclass]
     if sha != sources_sha(kclass):
         return None
     return (fetch_kib * FETCH_SCALE + write_kib * WRITE_SCALE) * 1024.0
@@ -243,7 +268,9 @@ def rigl_scan(capi, synth, layer_mod, d, idx, dims, scan_tokens, repeats=2):
             times.append(dt)
         stats = st.cpu().numpy()
         log(f"rigl: scan {rep} {dt:.2f} ms")
-    parts = scan_parts(capi, layer_mod, lay, idx, grad, r, ws, dims, Ts)
+    # the counter figures were taken at the default 8192 scan tokens
+    parts = scan_parts(capi, layer_mod, lay, idx, grad, r, ws, dims, Ts,
+                       "qwen3_scan" if Ts == 8192 else f"qwen3_scan_t{Ts}")
     log(f"rigl: scan parts {json.dumps({c: round(v['ms'], 4) for c, v in parts.items()})}")
     return dict(rigl_scan_ms=float(np.median(times)), scan_tokens=Ts, scan_kernels=parts,
                 dequant_ms=float(sum(dq_ms)), dequant_GBps=dq_bytes / (sum(dq_ms) * 1e-3) / 1e9,
@@ -254,7 +281,7 @@ def rigl_scan(capi, synth, layer_mod, d, idx, dims, scan_tokens, repeats=2):
                 rigl_k=int(k), rigl_r=int(r))
 
 
-def scan_parts(capi, layer_mod, lay, idx, grad, r, ws, dims, Ts):
+def scan_parts(capi, layer_mod, lay, idx, grad, r, ws, dims, Ts, workload):
     """Time per kernel class inside one RigL scan (HIP events on the launch
     stream, one scan per class): the dense gradient of every expert weight
     (operand staging and the two GEMMs), the fresh top-k of |g| over all N
@@ -280,7 +307,7 @@ def scan_parts(capi, layer_mod, lay, idx, grad, r, ws, dims, Ts):
         name = capi.KERNEL_CLASS_NAMES[c]
         if c == capi.K_TOPK:
             out["topk_fresh"] = dict(ms=ms[0], **roofline_entry("topk_fresh", 0.0, 4.0 * N, ms[0]),
-                                     traffic=counter_traffic("topk_fresh"),
+                                     traffic=counter_traffic(workload, "topk_fresh"),
                                      note="one read of the N fp32 keys is the algorithmic bytes")
             out["topk_all"] = dict(ms=sum(ms), launches=len(ms))
         else:
@@ -292,7 +319,7 @@ def scan_parts(capi, layer_mod, lay, idx, grad, r, ws, dims, Ts):
     out["dense_dw"].update(algorithmic_flops=fl, algorithmic_bytes=by, roofline_ms=t_roof,
                            frac=t_roof / ms, mfma_frac=fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                            hbm_frac=by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                           traffic=counter_traffic("dense_dw"))
+                           traffic=counter_traffic(workload, "dense_dw"))
     return out
 
 
@@ -335,7 +362,8 @@ def mixtral_layer(capi, synth, layer_mod, steps, lr):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     work = algorithmic_work(dims, k)
-    kern = {c: dict(ms=per_class[c], **roofline_entry(c, *work[c], per_class[c]))
+    kern = {c: dict(ms=per_class[c], traffic=counter_traffic("mixtral_step", c),
+                    **roofline_entry(c, *work[c], per_class[c]))
             for c in per_class if c in work and per_class[c] > 0}
     gemm_fl = sum(work[c][0] for c in ("gate_up", "down", "da", "dx"))
     gemm_ms = sum(per_class[c] for c in ("gate_up", "down", "da", "dx"))
@@ -357,7 +385,7 @@ def mixtral_layer(capi, synth, layer_mod, steps, lr):
             scans.append((time.perf_counter() - t0) * 1e3)
     stats = st.cpu().numpy()
     log(f"mixtral: rigl scan {np.median(scans):.2f} ms")
-    parts = scan_parts(capi, layer_mod, lay, idx, grad, r, ws, dims, T)
+    parts = scan_parts(capi, layer_mod, lay, idx, grad, r, ws, dims, T, "mixtral_scan")
     log(f"mixtral: scan parts {json.dumps({c: round(v['ms'], 4) for c, v in parts.items()})}")
     out = dict(workload="Mixtral-8x7B-shaped single MoE layer sparse train step",
                tokens=T, hidden=H, experts=E, top_k=K, intermediate=I, active_entries=k,
@@ -714,11 +742,11 @@ def main():
     fl, by = work[dominant]
     roof = roofline_entry(dominant, fl, by, kern_ms)
     roof.update(kernel_ms=kern_ms, launches=len(kms), algorithmic_flops=fl,
-                algorithmic_bytes=by, traffic=counter_traffic(dominant),
+                algorithmic_bytes=by, traffic=counter_traffic("qwen3_step", dominant),
                 traffic_note="rocprofv3 FETCH_SIZE x%.1f + WRITE_SIZE x%.1f per launch"
                              % (FETCH_SCALE, WRITE_SCALE))
     log(f"step {ms_step:.3f} ms -> {value:.0f} tokens/s; {dominant} {kern_ms:.3f} ms")
-    step_kernels = {c: dict(ms=per_class[c], traffic=counter_traffic(c),
+    step_kernels = {c: dict(ms=per_class[c], traffic=counter_traffic("qwen3_step", c),
                             **roofline_entry(c, *work[c], per_class[c]))
                     for c in per_class if c in work and per_class[c] > 0}
     del lay
