@@ -460,29 +460,40 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
   // entries of this tile: per row r, the plan segment (e, r, ct)
   const int64_t q_r0 = A.qbase + (int64_t(e) * A.R + r_lo) * A.nct + ct;
   const uint32_t nnz32 = uint32_t(A.nnz);  // list positions are below 2^32
-  for (int r = tid; r < nr; r += kThreads) {
-    const int64_t q = q_r0 + int64_t(r) * A.nct;
-    const uint32_t s0 = min(A.seg[q], nnz32);
-    rstart[r] = s0;
-    rowpre[r + 1] = int(max(min(A.seg[q + 1], nnz32), s0) - s0);
-  }
-  if (tid == 0) rowpre[0] = 0;
-  __syncthreads();
-  if (tid < 64) {  // inclusive scan of rowpre[1..nr] by wave 0
-    int carry = 0;
-    for (int b = 0; b < nr; b += 64) {
-      int v = (b + lane < nr) ? rowpre[b + lane + 1] : 0;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int u = __shfl_up(v, d, 64);
-        if (lane >= d) v += u;
-      }
-      if (b + lane < nr) rowpre[b + lane + 1] = v + carry;
-      carry += __shfl(v, 63, 64);
+  int nent;
+  uint32_t rs0;  // list position of the tile's first entry
+  if (A.nct == 1) {
+    // one column tile: the tile's entries are one run of the list (rows
+    // r_lo..r_hi-1 are consecutive segments) and an entry's row follows
+    // from its flat index, so no per-row table is built
+    rs0 = min(A.seg[q_r0], nnz32);
+    nent = int(max(min(A.seg[q_r0 + nr], nnz32), rs0) - rs0);
+  } else {
+    for (int r = tid; r < nr; r += kThreads) {
+      const int64_t q = q_r0 + int64_t(r) * A.nct;
+      const uint32_t s0 = min(A.seg[q], nnz32);
+      rstart[r] = s0;
+      rowpre[r + 1] = int(max(min(A.seg[q + 1], nnz32), s0) - s0);
     }
+    if (tid == 0) rowpre[0] = 0;
+    __syncthreads();
+    if (tid < 64) {  // inclusive scan of rowpre[1..nr] by wave 0
+      int carry = 0;
+      for (int b = 0; b < nr; b += 64) {
+        int v = (b + lane < nr) ? rowpre[b + lane + 1] : 0;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int u = __shfl_up(v, d, 64);
+          if (lane >= d) v += u;
+        }
+        if (b + lane < nr) rowpre[b + lane + 1] = v + carry;
+        carry += __shfl(v, 63, 64);
+      }
+    }
+    __syncthreads();
+    nent = rowpre[nr];
+    rs0 = rstart[0];
   }
-  __syncthreads();
-  const int nent = rowpre[nr];
   if (nent == 0) continue;  // uniform
 
   const int off = A.offsets[e];
@@ -505,15 +516,15 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
       const int64_t rb0 = A.base + (int64_t(e) * A.R + r_lo) * A.C + c0;
       if (A.nct == 1) {
         // one column tile: the tile's rows are one run of the list from
-        // rstart[0], and an entry's row follows from its flat index
+        // rs0, and an entry's row follows from its flat index
         // (offset x < nr*C < 2^24 from the tile's first row; the float
         // quotient is off by at most one and corrected exactly)
 #pragma unroll
         for (int i = 0; i < kE; ++i) {
           const int qi = qw + 64 * i;
           const bool used = i < per && qi < nent;
-          opos[i] = used ? rstart[0] + uint32_t(qi) : 0xffffffffu;
-          val[i] = used ? opos[i] : rstart[0];
+          opos[i] = used ? rs0 + uint32_t(qi) : 0xffffffffu;
+          val[i] = used ? opos[i] : rs0;
         }
 #pragma unroll
         for (int i = 0; i < kE; ++i) val[i] = A.idx[val[i]];
@@ -536,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
           const int qi = qw + 64 * i;
           opos[i] = 0xffffffffu;
           rows[i] = 0;
-          val[i] = rstart[0];
+          val[i] = rs0;
           if (i < per && qi < nent) {
             int hi = nr - 1;
             while (r < hi) {  // last row with rowpre <= qi
