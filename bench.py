@@ -169,6 +169,46 @@ def time_kernel_classes(capi, lay, classes, lr):
     return out
 
 
+def adam_scatter_ceiling(capi, lay, lr, reps=10):
+    """SparseAdam's update of the expert list against a plain scattered write
+    of the same list (usaf_scatter of the compact weights back to W at idx,
+    which leaves W unchanged), each timed alone in the cache state the step
+    leaves it: forward, loss and masked backward, then the timed call; median
+    of reps.  The scattered 2-byte writes bound the update, so this is its
+    measured ceiling."""
+    import numpy as np
+    import torch
+    k = lay.idx.numel()
+
+    def prelude():
+        lay.nonfinite.zero_()
+        lay.forward()
+        lay.loss_grad()
+        lay.backward()
+
+    def adam():
+        capi.sparse_adam(lay.act, lay.W, lay.idx, k, lay.dW, lay.m, lay.v, lay.t + 1, lr, 0.9,
+                         0.999, 1e-8, lay.nonfinite, None, w_list=lay.w_list)
+
+    def scatter():
+        capi.scatter(lay.act, lay.W, lay.idx, k, lay.w_list)
+
+    out = {}
+    for name, fn in (("sparse_adam_in_step_ms", adam), ("scatter_in_step_ms", scatter)):
+        ts = []
+        for _ in range(reps):
+            prelude()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        out[name] = float(np.median(ts))
+    out["vs_scatter_ceiling"] = out["sparse_adam_in_step_ms"] / out["scatter_in_step_ms"]
+    return out
+
+
 def rigl_scan(capi, synth, layer_mod, d, idx, dims, scan_tokens, repeats=2):
     """int4 resident dequant, then forward + dense backward + RigL on
     `scan_tokens` tokens; returns timings and turnover."""
@@ -749,6 +789,12 @@ def main():
     step_kernels = {c: dict(ms=per_class[c], traffic=counter_traffic("qwen3_step", c),
                             **roofline_entry(c, *work[c], per_class[c]))
                     for c in per_class if c in work and per_class[c] > 0}
+    if "adam" in step_kernels:
+        ceil = adam_scatter_ceiling(capi, lay, lr)
+        step_kernels["adam"].update(ceil)
+        log(f"SparseAdam in-step {ceil['sparse_adam_in_step_ms'] * 1e3:.1f} us against a plain "
+            f"scatter of the same list {ceil['scatter_in_step_ms'] * 1e3:.1f} us "
+            f"({ceil['vs_scatter_ceiling']:.3f}x)")
     del lay
     torch.cuda.empty_cache()
 

@@ -263,6 +263,17 @@ USAF_API usaf_status usaf_sparse_adam(int32_t w_dtype, void *W, const uint32_t *
 USAF_API usaf_status usaf_gather(int32_t w_dtype, const void *W, const uint32_t *idx, int64_t n,
                         void *out, hipStream_t stream);
 
+/* W[idx[i]] = vals[i] for i < n (w_dtype elements): a compact list written
+ * back into the flat weights, the inverse of usaf_gather (README "how it
+ * works": only the selected subset is trained, so a checkpoint holds the
+ * trained weights as such a list).  Also the plain scattered write that
+ * usaf_sparse_adam's own write-back of the list is measured against.  The
+ * idx entries must be distinct (which of two equal entries' values lands is
+ * unspecified).  Errors: INVALID_ARG for n < 0 or null pointers with n > 0,
+ * or an unknown w_dtype. */
+USAF_API usaf_status usaf_scatter(int32_t w_dtype, void *W, const uint32_t *idx, int64_t n,
+                         const void *vals, hipStream_t stream);
+
 
 
 /* Resident dequantisation (README "how it works": caching bullet; dequant

@@ -26,7 +26,7 @@ EXPORTS = (
     "usaf_rigl_reselect", "usaf_sparse_adam", "usaf_dequant_resident", "usaf_dequant_affine",
     "usaf_mse_grad", "usaf_mse_grad_noalloc",
     "usaf_route", "usaf_status_string", "usaf_version", "usaf_timer_arm", "usaf_timer_read",
-    "usaf_gather", "usaf_residual_add", "usaf_masked_plan", "usaf_sorted_union",
+    "usaf_gather", "usaf_scatter", "usaf_residual_add", "usaf_masked_plan", "usaf_sorted_union",
     "usaf_adjacent_diff", "usaf_moe_forward_q4",
 )
 
@@ -96,6 +96,7 @@ def _load():
         "usaf_sparse_adam": [i32, vp, vp, i64, vp, vp, vp, vp, i64, C.c_double, C.c_double,
                              C.c_double, C.c_double, vp, vp],
         "usaf_gather": [i32, vp, vp, i64, vp, vp],
+        "usaf_scatter": [i32, vp, vp, i64, vp, vp],
         "usaf_dequant_resident": [vp, vp, i64, i64, i32, vp, vp],
         "usaf_dequant_affine": [vp, vp, vp, i64, i64, i32, vp, vp],
         "usaf_mse_grad": [vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -228,6 +229,11 @@ def sparse_adam(w_dtype, W, idx, n, g, m, v, step, lr, beta1, beta2, eps, skip=N
 def gather(w_dtype, W, idx, n, out, stream=None):
     _check(lib.usaf_gather(int(w_dtype), _p(W), _p(idx), int(n), _p(out), _stream(stream)),
            "usaf_gather")
+
+
+def scatter(w_dtype, W, idx, n, vals, stream=None):
+    _check(lib.usaf_scatter(int(w_dtype), _p(W), _p(idx), int(n), _p(vals), _stream(stream)),
+           "usaf_scatter")
 
 
 def dequant_affine(q, scale_f16, zero_f16, rows, cols, group, out_bf16, stream=None):

@@ -73,6 +73,16 @@ __global__ __launch_bounds__(256) void gather_kernel(const W* __restrict__ w, co
     out[i] = w[idx[i]];
 }
 
+// W[idx[i]] = vals[i]: one entry per lane, the lanes of a wave writing
+// consecutive list entries.
+template <class W>
+__global__ __launch_bounds__(256) void scatter_kernel(W* __restrict__ w, const uint32_t* __restrict__ idx,
+                                                      int64_t n, const W* __restrict__ vals) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    w[idx[i]] = vals[i];
+}
+
 // int4 -> bf16: one thread per 8 outputs (one 32-bit word of codes).
 __global__ __launch_bounds__(256) void dequant_int4_kernel(const uint32_t* __restrict__ q,
                                                            const uint16_t* __restrict__ scale,
@@ -158,6 +168,21 @@ extern "C" usaf_status usaf_gather(int32_t w_dtype, const void* W, const uint32_
   else
     hipLaunchKernelGGL(gather_kernel<float>, dim3(grid_for(n)), dim3(256), 0, stream,
                        static_cast<const float*>(W), idx, n, static_cast<float*>(out));
+  USAF_LAUNCH_CHECK();
+  return USAF_OK;
+}
+
+extern "C" usaf_status usaf_scatter(int32_t w_dtype, void* W, const uint32_t* idx, int64_t n,
+                                    const void* vals, hipStream_t stream) {
+  if (n < 0 || (w_dtype != USAF_F32 && w_dtype != USAF_BF16)) return USAF_ERR_INVALID_ARG;
+  if (n == 0) return USAF_OK;
+  if (!W || !idx || !vals) return USAF_ERR_INVALID_ARG;
+  if (w_dtype == USAF_BF16)
+    hipLaunchKernelGGL(scatter_kernel<bf16_t>, dim3(grid_for(n)), dim3(256), 0, stream,
+                       static_cast<bf16_t*>(W), idx, n, static_cast<const bf16_t*>(vals));
+  else
+    hipLaunchKernelGGL(scatter_kernel<float>, dim3(grid_for(n)), dim3(256), 0, stream,
+                       static_cast<float*>(W), idx, n, static_cast<const float*>(vals));
   USAF_LAUNCH_CHECK();
   return USAF_OK;
 }

@@ -333,7 +333,9 @@ class MoEStack:
             sd[p + "mr"] = lay.mr.cpu()
             sd[p + "vr"] = lay.vr.cpu()
             sd[p + "touched"] = lay.touched.cpu()
-            sd[p + "touched_w"] = lay.W[lay.touched.long() & 0xFFFFFFFF].cpu()
+            tw = torch.empty(lay.touched.numel(), dtype=lay.W.dtype, device=lay.W.device)
+            capi.gather(self.act, lay.W, lay.touched, lay.touched.numel(), tw)
+            sd[p + "touched_w"] = tw.cpu()
         return sd
 
     def load_state_dict(self, sd: dict):
@@ -350,7 +352,10 @@ class MoEStack:
                 continue
             p = f"layer{l}."
             touched = sd[p + "touched"].to(dev)
-            lay.W[touched.long() & 0xFFFFFFFF] = sd[p + "touched_w"].to(dev)
+            tw = sd[p + "touched_w"].to(dev)
+            if touched.numel() != tw.numel() or tw.dtype != lay.W.dtype:
+                raise ValueError(f"layer {l}: touched weights do not match the touched list")
+            capi.scatter(self.act, lay.W, touched, touched.numel(), tw)
             lay.Wr.copy_(sd[p + "Wr"].to(dev))
             lay.mr.copy_(sd[p + "mr"].to(dev))
             lay.vr.copy_(sd[p + "vr"].to(dev))

@@ -118,6 +118,10 @@ def test_entry_points_refuse_bad_arguments_before_launch():
     assert L.usaf_sparse_adam(1, FAKE, None, 10, FAKE, FAKE, FAKE, FAKE, 1, f(1e-3), f(.9), f(.999), f(1e-8), None, None) == 1
     assert L.usaf_gather(7, FAKE, FAKE, 10, FAKE, None) == 1
     assert L.usaf_gather(1, None, None, 0, None, None) == 0
+    assert L.usaf_scatter(7, FAKE, FAKE, 10, FAKE, None) == 1
+    assert L.usaf_scatter(1, FAKE, None, 10, FAKE, None) == 1
+    assert L.usaf_scatter(1, FAKE, FAKE, -1, FAKE, None) == 1
+    assert L.usaf_scatter(1, None, None, 0, None, None) == 0
     # dequant: group != 64, cols % 64, negative rows, misaligned output
     assert L.usaf_dequant_resident(FAKE, FAKE, 4, 128, 128, FAKE, None) == 2
     assert L.usaf_dequant_resident(FAKE, FAKE, 4, 96, 64, FAKE, None) == 2

@@ -444,6 +444,37 @@ def test_sparse_adam(capi, act, use_list):
         assert torch.equal(wl, Wt[it.long()])
 
 
+@pytest.mark.parametrize("act,n", [(1, 4001), (0, 4001), (1, 1), (1, 0), (0, 300000)])
+def test_scatter_is_the_inverse_of_gather(capi, act, n):
+    """usaf_scatter writes a compact list back at its indices (numpy's
+    W[idx] = vals, bit for bit) and leaves every other weight alone; a
+    gather followed by a scatter of the gathered list changes nothing."""
+    say(f"scatter act={act} n={n}")
+    N = 1 << 20
+    w = synth.normal(N, 0.02, 30)
+    if act:
+        w = synth.to_bf16_values(w)
+    idx = synth.random_mask(N, n, 31) if n else np.zeros(0, np.uint32)
+    vals = synth.normal(max(n, 1), 1.0, 32)[:n]
+    dt = torch.bfloat16 if act else torch.float32
+    Wt = torch.from_numpy(w.astype(np.float32)).to(DEV).to(dt)
+    W0 = Wt.clone()
+    it = torch.from_numpy(idx.view(np.int32)).to(DEV)
+    vt = torch.from_numpy(vals.astype(np.float32)).to(DEV).to(dt)
+    capi.scatter(act, Wt, it, n, vt)
+    back = torch.empty(n, dtype=dt, device=DEV)
+    capi.gather(act, Wt, it, n, back)
+    torch.cuda.synchronize()
+    want = W0.clone()
+    want[it.long() & 0xFFFFFFFF] = vt
+    bits = (lambda x: x.view(torch.int16)) if act else (lambda x: x.view(torch.int32))
+    assert torch.equal(bits(Wt), bits(want))
+    assert torch.equal(bits(back), bits(vt))
+    capi.scatter(act, Wt, it, n, back)  # the gathered list written back: no change
+    torch.cuda.synchronize()
+    assert torch.equal(bits(Wt), bits(want))
+
+
 def check_update(w_gpu, w_ref, w_old, act):
     """The update itself, W_new - W_old, against the oracle's.  fp32: within
     the fp32 tolerance of max|dW|.  bf16: both sides round every step's
