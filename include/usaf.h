@@ -208,10 +208,10 @@ USAF_API usaf_status usaf_masked_backward(const usaf_moe_shape *shape, const voi
  * and writes the first k indices to out_idx [k] in ascending order.
  * exclude (nullable) is a strictly ascending list of n_exclude indices that
  * may not be chosen (RigL grow).  out_val (nullable) receives grad at
- * out_idx.  grad must be 16-byte aligned (UNSUPPORTED otherwise).
+ * out_idx.  grad and ws must be 16-byte aligned (UNSUPPORTED otherwise).
  * Errors: INVALID_ARG when k > n - n_exclude, n >= 2^32 or n_exclude > n.
- * ws: USAF_WS_TOPK bytes for n (about 4n bytes: the threshold bin's
- * candidate indices are buffered). */
+ * ws: USAF_WS_TOPK bytes for n (about 16n bytes: the candidates' keys and
+ * indices are buffered). */
 USAF_API usaf_status usaf_importance_topk(const float *grad, int64_t n, int64_t k,
                                  const uint32_t *exclude, int64_t n_exclude,
                                  uint32_t *out_idx, float *out_val,
@@ -225,8 +225,9 @@ USAF_API usaf_status usaf_importance_topk(const float *grad, int64_t n, int64_t 
  * Weights are not modified.  grad [N] fp32 (a dense scan's dW); Wflat [N]
  * (shape->act); old_idx [k] strictly ascending; old_m, old_v [k] fp32.
  * stats (nullable, device): counts, including the fresh top-k's novelty.
- * Outputs must not alias inputs; grad 16-byte aligned.  Errors:
- * INVALID_ARG for r > k, k > N, r > N - k.  ws: USAF_WS_RIGL bytes for (N, k). */
+ * Outputs must not alias inputs; grad and ws 16-byte aligned (UNSUPPORTED
+ * otherwise).  Errors: INVALID_ARG for r > k, k > N, r > N - k.
+ * ws: USAF_WS_RIGL bytes for (N, k). */
 USAF_API usaf_status usaf_rigl_reselect(const usaf_moe_shape *shape, const float *grad,
                                const void *Wflat, const uint32_t *old_idx,
                                const float *old_m, const float *old_v, int64_t k, int64_t r,

@@ -297,6 +297,10 @@ __global__ __launch_bounds__(256) void topk_pass_a_kernel(KF key, int64_t n, con
 // returns (bin, krem within the bin).
 __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int copies, int stride,
                                          uint32_t krem, int& bin_out, uint32_t& krem_out) {
+  // Scanning from the top bin down, the first bin at which the keys above it
+  // plus its own reach krem; bin 0 when none does.  Group sums of `per`
+  // bins first, then wave 0 finds the group and the bin within it with
+  // suffix sums over lanes (no serial walk).
   __shared__ uint32_t csum[256];
   __shared__ int sbin;
   __shared__ uint32_t skrem;
@@ -311,49 +315,119 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int copie
     csum[threadIdx.x] = s;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t above = 0;
-    int c = 255;
-    for (; c > 0; --c) {
-      if (above + csum[c] >= krem) break;
-      above += csum[c];
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    // suffix sums over the groups: lane l holds groups 4l..4l+3
+    uint32_t g[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) g[j] = csum[4 * lane + j];
+    const uint32_t s4 = (g[0] + g[1]) + (g[2] + g[3]);
+    uint32_t v = s4;  // groups of lanes l.. 63
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t u = __shfl_down(v, d, 64);
+      if (lane + d < 64) v += u;
     }
-    int b = min(nb - 1, c * per + per - 1);
-    for (; b > c * per; --b) {
-      uint32_t hb = 0;
-      for (int cc = 0; cc < copies; ++cc) hb += hist[size_t(cc) * stride + b];
-      if (above + hb >= krem) break;
-      above += hb;
+    // the highest group c >= 1 whose suffix (groups c..255) reaches krem
+    uint32_t cum = v - s4;  // groups above this lane's
+    int jc = -1;
+    uint32_t above_c = 0;
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      if (jc < 0 && 4 * lane + j >= 1 && cum + g[j] >= krem) {
+        jc = j;
+        above_c = cum;
+      }
+      cum += g[j];
     }
-    sbin = b;
-    skrem = krem - above;
+    const uint64_t hit = __ballot(jc >= 0);
+    int c;
+    uint32_t above;
+    if (hit) {
+      const int lh = 63 - __clzll((long long)hit);
+      c = 4 * lh + __shfl(jc, lh, 64);
+      above = __shfl(above_c, lh, 64);
+    } else {  // group 0, under every group above it
+      c = 0;
+      above = __shfl(v - (lane == 0 ? csum[0] : 0u), 0, 64);
+    }
+    // the bin within group c: bins c*per .. min(nb, c*per + per) - 1, the
+    // lowest taken when no higher one reaches krem
+    const int b0 = c * per;
+    const int nbin = min(per, nb - b0);
+    uint32_t hb = 0;
+    if (lane < nbin)
+      for (int cc = 0; cc < copies; ++cc) hb += hist[size_t(cc) * stride + b0 + lane];
+    uint32_t w = hb;  // bins lane.. of the group
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t u = __shfl_down(w, d, 64);
+      if (lane + d < 64) w += u;
+    }
+    const bool reach = lane >= 1 && lane < nbin && above + w >= krem;
+    const uint64_t rb = __ballot(reach);
+    const int jb = rb ? 63 - __clzll((long long)rb) : 0;
+    const uint32_t wj = __shfl(w, jb, 64), hj = __shfl(hb, jb, 64);
+    if (lane == 0) {
+      sbin = min(b0 + jb, nb - 1);
+      skrem = krem - (above + (wj - hj));
+    }
   }
   __syncthreads();
   bin_out = sbin;
   krem_out = skrem;
 }
 
-// Sums the privatised copies into chist, then selects the bin (1024 threads).
-__global__ __launch_bounds__(1024) void topk_select_a_kernel(TopkWs w, const uint32_t* gate) {
-  if (gated_off(gate)) return;
-  for (int b = threadIdx.x; b < kTopkBins; b += 1024) {
-    uint32_t s = 0;
-#pragma unroll 8
-    for (int c = 0; c < kHistCopies; ++c) s += w.hist[size_t(c) * kTopkBins + b];
-    w.chist[b] = s;
+// The privatised histogram copies summed into an LDS histogram by a block
+// of 1024 threads: thread t sums 4 consecutive bins (one 16-byte load per
+// copy) over half of the copies, all of its loads in flight together, and
+// the two halves meet in LDS.  With clear, the copies are zeroed behind the
+// loads.  Ends with a barrier.
+__device__ __forceinline__ void sum_copies_lds(uint32_t* __restrict__ hist, uint32_t* hs, bool clear) {
+  static_assert(kTopkBins == 2048 && kHistCopies % 2 == 0, "512 bin quads x 2 halves = 1024 threads");
+  constexpr int kHalf = kHistCopies / 2;
+  const int t = threadIdx.x, quad = t & 511, half = t >> 9;
+  uint4* src = reinterpret_cast<uint4*>(hist) + size_t(half * kHalf) * (kTopkBins / 4) + quad;
+  uint4 acc = make_uint4(0, 0, 0, 0);
+#pragma unroll 16
+  for (int c = 0; c < kHalf; ++c) {
+    const uint4 v = src[size_t(c) * (kTopkBins / 4)];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  if (clear) {
+#pragma unroll 16
+    for (int c = 0; c < kHalf; ++c) src[size_t(c) * (kTopkBins / 4)] = make_uint4(0, 0, 0, 0);
+  }
+  uint4* hq = reinterpret_cast<uint4*>(hs);
+  if (half == 0) hq[quad] = acc;
+  __syncthreads();
+  if (half == 1) {
+    uint4 v = hq[quad];
+    v.x += acc.x; v.y += acc.y; v.z += acc.z; v.w += acc.w;
+    hq[quad] = v;
   }
   __syncthreads();
+}
+
+// Sums the privatised copies, then selects the bin (1024 threads).
+__global__ __launch_bounds__(1024) void topk_select_a_kernel(TopkWs w, const uint32_t* gate) {
+  if (gated_off(gate)) return;
+  __shared__ __attribute__((aligned(16))) uint32_t hs[kTopkBins];
+  sum_copies_lds(w.hist, hs, false);
   int b;
   uint32_t krem;
-  find_bin(w.chist, kTopkBins, 1, 0, w.st[ST_KREM], b, krem);
-  __syncthreads();
-  for (int q = threadIdx.x; q < kTopkBins; q += 1024) w.chist[q] = 0;
+  find_bin(hs, kTopkBins, 1, 0, w.st[ST_KREM], b, krem);
   if (threadIdx.x == 0) {
     w.st[ST_B0] = uint32_t(b);
     w.st[ST_KREM] = krem;
     w.st[ST_PHI] = uint32_t(b) << 20;  // composite bits 62..52
     w.st[ST_PLO] = 0;
   }
+}
+
+// Set bits of a wave-wide mask held by the lanes below this one.
+__device__ __forceinline__ uint32_t bits_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
 }
 
 // Wave-wide exclusive prefix of a per-lane count, and the wave total.
@@ -731,21 +805,11 @@ static int64_t sample_count(int64_t n) {
 // The threshold bin from the sample: the bin holding the q-th sampled key
 // from the top.  The copies are summed and cleared for pass B1.
 __global__ __launch_bounds__(1024) void topk_sample_select_kernel(TopkWs w, uint32_t q) {
-  for (int b = threadIdx.x; b < kTopkBins; b += 1024) {
-    uint32_t s = 0;
-#pragma unroll 8
-    for (int c = 0; c < kHistCopies; ++c) {
-      s += w.hist[size_t(c) * kTopkBins + b];
-      w.hist[size_t(c) * kTopkBins + b] = 0;
-    }
-    w.chist[b] = s;
-  }
-  __syncthreads();
+  __shared__ __attribute__((aligned(16))) uint32_t hs[kTopkBins];
+  sum_copies_lds(w.hist, hs, true);
   int b;
   uint32_t krem;
-  find_bin(w.chist, kTopkBins, 1, 0, q, b, krem);
-  __syncthreads();
-  for (int x = threadIdx.x; x < kTopkBins; x += 1024) w.chist[x] = 0;
+  find_bin(hs, kTopkBins, 1, 0, q, b, krem);
   if (threadIdx.x == 0) {
     w.st[ST_BS] = uint32_t(b);
     w.st[ST_BSREM] = krem;
@@ -803,14 +867,16 @@ __global__ __launch_bounds__(256) void topk_pass_b1_kernel(const float* __restri
       staged = 0;
       wave_lds_sync();  // the staging buffer is free again
     };
-    // one row of 256 keys: the lane's 4 keys at i (c: at or above thr)
+    // one row of 256 keys: the lane's 4 keys at i (c: at or above thr).  A
+    // candidate's place in the row (index order: lane, then u) is the count
+    // of the candidates of the lanes below it, from one ballot per u
     auto row = [&](int64_t i, const uint32_t (&kv)[4], const bool (&c)[4]) {
-      const uint32_t mine = uint32_t(c[0]) + c[1] + c[2] + c[3];
-      if (__ballot(mine != 0)) {  // uniform: many rows of 256 keys hold no candidate
-        uint32_t tot;
-        const uint32_t ex = wave_excl(mine, tot);
+      const uint64_t b0 = __ballot(c[0]), b1 = __ballot(c[1]), b2 = __ballot(c[2]),
+                     b3 = __ballot(c[3]);
+      if (b0 | b1 | b2 | b3) {  // uniform: many rows of 256 keys hold no candidate
+        const uint32_t tot = uint32_t(__popcll(b0) + __popcll(b1) + __popcll(b2) + __popcll(b3));
         if (staged + tot > kStage) flush();  // uniform; a row holds at most kStage
-        uint32_t p = staged + ex;
+        uint32_t p = staged + ((bits_below(b0) + bits_below(b1)) + (bits_below(b2) + bits_below(b3)));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (c[u]) {
@@ -1382,6 +1448,7 @@ extern "C" usaf_status usaf_importance_topk(const float* grad, int64_t n, int64_
   if (!grad || !out_idx) return USAF_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(grad) & 15) return USAF_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < topk_ws_bytes(n)) return USAF_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return USAF_ERR_UNSUPPORTED;  // 16-byte histogram reads
   return topk_run(KeyGrad{grad}, n, k, n_exclude ? exclude : nullptr, n_exclude, out_idx, out_val,
                   grad, static_cast<char*>(ws), stream);
 }
@@ -1406,6 +1473,7 @@ extern "C" usaf_status usaf_rigl_reselect(const usaf_moe_shape* shape, const flo
   if (reinterpret_cast<uintptr_t>(grad) & 15) return USAF_ERR_UNSUPPORTED;
   const WsRigl L = ws_rigl(N, k);
   if (!ws || ws_bytes < L.total) return USAF_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return USAF_ERR_UNSUPPORTED;  // 16-byte histogram reads
   if (k == 0) return USAF_OK;
   char* w = static_cast<char*>(ws);
   uint32_t* dpos = reinterpret_cast<uint32_t*>(w + L.dpos);
