@@ -265,21 +265,34 @@ def rigl_scan(capi, synth, layer_mod, d, idx, dims, scan_tokens, repeats=2):
     # the forward on the same codes, dequantised as the GEMMs load them,
     # against the forward on their resident copy (just written above)
     w4 = capi.q4_experts(qa[0], sa[0], za[0], qa[1], sa[1], za[1], 128)
-    fwd_ms = {}
-    for name, run in (("resident", lambda: lay.forward()),
-                      ("q4_on_load", lambda: capi.moe_forward_q4(lay.shape, lay.X, lay.Wr, w4, lay.Y,
-                                                                 lay.state, lay.ws_fwd))):
-        ts = []
-        for rep in range(4):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            run()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        fwd_ms[name] = float(np.median(ts[1:]))
+
+    def forwards(ly):
+        out = {}
+        for name, run in (("resident", lambda: ly.forward()),
+                          ("q4_on_load", lambda: capi.moe_forward_q4(ly.shape, ly.X, ly.Wr, w4, ly.Y,
+                                                                     ly.state, ly.ws_fwd))):
+            ts = []
+            for rep in range(4):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                run()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            out[name] = float(np.median(ts[1:]))
+        return out
+
+    fwd_ms = forwards(lay)
+    # the same at the train step's 4096 tokens (the frozen layers of a stack)
+    lay_t = layer_mod.SparseMoELayer(T, H, E, K, I, act=capi.BF16, device=dev)
+    lay_t.X = lay.X[:T].contiguous()
+    lay_t.Wr = lay.Wr
+    lay_t.W = lay.W
+    fwd_t = forwards(lay_t)
+    del lay_t
     log(f"rigl: forward at {Ts} tokens, resident {fwd_ms['resident']:.3f} ms, 4-bit on load "
-        f"{fwd_ms['q4_on_load']:.3f} ms")
+        f"{fwd_ms['q4_on_load']:.3f} ms; at {T} tokens {fwd_t['resident']:.3f} / "
+        f"{fwd_t['q4_on_load']:.3f} ms")
     del qa, sa, za, w4
     # dequant once into the resident bf16 working copy (timed)
     for rep in range(2):
@@ -315,6 +328,7 @@ def rigl_scan(capi, synth, layer_mod, d, idx, dims, scan_tokens, repeats=2):
     return dict(rigl_scan_ms=float(np.median(times)), scan_tokens=Ts, scan_kernels=parts,
                 dequant_ms=float(sum(dq_ms)), dequant_GBps=dq_bytes / (sum(dq_ms) * 1e-3) / 1e9,
                 forward_ms_resident=fwd_ms["resident"], forward_ms_q4_on_load=fwd_ms["q4_on_load"],
+                forward_ms_at_step_tokens=dict(tokens=T, **fwd_t),
                 dequant_affine_g128_ms=float(sum(dqa_ms)),
                 dequant_affine_g128_GBps=dqa_bytes / (sum(dqa_ms) * 1e-3) / 1e9,
                 turnover_applied=float(stats[1]) / k, turnover_topk_vs_old=float(stats[2]) / k,

@@ -153,8 +153,9 @@ typedef struct {
  * only run forward, such as the frozen lower layers of a partly trained
  * stack).  Every output and every field of `state` it writes equals, bit for
  * bit, usaf_moe_forward on the usaf_dequant_affine copy of the same codes.
- * bf16 layers only (UNSUPPORTED otherwise); the code arrays must be 4-byte
- * aligned.  ws: USAF_WS_FORWARD bytes. */
+ * bf16 layers only (UNSUPPORTED otherwise); the code arrays must be 16-byte
+ * aligned and the scale and zero arrays 4-byte aligned (UNSUPPORTED
+ * otherwise).  ws: USAF_WS_FORWARD bytes. */
 USAF_API usaf_status usaf_moe_forward_q4(const usaf_moe_shape *shape, const void *X, const float *Wr,
                                          const usaf_q4_experts *w, void *Y,
                                          const usaf_moe_state *state, void *ws, size_t ws_bytes,

@@ -208,8 +208,10 @@ struct KMajor {
         *reinterpret_cast<uint4*>(lds + r * kRowB + 16 * (q ^ sw(r))) = make_uint4(0, 0, 0, 0);
     }
   }
+  static constexpr bool kPrep = false;  // nothing staged per tile
   // fragment rows base..base+31 (base a multiple of 32), k-substep kc
-  __device__ __forceinline__ static bf16x8_t frag(const unsigned char* lds, int base, int kc, int lane) {
+  __device__ __forceinline__ static bf16x8_t frag(const unsigned char* lds, int base, int kc, int lane,
+                                                  int /*kt*/ = 0) {
     const int r = base + (lane & 31);
     const int q = (2 * kc + (lane >> 5)) ^ sw(r);
     return *reinterpret_cast<const bf16x8_t*>(lds + r * kRowB + 16 * q);
@@ -248,8 +250,10 @@ struct MNMajor {
     for (int x = tid + kvalid * kCPR; x < BK * kCPR; x += 64 * NW)
       *reinterpret_cast<uint4*>(lds + x * 16) = make_uint4(0, 0, 0, 0);
   }
+  static constexpr bool kPrep = false;  // nothing staged per tile
   // fragment rows base..base+31 (the contiguous dimension), k-substep kc
-  __device__ __forceinline__ static bf16x8_t frag(const unsigned char* lds, int base, int kc, int lane) {
+  __device__ __forceinline__ static bf16x8_t frag(const unsigned char* lds, int base, int kc, int lane,
+                                                  int /*kt*/ = 0) {
     const int g = lane >> 4, pq = lane & 15, jj = pq >> 2, q = pq & 3;
     const int n = base + 16 * (g & 1) + 4 * q;
     const int k = 16 * kc + 8 * (g >> 1) + jj;
@@ -262,6 +266,106 @@ struct MNMajor {
   }
 };
 
+
+// A k-major operand of R rows held as affine 4-bit codes in groups of G = 2^gshift
+// along k (w = bf16(fp32(fp32(q - z) * s)), element 2i in the low nibble of
+// byte i), dequantised as its MFMA fragments are read.  Per 64-k stage, by
+// DMA: the rows' 32 code bytes as two 16-byte halves in two planes
+// ([half][row][16 B]: a fragment's 4-byte reads by 32 consecutive rows meet
+// 2-way bank conflicts at most), and for every row the aligned pair of fp16
+// scales, and of zeros, holding the stage's group (G is a multiple of 64, so
+// a stage lies in one group; the pair's other half belongs to the
+// neighbouring group or row).  Which half is the stage's follows from the
+// parity of row * groups_per_row + group; the row parities are kept per lane
+// (prep, once per tile).  The contraction must be a whole number of stages.
+// Src: code_row(r) -> global code row of tile row r (r < R, always valid);
+// q, s, z; qpitch (bytes per code row), kg (groups per row), gshift.
+template <int R, int NW>
+struct KMajorQ4 {
+  static constexpr int kBK = 64;
+  static constexpr int kFragReads = 3;
+  static constexpr bool kPrep = true;
+  static constexpr int kPlane = R * 16;                 // bytes of one half-row plane
+  static constexpr int kScaleOff = 2 * kPlane;          // fp16 scale pairs, 4 bytes per row
+  static constexpr int kZeroOff = kScaleOff + 4 * R;    // fp16 zero pairs
+  static constexpr int kBytes = kZeroOff + 4 * R;
+  static constexpr int kBlocks = R / 64;                // 64 rows per DMA instruction
+  static constexpr int kGroups = 4 * kBlocks;           // two code halves, scales, zeros
+  static constexpr bool kEven = kGroups % NW == 0;
+  static constexpr int kInst = (kGroups + NW - 1) / NW;
+  static constexpr int kInstMin = kGroups / NW;
+  static_assert(R % 64 == 0 && kInstMin > 0, "row blocks");
+  __device__ __forceinline__ static int group_of(int w, int i) { return kEven ? w * kInst + i : i * NW + w; }
+  __device__ __forceinline__ static bool has_inst(int w, int i) {
+    return kEven || i < kInstMin || w < kGroups - kInstMin * NW;
+  }
+  const unsigned char* src[kInst];  // codes: the row's byte 0 (+16 for the upper half)
+  int64_t elem[kInst];              // scales / zeros: the row's first element
+  const uint16_t* sz[kInst];
+  int kg, gsh6;                     // groups per row; log2(G) - 6
+  uint32_t parbits;                 // bit b: parity of code_row(32 b + lane % 32) * kg
+  template <class Src>
+  __device__ __forceinline__ void init(const Src& s, int, int w, int lane) {
+    kg = s.kg;
+    gsh6 = s.gshift - 6;
+#pragma unroll
+    for (int i = 0; i < kInst; ++i) {
+      const int j = min(group_of(w, i), kGroups - 1);
+      const int kind = j / kBlocks, b = j % kBlocks;  // 0, 1: code halves; 2: scales; 3: zeros
+      const int64_t row = s.code_row(64 * b + lane);
+      src[i] = s.q + row * s.qpitch + 16 * (kind & 1);
+      elem[i] = row * s.kg;
+      sz[i] = kind == 2 ? s.s : s.z;
+    }
+  }
+  template <class Src>
+  __device__ __forceinline__ void prep(const Src& s, int tid) {
+    parbits = 0;
+    if (s.kg & 1) {
+#pragma unroll
+      for (int b = 0; b < R / 32; ++b)
+        parbits |= uint32_t(s.code_row(32 * b + (tid & 31)) & 1) << b;
+    }
+  }
+  template <class Src>
+  __device__ __forceinline__ void issue(const Src&, int kt, unsigned char* lds, int w, int) const {
+    const int64_t g = kt >> gsh6;
+#pragma unroll
+    for (int i = 0; i < kInst; ++i) {
+      if (!has_inst(w, i)) break;  // wave-uniform
+      const int j = group_of(w, i);
+      const int kind = j / kBlocks, b = j % kBlocks;
+      if (kind < 2)
+        dma16(src[i] + 32 * kt, lds + kind * kPlane + b * 1024);
+      else
+        dma4(sz[i] + ((elem[i] + g) & ~int64_t(1)), lds + (kind == 2 ? kScaleOff : kZeroOff) + b * 256);
+    }
+  }
+  // the contraction is a whole number of stages: nothing to clear
+  __device__ __forceinline__ static void zero_tail(unsigned char*, int, int) {}
+  // fragment rows base..base+31, k-substep kc of stage kt: 8 dequantised weights
+  __device__ __forceinline__ bf16x8_t frag(const unsigned char* lds, int base, int kc, int lane,
+                                           int kt) const {
+    const int n = base + (lane & 31);
+    const int wd = 2 * (kc & 1) + (lane >> 5);
+    const uint32_t code = *reinterpret_cast<const uint32_t*>(lds + (kc >> 1) * kPlane + n * 16 + 4 * wd);
+    const uint32_t sp = *reinterpret_cast<const uint32_t*>(lds + kScaleOff + 4 * n);
+    const uint32_t zp = *reinterpret_cast<const uint32_t*>(lds + kZeroOff + 4 * n);
+    const uint32_t sh = 16u * (((parbits >> (n >> 5)) + uint32_t(kt >> gsh6)) & 1u);
+    const float sc = float(__builtin_bit_cast(_Float16, uint16_t(sp >> sh)));
+    const float zr = float(__builtin_bit_cast(_Float16, uint16_t(zp >> sh)));
+    // the low and high nibbles of the four bytes, each converted as a byte
+    const uint32_t lo = code & 0x0f0f0f0fu, hi = (code >> 4) & 0x0f0f0f0fu;
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float d0 = float((lo >> (8 * j)) & 0xffu) - zr;
+      const float d1 = float((hi >> (8 * j)) & 0xffu) - zr;
+      o[j] = f2bf2(d0 * sc, d1 * sc);
+    }
+    return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+  }
+};
 
 // lgkmcnt(0): this wave's LDS accesses have completed (the compiler cannot
 // see the cross-lane dependence of the staging below).
@@ -414,7 +518,7 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
 #pragma unroll
       for (int i = 0; i < VB; ++i) af[0][i] = AOp::frag(As, r0 + 32 * i, 0, lane);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) bfr[0][j] = BOp::frag(Bs, wn * CW + 32 * j, 0, lane);
+      for (int j = 0; j < NJ; ++j) bfr[0][j] = bo.frag(Bs, wn * CW + 32 * j, 0, lane, kt);
       if constexpr (!kFirst) {
         mfmas(pa, pb);  // the previous stage's last substep
         interleave_mfma_reads<NM, NR>();
@@ -425,7 +529,7 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
 #pragma unroll
         for (int i = 0; i < VB; ++i) af[n][i] = AOp::frag(As, r0 + 32 * i, kc + 1, lane);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) bfr[n][j] = BOp::frag(Bs, wn * CW + 32 * j, kc + 1, lane);
+        for (int j = 0; j < NJ; ++j) bfr[n][j] = bo.frag(Bs, wn * CW + 32 * j, kc + 1, lane, kt);
         mfmas(af[c], bfr[c]);
         interleave_mfma_reads<NM, NR>();
       }
@@ -478,6 +582,7 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_kernel(P p) {
       ao.issue(as, s, lds[s], w, lane);
       bo.issue(bs, s, lds[s] + A_BYTES, w, lane);
     }
+  if constexpr (BOp::kPrep) bo.prep(bs, tid);  // per-tile operand state, published by the first stage's barrier
   main_loop<P, IM, IM, NJ>(ao, bo, as, bs, lds, K, nk, tid, w, wm * P::RW, wn, lane, acc);
   __syncthreads();  // the ring is free: epilogues may stage through it
   p.epilogue(t, acc, wm, wn, lane, &lds[0][0] + w * P::kStageBytes);
@@ -519,6 +624,9 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_persistent(P p)
       bo.issue(bs, s, lds[s] + A_BYTES, w, lane);
     }
   while (true) {
+    // per-tile operand state (after the previous tile's last reads: the
+    // barrier below its main loop), published by the first stage's barrier
+    if constexpr (BOp::kPrep) bo.prep(bs, tid);
     f32x16_t acc[IM][NJ];
 #pragma unroll
     for (int i = 0; i < IM; ++i)

@@ -29,4 +29,14 @@ __device__ __forceinline__ void dma16(const void* g, unsigned char* lds_base) {
                : "memory", "m0");
 }
 
+// The same with 4 bytes per lane: lane l's 4 bytes land at lds_base + 4 l.
+// The global address must be 4-byte aligned.
+__device__ __forceinline__ void dma4(const void* g, unsigned char* lds_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(uint32_t(size_t((lds_void_t*)lds_base)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(l)
+               : "memory", "m0");
+}
+
 }  // namespace usaf

@@ -1235,8 +1235,11 @@ extern "C" usaf_status usaf_moe_forward_q4(const usaf_moe_shape* shape, const vo
   if (s.act != USAF_BF16) return USAF_ERR_UNSUPPORTED;
   if ((w->group != 64 && w->group != 128) || s.H % w->group || s.I % w->group)
     return USAF_ERR_UNSUPPORTED;
-  if ((reinterpret_cast<uintptr_t>(w->q_gu) | reinterpret_cast<uintptr_t>(w->q_d)) & 3)
-    return USAF_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(w->q_gu) | reinterpret_cast<uintptr_t>(w->q_d)) & 15)
+    return USAF_ERR_UNSUPPORTED;  // 16-byte code loads
+  if ((reinterpret_cast<uintptr_t>(w->s_gu) | reinterpret_cast<uintptr_t>(w->z_gu) |
+       reinterpret_cast<uintptr_t>(w->s_d) | reinterpret_cast<uintptr_t>(w->z_d)) & 3)
+    return USAF_ERR_UNSUPPORTED;  // 4-byte scale and zero pairs
   if (!ws || ws_bytes < ws_forward(s).total) return USAF_ERR_WORKSPACE;
   const WsForward L = ws_forward(s);
   char* wsc = static_cast<char*>(ws);

@@ -266,6 +266,62 @@ struct MDown {
   }
 };
 
+// The forward GEMMs on the pages' affine 4-bit storage (README "how it
+// works": caching bullet, the trade between a resident dequantised copy and
+// dequantising as the weights are used; quantisation recipe: codes in groups
+// along the input dimension): the same problems with the weight operand read
+// as codes and dequantised in the fragment reads (KMajorQ4).  A layer so
+// computed equals, bit for bit, the same layer on the resident copy of the
+// same codes: the weights are the same bf16 values, and every output
+// accumulates the same MFMA chunks in the same order.
+struct Q4Codes {
+  const uint8_t* q; const uint16_t* s; const uint16_t* z;
+  int64_t qpitch;  // bytes per code row (K / 2)
+  int kg;          // groups per row (K / G)
+  int gshift;      // log2(G)
+};
+// gate_up code rows in the feature order of GateUpRowsC
+template <int CW>
+struct GateUpCodesC : Q4Codes {
+  int64_t row0; int F0; int I;
+  __device__ __forceinline__ int64_t code_row(int c) const {
+    const int wn = c / CW, j = (c % CW) >> 5;
+    const int f = min(F0 + (CW / 2) * wn + 32 * (j >> 1) + (c & 31), I - 1);
+    return row0 + ((j & 1) ? I + f : f);
+  }
+};
+// consecutive code rows: row r -> row0 + min(r, n - 1)
+struct RowCodesC : Q4Codes {
+  int64_t row0; int n;
+  __device__ __forceinline__ int64_t code_row(int r) const { return row0 + min(r, n - 1); }
+};
+
+template <int BM_, int BN_, int NS_, int WM_, int WN_>
+struct MGateUpQ4 : MGateUp<BM_, BN_, NS_, WM_, WN_, 64> {
+  using Base = MGateUp<BM_, BN_, NS_, WM_, WN_, 64>;
+  using BOp = KMajorQ4<BN_, WM_ * WN_>;
+  static constexpr int kPStage =
+      Base::kPStage * WM_ * WN_ <= Base::AOp::kBytes + BOp::kBytes ? Base::kPStage : 0;
+  static constexpr int kStageBytes = kPStage;
+  Q4Codes c;
+  __device__ __forceinline__ GateUpCodesC<Base::CW> b_src(const MTile& t) const {
+    return GateUpCodesC<Base::CW>{c, int64_t(t.e) * 2 * this->I, t.n0, this->I};
+  }
+};
+
+template <int BM_, int BN_, int NS_, int WM_, int WN_>
+struct MDownQ4 : MDown<BM_, BN_, NS_, WM_, WN_, 64> {
+  using Base = MDown<BM_, BN_, NS_, WM_, WN_, 64>;
+  using BOp = KMajorQ4<BN_, WM_ * WN_>;
+  static constexpr int kPStage =
+      Base::kPStage * WM_ * WN_ <= Base::AOp::kBytes + BOp::kBytes ? Base::kPStage : 0;
+  static constexpr int kStageBytes = kPStage;
+  Q4Codes c;
+  __device__ __forceinline__ RowCodesC b_src(const MTile& t) const {
+    return RowCodesC{c, int64_t(t.e) * this->H + t.n0, t.nc};
+  }
+};
+
 template <int BM_, int BN_, int NS_, int WM_ = 2, int WN_ = 2, int BK_ = 64>
 struct MDa {
   static constexpr int BM = BM_, BN = BN_, NS = NS_, WM = WM_, WN = WN_, NTHR = 64 * WM_ * WN_;
@@ -719,6 +775,46 @@ usaf_status mfma_dense_dw(const usaf_moe_shape& s, const bf16_t* X, const bf16_t
   }
   timer_end(USAF_K_DENSE_DW, st);
   return USAF_OK;
+}
+
+// The 4-bit forward GEMMs.  Ring depths for the smaller weight stages
+// (a 256-column stage of codes, scales and zeros is 10 KiB against 32 KiB of
+// bf16): 160-row tiles 4 stages (120 KiB), 256-row tiles 3 (126 KiB).
+constexpr int kQ4NS = 4, kQ4BigNS = 3;
+
+static int log2_exact(int g) {
+  int s = 0;
+  while ((1 << s) < g) ++s;
+  return s;
+}
+
+usaf_status q4_gate_up(const usaf_moe_shape& s, const bf16_t* X, const usaf_q4_experts& w,
+                       const int32_t* offsets, const int32_t* perm, bf16_t* gu, bf16_t* a,
+                       hipStream_t st) {
+  const int NT = int(ceil_div(s.I, kFwdBN / 2));
+  const g2::Q4Codes c{w.q_gu, w.s_gu, w.z_gu, s.H / 2, s.H / w.group, log2_exact(w.group)};
+  if (big_groups(s)) {
+    using P = g2::MGateUpQ4<kBigBM, kFwdBN, kQ4BigNS, kBigWM, kBigWN>;
+    const P p{{X, nullptr, offsets, perm, gu, a, s.H, s.E, s.K, s.I, NT}, c};
+    return launch_persistent(p, grouped_tiles_bound(s, NT, kBigBM), st, USAF_K_GATE_UP);
+  }
+  using P = g2::MGateUpQ4<kFwdBM, kFwdBN, kQ4NS, kFwdWM, kFwdWN>;
+  const P p{{X, nullptr, offsets, perm, gu, a, s.H, s.E, s.K, s.I, NT}, c};
+  return launch_persistent(p, grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_GATE_UP);
+}
+
+usaf_status q4_down(const usaf_moe_shape& s, const bf16_t* a, const usaf_q4_experts& w,
+                    const int32_t* offsets, bf16_t* ybuf, hipStream_t st) {
+  const int NT = int(ceil_div(s.H, kFwdBN));
+  const g2::Q4Codes c{w.q_d, w.s_d, w.z_d, s.I / 2, s.I / w.group, log2_exact(w.group)};
+  if (big_groups(s)) {
+    using P = g2::MDownQ4<kBigBM, kFwdBN, kQ4BigNS, kBigWM, kBigWN>;
+    const P p{{a, nullptr, offsets, ybuf, s.H, s.E, s.I, NT}, c};
+    return launch_persistent(p, grouped_tiles_bound(s, NT, kBigBM), st, USAF_K_DOWN);
+  }
+  using P = g2::MDownQ4<kFwdBM, kFwdBN, kQ4NS, kFwdWM, kFwdWN>;
+  const P p{{a, nullptr, offsets, ybuf, s.H, s.E, s.I, NT}, c};
+  return launch_persistent(p, grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DOWN);
 }
 
 }  // namespace usaf

@@ -98,6 +98,16 @@ def test_entry_points_refuse_bad_arguments_before_launch():
     assert L.usaf_masked_plan(C.byref(shb), FAKE, 5, FAKE, need - 1, None) == 3
     assert L.usaf_masked_plan(C.byref(shb), FAKE, 5, None, need, None) == 3
     assert L.usaf_masked_plan(C.byref(shb), None, 0, FAKE, need, None) == 0  # empty list: nothing to plan
+    # 4-bit forward: fp32 layers, a group other than 64 / 128, misaligned codes or scales, nulls
+    shq = capi.Shape(128, 256, 8, 2, 128, 1)
+    q4 = lambda group=64, q=FAKE, sc=FAKE: capi.Q4Experts(q, sc, FAKE, q, sc, FAKE, group)
+    fwd_q4 = lambda shape, w: L.usaf_moe_forward_q4(C.byref(shape), FAKE, FAKE, C.byref(w), FAKE,
+                                                   C.byref(st), FAKE, 1 << 30, None)
+    assert fwd_q4(capi.Shape(128, 256, 8, 2, 128, 0), q4()) == 2
+    assert fwd_q4(shq, q4(group=32)) == 2
+    assert fwd_q4(shq, q4(q=FAKE + 4)) == 2
+    assert fwd_q4(shq, q4(sc=FAKE + 2)) == 2
+    assert fwd_q4(shq, q4(q=0)) == 1
     assert L.usaf_masked_plan(C.byref(sh), FAKE, 5, None, 0, None) == 0      # fp32 layers need no plan
     # top-k: k larger than the candidates; k == 0 is a no-op
     assert L.usaf_importance_topk(FAKE, 100, 101, None, 0, FAKE, None, FAKE, 1 << 20, None) == 1
