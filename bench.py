@@ -169,6 +169,37 @@ def time_kernel_classes(capi, lay, classes, lr):
     return out
 
 
+def practical_hbm_rates(nbytes=2416 * 10 ** 6):
+    """What plain device copies reach on this part: a copy (read + write),
+    a fill (write) and a sum (read) of an N-byte fp32 buffer (the size of
+    the Qwen3-shaped layer's dense gradient), median of 4 after one warm-up.
+    Context for the roofline fractions, which stay against the 8 TB/s
+    peak."""
+    import numpy as np
+    import torch
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+
+    def timed(fn):
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts[1:]))
+
+    out = dict(bytes=nbytes,
+               copy_GBps=2 * nbytes / timed(lambda: b.copy_(a)) / 1e6,
+               fill_GBps=nbytes / timed(lambda: b.fill_(1.0)) / 1e6,
+               sum_GBps=nbytes / timed(lambda: a.sum()) / 1e6)
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def adam_scatter_ceiling(capi, lay, lr, reps=10):
     """SparseAdam's update of the expert list against a plain scattered write
     of the same list (usaf_scatter of the compact weights back to W at idx,
@@ -820,6 +851,7 @@ def main():
                    "tokens": T, "hidden": H, "experts": E, "top_k": K, "intermediate": I,
                    "active_entries": k, "density": 0.005, "lr": lr},
         "roofline": roof,
+        "hbm_practical": practical_hbm_rates(),
         "nonfinite_steps": nonfinite,
         "step_kernels": step_kernels,
     }

@@ -143,7 +143,7 @@ USAF_API usaf_status usaf_moe_forward(const usaf_moe_shape *shape, const void *X
 typedef struct {
   const uint8_t *q_gu; const uint16_t *s_gu; const uint16_t *z_gu;
   const uint8_t *q_d;  const uint16_t *s_d;  const uint16_t *z_d;
-  int32_t group;  /* 64 or 128; must divide H and I */
+  int32_t group;  /* 64 or 128; for usaf_moe_forward_q4, 2 * group must divide H and I */
 } usaf_q4_experts;
 
 /* The layer forward of usaf_moe_forward with the expert weights read from

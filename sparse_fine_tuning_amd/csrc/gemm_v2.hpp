@@ -269,91 +269,110 @@ struct MNMajor {
 
 // A k-major operand of R rows held as affine 4-bit codes in groups of G = 2^gshift
 // along k (w = bf16(fp32(fp32(q - z) * s)), element 2i in the low nibble of
-// byte i), dequantised as its MFMA fragments are read.  Per 64-k stage, by
-// DMA: the rows' 32 code bytes as two 16-byte halves in two planes
-// ([half][row][16 B]: a fragment's 4-byte reads by 32 consecutive rows meet
-// 2-way bank conflicts at most), and for every row the aligned pair of fp16
-// scales, and of zeros, holding the stage's group (G is a multiple of 64, so
-// a stage lies in one group; the pair's other half belongs to the
-// neighbouring group or row).  Which half is the stage's follows from the
-// parity of row * groups_per_row + group; the row parities are kept per lane
-// (prep, once per tile).  The contraction must be a whole number of stages.
+// byte i), dequantised as its MFMA fragments are read.  The codes do not go
+// through the ring: they arrive by DMA in blocks of CB stages (a row's
+// 32 CB bytes at once, whole 64-byte lines rather than 16-byte pieces per
+// stage), into one of two LDS buffers by block parity, 16-byte chunks
+// swizzled by row as in KMajor; the fp16 scales and zeros arrive per row 8
+// groups (16 bytes) at a time, into one of two buffers by parity.  A block's
+// loads go out with its first stage's, so the per-stage vmcnt waits (counted
+// on the other operand's loads alone) cover them.  A block's loads are issued
+// NS - 1 stages ahead, while stage kt is current; the previous block of the
+// same parity ended with stage (block start) - CB - 1, which is below kt
+// when CB >= NS - 1 (the problem asserts it; a scale block spans
+// 8 G / 64 >= 8 stages), so no buffer is refilled while a stage still reads
+// it.  Requirements: the contraction a whole number of stages, G a multiple
+// of 64, an even number kg >= 2 of groups per row (4-byte aligned pairs).
 // Src: code_row(r) -> global code row of tile row r (r < R, always valid);
 // q, s, z; qpitch (bytes per code row), kg (groups per row), gshift.
-template <int R, int NW>
+template <int R, int NW, int CB>
 struct KMajorQ4 {
   static constexpr int kBK = 64;
   static constexpr int kFragReads = 3;
-  static constexpr bool kPrep = true;
-  static constexpr int kPlane = R * 16;                 // bytes of one half-row plane
-  static constexpr int kScaleOff = 2 * kPlane;          // fp16 scale pairs, 4 bytes per row
-  static constexpr int kZeroOff = kScaleOff + 4 * R;    // fp16 zero pairs
-  static constexpr int kBytes = kZeroOff + 4 * R;
-  static constexpr int kBlocks = R / 64;                // 64 rows per DMA instruction
-  static constexpr int kGroups = 4 * kBlocks;           // two code halves, scales, zeros
-  static constexpr bool kEven = kGroups % NW == 0;
-  static constexpr int kInst = (kGroups + NW - 1) / NW;
-  static constexpr int kInstMin = kGroups / NW;
-  static_assert(R % 64 == 0 && kInstMin > 0, "row blocks");
-  __device__ __forceinline__ static int group_of(int w, int i) { return kEven ? w * kInst + i : i * NW + w; }
-  __device__ __forceinline__ static bool has_inst(int w, int i) {
-    return kEven || i < kInstMin || w < kGroups - kInstMin * NW;
+  static constexpr bool kPrep = false;
+  static constexpr int kCB = CB;
+  static constexpr int kBytes = 0;                      // nothing in the ring
+  static constexpr int kInstMin = 0;                    // most stages issue no block loads
+  static constexpr int kRowB = 32 * CB;                 // code bytes of a row per block
+  static constexpr int kChunks = kRowB / 16;
+  static constexpr int kRowsPerInst = 64 / kChunks;
+  static constexpr int kCodeInst = R / kRowsPerInst;    // DMA instructions per code block
+  static constexpr int kCodeBuf = R * kRowB;
+  static constexpr int kScaleBuf = R * 16;              // one array's 8 groups of every row
+  static constexpr int kScaleInst = R / 16;             // per array: 4 lanes x 4 bytes per row
+  static constexpr int kCodePW = kCodeInst / NW, kScalePW = 2 * kScaleInst / NW;
+  static_assert(kChunks >= 2 && kChunks <= 8 && kCodePW * NW == kCodeInst &&
+                kScalePW * NW == 2 * kScaleInst, "code and scale blocks shared evenly by the waves");
+  __device__ __forceinline__ static unsigned char* code_lds() {
+    __shared__ __attribute__((aligned(16))) unsigned char buf[2 * kCodeBuf];
+    return buf;
   }
-  const unsigned char* src[kInst];  // codes: the row's byte 0 (+16 for the upper half)
-  int64_t elem[kInst];              // scales / zeros: the row's first element
-  const uint16_t* sz[kInst];
-  int kg, gsh6;                     // groups per row; log2(G) - 6
-  uint32_t parbits;                 // bit b: parity of code_row(32 b + lane % 32) * kg
+  __device__ __forceinline__ static unsigned char* scale_lds() {  // [parity][s, z][row][16 B]
+    __shared__ __attribute__((aligned(16))) unsigned char buf[4 * kScaleBuf];
+    return buf;
+  }
+  // 16-byte chunk slot swizzle, as KMajor::sw for rows of kRowB bytes
+  __device__ __forceinline__ static int sw(int r) { return (r / (256 / kRowB)) & (kChunks - 1); }
+  const unsigned char* cptr[kCodePW];  // the lane's code row, at its first chunk
+  int cchunk[kCodePW];                 // that chunk's index in the row
+  int64_t selem[kScalePW];             // scales / zeros: the lane's first element (group 2 d)
+  const uint16_t* sbase[kScalePW];
+  int qpitch, kg, gsh6;
   template <class Src>
   __device__ __forceinline__ void init(const Src& s, int, int w, int lane) {
+    qpitch = int(s.qpitch);
     kg = s.kg;
     gsh6 = s.gshift - 6;
 #pragma unroll
-    for (int i = 0; i < kInst; ++i) {
-      const int j = min(group_of(w, i), kGroups - 1);
-      const int kind = j / kBlocks, b = j % kBlocks;  // 0, 1: code halves; 2: scales; 3: zeros
-      const int64_t row = s.code_row(64 * b + lane);
-      src[i] = s.q + row * s.qpitch + 16 * (kind & 1);
-      elem[i] = row * s.kg;
-      sz[i] = kind == 2 ? s.s : s.z;
+    for (int i = 0; i < kCodePW; ++i) {
+      const int r = (w + NW * i) * kRowsPerInst + lane / kChunks;
+      cchunk[i] = (lane % kChunks) ^ sw(r);
+      cptr[i] = s.q + s.code_row(r) * s.qpitch;
+    }
+#pragma unroll
+    for (int i = 0; i < kScalePW; ++i) {
+      const int j = w + NW * i;  // 0 .. 2 kScaleInst - 1: scales, then zeros
+      const int r = (j % kScaleInst) * 16 + lane / 4;
+      selem[i] = s.code_row(r) * s.kg + 2 * (lane % 4);
+      sbase[i] = j < kScaleInst ? s.s : s.z;
     }
   }
   template <class Src>
-  __device__ __forceinline__ void prep(const Src& s, int tid) {
-    parbits = 0;
-    if (s.kg & 1) {
+  __device__ __forceinline__ void issue(const Src&, int kt, unsigned char*, int w, int lane) const {
+    if (kt % CB == 0) {  // uniform: a code block starts
+      unsigned char* dst = code_lds() + ((kt / CB) & 1) * kCodeBuf;
+      const int b0 = 32 * kt;  // the block's first byte in a row
 #pragma unroll
-      for (int b = 0; b < R / 32; ++b)
-        parbits |= uint32_t(s.code_row(32 * b + (tid & 31)) & 1) << b;
+      for (int i = 0; i < kCodePW; ++i) {
+        // a chunk past the row's end (a last block of fewer than CB stages)
+        // reads the row's last chunk instead; it is never used
+        const int off = min(b0 + 16 * cchunk[i], qpitch - 16);
+        dma16(cptr[i] + off, dst + (w + NW * i) * 1024);
+      }
+    }
+    if ((kt & ((8 << gsh6) - 1)) == 0) {  // uniform: a scale block (8 groups) starts
+      const int g0 = kt >> gsh6;
+      unsigned char* dst = scale_lds() + ((g0 >> 3) & 1) * 2 * kScaleBuf;
+#pragma unroll
+      for (int i = 0; i < kScalePW; ++i) {
+        const int j = w + NW * i;
+        // pairs past the row's groups read the row's last pair; never used
+        const int64_t e = selem[i] + min(g0, kg - 2 - 2 * (lane % 4));
+        dma4(sbase[i] + e, dst + (j >= kScaleInst ? kScaleBuf : 0) + (j % kScaleInst) * 256);
+      }
     }
   }
-  template <class Src>
-  __device__ __forceinline__ void issue(const Src&, int kt, unsigned char* lds, int w, int) const {
-    const int64_t g = kt >> gsh6;
-#pragma unroll
-    for (int i = 0; i < kInst; ++i) {
-      if (!has_inst(w, i)) break;  // wave-uniform
-      const int j = group_of(w, i);
-      const int kind = j / kBlocks, b = j % kBlocks;
-      if (kind < 2)
-        dma16(src[i] + 32 * kt, lds + kind * kPlane + b * 1024);
-      else
-        dma4(sz[i] + ((elem[i] + g) & ~int64_t(1)), lds + (kind == 2 ? kScaleOff : kZeroOff) + b * 256);
-    }
-  }
-  // the contraction is a whole number of stages: nothing to clear
   __device__ __forceinline__ static void zero_tail(unsigned char*, int, int) {}
   // fragment rows base..base+31, k-substep kc of stage kt: 8 dequantised weights
-  __device__ __forceinline__ bf16x8_t frag(const unsigned char* lds, int base, int kc, int lane,
-                                           int kt) const {
+  __device__ __forceinline__ bf16x8_t frag(const unsigned char*, int base, int kc, int lane, int kt) const {
     const int n = base + (lane & 31);
-    const int wd = 2 * (kc & 1) + (lane >> 5);
-    const uint32_t code = *reinterpret_cast<const uint32_t*>(lds + (kc >> 1) * kPlane + n * 16 + 4 * wd);
-    const uint32_t sp = *reinterpret_cast<const uint32_t*>(lds + kScaleOff + 4 * n);
-    const uint32_t zp = *reinterpret_cast<const uint32_t*>(lds + kZeroOff + 4 * n);
-    const uint32_t sh = 16u * (((parbits >> (n >> 5)) + uint32_t(kt >> gsh6)) & 1u);
-    const float sc = float(__builtin_bit_cast(_Float16, uint16_t(sp >> sh)));
-    const float zr = float(__builtin_bit_cast(_Float16, uint16_t(zp >> sh)));
+    const int byte = 32 * (kt % CB) + 8 * kc + 4 * (lane >> 5);
+    const uint32_t code = *reinterpret_cast<const uint32_t*>(
+        code_lds() + ((kt / CB) & 1) * kCodeBuf + n * kRowB + 16 * ((byte >> 4) ^ sw(n)) + (byte & 15));
+    const int g = kt >> gsh6;
+    const unsigned char* sb = scale_lds() + ((g >> 3) & 1) * 2 * kScaleBuf + n * 16 + 2 * (g & 7);
+    const float sc = float(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb)));
+    const float zr = float(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb + kScaleBuf)));
     // the low and high nibbles of the four bytes, each converted as a byte
     const uint32_t lo = code & 0x0f0f0f0fu, hi = (code >> 4) & 0x0f0f0f0fu;
     uint32_t o[4];

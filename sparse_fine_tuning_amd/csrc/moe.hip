@@ -1233,8 +1233,8 @@ extern "C" usaf_status usaf_moe_forward_q4(const usaf_moe_shape* shape, const vo
   if (!w->q_gu || !w->s_gu || !w->z_gu || !w->q_d || !w->s_d || !w->z_d) return USAF_ERR_INVALID_ARG;
   const usaf_moe_shape& s = *shape;
   if (s.act != USAF_BF16) return USAF_ERR_UNSUPPORTED;
-  if ((w->group != 64 && w->group != 128) || s.H % w->group || s.I % w->group)
-    return USAF_ERR_UNSUPPORTED;
+  if ((w->group != 64 && w->group != 128) || s.H % (2 * w->group) || s.I % (2 * w->group))
+    return USAF_ERR_UNSUPPORTED;  // an even number of groups per row (4-byte scale pairs)
   if ((reinterpret_cast<uintptr_t>(w->q_gu) | reinterpret_cast<uintptr_t>(w->q_d)) & 15)
     return USAF_ERR_UNSUPPORTED;  // 16-byte code loads
   if ((reinterpret_cast<uintptr_t>(w->s_gu) | reinterpret_cast<uintptr_t>(w->z_gu) |

@@ -274,6 +274,7 @@ struct MDown {
 // computed equals, bit for bit, the same layer on the resident copy of the
 // same codes: the weights are the same bf16 values, and every output
 // accumulates the same MFMA chunks in the same order.
+constexpr int kQ4CodeBlock = 2;  // stages per code block: a row's 64 code bytes per request
 struct Q4Codes {
   const uint8_t* q; const uint16_t* s; const uint16_t* z;
   int64_t qpitch;  // bytes per code row (K / 2)
@@ -299,7 +300,8 @@ struct RowCodesC : Q4Codes {
 template <int BM_, int BN_, int NS_, int WM_, int WN_>
 struct MGateUpQ4 : MGateUp<BM_, BN_, NS_, WM_, WN_, 64> {
   using Base = MGateUp<BM_, BN_, NS_, WM_, WN_, 64>;
-  using BOp = KMajorQ4<BN_, WM_ * WN_>;
+  using BOp = KMajorQ4<BN_, WM_ * WN_, kQ4CodeBlock>;
+  static_assert(BOp::kCB >= NS_ - 1, "a code buffer is refilled only after its stages are done");
   static constexpr int kPStage =
       Base::kPStage * WM_ * WN_ <= Base::AOp::kBytes + BOp::kBytes ? Base::kPStage : 0;
   static constexpr int kStageBytes = kPStage;
@@ -312,7 +314,8 @@ struct MGateUpQ4 : MGateUp<BM_, BN_, NS_, WM_, WN_, 64> {
 template <int BM_, int BN_, int NS_, int WM_, int WN_>
 struct MDownQ4 : MDown<BM_, BN_, NS_, WM_, WN_, 64> {
   using Base = MDown<BM_, BN_, NS_, WM_, WN_, 64>;
-  using BOp = KMajorQ4<BN_, WM_ * WN_>;
+  using BOp = KMajorQ4<BN_, WM_ * WN_, kQ4CodeBlock>;
+  static_assert(BOp::kCB >= NS_ - 1, "a code buffer is refilled only after its stages are done");
   static constexpr int kPStage =
       Base::kPStage * WM_ * WN_ <= Base::AOp::kBytes + BOp::kBytes ? Base::kPStage : 0;
   static constexpr int kStageBytes = kPStage;
@@ -777,10 +780,11 @@ usaf_status mfma_dense_dw(const usaf_moe_shape& s, const bf16_t* X, const bf16_t
   return USAF_OK;
 }
 
-// The 4-bit forward GEMMs.  Ring depths for the smaller weight stages
-// (a 256-column stage of codes, scales and zeros is 10 KiB against 32 KiB of
-// bf16): 160-row tiles 4 stages (120 KiB), 256-row tiles 3 (126 KiB).
-constexpr int kQ4NS = 4, kQ4BigNS = 3;
+// The 4-bit forward GEMMs: the ring holds the activations only (3 stages:
+// 60 KiB for 160-row tiles, 96 KiB for 256-row ones), beside the two code
+// buffers (2 x 32 KiB for 256 weight rows) and the two scale buffers
+// (2 x 2 x 4 KiB).
+constexpr int kQ4NS = 3, kQ4BigNS = 3;
 
 static int log2_exact(int g) {
   int s = 0;

@@ -108,6 +108,7 @@ def test_entry_points_refuse_bad_arguments_before_launch():
     assert fwd_q4(shq, q4(q=FAKE + 4)) == 2
     assert fwd_q4(shq, q4(sc=FAKE + 2)) == 2
     assert fwd_q4(shq, q4(q=0)) == 1
+    assert fwd_q4(capi.Shape(128, 256, 8, 2, 192, 1), q4()) == 2  # I / 64 = 3 groups: odd
     assert L.usaf_masked_plan(C.byref(sh), FAKE, 5, None, 0, None) == 0      # fp32 layers need no plan
     # top-k: k larger than the candidates; k == 0 is a no-op
     assert L.usaf_importance_topk(FAKE, 100, 101, None, 0, FAKE, None, FAKE, 1 << 20, None) == 1

@@ -634,7 +634,9 @@ def test_tiny_fp32_importance_then_three_steps(capi):
 # --------------------------------------------------------------------------
 # the pages' 4-bit storage, dequantised as the GEMMs load it
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("dims,group", [((200, 256, 8, 2, 128), 64), ((333, 512, 16, 4, 384), 128),
+# (1024, 256, 4, 2, 128): 512 slots per expert on average, the 256-row tiles
+@pytest.mark.parametrize("dims,group", [((200, 256, 8, 2, 128), 64), ((333, 512, 16, 4, 384), 64),
+                                        ((1024, 256, 4, 2, 128), 64),
                                         ((1024, 2048, 128, 8, 768), 128)])
 def test_forward_q4_equals_resident_dequant(capi, dims, group):
     """usaf_moe_forward_q4 on affine 4-bit codes against usaf_moe_forward on
