@@ -209,6 +209,8 @@ struct KMajor {
     }
   }
   static constexpr bool kPrep = false;  // nothing staged per tile
+  static constexpr bool kConvert = false;
+  __device__ __forceinline__ void convert(int, int) const {}
   // fragment rows base..base+31 (base a multiple of 32), k-substep kc
   __device__ __forceinline__ static bf16x8_t frag(const unsigned char* lds, int base, int kc, int lane,
                                                   int /*kt*/ = 0) {
@@ -251,6 +253,8 @@ struct MNMajor {
       *reinterpret_cast<uint4*>(lds + x * 16) = make_uint4(0, 0, 0, 0);
   }
   static constexpr bool kPrep = false;  // nothing staged per tile
+  static constexpr bool kConvert = false;
+  __device__ __forceinline__ void convert(int, int) const {}
   // fragment rows base..base+31 (the contiguous dimension), k-substep kc
   __device__ __forceinline__ static bf16x8_t frag(const unsigned char* lds, int base, int kc, int lane,
                                                   int /*kt*/ = 0) {
@@ -269,7 +273,8 @@ struct MNMajor {
 
 // A k-major operand of R rows held as affine 4-bit codes in groups of G = 2^gshift
 // along k (w = bf16(fp32(fp32(q - z) * s)), element 2i in the low nibble of
-// byte i), dequantised as its MFMA fragments are read.  The codes do not go
+// byte i), dequantised in LDS: by the whole block into a bf16 tile once per
+// stage (Convert), or by each wave as it reads its fragments.  The codes do not go
 // through the ring: they arrive by DMA in blocks of CB stages (a row's
 // 32 CB bytes at once, whole 64-byte lines rather than 16-byte pieces per
 // stage), into one of two LDS buffers by block parity, 16-byte chunks
@@ -285,10 +290,15 @@ struct MNMajor {
 // of 64, an even number kg >= 2 of groups per row (4-byte aligned pairs).
 // Src: code_row(r) -> global code row of tile row r (r < R, always valid);
 // q, s, z; qpitch (bytes per code row), kg (groups per row), gshift.
-template <int R, int NW, int CB>
+template <int R, int NW, int CB, bool Convert = false>
 struct KMajorQ4 {
   static constexpr int kBK = 64;
-  static constexpr int kFragReads = 3;
+  // Convert: each stage is dequantised once, by the whole block, into a bf16
+  // tile in KMajor's layout that every wave then reads; otherwise each wave
+  // dequantises the fragments it reads
+  static constexpr bool kConvert = Convert;
+  using Tile = KMajor<R, NW, 64>;
+  static constexpr int kFragReads = Convert ? 1 : 3;
   static constexpr bool kPrep = false;
   static constexpr int kCB = CB;
   static constexpr int kBytes = 0;                      // nothing in the ring
@@ -310,6 +320,48 @@ struct KMajorQ4 {
   __device__ __forceinline__ static unsigned char* scale_lds() {  // [parity][s, z][row][16 B]
     __shared__ __attribute__((aligned(16))) unsigned char buf[4 * kScaleBuf];
     return buf;
+  }
+  __device__ __forceinline__ static unsigned char* tile_lds() {  // the converted stage (Convert)
+    __shared__ __attribute__((aligned(16))) unsigned char buf[Convert ? R * 128 : 16];
+    return buf;
+  }
+  // 8 weights from 4 code bytes: w = bf16(fp32(fp32(q - z) * s)), the low
+  // and high nibbles of the four bytes each converted as a byte
+  __device__ __forceinline__ static uint4 dequant8(uint32_t code, float sc, float zr) {
+    const uint32_t lo = code & 0x0f0f0f0fu, hi = (code >> 4) & 0x0f0f0f0fu;
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float d0 = float((lo >> (8 * j)) & 0xffu) - zr;
+      const float d1 = float((hi >> (8 * j)) & 0xffu) - zr;
+      o[j] = f2bf2(d0 * sc, d1 * sc);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  __device__ __forceinline__ void scale_zero(int n, int kt, float& sc, float& zr) const {
+    const int g = kt >> gsh6;
+    const unsigned char* sb = scale_lds() + ((g >> 3) & 1) * 2 * kScaleBuf + n * 16 + 2 * (g & 7);
+    sc = float(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb)));
+    zr = float(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb + kScaleBuf)));
+  }
+  // Convert: stage kt's codes into the bf16 tile, 32 weights (16 code
+  // bytes) per thread and pass; the caller's barrier publishes the tile
+  __device__ __forceinline__ void convert(int kt, int tid) const {
+    if constexpr (Convert) {
+      for (int u = tid; u < 2 * R; u += 64 * NW) {
+        const int r = u >> 1, h = u & 1;  // row, half of the stage's 64 k
+        const int c = 2 * (kt % CB) + h;  // code chunk in the row's block
+        const uint4 q = *reinterpret_cast<const uint4*>(code_lds() + ((kt / CB) & 1) * kCodeBuf +
+                                                         r * kRowB + 16 * (c ^ sw(r)));
+        float sc, zr;
+        scale_zero(r, kt, sc, zr);
+        const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)  // bf16 chunk 4 h + j of the row (8 k)
+          *reinterpret_cast<uint4*>(tile_lds() + r * 128 + 16 * ((4 * h + j) ^ Tile::sw(r))) =
+              dequant8(qw[j], sc, zr);
+      }
+    }
   }
   // 16-byte chunk slot swizzle, as KMajor::sw for rows of kRowB bytes
   __device__ __forceinline__ static int sw(int r) { return (r / (256 / kRowB)) & (kChunks - 1); }
@@ -363,26 +415,16 @@ struct KMajorQ4 {
     }
   }
   __device__ __forceinline__ static void zero_tail(unsigned char*, int, int) {}
-  // fragment rows base..base+31, k-substep kc of stage kt: 8 dequantised weights
+  // fragment rows base..base+31, k-substep kc of stage kt: 8 bf16 weights
   __device__ __forceinline__ bf16x8_t frag(const unsigned char*, int base, int kc, int lane, int kt) const {
+    if constexpr (Convert) return Tile::frag(tile_lds(), base, kc, lane);
     const int n = base + (lane & 31);
     const int byte = 32 * (kt % CB) + 8 * kc + 4 * (lane >> 5);
     const uint32_t code = *reinterpret_cast<const uint32_t*>(
         code_lds() + ((kt / CB) & 1) * kCodeBuf + n * kRowB + 16 * ((byte >> 4) ^ sw(n)) + (byte & 15));
-    const int g = kt >> gsh6;
-    const unsigned char* sb = scale_lds() + ((g >> 3) & 1) * 2 * kScaleBuf + n * 16 + 2 * (g & 7);
-    const float sc = float(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb)));
-    const float zr = float(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb + kScaleBuf)));
-    // the low and high nibbles of the four bytes, each converted as a byte
-    const uint32_t lo = code & 0x0f0f0f0fu, hi = (code >> 4) & 0x0f0f0f0fu;
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float d0 = float((lo >> (8 * j)) & 0xffu) - zr;
-      const float d1 = float((hi >> (8 * j)) & 0xffu) - zr;
-      o[j] = f2bf2(d0 * sc, d1 * sc);
-    }
-    return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+    float sc, zr;
+    scale_zero(n, kt, sc, zr);
+    return __builtin_bit_cast(bf16x8_t, dequant8(code, sc, zr));
   }
 };
 
@@ -529,6 +571,13 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
       ao.issue(as, kt + NS - 1, nxt, w, lane);
       bo.issue(bs, kt + NS - 1, nxt + A_BYTES, w, lane);
     }
+    if constexpr (BOp::kConvert) {
+      // the previous stage's last substep first (its fragments are in
+      // registers), then the block converts this stage's weight tile
+      if constexpr (!kFirst && VB > 0) mfmas(pa, pb);
+      bo.convert(kt, tid);
+      __syncthreads();
+    }
     if constexpr (VB > 0) {
       const unsigned char* As = cur;
       const unsigned char* Bs = cur + A_BYTES;
@@ -538,7 +587,7 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
       for (int i = 0; i < VB; ++i) af[0][i] = AOp::frag(As, r0 + 32 * i, 0, lane);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bfr[0][j] = bo.frag(Bs, wn * CW + 32 * j, 0, lane, kt);
-      if constexpr (!kFirst) {
+      if constexpr (!kFirst && !BOp::kConvert) {
         mfmas(pa, pb);  // the previous stage's last substep
         interleave_mfma_reads<NM, NR>();
       }
