@@ -174,39 +174,60 @@ struct StageRegs {
   float w[kSlots];
 };
 
+// The loads of a chunk are issued without branches: a slot past the
+// window's end reloads the window's last slot (zeroed when stored), so every
+// thread issues exactly kSlots loads per chunk and the compiler's waits
+// before a store need only cover the oldest chunk in flight.
 template <bool kDown>
 __device__ __forceinline__ void stage_fetch(const MaskedArgs& A, int b, int nblk_r, int p0,
                                             int pend, int slot0, int r_lo, int c0,
                                             const int* tok_tab, const float* w_tab,
                                             StageRegs& sr) {
-  // p0 indexes the token table window; slot0 + p is the expert-major slot row
+  // p0 (a multiple of 8) indexes the token table window, whose entries are
+  // valid up to pend rounded up to 8; slot0 + p is the expert-major slot row
   const bool isR = b < nblk_r;
   const int j0 = (isR ? b : b - nblk_r) * 8;
+  // the chunk's 8 tokens (and down's weights) in two 16-byte LDS reads each
+  const int4 ta = *reinterpret_cast<const int4*>(tok_tab + p0);
+  const int4 tb = *reinterpret_cast<const int4*>(tok_tab + p0 + 4);
+  const int tok[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+  if constexpr (kDown) {
+    const float4 wa = *reinterpret_cast<const float4*>(w_tab + p0);
+    const float4 wb = *reinterpret_cast<const float4*>(w_tab + p0 + 4);
+    const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+    for (int t = 0; t < kSlots; ++t) sr.w[t] = isR ? 0.f : wv[t];
+  } else {
+#pragma unroll
+    for (int t = 0; t < kSlots; ++t) sr.w[t] = 0.f;
+  }
+  // column operand (isR): gate_up X by token, down a by slot; row operand:
+  // gate_up dGU by slot, down dY by token
+  const bf16_t* base = isR ? A.Rm + c0 + j0 : A.L + r_lo + j0;
+  const int64_t ld = isR ? A.C : A.R;
+  const bool by_tok = isR != kDown;
 #pragma unroll
   for (int t = 0; t < kSlots; ++t) {
-    const int p = p0 + t;
-    sr.v[t] = make_uint4(0, 0, 0, 0);
-    sr.w[t] = 0.f;
-    if (p < pend) {
-      const bf16_t* src;
-      if (isR) {
-        src = kDown ? A.Rm + int64_t(slot0 + p) * A.C + c0
-                    : A.Rm + int64_t(tok_tab[p]) * A.C + c0;
-      } else {
-        src = kDown ? A.L + int64_t(tok_tab[p]) * A.R + r_lo
-                    : A.L + int64_t(slot0 + p) * A.R + r_lo;
-        if (kDown) sr.w[t] = w_tab[p];
-      }
-      sr.v[t] = *reinterpret_cast<const uint4*>(src + j0);
-    }
+    const int p = min(p0 + t, pend - 1);
+    const int64_t row = by_tok ? int64_t(tok[t]) : int64_t(slot0 + p);
+    sr.v[t] = *reinterpret_cast<const uint4*>(base + row * ld);
   }
 }
 
 template <bool kDown>
-__device__ __forceinline__ void stage_store(int b, int nblk_r, const StageRegs& sr,
+__device__ __forceinline__ void stage_store(int b, int nblk_r, StageRegs sr, int p0, int pend,
                                             unsigned char* lds_l, unsigned char* lds_r) {
   const bool isR = b < nblk_r;
   const int j0 = (isR ? b : b - nblk_r) * 8;
+  // slots past the window are zeroed by masks, not branches: a branch that
+  // overwrote the registers of a load in flight would make the compiler
+  // wait for every load before the store
+#pragma unroll
+  for (int t = 0; t < kSlots; ++t) {
+    const uint32_t m = p0 + t < pend ? 0xffffffffu : 0u;
+    sr.v[t] = make_uint4(sr.v[t].x & m, sr.v[t].y & m, sr.v[t].z & m, sr.v[t].w & m);
+    sr.w[t] = __uint_as_float(__float_as_uint(sr.w[t]) & m);
+  }
   uint4 out[8];
   if (isR || !kDown) {
     transpose8x8(sr.v, out);
@@ -432,8 +453,8 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
   __shared__ __attribute__((aligned(16))) unsigned char lds_r[2][kRsBytes];
   __shared__ int rowpre[kMaxRows<kDown> + 1];
   __shared__ uint32_t rstart[kMaxRows<kDown>];
-  __shared__ int tok_tab[kTokTab<kDown>];
-  __shared__ float w_tab[kDown ? kTokTab<kDown> : 1];
+  __shared__ __attribute__((aligned(16))) int tok_tab[kTokTab<kDown>];
+  __shared__ __attribute__((aligned(16))) float w_tab[kDown ? kTokTab<kDown> : 4];
 
   constexpr int kE = kEnt<kDown>;
   const int tid = threadIdx.x;
@@ -625,7 +646,9 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
       });
     };
     // stream the expert's slots, a token-table window at a time
-    const bool stager = tid < nblk_r + nblk_l;  // one staging block per thread
+    const int nblk = nblk_r + nblk_l;
+    const bool stager = tid < nblk;  // one staging block per thread
+    const int bf = min(tid, nblk - 1);  // block whose loads this thread issues (stagers: its own)
     for (int w0 = 0; w0 < ne; w0 += kTokTab<kDown>) {
       const int wn = min(kTokTab<kDown>, ne - w0);
       __syncthreads();  // previous window's tables and buffers consumed
@@ -634,39 +657,43 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
         tok_tab[p] = sid / A.K;
         if (kDown) w_tab[p] = A.topk_w[sid];
       }
+      if (tid < kSlots && wn + tid < ((wn + kSlots - 1) & ~(kSlots - 1))) {
+        tok_tab[wn + tid] = 0;  // a valid row for the loads of a window's last partial chunk
+        if (kDown) w_tab[wn + tid] = 0.f;
+      }
       __syncthreads();
       const int nch = (wn + kSlots - 1) / kSlots;
-      // chunk c is multiplied from buffer c & 1.  The staging threads hold
-      // the loads of kPre chunks in registers (chunk m in set m % kPre):
-      // while chunk c is multiplied they write chunk c+1 into the other
-      // buffer and reuse its registers to load chunk c+1+kPre, so every
-      // load has kPre chunk steps to arrive
+      // chunk c is multiplied from buffer c & 1.  Every thread holds the
+      // loads of kPre chunks in registers (chunk m in set m % kPre): while
+      // chunk c is multiplied the staging threads write chunk c+1 into the
+      // other buffer, and every thread reuses its registers to load chunk
+      // c+1+kPre, so every load has kPre chunk steps to arrive.  Loads are
+      // unconditional (chunks past the last reload it; threads beyond the
+      // staging blocks load the last block's data and store nothing), and
+      // the chunk loop runs a whole number of kPre steps (the steps past
+      // the last chunk store zeros no product reads and multiply nothing),
+      // so the waits before a store count exactly the chunks in flight.
       constexpr int kP = kPre<kDown>;
       StageRegs sr[kP];
-      if (stager) {
-        stage_fetch<kDown>(A, tid, nblk_r, 0, wn, off + w0, r_al, c0, tok_tab, w_tab, sr[0]);
-        stage_store<kDown>(tid, nblk_r, sr[0], lds_l[0], lds_r[0]);
-        static_for<kP>([&](auto J) {
-          constexpr int m = decltype(J)::value + 1;
-          if (m < nch)
-            stage_fetch<kDown>(A, tid, nblk_r, m * kSlots, wn, off + w0, r_al, c0, tok_tab, w_tab,
-                               sr[m % kP]);
-        });
-      }
+      stage_fetch<kDown>(A, bf, nblk_r, 0, wn, off + w0, r_al, c0, tok_tab, w_tab, sr[0]);
+      if (stager) stage_store<kDown>(tid, nblk_r, sr[0], 0, wn, lds_l[0], lds_r[0]);
+      static_for<kP>([&](auto J) {
+        constexpr int m = decltype(J)::value + 1;
+        stage_fetch<kDown>(A, bf, nblk_r, min(m, nch - 1) * kSlots, wn, off + w0, r_al, c0,
+                           tok_tab, w_tab, sr[m % kP]);
+      });
       for (int cb = 0; cb < nch; cb += kP) {
         static_for<kP>([&](auto J) {
           constexpr int j = decltype(J)::value;
           constexpr int s = (j + 1) % kP;  // set of chunk c + 1 (cb is a multiple of kP)
           const int c = cb + j;
-          if (c >= nch) return;  // uniform
           __syncthreads();  // buffer c & 1 written; buffer (c+1) & 1 no longer read
-          if (stager && c + 1 < nch) {
-            stage_store<kDown>(tid, nblk_r, sr[s], lds_l[(c + 1) & 1], lds_r[(c + 1) & 1]);
-            if (c + 1 + kP < nch)
-              stage_fetch<kDown>(A, tid, nblk_r, (c + 1 + kP) * kSlots, wn, off + w0, r_al, c0,
-                                 tok_tab, w_tab, sr[s]);
-          }
-          compute(lds_l[c & 1], lds_r[c & 1]);
+          if (stager)
+            stage_store<kDown>(tid, nblk_r, sr[s], (c + 1) * kSlots, wn, lds_l[(c + 1) & 1],
+                               lds_r[(c + 1) & 1]);
+          stage_fetch<kDown>(A, bf, nblk_r, min(c + 1 + kP, nch - 1) * kSlots, wn, off + w0, r_al,
+                             c0, tok_tab, w_tab, sr[s]);
+          if (c < nch) compute(lds_l[c & 1], lds_r[c & 1]);  // uniform
         });
       }
     }
