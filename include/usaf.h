@@ -196,7 +196,9 @@ USAF_API usaf_status usaf_masked_plan(const usaf_moe_shape *shape, const uint32_
  * is NaN/Inf (sparse mode); the caller zeroes it before the step.
  * An empty list (nnz == 0, idx may be NULL) computes everything but dW.
  * ws: USAF_WS_BACKWARD bytes.  Errors: INVALID_ARG for nnz < 0, nnz > N, a
- * null required pointer, or idx == NULL with 0 < nnz < N. */
+ * null required pointer, or idx == NULL with 0 < nnz < N; UNSUPPORTED for a
+ * sparse list on a bf16 layer whose X (T*H*2 bytes) or expert-major dgu
+ * (T*K*2I*2 bytes) reaches 4 GiB, or with T*K >= 2^24. */
 USAF_API usaf_status usaf_masked_backward(const usaf_moe_shape *shape, const void *X, const float *Wr,
                                  const void *Wflat, const usaf_moe_state *state,
                                  const void *dY, const uint32_t *idx, int64_t nnz,

@@ -54,11 +54,14 @@ template <bool kDown>
 constexpr int kMaxRows = kDown ? 2048 : 1536;
 template <bool kDown>
 constexpr int kLsBytes = (kMaxRows<kDown> + 8) * kSlots * 2;
-// row limit for CB columns: LDS and one staging block per thread
-// ((CB + RB + 16) / 8 <= kThreads, rows staged from r_lo rounded down to 8)
+// row limit for CB columns: LDS and one staging block per thread.  The
+// column operand's CB / 8 blocks take whole waves, the row operand's blocks
+// (rows staged from r_lo rounded down to 8, at most (RB + 14) / 8 of them)
+// the threads after them.
 template <bool kDown>
 constexpr int row_limit(int CB) {
-  const int by_threads = (8 * kThreads - 16 - CB) & ~7;
+  const int col_threads = 64 * ((CB / 8 + 63) / 64);
+  const int by_threads = (8 * (kThreads - col_threads) - 16) & ~7;
   return kMaxRows<kDown> < by_threads ? kMaxRows<kDown> : by_threads;
 }
 static_assert(row_limit<false>(kMaxCB) >= 8 && row_limit<true>(kMaxCB) >= 8, "rows per tile");
@@ -174,62 +177,67 @@ struct StageRegs {
   float w[kSlots];
 };
 
+// Staging roles.  The waves [0, ncw) stage the column operand (lane b: the
+// block of columns 8b..8b+7 of the tile), the waves after them the row
+// operand (rows from r_lo rounded down to 8); lanes past their operand's
+// blocks load its last block again and store nothing.  An operand's rows are
+// tokens (gate_up X, down dY) or the expert's slots (gate_up dGU, down a), so
+// within a wave the base pointer and the row pitch are uniform and each
+// lane's load is that base plus a 32-bit offset.
+struct StageRole {
+  const unsigned char* base;  // wave-uniform: the operand's first element of the tile
+  uint32_t ld2;               // wave-uniform: bytes per operand row
+  bool col;                   // wave-uniform: the column operand
+  bool by_tok;                // wave-uniform: operand rows are tokens
+  bool stores;                // the lane's block lies in the tile
+  uint32_t lane_off;          // bytes from base to the lane's block
+  uint32_t unit;              // the block's first 16-byte LDS unit
+};
+
 // The loads of a chunk are issued without branches: a slot past the
-// window's end reloads the window's last slot (zeroed when stored), so every
-// thread issues exactly kSlots loads per chunk and the compiler's waits
-// before a store need only cover the oldest chunk in flight.
+// window's end reloads a valid row (the row tables are padded to a whole
+// chunk; such slots are zeroed when stored), so every thread issues exactly
+// kSlots loads per chunk and the waits before a store need only cover the
+// oldest chunk in flight.
 template <bool kDown>
-__device__ __forceinline__ void stage_fetch(const MaskedArgs& A, int b, int nblk_r, int p0,
-                                            int pend, int slot0, int r_lo, int c0,
-                                            const int* tok_tab, const float* w_tab,
+__device__ __forceinline__ void stage_fetch(const StageRole& R, int p0, const int* tok_tab,
+                                            const int* slot_tab, const float* w_tab,
                                             StageRegs& sr) {
-  // p0 (a multiple of 8) indexes the token table window, whose entries are
-  // valid up to pend rounded up to 8; slot0 + p is the expert-major slot row
-  const bool isR = b < nblk_r;
-  const int j0 = (isR ? b : b - nblk_r) * 8;
-  // the chunk's 8 tokens (and down's weights) in two 16-byte LDS reads each
-  const int4 ta = *reinterpret_cast<const int4*>(tok_tab + p0);
-  const int4 tb = *reinterpret_cast<const int4*>(tok_tab + p0 + 4);
-  const int tok[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+  // p0 (a multiple of 8) indexes the window's tables
   if constexpr (kDown) {
-    const float4 wa = *reinterpret_cast<const float4*>(w_tab + p0);
-    const float4 wb = *reinterpret_cast<const float4*>(w_tab + p0 + 4);
-    const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-#pragma unroll
-    for (int t = 0; t < kSlots; ++t) sr.w[t] = isR ? 0.f : wv[t];
-  } else {
-#pragma unroll
-    for (int t = 0; t < kSlots; ++t) sr.w[t] = 0.f;
+    if (!R.col) {  // dY rows are scaled by the slots' routing weights when stored
+      const float4 wa = *reinterpret_cast<const float4*>(w_tab + p0);
+      const float4 wb = *reinterpret_cast<const float4*>(w_tab + p0 + 4);
+      sr.w[0] = wa.x; sr.w[1] = wa.y; sr.w[2] = wa.z; sr.w[3] = wa.w;
+      sr.w[4] = wb.x; sr.w[5] = wb.y; sr.w[6] = wb.z; sr.w[7] = wb.w;
+    }
   }
-  // column operand (isR): gate_up X by token, down a by slot; row operand:
-  // gate_up dGU by slot, down dY by token
-  const bf16_t* base = isR ? A.Rm + c0 + j0 : A.L + r_lo + j0;
-  const int64_t ld = isR ? A.C : A.R;
-  const bool by_tok = isR != kDown;
+  // the chunk's 8 operand rows: tokens, or slots from slot0 (the row
+  // table of the wave's operand; two 16-byte LDS reads), then 8 loads from
+  // the wave-uniform base at 32-bit offsets
+  const int* rt = R.by_tok ? tok_tab : slot_tab;
+  const int4 ta = *reinterpret_cast<const int4*>(rt + p0);
+  const int4 tb = *reinterpret_cast<const int4*>(rt + p0 + 4);
+  const int row[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
 #pragma unroll
-  for (int t = 0; t < kSlots; ++t) {
-    const int p = min(p0 + t, pend - 1);
-    const int64_t row = by_tok ? int64_t(tok[t]) : int64_t(slot0 + p);
-    sr.v[t] = *reinterpret_cast<const uint4*>(base + row * ld);
-  }
+  for (int t = 0; t < kSlots; ++t)
+    sr.v[t] = *reinterpret_cast<const uint4*>(R.base + (__umul24(uint32_t(row[t]), R.ld2) + R.lane_off));
 }
 
 template <bool kDown>
-__device__ __forceinline__ void stage_store(int b, int nblk_r, StageRegs sr, int p0, int pend,
+__device__ __forceinline__ void stage_store(const StageRole& R, StageRegs sr, int p0, int pend,
                                             unsigned char* lds_l, unsigned char* lds_r) {
-  const bool isR = b < nblk_r;
-  const int j0 = (isR ? b : b - nblk_r) * 8;
-  // slots past the window are zeroed by masks, not branches: a branch that
-  // overwrote the registers of a load in flight would make the compiler
-  // wait for every load before the store
+  if (p0 + kSlots > pend) {  // uniform: the window's last chunk, its slots past the end zeroed
+    asm volatile("");  // kept a branch: the other chunks skip the masking
 #pragma unroll
-  for (int t = 0; t < kSlots; ++t) {
-    const uint32_t m = p0 + t < pend ? 0xffffffffu : 0u;
-    sr.v[t] = make_uint4(sr.v[t].x & m, sr.v[t].y & m, sr.v[t].z & m, sr.v[t].w & m);
-    sr.w[t] = __uint_as_float(__float_as_uint(sr.w[t]) & m);
+    for (int t = 0; t < kSlots; ++t) {
+      const uint32_t m = p0 + t < pend ? 0xffffffffu : 0u;
+      sr.v[t] = make_uint4(sr.v[t].x & m, sr.v[t].y & m, sr.v[t].z & m, sr.v[t].w & m);
+      sr.w[t] = __uint_as_float(__float_as_uint(sr.w[t]) & m);
+    }
   }
   uint4 out[8];
-  if (isR || !kDown) {
+  if (!kDown || R.col) {
     transpose8x8(sr.v, out);
   } else {
     // down: bf16(w_p * dY) for the 8 slots of each element, slots 2d and
@@ -247,10 +255,10 @@ __device__ __forceinline__ void stage_store(int b, int nblk_r, StageRegs sr, int
       out[j] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
-  unsigned char* dst = isR ? lds_r : lds_l;
+  unsigned char* dst = R.col ? lds_r : lds_l;
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    *reinterpret_cast<uint4*>(dst + size_t(sw16(uint32_t(j0 + j))) * 16) = out[j];
+    *reinterpret_cast<uint4*>(dst + size_t(sw16(R.unit + uint32_t(j))) * 16) = out[j];
 }
 
 // Entries of each group g = (expert e, column tile ct) of one tensor, one
@@ -454,6 +462,7 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
   __shared__ int rowpre[kMaxRows<kDown> + 1];
   __shared__ uint32_t rstart[kMaxRows<kDown>];
   __shared__ __attribute__((aligned(16))) int tok_tab[kTokTab<kDown>];
+  __shared__ __attribute__((aligned(16))) int slot_tab[kTokTab<kDown>];
   __shared__ __attribute__((aligned(16))) float w_tab[kDown ? kTokTab<kDown> : 4];
 
   constexpr int kE = kEnt<kDown>;
@@ -646,19 +655,38 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
       });
     };
     // stream the expert's slots, a token-table window at a time
-    const int nblk = nblk_r + nblk_l;
-    const bool stager = tid < nblk;  // one staging block per thread
-    const int bf = min(tid, nblk - 1);  // block whose loads this thread issues (stagers: its own)
+    StageRole role;
+    {
+      const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+      const int ncw = (nblk_r + 63) >> 6;
+      role.col = wv < ncw;
+      const int nb = role.col ? nblk_r : nblk_l;
+      const int b = role.col ? tid : tid - 64 * ncw;
+      role.stores = b < nb;
+      const int bc = min(b, nb - 1);
+      role.ld2 = 2u * uint32_t(role.col ? A.C : A.R);
+      role.by_tok = role.col != kDown;
+      // operand rows by slot start at the expert's first slot
+      const unsigned char* b0 = role.col ? reinterpret_cast<const unsigned char*>(A.Rm + c0)
+                                         : reinterpret_cast<const unsigned char*>(A.L + r_al);
+      role.base = role.by_tok ? b0 : b0 + int64_t(off) * role.ld2;
+      role.lane_off = 16u * uint32_t(bc);
+      role.unit = 8u * uint32_t(bc);
+    }
     for (int w0 = 0; w0 < ne; w0 += kTokTab<kDown>) {
       const int wn = min(kTokTab<kDown>, ne - w0);
       __syncthreads();  // previous window's tables and buffers consumed
+      // row tables: the slot's token, and its slot row (from the window's
+      // first), padded to a whole chunk with valid rows
       for (int p = tid; p < wn; p += kThreads) {
         const int sid = A.perm[off + w0 + p];
         tok_tab[p] = sid / A.K;
+        slot_tab[p] = w0 + p;
         if (kDown) w_tab[p] = A.topk_w[sid];
       }
       if (tid < kSlots && wn + tid < ((wn + kSlots - 1) & ~(kSlots - 1))) {
-        tok_tab[wn + tid] = 0;  // a valid row for the loads of a window's last partial chunk
+        tok_tab[wn + tid] = 0;
+        slot_tab[wn + tid] = w0 + wn - 1;
         if (kDown) w_tab[wn + tid] = 0.f;
       }
       __syncthreads();
@@ -668,19 +696,17 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
       // chunk c is multiplied the staging threads write chunk c+1 into the
       // other buffer, and every thread reuses its registers to load chunk
       // c+1+kPre, so every load has kPre chunk steps to arrive.  Loads are
-      // unconditional (chunks past the last reload it; threads beyond the
-      // staging blocks load the last block's data and store nothing), and
-      // the chunk loop runs a whole number of kPre steps (the steps past
-      // the last chunk store zeros no product reads and multiply nothing),
-      // so the waits before a store count exactly the chunks in flight.
+      // unconditional (chunks past the last reload it), and the chunk loop
+      // runs a whole number of kPre steps (the steps past the last chunk
+      // store what no product reads and multiply nothing), so the waits
+      // before a store count exactly the chunks in flight.
       constexpr int kP = kPre<kDown>;
       StageRegs sr[kP];
-      stage_fetch<kDown>(A, bf, nblk_r, 0, wn, off + w0, r_al, c0, tok_tab, w_tab, sr[0]);
-      if (stager) stage_store<kDown>(tid, nblk_r, sr[0], 0, wn, lds_l[0], lds_r[0]);
+      stage_fetch<kDown>(role, 0, tok_tab, slot_tab, w_tab, sr[0]);
+      if (role.stores) stage_store<kDown>(role, sr[0], 0, wn, lds_l[0], lds_r[0]);
       static_for<kP>([&](auto J) {
         constexpr int m = decltype(J)::value + 1;
-        stage_fetch<kDown>(A, bf, nblk_r, min(m, nch - 1) * kSlots, wn, off + w0, r_al, c0,
-                           tok_tab, w_tab, sr[m % kP]);
+        stage_fetch<kDown>(role, min(m, nch - 1) * kSlots, tok_tab, slot_tab, w_tab, sr[m % kP]);
       });
       for (int cb = 0; cb < nch; cb += kP) {
         static_for<kP>([&](auto J) {
@@ -688,11 +714,11 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
           constexpr int s = (j + 1) % kP;  // set of chunk c + 1 (cb is a multiple of kP)
           const int c = cb + j;
           __syncthreads();  // buffer c & 1 written; buffer (c+1) & 1 no longer read
-          if (stager)
-            stage_store<kDown>(tid, nblk_r, sr[s], (c + 1) * kSlots, wn, lds_l[(c + 1) & 1],
+          if (role.stores)
+            stage_store<kDown>(role, sr[s], (c + 1) * kSlots, wn, lds_l[(c + 1) & 1],
                                lds_r[(c + 1) & 1]);
-          stage_fetch<kDown>(A, bf, nblk_r, min(c + 1 + kP, nch - 1) * kSlots, wn, off + w0, r_al,
-                             c0, tok_tab, w_tab, sr[s]);
+          stage_fetch<kDown>(role, min(c + 1 + kP, nch - 1) * kSlots, tok_tab, slot_tab, w_tab,
+                             sr[s]);
           if (c < nch) compute(lds_l[c & 1], lds_r[c & 1]);  // uniform
         });
       }
@@ -770,6 +796,16 @@ static PlanLayout plan_layout(const usaf_moe_shape& s, int64_t nnz) {
 
 int64_t masked_plan_bytes(const usaf_moe_shape& s) { return int64_t(plan_layout(s, 1).total); }
 
+// The gradient kernels address an operand row by a 24-bit row index times
+// the row pitch, as a 32-bit byte offset from the tile's base (token rows
+// from the tensor's start, slot rows from the expert's first slot): the
+// token-row tensors (X, dY: T x H) and the slot-row tensors (dGU: S x 2I)
+// must stay below 4 GiB, and T, S below 2^24.
+bool masked_dw_fits(const usaf_moe_shape& s) {
+  const int64_t S = int64_t(s.T) * s.K, lim = int64_t(1) << 32;
+  return S < (int64_t(1) << 24) && int64_t(s.T) * s.H * 2 < lim && S * 2 * s.I * 2 < lim;
+}
+
 // The plan of a list: segment starts, then each tensor's tiles.  Depends on
 // idx and the shape only, so one plan serves every step until the list
 // changes.
@@ -814,6 +850,7 @@ usaf_status masked_dw_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64_t
                            float* dW, int32_t* nonfinite, const void* plan, void* ws_plan,
                            hipStream_t st) {
   if (nnz == 0) return USAF_OK;
+  if (!masked_dw_fits(s)) return USAF_ERR_UNSUPPORTED;
   const PlanLayout P = plan_layout(s, nnz);
   if (P.b0 >= (int64_t(1) << 31) || P.b1 >= (int64_t(1) << 31)) return USAF_ERR_UNSUPPORTED;
   timer_begin(USAF_K_MASKED_DW, st);

@@ -1274,6 +1274,8 @@ extern "C" usaf_status usaf_masked_backward(const usaf_moe_shape* shape, const v
   if (!idx && nnz != N && nnz != 0) return USAF_ERR_INVALID_ARG;
   if (nnz > 0 && !dW) return USAF_ERR_INVALID_ARG;
   if (!ws || ws_bytes < ws_backward(*shape).total) return USAF_ERR_WORKSPACE;
+  if (shape->act == USAF_BF16 && idx && nnz > 0 && !masked_dw_fits(*shape))
+    return USAF_ERR_UNSUPPORTED;
   if (shape->act == USAF_BF16)
     return backward_impl<bf16_t>(*shape, static_cast<const bf16_t*>(X), Wr,
                                  static_cast<const bf16_t*>(Wflat), *state,

@@ -12,6 +12,7 @@ namespace usaf {
 
 // Bytes of a masked-gradient plan (segment starts and tile lists).
 int64_t masked_plan_bytes(const usaf_moe_shape& s);
+bool masked_dw_fits(const usaf_moe_shape& s);  // sizes the masked gradient kernels address
 // Compute units of the current device (cached per device).
 int device_cus();
 // The loss kernels of usaf_mse_grad with their partial sums in `part`

@@ -89,6 +89,11 @@ def test_entry_points_refuse_bad_arguments_before_launch():
                                   None, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == 1
     assert L.usaf_masked_backward(C.byref(sh), FAKE, FAKE, FAKE, C.byref(bad_state), FAKE, FAKE, 5,
                                   None, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == 1
+    # a sparse list on a bf16 layer whose X reaches 4 GiB (T*H*2 = 2^32 bytes):
+    # the masked gradient addresses operand rows by 32-bit offsets
+    big = capi.Shape(1 << 20, 2048, 8, 2, 32, 1)
+    assert L.usaf_masked_backward(C.byref(big), FAKE, FAKE, FAKE, C.byref(st), FAKE, FAKE, 5,
+                                  None, FAKE, FAKE, None, None, FAKE, 1 << 62, None) == 2
     # masked plan: nnz range, a list pointer, the plan's size (bf16 layers)
     shb = capi.Shape(128, 64, 8, 2, 32, 1)
     need = capi.workspace_size(capi.WS_MASKED_PLAN, shb)
