@@ -68,7 +68,7 @@ struct KeyDropBf16 {
   const bf16_t* W;
   const uint32_t* idx;
   __device__ __forceinline__ bool operator()(int64_t i, uint32_t& key) const {
-    key = (0x7fffu - (uint32_t(W[idx[i]]) & 0x7fffu)) << 16;
+    key = (0x7fffu - (uint32_t(W[idx ? idx[i] : i]) & 0x7fffu)) << 16;
     return true;
   }
 };
@@ -76,7 +76,7 @@ struct KeyDropF32 {
   const float* W;
   const uint32_t* idx;
   __device__ __forceinline__ bool operator()(int64_t i, uint32_t& key) const {
-    key = 0x7fffffffu - (__float_as_uint(W[idx[i]]) & 0x7fffffffu);
+    key = 0x7fffffffu - (__float_as_uint(W[idx ? idx[i] : i]) & 0x7fffffffu);
     return true;
   }
 };
@@ -658,6 +658,7 @@ __global__ __launch_bounds__(1024) void scan_u32_kernel(uint32_t* __restrict__ a
 __global__ __launch_bounds__(256) void topk_pass_c_kernel(TopkWs w, uint32_t* __restrict__ out_idx,
                                                           float* __restrict__ out_val,
                                                           const float* __restrict__ valsrc,
+                                                          uint32_t* __restrict__ out_key,
                                                           const uint32_t* gate) {
   if (gated_off(gate)) return;
   __shared__ uint64_t mask[4][kChunk / 64];
@@ -695,6 +696,7 @@ __global__ __launch_bounds__(256) void topk_pass_c_kernel(TopkWs w, uint32_t* __
     const uint32_t i = base + uint32_t(lane) * 64u + uint32_t(b);
     out_idx[p] = i;
     if (out_val) out_val[p] = valsrc[i];
+    if (out_key) out_key[p] = __float_as_uint(valsrc[i]) & 0x7fffffffu;
     ++p;
   }
 }
@@ -714,7 +716,8 @@ static void scan_launch(uint32_t* a, int64_t n, uint32_t* bsum, const uint32_t* 
 // counts, their scan and the ordered output.
 template <class KF>
 static void topk_finish(KF key, const TopkWs& w, uint32_t* out_idx, float* out_val,
-                        const float* valsrc, hipStream_t st, const uint32_t* gate) {
+                        const float* valsrc, uint32_t* out_key, hipStream_t st,
+                        const uint32_t* gate) {
   const dim3 blk{256, 1, 1};
   const unsigned cgrid = 1024;
   const int shifts[5] = {41, 30, 19, 8, 0}, widths[5] = {11, 11, 11, 11, 8};
@@ -726,7 +729,7 @@ static void topk_finish(KF key, const TopkWs& w, uint32_t* out_idx, float* out_v
   hipLaunchKernelGGL(topk_cand_count_kernel<KF>, dim3(cgrid), blk, 0, st, key, w, gate);
   scan_launch(w.cnt, w.nchunks, w.bsum, gate, nullptr, st);
   hipLaunchKernelGGL(topk_pass_c_kernel, dim3(unsigned(ceil_div(w.nchunks, 4))), blk, 0, st, w,
-                     out_idx, out_val, valsrc, gate);
+                     out_idx, out_val, valsrc, out_key, gate);
 }
 
 template <class KF>
@@ -1012,7 +1015,8 @@ __global__ __launch_bounds__(256) void topk_cc_count_kernel(TopkWs w) {
 // order (16 consecutive candidates per thread).
 __global__ __launch_bounds__(256) void topk_cc_emit_kernel(TopkWs w, uint32_t* __restrict__ out_idx,
                                                            float* __restrict__ out_val,
-                                                           const float* __restrict__ valsrc) {
+                                                           const float* __restrict__ valsrc,
+                                                           uint32_t* __restrict__ out_key) {
   const uint64_t theta = (uint64_t(w.st[ST_PHI]) << 32) | w.st[ST_PLO];
   const int64_t m = w.st[ST_NCAND];
   __shared__ uint32_t wcnt[kEmitSeg / 256][4];
@@ -1023,12 +1027,13 @@ __global__ __launch_bounds__(256) void topk_cc_emit_kernel(TopkWs w, uint32_t* _
     // index order, so ballot ranks within a row give the output order
     const int64_t j0 = sg * kEmitSeg;
     bool sel[kEmitSeg / 256];
-    uint32_t idx[kEmitSeg / 256], lp[kEmitSeg / 256];
+    uint32_t idx[kEmitSeg / 256], ck[kEmitSeg / 256], lp[kEmitSeg / 256];
 #pragma unroll
     for (int u = 0; u < kEmitSeg / 256; ++u) {
       const int64_t j = j0 + u * 256 + threadIdx.x;
       idx[u] = j < m ? w.above[j] : 0u;
-      sel[u] = j < m && composite(w.cckey[j], idx[u]) >= theta;
+      ck[u] = j < m ? w.cckey[j] : 0u;
+      sel[u] = j < m && composite(ck[u], idx[u]) >= theta;
       const uint64_t b = __ballot(sel[u]);
       lp[u] = uint32_t(__popcll(b & below));
       if (lane == 0) wcnt[u][wid] = uint32_t(__popcll(b));
@@ -1043,6 +1048,7 @@ __global__ __launch_bounds__(256) void topk_cc_emit_kernel(TopkWs w, uint32_t* _
         const uint32_t p = run + before + lp[u];
         out_idx[p] = idx[u];
         if (out_val) out_val[p] = valsrc[idx[u]];
+        if (out_key) out_key[p] = ck[u];
       }
       run += (wcnt[u][0] + wcnt[u][1]) + (wcnt[u][2] + wcnt[u][3]);
     }
@@ -1051,17 +1057,21 @@ __global__ __launch_bounds__(256) void topk_cc_emit_kernel(TopkWs w, uint32_t* _
 }
 
 static usaf_status topk_run_sampled(const float* g, int64_t n, int64_t k, uint32_t* out_idx,
-                                    float* out_val, char* ws, hipStream_t st);
+                                    float* out_val, uint32_t* out_key, char* ws, hipStream_t st);
 
 // Enqueue one selection: the k eligible elements ranked first by (key desc,
 // index asc) among n (minus the excluded), written ascending to out_idx.
+// out_key (nullable; gradient keys only) receives each selected entry's key,
+// |g| as bits, aligned with out_idx.
 template <class KF>
 usaf_status topk_run(KF key, int64_t n, int64_t k, const uint32_t* ex, int64_t nex,
                      uint32_t* out_idx, float* out_val, const float* valsrc, char* ws,
-                     hipStream_t st, const uint32_t* gate = nullptr) {
+                     hipStream_t st, const uint32_t* gate = nullptr, uint32_t* out_key = nullptr) {
   if (k == 0 || n == 0) return USAF_OK;
+  if (out_key && !std::is_same<KF, KeyGrad>::value) return USAF_ERR_UNSUPPORTED;
+  if (out_key && !valsrc) valsrc = valsrc_of(key);
   if (!ex && !gate && n >= kSampledMin && std::is_same<KF, KeyGrad>::value)
-    return topk_run_sampled(valsrc_of(key), n, k, out_idx, out_val, ws, st);
+    return topk_run_sampled(valsrc_of(key), n, k, out_idx, out_val, out_key, ws, st);
   const int64_t ntiles = ceil_div(n, kTopkTile);
   const TopkWs w = topk_ws(ws, n);
   const dim3 blk{256, 1, 1}, grid{unsigned(ntiles), 1, 1};
@@ -1070,7 +1080,7 @@ usaf_status topk_run(KF key, int64_t n, int64_t k, const uint32_t* ex, int64_t n
   hipLaunchKernelGGL(topk_pass_a_kernel<KF>, grid, blk, 0, st, key, n, ex, nex, w, gate);
   hipLaunchKernelGGL(topk_select_a_kernel, dim3(1), dim3(1024), 0, st, w, gate);
   hipLaunchKernelGGL(topk_pass_b_kernel<KF>, grid, blk, 0, st, key, n, ex, nex, w, gate);
-  topk_finish<KF>(key, w, out_idx, out_val, valsrc, st, gate);
+  topk_finish<KF>(key, w, out_idx, out_val, valsrc, out_key, st, gate);
   timer_end(USAF_K_TOPK, st);
   USAF_LAUNCH_CHECK();
   return USAF_OK;
@@ -1078,7 +1088,7 @@ usaf_status topk_run(KF key, int64_t n, int64_t k, const uint32_t* ex, int64_t n
 
 // The sampled single pass (see the file comment) over a whole gradient.
 static usaf_status topk_run_sampled(const float* g, int64_t n, int64_t k, uint32_t* out_idx,
-                                    float* out_val, char* ws, hipStream_t st) {
+                                    float* out_val, uint32_t* out_key, char* ws, hipStream_t st) {
   const TopkWs w = topk_ws(ws, n);
   const dim3 blk{256, 1, 1};
   const int64_t S = sample_count(n);
@@ -1112,7 +1122,7 @@ static usaf_status topk_run_sampled(const float* g, int64_t n, int64_t k, uint32
   }
   hipLaunchKernelGGL(topk_cc_count_kernel, dim3(cgrid), blk, 0, st, w);
   scan_launch(w.cnt, w.nchunks, w.bsum, nullptr, nullptr, st);
-  hipLaunchKernelGGL(topk_cc_emit_kernel, dim3(cgrid), blk, 0, st, w, out_idx, out_val, g);
+  hipLaunchKernelGGL(topk_cc_emit_kernel, dim3(cgrid), blk, 0, st, w, out_idx, out_val, g, out_key);
   timer_end(USAF_K_TOPK, st);
   USAF_LAUNCH_CHECK();
   return USAF_OK;
@@ -1362,25 +1372,17 @@ __global__ __launch_bounds__(256) void union_merge_kernel(const uint32_t* __rest
   }
 }
 
-// Compact keys of RigL's list-sized selections: the drop key of W at each
-// old entry and (when the fresh top-k is to give the grow set) |g| at each
-// fresh entry.
-template <class W, class KD>
-__global__ __launch_bounds__(256) void rigl_keys_kernel(const W* __restrict__ Wf,
-                                                        const uint32_t* __restrict__ old_idx,
-                                                        const float* __restrict__ g,
-                                                        const uint32_t* __restrict__ fresh, int64_t k,
-                                                        uint32_t* __restrict__ kdrop,
-                                                        uint32_t* __restrict__ kgrow,
-                                                        const uint32_t* __restrict__ grow_gate) {
-  const bool grow = *grow_gate != 0;
-  const KD drop{Wf, old_idx};
+// The drop keys of RigL's list-sized drop selection: the key of W at each
+// old entry, from the flat weights (KD with the old list) or from a compact
+// copy of them (KD without a list).
+template <class KD>
+__global__ __launch_bounds__(256) void rigl_drop_keys_kernel(KD drop, int64_t k,
+                                                             uint32_t* __restrict__ kdrop) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < k; i += stride) {
     uint32_t key;
     drop(i, key);
     kdrop[i] = key;
-    if (grow) kgrow[i] = __float_as_uint(g[fresh[i]]) & 0x7fffffffu;
   }
 }
 
@@ -1460,7 +1462,8 @@ extern "C" usaf_status usaf_importance_topk(const float* grad, int64_t n, int64_
 // from a full selection that excludes the old set.  Which one runs is
 // decided on the device (gated kernels), without a host round trip.
 extern "C" usaf_status usaf_rigl_reselect(const usaf_moe_shape* shape, const float* grad,
-                                          const void* Wflat, const uint32_t* old_idx,
+                                          const void* Wflat, const void* old_w,
+                                          const uint32_t* old_idx,
                                           const float* old_m, const float* old_v, int64_t k,
                                           int64_t r, uint32_t* new_idx, float* new_m, float* new_v,
                                           usaf_rigl_stats* stats, void* ws, size_t ws_bytes,
@@ -1491,8 +1494,10 @@ extern "C" usaf_status usaf_rigl_reselect(const usaf_moe_shape* shape, const flo
   uint32_t* B_drop = B_fresh + bstride;                              // dpos bounds of old's blocks
   uint32_t* B_grow = B_drop + bstride;                               // grown bounds of old's blocks
   const unsigned bgrid = unsigned(ceil_div(nb + 1, 4));
-  // fresh top-k of |g| and which of its entries are new
-  USAF_TRY(topk_run(KeyGrad{grad}, N, k, nullptr, 0, fresh, nullptr, nullptr, tws, stream));
+  // fresh top-k of |g| (with its keys, the grow selection's keys) and which
+  // of its entries are new
+  USAF_TRY(topk_run(KeyGrad{grad}, N, k, nullptr, 0, fresh, nullptr, nullptr, tws, stream, nullptr,
+                    kgrow));
   hipLaunchKernelGGL(rigl_stats_init_kernel, dim3(1), dim3(1), 0, stream, cnt);
   hipLaunchKernelGGL(part_bounds_kernel, dim3(bgrid), dim3(256), 0, stream, fresh, nb, old_idx, k,
                      B_fresh, nullptr);
@@ -1502,14 +1507,14 @@ extern "C" usaf_status usaf_rigl_reselect(const usaf_moe_shape* shape, const flo
   if (r > 0) {
     hipLaunchKernelGGL(rigl_gate_kernel, dim3(1), dim3(1), 0, stream, cnt, r, cnt + 1);
     const unsigned kgrid = unsigned(std::min<int64_t>(ceil_div(k, 256), 8192));
+    const uint32_t* kidx = old_w ? nullptr : old_idx;  // the compact list is read in order
+    const void* wsrc = old_w ? old_w : Wflat;
     if (shape->act == USAF_BF16)
-      hipLaunchKernelGGL((rigl_keys_kernel<bf16_t, KeyDropBf16>), dim3(kgrid), dim3(256), 0, stream,
-                         static_cast<const bf16_t*>(Wflat), old_idx, grad, fresh, k, kdrop, kgrow,
-                         cnt + 1);
+      hipLaunchKernelGGL(rigl_drop_keys_kernel<KeyDropBf16>, dim3(kgrid), dim3(256), 0, stream,
+                         KeyDropBf16{static_cast<const bf16_t*>(wsrc), kidx}, k, kdrop);
     else
-      hipLaunchKernelGGL((rigl_keys_kernel<float, KeyDropF32>), dim3(kgrid), dim3(256), 0, stream,
-                         static_cast<const float*>(Wflat), old_idx, grad, fresh, k, kdrop, kgrow,
-                         cnt + 1);
+      hipLaunchKernelGGL(rigl_drop_keys_kernel<KeyDropF32>, dim3(kgrid), dim3(256), 0, stream,
+                         KeyDropF32{static_cast<const float*>(wsrc), kidx}, k, kdrop);
     USAF_LAUNCH_CHECK();
     // grow from the fresh top-k (when it holds >= r new entries) ...
     USAF_TRY(topk_run(KeyArr{kgrow, flag}, k, r, nullptr, 0, gpos, nullptr, nullptr, tws, stream,

@@ -185,7 +185,7 @@ def rigl(layer: SparseMoELayer, grad: torch.Tensor, r: int, stream=None, ws=None
     new_v = torch.empty_like(layer.v)
     stats = torch.zeros(3, dtype=torch.int64, device=layer.device)
     capi.rigl_reselect(layer.shape, grad, layer.W, layer.idx, layer.m, layer.v, k, r, new_idx,
-                       new_m, new_v, stats, ws, stream)
+                       new_m, new_v, stats, ws, stream, old_w=layer.w_list)
     layer.idx, layer.m, layer.v = new_idx, new_m, new_v
     layer.refresh_list()
     return stats

@@ -293,7 +293,7 @@ class MoEStack:
             new_m = torch.empty_like(lay.m)
             new_v = torch.empty_like(lay.v)
             capi.rigl_reselect(self.shape, grad, lay.W, lay.idx, lay.m, lay.v, k, r, new_idx,
-                               new_m, new_v, stats[l], self._ws_rigl, stream)
+                               new_m, new_v, stats[l], self._ws_rigl, stream, old_w=lay.w_list)
             lay.idx, lay.m, lay.v = new_idx, new_m, new_v
             lay.note_touched()
             lay.refresh_list(self.act)

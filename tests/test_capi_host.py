@@ -123,11 +123,11 @@ def test_entry_points_refuse_bad_arguments_before_launch():
     # a workspace off 16-byte alignment
     assert L.usaf_importance_topk(FAKE, 100, 5, None, 0, FAKE, None, FAKE + 4, 1 << 20, None) == 2
     # rigl: r > k, k > N
-    assert L.usaf_rigl_reselect(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 10, 11, FAKE, FAKE,
+    assert L.usaf_rigl_reselect(C.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, 10, 11, FAKE, FAKE,
                                 FAKE, None, FAKE, 1 << 30, None) == 1
-    assert L.usaf_rigl_reselect(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, N + 1, 1, FAKE, FAKE,
+    assert L.usaf_rigl_reselect(C.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, N + 1, 1, FAKE, FAKE,
                                 FAKE, None, FAKE, 1 << 30, None) == 1
-    assert L.usaf_rigl_reselect(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 10, 3, FAKE, FAKE,
+    assert L.usaf_rigl_reselect(C.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, 10, 3, FAKE, FAKE,
                                 FAKE, None, FAKE + 4, 1 << 40, None) == 2
     # adam: step < 1, bad dtype, n == 0 no-op
     f = C.c_double

@@ -386,17 +386,24 @@ def test_rigl_exact(capi, act, old_is_top, dims):
     new_v = torch.empty(k, dtype=torch.float32, device=DEV)
     stats = torch.zeros(3, dtype=torch.int64, device=DEV)
     ws = torch.empty(capi.workspace_size(capi.WS_RIGL, None, N, k), dtype=torch.uint8, device=DEV)
-    capi.rigl_reselect(shape, torch.from_numpy(g).to(DEV), Wt,
-                       torch.from_numpy(S_old.view(np.int32)).to(DEV),
-                       torch.from_numpy(m).to(DEV), torch.from_numpy(v).to(DEV), k, r,
-                       new_idx, new_m, new_v, stats, ws)
-    torch.cuda.synchronize()
+    old_t = torch.from_numpy(S_old.view(np.int32)).to(DEV)
+    g_t = torch.from_numpy(g).to(DEV)
     ref = O.rigl_reselect(g, w, S_old, m, v, k, r)
-    assert np.array_equal(npu32(new_idx), ref["S_new"])
-    assert np.array_equal(new_m.cpu().numpy(), ref["m"].astype(np.float32))
-    assert np.array_equal(new_v.cpu().numpy(), ref["v"].astype(np.float32))
-    s = stats.cpu().numpy()
-    assert s[0] == r and s[1] == r and s[2] == ref["topk_new_vs_old"]
+    # drop keys gathered from the flat weights, then read from a compact copy
+    # of them at the old list (SparseAdam's list)
+    old_w = torch.empty(k, dtype=Wt.dtype, device=DEV)
+    capi.gather(act, Wt, old_t, k, old_w)
+    for ow in (None, old_w):
+        stats.zero_()
+        capi.rigl_reselect(shape, g_t, Wt, old_t, torch.from_numpy(m).to(DEV),
+                           torch.from_numpy(v).to(DEV), k, r, new_idx, new_m, new_v, stats, ws,
+                           old_w=ow)
+        torch.cuda.synchronize()
+        assert np.array_equal(npu32(new_idx), ref["S_new"])
+        assert np.array_equal(new_m.cpu().numpy(), ref["m"].astype(np.float32))
+        assert np.array_equal(new_v.cpu().numpy(), ref["v"].astype(np.float32))
+        s = stats.cpu().numpy()
+        assert s[0] == r and s[1] == r and s[2] == ref["topk_new_vs_old"]
     assert (ref["topk_new_vs_old"] < r) == old_is_top
 
 
