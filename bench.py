@@ -44,33 +44,33 @@ WRITE_SCALE = 1.0   # and 1,048,576 KiB of WRITE_SIZE
 # staging and the two GEMMs of one scan; topk_fresh sums every launch of the
 # scan's first selection (sample, full read, compaction, candidate rounds,
 # emit).
-G = "40a2f9c78d31f644"  # the GEMM sources
+G = "9fb9f79010128068"  # the GEMM sources
 COUNTER_TRAFFIC = {
     "qwen3_step": {
         "router_gemm": (8788, 16384, G),
-        "gate_up": (470370, 147459, G),
-        "down": (221388, 131072, G),
-        "da": (336108, 100110, G),
-        "dx": (628052, 131072, G),
-        "masked_dw": (169551, 11803, "92ef7fede1db8c9f"),
-        "adam": (28614, 123523, "e0a95258367d5586"),
+        "gate_up": (470381, 147461, G),
+        "down": (221377, 131072, G),
+        "da": (320109, 100105, G),
+        "dx": (563591, 131072, G),
+        "masked_dw": (168993, 11803, "392f30b300880270"),
+        "adam": (28622, 123522, "a431573056f07bd3"),
     },
     "qwen3_scan": {
-        "dense_dw": (876683, 2883584, G),
-        "topk_fresh": (1338682, 90728, "49b97a47907be4cd"),
+        "dense_dw": (882812, 2883584, G),
+        "topk_fresh": (1338673, 102477, "21132fbfaed0c251"),
     },
     "mixtral_step": {
-        "router_gemm": (16518, 1024, G),
-        "gate_up": (1920774, 702978, G),
-        "down": (1161307, 68064, G),
-        "da": (2295388, 468116, G),
-        "dx": (2454283, 78256, G),
-        "masked_dw": (754271, 45258, "92ef7fede1db8c9f"),
-        "adam": (62211, 281417, "e0a95258367d5586"),
+        "router_gemm": (16526, 1024, G),
+        "gate_up": (1936804, 702943, G),
+        "down": (1133573, 68064, G),
+        "da": (2271705, 468189, G),
+        "dx": (2471086, 78256, G),
+        "masked_dw": (762941, 45065, "392f30b300880270"),
+        "adam": (62219, 281415, "a431573056f07bd3"),
     },
     "mixtral_scan": {
-        "dense_dw": (4903818, 5636096, G),
-        "topk_fresh": (3122501, 193401, "49b97a47907be4cd"),
+        "dense_dw": (4899516, 5636096, G),
+        "topk_fresh": (3122493, 220993, "21132fbfaed0c251"),
     },
 }
 KERNEL_SOURCES = {
