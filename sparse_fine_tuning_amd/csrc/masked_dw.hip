@@ -603,6 +603,37 @@ __global__ __launch_bounds__(kThreads) void masked_dw_sddmm_kernel(MaskedArgs A,
           offs[i] = (loff << 16) | (sw16(col) * 16);
         }
       }
+      // Bank-aware lane order: the 16 lanes of a quarter-wave read LDS
+      // together, and their column reads conflict when two fall in one
+      // 16-byte bank group (random columns meet ~3 per group).  For each i
+      // the wave sorts its 64 entries by the column's bank group (a
+      // counting sort on the group's 4 bits, by ballots) and deals the
+      // sorted order across the quarters (sorted position p goes to lane
+      // 16 (p mod 4) + p / 4), so equal groups land in different quarters;
+      // rows stay within the 64 neighbouring entries, mostly one broadcast
+      // row per quarter.  Results do not depend on the order.
+      const uint64_t below = (uint64_t(1) << lane) - 1;
+#pragma unroll
+      for (int i = 0; i < kE; ++i) {
+        if (i >= per) break;  // uniform
+        const uint32_t g = ((offs[i] & 0xffffu) >> 4) & 15u;
+        uint64_t eq = ~uint64_t(0);
+        uint32_t less = 0;
+#pragma unroll
+        for (int b = 3; b >= 0; --b) {
+          const uint64_t B = __ballot((g >> b) & 1u);
+          if ((g >> b) & 1u) {
+            less += uint32_t(__popcll(eq & ~B));
+            eq &= B;
+          } else {
+            eq &= ~B;
+          }
+        }
+        const uint32_t p = less + uint32_t(__popcll(eq & below));
+        const int dst = int(((p & 3u) << 4) | (p >> 2));
+        offs[i] = uint32_t(__builtin_amdgcn_ds_permute(dst << 2, int(offs[i])));
+        opos[i] = uint32_t(__builtin_amdgcn_ds_permute(dst << 2, int(opos[i])));
+      }
     }
     // Products over one staged chunk, entries in branch-free groups of 4 (an
     // unused entry reads row 0 and column 0): bf16 dot2 with fp32
