@@ -273,56 +273,51 @@ struct MNMajor {
 
 // A k-major operand of R rows held as affine 4-bit codes in groups of G = 2^gshift
 // along k (w = bf16(fp32(fp32(q - z) * s)), element 2i in the low nibble of
-// byte i), dequantised in LDS: by the whole block into a bf16 tile once per
-// stage (Convert), or by each wave as it reads its fragments.  The codes do not go
-// through the ring: they arrive by DMA in blocks of CB stages (a row's
-// 32 CB bytes at once, whole 64-byte lines rather than 16-byte pieces per
-// stage), into one of two LDS buffers by block parity, 16-byte chunks
-// swizzled by row as in KMajor; the fp16 scales and zeros arrive per row 8
-// groups (16 bytes) at a time, into one of two buffers by parity.  A block's
-// loads go out with its first stage's, so the per-stage vmcnt waits (counted
-// on the other operand's loads alone) cover them.  A block's loads are issued
-// NS - 1 stages ahead, while stage kt is current; the previous block of the
-// same parity ended with stage (block start) - CB - 1, which is below kt
-// when CB >= NS - 1 (the problem asserts it; a scale block spans
-// 8 G / 64 >= 8 stages), so no buffer is refilled while a stage still reads
-// it.  Requirements: the contraction a whole number of stages, G a multiple
-// of 64, an even number kg >= 2 of groups per row (4-byte aligned pairs).
-// Src: code_row(r) -> global code row of tile row r (r < R, always valid);
-// q, s, z; qpitch (bytes per code row), kg (groups per row), gshift.
-template <int R, int NW, int CB, bool Convert = false>
+// byte i), dequantised in LDS one stage ahead of the MFMAs.  The codes do not
+// go through the ring: a stage's 32 code bytes per row and its scale and
+// zero pairs (the two fp16 of the aligned group pair holding the stage's
+// group, 4 bytes each) arrive by DMA in a batch of their own, one stage
+// further ahead than the other operand's stage in the same batch, into one
+// of three code / scale buffers.  While the MFMAs of stage kt read the bf16
+// tile of stage kt, the whole block converts stage kt + 1 (its loads landed
+// with stage kt's wait) into the other of two bf16 tiles (KMajor's layout),
+// in four parts between the MFMA substeps; the next stage's barrier
+// publishes it.  A tile's first stage is converted before its main loop.
+// Buffer reuse: the batch issued during stage kt fills code buffer
+// (kt + NS) mod 3, last read while stage kt + NS - 3 <= kt was converted:
+// during stage kt - 1, or (NS = 3, kt = 0) at the tile's start, which is
+// why a first stage's conversion precedes its batch; tile (kt + 1) mod 2
+// was last read by stage kt - 1.  Every
+// batch issues the same loads (stages past the last reload the last), so
+// the ring's vmcnt waits count them exactly.  Requirements: R = 32 NW (each
+// wave loads 32 rows of codes and 64 scale or zero pairs per stage), the
+// contraction a whole number of stages, G a multiple of 64, an even number
+// kg of groups per row.  Src: code_row(r) -> global code row of tile row r
+// (r < R, always valid); q, s, z; qpitch (bytes per code row), kg (groups
+// per row), gshift.
+template <int R, int NW>
 struct KMajorQ4 {
   static constexpr int kBK = 64;
-  // Convert: each stage is dequantised once, by the whole block, into a bf16
-  // tile in KMajor's layout that every wave then reads; otherwise each wave
-  // dequantises the fragments it reads
-  static constexpr bool kConvert = Convert;
+  static constexpr bool kConvert = true;
   using Tile = KMajor<R, NW, 64>;
-  static constexpr int kFragReads = Convert ? 1 : 3;
+  static constexpr int kFragReads = 1;
   static constexpr bool kPrep = false;
-  static constexpr int kCB = CB;
-  static constexpr int kBytes = 0;                      // nothing in the ring
-  static constexpr int kInstMin = 0;                    // most stages issue no block loads
-  static constexpr int kRowB = 32 * CB;                 // code bytes of a row per block
-  static constexpr int kChunks = kRowB / 16;
-  static constexpr int kRowsPerInst = 64 / kChunks;
-  static constexpr int kCodeInst = R / kRowsPerInst;    // DMA instructions per code block
-  static constexpr int kCodeBuf = R * kRowB;
-  static constexpr int kScaleBuf = R * 16;              // one array's 8 groups of every row
-  static constexpr int kScaleInst = R / 16;             // per array: 4 lanes x 4 bytes per row
-  static constexpr int kCodePW = kCodeInst / NW, kScalePW = 2 * kScaleInst / NW;
-  static_assert(kChunks >= 2 && kChunks <= 8 && kCodePW * NW == kCodeInst &&
-                kScalePW * NW == 2 * kScaleInst, "code and scale blocks shared evenly by the waves");
+  static constexpr int kBytes = 0;     // nothing in the ring
+  static constexpr int kInstMin = 2;   // per batch and wave: 32 code rows, 64 scale or zero pairs
+  static constexpr int kCodeBuf = R * 32;
+  static constexpr int kScaleBuf = 2 * R * 4;   // [s, z][row][the group pair]
+  static constexpr int kTileBuf = R * 128;
+  static_assert(R == 32 * NW && NW >= 2 && NW % 2 == 0, "one code and one scale instruction per wave");
   __device__ __forceinline__ static unsigned char* code_lds() {
-    __shared__ __attribute__((aligned(16))) unsigned char buf[2 * kCodeBuf];
+    __shared__ __attribute__((aligned(16))) unsigned char buf[3 * kCodeBuf];
     return buf;
   }
-  __device__ __forceinline__ static unsigned char* scale_lds() {  // [parity][s, z][row][16 B]
-    __shared__ __attribute__((aligned(16))) unsigned char buf[4 * kScaleBuf];
+  __device__ __forceinline__ static unsigned char* scale_lds() {
+    __shared__ __attribute__((aligned(16))) unsigned char buf[3 * kScaleBuf];
     return buf;
   }
-  __device__ __forceinline__ static unsigned char* tile_lds() {  // the converted stage (Convert)
-    __shared__ __attribute__((aligned(16))) unsigned char buf[Convert ? R * 128 : 16];
+  __device__ __forceinline__ static unsigned char* tile_lds() {
+    __shared__ __attribute__((aligned(16))) unsigned char buf[2 * kTileBuf];
     return buf;
   }
   // 8 weights from 4 code bytes: w = bf16(fp32(fp32(q - z) * s)), the low
@@ -338,93 +333,70 @@ struct KMajorQ4 {
     }
     return make_uint4(o[0], o[1], o[2], o[3]);
   }
-  __device__ __forceinline__ void scale_zero(int n, int kt, float& sc, float& zr) const {
-    const int g = kt >> gsh6;
-    const unsigned char* sb = scale_lds() + ((g >> 3) & 1) * 2 * kScaleBuf + n * 16 + 2 * (g & 7);
-    sc = float(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb)));
-    zr = float(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb + kScaleBuf)));
-  }
-  // Convert: stage kt's codes into the bf16 tile, 32 weights (16 code
-  // bytes) per thread and pass; the caller's barrier publishes the tile
-  __device__ __forceinline__ void convert(int kt, int tid) const {
-    if constexpr (Convert) {
-      for (int u = tid; u < 2 * R; u += 64 * NW) {
-        const int r = u >> 1, h = u & 1;  // row, half of the stage's 64 k
-        const int c = 2 * (kt % CB) + h;  // code chunk in the row's block
-        const uint4 q = *reinterpret_cast<const uint4*>(code_lds() + ((kt / CB) & 1) * kCodeBuf +
-                                                         r * kRowB + 16 * (c ^ sw(r)));
-        float sc, zr;
-        scale_zero(r, kt, sc, zr);
-        const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)  // bf16 chunk 4 h + j of the row (8 k)
-          *reinterpret_cast<uint4*>(tile_lds() + r * 128 + 16 * ((4 * h + j) ^ Tile::sw(r))) =
-              dequant8(qw[j], sc, zr);
-      }
-    }
-  }
-  // 16-byte chunk slot swizzle, as KMajor::sw for rows of kRowB bytes
-  __device__ __forceinline__ static int sw(int r) { return (r / (256 / kRowB)) & (kChunks - 1); }
-  const unsigned char* cptr[kCodePW];  // the lane's code row, at its first chunk
-  int cchunk[kCodePW];                 // that chunk's index in the row
-  int64_t selem[kScalePW];             // scales / zeros: the lane's first element (group 2 d)
-  const uint16_t* sbase[kScalePW];
-  int qpitch, kg, gsh6;
-  template <class Src>
-  __device__ __forceinline__ void init(const Src& s, int, int w, int lane) {
-    qpitch = int(s.qpitch);
-    kg = s.kg;
-    gsh6 = s.gshift - 6;
-#pragma unroll
-    for (int i = 0; i < kCodePW; ++i) {
-      const int r = (w + NW * i) * kRowsPerInst + lane / kChunks;
-      cchunk[i] = (lane % kChunks) ^ sw(r);
-      cptr[i] = s.q + s.code_row(r) * s.qpitch;
-    }
-#pragma unroll
-    for (int i = 0; i < kScalePW; ++i) {
-      const int j = w + NW * i;  // 0 .. 2 kScaleInst - 1: scales, then zeros
-      const int r = (j % kScaleInst) * 16 + lane / 4;
-      selem[i] = s.code_row(r) * s.kg + 2 * (lane % 4);
-      sbase[i] = j < kScaleInst ? s.s : s.z;
-    }
-  }
-  template <class Src>
-  __device__ __forceinline__ void issue(const Src&, int kt, unsigned char*, int w, int lane) const {
-    if (kt % CB == 0) {  // uniform: a code block starts
-      unsigned char* dst = code_lds() + ((kt / CB) & 1) * kCodeBuf;
-      const int b0 = 32 * kt;  // the block's first byte in a row
-#pragma unroll
-      for (int i = 0; i < kCodePW; ++i) {
-        // a chunk past the row's end (a last block of fewer than CB stages)
-        // reads the row's last chunk instead; it is never used
-        const int off = min(b0 + 16 * cchunk[i], qpitch - 16);
-        dma16(cptr[i] + off, dst + (w + NW * i) * 1024);
-      }
-    }
-    if ((kt & ((8 << gsh6) - 1)) == 0) {  // uniform: a scale block (8 groups) starts
-      const int g0 = kt >> gsh6;
-      unsigned char* dst = scale_lds() + ((g0 >> 3) & 1) * 2 * kScaleBuf;
-#pragma unroll
-      for (int i = 0; i < kScalePW; ++i) {
-        const int j = w + NW * i;
-        // pairs past the row's groups read the row's last pair; never used
-        const int64_t e = selem[i] + min(g0, kg - 2 - 2 * (lane % 4));
-        dma4(sbase[i] + e, dst + (j >= kScaleInst ? kScaleBuf : 0) + (j % kScaleInst) * 256);
-      }
-    }
-  }
-  __device__ __forceinline__ static void zero_tail(unsigned char*, int, int) {}
-  // fragment rows base..base+31, k-substep kc of stage kt: 8 bf16 weights
-  __device__ __forceinline__ bf16x8_t frag(const unsigned char*, int base, int kc, int lane, int kt) const {
-    if constexpr (Convert) return Tile::frag(tile_lds(), base, kc, lane);
-    const int n = base + (lane & 31);
-    const int byte = 32 * (kt % CB) + 8 * kc + 4 * (lane >> 5);
-    const uint32_t code = *reinterpret_cast<const uint32_t*>(
-        code_lds() + ((kt / CB) & 1) * kCodeBuf + n * kRowB + 16 * ((byte >> 4) ^ sw(n)) + (byte & 15));
+  // A thread's share of converting a stage: R rows x 2 halves of the
+  // stage's 64 k over the block's 64 NW = 2 R threads, one each; load()
+  // reads its 16 code bytes and the row's scale and zero, part(j) writes
+  // 8 weights (bf16 chunk 4 h + j of the row)
+  struct Conv {
+    uint4 q;
     float sc, zr;
-    scale_zero(n, kt, sc, zr);
-    return __builtin_bit_cast(bf16x8_t, dequant8(code, sc, zr));
+    unsigned char* dst;
+    int r, h;
+  };
+  __device__ __forceinline__ Conv conv_load(int st, int tid) const {
+    Conv c;
+    c.r = tid >> 1;
+    c.h = tid & 1;
+    const int b = st % 3;
+    c.q = *reinterpret_cast<const uint4*>(code_lds() + b * kCodeBuf + c.r * 32 + 16 * c.h);
+    const int half = ((st << 6) >> gshift) & 1;  // the stage's group within its pair
+    const unsigned char* sb = scale_lds() + b * kScaleBuf + c.r * 4 + 2 * half;
+    c.sc = float(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb)));
+    c.zr = float(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb + R * 4)));
+    c.dst = tile_lds() + (st & 1) * kTileBuf + c.r * 128;
+    return c;
+  }
+  __device__ __forceinline__ static void conv_part(const Conv& c, int j) {
+    const uint32_t qw = j == 0 ? c.q.x : j == 1 ? c.q.y : j == 2 ? c.q.z : c.q.w;
+    *reinterpret_cast<uint4*>(c.dst + 16 * ((4 * c.h + j) ^ Tile::sw(c.r))) = dequant8(qw, c.sc, c.zr);
+  }
+  __device__ __forceinline__ void convert(int st, int tid) const {
+    const Conv c = conv_load(st, tid);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) conv_part(c, j);
+  }
+  const unsigned char* cptr;   // the lane's code row at its 16-byte chunk
+  const uint16_t* sptr;        // the lane's scale or zero row
+  int gshift, kg, last;        // last: the tile's last stage
+  template <class Src>
+  __device__ __forceinline__ void init(const Src& s, int kend, int w, int lane) {
+    gshift = s.gshift;
+    kg = s.kg;
+    last = kend / 64 - 1;
+    cptr = s.q + s.code_row(32 * w + (lane >> 1)) * s.qpitch + 16 * (lane & 1);
+    const int sr = 64 * (w % (NW / 2)) + lane;  // scales: waves 0 .. NW/2 - 1, zeros: the rest
+    sptr = (w < NW / 2 ? s.s : s.z) + s.code_row(sr % R) * s.kg;
+  }
+  // the code and scale loads of stage st (clamped to the last) into buffer st mod 3
+  __device__ __forceinline__ void load_stage(int st, int w) const {
+    const int b = st % 3;
+    const int sc = min(st, last);
+    dma16(cptr + 32 * sc, code_lds() + b * kCodeBuf + w * 1024);
+    const int pair = ((sc << 6) >> gshift) & ~1;
+    dma4(sptr + pair, scale_lds() + b * kScaleBuf + (w >= NW / 2 ? R * 4 : 0) + (w % (NW / 2)) * 256);
+  }
+  // the batch of ring stage kt carries stage kt + 1's codes
+  template <class Src>
+  __device__ __forceinline__ void issue(const Src&, int kt, unsigned char*, int w, int) const {
+    load_stage(kt + 1, w);
+  }
+  // before a tile's first batch: stage 0's codes
+  template <class Src>
+  __device__ __forceinline__ void issue_first(const Src&, int w) const { load_stage(0, w); }
+  __device__ __forceinline__ static void zero_tail(unsigned char*, int, int) {}
+  // fragment rows base..base+31, k-substep kc of stage kt: from stage kt's tile
+  __device__ __forceinline__ bf16x8_t frag(const unsigned char*, int base, int kc, int lane, int kt) const {
+    return Tile::frag(tile_lds() + (kt & 1) * kTileBuf, base, kc, lane);
   }
 };
 
@@ -517,6 +489,17 @@ struct WaveRows {
 //                 unsigned char* stage)   (stage: kStageBytes of LDS private to the wave)
 // Each wave computes RW x CW.
 // ---------------------------------------------------------------------------
+// The per-thread conversion state of an operand converted in LDS (none for
+// the others).
+template <class Op, class = void>
+struct ConvOf {
+  struct type {};
+};
+template <class Op>
+struct ConvOf<Op, std::void_t<typename Op::Conv>> {
+  using type = typename Op::Conv;
+};
+
 // Scheduling request for one substep of the main loop: its NM MFMAs, each
 // followed by a share of the NR LDS fragment reads of the next substep, so
 // every fragment is read about one substep before its MFMA needs it.
@@ -566,18 +549,25 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
       BOp::zero_tail(cur + A_BYTES, kvalid, tid);
       __syncthreads();
     }
+    // an operand converted in LDS: a tile's first stage before its MFMAs
+    // (and before this stage's batch, whose loads may refill the buffer it
+    // reads), then stage kt + 1 in four parts between this stage's substeps
+    if constexpr (BOp::kConvert && kFirst) {
+      bo.convert(0, tid);
+      __syncthreads();
+    }
     if (kt + NS - 1 < nk) {
       unsigned char* nxt = lds[(kt + NS - 1) % NS];
       ao.issue(as, kt + NS - 1, nxt, w, lane);
       bo.issue(bs, kt + NS - 1, nxt + A_BYTES, w, lane);
     }
-    if constexpr (BOp::kConvert) {
-      // the previous stage's last substep first (its fragments are in
-      // registers), then the block converts this stage's weight tile
-      if constexpr (!kFirst && VB > 0) mfmas(pa, pb);
-      bo.convert(kt, tid);
-      __syncthreads();
-    }
+    // (the last stage converts the reloaded last stage into the tile no
+    // stage of this tile reads, which keeps the stage body free of branches)
+    typename ConvOf<BOp>::type cv{};
+    if constexpr (BOp::kConvert) cv = bo.conv_load(kt + 1, tid);
+    auto conv_part = [&](int j) {
+      if constexpr (BOp::kConvert) BOp::conv_part(cv, j);
+    };
     if constexpr (VB > 0) {
       const unsigned char* As = cur;
       const unsigned char* Bs = cur + A_BYTES;
@@ -587,7 +577,7 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
       for (int i = 0; i < VB; ++i) af[0][i] = AOp::frag(As, r0 + 32 * i, 0, lane);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bfr[0][j] = bo.frag(Bs, wn * CW + 32 * j, 0, lane, kt);
-      if constexpr (!kFirst && !BOp::kConvert) {
+      if constexpr (!kFirst) {
         mfmas(pa, pb);  // the previous stage's last substep
         interleave_mfma_reads<NM, NR>();
       }
@@ -600,12 +590,19 @@ __device__ __forceinline__ void main_loop(const AOp& ao, const BOp& bo, const AS
         for (int j = 0; j < NJ; ++j) bfr[n][j] = bo.frag(Bs, wn * CW + 32 * j, kc + 1, lane, kt);
         mfmas(af[c], bfr[c]);
         interleave_mfma_reads<NM, NR>();
+        if constexpr (KC == 4) conv_part(kc);
       }
+      if constexpr (KC == 4) conv_part(3);
       constexpr int last = (KC - 1) & 1;
+      static_assert(!BOp::kConvert || KC == 4, "the conversion is split over four substeps");
 #pragma unroll
       for (int i = 0; i < VB; ++i) pa[i] = af[last][i];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) pb[j] = bfr[last][j];
+    } else {
+      // a wave with no rows in this tile still converts its share
+#pragma unroll
+      for (int j = 0; j < 4; ++j) conv_part(j);
     }
   };
   if (nk > 0) {
@@ -637,6 +634,7 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_kernel(P p) {
   ao.init(as, K, w, lane);
   bo.init(bs, K, w, lane);
   const int nk = (K + AOp::kBK - 1) / AOp::kBK;
+  if constexpr (BOp::kConvert) bo.issue_first(bs, w);
   f32x16_t acc[IM][NJ];
 #pragma unroll
   for (int i = 0; i < IM; ++i)
@@ -685,6 +683,7 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_persistent(P p)
   ao.init(as, t.ke, w, lane);
   bo.init(bs, t.ke, w, lane);
   int nk = (t.ke + AOp::kBK - 1) / AOp::kBK;
+  if constexpr (BOp::kConvert) bo.issue_first(bs, w);
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) {
@@ -726,6 +725,7 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_persistent(P p)
       ao.init(as, tn.ke, w, lane);
       bo.init(bs, tn.ke, w, lane);
       nk = (tn.ke + AOp::kBK - 1) / AOp::kBK;
+      if constexpr (BOp::kConvert) bo.issue_first(bs, w);
 #pragma unroll
       for (int s = 0; s < NS - 1; ++s)
         if (s < nk) {

@@ -274,7 +274,6 @@ struct MDown {
 // computed equals, bit for bit, the same layer on the resident copy of the
 // same codes: the weights are the same bf16 values, and every output
 // accumulates the same MFMA chunks in the same order.
-constexpr int kQ4CodeBlock = 2;  // stages per code block: a row's 64 code bytes per request
 struct Q4Codes {
   const uint8_t* q; const uint16_t* s; const uint16_t* z;
   int64_t qpitch;  // bytes per code row (K / 2)
@@ -297,11 +296,10 @@ struct RowCodesC : Q4Codes {
   __device__ __forceinline__ int64_t code_row(int r) const { return row0 + min(r, n - 1); }
 };
 
-template <int BM_, int BN_, int NS_, int WM_, int WN_, bool CV_>
+template <int BM_, int BN_, int NS_, int WM_, int WN_>
 struct MGateUpQ4 : MGateUp<BM_, BN_, NS_, WM_, WN_, 64> {
   using Base = MGateUp<BM_, BN_, NS_, WM_, WN_, 64>;
-  using BOp = KMajorQ4<BN_, WM_ * WN_, kQ4CodeBlock, CV_>;
-  static_assert(BOp::kCB >= NS_ - 1, "a code buffer is refilled only after its stages are done");
+  using BOp = KMajorQ4<BN_, WM_ * WN_>;
   static constexpr int kPStage =
       Base::kPStage * WM_ * WN_ <= Base::AOp::kBytes + BOp::kBytes ? Base::kPStage : 0;
   static constexpr int kStageBytes = kPStage;
@@ -311,11 +309,10 @@ struct MGateUpQ4 : MGateUp<BM_, BN_, NS_, WM_, WN_, 64> {
   }
 };
 
-template <int BM_, int BN_, int NS_, int WM_, int WN_, bool CV_>
+template <int BM_, int BN_, int NS_, int WM_, int WN_>
 struct MDownQ4 : MDown<BM_, BN_, NS_, WM_, WN_, 64> {
   using Base = MDown<BM_, BN_, NS_, WM_, WN_, 64>;
-  using BOp = KMajorQ4<BN_, WM_ * WN_, kQ4CodeBlock, CV_>;
-  static_assert(BOp::kCB >= NS_ - 1, "a code buffer is refilled only after its stages are done");
+  using BOp = KMajorQ4<BN_, WM_ * WN_>;
   static constexpr int kPStage =
       Base::kPStage * WM_ * WN_ <= Base::AOp::kBytes + BOp::kBytes ? Base::kPStage : 0;
   static constexpr int kStageBytes = kPStage;
@@ -782,10 +779,9 @@ usaf_status mfma_dense_dw(const usaf_moe_shape& s, const bf16_t* X, const bf16_t
 
 // The 4-bit forward GEMMs: the ring holds the activations only (3 stages,
 // 60 KiB, for 160-row tiles; 2 stages, 64 KiB, for 256-row ones), beside
-// the two code buffers (2 x 16 KiB for 256 weight rows), the two scale
-// buffers (2 x 2 x 4 KiB) and the converted bf16 stage (32 KiB).
-constexpr bool kQ4Convert = true;
-constexpr int kQ4NS = 3, kQ4BigNS = kQ4Convert ? 2 : 3;
+// three code buffers (3 x 8 KiB for 256 weight rows), three scale buffers
+// (3 x 2 KiB) and two converted bf16 stages (2 x 32 KiB).
+constexpr int kQ4NS = 3, kQ4BigNS = 2;
 
 static int log2_exact(int g) {
   int s = 0;
@@ -799,11 +795,11 @@ usaf_status q4_gate_up(const usaf_moe_shape& s, const bf16_t* X, const usaf_q4_e
   const int NT = int(ceil_div(s.I, kFwdBN / 2));
   const g2::Q4Codes c{w.q_gu, w.s_gu, w.z_gu, s.H / 2, s.H / w.group, log2_exact(w.group)};
   if (big_groups(s)) {
-    using P = g2::MGateUpQ4<kBigBM, kFwdBN, kQ4BigNS, kBigWM, kBigWN, kQ4Convert>;
+    using P = g2::MGateUpQ4<kBigBM, kFwdBN, kQ4BigNS, kBigWM, kBigWN>;
     const P p{{X, nullptr, offsets, perm, gu, a, s.H, s.E, s.K, s.I, NT}, c};
     return launch_persistent(p, grouped_tiles_bound(s, NT, kBigBM), st, USAF_K_GATE_UP);
   }
-  using P = g2::MGateUpQ4<kFwdBM, kFwdBN, kQ4NS, kFwdWM, kFwdWN, kQ4Convert>;
+  using P = g2::MGateUpQ4<kFwdBM, kFwdBN, kQ4NS, kFwdWM, kFwdWN>;
   const P p{{X, nullptr, offsets, perm, gu, a, s.H, s.E, s.K, s.I, NT}, c};
   return launch_persistent(p, grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_GATE_UP);
 }
@@ -813,11 +809,11 @@ usaf_status q4_down(const usaf_moe_shape& s, const bf16_t* a, const usaf_q4_expe
   const int NT = int(ceil_div(s.H, kFwdBN));
   const g2::Q4Codes c{w.q_d, w.s_d, w.z_d, s.I / 2, s.I / w.group, log2_exact(w.group)};
   if (big_groups(s)) {
-    using P = g2::MDownQ4<kBigBM, kFwdBN, kQ4BigNS, kBigWM, kBigWN, kQ4Convert>;
+    using P = g2::MDownQ4<kBigBM, kFwdBN, kQ4BigNS, kBigWM, kBigWN>;
     const P p{{a, nullptr, offsets, ybuf, s.H, s.E, s.I, NT}, c};
     return launch_persistent(p, grouped_tiles_bound(s, NT, kBigBM), st, USAF_K_DOWN);
   }
-  using P = g2::MDownQ4<kFwdBM, kFwdBN, kQ4NS, kFwdWM, kFwdWN, kQ4Convert>;
+  using P = g2::MDownQ4<kFwdBM, kFwdBN, kQ4NS, kFwdWM, kFwdWN>;
   const P p{{a, nullptr, offsets, ybuf, s.H, s.E, s.I, NT}, c};
   return launch_persistent(p, grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DOWN);
 }
