@@ -229,14 +229,18 @@ USAF_API usaf_status usaf_importance_topk(const float *grad, int64_t n, int64_t 
  * (shape->act); old_w (nullable, shape->act, [k]): Wflat at old_idx, e.g.
  * usaf_sparse_adam's compact list, read in order instead of gathering the
  * drop keys from Wflat; old_idx [k] strictly ascending; old_m, old_v [k] fp32.
+ * new_w (nullable, shape->act, [k]; needs old_w): Wflat at new_idx, the kept
+ * entries' weights copied from old_w and the grown ones' read from Wflat
+ * (the new compact list of usaf_sparse_adam, without a gather of the list).
  * stats (nullable, device): counts, including the fresh top-k's novelty.
  * Outputs must not alias inputs; grad and ws 16-byte aligned (UNSUPPORTED
- * otherwise).  Errors: INVALID_ARG for r > k, k > N, r > N - k.
+ * otherwise).  Errors: INVALID_ARG for r > k, k > N, r > N - k, new_w
+ * without old_w.
  * ws: USAF_WS_RIGL bytes for (N, k). */
 USAF_API usaf_status usaf_rigl_reselect(const usaf_moe_shape *shape, const float *grad,
                                const void *Wflat, const void *old_w, const uint32_t *old_idx,
                                const float *old_m, const float *old_v, int64_t k, int64_t r,
-                               uint32_t *new_idx, float *new_m, float *new_v,
+                               uint32_t *new_idx, float *new_m, float *new_v, void *new_w,
                                usaf_rigl_stats *stats, void *ws, size_t ws_bytes,
                                hipStream_t stream);
 

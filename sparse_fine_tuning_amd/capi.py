@@ -92,7 +92,7 @@ def _load():
         "usaf_masked_backward": [vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp],
         "usaf_masked_plan": [vp, vp, i64, vp, sz, vp],
         "usaf_importance_topk": [vp, i64, i64, vp, i64, vp, vp, vp, sz, vp],
-        "usaf_rigl_reselect": [vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
+        "usaf_rigl_reselect": [vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp],
         "usaf_sparse_adam": [i32, vp, vp, i64, vp, vp, vp, vp, i64, C.c_double, C.c_double,
                              C.c_double, C.c_double, vp, vp],
         "usaf_gather": [i32, vp, vp, i64, vp, vp],
@@ -210,9 +210,9 @@ def importance_topk(grad, n, k, exclude, n_exclude, out_idx, out_val, ws, stream
 
 
 def rigl_reselect(shape, grad, Wflat, old_idx, old_m, old_v, k, r, new_idx, new_m, new_v, stats,
-                  ws, stream=None, old_w=None):
+                  ws, stream=None, old_w=None, new_w=None):
     _check(lib.usaf_rigl_reselect(C.byref(shape), _p(grad), _p(Wflat), _p(old_w), _p(old_idx), _p(old_m),
-                                  _p(old_v), int(k), int(r), _p(new_idx), _p(new_m), _p(new_v),
+                                  _p(old_v), int(k), int(r), _p(new_idx), _p(new_m), _p(new_v), _p(new_w),
                                   _p(stats), _p(ws), ws.numel() * ws.element_size(),
                                   _stream(stream)),
            "usaf_rigl_reselect")

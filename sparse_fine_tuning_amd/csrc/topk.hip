@@ -1232,13 +1232,17 @@ __global__ __launch_bounds__(256) void member_merge_kernel(const uint32_t* __res
 // entries below old_idx[q0] (0 for the first block).  A kept entry at old
 // position q lands at (q - dropped before q) + (grown below it) with its
 // moments; a grown entry j whose value falls in this block's old range lands
-// at j + (kept entries below it) with zero moments.
+// at j + (kept entries below it) with zero moments.  With new_w, the compact
+// weight list follows: a kept entry's weight from old_w, a grown entry's
+// from the flat weights.
+template <class W>
 __global__ __launch_bounds__(256) void rigl_place_kernel(
     const uint32_t* __restrict__ old_idx, const float* __restrict__ old_m,
     const float* __restrict__ old_v, int64_t k, const uint32_t* __restrict__ dpos,
     const uint32_t* __restrict__ D, const uint32_t* __restrict__ grown,
     const uint32_t* __restrict__ G, uint32_t* __restrict__ new_idx, float* __restrict__ new_m,
-    float* __restrict__ new_v) {
+    float* __restrict__ new_v, const W* __restrict__ old_w, const W* __restrict__ Wf,
+    W* __restrict__ new_w) {
   __shared__ uint32_t os[kPB];       // old entries of the block
   __shared__ uint32_t pre[kPB + 1];  // dropped flags, then dropped before each position
   __shared__ uint32_t gs[kPCap];     // grown entries in the block's range
@@ -1283,6 +1287,7 @@ __global__ __launch_bounds__(256) void rigl_place_kernel(
     new_idx[out] = f;
     new_m[out] = old_m[q0 + j];
     new_v[out] = old_v[q0 + j];
+    if (new_w) new_w[out] = old_w[q0 + j];
   }
   for (int x = tid; x < glen; x += 256) {
     const uint32_t f = staged ? gs[x] : grown[g0 + x];
@@ -1292,6 +1297,7 @@ __global__ __launch_bounds__(256) void rigl_place_kernel(
     new_idx[out] = f;
     new_m[out] = 0.f;
     new_v[out] = 0.f;
+    if (new_w) new_w[out] = Wf[f];
   }
 }
 
@@ -1466,13 +1472,14 @@ extern "C" usaf_status usaf_rigl_reselect(const usaf_moe_shape* shape, const flo
                                           const uint32_t* old_idx,
                                           const float* old_m, const float* old_v, int64_t k,
                                           int64_t r, uint32_t* new_idx, float* new_m, float* new_v,
-                                          usaf_rigl_stats* stats, void* ws, size_t ws_bytes,
-                                          hipStream_t stream) {
+                                          void* new_w, usaf_rigl_stats* stats, void* ws,
+                                          size_t ws_bytes, hipStream_t stream) {
   USAF_TRY(check_shape(shape));
   const int64_t N = n_weights(*shape);
   if (k < 0 || r < 0 || k > N || r > k || r > N - k) return USAF_ERR_INVALID_ARG;
   if (!grad || !Wflat || !old_idx || !old_m || !old_v || !new_idx || !new_m || !new_v)
     return USAF_ERR_INVALID_ARG;
+  if (new_w && !old_w) return USAF_ERR_INVALID_ARG;  // kept weights come from old_w
   if (reinterpret_cast<uintptr_t>(grad) & 15) return USAF_ERR_UNSUPPORTED;
   const WsRigl L = ws_rigl(N, k);
   if (!ws || ws_bytes < L.total) return USAF_ERR_WORKSPACE;
@@ -1532,8 +1539,16 @@ extern "C" usaf_status usaf_rigl_reselect(const usaf_moe_shape* shape, const flo
                      B_drop, nullptr);
   hipLaunchKernelGGL(part_bounds_kernel, dim3(bgrid), dim3(256), 0, stream, old_idx, nb, grown, r,
                      B_grow, nullptr);
-  hipLaunchKernelGGL(rigl_place_kernel, dim3(unsigned(nb)), dim3(256), 0, stream, old_idx, old_m,
-                     old_v, k, dpos, B_drop, grown, B_grow, new_idx, new_m, new_v);
+  if (shape->act == USAF_BF16)
+    hipLaunchKernelGGL(rigl_place_kernel<bf16_t>, dim3(unsigned(nb)), dim3(256), 0, stream, old_idx,
+                       old_m, old_v, k, dpos, B_drop, grown, B_grow, new_idx, new_m, new_v,
+                       static_cast<const bf16_t*>(old_w), static_cast<const bf16_t*>(Wflat),
+                       static_cast<bf16_t*>(new_w));
+  else
+    hipLaunchKernelGGL(rigl_place_kernel<float>, dim3(unsigned(nb)), dim3(256), 0, stream, old_idx,
+                       old_m, old_v, k, dpos, B_drop, grown, B_grow, new_idx, new_m, new_v,
+                       static_cast<const float*>(old_w), static_cast<const float*>(Wflat),
+                       static_cast<float*>(new_w));
   timer_end(USAF_K_RIGL_MERGE, stream);
   USAF_LAUNCH_CHECK();
   if (stats) {

@@ -95,13 +95,16 @@ class SparseMoELayer:
         self.dW = torch.empty(k, dtype=torch.float32, device=self.device)
         self.refresh_list()
 
-    def refresh_list(self):
+    def refresh_list(self, w_list=None):
         """Per-list state rebuilt whenever the list changes: the compact copy
         of the active weights (W at idx) that SparseAdam reads instead of the
-        scattered entries, and the masked gradient's plan."""
+        scattered entries (gathered, unless the caller has it, as RigL's
+        reselection does), and the masked gradient's plan."""
         k = self.idx.numel()
-        self.w_list = torch.empty(k, dtype=_dt(self.act), device=self.device)
-        capi.gather(self.act, self.W, self.idx, k, self.w_list)
+        if w_list is None:
+            w_list = torch.empty(k, dtype=_dt(self.act), device=self.device)
+            capi.gather(self.act, self.W, self.idx, k, w_list)
+        self.w_list = w_list
         if getattr(self, "plan", None) is None:
             self.plan = torch.empty(capi.workspace_size(capi.WS_MASKED_PLAN, self.shape),
                                     dtype=torch.uint8, device=self.device)
@@ -184,8 +187,9 @@ def rigl(layer: SparseMoELayer, grad: torch.Tensor, r: int, stream=None, ws=None
     new_m = torch.empty_like(layer.m)
     new_v = torch.empty_like(layer.v)
     stats = torch.zeros(3, dtype=torch.int64, device=layer.device)
+    new_w = torch.empty_like(layer.w_list)
     capi.rigl_reselect(layer.shape, grad, layer.W, layer.idx, layer.m, layer.v, k, r, new_idx,
-                       new_m, new_v, stats, ws, stream, old_w=layer.w_list)
+                       new_m, new_v, stats, ws, stream, old_w=layer.w_list, new_w=new_w)
     layer.idx, layer.m, layer.v = new_idx, new_m, new_v
-    layer.refresh_list()
+    layer.refresh_list(w_list=new_w)
     return stats

@@ -110,12 +110,15 @@ class _Layer:
         self.note_touched()
         self.refresh_list(act)
 
-    def refresh_list(self, act: int):
-        """The compact weight list SparseAdam reads and the masked gradient's
+    def refresh_list(self, act: int, w_list=None):
+        """The compact weight list SparseAdam reads (gathered, unless the
+        caller has it, as RigL's reselection does) and the masked gradient's
         plan, both rebuilt whenever the list changes."""
         k = self.idx.numel()
-        self.w_list = torch.empty(k, dtype=_dt(act), device=self.idx.device)
-        capi.gather(act, self.W, self.idx, k, self.w_list)
+        if w_list is None:
+            w_list = torch.empty(k, dtype=_dt(act), device=self.idx.device)
+            capi.gather(act, self.W, self.idx, k, w_list)
+        self.w_list = w_list
         if self.plan is None:
             self.plan = torch.empty(capi.workspace_size(capi.WS_MASKED_PLAN, self.shape),
                                     dtype=torch.uint8, device=self.idx.device)
@@ -292,11 +295,13 @@ class MoEStack:
             new_idx = torch.empty_like(lay.idx)
             new_m = torch.empty_like(lay.m)
             new_v = torch.empty_like(lay.v)
+            new_w = torch.empty_like(lay.w_list)
             capi.rigl_reselect(self.shape, grad, lay.W, lay.idx, lay.m, lay.v, k, r, new_idx,
-                               new_m, new_v, stats[l], self._ws_rigl, stream, old_w=lay.w_list)
+                               new_m, new_v, stats[l], self._ws_rigl, stream, old_w=lay.w_list,
+                               new_w=new_w)
             lay.idx, lay.m, lay.v = new_idx, new_m, new_v
             lay.note_touched()
-            lay.refresh_list(self.act)
+            lay.refresh_list(self.act, w_list=new_w)
 
         self.forward(stream)
         self.backward(select=reselect, stream=stream)

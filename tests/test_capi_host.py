@@ -124,11 +124,14 @@ def test_entry_points_refuse_bad_arguments_before_launch():
     assert L.usaf_importance_topk(FAKE, 100, 5, None, 0, FAKE, None, FAKE + 4, 1 << 20, None) == 2
     # rigl: r > k, k > N
     assert L.usaf_rigl_reselect(C.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, 10, 11, FAKE, FAKE,
-                                FAKE, None, FAKE, 1 << 30, None) == 1
+                                FAKE, None, None, FAKE, 1 << 30, None) == 1
     assert L.usaf_rigl_reselect(C.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, N + 1, 1, FAKE, FAKE,
-                                FAKE, None, FAKE, 1 << 30, None) == 1
+                                FAKE, None, None, FAKE, 1 << 30, None) == 1
+    # new_w needs old_w (the kept entries' weights come from it)
     assert L.usaf_rigl_reselect(C.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, 10, 3, FAKE, FAKE,
-                                FAKE, None, FAKE + 4, 1 << 40, None) == 2
+                                FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert L.usaf_rigl_reselect(C.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, 10, 3, FAKE, FAKE,
+                                FAKE, None, None, FAKE + 4, 1 << 40, None) == 2
     # adam: step < 1, bad dtype, n == 0 no-op
     f = C.c_double
     assert L.usaf_sparse_adam(1, FAKE, None, 10, None, FAKE, FAKE, FAKE, 0, f(1e-3), f(.9), f(.999), f(1e-8), None, None) == 1

@@ -393,13 +393,18 @@ def test_rigl_exact(capi, act, old_is_top, dims):
     # of them at the old list (SparseAdam's list)
     old_w = torch.empty(k, dtype=Wt.dtype, device=DEV)
     capi.gather(act, Wt, old_t, k, old_w)
+    new_w = torch.empty_like(old_w)
     for ow in (None, old_w):
         stats.zero_()
         capi.rigl_reselect(shape, g_t, Wt, old_t, torch.from_numpy(m).to(DEV),
                            torch.from_numpy(v).to(DEV), k, r, new_idx, new_m, new_v, stats, ws,
-                           old_w=ow)
+                           old_w=ow, new_w=None if ow is None else new_w)
         torch.cuda.synchronize()
         assert np.array_equal(npu32(new_idx), ref["S_new"])
+        if ow is not None:  # the new compact list is W at the new list
+            want = torch.empty_like(old_w)
+            capi.gather(act, Wt, new_idx, k, want)
+            assert torch.equal(new_w, want)
         assert np.array_equal(new_m.cpu().numpy(), ref["m"].astype(np.float32))
         assert np.array_equal(new_v.cpu().numpy(), ref["v"].astype(np.float32))
         s = stats.cpu().numpy()
