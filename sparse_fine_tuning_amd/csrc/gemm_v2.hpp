@@ -333,15 +333,35 @@ struct KMajorQ4 {
     }
     return make_uint4(o[0], o[1], o[2], o[3]);
   }
+  // The same weights by one fused multiply-add each, w = bf16(fma(q, s, -z s)),
+  // for rows where it is exact: with s > 0 finite and z finite, 0 or
+  // |z| >= 2^-10, q - z (q <= 15, z with at most 11 significant bits at
+  // weight >= 2^-20), z s (22 bits) and q s (15 bits) are all exact in
+  // fp32, so fma rounds the exact (q - z) s once, as fp32(fp32(q - z) s)
+  // does, and an exact zero comes out +0 in both (s > 0).
+  __device__ __forceinline__ static uint4 dequant8_fma(uint32_t code, float sc, float zs) {
+    const uint32_t lo = code & 0x0f0f0f0fu, hi = (code >> 4) & 0x0f0f0f0fu;
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = f2bf2(__builtin_fmaf(float((lo >> (8 * j)) & 0xffu), sc, -zs),
+                   __builtin_fmaf(float((hi >> (8 * j)) & 0xffu), sc, -zs));
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  __device__ __forceinline__ static bool fma_exact(float sc, float zr) {
+    const float az = __builtin_fabsf(zr);
+    return sc > 0.f && sc <= 65504.f && az <= 65504.f && (az == 0.f || az >= 0x1p-10f);
+  }
   // A thread's share of converting a stage: R rows x 2 halves of the
   // stage's 64 k over the block's 64 NW = 2 R threads, one each; load()
   // reads its 16 code bytes and the row's scale and zero, part(j) writes
   // 8 weights (bf16 chunk 4 h + j of the row)
   struct Conv {
     uint4 q;
-    float sc, zr;
+    float sc, zr, zs;
     unsigned char* dst;
     int r, h;
+    bool fast;  // wave-uniform: every lane's row takes the fused form
   };
   __device__ __forceinline__ Conv conv_load(int st, int tid) const {
     Conv c;
@@ -354,11 +374,14 @@ struct KMajorQ4 {
     c.sc = float(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb)));
     c.zr = float(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb + R * 4)));
     c.dst = tile_lds() + (st & 1) * kTileBuf + c.r * 128;
+    c.zs = c.zr * c.sc;
+    c.fast = __all(fma_exact(c.sc, c.zr));
     return c;
   }
   __device__ __forceinline__ static void conv_part(const Conv& c, int j) {
     const uint32_t qw = j == 0 ? c.q.x : j == 1 ? c.q.y : j == 2 ? c.q.z : c.q.w;
-    *reinterpret_cast<uint4*>(c.dst + 16 * ((4 * c.h + j) ^ Tile::sw(c.r))) = dequant8(qw, c.sc, c.zr);
+    *reinterpret_cast<uint4*>(c.dst + 16 * ((4 * c.h + j) ^ Tile::sw(c.r))) =
+        c.fast ? dequant8_fma(qw, c.sc, c.zs) : dequant8(qw, c.sc, c.zr);
   }
   __device__ __forceinline__ void convert(int st, int tid) const {
     const Conv c = conv_load(st, tid);

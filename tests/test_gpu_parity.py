@@ -646,6 +646,54 @@ def test_tiny_fp32_importance_then_three_steps(capi):
 # --------------------------------------------------------------------------
 # the pages' 4-bit storage, dequantised as the GEMMs load it
 # --------------------------------------------------------------------------
+def test_forward_q4_edge_scales_and_zeros(capi):
+    """The 4-bit forward converts a row by one fused multiply-add only where
+    that is exact (scale > 0 finite, zero 0 or |zero| >= 2^-10), otherwise as
+    fp32(fp32(q - z) s): rows with negative, zero and subnormal scales, tiny,
+    negative-zero, integer (q == z: exact zeros) and negative zeros, and zeros
+    on both sides of 2^-10, give the same bits as the resident dequant (which
+    equals the oracle's), in both weight tensors."""
+    from sparse_fine_tuning_amd.layer import SparseMoELayer
+    dims, group = (200, 256, 8, 2, 128), 64
+    T, H, E, K, I = dims
+    say(f"forward q4 edge scales dims={dims}")
+    d = synth.moe_layer(*dims, bf16=True, seeds=(95, 96, 97, 98, 99))
+    qg, sg, zg = synth.quantize_affine_int4(d["W_gu"].reshape(E * 2 * I, H), group)
+    qd, sd, zd = synth.quantize_affine_int4(d["W_d"].reshape(E * H, I), group)
+    edge = [(-0.5, None), (0.0, None), (2.0 ** -24, None), (0.25, 2.0 ** -12), (0.25, -0.0),
+            (0.125, 3.0), (0.125, -2.5), (0.0625, 2.0 ** -10), (0.0625, 2.0 ** -11),
+            (-0.25, 7.0), (0.5, 15.0)]
+    for sarr, zarr in ((sg, zg), (sd, zd)):
+        for i, (sv, zv) in enumerate(edge):
+            for row in (i, 37 + 5 * i, sarr.shape[0] - 1 - i):  # rows in several tiles and waves
+                sarr[row] = np.float16(sv).view(np.uint16)  # the arrays hold fp16 bits
+                if zv is not None:
+                    zarr[row] = np.float16(zv).view(np.uint16)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    i16 = lambda a: dev(np.ascontiguousarray(a).view(np.int16))
+    tq = [dev(qg), i16(sg), i16(zg), dev(qd), i16(sd), i16(zd)]
+    res = SparseMoELayer(*dims, act=capi.BF16, device=DEV)
+    res.load(d["X"], d["Wr"], np.zeros_like(d["W_gu"]), np.zeros_like(d["W_d"]), d["tgt"])
+    ngu = E * 2 * I * H
+    capi.dequant_affine(tq[0], tq[1], tq[2], E * 2 * I, H, group, res.W[:ngu])
+    capi.dequant_affine(tq[3], tq[4], tq[5], E * H, I, group, res.W[ngu:])
+    res.forward()
+    onl = SparseMoELayer(*dims, act=capi.BF16, device=DEV)
+    onl.X, onl.Wr = res.X, res.Wr
+    capi.moe_forward_q4(onl.shape, onl.X, onl.Wr, capi.q4_experts(*tq, group), onl.Y, onl.state,
+                        onl.ws_fwd)
+    torch.cuda.synchronize()
+    for name in ("gu", "a"):
+        assert torch.equal(res.st[name].view(torch.int16), onl.st[name].view(torch.int16)), name
+    assert torch.equal(res.Y.view(torch.int16), onl.Y.view(torch.int16))
+    W_gu = O.dequant_affine(qg, sg, zg, group)
+    W_d = O.dequant_affine(qd, sd, zd, group)
+    assert np.array_equal(bf16_bits(W_gu.ravel()),
+                          res.W[:ngu].view(torch.int16).cpu().numpy().view(np.uint16))
+    assert np.array_equal(bf16_bits(W_d.ravel()),
+                          res.W[ngu:].view(torch.int16).cpu().numpy().view(np.uint16))
+
+
 # (1024, 256, 4, 2, 128): 512 slots per expert on average, the 256-row tiles
 @pytest.mark.parametrize("dims,group", [((200, 256, 8, 2, 128), 64), ((333, 512, 16, 4, 384), 64),
                                         ((1024, 256, 4, 2, 128), 64),
