@@ -29,9 +29,9 @@
 // first 64 keys of every 4096 are histogrammed on 22 key bits (two levels of
 // 11), and the key at which the sample holds 1.25x its share of k (plus 16)
 // is taken as a threshold.  One full read (pass B1) then stores every key at
-// or above it as a candidate
-// (with a histogram of the candidates); the candidates are made contiguous
-// and the exact k-th composite is resolved on them as above, then written
+// or above it as a candidate; the candidates are made contiguous (with a
+// histogram of their top key bits) and the exact k-th composite is resolved
+// on them as above, then written
 // out in index order.  The result is exact whatever the sample says: if
 // fewer than k keys reach the threshold, pass B1 runs again with every key a
 // candidate (a device-gated retry, no host round trip).
@@ -845,10 +845,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 __global__ __launch_bounds__(256) void topk_pass_b1_kernel(const float* __restrict__ g, int64_t n,
                                                            TopkWs w, const uint32_t* gate) {
   if (gated_off(gate)) return;
-  __shared__ uint32_t h[kTopkBins];
   __shared__ uint32_t sidx[4][kStage], skey[4][kStage];
-  for (int b = threadIdx.x; b < kTopkBins; b += 256) h[b] = 0;
-  __syncthreads();
   const uint32_t thr = w.st[ST_T];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int64_t chunk = int64_t(blockIdx.x) * 4 + wid;
@@ -886,19 +883,22 @@ __global__ __launch_bounds__(256) void topk_pass_b1_kernel(const float* __restri
             si[p] = uint32_t(i + u);
             sk[p] = kv[u];
             ++p;
-            atomicAdd(&h[kv[u] >> 20], 1u);
           }
         }
         staged += tot;
       }
     };
-    if (i0 + kSuper <= n) {  // uniform: a full chunk, 4 loads of 16 bytes in flight per lane
-      constexpr int kAhead = 4;
-      for (int r0 = 0; r0 < kSuper / 256; r0 += kAhead) {
-        uint4 vv[kAhead];
+    if (i0 + kSuper <= n) {  // uniform: a full chunk
+      // rows in batches of kAhead 16-byte loads per lane, two batches in
+      // flight: batch b + 1 is loaded before batch b is processed
+      constexpr int kAhead = 4, kRows = kSuper / 256;
+      static_assert(kRows % (2 * kAhead) == 0, "whole pairs of batches");
+      auto load = [&](int r0, uint4 (&vv)[kAhead]) {
 #pragma unroll
         for (int a = 0; a < kAhead; ++a)
           vv[a] = *reinterpret_cast<const uint4*>(g + i0 + (r0 + a) * 256 + lane * 4);
+      };
+      auto process = [&](int r0, const uint4 (&vv)[kAhead]) {
 #pragma unroll
         for (int a = 0; a < kAhead; ++a) {
           const uint32_t kv[4] = {vv[a].x & 0x7fffffffu, vv[a].y & 0x7fffffffu,
@@ -906,6 +906,14 @@ __global__ __launch_bounds__(256) void topk_pass_b1_kernel(const float* __restri
           const bool c[4] = {kv[0] >= thr, kv[1] >= thr, kv[2] >= thr, kv[3] >= thr};
           row(i0 + (r0 + a) * 256 + lane * 4, kv, c);
         }
+      };
+      uint4 va[kAhead], vb[kAhead];
+      load(0, va);
+      for (int r0 = 0; r0 < kRows; r0 += 2 * kAhead) {
+        load(r0 + kAhead, vb);
+        process(r0, va);
+        if (r0 + 2 * kAhead < kRows) load(r0 + 2 * kAhead, va);  // uniform
+        process(r0 + kAhead, vb);
       }
     } else {  // the last, partial chunk
       for (int r = 0; r < kSuper / 256; ++r) {
@@ -929,10 +937,6 @@ __global__ __launch_bounds__(256) void topk_pass_b1_kernel(const float* __restri
       w.cnt[chunk] = stored;
     }
   }
-  __syncthreads();
-  uint32_t* dst = w.hist + size_t(blockIdx.x % kHistCopies) * kTopkBins;
-  for (int b = threadIdx.x; b < kTopkBins; b += 256)
-    if (h[b]) atomicAdd(&dst[b], h[b]);
 }
 
 // Fewer than k candidates (their total is st[NCAND], from the count scan):
@@ -953,6 +957,9 @@ __global__ __launch_bounds__(1024) void topk_retry_kernel(TopkWs w, uint32_t k) 
 // entries go to [cnt[c], cnt[c] + ccnt[c]) of above (indices) and cckey
 // (keys).  One wave per chunk.
 __global__ __launch_bounds__(256) void topk_compact_kernel(TopkWs w, int64_t nsup) {
+  __shared__ uint32_t h[kTopkBins];
+  for (int b = threadIdx.x; b < kTopkBins; b += 256) h[b] = 0;
+  __syncthreads();
   const int lane = threadIdx.x & 63;
   for (int64_t c = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); c < nsup;
        c += int64_t(gridDim.x) * 4) {
@@ -960,10 +967,16 @@ __global__ __launch_bounds__(256) void topk_compact_kernel(TopkWs w, int64_t nsu
     const uint32_t* src = w.cand + c * kSuper;
     const uint32_t* ksrc = w.ckey + c * kSuper;
     for (uint32_t j = lane; j < m; j += 64) {
+      const uint32_t key = ksrc[j];
       w.above[o + j] = src[j];
-      w.cckey[o + j] = ksrc[j];
+      w.cckey[o + j] = key;
+      atomicAdd(&h[key >> 20], 1u);  // the candidates' top 11 key bits
     }
   }
+  __syncthreads();
+  uint32_t* dst = w.hist + size_t(blockIdx.x % kHistCopies) * kTopkBins;
+  for (int b = threadIdx.x; b < kTopkBins; b += 256)
+    if (h[b]) atomicAdd(&dst[b], h[b]);
 }
 
 // Candidate rounds on the contiguous candidates (st[NCAND] of them):
