@@ -644,6 +644,8 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_kernel(P p) {
   constexpr int NLOAD = AOp::kInstMin + BOp::kInstMin;  // the fewest any wave issues per stage
   static_assert((NS - 2) * NLOAD < 64, "vmcnt");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[NS][A_BYTES + B_BYTES];
+  static_assert(P::kStageBytes * (P::NTHR / 64) <= NS * (A_BYTES + B_BYTES),
+                "every wave's epilogue staging region lies in the ring");
   MTile t;
   if (!p.tile(xcd_remap_blocks(blockIdx.x, gridDim.x), t)) return;
   const int tid = threadIdx.x, lane = tid & 63;
