@@ -44,33 +44,33 @@ WRITE_SCALE = 1.0   # and 1,048,576 KiB of WRITE_SIZE
 # staging and the two GEMMs of one scan; topk_fresh sums every launch of the
 # scan's first selection (sample, full read, compaction, candidate rounds,
 # emit).
-G = "9fb9f79010128068"  # the GEMM sources
+G = "8f25601fde1b0a8f"  # the GEMM sources
 COUNTER_TRAFFIC = {
     "qwen3_step": {
         "router_gemm": (8788, 16384, G),
-        "gate_up": (470381, 147461, G),
-        "down": (221377, 131072, G),
-        "da": (320109, 100105, G),
-        "dx": (563591, 131072, G),
-        "masked_dw": (168993, 11803, "392f30b300880270"),
-        "adam": (28622, 123522, "a431573056f07bd3"),
+        "gate_up": (470345, 147460, G),
+        "down": (221373, 131072, G),
+        "da": (337930, 100123, G),
+        "dx": (631654, 131072, G),
+        "masked_dw": (168661, 12827, "4b2b9fc26f8747eb"),
+        "adam": (28622, 123523, "a431573056f07bd3"),
     },
     "qwen3_scan": {
-        "dense_dw": (882812, 2883584, G),
-        "topk_fresh": (1338673, 102477, "21132fbfaed0c251"),
+        "dense_dw": (879892, 2883584, G),
+        "topk_fresh": (1338698, 102138, "86e77014bed80652"),
     },
     "mixtral_step": {
         "router_gemm": (16526, 1024, G),
-        "gate_up": (1936804, 702943, G),
-        "down": (1133573, 68064, G),
-        "da": (2271705, 468189, G),
-        "dx": (2471086, 78256, G),
-        "masked_dw": (762941, 45065, "392f30b300880270"),
-        "adam": (62219, 281415, "a431573056f07bd3"),
+        "gate_up": (1992693, 702975, G),
+        "down": (1162797, 68064, G),
+        "da": (2251383, 468195, G),
+        "dx": (2465877, 78256, G),
+        "masked_dw": (773899, 45646, "4b2b9fc26f8747eb"),
+        "adam": (62219, 281414, "a431573056f07bd3"),
     },
     "mixtral_scan": {
-        "dense_dw": (4899516, 5636096, G),
-        "topk_fresh": (3122493, 220993, "21132fbfaed0c251"),
+        "dense_dw": (4899947, 5636096, G),
+        "topk_fresh": (3122522, 220163, "86e77014bed80652"),
     },
 }
 KERNEL_SOURCES = {
