@@ -34,6 +34,8 @@ struct MTile {
   int kb, ke;  // contraction range [kb, ke)
   int off;     // expert-major row offset of the group
   int nt;      // column-tile index
+  int part = 0, nparts = 1;  // a contraction part of a split tail tile: part of nparts
+  int tidx = 0;              // the tail tile's index among the split ones
 };
 
 // Logical tile ids are XCD-remapped (xcd_remap_blocks) so tiles that share

@@ -32,6 +32,7 @@
 // Epilogues therefore read and write 4-column vectors per lane.
 #pragma once
 
+#include <climits>
 #include <type_traits>
 #include <utility>
 
@@ -115,6 +116,135 @@ __device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ offsets
   t.mc = min(q, cnt - t.m0);
   t.off = sh[3];
   return true;
+}
+
+// Tiles of all groups (the grouped_tile numbering), block-uniform.
+template <int BM>
+__device__ __forceinline__ int grouped_count(const int32_t* __restrict__ offsets, int E, int NT) {
+  __shared__ int total;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int sum = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+      int tiles = cnt > 0 ? ((cnt + row_tile<BM>(cnt) - 1) / row_tile<BM>(cnt)) * NT : 0;
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) tiles += __shfl_xor(tiles, d, 64);
+      sum += tiles;
+    }
+    if (lane == 0) total = sum;
+  }
+  __syncthreads();
+  const int t = total;
+  __syncthreads();  // the next call may overwrite it
+  return t;
+}
+
+// Problems that opt in (static constexpr bool kTailSplit = true) provide
+// SplitWs sk, TailSplit split() and tile(L, t, plan), which numbers split
+// units; the kernels compute the plan once per block.
+template <class P, class = void>
+struct TailSplitOf {
+  static constexpr bool value = false;
+};
+template <class P>
+struct TailSplitOf<P, std::void_t<decltype(P::kTailSplit)>> {
+  static constexpr bool value = P::kTailSplit;
+};
+
+// Tail split of a persistent launch of G blocks over T tiles: when at least
+// one full round of G tiles runs and the last round is at most half full,
+// its tail = T mod G tiles are each cut into S <= 4 contraction parts (S tail
+// <= G, S tail <= cap, S <= the tile's stages), so that the idle blocks of
+// the last round share them.  Units: the full rounds' tiles in order, then
+// tail tile i's parts as units full + S i + part.
+// The plan depends on the persistent grid's size G.  No split: full = INT_MAX.
+struct TailSplit {
+  int full, tail, S;
+};
+// Partial buffer of a split launch: cap units of one tile's fp32
+// accumulators; grid: the persistent launch's block count.
+struct SplitWs {
+  float* ws = nullptr;
+  int cap = 0;
+  int grid = 0;
+};
+template <int BM, int BK>
+__device__ __forceinline__ TailSplit grouped_split_plan(const int32_t* __restrict__ offsets, int E,
+                                                        int NT, int K, const SplitWs& sk) {
+  TailSplit p{INT_MAX, 0, 1};
+  const int cap = sk.cap;
+  if (cap < 2) return p;  // uniform
+  const int T = grouped_count<BM>(offsets, E, NT), G = sk.grid;
+  const int nk = (K + BK - 1) / BK;
+  const int R = T / G, rem = T - R * G;
+  if (R >= 1 && rem > 0 && 2 * rem <= G) {
+    const int S = min(min(4, G / rem), min(cap / rem, nk));
+    if (S >= 2) p = TailSplit{R * G, rem, S};
+  }
+  return p;
+}
+// Unit L of a grouped problem with contraction K (stages of BK) split by
+// plan sp; false past the last unit.  A part covers stages
+// [part nk / S, (part + 1) nk / S) of the tile, as [kb, ke).
+template <int BM, int BK>
+__device__ __forceinline__ bool grouped_split_tile(const int32_t* __restrict__ offsets, int E, int NT,
+                                                   int L, int K, const TailSplit& sp, MTile& t) {
+  const int nk = (K + BK - 1) / BK;
+  int tl = L, part = 0;
+  if (L >= sp.full) {
+    const int j = L - sp.full;
+    if (j >= sp.tail * sp.S) return false;
+    tl = sp.full + j / sp.S;
+    part = j % sp.S;
+  }
+  if (!grouped_tile<BM>(offsets, E, NT, tl, t)) return false;
+  t.kb = 0;
+  t.ke = K;
+  t.nparts = 1;
+  if (tl >= sp.full) {
+    t.nparts = sp.S;
+    t.part = part;
+    t.tidx = tl - sp.full;
+    t.kb = BK * (part * nk / sp.S);
+    t.ke = min(K, BK * ((part + 1) * nk / sp.S));
+  }
+  return true;
+}
+
+// A split part's fp32 accumulators, raw (the MFMA layout, per thread), at
+// unit u = tidx S + part of the partial buffer: float4 f of thread x at
+// ((u F4 + f) NTHR + x), F4 = IM NJ 4 per thread.
+template <int NTHR, int IM, int NJ>
+__device__ __forceinline__ void store_partial(float* ws, int u, const f32x16_t (&acc)[IM][NJ], int tid) {
+  constexpr int F4 = IM * NJ * 4;
+  float4* dst = reinterpret_cast<float4*>(ws) + int64_t(u) * F4 * NTHR + tid;
+#pragma unroll
+  for (int i = 0; i < IM; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        dst[((i * NJ + j) * 4 + q) * NTHR] =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+}
+template <int NTHR, int IM, int NJ>
+__device__ __forceinline__ void add_partial(const float* ws, int u, f32x16_t (&acc)[IM][NJ], int tid) {
+  constexpr int F4 = IM * NJ * 4;
+  const float4* src = reinterpret_cast<const float4*>(ws) + int64_t(u) * F4 * NTHR + tid;
+#pragma unroll
+  for (int i = 0; i < IM; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = src[((i * NJ + j) * 4 + q) * NTHR];
+        acc[i][j][4 * q] += v.x;
+        acc[i][j][4 * q + 1] += v.y;
+        acc[i][j][4 * q + 2] += v.z;
+        acc[i][j][4 * q + 3] += v.w;
+      }
 }
 
 // CW: columns of the tile held by one wave
@@ -369,7 +499,7 @@ struct KMajorQ4 {
     c.h = tid & 1;
     const int b = st % 3;
     c.q = *reinterpret_cast<const uint4*>(code_lds() + b * kCodeBuf + c.r * 32 + 16 * c.h);
-    const int half = ((st << 6) >> gshift) & 1;  // the stage's group within its pair
+    const int half = (((st + kst0) << 6) >> gshift) & 1;  // the stage's group within its pair
     const unsigned char* sb = scale_lds() + b * kScaleBuf + c.r * 4 + 2 * half;
     c.sc = float(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb)));
     c.zr = float(__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb + R * 4)));
@@ -391,12 +521,14 @@ struct KMajorQ4 {
   const unsigned char* cptr;   // the lane's code row at its 16-byte chunk
   const uint16_t* sptr;        // the lane's scale or zero row
   int gshift, kg, last;        // last: the tile's last stage
+  int kst0;                    // the row's stage of the tile's stage 0 (a contraction part's start)
   template <class Src>
   __device__ __forceinline__ void init(const Src& s, int kend, int w, int lane) {
     gshift = s.gshift;
     kg = s.kg;
     last = kend / 64 - 1;
-    cptr = s.q + s.code_row(32 * w + (lane >> 1)) * s.qpitch + 16 * (lane & 1);
+    kst0 = s.kst0;
+    cptr = s.q + s.code_row(32 * w + (lane >> 1)) * s.qpitch + 32 * kst0 + 16 * (lane & 1);
     const int sr = 64 * (w % (NW / 2)) + lane;  // scales: waves 0 .. NW/2 - 1, zeros: the rest
     sptr = (w < NW / 2 ? s.s : s.z) + s.code_row(sr % R) * s.kg;
   }
@@ -405,7 +537,7 @@ struct KMajorQ4 {
     const int b = st % 3;
     const int sc = min(st, last);
     dma16(cptr + 32 * sc, code_lds() + b * kCodeBuf + w * 1024);
-    const int pair = ((sc << 6) >> gshift) & ~1;
+    const int pair = (((sc + kst0) << 6) >> gshift) & ~1;
     dma4(sptr + pair, scale_lds() + b * kScaleBuf + (w >= NW / 2 ? R * 4 : 0) + (w % (NW / 2)) * 256);
   }
   // the batch of ring stage kt carries stage kt + 1's codes
@@ -696,18 +828,26 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_persistent(P p)
   __shared__ __attribute__((aligned(1024))) unsigned char lds[NS][A_BYTES + B_BYTES];
   const int G = gridDim.x;
   int L = xcd_remap_blocks(blockIdx.x, G);
+  TailSplit plan{INT_MAX, 0, 1};
+  if constexpr (TailSplitOf<P>::value) plan = p.split();
+  auto tile = [&](int l, MTile& tt) {
+    if constexpr (TailSplitOf<P>::value) return p.tile(l, tt, plan);
+    else return p.tile(l, tt);
+  };
   MTile t;
-  if (!p.tile(L, t)) return;
+  if (!tile(L, t)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w / P::WN, wn = w % P::WN;
+  // a tile's contraction is [kb, ke): the sources start at kb
   auto as = p.a_src(t);
   auto bs = p.b_src(t);
   AOp ao;
   BOp bo;
-  ao.init(as, t.ke, w, lane);
-  bo.init(bs, t.ke, w, lane);
-  int nk = (t.ke + AOp::kBK - 1) / AOp::kBK;
+  int klen = t.ke - t.kb;
+  ao.init(as, klen, w, lane);
+  bo.init(bs, klen, w, lane);
+  int nk = (klen + AOp::kBK - 1) / AOp::kBK;
   if constexpr (BOp::kConvert) bo.issue_first(bs, w);
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
@@ -738,18 +878,19 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_persistent(P p)
     vb = __builtin_amdgcn_readfirstlane(vb);
     static_for<IM + 1>([&](auto V_) {
       constexpr int v = decltype(V_)::value;
-      if (vb == v) main_loop<P, v, IM, NJ>(ao, bo, as, bs, lds, t.ke, nk, tid, w, r0, wn, lane, acc);
+      if (vb == v) main_loop<P, v, IM, NJ>(ao, bo, as, bs, lds, klen, nk, tid, w, r0, wn, lane, acc);
     });
     __syncthreads();  // every wave is done with the ring
     MTile tn;
     L += G;
-    const bool more = p.tile(L, tn);
+    const bool more = tile(L, tn);
     if (more) {
       as = p.a_src(tn);
       bs = p.b_src(tn);
-      ao.init(as, tn.ke, w, lane);
-      bo.init(bs, tn.ke, w, lane);
-      nk = (tn.ke + AOp::kBK - 1) / AOp::kBK;
+      klen = tn.ke - tn.kb;
+      ao.init(as, klen, w, lane);
+      bo.init(bs, klen, w, lane);
+      nk = (klen + AOp::kBK - 1) / AOp::kBK;
       if constexpr (BOp::kConvert) bo.issue_first(bs, w);
 #pragma unroll
       for (int s = 0; s < NS - 1; ++s)
@@ -762,10 +903,44 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_persistent(P p)
     // prologue leaves free (its first stage refills it only after a barrier
     // every wave reaches after its epilogue)
     unsigned char* pst = P::kPStage ? &lds[NS - 1][0] + w * P::kPStage : nullptr;
-    p.epilogue(t, acc, wm, wn, lane, pst);
+    if constexpr (TailSplitOf<P>::value) {
+      // a part of a split tile leaves its raw sums for gemm2_split_reduce
+      if (t.nparts > 1)
+        store_partial<P::NTHR, IM, NJ>(p.sk.ws, t.tidx * t.nparts + t.part, acc, tid);
+      else
+        p.epilogue(t, acc, wm, wn, lane, pst);
+    } else {
+      p.epilogue(t, acc, wm, wn, lane, pst);
+    }
     if (!more) break;
     t = tn;
   }
+}
+
+// The tiles a persistent launch split (grouped_split_plan): one wave per
+// block, block x = NW b + w for wave w of tail tile b (at most G NW blocks),
+// adds that wave's accumulators over the tile's parts in part order and
+// runs its share of the problem's epilogue (epilogues work per wave).
+template <class P>
+__global__ __launch_bounds__(64) void gemm2_split_reduce(P p) {
+  constexpr int IM = P::IM, NJ = P::NJ, NW = P::NTHR / 64;
+  constexpr int kStage = P::kPStage > 0 ? P::kPStage : 16;
+  __shared__ __attribute__((aligned(16))) unsigned char stage[kStage];
+  const TailSplit sp = p.split();
+  const int b = blockIdx.x / NW, w = blockIdx.x % NW;
+  if (b >= sp.tail) return;
+  MTile t;
+  if (!p.tile(sp.full + b * sp.S, t, sp)) return;
+  const int lane = threadIdx.x, tid = 64 * w + lane;
+  f32x16_t acc[IM][NJ];
+#pragma unroll
+  for (int i = 0; i < IM; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  for (int q = 0; q < sp.S; ++q) add_partial<P::NTHR, IM, NJ>(p.sk.ws, b * sp.S + q, acc, tid);
+  p.epilogue(t, acc, w / P::WN, w % P::WN, lane, P::kPStage > 0 ? stage : nullptr);
 }
 
 }  // namespace g2

@@ -1056,7 +1056,9 @@ static usaf_status forward_impl(const usaf_moe_shape& s, const T* X, const float
   if constexpr (kMfma) {
     USAF_TRY(mfma_gate_up(s, X, Wgu, st.offsets, st.perm, static_cast<T*>(st.gu),
                           static_cast<T*>(st.a), stream));
-    USAF_TRY(mfma_down(s, static_cast<const T*>(st.a), Wd, st.offsets, ybuf, stream));
+    USAF_TRY(mfma_down(s, static_cast<const T*>(st.a), Wd, st.offsets, ybuf,
+                       reinterpret_cast<float*>(ws + L.ybuf + bf16_spare_offset(s)),
+                       bf16_spare_offset(s), stream));
   } else {
     GateUpFwd<T> gp{X, Wgu, st.offsets, st.perm, static_cast<T*>(st.gu), static_cast<T*>(st.a),
                     s.H, s.E, s.K, s.I};
@@ -1123,7 +1125,9 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
   USAF_LAUNCH_CHECK();
   if (dX) {
     if constexpr (kMfma) {
-      USAF_TRY(mfma_dx(s, dgu, Wgu, st.offsets, vbuf, stream));
+      USAF_TRY(mfma_dx(s, dgu, Wgu, st.offsets, vbuf,
+                       reinterpret_cast<float*>(ws + L.vbuf + bf16_spare_offset(s)),
+                       bf16_spare_offset(s), stream));
     } else {
       DxBwd<T> dx{dgu, Wgu, st.offsets, vbuf, s.H, s.E, s.I};
       USAF_TRY(launch_fma(dx, dim3(mtiles_bound(s), unsigned(s.H / 64)), stream, USAF_K_DX));
@@ -1252,7 +1256,9 @@ extern "C" usaf_status usaf_moe_forward_q4(const usaf_moe_shape* shape, const vo
   USAF_TRY(route_impl(s, parts, nparts, st, stream));
   USAF_TRY(q4_gate_up(s, Xb, *w, st.offsets, st.perm, static_cast<bf16_t*>(st.gu),
                       static_cast<bf16_t*>(st.a), stream));
-  USAF_TRY(q4_down(s, static_cast<const bf16_t*>(st.a), *w, st.offsets, ybuf, stream));
+  USAF_TRY(q4_down(s, static_cast<const bf16_t*>(st.a), *w, st.offsets, ybuf,
+                   reinterpret_cast<float*>(wsc + L.ybuf + bf16_spare_offset(s)),
+                   bf16_spare_offset(s), stream));
   timer_begin(USAF_K_COMBINE_Y, stream);
   hipLaunchKernelGGL(combine_y_kernel<bf16_t>, dim3(unsigned(s.T)), dim3(256), 0, stream, ybuf,
                      st.topk_w, st.slot_pos, s.H, s.K, static_cast<bf16_t*>(Y));

@@ -41,9 +41,12 @@ inline usaf_status check_shape(const usaf_moe_shape* s) {
 
 // Forward workspace: expert outputs before the combine, [S, H] in the
 // activation dtype (sized for fp32; also holds the router split-K partials).
+// bf16 layers keep the down GEMM's split partials in the second half.
 struct WsForward {
   size_t ybuf, total;
 };
+// The half of an [S, H] fp32-sized region that bf16 rows leave free.
+inline size_t bf16_spare_offset(const usaf_moe_shape& s) { return size_t(s.T) * s.K * s.H * 2; }
 inline WsForward ws_forward(const usaf_moe_shape& s) {
   WsForward L;
   const size_t S = size_t(s.T) * s.K;
@@ -94,15 +97,19 @@ inline int mfma_router_splits(const usaf_moe_shape& s) {
 usaf_status mfma_gate_up(const usaf_moe_shape& s, const uint16_t* X, const uint16_t* Wgu,
                          const int32_t* offsets, const int32_t* perm, uint16_t* gu, uint16_t* a,
                          hipStream_t st);
+// split_ws: split_bytes of scratch for the tail split's fp32 partials
+// (none: no split); not ybuf.
 usaf_status mfma_down(const usaf_moe_shape& s, const uint16_t* a, const uint16_t* Wd,
-                      const int32_t* offsets, uint16_t* ybuf, hipStream_t st);
+                      const int32_t* offsets, uint16_t* ybuf, float* split_ws, size_t split_bytes,
+                      hipStream_t st);
 int mfma_dw_partials(const usaf_moe_shape& s);
 usaf_status mfma_da(const usaf_moe_shape& s, const uint16_t* dY, const uint16_t* Wd,
                     const int32_t* offsets, const int32_t* perm, const float* topk_w,
                     const uint16_t* gu, const uint16_t* a, uint16_t* dgu, float* dwpart,
                     hipStream_t st);
 usaf_status mfma_dx(const usaf_moe_shape& s, const uint16_t* dgu, const uint16_t* Wgu,
-                    const int32_t* offsets, uint16_t* vbuf, hipStream_t st);
+                    const int32_t* offsets, uint16_t* vbuf, float* split_ws, size_t split_bytes,
+                    hipStream_t st);
 // stage: S*H*2 bf16 scratch (the backward workspace's vbuf) for the
 // expert-major gathered X and w*dY operands.
 usaf_status mfma_dense_dw(const usaf_moe_shape& s, const uint16_t* X, const uint16_t* dY,
@@ -129,5 +136,6 @@ usaf_status q4_gate_up(const usaf_moe_shape& s, const uint16_t* X, const usaf_q4
                        const int32_t* offsets, const int32_t* perm, uint16_t* gu, uint16_t* a,
                        hipStream_t st);
 usaf_status q4_down(const usaf_moe_shape& s, const uint16_t* a, const usaf_q4_experts& w,
-                    const int32_t* offsets, uint16_t* ybuf, hipStream_t st);
+                    const int32_t* offsets, uint16_t* ybuf, float* split_ws, size_t split_bytes,
+                    hipStream_t st);
 }  // namespace usaf

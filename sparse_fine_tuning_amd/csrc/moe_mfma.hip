@@ -241,16 +241,21 @@ struct MDown {
   using BOp = KMajor<BN, WM_ * WN_, BK_>;
   const bf16_t* a; const bf16_t* Wd; const int32_t* offsets; bf16_t* ybuf;
   int H, E, I, NT;
-  __device__ __forceinline__ bool tile(int L, MTile& t) const {
-    if (!grouped_tile<BM>(offsets, E, NT, L, t)) return false;
-    t.kb = 0; t.ke = I; t.n0 = t.nt * BN; t.nc = min(BN, H - t.n0);
+  SplitWs sk;  // tail split partials (none: no split)
+  static constexpr bool kTailSplit = true;
+  __device__ __forceinline__ TailSplit split() const {
+    return grouped_split_plan<BM, BK_>(offsets, E, NT, I, sk);
+  }
+  __device__ __forceinline__ bool tile(int L, MTile& t, const TailSplit& plan) const {
+    if (!grouped_split_tile<BM, BK_>(offsets, E, NT, L, I, plan, t)) return false;
+    t.n0 = t.nt * BN; t.nc = min(BN, H - t.n0);
     return true;
   }
   __device__ __forceinline__ PlainRowsC a_src(const MTile& t) const {
-    return PlainRowsC{a + int64_t(t.off + t.m0) * I, I, t.mc};
+    return PlainRowsC{a + int64_t(t.off + t.m0) * I + t.kb, I, t.mc};
   }
   __device__ __forceinline__ PlainRowsC b_src(const MTile& t) const {
-    return PlainRowsC{Wd + (int64_t(t.e) * H + t.n0) * I, I, t.nc};
+    return PlainRowsC{Wd + (int64_t(t.e) * H + t.n0) * I + t.kb, I, t.nc};
   }
   // staging through one ring stage, where the wave's block fits there
   static constexpr int kPStage = ((CW == 32 || CW == 64) &&
@@ -279,6 +284,7 @@ struct Q4Codes {
   int64_t qpitch;  // bytes per code row (K / 2)
   int kg;          // groups per row (K / G)
   int gshift;      // log2(G)
+  int kst0 = 0;    // first 64-wide stage of the tile's contraction
 };
 // gate_up code rows in the feature order of GateUpRowsC
 template <int CW>
@@ -318,7 +324,9 @@ struct MDownQ4 : MDown<BM_, BN_, NS_, WM_, WN_, 64> {
   static constexpr int kStageBytes = kPStage;
   Q4Codes c;
   __device__ __forceinline__ RowCodesC b_src(const MTile& t) const {
-    return RowCodesC{c, int64_t(t.e) * this->H + t.n0, t.nc};
+    RowCodesC r{c, int64_t(t.e) * this->H + t.n0, t.nc};
+    r.kst0 = t.kb / 64;
+    return r;
   }
 };
 
@@ -505,16 +513,21 @@ struct MDx {
   using BOp = MNMajor<BN, WM_ * WN_, BK_>;
   const bf16_t* dgu; const bf16_t* Wgu; const int32_t* offsets; bf16_t* vbuf;
   int H, E, I, NT;
-  __device__ __forceinline__ bool tile(int L, MTile& t) const {
-    if (!grouped_tile<BM>(offsets, E, NT, L, t)) return false;
-    t.kb = 0; t.ke = 2 * I; t.n0 = t.nt * BN; t.nc = min(BN, H - t.n0);
+  SplitWs sk;  // tail split partials (none: no split)
+  static constexpr bool kTailSplit = true;
+  __device__ __forceinline__ TailSplit split() const {
+    return grouped_split_plan<BM, BK_>(offsets, E, NT, 2 * I, sk);
+  }
+  __device__ __forceinline__ bool tile(int L, MTile& t, const TailSplit& plan) const {
+    if (!grouped_split_tile<BM, BK_>(offsets, E, NT, L, 2 * I, plan, t)) return false;
+    t.n0 = t.nt * BN; t.nc = min(BN, H - t.n0);
     return true;
   }
   __device__ __forceinline__ PlainRowsC a_src(const MTile& t) const {
-    return PlainRowsC{dgu + int64_t(t.off + t.m0) * 2 * I, 2 * I, t.mc};
+    return PlainRowsC{dgu + int64_t(t.off + t.m0) * 2 * I + t.kb, 2 * I, t.mc};
   }
   __device__ __forceinline__ StridedKC b_src(const MTile& t) const {
-    return StridedKC{Wgu + int64_t(t.e) * 2 * I * H + t.n0, H, t.nc};
+    return StridedKC{Wgu + (int64_t(t.e) * 2 * I + t.kb) * H + t.n0, H, t.nc};
   }
   // staging through one ring stage, where the wave's block fits there
   static constexpr int kPStage = ((CW == 32 || CW == 64) &&
@@ -676,6 +689,31 @@ static usaf_status launch_persistent(const P& p, int64_t tiles, hipStream_t st, 
   return USAF_OK;
 }
 
+// The same with the tail split (grouped_split_plan) of a problem that opts
+// in, given split_bytes of partial buffer at split_ws: the persistent
+// launch, then the reduction of the split tiles on the same grid.
+template <class P>
+static usaf_status launch_persistent_split(P p, int64_t tiles, float* split_ws, size_t split_bytes,
+                                           hipStream_t st, int kclass) {
+  if (tiles <= 0) return USAF_OK;
+  const size_t unit = size_t(P::NTHR) * P::IM * P::NJ * 16 * 4;  // a tile's accumulators
+  const size_t cap = split_ws ? split_bytes / unit : 0;
+  int64_t blocks = int64_t(P::kBlocksPerCU) * device_cus();
+  if (blocks > tiles) blocks = tiles;
+  blocks = (blocks + 7) / 8 * 8;
+  p.sk = g2::SplitWs{split_ws, int(cap < size_t(1 << 20) ? cap : size_t(1 << 20)), int(blocks)};
+  timer_begin(kclass, st);
+  hipLaunchKernelGGL(g2::gemm2_persistent<P>, dim3(unsigned(blocks)), dim3(P::NTHR), 0, st, p);
+  USAF_LAUNCH_CHECK();
+  if (p.sk.cap >= 2) {  // the tail is at most half the grid: (G / 2) NW one-wave blocks
+    const int64_t rblocks = (blocks / 2) * (P::NTHR / 64);
+    hipLaunchKernelGGL(g2::gemm2_split_reduce<P>, dim3(unsigned(rblocks)), dim3(64), 0, st, p);
+    USAF_LAUNCH_CHECK();
+  }
+  timer_end(kclass, st);
+  return USAF_OK;
+}
+
 static int64_t grouped_tiles_bound(const usaf_moe_shape& s, int NT, int BM = kMB) {
   return (ceil_div(int64_t(s.T) * s.K, BM) + s.E) * NT;
 }
@@ -723,9 +761,16 @@ usaf_status mfma_gate_up(const usaf_moe_shape& s, const bf16_t* X, const bf16_t*
 }
 
 usaf_status mfma_down(const usaf_moe_shape& s, const bf16_t* a, const bf16_t* Wd,
-                      const int32_t* offsets, bf16_t* ybuf, hipStream_t st) {
+                      const int32_t* offsets, bf16_t* ybuf, float* split_ws, size_t split_bytes,
+                      hipStream_t st) {
   const int NT = int(ceil_div(s.H, kFwdBN));
-  return launch_fwd<g2::MDown>(s, NT, st, USAF_K_DOWN, a, Wd, offsets, ybuf, s.H, s.E, s.I, NT);
+  if (big_groups(s))
+    return launch_persistent_split(
+        g2::MDown<kBigBM, kFwdBN, kBigNS, kBigWM, kBigWN, kBigBK>{a, Wd, offsets, ybuf, s.H, s.E, s.I, NT},
+        grouped_tiles_bound(s, NT, kBigBM), split_ws, split_bytes, st, USAF_K_DOWN);
+  return launch_persistent_split(
+      g2::MDown<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN, kFwdBK>{a, Wd, offsets, ybuf, s.H, s.E, s.I, NT},
+      grouped_tiles_bound(s, NT, kFwdBM), split_ws, split_bytes, st, USAF_K_DOWN);
 }
 
 int mfma_dw_partials(const usaf_moe_shape& s) { return kDaWN * int(ceil_div(s.I, kFwdBN)); }
@@ -743,9 +788,16 @@ usaf_status mfma_da(const usaf_moe_shape& s, const bf16_t* dY, const bf16_t* Wd,
 }
 
 usaf_status mfma_dx(const usaf_moe_shape& s, const bf16_t* dgu, const bf16_t* Wgu,
-                    const int32_t* offsets, bf16_t* vbuf, hipStream_t st) {
+                    const int32_t* offsets, bf16_t* vbuf, float* split_ws, size_t split_bytes,
+                    hipStream_t st) {
   const int NT = int(ceil_div(s.H, kFwdBN));
-  return launch_fwd<g2::MDx>(s, NT, st, USAF_K_DX, dgu, Wgu, offsets, vbuf, s.H, s.E, s.I, NT);
+  if (big_groups(s))
+    return launch_persistent_split(
+        g2::MDx<kBigBM, kFwdBN, kBigNS, kBigWM, kBigWN, kBigBK>{dgu, Wgu, offsets, vbuf, s.H, s.E, s.I, NT},
+        grouped_tiles_bound(s, NT, kBigBM), split_ws, split_bytes, st, USAF_K_DX);
+  return launch_persistent_split(
+      g2::MDx<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN, kFwdBK>{dgu, Wgu, offsets, vbuf, s.H, s.E, s.I, NT},
+      grouped_tiles_bound(s, NT, kFwdBM), split_ws, split_bytes, st, USAF_K_DX);
 }
 
 usaf_status mfma_dense_dw(const usaf_moe_shape& s, const bf16_t* X, const bf16_t* dY,
@@ -805,17 +857,26 @@ usaf_status q4_gate_up(const usaf_moe_shape& s, const bf16_t* X, const usaf_q4_e
 }
 
 usaf_status q4_down(const usaf_moe_shape& s, const bf16_t* a, const usaf_q4_experts& w,
-                    const int32_t* offsets, bf16_t* ybuf, hipStream_t st) {
+                    const int32_t* offsets, bf16_t* ybuf, float* split_ws, size_t split_bytes,
+                    hipStream_t st) {
+  // the same tiles, grid and tail split as mfma_down: the same sums in the
+  // same order
   const int NT = int(ceil_div(s.H, kFwdBN));
   const g2::Q4Codes c{w.q_d, w.s_d, w.z_d, s.I / 2, s.I / w.group, log2_exact(w.group)};
   if (big_groups(s)) {
     using P = g2::MDownQ4<kBigBM, kFwdBN, kQ4BigNS, kBigWM, kBigWN>;
+    static_assert(P::kBlocksPerCU == g2::MDown<kBigBM, kFwdBN, kBigNS, kBigWM, kBigWN, kBigBK>::kBlocksPerCU,
+                  "the 4-bit and bf16 down launches share their grid");
     const P p{{a, nullptr, offsets, ybuf, s.H, s.E, s.I, NT}, c};
-    return launch_persistent(p, grouped_tiles_bound(s, NT, kBigBM), st, USAF_K_DOWN);
+    return launch_persistent_split(p, grouped_tiles_bound(s, NT, kBigBM), split_ws, split_bytes, st,
+                                   USAF_K_DOWN);
   }
   using P = g2::MDownQ4<kFwdBM, kFwdBN, kQ4NS, kFwdWM, kFwdWN>;
+  static_assert(P::kBlocksPerCU == g2::MDown<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN, kFwdBK>::kBlocksPerCU,
+                "the 4-bit and bf16 down launches share their grid");
   const P p{{a, nullptr, offsets, ybuf, s.H, s.E, s.I, NT}, c};
-  return launch_persistent(p, grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DOWN);
+  return launch_persistent_split(p, grouped_tiles_bound(s, NT, kFwdBM), split_ws, split_bytes, st,
+                                 USAF_K_DOWN);
 }
 
 }  // namespace usaf
