@@ -101,9 +101,11 @@ constexpr int kHdrTiles = 0, kHdrTarget = 2, kHdrNnz = 4, kHdrPtr = 6, kHdrFirst
 __global__ __launch_bounds__(256) void masked_plan_kernel(const uint32_t* __restrict__ idx,
                                                           int64_t nnz, SegLayout Lq,
                                                           uint32_t* __restrict__ seg,
-                                                          int* __restrict__ tile_counters) {
+                                                          int* __restrict__ tile_counters,
+                                                          int* __restrict__ ng, int ngroups) {
   const int64_t q = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (q < 2) tile_counters[kHdrTiles + q] = 0;  // the tile builders append after this kernel
+  if (q < ngroups) ng[q] = 0;                   // the group totals add into these
   if (q == 0) {
     uint32_t* hdr = reinterpret_cast<uint32_t*>(tile_counters);
     hdr[kHdrNnz] = uint32_t(uint64_t(nnz));
@@ -261,30 +263,41 @@ __device__ __forceinline__ void stage_store(const StageRole& R, StageRegs sr, in
     *reinterpret_cast<uint4*>(dst + size_t(sw16(R.unit + uint32_t(j))) * 16) = out[j];
 }
 
-// Entries of each group g = (expert e, column tile ct) of one tensor, one
-// wave per group.
+// Entries of each group g = (expert e, column tile ct) of one tensor.  With
+// one column tile a group's rows are consecutive segments (one difference);
+// otherwise block (g, sub) adds the counts of its share of the group's rows
+// (each thread kUnroll independent loads at a time, rows past the share
+// clamped and counted as empty) into ng[g], which the plan kernel zeroed.
 __global__ __launch_bounds__(256) void masked_group_totals_kernel(const uint32_t* __restrict__ seg,
                                                                   int64_t qbase, int E, int R, int nct,
                                                                   int* __restrict__ ng) {
-  const int lane = threadIdx.x & 63;
-  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (g >= E * nct) return;  // uniform per wave
+  const int g = blockIdx.x, tid = threadIdx.x;
   const int e = g / nct, ct = g - e * nct;
   const int64_t q0 = qbase + int64_t(e) * R * nct + ct;
-  int total;
   if (nct == 1) {
-    total = int(seg[q0 + R] - seg[q0]);  // the group's rows are consecutive segments
-  } else {
-    int part = 0;
-    for (int r = lane; r < R; r += 64) {
-      const int64_t q = q0 + int64_t(r) * nct;
-      part += int(seg[q + 1] - seg[q]);
+    if (blockIdx.y == 0 && tid == 0) ng[g] = int(seg[q0 + R] - seg[q0]);
+    return;
+  }
+  constexpr int kUnroll = 8;
+  const int per = (R + int(gridDim.y) - 1) / int(gridDim.y);
+  const int r_lo = int(blockIdx.y) * per, r_hi = min(R, r_lo + per);
+  int part = 0;
+  for (int r0 = r_lo; r0 < r_hi; r0 += 256 * kUnroll) {
+    uint2 v[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const uint32_t* p = seg + q0 + int64_t(min(r0 + 256 * j + tid, R - 1)) * nct;
+      v[j] = make_uint2(p[0], p[1]);
     }
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) part += __shfl_xor(part, d, 64);
-    total = part;
+    for (int j = 0; j < kUnroll; ++j) part += int(v[j].y - v[j].x) & -int(r0 + 256 * j + tid < r_hi);
   }
-  if (lane == 0) ng[g] = total;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) part += __shfl_xor(part, d, 64);
+  __shared__ int red[4];
+  if ((tid & 63) == 0) red[tid >> 6] = part;
+  __syncthreads();
+  if (tid == 0) atomicAdd(ng + g, (red[0] + red[1]) + (red[2] + red[3]));
 }
 
 // The tensor-wide entry target of a tile: the smallest t <= cap with
@@ -326,6 +339,21 @@ __global__ __launch_bounds__(256) void masked_target_kernel(const int* __restric
   if (tid == 0) *target = lo;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts by 1, 2,
+// 4 and 8 (lanes without a source add 0) give each 16-lane row its own
+// prefix; the row-15 broadcast adds row 0's total into row 1 and row 2's
+// into row 3, the row-31 broadcast adds rows 0-1 into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  int v = x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  return v;
+}
+
 // Tiles of one tensor.  Group g = (expert e, column tile ct), e-major; its
 // rows' entry counts come from the plan's segment starts (per group fewer
 // than 2^31 entries).  The group is split into nt = max(ceil(R / RB),
@@ -362,12 +390,30 @@ __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __res
   // at most the tensor-wide target, which spreads the work over the CUs
   const int tcap = min(cap, *target);
   const int nt = max(int((R + RB - 1) / RB), int((int64_t(total) + tcap - 1) / tcap));
-  // two walks over the rows: the first counts the group's tiles and
-  // reserves them at once (a group's tiles stay consecutive in the list), the
-  // second writes them; each walk loads the counts of 16 chunks of 64 rows at
-  // once (independent loads), then scans them chunk by chunk
+  // One walk over the rows records the group's tiles in registers (tile i
+  // in lane i mod 64 of rec[i / 64]); the group then reserves them at once,
+  // so its tiles stay consecutive in the list, and its lanes write them.  A
+  // group with more than kRec tiles walks a second time to write them.  The
+  // walk reads the counts of kSpan chunks of 64 rows with independent loads
+  // (rows past R clamped to a valid segment and counted as empty), the next
+  // span's while it scans the current one chunk by chunk.
+  constexpr int kSpan = 16, kRecRegs = 4, kRec = 64 * kRecRegs;
+  // (the counts are formed where they are used, so that nothing waits for
+  // the loads before the scan that precedes their use)
+  auto load_span = [&](int s0, uint2 (&cnts)[kSpan]) {
+#pragma unroll
+    for (int j = 0; j < kSpan; ++j) {
+      const int r = min(s0 + 64 * j + lane, R - 1);
+      const uint32_t* p = seg + q0 + int64_t(r) * nct;
+      cnts[j] = make_uint2(p[0], p[1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // issued here, not next to their use
+  };
+  uint32_t rec[kRecRegs];
+#pragma unroll
+  for (int i = 0; i < kRecRegs; ++i) rec[i] = 0;
   int base = 0;
-  constexpr int kSpan = 16;  // 64-row chunks whose counts are loaded together
+#pragma unroll 1
   for (int walk = 0; walk < 2; ++walk) {
     int open_r = 0, open_x = 0;  // first row of the open tile, its exclusive prefix
     int carry = 0;               // exclusive prefix of the chunk's first row
@@ -380,29 +426,25 @@ __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __res
       return (k * total + nt - 1) / nt;
     };
     int64_t quant = next_quant(0);
-    for (int s0 = 0; s0 < R; s0 += 64 * kSpan) {
-      int cnts[kSpan];
+    auto emit = [&](int r_lo, int r_hi) {
+      const uint32_t y = uint32_t(r_lo) | (uint32_t(r_hi) << 16);
+      if (walk == 0) {
 #pragma unroll
-      for (int j = 0; j < kSpan; ++j) {
-        const int r = s0 + 64 * j + lane;
-        cnts[j] = 0;
-        if (r < R) {
-          const int64_t q = q0 + int64_t(r) * nct;
-          cnts[j] = int(seg[q + 1] - seg[q]);
-        }
+        for (int i = 0; i < kRecRegs; ++i)
+          if (n == 64 * i + lane) rec[i] = y;
+      } else if (lane == 0) {
+        tiles[base + n] = make_uint2(tx, y);
       }
+      ++n;
+    };
+    auto scan_span = [&](int s0, const uint2 (&cnts)[kSpan]) {
 #pragma unroll
       for (int j = 0; j < kSpan; ++j) {
         const int r0 = s0 + 64 * j;
         if (r0 >= R) break;  // uniform
         const int r = r0 + lane;
-        const int cnt = cnts[j];
-        int incl = cnt;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int v = __shfl_up(incl, d, 64);
-          if (lane >= d) incl += v;
-        }
+        const int cnt = int(cnts[j].y - cnts[j].x) & -int(r < R);
+        const int incl = wave_incl_scan(cnt);
         const int excl = carry + incl - cnt;
         // at most one cut per row, taken in row order
         while (true) {
@@ -414,27 +456,36 @@ __global__ __launch_bounds__(256) void masked_tiles_kernel(const uint32_t* __res
           if (!m) break;
           const int c = __ffsll((long long)m) - 1;
           const int cr = r0 + c;
-          const int cx = __shfl(excl, c, 64);
-          if (cx > open_x) {
-            if (walk == 1 && lane == 0)
-              tiles[base + n] = make_uint2(tx, uint32_t(open_r) | (uint32_t(cr) << 16));
-            ++n;
-          }
+          const int cx = __builtin_amdgcn_readlane(excl, c);
+          if (cx > open_x) emit(open_r, cr);
           open_r = cr;
           open_x = cx;
           quant = next_quant(open_x);
           ++ncut;
         }
-        carry += __shfl(incl, 63, 64);
+        carry += __builtin_amdgcn_readlane(incl, 63);
       }
+    };
+    // two span buffers, each refilled right after it is scanned (the last
+    // refills read clamped rows and go unused)
+    uint2 ca[kSpan], cb[kSpan];
+    load_span(0, ca);
+    for (int s0 = 0; s0 < R; s0 += 2 * 64 * kSpan) {
+      load_span(s0 + 64 * kSpan, cb);
+      scan_span(s0, ca);
+      load_span(s0 + 2 * 64 * kSpan, ca);
+      if (s0 + 64 * kSpan < R) scan_span(s0 + 64 * kSpan, cb);  // uniform
     }
-    if (carry > open_x) {
-      if (walk == 1 && lane == 0) tiles[base + n] = make_uint2(tx, uint32_t(open_r) | (uint32_t(R) << 16));
-      ++n;
-    }
+    if (carry > open_x) emit(open_r, R);
     if (walk == 0) {
       if (lane == 0) base = atomicAdd(ntiles, n);
       base = __shfl(base, 0, 64);
+      if (n <= kRec) {
+#pragma unroll
+        for (int i = 0; i < kRecRegs; ++i)
+          if (64 * i + lane < n) tiles[base + 64 * i + lane] = make_uint2(tx, rec[i]);
+        return;
+      }
     }
   }
 }
@@ -848,10 +899,11 @@ usaf_status masked_plan_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64
   unsigned char* base = static_cast<unsigned char*>(plan);
   uint32_t* seg = reinterpret_cast<uint32_t*>(base);
   int* counters = reinterpret_cast<int*>(base + P.counters);
-  hipLaunchKernelGGL(masked_plan_kernel, dim3(unsigned(ceil_div(P.Lq.Q + 1, 256))), dim3(256), 0, st,
-                     idx, nnz, P.Lq, seg, counters);
-  USAF_LAUNCH_CHECK();
   int* ng = reinterpret_cast<int*>(base + P.ngrp);
+  const int ngroups = s.E * (P.Lq.nct0 + P.Lq.nct1);  // <= Q + 1 threads
+  hipLaunchKernelGGL(masked_plan_kernel, dim3(unsigned(ceil_div(P.Lq.Q + 1, 256))), dim3(256), 0, st,
+                     idx, nnz, P.Lq, seg, counters, ng, ngroups);
+  USAF_LAUNCH_CHECK();
   const int cus = std::min(device_cus(), kMaxCUs);
   for (int tensor = 0; tensor < 2; ++tensor) {
     const int nct = tensor == 0 ? P.Lq.nct0 : P.Lq.nct1;
@@ -860,7 +912,9 @@ usaf_status masked_plan_bf16(const usaf_moe_shape& s, const uint32_t* idx, int64
     const int R = tensor == 0 ? P.Lq.R0 : P.Lq.R1, RB = tensor == 0 ? P.RB0 : P.RB1;
     const int cap = tensor == 0 ? kCap<false> : kCap<true>;
     int* ngt = ng + (tensor == 0 ? 0 : s.E * P.Lq.nct0);
-    hipLaunchKernelGGL(masked_group_totals_kernel, dim3(unsigned(ceil_div(groups, 4))), dim3(256), 0, st,
+    // about 2048 rows per block (at most 16 blocks per group)
+    const int nsub = nct == 1 ? 1 : std::min(16, int(ceil_div(R, 2048)));
+    hipLaunchKernelGGL(masked_group_totals_kernel, dim3(unsigned(groups), unsigned(nsub)), dim3(256), 0, st,
                        seg, qb, s.E, R, nct, ngt);
     USAF_LAUNCH_CHECK();
     hipLaunchKernelGGL(masked_target_kernel, dim3(1), dim3(256), 0, st, ngt, groups, R, RB, cap, cus,
