@@ -731,7 +731,8 @@ constexpr int kFwdBM = 160, kFwdBN = 256, kFwdNS = 3;  // gate_up, down, dA, dX:
 constexpr int kFwdWM = 2, kFwdWN = 4;                  // 8 waves: 2 per SIMD
 constexpr int kFwdBK = 64;                             // contraction depth of a stage
 constexpr int kDaWN = 4;                               // dA: 8 waves of 64 columns
-constexpr int kDwBM = 256, kDwBN = 256, kDwNS = 2;     // dense dW: 128 KiB LDS
+constexpr int kDwBM = 256, kDwBN = 256, kDwNS = 3;     // dense dW: 3 stages of depth 32, 96 KiB LDS
+constexpr int kDwBK = 32;
 
 // Groups of at least kBigRows rows on average (few large experts) take
 // 256-row tiles: twice the MFMA work per staged byte, and little ragged waste.
@@ -817,12 +818,12 @@ usaf_status mfma_dense_dw(const usaf_moe_shape& s, const bf16_t* X, const bf16_t
   }
   {
     const int MT = int(ceil_div(2 * s.I, kDwBM)), NT = int(ceil_div(s.H, kDwBN));
-    g2::MDenseDw<false, kDwBM, kDwBN, kDwNS> p{dgu, Xg, offsets, dW, s.H, s.E, s.I, MT, NT, ngu};
+    g2::MDenseDw<false, kDwBM, kDwBN, kDwNS, 2, 2, kDwBK> p{dgu, Xg, offsets, dW, s.H, s.E, s.I, MT, NT, ngu};
     USAF_TRY(launch_v2(p, int64_t(MT) * NT * s.E, st, -1));
   }
   {
     const int MT = int(ceil_div(s.H, kDwBM)), NT = int(ceil_div(s.I, kDwBN));
-    g2::MDenseDw<true, kDwBM, kDwBN, kDwNS> p{wdYg, a, offsets, dW, s.H, s.E, s.I, MT, NT, ngu};
+    g2::MDenseDw<true, kDwBM, kDwBN, kDwNS, 2, 2, kDwBK> p{wdYg, a, offsets, dW, s.H, s.E, s.I, MT, NT, ngu};
     USAF_TRY(launch_v2(p, int64_t(MT) * NT * s.E, st, -1));
   }
   timer_end(USAF_K_DENSE_DW, st);
