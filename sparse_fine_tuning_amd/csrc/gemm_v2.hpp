@@ -164,11 +164,13 @@ struct TailSplit {
   int full, tail, S;
 };
 // Partial buffer of a split launch: cap units of one tile's fp32
-// accumulators; grid: the persistent launch's block count.
+// accumulators; grid: the persistent launch's block count; hdr: where the
+// launch leaves its plan (full, tail, S) for the reduction.
 struct SplitWs {
   float* ws = nullptr;
   int cap = 0;
   int grid = 0;
+  int* hdr = nullptr;
 };
 template <int BM, int BK>
 __device__ __forceinline__ TailSplit grouped_split_plan(const int32_t* __restrict__ offsets, int E,
@@ -829,7 +831,14 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_persistent(P p)
   const int G = gridDim.x;
   int L = xcd_remap_blocks(blockIdx.x, G);
   TailSplit plan{INT_MAX, 0, 1};
-  if constexpr (TailSplitOf<P>::value) plan = p.split();
+  if constexpr (TailSplitOf<P>::value) {
+    plan = p.split();
+    if (blockIdx.x == 0 && threadIdx.x == 0 && p.sk.hdr) {
+      p.sk.hdr[0] = plan.full;
+      p.sk.hdr[1] = plan.tail;
+      p.sk.hdr[2] = plan.S;
+    }
+  }
   auto tile = [&](int l, MTile& tt) {
     if constexpr (TailSplitOf<P>::value) return p.tile(l, tt, plan);
     else return p.tile(l, tt);
@@ -917,7 +926,8 @@ __global__ __launch_bounds__(P::NTHR, P::kWavesPerEU) void gemm2_persistent(P p)
   }
 }
 
-// The tiles a persistent launch split (grouped_split_plan): one wave per
+// The tiles a persistent launch split (grouped_split_plan, as the launch
+// recorded it in sk.hdr; no tail: every block returns at once): one wave per
 // block, block x = NW b + w for wave w of tail tile b (at most G NW blocks),
 // adds that wave's accumulators over the tile's parts in part order and
 // runs its share of the problem's epilogue (epilogues work per wave).
@@ -926,7 +936,7 @@ __global__ __launch_bounds__(64) void gemm2_split_reduce(P p) {
   constexpr int IM = P::IM, NJ = P::NJ, NW = P::NTHR / 64;
   constexpr int kStage = P::kPStage > 0 ? P::kPStage : 16;
   __shared__ __attribute__((aligned(16))) unsigned char stage[kStage];
-  const TailSplit sp = p.split();
+  const TailSplit sp{p.sk.hdr[0], p.sk.hdr[1], p.sk.hdr[2]};
   const int b = blockIdx.x / NW, w = blockIdx.x % NW;
   if (b >= sp.tail) return;
   MTile t;

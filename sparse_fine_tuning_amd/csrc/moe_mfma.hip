@@ -696,12 +696,14 @@ template <class P>
 static usaf_status launch_persistent_split(P p, int64_t tiles, float* split_ws, size_t split_bytes,
                                            hipStream_t st, int kclass) {
   if (tiles <= 0) return USAF_OK;
+  // the buffer's last 256 bytes hold the plan the launch records
   const size_t unit = size_t(P::NTHR) * P::IM * P::NJ * 16 * 4;  // a tile's accumulators
-  const size_t cap = split_ws ? split_bytes / unit : 0;
+  const size_t cap = split_ws && split_bytes > 256 ? (split_bytes - 256) / unit : 0;
   int64_t blocks = int64_t(P::kBlocksPerCU) * device_cus();
   if (blocks > tiles) blocks = tiles;
   blocks = (blocks + 7) / 8 * 8;
-  p.sk = g2::SplitWs{split_ws, int(cap < size_t(1 << 20) ? cap : size_t(1 << 20)), int(blocks)};
+  int* hdr = cap >= 2 ? reinterpret_cast<int*>(reinterpret_cast<char*>(split_ws) + split_bytes - 256) : nullptr;
+  p.sk = g2::SplitWs{split_ws, int(cap < size_t(1 << 20) ? cap : size_t(1 << 20)), int(blocks), hdr};
   timer_begin(kclass, st);
   hipLaunchKernelGGL(g2::gemm2_persistent<P>, dim3(unsigned(blocks)), dim3(P::NTHR), 0, st, p);
   USAF_LAUNCH_CHECK();
