@@ -43,34 +43,34 @@ WRITE_SCALE = 1.0   # and 1,048,576 KiB of WRITE_SIZE
 # being kept per list; expert + router Adam); dense_dw sums the operand
 # staging and the two GEMMs of one scan; topk_fresh sums every launch of the
 # scan's first selection (sample, full read, compaction, candidate rounds,
-# emit).
-G = "8f25601fde1b0a8f"  # the GEMM sources
+# emit); down and dx sum the GEMM and its tail-split reduction.
+G = "bbf5451a09d2feb1"  # the GEMM sources
 COUNTER_TRAFFIC = {
     "qwen3_step": {
-        "router_gemm": (8788, 16384, G),
-        "gate_up": (470345, 147460, G),
-        "down": (221373, 131072, G),
-        "da": (337930, 100123, G),
-        "dx": (631654, 131072, G),
-        "masked_dw": (168661, 12827, "4b2b9fc26f8747eb"),
+        "router_gemm": (8784, 16384, G),
+        "gate_up": (470332, 147460, G),
+        "down": (221419, 131072, G),
+        "da": (325767, 100102, G),
+        "dx": (571925, 131072, G),
+        "masked_dw": (168872, 12825, "77b40f89d50aabb9"),
         "adam": (28622, 123523, "a431573056f07bd3"),
     },
     "qwen3_scan": {
-        "dense_dw": (879892, 2883584, G),
-        "topk_fresh": (1338698, 102138, "86e77014bed80652"),
+        "dense_dw": (865910, 2883584, G),
+        "topk_fresh": (1338699, 102144, "79b8f877d6085a62"),
     },
     "mixtral_step": {
         "router_gemm": (16526, 1024, G),
-        "gate_up": (1992693, 702975, G),
-        "down": (1162797, 68064, G),
-        "da": (2251383, 468195, G),
-        "dx": (2465877, 78256, G),
-        "masked_dw": (773899, 45646, "4b2b9fc26f8747eb"),
-        "adam": (62219, 281414, "a431573056f07bd3"),
+        "gate_up": (1894829, 703255, G),
+        "down": (1194486, 118272, G),
+        "da": (2203410, 467717, G),
+        "dx": (2495166, 135628, G),
+        "masked_dw": (779115, 45239, "77b40f89d50aabb9"),
+        "adam": (62219, 281415, "a431573056f07bd3"),
     },
     "mixtral_scan": {
-        "dense_dw": (4899947, 5636096, G),
-        "topk_fresh": (3122522, 220163, "86e77014bed80652"),
+        "dense_dw": (4912465, 5636096, G),
+        "topk_fresh": (3123157, 220491, "79b8f877d6085a62"),
     },
 }
 KERNEL_SOURCES = {
