@@ -1054,8 +1054,11 @@ static usaf_status forward_impl(const usaf_moe_shape& s, const T* X, const float
   }
   // experts
   if constexpr (kMfma) {
+    // the whole [S, H] fp32-sized region is free during gate_up (the
+    // router partials are consumed, the down outputs not yet written)
     USAF_TRY(mfma_gate_up(s, X, Wgu, st.offsets, st.perm, static_cast<T*>(st.gu),
-                          static_cast<T*>(st.a), stream));
+                          static_cast<T*>(st.a), reinterpret_cast<float*>(ws + L.ybuf),
+                          2 * bf16_spare_offset(s), stream));
     USAF_TRY(mfma_down(s, static_cast<const T*>(st.a), Wd, st.offsets, ybuf,
                        reinterpret_cast<float*>(ws + L.ybuf + bf16_spare_offset(s)),
                        bf16_spare_offset(s), stream));
@@ -1094,7 +1097,9 @@ static usaf_status backward_impl(const usaf_moe_shape& s, const T* X, const floa
   const T* a = static_cast<const T*>(st.a);
 
   if constexpr (kMfma) {
-    USAF_TRY(mfma_da(s, dY, Wd, st.offsets, st.perm, st.topk_w, gu, a, dgu, dwpart, stream));
+    // vbuf is free during dA (dX writes it afterwards)
+    USAF_TRY(mfma_da(s, dY, Wd, st.offsets, st.perm, st.topk_w, gu, a, dgu, dwpart,
+                     reinterpret_cast<float*>(ws + L.vbuf), 2 * bf16_spare_offset(s), stream));
   } else {
     DaBwd<T> da{dY, Wd, st.offsets, st.perm, st.topk_w, gu, a, dgu, dwpart, s.H, s.E, s.K, s.I, NT};
     USAF_TRY(launch_fma(da, dim3(mtiles_bound(s), unsigned(NT)), stream, USAF_K_DA));
@@ -1255,7 +1260,8 @@ extern "C" usaf_status usaf_moe_forward_q4(const usaf_moe_shape* shape, const vo
   USAF_TRY(mfma_router(s, Xb, Wr, parts, nparts, stream));
   USAF_TRY(route_impl(s, parts, nparts, st, stream));
   USAF_TRY(q4_gate_up(s, Xb, *w, st.offsets, st.perm, static_cast<bf16_t*>(st.gu),
-                      static_cast<bf16_t*>(st.a), stream));
+                      static_cast<bf16_t*>(st.a), reinterpret_cast<float*>(wsc + L.ybuf),
+                      2 * bf16_spare_offset(s), stream));
   USAF_TRY(q4_down(s, static_cast<const bf16_t*>(st.a), *w, st.offsets, ybuf,
                    reinterpret_cast<float*>(wsc + L.ybuf + bf16_spare_offset(s)),
                    bf16_spare_offset(s), stream));

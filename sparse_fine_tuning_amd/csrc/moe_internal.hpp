@@ -94,9 +94,12 @@ inline int mfma_router_splits(const usaf_moe_shape& s) {
   while (ks < kMaxRouterParts && tiles * ks < 256 && s.H / (64 * ks * 2) >= 1) ks *= 2;
   return ks;
 }
+// split_ws / split_bytes of the grouped GEMMs: scratch for the tail split's
+// fp32 partials (see launch_persistent_split; none: no split), free while
+// the GEMM runs and apart from its outputs.
 usaf_status mfma_gate_up(const usaf_moe_shape& s, const uint16_t* X, const uint16_t* Wgu,
                          const int32_t* offsets, const int32_t* perm, uint16_t* gu, uint16_t* a,
-                         hipStream_t st);
+                         float* split_ws, size_t split_bytes, hipStream_t st);
 // split_ws: split_bytes of scratch for the tail split's fp32 partials
 // (none: no split); not ybuf.
 usaf_status mfma_down(const usaf_moe_shape& s, const uint16_t* a, const uint16_t* Wd,
@@ -106,7 +109,7 @@ int mfma_dw_partials(const usaf_moe_shape& s);
 usaf_status mfma_da(const usaf_moe_shape& s, const uint16_t* dY, const uint16_t* Wd,
                     const int32_t* offsets, const int32_t* perm, const float* topk_w,
                     const uint16_t* gu, const uint16_t* a, uint16_t* dgu, float* dwpart,
-                    hipStream_t st);
+                    float* split_ws, size_t split_bytes, hipStream_t st);
 usaf_status mfma_dx(const usaf_moe_shape& s, const uint16_t* dgu, const uint16_t* Wgu,
                     const int32_t* offsets, uint16_t* vbuf, float* split_ws, size_t split_bytes,
                     hipStream_t st);
@@ -134,7 +137,7 @@ size_t union_ws_bytes(int64_t n);  // usaf_sorted_union of lists totalling n ent
 // Forward expert GEMMs on 4-bit affine codes, dequantised as they load.
 usaf_status q4_gate_up(const usaf_moe_shape& s, const uint16_t* X, const usaf_q4_experts& w,
                        const int32_t* offsets, const int32_t* perm, uint16_t* gu, uint16_t* a,
-                       hipStream_t st);
+                       float* split_ws, size_t split_bytes, hipStream_t st);
 usaf_status q4_down(const usaf_moe_shape& s, const uint16_t* a, const usaf_q4_experts& w,
                     const int32_t* offsets, uint16_t* ybuf, float* split_ws, size_t split_bytes,
                     hipStream_t st);

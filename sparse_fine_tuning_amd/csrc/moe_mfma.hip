@@ -119,14 +119,22 @@ struct MGateUp {
   const bf16_t* X; const bf16_t* Wgu; const int32_t* offsets; const int32_t* perm;
   bf16_t* gu; bf16_t* a;
   int H, E, K, I, NT;
-  __device__ __forceinline__ bool tile(int L, MTile& t) const {
-    if (!grouped_tile<BM>(offsets, E, NT, L, t)) return false;
-    t.kb = 0; t.ke = H; t.n0 = t.nt * (BN / 2); t.nc = 0;
+  SplitWs sk;  // tail split partials (none: no split)
+  static constexpr bool kTailSplit = true;
+  __device__ __forceinline__ TailSplit split() const {
+    return grouped_split_plan<BM, BK_>(offsets, E, NT, H, sk);
+  }
+  __device__ __forceinline__ bool tile(int L, MTile& t, const TailSplit& plan) const {
+    if (!grouped_split_tile<BM, BK_>(offsets, E, NT, L, H, plan, t)) return false;
+    t.n0 = t.nt * (BN / 2); t.nc = 0;
     return true;
   }
-  __device__ __forceinline__ TokRowsC a_src(const MTile& t) const { return TokRowsC{X, perm, K, t.off + t.m0, t.mc, H}; }
+  // a contraction part [kb, ke): both operands' rows start at column kb
+  __device__ __forceinline__ TokRowsC a_src(const MTile& t) const {
+    return TokRowsC{X + t.kb, perm, K, t.off + t.m0, t.mc, H};
+  }
   __device__ __forceinline__ GateUpRowsC<CW> b_src(const MTile& t) const {
-    return GateUpRowsC<CW>{Wgu + int64_t(t.e) * 2 * I * H, t.n0, I, H};
+    return GateUpRowsC<CW>{Wgu + int64_t(t.e) * 2 * I * H + t.kb, t.n0, I, H};
   }
   // persistent epilogue staging: one tensor's 32-row block (CW/2 features)
   static constexpr int kPStage =
@@ -311,7 +319,9 @@ struct MGateUpQ4 : MGateUp<BM_, BN_, NS_, WM_, WN_, 64> {
   static constexpr int kStageBytes = kPStage;
   Q4Codes c;
   __device__ __forceinline__ GateUpCodesC<Base::CW> b_src(const MTile& t) const {
-    return GateUpCodesC<Base::CW>{c, int64_t(t.e) * 2 * this->I, t.n0, this->I};
+    GateUpCodesC<Base::CW> r{c, int64_t(t.e) * 2 * this->I, t.n0, this->I};
+    r.kst0 = t.kb / 64;
+    return r;
   }
 };
 
@@ -343,14 +353,22 @@ struct MDa {
   const bf16_t* dY; const bf16_t* Wd; const int32_t* offsets; const int32_t* perm;
   const float* topk_w; const bf16_t* gu; const bf16_t* a; bf16_t* dgu; float* dwpart;
   int H, E, K, I, NT, NTP;
-  __device__ __forceinline__ bool tile(int L, MTile& t) const {
-    if (!grouped_tile<BM>(offsets, E, NT, L, t)) return false;
-    t.kb = 0; t.ke = H; t.n0 = t.nt * BN; t.nc = min(BN, I - t.n0);
+  SplitWs sk;  // tail split partials (none: no split)
+  static constexpr bool kTailSplit = true;
+  __device__ __forceinline__ TailSplit split() const {
+    return grouped_split_plan<BM, BK_>(offsets, E, NT, H, sk);
+  }
+  __device__ __forceinline__ bool tile(int L, MTile& t, const TailSplit& plan) const {
+    if (!grouped_split_tile<BM, BK_>(offsets, E, NT, L, H, plan, t)) return false;
+    t.n0 = t.nt * BN; t.nc = min(BN, I - t.n0);
     return true;
   }
-  __device__ __forceinline__ TokRowsC a_src(const MTile& t) const { return TokRowsC{dY, perm, K, t.off + t.m0, t.mc, H}; }
+  // a contraction part [kb, ke): dY's rows from column kb, W_d from row kb
+  __device__ __forceinline__ TokRowsC a_src(const MTile& t) const {
+    return TokRowsC{dY + t.kb, perm, K, t.off + t.m0, t.mc, H};
+  }
   __device__ __forceinline__ StridedKC b_src(const MTile& t) const {
-    return StridedKC{Wd + int64_t(t.e) * H * I + t.n0, I, t.nc};
+    return StridedKC{Wd + (int64_t(t.e) * H + t.kb) * I + t.n0, I, t.nc};
   }
   // staging through one ring stage, where the wave's block fits there
   static constexpr int kPStage = ((CW == 32 || CW == 64) &&
@@ -675,23 +693,9 @@ int device_cus() {
 }
 
 // Persistent launch: about P::kBlocksPerCU blocks per CU (a multiple of 8
-// for the XCD remap), never more blocks than tiles.
-template <class P>
-static usaf_status launch_persistent(const P& p, int64_t tiles, hipStream_t st, int kclass) {
-  if (tiles <= 0) return USAF_OK;
-  int64_t blocks = int64_t(P::kBlocksPerCU) * device_cus();
-  if (blocks > tiles) blocks = tiles;
-  blocks = (blocks + 7) / 8 * 8;
-  timer_begin(kclass, st);
-  hipLaunchKernelGGL(g2::gemm2_persistent<P>, dim3(unsigned(blocks)), dim3(P::NTHR), 0, st, p);
-  timer_end(kclass, st);
-  USAF_LAUNCH_CHECK();
-  return USAF_OK;
-}
-
-// The same with the tail split (grouped_split_plan) of a problem that opts
-// in, given split_bytes of partial buffer at split_ws: the persistent
-// launch, then the reduction of the split tiles on the same grid.
+// for the XCD remap), never more blocks than tiles; with split_bytes of
+// partial buffer at split_ws, the tail split (grouped_split_plan) and the
+// reduction of the split tiles after the launch.
 template <class P>
 static usaf_status launch_persistent_split(P p, int64_t tiles, float* split_ws, size_t split_bytes,
                                            hipStream_t st, int kclass) {
@@ -745,22 +749,19 @@ static bool big_groups(const usaf_moe_shape& s) {
   return int64_t(s.T) * s.K >= int64_t(kBigRows) * s.E;
 }
 
-template <template <int, int, int, int, int, int> class M, class... Args>
-static usaf_status launch_fwd(const usaf_moe_shape& s, int NT, hipStream_t st, int kclass,
-                              Args... args) {
-  if (big_groups(s))
-    return launch_persistent(M<kBigBM, kFwdBN, kBigNS, kBigWM, kBigWN, kBigBK>{args...},
-                             grouped_tiles_bound(s, NT, kBigBM), st, kclass);
-  return launch_persistent(M<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN, kFwdBK>{args...},
-                           grouped_tiles_bound(s, NT, kFwdBM), st, kclass);
-}
-
 usaf_status mfma_gate_up(const usaf_moe_shape& s, const bf16_t* X, const bf16_t* Wgu,
                          const int32_t* offsets, const int32_t* perm, bf16_t* gu, bf16_t* a,
-                         hipStream_t st) {
+                         float* split_ws, size_t split_bytes, hipStream_t st) {
   const int NT = int(ceil_div(s.I, kFwdBN / 2));
-  return launch_fwd<g2::MGateUp>(s, NT, st, USAF_K_GATE_UP, X, Wgu, offsets, perm, gu, a, s.H,
-                                 s.E, s.K, s.I, NT);
+  if (big_groups(s))
+    return launch_persistent_split(
+        g2::MGateUp<kBigBM, kFwdBN, kBigNS, kBigWM, kBigWN, kBigBK>{X, Wgu, offsets, perm, gu, a, s.H, s.E,
+                                                                    s.K, s.I, NT},
+        grouped_tiles_bound(s, NT, kBigBM), split_ws, split_bytes, st, USAF_K_GATE_UP);
+  return launch_persistent_split(
+      g2::MGateUp<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN, kFwdBK>{X, Wgu, offsets, perm, gu, a, s.H, s.E,
+                                                                  s.K, s.I, NT},
+      grouped_tiles_bound(s, NT, kFwdBM), split_ws, split_bytes, st, USAF_K_GATE_UP);
 }
 
 usaf_status mfma_down(const usaf_moe_shape& s, const bf16_t* a, const bf16_t* Wd,
@@ -781,13 +782,14 @@ int mfma_dw_partials(const usaf_moe_shape& s) { return kDaWN * int(ceil_div(s.I,
 usaf_status mfma_da(const usaf_moe_shape& s, const bf16_t* dY, const bf16_t* Wd,
                     const int32_t* offsets, const int32_t* perm, const float* topk_w,
                     const bf16_t* gu, const bf16_t* a, bf16_t* dgu, float* dwpart,
-                    hipStream_t st) {
+                    float* split_ws, size_t split_bytes, hipStream_t st) {
   // dA keeps the 160-row tiles for large groups too: its epilogue's g|u
   // loads spill on 256-row tiles (measured 13% slower at the Mixtral shape)
   const int NT = int(ceil_div(s.I, kFwdBN));
-  return launch_persistent(g2::MDa<kFwdBM, kFwdBN, kFwdNS, 2, kDaWN, kFwdBK>{dY, Wd, offsets, perm, topk_w, gu, a, dgu, dwpart, s.H,
-                                           s.E, s.K, s.I, NT, kDaWN * NT},
-                   grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_DA);
+  return launch_persistent_split(
+      g2::MDa<kFwdBM, kFwdBN, kFwdNS, 2, kDaWN, kFwdBK>{dY, Wd, offsets, perm, topk_w, gu, a, dgu, dwpart,
+                                                        s.H, s.E, s.K, s.I, NT, kDaWN * NT},
+      grouped_tiles_bound(s, NT, kFwdBM), split_ws, split_bytes, st, USAF_K_DA);
 }
 
 usaf_status mfma_dx(const usaf_moe_shape& s, const bf16_t* dgu, const bf16_t* Wgu,
@@ -846,17 +848,24 @@ static int log2_exact(int g) {
 
 usaf_status q4_gate_up(const usaf_moe_shape& s, const bf16_t* X, const usaf_q4_experts& w,
                        const int32_t* offsets, const int32_t* perm, bf16_t* gu, bf16_t* a,
-                       hipStream_t st) {
+                       float* split_ws, size_t split_bytes, hipStream_t st) {
+  // the same tiles, grid and tail split as mfma_gate_up
   const int NT = int(ceil_div(s.I, kFwdBN / 2));
   const g2::Q4Codes c{w.q_gu, w.s_gu, w.z_gu, s.H / 2, s.H / w.group, log2_exact(w.group)};
   if (big_groups(s)) {
     using P = g2::MGateUpQ4<kBigBM, kFwdBN, kQ4BigNS, kBigWM, kBigWN>;
+    static_assert(P::kBlocksPerCU == g2::MGateUp<kBigBM, kFwdBN, kBigNS, kBigWM, kBigWN, kBigBK>::kBlocksPerCU,
+                  "the 4-bit and bf16 gate_up launches share their grid");
     const P p{{X, nullptr, offsets, perm, gu, a, s.H, s.E, s.K, s.I, NT}, c};
-    return launch_persistent(p, grouped_tiles_bound(s, NT, kBigBM), st, USAF_K_GATE_UP);
+    return launch_persistent_split(p, grouped_tiles_bound(s, NT, kBigBM), split_ws, split_bytes, st,
+                                   USAF_K_GATE_UP);
   }
   using P = g2::MGateUpQ4<kFwdBM, kFwdBN, kQ4NS, kFwdWM, kFwdWN>;
+  static_assert(P::kBlocksPerCU == g2::MGateUp<kFwdBM, kFwdBN, kFwdNS, kFwdWM, kFwdWN, kFwdBK>::kBlocksPerCU,
+                "the 4-bit and bf16 gate_up launches share their grid");
   const P p{{X, nullptr, offsets, perm, gu, a, s.H, s.E, s.K, s.I, NT}, c};
-  return launch_persistent(p, grouped_tiles_bound(s, NT, kFwdBM), st, USAF_K_GATE_UP);
+  return launch_persistent_split(p, grouped_tiles_bound(s, NT, kFwdBM), split_ws, split_bytes, st,
+                                 USAF_K_GATE_UP);
 }
 
 usaf_status q4_down(const usaf_moe_shape& s, const bf16_t* a, const usaf_q4_experts& w,

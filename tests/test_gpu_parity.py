@@ -192,6 +192,8 @@ CASES = [
     ("tail_split_bf16", (2000, 2048, 24, 4, 256), 1, (130, 131, 132, 133, 134)),
     # 3 parts, the last one ragged (I = 160: 64 + 64 + 32)
     ("tail_split_ragged_k_bf16", (1200, 4096, 18, 2, 160), 1, (130, 131, 132, 133, 134)),
+    # gate_up split in 2 parts and dA in 4 (160-row tiles)
+    ("tail_split_gate_up_da_bf16", (1024, 1024, 17, 4, 2048), 1, (150, 151, 152, 153, 154)),
 ]
 
 
@@ -203,21 +205,23 @@ def row_tile(BM, cnt):
     return ((cnt + n - 1) // n + 31) // 32 * 32 if n > 0 else BM
 
 
-def tail_split_parts(offsets, dims, contraction):
-    """Parts per tail tile of the bf16 down (contraction I) or dX (2I) launch
-    on this device: 1 when the launch runs unsplit.  The launch has one block
-    per CU (these tile shapes fill a CU's LDS); its last round of tiles, when
-    at most half full, is split into S <= 4 parts, bounded by the partial
-    buffer (the spare half of the [T K, H] fp32-sized region) and the
+def tail_split_parts(offsets, dims, gemm):
+    """Parts per tail tile of a bf16 grouped GEMM launch ("gate_up", "down",
+    "da" or "dx") on this device: 1 when the launch runs unsplit.  The
+    launch has one block per CU (these tile shapes fill a CU's LDS); its last
+    round of tiles, when at most half full, is split into S <= 4 parts,
+    bounded by the partial buffer (the [T K, H] fp32-sized region for
+    gate_up and dA, its spare half for down and dX, less 256 bytes) and the
     contraction's 64-wide stages."""
     T, H, E, K, I = dims
-    big = T * K >= 512 * E
+    big = T * K >= 512 * E and gemm != "da"
     BM, IM = (256, 4) if big else (160, 3)
-    NT = (H + 255) // 256
+    NT, contraction, room = {"gate_up": ((I + 127) // 128, H, 4), "down": ((H + 255) // 256, I, 2),
+                             "da": ((I + 255) // 256, H, 4), "dx": ((H + 255) // 256, 2 * I, 2)}[gemm]
     cnt = np.diff(offsets)
     tiles = int(sum(((c + row_tile(BM, c) - 1) // row_tile(BM, c)) * NT for c in cnt if c > 0))
     G = (torch.cuda.get_device_properties(0).multi_processor_count + 7) // 8 * 8
-    cap = T * K * H * 2 // (512 * IM * 2 * 64)
+    cap = (T * K * H * room - 256) // (512 * IM * 2 * 64)
     R, rem = divmod(tiles, G)
     if cap < 2 or R < 1 or rem == 0 or 2 * rem > G:
         return 1
@@ -242,9 +246,10 @@ def test_layer_forward_backward(capi, name, dims, act, seeds):
     assert np.array_equal(ids, fw["topk_ids"]), "routing differs"
     assert np.array_equal(st["offsets"].cpu().numpy(), fw["offsets"])
     if name.startswith("tail_split") and torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        parts = [tail_split_parts(fw["offsets"], dims, c) for c in (I, 2 * I)]
-        say(f"  tail split parts: down {parts[0]}, dX {parts[1]}")
-        assert min(parts) >= 2, "the case no longer exercises the tail split"
+        parts = {g: tail_split_parts(fw["offsets"], dims, g) for g in ("gate_up", "down", "da", "dx")}
+        say(f"  tail split parts: {parts}")
+        want = ("gate_up", "da") if "gate_up_da" in name else ("down", "dx")
+        assert min(parts[g] for g in want) >= 2, "the case no longer exercises the tail split"
     perm = st["perm"].cpu().numpy()
     assert np.array_equal(perm, fw["perm"])
     assert rel(npf(st["logits"]), fw["logits"]) <= tol
@@ -739,12 +744,13 @@ def test_forward_q4_edge_scales_and_zeros(capi):
 # (1024, 256, 4, 2, 128): 512 slots per expert on average, the 256-row tiles
 # (2200, 4096, 4, 2, 256) and (2000, 2048, 24, 4, 256): down launches whose
 # last round is split in 2 and 4 contraction parts (a part may start on the
-# second group of a scale pair)
+# second group of a scale pair); (1024, 2048, 16, 4, 1152): gate_up split in 4
 @pytest.mark.parametrize("dims,group", [((200, 256, 8, 2, 128), 64), ((333, 512, 16, 4, 384), 64),
                                         ((1024, 256, 4, 2, 128), 64),
                                         ((1024, 2048, 128, 8, 768), 128),
                                         ((2200, 4096, 4, 2, 256), 64),
-                                        ((2000, 2048, 24, 4, 256), 128)])
+                                        ((2000, 2048, 24, 4, 256), 128),
+                                        ((1024, 2048, 16, 4, 1152), 64)])
 def test_forward_q4_equals_resident_dequant(capi, dims, group):
     """usaf_moe_forward_q4 on affine 4-bit codes against usaf_moe_forward on
     the usaf_dequant_affine copy of the same codes: every state tensor and
@@ -779,10 +785,12 @@ def test_forward_q4_equals_resident_dequant(capi, dims, group):
             x, y = x.view(torch.int16), y.view(torch.int16)
         assert torch.equal(x, y), name
     assert torch.equal(res.Y.view(torch.int16), onl.Y.view(torch.int16))
-    if T >= 2000 and torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        parts = tail_split_parts(res.st["offsets"].cpu().numpy(), dims, I)
-        say(f"  down tail split parts: {parts}")
-        assert parts >= 2, "the case no longer exercises the tail split"
+    split_cases = ((2200, 4096, 4, 2, 256), (2000, 2048, 24, 4, 256), (1024, 2048, 16, 4, 1152))
+    if dims in split_cases and torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        off = res.st["offsets"].cpu().numpy()
+        parts = {g: tail_split_parts(off, dims, g) for g in ("gate_up", "down")}
+        say(f"  tail split parts: {parts}")
+        assert max(parts.values()) >= 2, "the case no longer exercises the tail split"
     # the oracle: its dequant of the codes, then its layer
     R = O.Rounding(O.BF16, O.CONTRACT)
     W_gu = O.dequant_affine(qg, sg, zg, group).reshape(E, 2 * I, H)
