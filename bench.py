@@ -43,34 +43,34 @@ WRITE_SCALE = 1.0   # and 1,048,576 KiB of WRITE_SIZE
 # being kept per list; expert + router Adam); dense_dw sums the operand
 # staging and the two GEMMs of one scan; topk_fresh sums every launch of the
 # scan's first selection (sample, full read, compaction, candidate rounds,
-# emit); down and dx sum the GEMM and its tail-split reduction.
-G = "bbf5451a09d2feb1"  # the GEMM sources
+# emit); the grouped GEMMs sum the GEMM and its tail-split reduction.
+G = "be7cec260b74c1c3"  # the GEMM sources
 COUNTER_TRAFFIC = {
     "qwen3_step": {
         "router_gemm": (8784, 16384, G),
-        "gate_up": (470332, 147460, G),
-        "down": (221419, 131072, G),
-        "da": (325767, 100102, G),
-        "dx": (571925, 131072, G),
-        "masked_dw": (168872, 12825, "77b40f89d50aabb9"),
+        "gate_up": (470364, 147462, G),
+        "down": (221403, 131072, G),
+        "da": (317419, 100111, G),
+        "dx": (543301, 131072, G),
+        "masked_dw": (168794, 12824, "6803601c95aa6e76"),
         "adam": (28622, 123523, "a431573056f07bd3"),
     },
     "qwen3_scan": {
-        "dense_dw": (865910, 2883584, G),
-        "topk_fresh": (1338699, 102144, "79b8f877d6085a62"),
+        "dense_dw": (867356, 2883584, G),
+        "topk_fresh": (1338699, 102130, "b540280715697c17"),
     },
     "mixtral_step": {
         "router_gemm": (16526, 1024, G),
-        "gate_up": (1894829, 703255, G),
-        "down": (1194486, 118272, G),
-        "da": (2203410, 467717, G),
-        "dx": (2495166, 135628, G),
-        "masked_dw": (779115, 45239, "77b40f89d50aabb9"),
-        "adam": (62219, 281415, "a431573056f07bd3"),
+        "gate_up": (1957473, 749553, G),
+        "down": (1176567, 118272, G),
+        "da": (2251406, 517255, G),
+        "dx": (2479262, 135628, G),
+        "masked_dw": (765037, 45343, "6803601c95aa6e76"),
+        "adam": (62219, 281414, "a431573056f07bd3"),
     },
     "mixtral_scan": {
-        "dense_dw": (4912465, 5636096, G),
-        "topk_fresh": (3123157, 220491, "79b8f877d6085a62"),
+        "dense_dw": (4906550, 5636096, G),
+        "topk_fresh": (3123063, 220449, "b540280715697c17"),
     },
 }
 KERNEL_SOURCES = {
