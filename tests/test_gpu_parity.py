@@ -194,6 +194,9 @@ CASES = [
     ("tail_split_ragged_k_bf16", (1200, 4096, 18, 2, 160), 1, (130, 131, 132, 133, 134)),
     # gate_up split in 2 parts and dA in 4 (160-row tiles)
     ("tail_split_gate_up_da_bf16", (1024, 1024, 17, 4, 2048), 1, (150, 151, 152, 153, 154)),
+    # experts of 8344, 8053 and 8203 slots: the dense dW contracts over 250+
+    # stages of 32 slots, the grouped GEMMs run 32-33 row tiles per expert
+    ("long_groups_bf16", (12300, 128, 3, 2, 64), 1, (160, 161, 162, 163, 164)),
 ]
 
 
