@@ -171,6 +171,10 @@ CASES = [
     ("ragged_fp32", (200, 128, 6, 3, 96), 0, (30, 31, 32, 33, 34)),
     ("empty_experts_fp32", (8, 64, 16, 1, 32), 0, (40, 41, 42, 43, 44)),
     ("ragged_bf16", (200, 128, 8, 2, 96), 1, (50, 51, 52, 53, 54)),
+    # the MFMA path with most experts empty: one token (two slots), and eight
+    # tokens over sixteen experts
+    ("single_token_bf16", (1, 128, 8, 2, 64), 1, (45, 46, 47, 48, 49)),
+    ("empty_experts_bf16", (8, 128, 16, 1, 64), 1, (40, 41, 42, 43, 44)),
     ("wide_bf16", (333, 256, 16, 4, 160), 1, (60, 61, 62, 63, 64)),
     # column-tiled masked gradient: gate_up has H > 2048 columns, down has I > 2048
     ("coltiled_gate_up_bf16", (64, 4096, 4, 2, 64), 1, (70, 71, 72, 73, 74)),
