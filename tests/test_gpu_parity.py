@@ -175,6 +175,8 @@ CASES = [
     # tokens over sixteen experts
     ("single_token_bf16", (1, 128, 8, 2, 64), 1, (45, 46, 47, 48, 49)),
     ("empty_experts_bf16", (8, 128, 16, 1, 64), 1, (40, 41, 42, 43, 44)),
+    # every token routed to every expert (K = E): equal groups of T slots
+    ("all_experts_bf16", (96, 128, 4, 4, 64), 1, (35, 36, 37, 38, 39)),
     ("wide_bf16", (333, 256, 16, 4, 160), 1, (60, 61, 62, 63, 64)),
     # column-tiled masked gradient: gate_up has H > 2048 columns, down has I > 2048
     ("coltiled_gate_up_bf16", (64, 4096, 4, 2, 64), 1, (70, 71, 72, 73, 74)),
