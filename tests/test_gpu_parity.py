@@ -750,11 +750,13 @@ def test_forward_q4_edge_scales_and_zeros(capi):
                           res.W[ngu:].view(torch.int16).cpu().numpy().view(np.uint16))
 
 
+# (1, 256, 8, 2, 128) and (8, 256, 16, 1, 128): most experts empty;
 # (1024, 256, 4, 2, 128): 512 slots per expert on average, the 256-row tiles
 # (2200, 4096, 4, 2, 256) and (2000, 2048, 24, 4, 256): down launches whose
 # last round is split in 2 and 4 contraction parts (a part may start on the
 # second group of a scale pair); (1024, 2048, 16, 4, 1152): gate_up split in 4
-@pytest.mark.parametrize("dims,group", [((200, 256, 8, 2, 128), 64), ((333, 512, 16, 4, 384), 64),
+@pytest.mark.parametrize("dims,group", [((1, 256, 8, 2, 128), 64), ((8, 256, 16, 1, 128), 64),
+                                        ((200, 256, 8, 2, 128), 64), ((333, 512, 16, 4, 384), 64),
                                         ((1024, 256, 4, 2, 128), 64),
                                         ((1024, 2048, 128, 8, 768), 128),
                                         ((2200, 4096, 4, 2, 256), 64),
