@@ -369,6 +369,7 @@ def test_repeat_runs_are_bit_identical(capi):
 # --------------------------------------------------------------------------
 TOPK_CASES = [(10000, 500, "normal"), (50000, 12345, "ties"), (4096 * 3 + 17, 4096 * 3 + 17, "normal"),
               (9999, 1, "ties"), (200000, 1000, "exclude"), (100000, 3000, "ties_exclude"),
+              (1, 1, "normal"), (2, 1, "allsame"), (3, 2, "ties"),
               (4096, 4000, "allsame"), (123457, 61728, "exclude"),
               # from 2^20 keys on, a whole gradient takes the sampled single pass
               (3000001, 15000, "normal"), (2500000, 200000, "ties"), (1 << 20, 1 << 20, "normal"),
