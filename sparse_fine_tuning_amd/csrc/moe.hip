@@ -28,6 +28,35 @@ __device__ __forceinline__ uint32_t logit_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Maximum over the wave of a 64-bit key, the same in every lane: within each
+// row of 16 lanes by DPP (swap neighbours, swap pairs, mirror the halves,
+// mirror the row), then over the four rows' first lanes.
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(v)), kCtrl, 0xf, 0xf, false));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(v >> 32)), kCtrl, 0xf, 0xf, false));
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), l));
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o = dpp_u64<0xB1>(v);   // quad_perm 1,0,3,2
+  v = o > v ? o : v;
+  o = dpp_u64<0x4E>(v);            // quad_perm 2,3,0,1
+  v = o > v ? o : v;
+  o = dpp_u64<0x141>(v);           // row_half_mirror
+  v = o > v ? o : v;
+  o = dpp_u64<0x140>(v);           // row_mirror
+  v = o > v ? o : v;
+  const uint64_t r0 = readlane_u64(v, 0), r1 = readlane_u64(v, 16);
+  const uint64_t r2 = readlane_u64(v, 32), r3 = readlane_u64(v, 48);
+  const uint64_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
+}
+
 // One wave per token: K rounds of a wave-wide max over (key, -expert id),
 // then softmax over the K chosen logits.  E <= 64 NV, K <= 64: lane l holds
 // experts l, l + 64, ... in NV registers.
@@ -77,13 +106,9 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     uint64_t best = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) best = comp[i] > best ? comp[i] : best;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      uint64_t o = __shfl_xor(best, off, 64);
-      best = o > best ? o : best;
-    }
+    best = wave_max_u64(best);
     const int e = int(0xffffffffu - uint32_t(best & 0xffffffffull));
-    // the owner lane (e % 64) retires the expert and broadcasts its logit
+    // the owner lane (e % 64) retires the expert; its logit is read from it
     float le = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
@@ -91,7 +116,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
         comp[i] = 0;
         le = val[i];
       }
-    le = __shfl(le, e & 63, 64);
+    le = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(le), e & 63));
     if (lane == j) {
       my_id = e;
       my_l = le;
